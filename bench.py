@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the quaternion cumulative-product scan, forward + backward, on
+one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that is
+already resident in HBM: the forward (q, init -> cum, writing the saved
+boundary state) then the backward (q, init, d_cum, boundary state -> d_q,
+d_init).  Default workload: b=8, s=4096, h=32, j=32, float32 storage
+(33,554,432 quaternions, 512 MiB per [b,s,h,j,4] tensor), seeded unit
+quaternions.
+
+Reported value: algorithmic bytes per step (32 B/quaternion forward + 48 B
+backward, plus 16 B per column for init and d_init) / wall time per step.
+The last stdout line is one JSON record; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "quat cumprod fwd+bwd GB/s and % HBM peak, b8·s4096·h32·j32 fp32"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "quaternion_cumprod_autodiff_amd", "csrc", "qc_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_headline.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload_key: str):
+    """HBM bytes per backward launch from the committed rocprofv3 counter
+    summary, or None when missing or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha() or rec.get("workload") != workload_key:
+        return None
+    return rec.get("bwd_hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, min_seconds: float = 10.0):
+    """The float64 oracle timed on the host cores on a bounded sample: the
+    first batch entry of the workload (all h*j columns, all s steps)."""
+    import numpy as np
+
+    import oracle
+    q = inp.q[:1].astype(np.float64)
+    init = inp.init[:1].astype(np.float64)
+    d = inp.d_cum[:1].astype(np.float64)
+    n = q.shape[0] * q.shape[1] * q.shape[2] * q.shape[3]
+    cols = q.shape[2] * q.shape[3]
+    threads = oracle.threads(0)
+    oracle.fwd(q[:, :64], init)             # load and warm up
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.fwd(q, init, threads)
+        oracle.bwd(q, init, d, threads)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_pass = t_total / reps
+    gbps = (80.0 * n + 32.0 * cols) / per_pass / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch entry 0 of the workload ({cols} columns x {q.shape[1]} steps = {n} quaternions), "
+                      f"float64 forward + reverse-recurrence backward, {reps} pass(es), {per_pass:.2f} s per pass"}
+
+
+def copy_calibration(nbytes: int, steps: int, warmup: int):
+    """Plain device-to-device copy of a tensor of known size (HBM ceiling and
+    the reference point for scaling hardware byte counters)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    return 2.0 * nbytes / dt / 1e9, dt
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    from quaternion_cumprod_autodiff_amd.inputs import CONFIGS, make_config
+    ap.add_argument("--config", default="headline", choices=list(CONFIGS))
+    ap.add_argument("--path", default=None, choices=["auto", "column", "chunked"])
+    ap.add_argument("--leaves-only", action="store_true",
+                    help="backward without the saved boundary state (re-derives it from q)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only time a plain device copy of one [b,s,h,j,4] tensor")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(columns shard across GPUs without communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quaternion_cumprod_autodiff_amd import capi
+
+    b, s, h, j, recipe, io = CONFIGS[args.config]
+    n = b * s * h * j
+    cols = b * h * j
+    io_bytes = 16 if io == "f32" else 8
+
+    if args.copy_calibration:
+        gbps, dt = copy_calibration(n * io_bytes, args.steps, args.warmup)
+        print(json.dumps({"copy_bytes": n * io_bytes, "copy_GBps": round(gbps, 1), "ms": round(dt * 1e3, 4)}))
+        return
+
+    t0 = time.perf_counter()
+    inp = make_config(args.config, want_f64=False)
+    log(f"[bench] inputs {args.config} generated in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if io == "bf16" else np.float32)).to(dev)
+        return t.view(torch.bfloat16) if io == "bf16" else t
+
+    q, init, d_cum = up(inp.q), up(inp.init), up(inp.d_cum)
+    cum = torch.empty_like(q)
+    d_q = torch.empty_like(q)
+    d_init = torch.empty_like(init)
+    ckpt = None if args.leaves_only else capi.new_ckpt(q)
+
+    def fwd():
+        capi.quat_cumprod_fwd(q, init, cum, ckpt, path=args.path)
+
+    def bwd():
+        capi.quat_cumprod_bwd(q, init, d_cum, ckpt, d_q=d_q, d_init=d_init, path=args.path)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    status = capi.default_workspace.status(dev)
+    if status != 0:
+        raise RuntimeError("a cross-block wait hit its spin limit during warm-up")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    fe = [(ev(), ev()) for _ in range(args.steps)]
+    be = [(ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        fe[k][0].record()
+        fwd()
+        fe[k][1].record()
+        be[k][0].record()
+        bwd()
+        be[k][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if capi.default_workspace.status(dev) != 0:
+        raise RuntimeError("a cross-block wait hit its spin limit during the timed steps")
+
+    fwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in fe]))
+    bwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in be]))
+    ms_step = wall / args.steps * 1e3
+    fwd_bytes = 2 * io_bytes * n + io_bytes * cols
+    bwd_bytes = 3 * io_bytes * n + 2 * io_bytes * cols
+    value = (fwd_bytes + bwd_bytes) / (ms_step * 1e-3) / 1e9
+    bwd_gbps = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+    workload = f"{args.config} b{b} s{s} h{h} j{j} {io} I/O, forward + backward"
+    traffic = load_traffic(workload) if (args.path in (None, "auto", "chunked") and not args.leaves_only) else None
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64" if io == "f32" else "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "b": b, "s": s, "h": h, "j": j, "io_dtype": io, "recipe": recipe,
+                   "path": args.path or "auto",
+                   "backward": "leaves-only" if args.leaves_only else "saved boundary state"},
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "elements_per_s": round(n / (ms_step * 1e-3), 1),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_GBps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "kernel": "bwd_chunked_kernel", "achieved": round(bwd_gbps, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * quat_cumprod.h -- C ABI of the MI355X (gfx950) quaternion cumulative-product
+ * scan and its vector-Jacobian product.
+ *
+ * What is computed (burn-mamba source page
+ * "burn_mamba/mamba3/quat_scan/backward.rs", module doc "Gradient math"):
+ *
+ *   forward   cum[t] = q_t (x) cum[t-1],  cum[-1] = init,  t = 0 .. s-1
+ *             (equivalently cum[t] = P_t (x) init with P_t = q_t (x) ... (x) q_0)
+ *   backward  given the cotangent d_cum of cum:
+ *             S[t]   = sum_{u >= t} conj(P_u) (x) d_cum[u]     (reverse cumsum)
+ *             G[t]   = P_t (x) S[t] / |P_t|^2
+ *             d_q[t] = G[t] (x) conj(cum[t-1])                 (cum[-1] = init)
+ *             d_init = S[0]
+ *
+ * (x) is the Hamilton product on scalar-first quaternions (w, x, y, z) with
+ * i^2 = j^2 = k^2 = ijk = -1; conj(w, x, y, z) = (w, -x, -y, -z).  The page
+ * states the closed form for unit quaternions (|P_t| = 1); the division by
+ * |P_t|^2 keeps it the exact VJP of the given, rounded inputs, which are never
+ * exactly unit.  It requires every prefix product P_t to be non-zero in the
+ * working precision (no exactly-zero step q_t); results are not finite
+ * otherwise.
+ *
+ * Any gradient of the final carry cum[:, s-1] must already be added into
+ * d_cum[:, s-1]: the page folds it there before the backward node runs, so the
+ * node has a single cotangent input.
+ *
+ * Tensor layout (row-major, contiguous, no strides):
+ *   q, cum, d_cum, d_q : [b, s, h, j, 4]    init, d_init : [b, h, j, 4]
+ * The quaternion columns of one (b, t) row are the h*j contiguous entries.
+ *
+ * Storage dtypes: QC_DTYPE_F32 (float32 I/O, float64 arithmetic inside) and
+ * QC_DTYPE_BF16 (bfloat16 I/O as raw 16-bit patterns, float32 arithmetic
+ * inside, round-to-nearest-even stores).
+ *
+ * Pointers:
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device,
+ *     owned by the caller.  The library never allocates, frees or keeps a
+ *     pointer after a call returns.
+ *   - Alignment: 16 bytes for float32 tensors, 8 bytes for bfloat16 tensors,
+ *     16 bytes for ckpt and workspace.
+ *   - Outputs must not overlap any input, the workspace or each other.
+ *   - stream is a hipStream_t passed as void*; NULL is the null stream.
+ *
+ * Calls are asynchronous: arguments are validated on the host before any HIP
+ * call, then kernels are enqueued on `stream`.  A negative return value means
+ * nothing was enqueued (except QC_ERR_HIP, which means a launch failed).
+ *
+ * Workspace: a device buffer of at least quat_cumprod_workspace_bytes(...)
+ * bytes.  It must be zeroed once after allocation (quat_cumprod_workspace_init
+ * does this on a stream); every call leaves it zeroed again for the next
+ * call.  Calls sharing one workspace must be ordered (same stream or
+ * synchronised); concurrent calls need separate workspaces.
+ */
+#ifndef QUAT_CUMPROD_H
+#define QUAT_CUMPROD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtype of q, init, cum, d_cum, d_q, d_init. */
+enum {
+    QC_DTYPE_F32 = 0,
+    QC_DTYPE_BF16 = 1
+};
+
+/* Return codes. */
+enum {
+    QC_OK = 0,
+    QC_ERR_NULL = -1,       /* a required pointer is NULL */
+    QC_ERR_SHAPE = -2,      /* a dimension < 1, or sizes overflow the library's limits */
+    QC_ERR_ALIGN = -3,      /* a pointer is not aligned as required */
+    QC_ERR_DTYPE = -4,      /* unknown dtype */
+    QC_ERR_ALIAS = -5,      /* an output overlaps an input, another output or the workspace */
+    QC_ERR_WORKSPACE = -6,  /* workspace or ckpt buffer NULL or too small */
+    QC_ERR_HIP = -7,        /* a HIP runtime call failed (see quat_cumprod_last_hip_error) */
+    QC_ERR_OPTION = -8      /* invalid qc_options field */
+};
+
+/* Execution-path choice for the *_ex entry points. */
+enum {
+    QC_PATH_AUTO = 0,       /* library heuristic */
+    QC_PATH_COLUMN = 1,     /* one lane walks a whole column sequentially */
+    QC_PATH_CHUNKED = 2     /* sequence-parallel tiles with cross-block carries */
+};
+
+typedef struct {
+    int32_t path;           /* QC_PATH_* */
+    int32_t reserved[7];    /* must be zero */
+} qc_options;
+
+/* Bytes of workspace that quat_cumprod_fwd and quat_cumprod_bwd need for this
+ * shape and dtype (one workspace serves both).  Returns 0 for invalid
+ * arguments. */
+size_t quat_cumprod_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype);
+
+/* Bytes of the optional saved boundary state ("ckpt") that the forward can
+ * write and the backward can read: the prefix products P at a fixed stride
+ * of sequence steps, kept in the internal precision.  Its contents are
+ * internal to this library; only its size is part of the ABI.  Returns 0 for
+ * invalid arguments. */
+size_t quat_cumprod_ckpt_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype);
+
+/* Zero a freshly allocated workspace on `stream` (a fill kernel, so it may be
+ * captured in a HIP graph).  Needed once per allocation. */
+int quat_cumprod_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward scan (the page's Mamba3QuatScanBackendExt::quat_cumprod).
+ *   q      [b,s,h,j,4] in      init [b,h,j,4] in      cum [b,s,h,j,4] out
+ *   ckpt   optional out (NULL = none): saved boundary state for the
+ *          backward, ckpt_bytes >= quat_cumprod_ckpt_bytes(...). */
+int quat_cumprod_fwd(const void* q, const void* init, void* cum,
+                     void* ckpt, size_t ckpt_bytes,
+                     int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward (the page's quat_scan_backward): recomputes the prefix products
+ * from the saved leaves q and init, never from stored scan intermediates.
+ *   q, init, d_cum   in
+ *   ckpt             optional in (NULL = none): the boundary state written by
+ *                    quat_cumprod_fwd for the same q, shape and dtype.  With
+ *                    it the backward reads q and d_cum once; without it the
+ *                    backward first re-derives the boundary prefix products
+ *                    from q (one more read of q).
+ *   d_q [b,s,h,j,4], d_init [b,h,j,4]   out, each optional (NULL = not
+ *                    wanted, as for an untracked input); both NULL is a no-op. */
+int quat_cumprod_bwd(const void* q, const void* init, const void* d_cum,
+                     const void* ckpt, size_t ckpt_bytes,
+                     void* d_q, void* d_init,
+                     int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same as above with an explicit path choice (opts may be NULL = defaults). */
+int quat_cumprod_fwd_ex(const void* q, const void* init, void* cum,
+                        void* ckpt, size_t ckpt_bytes,
+                        int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        const qc_options* opts);
+int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum,
+                        const void* ckpt, size_t ckpt_bytes,
+                        void* d_q, void* d_init,
+                        int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        const qc_options* opts);
+
+/* Synchronise `stream`, then read the workspace's device-side status word:
+ * 0 = every cross-block wait completed; 1 = a wait hit its spin limit; 2 = a
+ * call ran on a workspace that had not been zeroed.  Non-zero means the
+ * results of some call since the last clear are invalid (and, for 2, the
+ * workspace must be re-initialised).  clear != 0 resets it to 0. */
+int quat_cumprod_workspace_status(void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t clear, int32_t* status_out);
+
+/* Static description of a return code. */
+const char* quat_cumprod_strerror(int32_t code);
+
+/* Text of the last HIP error this library saw on the calling thread ("" if none). */
+const char* quat_cumprod_last_hip_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t quat_cumprod_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUAT_CUMPROD_H */

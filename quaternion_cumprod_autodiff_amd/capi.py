@@ -1,0 +1,245 @@
+"""ctypes binding of the C ABI in include/quat_cumprod.h.
+
+Argument marshalling only: shapes, dtypes and device pointers of torch
+tensors go in, every step of the scan runs in the HIP library
+(libquatcumprod.so, built in-tree by build.py).  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from .build import LIB_PATH
+
+QC_DTYPE_F32 = 0
+QC_DTYPE_BF16 = 1
+QC_PATH_AUTO = 0
+QC_PATH_COLUMN = 1
+QC_PATH_CHUNKED = 2
+PATHS = {"auto": QC_PATH_AUTO, "column": QC_PATH_COLUMN, "chunked": QC_PATH_CHUNKED}
+
+_DTYPES = {torch.float32: QC_DTYPE_F32, torch.bfloat16: QC_DTYPE_BF16}
+
+# The exported symbols, as declared in include/quat_cumprod.h.
+EXPORTS = (
+    "quat_cumprod_workspace_bytes", "quat_cumprod_ckpt_bytes", "quat_cumprod_workspace_init",
+    "quat_cumprod_fwd", "quat_cumprod_bwd", "quat_cumprod_fwd_ex", "quat_cumprod_bwd_ex",
+    "quat_cumprod_workspace_status", "quat_cumprod_strerror", "quat_cumprod_last_hip_error",
+    "quat_cumprod_version",
+)
+
+
+class QcOptions(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
+class QuatCumprodError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        lib = load()
+        msg = lib.quat_cumprod_strerror(code).decode()
+        if code == -7:
+            msg += ": " + lib.quat_cumprod_last_hip_error().decode()
+        super().__init__(f"{where}: {msg} (code {code})")
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load(path: str | None = None):
+    """Load libquatcumprod.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"HIP library not built: {p} is missing "
+                               "(run __graft_entry__.build() or quaternion_cumprod_autodiff_amd/build.py)")
+        lib = ctypes.CDLL(p)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        dims = [i64, i64, i64, i64, i32]
+        lib.quat_cumprod_workspace_bytes.argtypes = dims
+        lib.quat_cumprod_workspace_bytes.restype = sz
+        lib.quat_cumprod_ckpt_bytes.argtypes = dims
+        lib.quat_cumprod_ckpt_bytes.restype = sz
+        lib.quat_cumprod_workspace_init.argtypes = [vp, sz, vp]
+        lib.quat_cumprod_workspace_init.restype = ctypes.c_int
+        fwd = [vp, vp, vp, vp, sz] + dims + [vp, sz, vp]
+        bwd = [vp, vp, vp, vp, sz, vp, vp] + dims + [vp, sz, vp]
+        lib.quat_cumprod_fwd.argtypes = fwd
+        lib.quat_cumprod_fwd.restype = ctypes.c_int
+        lib.quat_cumprod_bwd.argtypes = bwd
+        lib.quat_cumprod_bwd.restype = ctypes.c_int
+        lib.quat_cumprod_fwd_ex.argtypes = fwd + [ctypes.POINTER(QcOptions)]
+        lib.quat_cumprod_fwd_ex.restype = ctypes.c_int
+        lib.quat_cumprod_bwd_ex.argtypes = bwd + [ctypes.POINTER(QcOptions)]
+        lib.quat_cumprod_bwd_ex.restype = ctypes.c_int
+        lib.quat_cumprod_workspace_status.argtypes = [vp, sz, vp, i32, ctypes.POINTER(i32)]
+        lib.quat_cumprod_workspace_status.restype = ctypes.c_int
+        lib.quat_cumprod_strerror.argtypes = [i32]
+        lib.quat_cumprod_strerror.restype = ctypes.c_char_p
+        lib.quat_cumprod_last_hip_error.argtypes = []
+        lib.quat_cumprod_last_hip_error.restype = ctypes.c_char_p
+        lib.quat_cumprod_version.argtypes = []
+        lib.quat_cumprod_version.restype = i32
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise QuatCumprodError(rc, where)
+
+
+def _dims(q: torch.Tensor):
+    if q.dim() != 5 or q.shape[-1] != 4:
+        raise ValueError(f"q must be [b, s, h, j, 4], got {tuple(q.shape)}")
+    b, s, h, j, _ = q.shape
+    return int(b), int(s), int(h), int(j)
+
+
+def _check_like(name: str, t: torch.Tensor | None, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    return _DTYPES[t.dtype]
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _options(path: str | None):
+    if path is None:
+        return None
+    o = QcOptions()
+    o.path = PATHS[path]
+    return ctypes.byref(o)
+
+
+def workspace_bytes(b, s, h, j, dtype=torch.float32) -> int:
+    return int(load().quat_cumprod_workspace_bytes(b, s, h, j, _DTYPES[dtype]))
+
+
+def ckpt_bytes(b, s, h, j, dtype=torch.float32) -> int:
+    return int(load().quat_cumprod_ckpt_bytes(b, s, h, j, _DTYPES[dtype]))
+
+
+class Workspace:
+    """A zero-initialised device workspace that grows on demand (per device)."""
+
+    def __init__(self):
+        self._buf: dict[int, torch.Tensor] = {}
+
+    def get(self, nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        buf = self._buf.get(idx)
+        if buf is None or buf.numel() < nbytes:
+            nbytes = max(nbytes, 1 << 20)
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            _check(load().quat_cumprod_workspace_init(_ptr(buf), buf.numel(), _stream(stream)),
+                   "quat_cumprod_workspace_init")
+            self._buf[idx] = buf
+        return buf
+
+    def status(self, device: torch.device, stream=None, clear: bool = True) -> int:
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        buf = self._buf.get(idx)
+        if buf is None:
+            return 0
+        out = ctypes.c_int32(0)
+        _check(load().quat_cumprod_workspace_status(_ptr(buf), buf.numel(), _stream(stream), int(clear),
+                                                    ctypes.byref(out)), "quat_cumprod_workspace_status")
+        return int(out.value)
+
+
+default_workspace = Workspace()
+
+
+def new_ckpt(q: torch.Tensor) -> torch.Tensor:
+    """Allocate a buffer for the saved boundary state of a forward over q."""
+    b, s, h, j = _dims(q)
+    return torch.empty(ckpt_bytes(b, s, h, j, q.dtype), dtype=torch.uint8, device=q.device)
+
+
+def quat_cumprod_fwd(q: torch.Tensor, init: torch.Tensor, cum: torch.Tensor | None = None,
+                     ckpt: torch.Tensor | None = None, *, path: str | None = None, stream=None,
+                     workspace: Workspace | None = None) -> torch.Tensor:
+    """cum[t] = q_t (x) cum[t-1], cum[-1] = init (device computation).
+
+    If ``ckpt`` (from :func:`new_ckpt`) is given, the boundary state for the
+    backward is written into it as well.
+    """
+    b, s, h, j = _dims(q)
+    dt = _dtype_code(q)
+    if cum is None:
+        cum = torch.empty_like(q)
+    _check_like("init", init, (b, h, j, 4), q.dtype, q.device)
+    _check_like("cum", cum, q.shape, q.dtype, q.device)
+    if ckpt is not None and ckpt.device != q.device:
+        raise ValueError("ckpt must be on q's device")
+    ws = (workspace or default_workspace).get(workspace_bytes(b, s, h, j, q.dtype), q.device, stream)
+    rc = load().quat_cumprod_fwd_ex(_ptr(q), _ptr(init), _ptr(cum), _ptr(ckpt),
+                                    0 if ckpt is None else ckpt.numel() * ckpt.element_size(),
+                                    b, s, h, j, dt, _ptr(ws), ws.numel(), _stream(stream), _options(path))
+    _check(rc, "quat_cumprod_fwd")
+    return cum
+
+
+def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
+                     ckpt: torch.Tensor | None = None, *, want_dq: bool = True, want_dinit: bool = True,
+                     d_q: torch.Tensor | None = None, d_init: torch.Tensor | None = None,
+                     path: str | None = None, stream=None, workspace: Workspace | None = None):
+    """VJP of the scan: returns (d_q, d_init); an unwanted output is None."""
+    b, s, h, j = _dims(q)
+    dt = _dtype_code(q)
+    if want_dq and d_q is None:
+        d_q = torch.empty_like(q)
+    if want_dinit and d_init is None:
+        d_init = torch.empty_like(init)
+    if not want_dq:
+        d_q = None
+    if not want_dinit:
+        d_init = None
+    _check_like("init", init, (b, h, j, 4), q.dtype, q.device)
+    _check_like("d_cum", d_cum, q.shape, q.dtype, q.device)
+    _check_like("d_q", d_q, q.shape, q.dtype, q.device)
+    _check_like("d_init", d_init, (b, h, j, 4), q.dtype, q.device)
+    if ckpt is not None and ckpt.device != q.device:
+        raise ValueError("ckpt must be on q's device")
+    ws = (workspace or default_workspace).get(workspace_bytes(b, s, h, j, q.dtype), q.device, stream)
+    rc = load().quat_cumprod_bwd_ex(_ptr(q), _ptr(init), _ptr(d_cum), _ptr(ckpt),
+                                    0 if ckpt is None else ckpt.numel() * ckpt.element_size(),
+                                    _ptr(d_q), _ptr(d_init), b, s, h, j, dt, _ptr(ws), ws.numel(),
+                                    _stream(stream), _options(path))
+    _check(rc, "quat_cumprod_bwd")
+    return d_q, d_init

@@ -1,0 +1,300 @@
+// qc_abi.cpp -- C ABI of the quaternion cumulative-product scan (see
+// include/quat_cumprod.h): argument validation, path choice, workspace
+// layout and kernel launches on the caller's stream.
+//
+// All validation happens before the first HIP call, so a rejected call
+// touches no device state.
+#include "quat_cumprod.h"
+#include "qc_internal.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+
+namespace {
+
+using qc::kCkptStride;
+
+thread_local std::string g_last_hip_error;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = hipGetErrorString(e);
+    return QC_ERR_HIP;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;   // quaternions per tensor
+constexpr size_t kAlignWs = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+    int64_t b = 0, s = 0, M = 0, N = 0;
+    int dtype = 0;
+    size_t io_bytes = 0;      // bytes per stored quaternion
+    size_t ct_bytes = 0;      // bytes per internal quaternion
+    int wc = 0;
+    int64_t n_cg = 0, n_chains = 0;
+    int64_t fwd_tiles = 0, bwd_tiles = 0;   // per chain
+    int64_t n_ck = 0;
+    size_t ckpt_bytes = 0;
+    size_t off_flags = 0, off_desc = 0, off_ckpt = 0, ws_bytes = 0;
+    int64_t n_cols = 0;
+};
+
+int column_group_width(int64_t M) {
+    if (M >= 64) return 64;
+    int w = 1;
+    while (w < M) w <<= 1;
+    return w;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a <= limit / b; }
+
+int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p) {
+    if (dtype != QC_DTYPE_F32 && dtype != QC_DTYPE_BF16) return QC_ERR_DTYPE;
+    if (b < 1 || s < 1 || h < 1 || j < 1) return QC_ERR_SHAPE;
+    if (!mul_ok(h, j, int64_t(1) << 31)) return QC_ERR_SHAPE;
+    const int64_t M = h * j;
+    if (!mul_ok(b, M, int64_t(1) << 31)) return QC_ERR_SHAPE;
+    if (!mul_ok(b * M, s, kMaxElems)) return QC_ERR_SHAPE;
+    p->b = b; p->s = s; p->M = M; p->N = b * s * M; p->dtype = dtype;
+    p->io_bytes = dtype == QC_DTYPE_F32 ? 16 : 8;
+    p->ct_bytes = dtype == QC_DTYPE_F32 ? 32 : 16;
+    p->n_cols = b * M;
+    p->wc = column_group_width(M);
+    p->n_cg = (M + p->wc - 1) / p->wc;
+    p->n_chains = b * p->n_cg;
+    const int64_t tf = qc::fwd_tile_steps(p->wc), tb = qc::bwd_tile_steps(p->wc);
+    p->fwd_tiles = (s + tf - 1) / tf;
+    p->bwd_tiles = (s + tb - 1) / tb;
+    // Grid (one block per tile) and the 32-bit ticket bound the tile count.
+    const int64_t max_blocks = int64_t(1) << 22;
+    if (!mul_ok(p->n_chains, p->bwd_tiles, max_blocks)) return QC_ERR_SHAPE;
+    if ((p->n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock > max_blocks) return QC_ERR_SHAPE;
+    p->n_ck = (s + kCkptStride - 1) / kCkptStride;
+    p->ckpt_bytes = size_t(b) * size_t(p->n_ck) * size_t(M) * p->ct_bytes;
+    const int64_t nodes = p->n_chains * (p->fwd_tiles > p->bwd_tiles ? p->fwd_tiles : p->bwd_tiles);
+    p->off_flags = size_t(qc::kHdrWords) * 4;
+    p->off_desc = round_up(p->off_flags + size_t(nodes) * 4, kAlignWs);
+    p->off_ckpt = round_up(p->off_desc + size_t(nodes) * size_t(p->wc) * p->ct_bytes, kAlignWs);
+    p->ws_bytes = round_up(p->off_ckpt + p->ckpt_bytes, kAlignWs);
+    return QC_OK;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Ranges flagged as outputs must be disjoint from every other range.
+bool any_alias(const Range* r, const bool* is_out, int n) {
+    for (int i = 0; i < n; ++i)
+        for (int k = i + 1; k < n; ++k)
+            if ((is_out[i] || is_out[k]) && overlap(r[i], r[k])) return true;
+    return false;
+}
+
+int check_options(const qc_options* o, int* path) {
+    *path = QC_PATH_AUTO;
+    if (!o) return QC_OK;
+    if (o->path < QC_PATH_AUTO || o->path > QC_PATH_CHUNKED) return QC_ERR_OPTION;
+    for (int i = 0; i < 7; ++i)
+        if (o->reserved[i] != 0) return QC_ERR_OPTION;
+    *path = o->path;
+    return QC_OK;
+}
+
+// The column path wins the forward when enough columns exist to fill the
+// chip with one lane per column; the backward always prefers the chunked path
+// (it reads q and d_cum once instead of twice).
+constexpr int64_t kColumnPathMinColumns = int64_t(1) << 18;
+
+qc::KernelArgs base_args(const Plan& p, void* ws) {
+    qc::KernelArgs a{};
+    a.b = p.b; a.s = p.s; a.M = p.M; a.n_ck = p.n_ck;
+    a.n_cg = p.n_cg; a.n_chains = p.n_chains;
+    a.hdr = reinterpret_cast<uint32_t*>(ws);
+    a.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.off_flags);
+    a.desc = static_cast<char*>(ws) + p.off_desc;
+    a.spin_limit = qc::kSpinLimit;
+    return a;
+}
+
+int launch_forward(const Plan& p, const void* q, const void* init, void* cum, void* ckpt, void* ws,
+                   hipStream_t st, bool column) {
+    qc::KernelArgs a = base_args(p, ws);
+    a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt;
+    hipError_t e;
+    if (column) {
+        a.n_tiles = 1;
+        a.n_blocks = uint32_t((p.n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock);
+        e = qc::launch_fwd_column(p.dtype, a, st);
+    } else {
+        a.n_tiles = p.fwd_tiles;
+        a.n_blocks = uint32_t(p.n_chains * p.fwd_tiles);
+        e = qc::launch_fwd_chunked(p.dtype, p.wc, a, st);
+    }
+    return e == hipSuccess ? QC_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t quat_cumprod_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype) {
+    Plan p;
+    return make_plan(b, s, h, j, dtype, &p) == QC_OK ? p.ws_bytes : 0;
+}
+
+size_t quat_cumprod_ckpt_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype) {
+    Plan p;
+    return make_plan(b, s, h, j, dtype, &p) == QC_OK ? p.ckpt_bytes : 0;
+}
+
+int quat_cumprod_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return QC_ERR_NULL;
+    if (!aligned(workspace, 16)) return QC_ERR_ALIGN;
+    if (workspace_bytes < size_t(qc::kHdrWords) * 4) return QC_ERR_WORKSPACE;
+    const hipError_t e = qc::launch_zero_words(static_cast<uint32_t*>(workspace), workspace_bytes / 4,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QC_OK : hip_fail(e);
+}
+
+int quat_cumprod_fwd_ex(const void* q, const void* init, void* cum, void* ckpt, size_t ckpt_bytes,
+                        int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                        void* workspace, size_t workspace_bytes, void* stream, const qc_options* opts) {
+    int path;
+    int rc = check_options(opts, &path);
+    if (rc != QC_OK) return rc;
+    Plan p;
+    rc = make_plan(b, s, h, j, dtype, &p);
+    if (rc != QC_OK) return rc;
+    if (!q || !init || !cum) return QC_ERR_NULL;
+    if (!workspace) return QC_ERR_WORKSPACE;
+    if (ckpt && ckpt_bytes < p.ckpt_bytes) return QC_ERR_WORKSPACE;
+    if (workspace_bytes < p.ws_bytes) return QC_ERR_WORKSPACE;
+    if (!aligned(q, p.io_bytes) || !aligned(init, p.io_bytes) || !aligned(cum, p.io_bytes)) return QC_ERR_ALIGN;
+    if ((ckpt && !aligned(ckpt, 16)) || !aligned(workspace, 16)) return QC_ERR_ALIGN;
+    const size_t big = size_t(p.N) * p.io_bytes, small = size_t(p.n_cols) * p.io_bytes;
+    const Range rs[] = {{q, big}, {init, small}, {cum, big}, {ckpt, p.ckpt_bytes}, {workspace, p.ws_bytes}};
+    const bool out[] = {false, false, true, true, true};
+    if (any_alias(rs, out, 5)) return QC_ERR_ALIAS;
+
+    const bool column = path == QC_PATH_COLUMN || (path == QC_PATH_AUTO && p.n_cols >= kColumnPathMinColumns);
+    return launch_forward(p, q, init, cum, ckpt, workspace, static_cast<hipStream_t>(stream), column);
+}
+
+int quat_cumprod_fwd(const void* q, const void* init, void* cum, void* ckpt, size_t ckpt_bytes,
+                     int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    return quat_cumprod_fwd_ex(q, init, cum, ckpt, ckpt_bytes, b, s, h, j, dtype, workspace, workspace_bytes,
+                               stream, nullptr);
+}
+
+int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, const void* ckpt, size_t ckpt_bytes,
+                        void* d_q, void* d_init,
+                        int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                        void* workspace, size_t workspace_bytes, void* stream, const qc_options* opts) {
+    int path;
+    int rc = check_options(opts, &path);
+    if (rc != QC_OK) return rc;
+    Plan p;
+    rc = make_plan(b, s, h, j, dtype, &p);
+    if (rc != QC_OK) return rc;
+    if (!q || !init || !d_cum) return QC_ERR_NULL;
+    if (!d_q && !d_init) return QC_OK;
+    if (!workspace) return QC_ERR_WORKSPACE;
+    if (ckpt && ckpt_bytes < p.ckpt_bytes) return QC_ERR_WORKSPACE;
+    if (workspace_bytes < p.ws_bytes) return QC_ERR_WORKSPACE;
+    if (!aligned(q, p.io_bytes) || !aligned(init, p.io_bytes) || !aligned(d_cum, p.io_bytes)) return QC_ERR_ALIGN;
+    if ((d_q && !aligned(d_q, p.io_bytes)) || (d_init && !aligned(d_init, p.io_bytes))) return QC_ERR_ALIGN;
+    if ((ckpt && !aligned(ckpt, 16)) || !aligned(workspace, 16)) return QC_ERR_ALIGN;
+    const size_t big = size_t(p.N) * p.io_bytes, small = size_t(p.n_cols) * p.io_bytes;
+    const Range rs[] = {{q, big}, {init, small}, {d_cum, big}, {ckpt, p.ckpt_bytes},
+                        {d_q, big}, {d_init, small}, {workspace, p.ws_bytes}};
+    const bool out[] = {false, false, false, false, true, true, true};
+    if (any_alias(rs, out, 7)) return QC_ERR_ALIAS;
+
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    qc::KernelArgs a = base_args(p, workspace);
+    a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init;
+    hipError_t e;
+    if (path == QC_PATH_COLUMN) {
+        a.n_tiles = 1;
+        a.n_blocks = uint32_t((p.n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock);
+        e = qc::launch_bwd_column(p.dtype, a, st);
+        return e == hipSuccess ? QC_OK : hip_fail(e);
+    }
+    void* ck = const_cast<void*>(ckpt);
+    if (!ck) {
+        // Leaves-only backward: re-derive the boundary prefix products from q.
+        ck = static_cast<char*>(workspace) + p.off_ckpt;
+        rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false);
+        if (rc != QC_OK) return rc;
+    }
+    a.ckpt = ck;
+    a.n_tiles = p.bwd_tiles;
+    a.n_blocks = uint32_t(p.n_chains * p.bwd_tiles);
+    e = qc::launch_bwd_chunked(p.dtype, p.wc, a, st);
+    return e == hipSuccess ? QC_OK : hip_fail(e);
+}
+
+int quat_cumprod_bwd(const void* q, const void* init, const void* d_cum, const void* ckpt, size_t ckpt_bytes,
+                     void* d_q, void* d_init,
+                     int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    return quat_cumprod_bwd_ex(q, init, d_cum, ckpt, ckpt_bytes, d_q, d_init, b, s, h, j, dtype, workspace,
+                               workspace_bytes, stream, nullptr);
+}
+
+int quat_cumprod_workspace_status(void* workspace, size_t workspace_bytes, void* stream, int32_t clear,
+                                  int32_t* status_out) {
+    if (!workspace || !status_out) return QC_ERR_NULL;
+    if (!aligned(workspace, 16)) return QC_ERR_ALIGN;
+    if (workspace_bytes < size_t(qc::kHdrWords) * 4) return QC_ERR_WORKSPACE;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t* word = static_cast<uint32_t*>(workspace) + qc::kHdrStatus;
+    uint32_t v = 0;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMemcpy(&v, word, sizeof v, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+    if (clear && v != 0) {
+        e = qc::launch_zero_words(word, 1, st);
+        if (e != hipSuccess) return hip_fail(e);
+        e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    *status_out = int32_t(v);
+    return QC_OK;
+}
+
+const char* quat_cumprod_strerror(int32_t code) {
+    switch (code) {
+        case QC_OK: return "ok";
+        case QC_ERR_NULL: return "a required pointer is NULL";
+        case QC_ERR_SHAPE: return "invalid shape (a dimension < 1, or sizes beyond the library's limits)";
+        case QC_ERR_ALIGN: return "misaligned pointer";
+        case QC_ERR_DTYPE: return "unknown dtype";
+        case QC_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
+        case QC_ERR_WORKSPACE: return "workspace or ckpt buffer missing or too small";
+        case QC_ERR_HIP: return "HIP runtime error";
+        case QC_ERR_OPTION: return "invalid option";
+        default: return "unknown error code";
+    }
+}
+
+const char* quat_cumprod_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int32_t quat_cumprod_version(void) { return 100; }
+
+}  // extern "C"

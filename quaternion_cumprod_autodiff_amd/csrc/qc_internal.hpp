@@ -1,0 +1,76 @@
+// qc_internal.hpp -- declarations shared by the gfx950 kernels and the C-ABI
+// dispatcher of the quaternion cumulative-product scan.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace qc {
+
+// Stride, in sequence steps, of the saved boundary state: entry n holds the
+// prefix product P_{nK-1} (identity for n = 0) of every column.
+constexpr int kCkptStride = 64;
+
+// Bounded waits: a cross-block wait gives up after this many polls (each poll
+// is one coherent load plus a short sleep, about a microsecond, so well under
+// a second in all) and raises the workspace status word instead of spinning
+// forever.  Status 1 = a wait timed out, 2 = the workspace was not zeroed.
+constexpr uint32_t kSpinLimit = 1u << 16;
+
+// Workspace header words.
+enum : int { kHdrTicket = 0, kHdrDone = 1, kHdrStatus = 2, kHdrWords = 64 };
+
+// Tile geometry of the chunked path, by column-group width WC (a power of two
+// <= 64).  A wave holds R = 64/WC time slices of WC adjacent columns; a block
+// has NW waves; every lane owns L consecutive steps of one column.  A tile is
+// WC columns x (R*NW*L) steps.  The forward tile length is 128 steps and the
+// backward one 64 = kCkptStride, so backward tiles start on saved boundaries.
+struct Geometry {
+    int wc;
+    int fwd_l, fwd_nw;
+    int bwd_l, bwd_nw;
+};
+
+constexpr Geometry geometry_for(int wc) {
+    return wc == 64 ? Geometry{64, 16, 8, 8, 8}
+         : wc == 32 ? Geometry{32, 16, 4, 8, 4}
+         : wc == 16 ? Geometry{16, 16, 2, 8, 2}
+         : wc == 8  ? Geometry{8, 16, 1, 8, 1}
+         : wc == 4  ? Geometry{4, 8, 1, 4, 1}
+         : wc == 2  ? Geometry{2, 4, 1, 2, 1}
+         :            Geometry{1, 2, 1, 1, 1};
+}
+
+constexpr int fwd_tile_steps(int wc) { return (64 / wc) * geometry_for(wc).fwd_nw * geometry_for(wc).fwd_l; }
+constexpr int bwd_tile_steps(int wc) { return (64 / wc) * geometry_for(wc).bwd_nw * geometry_for(wc).bwd_l; }
+
+// Arguments of every scan kernel (passed by value).
+struct KernelArgs {
+    const void* q;        // [b][s][M] quaternions, storage dtype
+    const void* init;     // [b][M]
+    const void* d_cum;    // [b][s][M]           (backward)
+    void* out;            // cum (forward, may be null) or d_q (backward, may be null)
+    void* d_init;         // [b][M]              (backward, may be null)
+    void* ckpt;           // [b][n_ck][M] quaternions in the compute type (may be null)
+    uint32_t* hdr;        // workspace header
+    uint32_t* flags;      // one ready flag per tile
+    void* desc;           // per-tile carry values, WC quaternions each
+    int64_t b, s, M;
+    int64_t n_ck;         // ceil(s / kCkptStride)
+    int64_t n_cg;         // column groups per batch entry
+    int64_t n_chains;     // b * n_cg
+    int64_t n_tiles;      // tiles per chain
+    uint32_t n_blocks;    // grid size
+    uint32_t spin_limit;
+};
+
+hipError_t launch_fwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_t st);
+hipError_t launch_bwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_t st);
+hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st);
+hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);
+hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st);
+
+constexpr int kColumnBlock = 256;   // threads per block on the column path
+
+}  // namespace qc

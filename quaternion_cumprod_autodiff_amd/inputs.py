@@ -56,19 +56,39 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _round_to_storage(x64: np.ndarray, dtype: str):
-    """Return (storage array, float64 array of the stored values)."""
+_CHUNK = 1 << 18   # quaternions per generation chunk (small temporaries get reused)
+
+
+def _rounded(x64: np.ndarray, dtype: str):
+    """Round float64 values to the storage dtype: (storage values, widened float64)."""
     x32 = x64.astype(np.float32)  # nearest-even
     if dtype == "f32":
-        return x32, x32.astype(np.float64)
+        return x32, x32
     if dtype == "bf16":
         bits = f32_to_bf16_bits(x32)
-        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+        return bits, bf16_bits_to_f32(bits)
     raise ValueError(f"unknown storage dtype {dtype!r}")
 
 
-def _unit4(rng: np.random.Generator, shape) -> np.ndarray:
-    v = rng.standard_normal(tuple(shape) + (4,))
+class _Sink:
+    """Storage array (+ optional float64 copy) filled chunk by chunk."""
+
+    def __init__(self, n: int, dtype: str, want_f64: bool):
+        if dtype not in ("f32", "bf16"):
+            raise ValueError(f"unknown storage dtype {dtype!r}")
+        self.dtype = dtype
+        self.st = np.empty((n, 4), dtype=np.float32 if dtype == "f32" else np.uint16)
+        self.f64 = np.empty((n, 4), dtype=np.float64) if want_f64 else None
+
+    def put(self, lo: int, x64: np.ndarray):
+        st, wide = _rounded(x64, self.dtype)
+        hi = lo + x64.shape[0]
+        self.st[lo:hi] = st
+        if self.f64 is not None:
+            self.f64[lo:hi] = wide
+
+
+def _normalise(v: np.ndarray) -> np.ndarray:
     v /= np.sqrt(np.sum(v * v, axis=-1, keepdims=True))
     return v
 
@@ -90,35 +110,44 @@ class ScanInputs:
 
 def make_inputs(b: int, s: int, h: int, j: int, recipe: str = "unit",
                 dtype: str = "f32", seed: int = 0, want_f64: bool = True) -> ScanInputs:
-    """Draw q, init, d_cum for a [b, s, h, j] problem (see module docstring)."""
+    """Draw q, init, d_cum for a [b, s, h, j] problem (see module docstring).
+
+    Draws are made in chunks, which yields exactly the same stream as one
+    draw of the whole array (numpy Generators are chunk-invariant)."""
     rng = np.random.default_rng(seed)
-    shp = (b, s, h, j)
-    if recipe in ("unit", "scaled"):
-        q = _unit4(rng, shp)
-        if recipe == "scaled":
-            q *= rng.uniform(0.5, 1.5, size=shp)[..., None]
+    n = b * s * h * j
+    q = _Sink(n, dtype, want_f64)
+    if recipe == "unit":
+        for lo in range(0, n, _CHUNK):
+            q.put(lo, _normalise(rng.standard_normal((min(n, lo + _CHUNK) - lo, 4))))
+    elif recipe == "scaled":
+        v = _normalise(rng.standard_normal((n, 4)))
+        v *= rng.uniform(0.5, 1.5, size=n)[:, None]
+        q.put(0, v)
+        del v
     elif recipe == "drift":
-        theta = rng.uniform(0.0, 0.05, size=shp)
-        u = rng.standard_normal(shp + (3,))
-        u /= np.sqrt(np.sum(u * u, axis=-1, keepdims=True))
-        half = 0.5 * theta
-        q = np.empty(shp + (4,), dtype=np.float64)
-        q[..., 0] = np.cos(half)
-        q[..., 1:] = np.sin(half)[..., None] * u
-        del theta, u, half
+        theta = rng.uniform(0.0, 0.05, size=n)
+        for lo in range(0, n, _CHUNK):
+            hi = min(n, lo + _CHUNK)
+            u = _normalise(rng.standard_normal((hi - lo, 3)))
+            half = 0.5 * theta[lo:hi]
+            v = np.empty((hi - lo, 4))
+            v[:, 0] = np.cos(half)
+            v[:, 1:] = np.sin(half)[:, None] * u
+            q.put(lo, v)
+        del theta
     else:
         raise ValueError(f"unknown recipe {recipe!r}")
-    init = _unit4(rng, (b, h, j))
-    d_cum = rng.standard_normal(shp + (4,))
+    init = _Sink(b * h * j, dtype, want_f64)
+    init.put(0, _normalise(rng.standard_normal((b * h * j, 4))))
+    d = _Sink(n, dtype, want_f64)
+    for lo in range(0, n, _CHUNK):
+        d.put(lo, rng.standard_normal((min(n, lo + _CHUNK) - lo, 4)))
 
-    q_st, q64 = _round_to_storage(q, dtype)
-    del q
-    init_st, init64 = _round_to_storage(init, dtype)
-    d_st, d64 = _round_to_storage(d_cum, dtype)
-    del d_cum
-    if not want_f64:
-        q64 = init64 = d64 = None
-    return ScanInputs(b, s, h, j, dtype, q_st, init_st, d_st, q64, init64, d64)
+    big, small = (b, s, h, j, 4), (b, h, j, 4)
+    f64 = (lambda x, shp: x.f64.reshape(shp) if x.f64 is not None else None)
+    return ScanInputs(b, s, h, j, dtype, q.st.reshape(big), init.st.reshape(small), d.st.reshape(big),
+                      f64(q, big), f64(init, small), f64(d, big))
 
 
 def make_config(name: str, seed: int = 0, want_f64: bool = True) -> ScanInputs:

@@ -1,0 +1,179 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/quat_cumprod.h declares, sizes its buffers as documented, and rejects
+bad arguments with the documented codes before any HIP call (so fake device
+pointers are safe here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from quaternion_cumprod_autodiff_amd import capi
+from quaternion_cumprod_autodiff_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "quat_cumprod.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_ALIAS, E_WS, E_HIP, E_OPT = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from quaternion_cumprod_autodiff_amd.build import build
+        build()
+    return capi.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(quat_cumprod_\w+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_uses():
+    assert header_functions() == sorted(capi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (quat_cumprod_\w+)", out))
+    missing = [f for f in header_functions() if f not in exported]
+    assert not missing, missing
+    for f in header_functions():
+        assert getattr(lib, f) is not None
+
+
+def test_no_oracle_symbols_in_library():
+    out = subprocess.run(["nm", "-D", LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "oracle" not in out
+
+
+def test_version_and_strerror(lib):
+    assert lib.quat_cumprod_version() == 100
+    for code in (OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_ALIAS, E_WS, E_HIP, E_OPT):
+        msg = lib.quat_cumprod_strerror(code).decode()
+        assert msg and msg != "unknown error code"
+    assert lib.quat_cumprod_strerror(-99).decode() == "unknown error code"
+    assert lib.quat_cumprod_last_hip_error().decode() == ""
+
+
+def test_buffer_sizes(lib):
+    # ckpt: one internal-precision quaternion per column every 64 steps.
+    for (b, s, h, j) in [(1, 1, 1, 1), (8, 4096, 32, 32), (1, 262144, 2, 8), (2, 65, 3, 5)]:
+        n_ck = -(-s // 64)
+        assert lib.quat_cumprod_ckpt_bytes(b, s, h, j, 0) == b * n_ck * h * j * 32
+        assert lib.quat_cumprod_ckpt_bytes(b, s, h, j, 1) == b * n_ck * h * j * 16
+        ws = lib.quat_cumprod_workspace_bytes(b, s, h, j, 0)
+        assert ws >= lib.quat_cumprod_ckpt_bytes(b, s, h, j, 0) + 256 and ws % 256 == 0
+    for bad in [(0, 1, 1, 1), (1, 0, 1, 1), (1, 1, 0, 1), (1, 1, 1, -3)]:
+        assert lib.quat_cumprod_workspace_bytes(*bad, 0) == 0
+        assert lib.quat_cumprod_ckpt_bytes(*bad, 0) == 0
+    assert lib.quat_cumprod_workspace_bytes(1, 1, 1, 1, 7) == 0
+    # sizes beyond the library's limits are rejected, not wrapped
+    assert lib.quat_cumprod_workspace_bytes(1 << 20, 1 << 20, 1 << 10, 1 << 10, 0) == 0
+
+
+# Fake, well-aligned, non-overlapping device addresses (never dereferenced).
+def P(n):
+    return ctypes.c_void_p(0x10_0000_0000 * n)
+
+
+SHAPE = (2, 100, 3, 4)
+
+
+def fwd(lib, q=1, init=2, cum=3, ckpt=None, ckb=0, shape=SHAPE, dt=0, ws=5, wsb=None, opts=None):
+    ptr = lambda v: None if v is None else (v if isinstance(v, ctypes.c_void_p) else P(v))
+    if wsb is None:
+        wsb = lib.quat_cumprod_workspace_bytes(*shape, dt) if dt in (0, 1) else 1 << 20
+    return lib.quat_cumprod_fwd_ex(ptr(q), ptr(init), ptr(cum), ptr(ckpt), ckb, *shape, dt, ptr(ws), wsb,
+                                   None, opts)
+
+
+def bwd(lib, q=1, init=2, dcum=3, ckpt=None, ckb=0, dq=6, di=7, shape=SHAPE, dt=0, ws=5, wsb=None, opts=None):
+    ptr = lambda v: None if v is None else (v if isinstance(v, ctypes.c_void_p) else P(v))
+    if wsb is None:
+        wsb = lib.quat_cumprod_workspace_bytes(*shape, dt) if dt in (0, 1) else 1 << 20
+    return lib.quat_cumprod_bwd_ex(ptr(q), ptr(init), ptr(dcum), ptr(ckpt), ckb, ptr(dq), ptr(di), *shape, dt,
+                                   ptr(ws), wsb, None, opts)
+
+
+def test_null_pointers(lib):
+    assert fwd(lib, q=None) == E_NULL
+    assert fwd(lib, init=None) == E_NULL
+    assert fwd(lib, cum=None) == E_NULL
+    assert bwd(lib, q=None) == E_NULL
+    assert bwd(lib, init=None) == E_NULL
+    assert bwd(lib, dcum=None) == E_NULL
+    assert fwd(lib, ws=None) == E_WS
+    assert bwd(lib, ws=None) == E_WS
+
+
+def test_bwd_without_outputs_is_a_noop(lib):
+    # Both gradients unwanted (untracked inputs): returns before any HIP call.
+    assert bwd(lib, dq=None, di=None) == OK
+    assert bwd(lib, dq=None, di=None, ws=None) == OK
+
+
+def test_shapes_and_dtype(lib):
+    for shape in [(0, 100, 3, 4), (2, 0, 3, 4), (2, 100, 0, 4), (2, 100, 3, -1)]:
+        assert fwd(lib, shape=shape, wsb=1 << 30) == E_SHAPE
+        assert bwd(lib, shape=shape, wsb=1 << 30) == E_SHAPE
+    assert fwd(lib, dt=2) == E_DTYPE
+    assert bwd(lib, dt=-1) == E_DTYPE
+
+
+def test_alignment(lib):
+    odd = ctypes.c_void_p(0x10_0000_0000 * 9 + 8)   # 8-byte aligned only
+    assert fwd(lib, q=odd) == E_ALIGN
+    assert fwd(lib, cum=odd) == E_ALIGN
+    assert bwd(lib, dq=odd) == E_ALIGN
+    assert bwd(lib, di=odd) == E_ALIGN
+    # bfloat16 tensors need only 8-byte alignment; the workspace needs 16.
+    wsb16 = lib.quat_cumprod_workspace_bytes(*SHAPE, 1)
+    assert fwd(lib, q=odd, dt=1, wsb=wsb16, ws=ctypes.c_void_p(0x10_0000_0000 * 10 + 8)) == E_ALIGN
+    assert fwd(lib, ckpt=odd, ckb=1 << 20) == E_ALIGN
+
+
+def test_workspace_and_ckpt_sizes(lib):
+    need = lib.quat_cumprod_workspace_bytes(*SHAPE, 0)
+    assert fwd(lib, wsb=need - 1) == E_WS
+    assert bwd(lib, wsb=need - 256) == E_WS
+    ck = lib.quat_cumprod_ckpt_bytes(*SHAPE, 0)
+    assert fwd(lib, ckpt=8, ckb=ck - 1) == E_WS
+    assert bwd(lib, ckpt=8, ckb=ck - 1) == E_WS
+
+
+def test_aliasing(lib):
+    assert fwd(lib, cum=1) == E_ALIAS             # cum is q
+    assert fwd(lib, ckpt=2, ckb=1 << 30) == E_ALIAS   # ckpt over init
+    assert fwd(lib, ws=3) == E_ALIAS              # workspace over cum
+    inside_q = ctypes.c_void_p(0x10_0000_0000 + 4096)
+    assert fwd(lib, cum=inside_q) == E_ALIAS      # partial overlap
+    assert bwd(lib, dq=3) == E_ALIAS              # d_q over d_cum
+    assert bwd(lib, di=6) == E_ALIAS              # d_init over d_q
+    assert bwd(lib, dq=8, ckpt=8, ckb=1 << 30) == E_ALIAS   # d_q over ckpt
+
+
+def test_options(lib):
+    o = capi.QcOptions()
+    o.path = 3
+    assert fwd(lib, opts=ctypes.byref(o)) == E_OPT
+    o.path = 0
+    o.reserved[2] = 1
+    assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
+
+
+def test_workspace_helpers_validate(lib):
+    assert lib.quat_cumprod_workspace_init(None, 1024, None) == E_NULL
+    assert lib.quat_cumprod_workspace_init(ctypes.c_void_p(0x1008), 1024, None) == E_ALIGN
+    assert lib.quat_cumprod_workspace_init(P(1), 16, None) == E_WS
+    out = ctypes.c_int32(0)
+    assert lib.quat_cumprod_workspace_status(None, 1024, None, 0, ctypes.byref(out)) == E_NULL
+    assert lib.quat_cumprod_workspace_status(P(1), 1024, None, 0, None) == E_NULL
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        capi.load(str(tmp_path / "missing.so"))
