@@ -47,10 +47,11 @@
  * nothing was enqueued (except QC_ERR_HIP, which means a launch failed).
  *
  * Workspace: a device buffer of at least quat_cumprod_workspace_bytes(...)
- * bytes.  It must be zeroed once after allocation (quat_cumprod_workspace_init
- * does this on a stream); every call leaves it zeroed again for the next
- * call.  Calls sharing one workspace must be ordered (same stream or
- * synchronised); concurrent calls need separate workspaces.
+ * bytes, holding cross-block carries, ready flags and (for a backward without
+ * saved boundary state) re-derived boundary products.  It needs no
+ * initialisation: every call first clears, with a small kernel on `stream`,
+ * the part it uses.  Calls sharing one workspace must be ordered (same stream
+ * or synchronised); concurrent calls need separate workspaces.
  */
 #ifndef QUAT_CUMPROD_H
 #define QUAT_CUMPROD_H
@@ -105,8 +106,9 @@ size_t quat_cumprod_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t j, 
  * invalid arguments. */
 size_t quat_cumprod_ckpt_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype);
 
-/* Zero a freshly allocated workspace on `stream` (a fill kernel, so it may be
- * captured in a HIP graph).  Needed once per allocation. */
+/* Zero a workspace on `stream` with a fill kernel (so it may be captured in a
+ * HIP graph).  Optional: calls clear what they use; this only gives the status
+ * word a defined value before the first call. */
 int quat_cumprod_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Forward scan (the page's Mamba3QuatScanBackendExt::quat_cumprod).
@@ -147,11 +149,11 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum,
                         void* workspace, size_t workspace_bytes, void* stream,
                         const qc_options* opts);
 
-/* Synchronise `stream`, then read the workspace's device-side status word:
- * 0 = every cross-block wait completed; 1 = a wait hit its spin limit; 2 = a
- * call ran on a workspace that had not been zeroed.  Non-zero means the
- * results of some call since the last clear are invalid (and, for 2, the
- * workspace must be re-initialised).  clear != 0 resets it to 0. */
+/* Synchronise `stream`, then read the workspace's device-side status word,
+ * which describes the most recent call on that workspace: 0 = every
+ * cross-block wait completed; 1 = a wait hit its spin limit; 2 = a block drew
+ * a ticket beyond its grid.  Non-zero means that call's results are invalid.
+ * clear != 0 resets the word to 0. */
 int quat_cumprod_workspace_status(void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t clear, int32_t* status_out);
 

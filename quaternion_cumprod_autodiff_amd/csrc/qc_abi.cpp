@@ -129,16 +129,28 @@ qc::KernelArgs base_args(const Plan& p, void* ws) {
     return a;
 }
 
+// Clear the ticket and the flags a launch of `n_tiles` tiles per chain uses
+// (and, at the start of an API call, the status word).
+int clear_state(const Plan& p, void* ws, int64_t n_tiles, bool call_start, hipStream_t st) {
+    const qc::KernelArgs a = base_args(p, ws);
+    const hipError_t e = qc::launch_clear_state(a.hdr, a.flags, size_t(p.n_chains * n_tiles), call_start, st);
+    return e == hipSuccess ? QC_OK : hip_fail(e);
+}
+
 int launch_forward(const Plan& p, const void* q, const void* init, void* cum, void* ckpt, void* ws,
-                   hipStream_t st, bool column) {
+                   hipStream_t st, bool column, bool call_start) {
     qc::KernelArgs a = base_args(p, ws);
     a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt;
     hipError_t e;
     if (column) {
+        int rc = clear_state(p, ws, 0, call_start, st);
+        if (rc != QC_OK) return rc;
         a.n_tiles = 1;
         a.n_blocks = uint32_t((p.n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock);
         e = qc::launch_fwd_column(p.dtype, a, st);
     } else {
+        int rc = clear_state(p, ws, p.fwd_tiles, call_start, st);
+        if (rc != QC_OK) return rc;
         a.n_tiles = p.fwd_tiles;
         a.n_blocks = uint32_t(p.n_chains * p.fwd_tiles);
         e = qc::launch_fwd_chunked(p.dtype, p.wc, a, st);
@@ -190,7 +202,7 @@ int quat_cumprod_fwd_ex(const void* q, const void* init, void* cum, void* ckpt, 
     if (any_alias(rs, out, 5)) return QC_ERR_ALIAS;
 
     const bool column = path == QC_PATH_COLUMN || (path == QC_PATH_AUTO && p.n_cols >= kColumnPathMinColumns);
-    return launch_forward(p, q, init, cum, ckpt, workspace, static_cast<hipStream_t>(stream), column);
+    return launch_forward(p, q, init, cum, ckpt, workspace, static_cast<hipStream_t>(stream), column, true);
 }
 
 int quat_cumprod_fwd(const void* q, const void* init, void* cum, void* ckpt, size_t ckpt_bytes,
@@ -229,6 +241,8 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
     a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init;
     hipError_t e;
     if (path == QC_PATH_COLUMN) {
+        rc = clear_state(p, workspace, 0, true, st);
+        if (rc != QC_OK) return rc;
         a.n_tiles = 1;
         a.n_blocks = uint32_t((p.n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock);
         e = qc::launch_bwd_column(p.dtype, a, st);
@@ -238,9 +252,11 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
     if (!ck) {
         // Leaves-only backward: re-derive the boundary prefix products from q.
         ck = static_cast<char*>(workspace) + p.off_ckpt;
-        rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false);
+        rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false, true);
         if (rc != QC_OK) return rc;
     }
+    rc = clear_state(p, workspace, p.bwd_tiles, ckpt != nullptr, st);
+    if (rc != QC_OK) return rc;
     a.ckpt = ck;
     a.n_tiles = p.bwd_tiles;
     a.n_blocks = uint32_t(p.n_chains * p.bwd_tiles);

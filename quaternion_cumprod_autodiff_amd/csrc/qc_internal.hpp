@@ -15,11 +15,11 @@ constexpr int kCkptStride = 64;
 // Bounded waits: a cross-block wait gives up after this many polls (each poll
 // is one coherent load plus a short sleep, about a microsecond, so well under
 // a second in all) and raises the workspace status word instead of spinning
-// forever.  Status 1 = a wait timed out, 2 = the workspace was not zeroed.
+// forever.  Status 1 = a wait timed out, 2 = a ticket beyond the grid.
 constexpr uint32_t kSpinLimit = 1u << 16;
 
 // Workspace header words.
-enum : int { kHdrTicket = 0, kHdrDone = 1, kHdrStatus = 2, kHdrWords = 64 };
+enum : int { kHdrTicket = 0, kHdrStatus = 2, kHdrWords = 64 };
 
 // Tile geometry of the chunked path, by column-group width WC (a power of two
 // <= 64).  A wave holds R = 64/WC time slices of WC adjacent columns; a block
@@ -70,6 +70,7 @@ hipError_t launch_bwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st);
+hipError_t launch_clear_state(uint32_t* hdr, uint32_t* flags, size_t n_flags, bool clear_status, hipStream_t st);
 
 constexpr int kColumnBlock = 256;   // threads per block on the column path
 

@@ -32,8 +32,10 @@
 // combine is fixed, so results are bitwise reproducible run to run.  Block
 // ids come from an atomic ticket, so a block only waits on blocks that
 // started before it; every wait is bounded (kSpinLimit) and raises a status
-// word instead of hanging.  The last block to finish resets the flags and the
-// ticket, leaving the workspace zeroed for the next call.
+// word instead of hanging.  Before every scan kernel a small kernel clears
+// the ticket and that launch's flags: the flag and carry areas of different
+// problem shapes overlap in the workspace, so nothing is assumed about what
+// earlier calls left there.
 //
 // Arithmetic: float64 for float32 storage, float32 for bfloat16 storage.
 #include "qc_internal.hpp"
@@ -229,28 +231,6 @@ __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t p
     return acc;
 }
 
-// Count finished blocks; the last one resets flags and counters (status kept).
-__device__ __forceinline__ void finish_block(const KernelArgs& a, uint32_t* s_last) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t done = __hip_atomic_fetch_add(&a.hdr[kHdrDone], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        *s_last = (done + 1u == a.n_blocks) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (*s_last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const int64_t n_flags = a.n_chains * a.n_tiles;
-        for (int64_t f = threadIdx.x; f < n_flags; f += blockDim.x)
-            __hip_atomic_store(a.flags + f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (threadIdx.x == 0) {
-            __hip_atomic_store(&a.hdr[kHdrTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.hdr[kHdrDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-}
-
 // Tile coordinates shared by the chunked kernels.
 struct TileCoord {
     int64_t chain, pos, bi, m, t0, base;
@@ -307,13 +287,13 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     constexpr int R = 64 / WC;
     __shared__ Q4<CT> s_wagg[NW][WC];
     __shared__ Q4<CT> s_carry[WC];
-    __shared__ uint32_t s_id, s_last;
+    __shared__ uint32_t s_id;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / WC, c = lane % WC;
     if (tid == 0) s_id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (s_id >= a.n_blocks) {   // workspace was not zeroed: refuse to index with this ticket
+    if (s_id >= a.n_blocks) {   // ticket not cleared: refuse to index with it
         if (tid == 0) __hip_atomic_store(&a.hdr[kHdrStatus], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
@@ -366,7 +346,6 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
             }
         }
     }
-    finish_block(a, &s_last);
 }
 
 // ----------------------------------------------------------- backward, chunked
@@ -389,18 +368,17 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
     __shared__ Q4<CT> s_wagg[NW][WC];
     __shared__ Q4<CT> s_wsum[NW][WC];
     __shared__ Q4<CT> s_after[WC];
-    __shared__ uint32_t s_id, s_last;
+    __shared__ uint32_t s_id;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / WC, c = lane % WC;
     if (tid == 0) s_id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (s_id >= a.n_blocks) {   // workspace was not zeroed: refuse to index with this ticket
+    if (s_id >= a.n_blocks) {   // ticket not cleared: refuse to index with it
         if (tid == 0) __hip_atomic_store(&a.hdr[kHdrStatus], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
     const TileCoord tc = tile_coord<WC, L, NW>(a, s_id, true, wave * R + r, c);
-    constexpr int T = R * NW * L;
 
     Raw qv[L], dv[L];
     if (tc.full) {
@@ -483,8 +461,6 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
             Lp = Lt;
         }
     }
-    (void)T;
-    finish_block(a, &s_last);
 }
 
 // ------------------------------------------------------------- column path
@@ -580,6 +556,17 @@ __global__ void zero_words_kernel(uint32_t* p, size_t n) {
         p[i] = 0u;
 }
 
+// Runs before each scan kernel: ticket := 0 and flags[0, n) := 0; the first
+// kernel of an API call also clears the status word.
+__global__ void clear_launch_state_kernel(uint32_t* hdr, uint32_t* flags, size_t n, uint32_t clear_status) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        hdr[kHdrTicket] = 0u;
+        if (clear_status) hdr[kHdrStatus] = 0u;
+    }
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
+        flags[i] = 0u;
+}
+
 // ------------------------------------------------------------------ launchers
 
 template <class IO, int WC>
@@ -652,6 +639,20 @@ hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st) {
     const void* fn = dtype == 0 ? reinterpret_cast<const void*>(&bwd_column_kernel<IoF32, 8>)
                                 : reinterpret_cast<const void*>(&bwd_column_kernel<IoBF16, 8>);
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(kColumnBlock), params, 0, st);
+}
+
+hipError_t launch_clear_state(uint32_t* hdr, uint32_t* flags, size_t n_flags, bool clear_status,
+                              hipStream_t st) {
+    size_t blocks = (n_flags + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 1024) blocks = 1024;
+    uint32_t* h = hdr;
+    uint32_t* f = flags;
+    size_t n = n_flags;
+    uint32_t cs = clear_status ? 1u : 0u;
+    void* params[] = {&h, &f, &n, &cs};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&clear_launch_state_kernel), dim3(unsigned(blocks)),
+                           dim3(256), params, 0, st);
 }
 
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st) {

@@ -212,3 +212,13 @@ def test_segment_chaining_on_device():
     dq_h, di_h = capi.quat_cumprod_bwd(q[:, :s1].contiguous(), init, d_head)
     np.testing.assert_allclose(to_f64(torch.cat([dq_h, dq_t], 1)), to_f64(dq), rtol=0, atol=1e-4)
     np.testing.assert_allclose(to_f64(di_h), to_f64(di), rtol=0, atol=1e-4)
+
+
+def test_workspace_reuse_small_then_large_shapes():
+    """Regression: the flag area of one shape overlaps the carry area of
+    another; every call must clear its own flags before use."""
+    seq = [make_config("medium"), make_config("tiny"), make_config("medium"),
+           make_inputs(1, 3000, 2, 8, "unit", "f32", seed=4), make_config("medium")]
+    for inp in seq:
+        print(f"[reuse b={inp.b} s={inp.s} h={inp.h} j={inp.j}]", flush=True)
+        compare(inp, path="chunked", use_ckpt=False)
