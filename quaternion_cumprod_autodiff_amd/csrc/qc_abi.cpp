@@ -28,25 +28,48 @@ constexpr size_t kAlignWs = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Chunked-path geometry of one kernel (forward or backward).
+struct Tiling {
+    int wc = 0;               // columns per group
+    int64_t n_cg = 0;         // groups per batch entry
+    int64_t n_chains = 0;     // b * n_cg
+    int64_t n_tiles = 0;      // tiles per chain
+};
+
 struct Plan {
     int64_t b = 0, s = 0, M = 0, N = 0;
     int dtype = 0;
     size_t io_bytes = 0;      // bytes per stored quaternion
     size_t ct_bytes = 0;      // bytes per internal quaternion
-    int wc = 0;
-    int64_t n_cg = 0, n_chains = 0;
-    int64_t fwd_tiles = 0, bwd_tiles = 0;   // per chain
+    Tiling fwd, bwd;
     int64_t n_ck = 0;
     size_t ckpt_bytes = 0;
-    size_t off_flags = 0, off_desc = 0, off_ckpt = 0, ws_bytes = 0;
+    size_t off_desc = 0, off_ckpt = 0, ws_bytes = 0;
     int64_t n_cols = 0;
 };
 
-int column_group_width(int64_t M) {
-    if (M >= 64) return 64;
+// Widest column group each kernel uses.  The forward holds few registers per
+// step and runs best with wide (64-column) groups; the backward holds about
+// 180 registers per lane, so narrower groups give smaller blocks, several of
+// which share a compute unit and overlap their load, compute and wait phases.
+constexpr int kFwdMaxWc = 64;
+constexpr int kBwdMaxWc = 32;
+
+int column_group_width(int64_t M, int cap) {
+    if (M >= cap) return cap;
     int w = 1;
     while (w < M) w <<= 1;
     return w;
+}
+
+Tiling make_tiling(int64_t b, int64_t s, int64_t M, int cap, bool backward) {
+    Tiling t;
+    t.wc = column_group_width(M, cap);
+    t.n_cg = (M + t.wc - 1) / t.wc;
+    t.n_chains = b * t.n_cg;
+    const int64_t steps = backward ? qc::bwd_tile_steps(t.wc) : qc::fwd_tile_steps(t.wc);
+    t.n_tiles = (s + steps - 1) / steps;
+    return t;
 }
 
 bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a <= limit / b; }
@@ -62,22 +85,20 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     p->io_bytes = dtype == QC_DTYPE_F32 ? 16 : 8;
     p->ct_bytes = dtype == QC_DTYPE_F32 ? 32 : 16;
     p->n_cols = b * M;
-    p->wc = column_group_width(M);
-    p->n_cg = (M + p->wc - 1) / p->wc;
-    p->n_chains = b * p->n_cg;
-    const int64_t tf = qc::fwd_tile_steps(p->wc), tb = qc::bwd_tile_steps(p->wc);
-    p->fwd_tiles = (s + tf - 1) / tf;
-    p->bwd_tiles = (s + tb - 1) / tb;
-    // Grid (one block per tile) and the 32-bit ticket bound the tile count.
-    const int64_t max_blocks = int64_t(1) << 22;
-    if (!mul_ok(p->n_chains, p->bwd_tiles, max_blocks)) return QC_ERR_SHAPE;
+    p->fwd = make_tiling(b, s, M, kFwdMaxWc, false);
+    p->bwd = make_tiling(b, s, M, kBwdMaxWc, true);
+    // One block per tile; the 32-bit ticket and the grid bound the count.
+    const int64_t max_blocks = int64_t(1) << 24;
+    if (!mul_ok(p->fwd.n_chains, p->fwd.n_tiles, max_blocks)) return QC_ERR_SHAPE;
+    if (!mul_ok(p->bwd.n_chains, p->bwd.n_tiles, max_blocks)) return QC_ERR_SHAPE;
     if ((p->n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock > max_blocks) return QC_ERR_SHAPE;
     p->n_ck = (s + kCkptStride - 1) / kCkptStride;
     p->ckpt_bytes = size_t(b) * size_t(p->n_ck) * size_t(M) * p->ct_bytes;
-    const int64_t nodes = p->n_chains * (p->fwd_tiles > p->bwd_tiles ? p->fwd_tiles : p->bwd_tiles);
-    p->off_flags = size_t(qc::kHdrWords) * 4;
-    p->off_desc = round_up(p->off_flags + size_t(nodes) * 4, kAlignWs);
-    p->off_ckpt = round_up(p->off_desc + size_t(nodes) * size_t(p->wc) * p->ct_bytes, kAlignWs);
+    const size_t slots_fwd = size_t(p->fwd.n_chains * p->fwd.n_tiles) * size_t(p->fwd.wc);
+    const size_t slots_bwd = size_t(p->bwd.n_chains * p->bwd.n_tiles) * size_t(p->bwd.wc);
+    const size_t slots = slots_fwd > slots_bwd ? slots_fwd : slots_bwd;
+    p->off_desc = round_up(size_t(qc::kHdrWords) * 4, kAlignWs);
+    p->off_ckpt = round_up(p->off_desc + slots * p->ct_bytes, kAlignWs);
     p->ws_bytes = round_up(p->off_ckpt + p->ckpt_bytes, kAlignWs);
     return QC_OK;
 }
@@ -118,43 +139,41 @@ int check_options(const qc_options* o, int* path) {
 // (it reads q and d_cum once instead of twice).
 constexpr int64_t kColumnPathMinColumns = int64_t(1) << 18;
 
-qc::KernelArgs base_args(const Plan& p, void* ws) {
+qc::KernelArgs base_args(const Plan& p, void* ws, const Tiling& tl) {
     qc::KernelArgs a{};
     a.b = p.b; a.s = p.s; a.M = p.M; a.n_ck = p.n_ck;
-    a.n_cg = p.n_cg; a.n_chains = p.n_chains;
+    a.n_cg = tl.n_cg; a.n_chains = tl.n_chains; a.n_tiles = tl.n_tiles;
+    a.n_blocks = uint32_t(tl.n_chains * tl.n_tiles);
     a.hdr = reinterpret_cast<uint32_t*>(ws);
-    a.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.off_flags);
     a.desc = static_cast<char*>(ws) + p.off_desc;
     a.spin_limit = qc::kSpinLimit;
     return a;
 }
 
-// Clear the ticket and the flags a launch of `n_tiles` tiles per chain uses
-// (and, at the start of an API call, the status word).
-int clear_state(const Plan& p, void* ws, int64_t n_tiles, bool call_start, hipStream_t st) {
-    const qc::KernelArgs a = base_args(p, ws);
-    const hipError_t e = qc::launch_clear_state(a.hdr, a.flags, size_t(p.n_chains * n_tiles), call_start, st);
+// Reset the ticket and mark the carry slots of a launch with tiling `tl` as
+// unpublished (and, at the start of an API call, clear the status word).
+int clear_state(const Plan& p, void* ws, const Tiling* tl, bool call_start, hipStream_t st) {
+    const size_t bytes = tl ? size_t(tl->n_chains * tl->n_tiles) * size_t(tl->wc) * p.ct_bytes : 0;
+    const hipError_t e = qc::launch_clear_state(reinterpret_cast<uint32_t*>(ws), static_cast<char*>(ws) + p.off_desc,
+                                                bytes, call_start, st);
     return e == hipSuccess ? QC_OK : hip_fail(e);
+}
+
+qc::KernelArgs column_args(const Plan& p, void* ws) {
+    qc::KernelArgs a = base_args(p, ws, p.fwd);
+    a.n_tiles = 1;
+    a.n_blocks = uint32_t((p.n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock);
+    return a;
 }
 
 int launch_forward(const Plan& p, const void* q, const void* init, void* cum, void* ckpt, void* ws,
                    hipStream_t st, bool column, bool call_start) {
-    qc::KernelArgs a = base_args(p, ws);
+    int rc = clear_state(p, ws, column ? nullptr : &p.fwd, call_start, st);
+    if (rc != QC_OK) return rc;
+    qc::KernelArgs a = column ? column_args(p, ws) : base_args(p, ws, p.fwd);
     a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt;
-    hipError_t e;
-    if (column) {
-        int rc = clear_state(p, ws, 0, call_start, st);
-        if (rc != QC_OK) return rc;
-        a.n_tiles = 1;
-        a.n_blocks = uint32_t((p.n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock);
-        e = qc::launch_fwd_column(p.dtype, a, st);
-    } else {
-        int rc = clear_state(p, ws, p.fwd_tiles, call_start, st);
-        if (rc != QC_OK) return rc;
-        a.n_tiles = p.fwd_tiles;
-        a.n_blocks = uint32_t(p.n_chains * p.fwd_tiles);
-        e = qc::launch_fwd_chunked(p.dtype, p.wc, a, st);
-    }
+    const hipError_t e = column ? qc::launch_fwd_column(p.dtype, a, st)
+                                : qc::launch_fwd_chunked(p.dtype, p.fwd.wc, a, st);
     return e == hipSuccess ? QC_OK : hip_fail(e);
 }
 
@@ -237,15 +256,12 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
     if (any_alias(rs, out, 7)) return QC_ERR_ALIAS;
 
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    qc::KernelArgs a = base_args(p, workspace);
-    a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init;
-    hipError_t e;
     if (path == QC_PATH_COLUMN) {
-        rc = clear_state(p, workspace, 0, true, st);
+        rc = clear_state(p, workspace, nullptr, true, st);
         if (rc != QC_OK) return rc;
-        a.n_tiles = 1;
-        a.n_blocks = uint32_t((p.n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock);
-        e = qc::launch_bwd_column(p.dtype, a, st);
+        qc::KernelArgs a = column_args(p, workspace);
+        a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init;
+        const hipError_t e = qc::launch_bwd_column(p.dtype, a, st);
         return e == hipSuccess ? QC_OK : hip_fail(e);
     }
     void* ck = const_cast<void*>(ckpt);
@@ -255,12 +271,11 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
         rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false, true);
         if (rc != QC_OK) return rc;
     }
-    rc = clear_state(p, workspace, p.bwd_tiles, ckpt != nullptr, st);
+    rc = clear_state(p, workspace, &p.bwd, ckpt != nullptr, st);
     if (rc != QC_OK) return rc;
-    a.ckpt = ck;
-    a.n_tiles = p.bwd_tiles;
-    a.n_blocks = uint32_t(p.n_chains * p.bwd_tiles);
-    e = qc::launch_bwd_chunked(p.dtype, p.wc, a, st);
+    qc::KernelArgs a = base_args(p, workspace, p.bwd);
+    a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init; a.ckpt = ck;
+    const hipError_t e = qc::launch_bwd_chunked(p.dtype, p.bwd.wc, a, st);
     return e == hipSuccess ? QC_OK : hip_fail(e);
 }
 

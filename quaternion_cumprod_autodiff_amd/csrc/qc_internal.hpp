@@ -13,9 +13,9 @@ namespace qc {
 constexpr int kCkptStride = 64;
 
 // Bounded waits: a cross-block wait gives up after this many polls (each poll
-// is one coherent load plus a short sleep, about a microsecond, so well under
-// a second in all) and raises the workspace status word instead of spinning
-// forever.  Status 1 = a wait timed out, 2 = a ticket beyond the grid.
+// is a few coherent loads plus a short sleep, about a microsecond, so well
+// under a second in all) and raises the workspace status word instead of
+// spinning forever.  Status 1 = a wait timed out, 2 = a ticket beyond the grid.
 constexpr uint32_t kSpinLimit = 1u << 16;
 
 // Workspace header words.
@@ -54,8 +54,7 @@ struct KernelArgs {
     void* d_init;         // [b][M]              (backward, may be null)
     void* ckpt;           // [b][n_ck][M] quaternions in the compute type (may be null)
     uint32_t* hdr;        // workspace header
-    uint32_t* flags;      // one ready flag per tile
-    void* desc;           // per-tile carry values, WC quaternions each
+    void* desc;           // per-tile carry slots, WC quaternions each (kEmpty until published)
     int64_t b, s, M;
     int64_t n_ck;         // ceil(s / kCkptStride)
     int64_t n_cg;         // column groups per batch entry
@@ -70,7 +69,7 @@ hipError_t launch_bwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st);
-hipError_t launch_clear_state(uint32_t* hdr, uint32_t* flags, size_t n_flags, bool clear_status, hipStream_t st);
+hipError_t launch_clear_state(uint32_t* hdr, void* slots, size_t slot_bytes, bool clear_status, hipStream_t st);
 
 constexpr int kColumnBlock = 256;   // threads per block on the column path
 

@@ -29,13 +29,18 @@
 // ordered combination of the nodes on the Fenwick query path from i-1 down.
 // Waits therefore form chains of depth log2(tiles), every tile reads and
 // combines O(log tiles) values, and the association of every floating-point
-// combine is fixed, so results are bitwise reproducible run to run.  Block
-// ids come from an atomic ticket, so a block only waits on blocks that
-// started before it; every wait is bounded (kSpinLimit) and raises a status
-// word instead of hanging.  Before every scan kernel a small kernel clears
-// the ticket and that launch's flags: the flag and carry areas of different
-// problem shapes overlap in the workspace, so nothing is assumed about what
-// earlier calls left there.
+// combine is fixed, so results are bitwise reproducible run to run.
+//
+// Publication protocol.  Before each scan kernel a small kernel fills the
+// launch's carry slots with kEmpty, an all-ones NaN pattern that no kernel
+// ever stores.  A node's words are then written with agent-scope atomic
+// stores and read with agent-scope atomic loads; each word is single-copy
+// atomic, so a reader only waits until none of its words is kEmpty.  No
+// separate ready flag, hence no release/acquire fence (on this chip an
+// agent-scope fence writes back or invalidates the whole L2, which costs
+// more than the scan itself).  Block ids come from an atomic ticket, so a
+// block only waits on blocks that started before it; every wait is bounded
+// (kSpinLimit) and raises a status word instead of hanging.
 //
 // Arithmetic: float64 for float32 storage, float32 for bfloat16 storage.
 #include "qc_internal.hpp"
@@ -127,15 +132,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return u >> 16;
 }
 
-// float32 storage: one float4 (16 B) per quaternion; float64 arithmetic.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// The [b,s,h,j,4] tensors are streamed exactly once per kernel, so their
+// loads and stores are non-temporal (they would only evict useful lines).
+// float32 storage: one 16-byte vector per quaternion; float64 arithmetic.
 struct IoF32 {
     using CT = double;
-    using Raw = float4;
+    using Raw = f32x4;
     static __device__ __forceinline__ Raw load(const void* base, int64_t idx) {
-        return reinterpret_cast<const float4*>(base)[idx];
+        return reinterpret_cast<const Raw*>(base)[idx];
     }
-    static __device__ __forceinline__ Raw one_raw() { return make_float4(1.f, 0.f, 0.f, 0.f); }
-    static __device__ __forceinline__ Raw zero_raw() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    static __device__ __forceinline__ Raw load_stream(const void* base, int64_t idx) {
+        return __builtin_nontemporal_load(reinterpret_cast<const Raw*>(base) + idx);
+    }
+    static __device__ __forceinline__ Raw one_raw() { return Raw{1.f, 0.f, 0.f, 0.f}; }
+    static __device__ __forceinline__ Raw zero_raw() { return Raw{0.f, 0.f, 0.f, 0.f}; }
     static __device__ __forceinline__ Q4<CT> ct(const Raw& v) {
         return {double(v.x), double(v.y), double(v.z), double(v.w)};
     }
@@ -143,92 +156,191 @@ struct IoF32 {
     // re-converts here instead of keeping float64 copies of every step alive
     // between the two sweeps (twice the registers).
     static __device__ __forceinline__ Q4<CT> ct_fresh(Raw v) {
-        asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+        asm volatile("" : "+v"(v));
         return ct(v);
     }
+    static __device__ __forceinline__ Raw pack(const Q4<CT>& v) {
+        return Raw{float(v.w), float(v.x), float(v.y), float(v.z)};
+    }
     static __device__ __forceinline__ void store(void* base, int64_t idx, const Q4<CT>& v) {
-        reinterpret_cast<float4*>(base)[idx] = make_float4(float(v.w), float(v.x), float(v.y), float(v.z));
+        reinterpret_cast<Raw*>(base)[idx] = pack(v);
+    }
+    static __device__ __forceinline__ void store_stream(void* base, int64_t idx, const Q4<CT>& v) {
+        __builtin_nontemporal_store(pack(v), reinterpret_cast<Raw*>(base) + idx);
     }
 };
 
 // bfloat16 storage: 4 x 16-bit patterns (8 B) per quaternion; float32 arithmetic.
 struct IoBF16 {
     using CT = float;
-    using Raw = uint2;
+    using Raw = u32x2;
     static __device__ __forceinline__ Raw load(const void* base, int64_t idx) {
-        return reinterpret_cast<const uint2*>(base)[idx];
+        return reinterpret_cast<const Raw*>(base)[idx];
     }
-    static __device__ __forceinline__ Raw one_raw() { return make_uint2(0x3f80u, 0u); }
-    static __device__ __forceinline__ Raw zero_raw() { return make_uint2(0u, 0u); }
+    static __device__ __forceinline__ Raw load_stream(const void* base, int64_t idx) {
+        return __builtin_nontemporal_load(reinterpret_cast<const Raw*>(base) + idx);
+    }
+    static __device__ __forceinline__ Raw one_raw() { return Raw{0x3f80u, 0u}; }
+    static __device__ __forceinline__ Raw zero_raw() { return Raw{0u, 0u}; }
     static __device__ __forceinline__ Q4<CT> ct(const Raw& v) {
         return {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
     }
     static __device__ __forceinline__ Q4<CT> ct_fresh(Raw v) {
-        asm volatile("" : "+v"(v.x), "+v"(v.y));
+        asm volatile("" : "+v"(v));
         return ct(v);
     }
+    static __device__ __forceinline__ Raw pack(const Q4<CT>& v) {
+        return Raw{f32_to_bf16_bits(v.w) | (f32_to_bf16_bits(v.x) << 16),
+                   f32_to_bf16_bits(v.y) | (f32_to_bf16_bits(v.z) << 16)};
+    }
     static __device__ __forceinline__ void store(void* base, int64_t idx, const Q4<CT>& v) {
-        const uint32_t lo = f32_to_bf16_bits(v.w) | (f32_to_bf16_bits(v.x) << 16);
-        const uint32_t hi = f32_to_bf16_bits(v.y) | (f32_to_bf16_bits(v.z) << 16);
-        reinterpret_cast<uint2*>(base)[idx] = make_uint2(lo, hi);
+        reinterpret_cast<Raw*>(base)[idx] = pack(v);
+    }
+    static __device__ __forceinline__ void store_stream(void* base, int64_t idx, const Q4<CT>& v) {
+        __builtin_nontemporal_store(pack(v), reinterpret_cast<Raw*>(base) + idx);
     }
 };
 
+// 1/x for the |P|^2 normalisation: hardware reciprocal estimate refined by
+// Newton-Raphson steps r <- r + r (1 - x r) (quadratic convergence), cheaper
+// than a correctly rounded division and accurate to about one ulp.
+__device__ __forceinline__ double recip(double x) {
+    double r = __builtin_amdgcn_rcp(x);
+    double e = __builtin_fma(-x, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    e = __builtin_fma(-x, r, 1.0);
+    return __builtin_fma(r, e, r);
+}
+__device__ __forceinline__ float recip(float x) {
+    float r = __builtin_amdgcn_rcpf(x);
+    const float e = __builtin_fmaf(-x, r, 1.0f);
+    return __builtin_fmaf(r, e, r);
+}
+
 // ------------------------------------------------- cross-block carry helpers
 
-// Wait until a tile's ready flag is set, then make its carry values visible.
-// The wave polls one address uniformly; the wait is bounded.
-__device__ __forceinline__ void wait_ready(const KernelArgs& a, const uint32_t* flag) {
+template <typename T> struct Word;
+template <> struct Word<double> { using U = unsigned long long; };
+template <> struct Word<float> { using U = unsigned int; };
+
+// Store one carry word; a value whose bits happen to equal kEmpty (a NaN)
+// is stored as the canonical quiet NaN instead.
+template <typename T>
+__device__ __forceinline__ void put_word(T* p, T v) {
+    using U = typename Word<T>::U;
+    U bits = __builtin_bit_cast(U, v);
+    if (bits == ~U(0)) bits = __builtin_bit_cast(U, T(__builtin_nan("")));
+    __hip_atomic_store(reinterpret_cast<U*>(p), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publish a node: the lanes with `writer` set store their column's words.
+template <typename T>
+__device__ __forceinline__ void publish(Q4<T>* slot, const Q4<T>& v, bool writer) {
+    if (writer) {
+        T* f = reinterpret_cast<T*>(slot);
+        put_word(f + 0, v.w);
+        put_word(f + 1, v.x);
+        put_word(f + 2, v.y);
+        put_word(f + 3, v.z);
+    }
+}
+
+// One coherent read of a slot; true if all four words are published.
+template <typename T>
+__device__ __forceinline__ bool try_read(const Q4<T>* slot, Q4<T>* out) {
+    using U = typename Word<T>::U;
+    const U* f = reinterpret_cast<const U*>(slot);
+    constexpr U E = ~U(0);
+    const U w0 = __hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const U w1 = __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const U w2 = __hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const U w3 = __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *out = {__builtin_bit_cast(T, w0), __builtin_bit_cast(T, w1), __builtin_bit_cast(T, w2),
+            __builtin_bit_cast(T, w3)};
+    return w0 != E && w1 != E && w2 != E && w3 != E;
+}
+
+// Wait (bounded) until all four words of this lane's slot are published.
+// Polls back off from about 30 ns to about 2 us between attempts, so a slot
+// that many tiles wait on is not hammered with coherent loads.
+template <typename T>
+__device__ __forceinline__ Q4<T> wait_read(const KernelArgs& a, const Q4<T>* slot) {
+    Q4<T> v;
     uint32_t polls = 0;
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-        __builtin_amdgcn_s_sleep(1);
+    while (!try_read(slot, &v)) {
+        if (polls < 8) {
+            __builtin_amdgcn_s_sleep(1);
+        } else if (polls < 64) {
+            __builtin_amdgcn_s_sleep(8);
+        } else {
+            __builtin_amdgcn_s_sleep(64);
+        }
         if (++polls > a.spin_limit) {
             __hip_atomic_store(&a.hdr[kHdrStatus], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return v;
 }
 
-// Store a tile's carry values (lanes with `writer`), then release the flag.
-// Called by the whole wave: the fence covers every lane's stores.
-template <typename T>
-__device__ __forceinline__ void publish(const KernelArgs& a, Q4<T>* slot, uint32_t* flag,
-                                        const Q4<T>& v, bool writer, bool flag_writer) {
-    if (writer) *slot = v;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (flag_writer) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Fenwick look-back for tile `pos` (0-based) of `chain`, run by one wave.
-// `own` is this tile's aggregate.  Combine(later, earlier) is
+// Fenwick look-back for tile `pos` (0-based) of `chain`; called by every
+// thread of the block.  `own` is this tile's aggregate, valid in the wave
+// `own_wave`.  Combine(later, earlier) is
 //   product:  later (x) earlier           (forward carry P)
 //   sum:      later + earlier             (backward carry S, "later" = earlier in time)
-// Returns the exclusive prefix (identity / zero for the first tile).
-template <typename T, int WC, bool kProduct>
-__device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t pos,
-                                   const Q4<T>& own, int c, bool writer, bool flag_writer) {
+// The query path is walked in rounds of NW*R nodes: every lane slot
+// (wave*R + r) makes one coherent read attempt of one node for column c, so
+// nodes that are already published cost one round trip together; then
+// `own_wave` combines the round in the fixed order, waiting itself (nearest
+// node first) only for nodes that were not yet published, and publishes
+// node i as soon as its children are in.  Returns the exclusive prefix
+// (identity / zero for the first tile) to every thread.
+template <typename T, int WC, int NW, bool kProduct>
+__device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const Q4<T>& own,
+                                   bool own_wave, int wave, int r, int c, Q4<T> (*s_nodes)[WC],
+                                   uint8_t (*s_ok)[WC], Q4<T>* s_out) {
+    constexpr int R = 64 / WC;
+    constexpr int PAR = NW * R;
     const int64_t i = pos + 1;
     const int64_t low = i & (-i);
     const int64_t node0 = chain * a.n_tiles;   // node n lives at node0 + n - 1
     Q4<T>* desc = reinterpret_cast<Q4<T>*>(a.desc);
+    const int slot = wave * R + r;
     Q4<T> acc = kProduct ? q_one<T>() : q_zero<T>();
     bool published = (i == a.n_tiles);        // nothing reads the last node
-    int64_t jn = i - 1;
+    int64_t jn = i - 1;                       // next node on the query path (block-uniform)
     for (;;) {
-        if (!published && jn <= i - low) {
-            const Q4<T> node = kProduct ? qmul(own, acc) : qadd(own, acc);
-            publish(a, desc + (node0 + i - 1) * WC + c, a.flags + node0 + i - 1, node, writer, flag_writer);
+        if (own_wave && !published && jn <= i - low) {
+            publish(desc + (node0 + i - 1) * WC + c, kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
             published = true;
         }
         if (jn == 0) break;
-        wait_ready(a, a.flags + node0 + jn - 1);
-        const Q4<T> v = desc[(node0 + jn - 1) * WC + c];
-        acc = kProduct ? qmul(acc, v) : qadd(acc, v);
-        jn -= jn & (-jn);
+        int64_t mine = jn;                    // this slot's node: `slot` steps down the path
+        for (int k = 0; k < slot && mine > 0; ++k) mine -= mine & (-mine);
+        if (mine > 0) {
+            Q4<T> v;
+            const bool ok = try_read(desc + (node0 + mine - 1) * WC + c, &v);
+            s_nodes[slot][c] = v;
+            s_ok[slot][c] = ok ? 1 : 0;
+        }
+        __syncthreads();
+        for (int k = 0; k < PAR && jn > 0; ++k) {
+            if (own_wave) {
+                if (!published && jn <= i - low) {
+                    publish(desc + (node0 + i - 1) * WC + c, kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
+                    published = true;
+                }
+                const Q4<T> v = s_ok[k][c] ? s_nodes[k][c] : wait_read(a, desc + (node0 + jn - 1) * WC + c);
+                acc = kProduct ? qmul(acc, v) : qadd(acc, v);
+            }
+            jn -= jn & (-jn);
+        }
+        __syncthreads();                      // s_nodes is reused by the next round
     }
-    return acc;
+    if (own_wave && r == 0) s_out[c] = acc;
+    __syncthreads();
+    return s_out[c];
 }
 
 // Tile coordinates shared by the chunked kernels.
@@ -286,6 +398,8 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
     __shared__ Q4<CT> s_wagg[NW][WC];
+    __shared__ Q4<CT> s_nodes[NW * R][WC];
+    __shared__ uint8_t s_ok[NW * R][WC];
     __shared__ Q4<CT> s_carry[WC];
     __shared__ uint32_t s_id;
 
@@ -302,11 +416,12 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     Raw qv[L];
     if (tc.full) {
 #pragma unroll
-        for (int i = 0; i < L; ++i) qv[i] = IO::load(a.q, tc.base + int64_t(i) * a.M);
+        for (int i = 0; i < L; ++i) qv[i] = IO::load_stream(a.q, tc.base + int64_t(i) * a.M);
     } else {
 #pragma unroll
         for (int i = 0; i < L; ++i)
-            qv[i] = (tc.col_ok && tc.t0 + i < a.s) ? IO::load(a.q, tc.base + int64_t(i) * a.M) : IO::one_raw();
+            qv[i] = (tc.col_ok && tc.t0 + i < a.s) ? IO::load_stream(a.q, tc.base + int64_t(i) * a.M)
+                                                    : IO::one_raw();
     }
     Raw init_raw = IO::one_raw();
     if (a.out != nullptr && tc.col_ok) init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
@@ -318,12 +433,9 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 
     Q4<CT> tile_agg;
     const Q4<CT> F = tile_scan_product<CT, WC, NW>(A, s_wagg, wave, r, c, &tile_agg);
-    if (wave == NW - 1) {
-        const Q4<CT> E = fenwick_exclusive<CT, WC, true>(a, tc.chain, tc.pos, tile_agg, c, r == 0, lane == 0);
-        if (r == 0) s_carry[c] = E;
-    }
-    __syncthreads();
-    const Q4<CT> Ps = qmul(F, s_carry[c]);   // P_{t0-1}: prefix product before this slice
+    const Q4<CT> Et = fenwick_exclusive<CT, WC, NW, true>(a, tc.chain, tc.pos, tile_agg, wave == NW - 1, wave, r, c,
+                                                           s_nodes, s_ok, s_carry);
+    const Q4<CT> Ps = qmul(F, Et);   // P_{t0-1}: prefix product before this slice
 
     if (a.ckpt != nullptr && tc.col_ok && tc.t0 < a.s && (tc.t0 % kCkptStride) == 0)
         reinterpret_cast<Q4<CT>*>(a.ckpt)[(tc.bi * a.n_ck + tc.t0 / kCkptStride) * a.M + tc.m] = Ps;
@@ -334,14 +446,14 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 cm = qmul(IO::ct_fresh(qv[i]), cm);
-                IO::store(a.out, tc.base + int64_t(i) * a.M, cm);
+                IO::store_stream(a.out, tc.base + int64_t(i) * a.M, cm);
             }
         } else if (tc.col_ok) {
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 if (tc.t0 + i < a.s) {
                     cm = qmul(IO::ct_fresh(qv[i]), cm);
-                    IO::store(a.out, tc.base + int64_t(i) * a.M, cm);
+                    IO::store_stream(a.out, tc.base + int64_t(i) * a.M, cm);
                 }
             }
         }
@@ -350,15 +462,15 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 
 // ----------------------------------------------------------- backward, chunked
 //
-// Per slice (L steps from t0, E = P_{t0-1} from the saved boundary state and
-// the in-tile scan), with local products Lc_t = q_t (x) ... (x) q_{t0}:
-//   P_t = Lc_t (x) E,   conj(P_t) (x) d_t = conj(E) (x) [conj(Lc_t) (x) d_t]
-//   Yh  = sum_{t in slice} conj(Lc_t) (x) d_t            (local frame)
-//   S[t] = conj(E) (x) Sh_t + S_after,   Sh_t = sum_{u>=t in slice} conj(Lc_u) (x) d_u
-//   G[t] = P_t (x) S[t] / |P_t|^2 = Lc_t (x) (Sh_t + Z) / |Lc_t|^2,  Z = E (x) S_after / |E|^2
-//   cum[t-1] = Lc_{t-1} (x) (E (x) init)
-// so the long-range quantities enter once per slice and the per-step
-// arithmetic stays in the well-conditioned local frame.
+// Sweep 1 works in the slice's local frame, so it needs no carry: with
+// Lc_t = q_t (x) ... (x) q_{t0} it forms the slice product Lc_{t0+L-1} and
+// Yh = sum_t conj(Lc_t) (x) d_t.  Once the in-tile scan gives E = P_{t0-1}
+// (saved boundary state times the products of earlier slices), the slice's
+// share of S is Y = conj(E) (x) Yh, and the reverse sums of Y over later
+// slices, tiles and chains give S at the slice start.  Sweep 2 then follows
+// the closed form step by step in the global frame:
+//   P_t = q_t (x) P_{t-1},  G = P_t (x) S[t] / |P_t|^2,  d_q[t] = G (x) conj(cum[t-1]),
+//   S[t+1] = S[t] - conj(P_t) (x) d_t,  cum[t] = q_t (x) cum[t-1].
 
 template <class IO, int WC, int L, int NW>
 __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
@@ -367,6 +479,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
     constexpr int R = 64 / WC;
     __shared__ Q4<CT> s_wagg[NW][WC];
     __shared__ Q4<CT> s_wsum[NW][WC];
+    __shared__ Q4<CT> s_nodes[NW * R][WC];
+    __shared__ uint8_t s_ok[NW * R][WC];
     __shared__ Q4<CT> s_after[WC];
     __shared__ uint32_t s_id;
 
@@ -384,15 +498,15 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
     if (tc.full) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            qv[i] = IO::load(a.q, tc.base + int64_t(i) * a.M);
-            dv[i] = IO::load(a.d_cum, tc.base + int64_t(i) * a.M);
+            qv[i] = IO::load_stream(a.q, tc.base + int64_t(i) * a.M);
+            dv[i] = IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const bool ok = tc.col_ok && tc.t0 + i < a.s;
-            qv[i] = ok ? IO::load(a.q, tc.base + int64_t(i) * a.M) : IO::one_raw();
-            dv[i] = ok ? IO::load(a.d_cum, tc.base + int64_t(i) * a.M) : IO::zero_raw();
+            qv[i] = ok ? IO::load_stream(a.q, tc.base + int64_t(i) * a.M) : IO::one_raw();
+            dv[i] = ok ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M) : IO::zero_raw();
         }
     }
     // Boundary prefix product at the tile start and the initial carry.
@@ -404,7 +518,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
         init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
     }
 
-    // Sweep 1 (local frame): slice product and Yh = sum conj(Lc_t) (x) d_t.
+    // Sweep 1 (local frame).
     Q4<CT> Lc = q_one<CT>();
     Q4<CT> Yh = q_zero<CT>();
 #pragma unroll
@@ -432,33 +546,26 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
     __syncthreads();
     Q4<CT> later_waves = q_zero<CT>();
     for (int w2 = wave + 1; w2 < NW; ++w2) later_waves = qadd(later_waves, s_wsum[w2][c]);
-    if (wave == 0) {
-        const Q4<CT> tile_sum = qadd(shfl_q(sinc, c), later_waves);
-        const Q4<CT> Sa = fenwick_exclusive<CT, WC, false>(a, tc.chain, tc.pos, tile_sum, c, r == 0, lane == 0);
-        if (r == 0) s_after[c] = Sa;
-    }
-    __syncthreads();
-    const Q4<CT> S_after = qadd(qadd(later_in_wave, later_waves), s_after[c]);   // S at t0 + L
+    const Q4<CT> tile_sum = qadd(shfl_q(sinc, c), later_waves);   // valid in wave 0
+    const Q4<CT> Sa = fenwick_exclusive<CT, WC, NW, false>(a, tc.chain, tc.pos, tile_sum, wave == 0, wave, r, c,
+                                                            s_nodes, s_ok, s_after);
+    const Q4<CT> S_after = qadd(qadd(later_in_wave, later_waves), Sa);   // S at t0 + L
+    Q4<CT> S = qadd(Y, S_after);                                                   // S at t0
 
-    if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok)
-        IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Y, S_after));   // S[0]
+    if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok) IO::store(a.d_init, tc.bi * a.M + tc.m, S);   // S[0]
 
     if (a.out != nullptr && tc.col_ok) {
-        const Q4<CT> Z = qscale(qmul(E, S_after), CT(1) / qnorm2(E));
-        const Q4<CT> C = qmul(E, IO::ct(init_raw));   // cum[t0-1]
-        Q4<CT> Lp = q_one<CT>();
-        Q4<CT> run = q_zero<CT>();
+        Q4<CT> P = E;                                // P_{t-1}
+        Q4<CT> cm = qmul(E, IO::ct(init_raw));       // cum[t-1]
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             if (!tc.full && tc.t0 + i >= a.s) break;
-            const Q4<CT> Lt = qmul(IO::ct_fresh(qv[i]), Lp);
-            const Q4<CT> X = qcmul(Lt, IO::ct_fresh(dv[i]));
-            const Q4<CT> Sh = qsub(Yh, run);
-            run = qadd(run, X);
-            const Q4<CT> G = qscale(qmul(Lt, qadd(Sh, Z)), CT(1) / qnorm2(Lt));
-            const Q4<CT> cprev = qmul(Lp, C);
-            IO::store(a.out, tc.base + int64_t(i) * a.M, qmulc(G, cprev));
-            Lp = Lt;
+            const Q4<CT> qq = IO::ct_fresh(qv[i]);
+            P = qmul(qq, P);
+            const Q4<CT> G = qscale(qmul(P, S), recip(qnorm2(P)));
+            IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qmulc(G, cm));
+            S = qsub(S, qcmul(P, IO::ct_fresh(dv[i])));
+            cm = qmul(qq, cm);
         }
     }
 }
@@ -481,7 +588,7 @@ __global__ void __launch_bounds__(kColumnBlock) fwd_column_kernel(KernelArgs a) 
         Raw qv[U];
 #pragma unroll
         for (int i = 0; i < U; ++i)
-            qv[i] = (t0 + i < a.s) ? IO::load(a.q, base + (t0 + i) * a.M) : IO::one_raw();
+            qv[i] = (t0 + i < a.s) ? IO::load_stream(a.q, base + (t0 + i) * a.M) : IO::one_raw();
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int64_t t = t0 + i;
@@ -492,7 +599,7 @@ __global__ void __launch_bounds__(kColumnBlock) fwd_column_kernel(KernelArgs a) 
                 P = qmul(qq, P);
             }
             cm = qmul(qq, cm);
-            if (a.out != nullptr) IO::store(a.out, base + t * a.M, cm);
+            if (a.out != nullptr) IO::store_stream(a.out, base + t * a.M, cm);
         }
     }
 }
@@ -507,46 +614,44 @@ __global__ void __launch_bounds__(kColumnBlock) bwd_column_kernel(KernelArgs a) 
     const int64_t base = bi * a.s * a.M + m;
     // Pass 1: S[0] = sum_t conj(P_t) (x) d_t.
     Q4<CT> P = q_one<CT>();
-    Q4<CT> S0 = q_zero<CT>();
+    Q4<CT> S = q_zero<CT>();
     for (int64_t t0 = 0; t0 < a.s; t0 += U) {
         Raw qv[U], dv[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const bool ok = t0 + i < a.s;
-            qv[i] = ok ? IO::load(a.q, base + (t0 + i) * a.M) : IO::one_raw();
-            dv[i] = ok ? IO::load(a.d_cum, base + (t0 + i) * a.M) : IO::zero_raw();
+            qv[i] = ok ? IO::load_stream(a.q, base + (t0 + i) * a.M) : IO::one_raw();
+            dv[i] = ok ? IO::load_stream(a.d_cum, base + (t0 + i) * a.M) : IO::zero_raw();
         }
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             P = qmul(IO::ct(qv[i]), P);
-            S0 = qadd(S0, qcmul(P, IO::ct(dv[i])));
+            S = qadd(S, qcmul(P, IO::ct(dv[i])));
         }
     }
-    if (a.d_init != nullptr) IO::store(a.d_init, bi * a.M + m, S0);
+    if (a.d_init != nullptr) IO::store(a.d_init, bi * a.M + m, S);
     if (a.out == nullptr) return;
-    // Pass 2: S[t] = S[0] - sum_{u<t} conj(P_u) (x) d_u, then G and d_q.
-    const Q4<CT> ini = IO::ct(IO::load(a.init, bi * a.M + m));
-    Q4<CT> Pp = q_one<CT>();
-    Q4<CT> run = q_zero<CT>();
+    // Pass 2: the closed form step by step, S[t+1] = S[t] - conj(P_t) (x) d_t.
+    Q4<CT> cm = IO::ct(IO::load(a.init, bi * a.M + m));   // cum[-1] = init
+    P = q_one<CT>();
     for (int64_t t0 = 0; t0 < a.s; t0 += U) {
         Raw qv[U], dv[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const bool ok = t0 + i < a.s;
-            qv[i] = ok ? IO::load(a.q, base + (t0 + i) * a.M) : IO::one_raw();
-            dv[i] = ok ? IO::load(a.d_cum, base + (t0 + i) * a.M) : IO::zero_raw();
+            qv[i] = ok ? IO::load_stream(a.q, base + (t0 + i) * a.M) : IO::one_raw();
+            dv[i] = ok ? IO::load_stream(a.d_cum, base + (t0 + i) * a.M) : IO::zero_raw();
         }
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int64_t t = t0 + i;
             if (t >= a.s) break;
-            const Q4<CT> Pt = qmul(IO::ct(qv[i]), Pp);
-            const Q4<CT> X = qcmul(Pt, IO::ct(dv[i]));
-            const Q4<CT> S = qsub(S0, run);
-            run = qadd(run, X);
-            const Q4<CT> G = qscale(qmul(Pt, S), CT(1) / qnorm2(Pt));
-            IO::store(a.out, base + t * a.M, qmulc(G, qmul(Pp, ini)));
-            Pp = Pt;
+            const Q4<CT> qq = IO::ct(qv[i]);
+            P = qmul(qq, P);
+            const Q4<CT> G = qscale(qmul(P, S), recip(qnorm2(P)));
+            IO::store_stream(a.out, base + t * a.M, qmulc(G, cm));
+            S = qsub(S, qcmul(P, IO::ct(dv[i])));
+            cm = qmul(qq, cm);
         }
     }
 }
@@ -556,15 +661,16 @@ __global__ void zero_words_kernel(uint32_t* p, size_t n) {
         p[i] = 0u;
 }
 
-// Runs before each scan kernel: ticket := 0 and flags[0, n) := 0; the first
-// kernel of an API call also clears the status word.
-__global__ void clear_launch_state_kernel(uint32_t* hdr, uint32_t* flags, size_t n, uint32_t clear_status) {
+// Runs before each scan kernel: ticket := 0, the launch's carry slots :=
+// kEmpty (all ones), and at the start of an API call status := 0.
+__global__ void clear_launch_state_kernel(uint32_t* hdr, uint4* slots, size_t n16, uint32_t clear_status) {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         hdr[kHdrTicket] = 0u;
         if (clear_status) hdr[kHdrStatus] = 0u;
     }
-    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
-        flags[i] = 0u;
+    const uint4 e = make_uint4(~0u, ~0u, ~0u, ~0u);
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += size_t(gridDim.x) * blockDim.x)
+        slots[i] = e;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -641,16 +747,16 @@ hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st) {
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(kColumnBlock), params, 0, st);
 }
 
-hipError_t launch_clear_state(uint32_t* hdr, uint32_t* flags, size_t n_flags, bool clear_status,
-                              hipStream_t st) {
-    size_t blocks = (n_flags + 255) / 256;
+hipError_t launch_clear_state(uint32_t* hdr, void* slots, size_t slot_bytes, bool clear_status, hipStream_t st) {
+    const size_t n16 = slot_bytes / 16;
+    size_t blocks = (n16 + 255) / 256;
     if (blocks < 1) blocks = 1;
-    if (blocks > 1024) blocks = 1024;
+    if (blocks > 2048) blocks = 2048;
     uint32_t* h = hdr;
-    uint32_t* f = flags;
-    size_t n = n_flags;
+    uint4* s = static_cast<uint4*>(slots);
+    size_t n = n16;
     uint32_t cs = clear_status ? 1u : 0u;
-    void* params[] = {&h, &f, &n, &cs};
+    void* params[] = {&h, &s, &n, &cs};
     return hipLaunchKernel(reinterpret_cast<const void*>(&clear_launch_state_kernel), dim3(unsigned(blocks)),
                            dim3(256), params, 0, st);
 }
