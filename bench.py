@@ -29,7 +29,8 @@ if ROOT not in sys.path:
 METRIC = "quat cumprod fwd+bwd GB/s and % HBM peak, b8·s4096·h32·j32 fp32"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "quaternion_cumprod_autodiff_amd", "csrc", "qc_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_headline.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline.txt")
+WORKLOAD_KEY = "headline b8 s4096 h32 j32 f32 I/O, forward + backward"
 
 
 def log(*a):
@@ -41,17 +42,74 @@ def kernel_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def read_kv(path: str) -> dict:
+    out = {}
+    with open(path) as f:
+        for ln in f:
+            if "=" in ln and not ln.lstrip().startswith("#"):
+                k, v = ln.split("=", 1)
+                out[k.strip()] = v.strip()
+    return out
+
+
 def load_traffic(workload_key: str):
     """HBM bytes per backward launch from the committed rocprofv3 counter
     summary, or None when missing or taken on a different kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+        rec = read_kv(TRAFFIC_FILE)
+    except OSError:
         return None
     if rec.get("kernel_source_sha256") != kernel_source_sha() or rec.get("workload") != workload_key:
         return None
-    return rec.get("bwd_hbm_bytes_per_launch")
+    return float(rec["bwd_hbm_bytes_per_launch"])
+
+
+def summarize_traffic(pmc_dir: str, copy_bytes: float):
+    """Scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings (KiB per dispatch) by
+    what the same counters read for a plain device copy of known size, and
+    write the per-launch HBM bytes of the scan kernels to profiles/."""
+    import csv
+    import statistics
+
+    def per_kernel(run, counter):
+        vals = {}
+        path = os.path.join(pmc_dir, run, "run_counter_collection.csv")
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("bwd" if "bwd_chunked_kernel" in name else "fwd" if "fwd_chunked_kernel" in name
+                   else "copy" if "copyBuffer" in name else None)
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    f, w = per_kernel("FETCH_SIZE", "FETCH_SIZE"), per_kernel("WRITE_SIZE", "WRITE_SIZE")
+    fs = copy_bytes / per_kernel("copy_FETCH_SIZE", "FETCH_SIZE")["copy"]
+    ws = copy_bytes / per_kernel("copy_WRITE_SIZE", "WRITE_SIZE")["copy"]
+    rec = {
+        "workload": WORKLOAD_KEY,
+        "kernel_source_sha256": kernel_source_sha(),
+        "fetch_scale": f"{fs:.4f}", "write_scale": f"{ws:.4f}",
+        "fwd_fetch_bytes": f"{f['fwd'] * fs:.0f}", "fwd_write_bytes": f"{w['fwd'] * ws:.0f}",
+        "bwd_fetch_bytes": f"{f['bwd'] * fs:.0f}", "bwd_write_bytes": f"{w['bwd'] * ws:.0f}",
+        "fwd_hbm_bytes_per_launch": f"{f['fwd'] * fs + w['fwd'] * ws:.0f}",
+        "bwd_hbm_bytes_per_launch": f"{f['bwd'] * fs + w['bwd'] * ws:.0f}",
+    }
+    with open(TRAFFIC_FILE, "w") as out:
+        out.write("# HBM traffic per launch of the scan kernels, headline workload (b8 s4096 h32 j32, f32 I/O).\n")
+        out.write("# Counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), each\n")
+        out.write("# scaled by bytes / reading of the same counter for a plain device copy of one tensor.\n")
+        out.write("# Commands (run from /tmp, TMPDIR=/tmp, R = repository root):\n")
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $R/gpurun_out/pmc/{ctr} -o run -- "
+                      f"python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline\n")
+            out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $R/gpurun_out/pmc/copy_{ctr} -o run -- "
+                      f"python3 $R/bench.py --copy-calibration --steps 2 --warmup 1\n")
+        out.write(f"#   python3 $R/bench.py --summarize-traffic $R/gpurun_out/pmc\n")
+        for k, v in rec.items():
+            out.write(f"{k} = {v}\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(inp, min_seconds: float = 10.0):
@@ -109,9 +167,17 @@ def main():
     ap.add_argument("--leaves-only", action="store_true",
                     help="backward without the saved boundary state (re-derives it from q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without per-kernel event records (they add a bubble per record)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device copy of one [b,s,h,j,4] tensor")
+    ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
+                    help="write profiles/traffic_headline.txt from rocprofv3 FETCH_SIZE/WRITE_SIZE runs")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        b, s, h, j, _, io = CONFIGS["headline"]
+        summarize_traffic(args.summarize_traffic, float(b * s * h * j * 16))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -169,6 +235,10 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if args.no_kernel_events:
+            fwd()
+            bwd()
+            continue
         fe[k][0].record()
         fwd()
         fe[k][1].record()
@@ -180,8 +250,11 @@ def main():
     if capi.default_workspace.status(dev) != 0:
         raise RuntimeError("a cross-block wait hit its spin limit during the timed steps")
 
-    fwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in fe]))
-    bwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in be]))
+    if args.no_kernel_events:
+        fwd_ms = bwd_ms = float("nan")
+    else:
+        fwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in fe]))
+        bwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in be]))
     ms_step = wall / args.steps * 1e3
     fwd_bytes = 2 * io_bytes * n + io_bytes * cols
     bwd_bytes = 3 * io_bytes * n + 2 * io_bytes * cols

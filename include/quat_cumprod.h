@@ -47,11 +47,13 @@
  * nothing was enqueued (except QC_ERR_HIP, which means a launch failed).
  *
  * Workspace: a device buffer of at least quat_cumprod_workspace_bytes(...)
- * bytes, holding cross-block carries, ready flags and (for a backward without
- * saved boundary state) re-derived boundary products.  It needs no
- * initialisation: every call first clears, with a small kernel on `stream`,
- * the part it uses.  Calls sharing one workspace must be ordered (same stream
- * or synchronised); concurrent calls need separate workspaces.
+ * bytes, holding a block ticket, a status word, cross-block carries with
+ * per-launch ready flags and (for a backward without saved boundary state)
+ * re-derived boundary products.  Zero it once after allocation
+ * (quat_cumprod_workspace_init does so on a stream; hipMemset also works);
+ * every call leaves it ready for the next one, whatever the shape.  Calls
+ * sharing one workspace must be ordered (same stream or synchronised);
+ * concurrent calls need separate workspaces.
  */
 #ifndef QUAT_CUMPROD_H
 #define QUAT_CUMPROD_H
@@ -107,8 +109,7 @@ size_t quat_cumprod_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t j, 
 size_t quat_cumprod_ckpt_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype);
 
 /* Zero a workspace on `stream` with a fill kernel (so it may be captured in a
- * HIP graph).  Optional: calls clear what they use; this only gives the status
- * word a defined value before the first call. */
+ * HIP graph).  Needed once per allocation. */
 int quat_cumprod_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Forward scan (the page's Mamba3QuatScanBackendExt::quat_cumprod).
@@ -150,9 +151,10 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum,
                         const qc_options* opts);
 
 /* Synchronise `stream`, then read the workspace's device-side status word,
- * which describes the most recent call on that workspace: 0 = every
+ * which accumulates over the calls since it was last cleared: 0 = every
  * cross-block wait completed; 1 = a wait hit its spin limit; 2 = a block drew
- * a ticket beyond its grid.  Non-zero means that call's results are invalid.
+ * a ticket beyond its grid (the workspace was not zeroed after allocation).
+ * Non-zero means results of some call since the last clear are invalid.
  * clear != 0 resets the word to 0. */
 int quat_cumprod_workspace_status(void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t clear, int32_t* status_out);

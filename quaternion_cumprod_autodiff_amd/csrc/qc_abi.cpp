@@ -9,7 +9,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
+#include <random>
 #include <string>
 
 namespace {
@@ -17,6 +19,21 @@ namespace {
 using qc::kCkptStride;
 
 thread_local std::string g_last_hip_error;
+
+// Epochs mark the ready flags of each launch.  The counter starts at a random
+// value so that flags a different process left in recycled memory are not
+// expected to match, and skips 0 (the value of a zeroed workspace).
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> counter{[] {
+        std::random_device rd;
+        return static_cast<uint32_t>(rd());
+    }()};
+    uint32_t e;
+    do {
+        e = counter.fetch_add(1, std::memory_order_relaxed);
+    } while (e == 0);
+    return e;
+}
 
 int hip_fail(hipError_t e) {
     g_last_hip_error = hipGetErrorString(e);
@@ -44,15 +61,15 @@ struct Plan {
     Tiling fwd, bwd;
     int64_t n_ck = 0;
     size_t ckpt_bytes = 0;
-    size_t off_desc = 0, off_ckpt = 0, ws_bytes = 0;
+    size_t off_flags = 0, off_desc = 0, off_ckpt = 0, ws_bytes = 0;
     int64_t n_cols = 0;
 };
 
-// Widest column group each kernel uses.  The forward holds few registers per
-// step and runs best with wide (64-column) groups; the backward holds about
-// 180 registers per lane, so narrower groups give smaller blocks, several of
-// which share a compute unit and overlap their load, compute and wait phases.
-constexpr int kFwdMaxWc = 64;
+// Widest column group each kernel uses.  Groups of 32 columns make 4-wave
+// blocks on wide rows, so that (at 2-3 waves per SIMD for these register
+// counts) two or three blocks share a compute unit and overlap their load,
+// compute and carry-wait phases; wider groups would leave one block per CU.
+constexpr int kFwdMaxWc = 32;
 constexpr int kBwdMaxWc = 32;
 
 int column_group_width(int64_t M, int cap) {
@@ -97,7 +114,11 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     const size_t slots_fwd = size_t(p->fwd.n_chains * p->fwd.n_tiles) * size_t(p->fwd.wc);
     const size_t slots_bwd = size_t(p->bwd.n_chains * p->bwd.n_tiles) * size_t(p->bwd.wc);
     const size_t slots = slots_fwd > slots_bwd ? slots_fwd : slots_bwd;
-    p->off_desc = round_up(size_t(qc::kHdrWords) * 4, kAlignWs);
+    const size_t nodes_fwd = size_t(p->fwd.n_chains * p->fwd.n_tiles);
+    const size_t nodes_bwd = size_t(p->bwd.n_chains * p->bwd.n_tiles);
+    const size_t nodes = nodes_fwd > nodes_bwd ? nodes_fwd : nodes_bwd;
+    p->off_flags = round_up(size_t(qc::kHdrWords) * 4, kAlignWs);
+    p->off_desc = round_up(p->off_flags + nodes * 4, kAlignWs);
     p->off_ckpt = round_up(p->off_desc + slots * p->ct_bytes, kAlignWs);
     p->ws_bytes = round_up(p->off_ckpt + p->ckpt_bytes, kAlignWs);
     return QC_OK;
@@ -145,18 +166,11 @@ qc::KernelArgs base_args(const Plan& p, void* ws, const Tiling& tl) {
     a.n_cg = tl.n_cg; a.n_chains = tl.n_chains; a.n_tiles = tl.n_tiles;
     a.n_blocks = uint32_t(tl.n_chains * tl.n_tiles);
     a.hdr = reinterpret_cast<uint32_t*>(ws);
+    a.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.off_flags);
     a.desc = static_cast<char*>(ws) + p.off_desc;
     a.spin_limit = qc::kSpinLimit;
+    a.epoch = next_epoch();
     return a;
-}
-
-// Reset the ticket and mark the carry slots of a launch with tiling `tl` as
-// unpublished (and, at the start of an API call, clear the status word).
-int clear_state(const Plan& p, void* ws, const Tiling* tl, bool call_start, hipStream_t st) {
-    const size_t bytes = tl ? size_t(tl->n_chains * tl->n_tiles) * size_t(tl->wc) * p.ct_bytes : 0;
-    const hipError_t e = qc::launch_clear_state(reinterpret_cast<uint32_t*>(ws), static_cast<char*>(ws) + p.off_desc,
-                                                bytes, call_start, st);
-    return e == hipSuccess ? QC_OK : hip_fail(e);
 }
 
 qc::KernelArgs column_args(const Plan& p, void* ws) {
@@ -167,9 +181,7 @@ qc::KernelArgs column_args(const Plan& p, void* ws) {
 }
 
 int launch_forward(const Plan& p, const void* q, const void* init, void* cum, void* ckpt, void* ws,
-                   hipStream_t st, bool column, bool call_start) {
-    int rc = clear_state(p, ws, column ? nullptr : &p.fwd, call_start, st);
-    if (rc != QC_OK) return rc;
+                   hipStream_t st, bool column) {
     qc::KernelArgs a = column ? column_args(p, ws) : base_args(p, ws, p.fwd);
     a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt;
     const hipError_t e = column ? qc::launch_fwd_column(p.dtype, a, st)
@@ -221,7 +233,7 @@ int quat_cumprod_fwd_ex(const void* q, const void* init, void* cum, void* ckpt, 
     if (any_alias(rs, out, 5)) return QC_ERR_ALIAS;
 
     const bool column = path == QC_PATH_COLUMN || (path == QC_PATH_AUTO && p.n_cols >= kColumnPathMinColumns);
-    return launch_forward(p, q, init, cum, ckpt, workspace, static_cast<hipStream_t>(stream), column, true);
+    return launch_forward(p, q, init, cum, ckpt, workspace, static_cast<hipStream_t>(stream), column);
 }
 
 int quat_cumprod_fwd(const void* q, const void* init, void* cum, void* ckpt, size_t ckpt_bytes,
@@ -257,8 +269,6 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
 
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (path == QC_PATH_COLUMN) {
-        rc = clear_state(p, workspace, nullptr, true, st);
-        if (rc != QC_OK) return rc;
         qc::KernelArgs a = column_args(p, workspace);
         a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init;
         const hipError_t e = qc::launch_bwd_column(p.dtype, a, st);
@@ -268,11 +278,9 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
     if (!ck) {
         // Leaves-only backward: re-derive the boundary prefix products from q.
         ck = static_cast<char*>(workspace) + p.off_ckpt;
-        rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false, true);
+        rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false);
         if (rc != QC_OK) return rc;
     }
-    rc = clear_state(p, workspace, &p.bwd, ckpt != nullptr, st);
-    if (rc != QC_OK) return rc;
     qc::KernelArgs a = base_args(p, workspace, p.bwd);
     a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init; a.ckpt = ck;
     const hipError_t e = qc::launch_bwd_chunked(p.dtype, p.bwd.wc, a, st);

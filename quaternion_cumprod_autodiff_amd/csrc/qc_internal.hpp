@@ -54,7 +54,8 @@ struct KernelArgs {
     void* d_init;         // [b][M]              (backward, may be null)
     void* ckpt;           // [b][n_ck][M] quaternions in the compute type (may be null)
     uint32_t* hdr;        // workspace header
-    void* desc;           // per-tile carry slots, WC quaternions each (kEmpty until published)
+    uint32_t* flags;      // per-tile ready flag (holds the epoch once published)
+    void* desc;           // per-tile carry values, WC quaternions each
     int64_t b, s, M;
     int64_t n_ck;         // ceil(s / kCkptStride)
     int64_t n_cg;         // column groups per batch entry
@@ -62,6 +63,7 @@ struct KernelArgs {
     int64_t n_tiles;      // tiles per chain
     uint32_t n_blocks;    // grid size
     uint32_t spin_limit;
+    uint32_t epoch;       // this launch's ready-flag value (never 0)
 };
 
 hipError_t launch_fwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_t st);
@@ -69,7 +71,6 @@ hipError_t launch_bwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st);
-hipError_t launch_clear_state(uint32_t* hdr, void* slots, size_t slot_bytes, bool clear_status, hipStream_t st);
 
 constexpr int kColumnBlock = 256;   // threads per block on the column path
 

@@ -31,16 +31,20 @@
 // combines O(log tiles) values, and the association of every floating-point
 // combine is fixed, so results are bitwise reproducible run to run.
 //
-// Publication protocol.  Before each scan kernel a small kernel fills the
-// launch's carry slots with kEmpty, an all-ones NaN pattern that no kernel
-// ever stores.  A node's words are then written with agent-scope atomic
-// stores and read with agent-scope atomic loads; each word is single-copy
-// atomic, so a reader only waits until none of its words is kEmpty.  No
-// separate ready flag, hence no release/acquire fence (on this chip an
-// agent-scope fence writes back or invalidates the whole L2, which costs
-// more than the scan itself).  Block ids come from an atomic ticket, so a
-// block only waits on blocks that started before it; every wait is bounded
-// (kSpinLimit) and raises a status word instead of hanging.
+// Publication protocol.  Every carry access is an agent-scope atomic (a
+// coherent access that bypasses the per-XCD L2), so no L2 write-back or
+// invalidate is ever needed; on this chip those (what an agent-scope fence
+// does) cost more than the scan itself.  A node is published by storing its
+// values with agent-scope atomic stores, waiting until they have completed
+// (s_waitcnt vmcnt(0), without cache maintenance), then storing the node's
+// ready flag = the launch's epoch.  A reader polls the
+// flag and, once it carries the epoch, reads the values with agent-scope
+// atomic loads issued after the flag was observed.  Flags left by earlier
+// launches carry other epochs (and a zeroed workspace carries none), so
+// nothing is cleared between launches.  Block ids come from an atomic ticket,
+// so a block only waits on blocks that started before it; the block that
+// draws the last ticket resets the counter for the next launch.  Every wait
+// is bounded (kSpinLimit) and raises a status word instead of hanging.
 //
 // Arithmetic: float64 for float32 storage, float32 for bfloat16 storage.
 #include "qc_internal.hpp"
@@ -220,55 +224,49 @@ __device__ __forceinline__ float recip(float x) {
 
 // ------------------------------------------------- cross-block carry helpers
 
-template <typename T> struct Word;
-template <> struct Word<double> { using U = unsigned long long; };
-template <> struct Word<float> { using U = unsigned int; };
-
-// Store one carry word; a value whose bits happen to equal kEmpty (a NaN)
-// is stored as the canonical quiet NaN instead.
+// Publish a node: lanes with `writer` set store their column's value, the
+// wave waits for the stores to complete, then `flag_writer` raises the flag.
 template <typename T>
-__device__ __forceinline__ void put_word(T* p, T v) {
-    using U = typename Word<T>::U;
-    U bits = __builtin_bit_cast(U, v);
-    if (bits == ~U(0)) bits = __builtin_bit_cast(U, T(__builtin_nan("")));
-    __hip_atomic_store(reinterpret_cast<U*>(p), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Publish a node: the lanes with `writer` set store their column's words.
-template <typename T>
-__device__ __forceinline__ void publish(Q4<T>* slot, const Q4<T>& v, bool writer) {
+__device__ __forceinline__ void publish(const KernelArgs& a, int64_t node, Q4<T>* slot, const Q4<T>& v,
+                                        bool writer, bool flag_writer) {
     if (writer) {
         T* f = reinterpret_cast<T*>(slot);
-        put_word(f + 0, v.w);
-        put_word(f + 1, v.x);
-        put_word(f + 2, v.y);
-        put_word(f + 3, v.z);
+        __hip_atomic_store(f + 0, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(f + 1, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(f + 2, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(f + 3, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // Wait until this wave's value stores have completed at the agent's
+    // coherence point before the flag can become visible (the memory clobber
+    // also keeps the compiler from moving memory operations across it).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (flag_writer) __hip_atomic_store(a.flags + node, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One coherent read of a slot; true if all four words are published.
+// One read attempt of a node for this lane's column: true (and *out set) if
+// the node's flag carries this launch's epoch.
 template <typename T>
-__device__ __forceinline__ bool try_read(const Q4<T>* slot, Q4<T>* out) {
-    using U = typename Word<T>::U;
-    const U* f = reinterpret_cast<const U*>(slot);
-    constexpr U E = ~U(0);
-    const U w0 = __hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const U w1 = __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const U w2 = __hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const U w3 = __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *out = {__builtin_bit_cast(T, w0), __builtin_bit_cast(T, w1), __builtin_bit_cast(T, w2),
-            __builtin_bit_cast(T, w3)};
-    return w0 != E && w1 != E && w2 != E && w3 != E;
+__device__ __forceinline__ bool try_read(const KernelArgs& a, int64_t node, const Q4<T>* slot, Q4<T>* out) {
+    if (__hip_atomic_load(a.flags + node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) return false;
+    // The value loads depend on the flag's value, so they are issued after it
+    // returned; the clobber keeps the compiler from hoisting them.
+    asm volatile("" ::: "memory");
+    const T* f = reinterpret_cast<const T*>(slot);
+    *out = {__hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+            __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+            __hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+            __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+    return true;
 }
 
-// Wait (bounded) until all four words of this lane's slot are published.
+// Wait (bounded) until the node is published, then read this lane's column.
 // Polls back off from about 30 ns to about 2 us between attempts, so a slot
 // that many tiles wait on is not hammered with coherent loads.
 template <typename T>
-__device__ __forceinline__ Q4<T> wait_read(const KernelArgs& a, const Q4<T>* slot) {
-    Q4<T> v;
+__device__ __forceinline__ Q4<T> wait_read(const KernelArgs& a, int64_t node, const Q4<T>* slot) {
+    Q4<T> v = q_zero<T>();
     uint32_t polls = 0;
-    while (!try_read(slot, &v)) {
+    while (!try_read(a, node, slot, &v)) {
         if (polls < 8) {
             __builtin_amdgcn_s_sleep(1);
         } else if (polls < 64) {
@@ -284,43 +282,73 @@ __device__ __forceinline__ Q4<T> wait_read(const KernelArgs& a, const Q4<T>* slo
     return v;
 }
 
+// Fenwick look-back.  The query path of tile i (1-based) is i-1, then
+// repeatedly j - lowbit(j) down to 0; lane slot `slot` = wave*R + r of round
+// `round` reads the node `round*PAR + slot` steps down the path.
+template <int PAR>
+__device__ __forceinline__ int64_t path_node(int64_t jn, int steps) {
+    for (int k = 0; k < steps && jn > 0; ++k) jn -= jn & (-jn);
+    return jn;
+}
+
+// Address of column c's value in carry node `node` (0-based over all chains).
+template <typename T, int WC>
+__device__ __forceinline__ Q4<T>* slot_ptr(const KernelArgs& a, int64_t node, int c) {
+    return reinterpret_cast<Q4<T>*>(a.desc) + node * WC + c;
+}
+
+// First-round read attempt, issued right after the tile's data loads so that
+// its latency overlaps them and sweep 1: in steady state the predecessor
+// tiles have already published by then.  Slots are write-once per launch, so
+// an early successful read is final; a failed one is retried later.
+template <typename T, int WC, int NW>
+__device__ __forceinline__ bool fenwick_prefetch(const KernelArgs& a, int64_t chain, int64_t pos, int slot, int c,
+                                                 Q4<T>* v) {
+    const int64_t node = path_node<NW * (64 / WC)>(pos, slot);   // i - 1 = pos
+    if (node <= 0) return false;
+    return try_read(a, chain * a.n_tiles + node - 1, slot_ptr<T, WC>(a, chain * a.n_tiles + node - 1, c), v);
+}
+
 // Fenwick look-back for tile `pos` (0-based) of `chain`; called by every
 // thread of the block.  `own` is this tile's aggregate, valid in the wave
-// `own_wave`.  Combine(later, earlier) is
+// `own_wave`; (pre_v, pre_ok) is this slot's first-round prefetch.
+// Combine(later, earlier) is
 //   product:  later (x) earlier           (forward carry P)
 //   sum:      later + earlier             (backward carry S, "later" = earlier in time)
-// The query path is walked in rounds of NW*R nodes: every lane slot
-// (wave*R + r) makes one coherent read attempt of one node for column c, so
-// nodes that are already published cost one round trip together; then
+// The query path is walked in rounds of PAR = NW*R nodes: every lane slot
+// makes one read attempt of one node for column c (round 0 uses the
+// prefetch), so published nodes cost at most one round trip together; then
 // `own_wave` combines the round in the fixed order, waiting itself (nearest
-// node first) only for nodes that were not yet published, and publishes
-// node i as soon as its children are in.  Returns the exclusive prefix
-// (identity / zero for the first tile) to every thread.
+// node first) only for nodes that were not yet published, and publishes node
+// i as soon as its children are in.  Returns the exclusive prefix (identity /
+// zero for the first tile) to every thread.
 template <typename T, int WC, int NW, bool kProduct>
 __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const Q4<T>& own,
-                                   bool own_wave, int wave, int r, int c, Q4<T> (*s_nodes)[WC],
-                                   uint8_t (*s_ok)[WC], Q4<T>* s_out) {
+                                   bool own_wave, int wave, int r, int c, const Q4<T>& pre_v, bool pre_ok,
+                                   Q4<T> (*s_nodes)[WC], uint8_t (*s_ok)[WC], Q4<T>* s_out) {
     constexpr int R = 64 / WC;
     constexpr int PAR = NW * R;
     const int64_t i = pos + 1;
     const int64_t low = i & (-i);
     const int64_t node0 = chain * a.n_tiles;   // node n lives at node0 + n - 1
-    Q4<T>* desc = reinterpret_cast<Q4<T>*>(a.desc);
     const int slot = wave * R + r;
+    const bool wave_lane0 = (threadIdx.x & 63) == 0;
     Q4<T> acc = kProduct ? q_one<T>() : q_zero<T>();
     bool published = (i == a.n_tiles);        // nothing reads the last node
     int64_t jn = i - 1;                       // next node on the query path (block-uniform)
-    for (;;) {
+    for (int round = 0;; ++round) {
         if (own_wave && !published && jn <= i - low) {
-            publish(desc + (node0 + i - 1) * WC + c, kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
+            publish(a, node0 + i - 1, slot_ptr<T, WC>(a, node0 + i - 1, c), kProduct ? qmul(own, acc) : qadd(own, acc),
+                    r == 0, wave_lane0);
             published = true;
         }
         if (jn == 0) break;
-        int64_t mine = jn;                    // this slot's node: `slot` steps down the path
-        for (int k = 0; k < slot && mine > 0; ++k) mine -= mine & (-mine);
+        const int64_t mine = path_node<PAR>(jn, slot);
         if (mine > 0) {
-            Q4<T> v;
-            const bool ok = try_read(desc + (node0 + mine - 1) * WC + c, &v);
+            Q4<T> v = pre_v;
+            const int64_t nd = node0 + mine - 1;
+            const bool ok = round == 0 ? (pre_ok || try_read(a, nd, slot_ptr<T, WC>(a, nd, c), &v))
+                                       : try_read(a, nd, slot_ptr<T, WC>(a, nd, c), &v);
             s_nodes[slot][c] = v;
             s_ok[slot][c] = ok ? 1 : 0;
         }
@@ -328,10 +356,12 @@ __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t p
         for (int k = 0; k < PAR && jn > 0; ++k) {
             if (own_wave) {
                 if (!published && jn <= i - low) {
-                    publish(desc + (node0 + i - 1) * WC + c, kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
+                    publish(a, node0 + i - 1, slot_ptr<T, WC>(a, node0 + i - 1, c), kProduct ? qmul(own, acc) : qadd(own, acc),
+                    r == 0, wave_lane0);
                     published = true;
                 }
-                const Q4<T> v = s_ok[k][c] ? s_nodes[k][c] : wait_read(a, desc + (node0 + jn - 1) * WC + c);
+                const Q4<T> v = s_ok[k][c] ? s_nodes[k][c]
+                                           : wait_read<T>(a, node0 + jn - 1, slot_ptr<T, WC>(a, node0 + jn - 1, c));
                 acc = kProduct ? qmul(acc, v) : qadd(acc, v);
             }
             jn -= jn & (-jn);
@@ -405,9 +435,15 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / WC, c = lane % WC;
-    if (tid == 0) s_id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        const uint32_t id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Every block of this launch has drawn once the last ticket is out:
+        // reset the counter for the next launch on this workspace.
+        if (id == a.n_blocks - 1) __hip_atomic_store(&a.hdr[kHdrTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_id = id;
+    }
     __syncthreads();
-    if (s_id >= a.n_blocks) {   // ticket not cleared: refuse to index with it
+    if (s_id >= a.n_blocks) {   // workspace never zeroed: refuse to index with this ticket
         if (tid == 0) __hip_atomic_store(&a.hdr[kHdrStatus], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
@@ -425,6 +461,8 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     }
     Raw init_raw = IO::one_raw();
     if (a.out != nullptr && tc.col_ok) init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
+    Q4<CT> pre_v;
+    const bool pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
 
     // Slice product: A = q_{t0+L-1} (x) ... (x) q_{t0}.
     Q4<CT> A = IO::ct(qv[0]);
@@ -434,7 +472,7 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     Q4<CT> tile_agg;
     const Q4<CT> F = tile_scan_product<CT, WC, NW>(A, s_wagg, wave, r, c, &tile_agg);
     const Q4<CT> Et = fenwick_exclusive<CT, WC, NW, true>(a, tc.chain, tc.pos, tile_agg, wave == NW - 1, wave, r, c,
-                                                           s_nodes, s_ok, s_carry);
+                                                           pre_v, pre_ok, s_nodes, s_ok, s_carry);
     const Q4<CT> Ps = qmul(F, Et);   // P_{t0-1}: prefix product before this slice
 
     if (a.ckpt != nullptr && tc.col_ok && tc.t0 < a.s && (tc.t0 % kCkptStride) == 0)
@@ -462,15 +500,19 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 
 // ----------------------------------------------------------- backward, chunked
 //
-// Sweep 1 works in the slice's local frame, so it needs no carry: with
-// Lc_t = q_t (x) ... (x) q_{t0} it forms the slice product Lc_{t0+L-1} and
-// Yh = sum_t conj(Lc_t) (x) d_t.  Once the in-tile scan gives E = P_{t0-1}
-// (saved boundary state times the products of earlier slices), the slice's
-// share of S is Y = conj(E) (x) Yh, and the reverse sums of Y over later
-// slices, tiles and chains give S at the slice start.  Sweep 2 then follows
-// the closed form step by step in the global frame:
-//   P_t = q_t (x) P_{t-1},  G = P_t (x) S[t] / |P_t|^2,  d_q[t] = G (x) conj(cum[t-1]),
-//   S[t+1] = S[t] - conj(P_t) (x) d_t,  cum[t] = q_t (x) cum[t-1].
+// Each lane owns L consecutive steps t0 .. t0+L-1 of one column.  With the
+// local products Lc_t = q_t (x) ... (x) q_{t0} and E = P_{t0-1} (saved
+// boundary state times the products of earlier slices of the tile):
+//   P_t = Lc_t (x) E,   conj(P_t) (x) d_t = conj(E) (x) Xh_t,   Xh_t = conj(Lc_t) (x) d_t
+//   S[t] = conj(E) (x) Sh_t + S_after,   Sh_t = sum_{u >= t, u in slice} Xh_u
+//   G[t] = P_t (x) S[t] / |P_t|^2 = Lc_t (x) (Sh_t + Z) / |Lc_t|^2,   Z = E (x) S_after / |E|^2
+//   cum[t-1] = Lc_{t-1} (x) C,   C = E (x) init,   d_q[t] = G[t] (x) conj(cum[t-1])
+// where S_after (S just past the slice) is the reverse sum of the slices'
+// shares conj(E) (x) sum_t Xh_t over later slices, tiles and column chains.
+// Sweep 1 needs no carry and keeps Lc_t and Xh_t in registers; once the
+// carries are in, sweep 2 costs three products per step.  Long-range
+// quantities enter once per slice and the per-step arithmetic stays in the
+// well-conditioned local frame.
 
 template <class IO, int WC, int L, int NW>
 __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
@@ -486,9 +528,15 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / WC, c = lane % WC;
-    if (tid == 0) s_id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        const uint32_t id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Every block of this launch has drawn once the last ticket is out:
+        // reset the counter for the next launch on this workspace.
+        if (id == a.n_blocks - 1) __hip_atomic_store(&a.hdr[kHdrTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_id = id;
+    }
     __syncthreads();
-    if (s_id >= a.n_blocks) {   // ticket not cleared: refuse to index with it
+    if (s_id >= a.n_blocks) {   // workspace never zeroed: refuse to index with this ticket
         if (tid == 0) __hip_atomic_store(&a.hdr[kHdrStatus], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
@@ -517,19 +565,22 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
         Et = reinterpret_cast<const Q4<CT>*>(a.ckpt)[(tc.bi * a.n_ck + tile_t0 / kCkptStride) * a.M + tc.m];
         init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
     }
+    Q4<CT> pre_v;
+    const bool pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
 
-    // Sweep 1 (local frame).
-    Q4<CT> Lc = q_one<CT>();
+    // Sweep 1 (local frame): keep Lc_t and Xh_t; Yh = sum of Xh_t.
+    Q4<CT> Lc[L], Xh[L];
     Q4<CT> Yh = q_zero<CT>();
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-        Lc = qmul(IO::ct(qv[i]), Lc);
-        Yh = qadd(Yh, qcmul(Lc, IO::ct(dv[i])));
+        Lc[i] = i == 0 ? IO::ct(qv[0]) : qmul(IO::ct(qv[i]), Lc[i - 1]);
+        Xh[i] = qcmul(Lc[i], IO::ct(dv[i]));
+        Yh = qadd(Yh, Xh[i]);
     }
 
     // Forward prefix inside the tile -> E = P_{t0-1} of this slice.
     Q4<CT> tile_prod;
-    const Q4<CT> F = tile_scan_product<CT, WC, NW>(Lc, s_wagg, wave, r, c, &tile_prod);
+    const Q4<CT> F = tile_scan_product<CT, WC, NW>(Lc[L - 1], s_wagg, wave, r, c, &tile_prod);
     const Q4<CT> E = qmul(F, Et);
     const Q4<CT> Y = qcmul(E, Yh);   // this slice's share of S, global frame
 
@@ -548,24 +599,23 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
     for (int w2 = wave + 1; w2 < NW; ++w2) later_waves = qadd(later_waves, s_wsum[w2][c]);
     const Q4<CT> tile_sum = qadd(shfl_q(sinc, c), later_waves);   // valid in wave 0
     const Q4<CT> Sa = fenwick_exclusive<CT, WC, NW, false>(a, tc.chain, tc.pos, tile_sum, wave == 0, wave, r, c,
-                                                            s_nodes, s_ok, s_after);
-    const Q4<CT> S_after = qadd(qadd(later_in_wave, later_waves), Sa);   // S at t0 + L
-    Q4<CT> S = qadd(Y, S_after);                                                   // S at t0
+                                                            pre_v, pre_ok, s_nodes, s_ok, s_after);
+    const Q4<CT> S_after = qadd(qadd(later_in_wave, later_waves), Sa);   // S just past the slice
 
-    if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok) IO::store(a.d_init, tc.bi * a.M + tc.m, S);   // S[0]
+    if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok)
+        IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Y, S_after));   // S[0]
 
     if (a.out != nullptr && tc.col_ok) {
-        Q4<CT> P = E;                                // P_{t-1}
-        Q4<CT> cm = qmul(E, IO::ct(init_raw));       // cum[t-1]
+        const Q4<CT> Z = qscale(qmul(E, S_after), recip(qnorm2(E)));
+        const Q4<CT> C = qmul(E, IO::ct(init_raw));   // cum[t0-1]
+        Q4<CT> Sh = Yh;                                // Sh_t
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             if (!tc.full && tc.t0 + i >= a.s) break;
-            const Q4<CT> qq = IO::ct_fresh(qv[i]);
-            P = qmul(qq, P);
-            const Q4<CT> G = qscale(qmul(P, S), recip(qnorm2(P)));
-            IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qmulc(G, cm));
-            S = qsub(S, qcmul(P, IO::ct_fresh(dv[i])));
-            cm = qmul(qq, cm);
+            const Q4<CT> G = qmul(Lc[i], qadd(Sh, Z));
+            const Q4<CT> cprev = i == 0 ? C : qmul(Lc[i - 1], C);
+            IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qscale(qmulc(G, cprev), recip(qnorm2(Lc[i]))));
+            Sh = qsub(Sh, Xh[i]);
         }
     }
 }
@@ -661,18 +711,6 @@ __global__ void zero_words_kernel(uint32_t* p, size_t n) {
         p[i] = 0u;
 }
 
-// Runs before each scan kernel: ticket := 0, the launch's carry slots :=
-// kEmpty (all ones), and at the start of an API call status := 0.
-__global__ void clear_launch_state_kernel(uint32_t* hdr, uint4* slots, size_t n16, uint32_t clear_status) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        hdr[kHdrTicket] = 0u;
-        if (clear_status) hdr[kHdrStatus] = 0u;
-    }
-    const uint4 e = make_uint4(~0u, ~0u, ~0u, ~0u);
-    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += size_t(gridDim.x) * blockDim.x)
-        slots[i] = e;
-}
-
 // ------------------------------------------------------------------ launchers
 
 template <class IO, int WC>
@@ -745,20 +783,6 @@ hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st) {
     const void* fn = dtype == 0 ? reinterpret_cast<const void*>(&bwd_column_kernel<IoF32, 8>)
                                 : reinterpret_cast<const void*>(&bwd_column_kernel<IoBF16, 8>);
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(kColumnBlock), params, 0, st);
-}
-
-hipError_t launch_clear_state(uint32_t* hdr, void* slots, size_t slot_bytes, bool clear_status, hipStream_t st) {
-    const size_t n16 = slot_bytes / 16;
-    size_t blocks = (n16 + 255) / 256;
-    if (blocks < 1) blocks = 1;
-    if (blocks > 2048) blocks = 2048;
-    uint32_t* h = hdr;
-    uint4* s = static_cast<uint4*>(slots);
-    size_t n = n16;
-    uint32_t cs = clear_status ? 1u : 0u;
-    void* params[] = {&h, &s, &n, &cs};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&clear_launch_state_kernel), dim3(unsigned(blocks)),
-                           dim3(256), params, 0, st);
 }
 
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st) {
