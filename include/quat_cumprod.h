@@ -47,9 +47,9 @@
  * nothing was enqueued (except QC_ERR_HIP, which means a launch failed).
  *
  * Workspace: a device buffer of at least quat_cumprod_workspace_bytes(...)
- * bytes, holding a block ticket, a status word, cross-block carries with
- * per-launch ready flags and (for a backward without saved boundary state)
- * re-derived boundary products.  Zero it once after allocation
+ * bytes, holding a block ticket, a status word, self-validating cross-block
+ * carries and (for a backward without saved boundary state) re-derived
+ * boundary products.  Zero it once after allocation
  * (quat_cumprod_workspace_init does so on a stream; hipMemset also works);
  * every call leaves it ready for the next one, whatever the shape.  Calls
  * sharing one workspace must be ordered (same stream or synchronised);

@@ -20,9 +20,9 @@ using qc::kCkptStride;
 
 thread_local std::string g_last_hip_error;
 
-// Epochs mark the ready flags of each launch.  The counter starts at a random
-// value so that flags a different process left in recycled memory are not
-// expected to match, and skips 0 (the value of a zeroed workspace).
+// Epochs enter the check word of every carry slot a launch writes.  The
+// counter starts at a random value so that slots a different process left in
+// recycled memory are not expected to match, and skips 0.
 uint32_t next_epoch() {
     static std::atomic<uint32_t> counter{[] {
         std::random_device rd;
@@ -58,10 +58,11 @@ struct Plan {
     int dtype = 0;
     size_t io_bytes = 0;      // bytes per stored quaternion
     size_t ct_bytes = 0;      // bytes per internal quaternion
+    size_t slot_bytes = 0;    // bytes per carry slot (value words + check word)
     Tiling fwd, bwd;
     int64_t n_ck = 0;
     size_t ckpt_bytes = 0;
-    size_t off_flags = 0, off_desc = 0, off_ckpt = 0, ws_bytes = 0;
+    size_t off_desc = 0, off_ckpt = 0, ws_bytes = 0;
     int64_t n_cols = 0;
 };
 
@@ -101,6 +102,7 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     p->b = b; p->s = s; p->M = M; p->N = b * s * M; p->dtype = dtype;
     p->io_bytes = dtype == QC_DTYPE_F32 ? 16 : 8;
     p->ct_bytes = dtype == QC_DTYPE_F32 ? 32 : 16;
+    p->slot_bytes = dtype == QC_DTYPE_F32 ? 40 : 24;
     p->n_cols = b * M;
     p->fwd = make_tiling(b, s, M, kFwdMaxWc, false);
     p->bwd = make_tiling(b, s, M, kBwdMaxWc, true);
@@ -114,12 +116,8 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     const size_t slots_fwd = size_t(p->fwd.n_chains * p->fwd.n_tiles) * size_t(p->fwd.wc);
     const size_t slots_bwd = size_t(p->bwd.n_chains * p->bwd.n_tiles) * size_t(p->bwd.wc);
     const size_t slots = slots_fwd > slots_bwd ? slots_fwd : slots_bwd;
-    const size_t nodes_fwd = size_t(p->fwd.n_chains * p->fwd.n_tiles);
-    const size_t nodes_bwd = size_t(p->bwd.n_chains * p->bwd.n_tiles);
-    const size_t nodes = nodes_fwd > nodes_bwd ? nodes_fwd : nodes_bwd;
-    p->off_flags = round_up(size_t(qc::kHdrWords) * 4, kAlignWs);
-    p->off_desc = round_up(p->off_flags + nodes * 4, kAlignWs);
-    p->off_ckpt = round_up(p->off_desc + slots * p->ct_bytes, kAlignWs);
+    p->off_desc = round_up(size_t(qc::kHdrWords) * 4, kAlignWs);
+    p->off_ckpt = round_up(p->off_desc + slots * p->slot_bytes, kAlignWs);
     p->ws_bytes = round_up(p->off_ckpt + p->ckpt_bytes, kAlignWs);
     return QC_OK;
 }
@@ -166,7 +164,6 @@ qc::KernelArgs base_args(const Plan& p, void* ws, const Tiling& tl) {
     a.n_cg = tl.n_cg; a.n_chains = tl.n_chains; a.n_tiles = tl.n_tiles;
     a.n_blocks = uint32_t(tl.n_chains * tl.n_tiles);
     a.hdr = reinterpret_cast<uint32_t*>(ws);
-    a.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.off_flags);
     a.desc = static_cast<char*>(ws) + p.off_desc;
     a.spin_limit = qc::kSpinLimit;
     a.epoch = next_epoch();

@@ -54,8 +54,7 @@ struct KernelArgs {
     void* d_init;         // [b][M]              (backward, may be null)
     void* ckpt;           // [b][n_ck][M] quaternions in the compute type (may be null)
     uint32_t* hdr;        // workspace header
-    uint32_t* flags;      // per-tile ready flag (holds the epoch once published)
-    void* desc;           // per-tile carry values, WC quaternions each
+    void* desc;           // per-tile carry slots, WC columns each (value words + check word)
     int64_t b, s, M;
     int64_t n_ck;         // ceil(s / kCkptStride)
     int64_t n_cg;         // column groups per batch entry
@@ -63,7 +62,7 @@ struct KernelArgs {
     int64_t n_tiles;      // tiles per chain
     uint32_t n_blocks;    // grid size
     uint32_t spin_limit;
-    uint32_t epoch;       // this launch's ready-flag value (never 0)
+    uint32_t epoch;       // this launch's epoch, folded into every check word (never 0)
 };
 
 hipError_t launch_fwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_t st);

@@ -31,20 +31,21 @@
 // combines O(log tiles) values, and the association of every floating-point
 // combine is fixed, so results are bitwise reproducible run to run.
 //
-// Publication protocol.  Every carry access is an agent-scope atomic (a
-// coherent access that bypasses the per-XCD L2), so no L2 write-back or
-// invalidate is ever needed; on this chip those (what an agent-scope fence
-// does) cost more than the scan itself.  A node is published by storing its
-// values with agent-scope atomic stores, waiting until they have completed
-// (s_waitcnt vmcnt(0), without cache maintenance), then storing the node's
-// ready flag = the launch's epoch.  A reader polls the
-// flag and, once it carries the epoch, reads the values with agent-scope
-// atomic loads issued after the flag was observed.  Flags left by earlier
-// launches carry other epochs (and a zeroed workspace carries none), so
-// nothing is cleared between launches.  Block ids come from an atomic ticket,
-// so a block only waits on blocks that started before it; the block that
-// draws the last ticket resets the counter for the next launch.  Every wait
-// is bounded (kSpinLimit) and raises a status word instead of hanging.
+// Publication protocol.  Each column's carry in a node is a slot of 64-bit
+// words: the value bits followed by one check word, a hash of the value words
+// and of the launch epoch.  The slot is written with agent-scope atomic stores and read with
+// agent-scope atomic loads (coherent accesses that bypass the per-XCD L2, so
+// no L2 write-back or invalidate is ever needed: on this chip those cost
+// more than the scan itself).  A reader accepts a slot when its check word
+// matches its value words and the current epoch.  Slots left by earlier
+// launches fail (their epoch differs; a zeroed slot can never match), so
+// nothing is cleared between launches, and a slot read while it is being
+// written fails unless a 64-bit hash collides.  Publishing is therefore a handful of stores with no wait and
+// reading is one round trip, with no ready flag and no ordering between
+// words.  Block ids come from an atomic ticket, so a block only waits on
+// blocks that started before it; the block that draws the last ticket resets
+// the counter for the next launch.  Every wait is bounded (kSpinLimit) and
+// raises a status word instead of hanging.
 //
 // Arithmetic: float64 for float32 storage, float32 for bfloat16 storage.
 #include "qc_internal.hpp"
@@ -224,49 +225,83 @@ __device__ __forceinline__ float recip(float x) {
 
 // ------------------------------------------------- cross-block carry helpers
 
-// Publish a node: lanes with `writer` set store their column's value, the
-// wave waits for the stores to complete, then `flag_writer` raises the flag.
+using SlotWord = unsigned long long;
+
+// Value words per column slot (float64: one per component; float32: two
+// components per word), plus one check word.
+template <typename T> struct SlotLayout;
+template <> struct SlotLayout<double> { static constexpr int kValueWords = 4; };
+template <> struct SlotLayout<float> { static constexpr int kValueWords = 2; };
 template <typename T>
-__device__ __forceinline__ void publish(const KernelArgs& a, int64_t node, Q4<T>* slot, const Q4<T>& v,
-                                        bool writer, bool flag_writer) {
-    if (writer) {
-        T* f = reinterpret_cast<T*>(slot);
-        __hip_atomic_store(f + 0, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(f + 1, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(f + 2, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(f + 3, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+constexpr int slot_words() { return SlotLayout<T>::kValueWords + 1; }
+
+// Check word of a slot: a multiply-xorshift hash of the value words and the
+// launch epoch.  Being non-linear, a slot that mixes words of two different
+// writes matches with probability about 2^-63 whatever the bit patterns; the
+// low bit is forced to 1 so a zeroed slot never matches.
+template <int NV>
+__device__ __forceinline__ SlotWord check_word(const SlotWord* v, uint32_t epoch) {
+    SlotWord h = SlotWord(epoch) * 0x9E3779B97F4A7C15ull;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        h = (h ^ v[k]) * 0xFF51AFD7ED558CCDull;
+        h ^= h >> 33;
     }
-    // Wait until this wave's value stores have completed at the agent's
-    // coherence point before the flag can become visible (the memory clobber
-    // also keeps the compiler from moving memory operations across it).
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (flag_writer) __hip_atomic_store(a.flags + node, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return h | 1ull;
 }
 
-// One read attempt of a node for this lane's column: true (and *out set) if
-// the node's flag carries this launch's epoch.
-template <typename T>
-__device__ __forceinline__ bool try_read(const KernelArgs& a, int64_t node, const Q4<T>* slot, Q4<T>* out) {
-    if (__hip_atomic_load(a.flags + node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) return false;
-    // The value loads depend on the flag's value, so they are issued after it
-    // returned; the clobber keeps the compiler from hoisting them.
-    asm volatile("" ::: "memory");
-    const T* f = reinterpret_cast<const T*>(slot);
-    *out = {__hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-            __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-            __hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-            __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
-    return true;
+__device__ __forceinline__ void pack_words(const Q4<double>& q, SlotWord* v) {
+    v[0] = __builtin_bit_cast(SlotWord, q.w);
+    v[1] = __builtin_bit_cast(SlotWord, q.x);
+    v[2] = __builtin_bit_cast(SlotWord, q.y);
+    v[3] = __builtin_bit_cast(SlotWord, q.z);
+}
+__device__ __forceinline__ void pack_words(const Q4<float>& q, SlotWord* v) {
+    v[0] = SlotWord(__float_as_uint(q.w)) | (SlotWord(__float_as_uint(q.x)) << 32);
+    v[1] = SlotWord(__float_as_uint(q.y)) | (SlotWord(__float_as_uint(q.z)) << 32);
+}
+__device__ __forceinline__ Q4<double> unpack_words(const SlotWord* v, double) {
+    return {__builtin_bit_cast(double, v[0]), __builtin_bit_cast(double, v[1]), __builtin_bit_cast(double, v[2]),
+            __builtin_bit_cast(double, v[3])};
+}
+__device__ __forceinline__ Q4<float> unpack_words(const SlotWord* v, float) {
+    return {__uint_as_float(uint32_t(v[0])), __uint_as_float(uint32_t(v[0] >> 32)), __uint_as_float(uint32_t(v[1])),
+            __uint_as_float(uint32_t(v[1] >> 32))};
+}
+
+// Publish this lane's column of a node (lanes with `writer` set).
+template <typename T, int WC>
+__device__ __forceinline__ void publish(const KernelArgs& a, SlotWord* slot, const Q4<T>& v, bool writer) {
+    if (writer) {
+        constexpr int NV = SlotLayout<T>::kValueWords;
+        SlotWord w[NV + 1];
+        pack_words(v, w);
+        w[NV] = check_word<NV>(w, a.epoch);
+#pragma unroll
+        for (int k = 0; k <= NV; ++k) __hip_atomic_store(slot + k * WC, w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// One read attempt of this lane's column of a node: true (and *out set) if
+// the slot holds a complete value of this launch.
+template <typename T, int WC>
+__device__ __forceinline__ bool try_read(const KernelArgs& a, const SlotWord* slot, Q4<T>* out) {
+    constexpr int NV = SlotLayout<T>::kValueWords;
+    SlotWord w[NV + 1];
+#pragma unroll
+    for (int k = 0; k <= NV; ++k) w[k] = __hip_atomic_load(slot + k * WC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *out = unpack_words(w, T());
+    return w[NV] == check_word<NV>(w, a.epoch);
 }
 
 // Wait (bounded) until the node is published, then read this lane's column.
 // Polls back off from about 30 ns to about 2 us between attempts, so a slot
 // that many tiles wait on is not hammered with coherent loads.
-template <typename T>
-__device__ __forceinline__ Q4<T> wait_read(const KernelArgs& a, int64_t node, const Q4<T>* slot) {
+template <typename T, int WC>
+__device__ __forceinline__ Q4<T> wait_read(const KernelArgs& a, const SlotWord* slot) {
     Q4<T> v = q_zero<T>();
     uint32_t polls = 0;
-    while (!try_read(a, node, slot, &v)) {
+    while (!try_read<T, WC>(a, slot, &v)) {
         if (polls < 8) {
             __builtin_amdgcn_s_sleep(1);
         } else if (polls < 64) {
@@ -291,10 +326,12 @@ __device__ __forceinline__ int64_t path_node(int64_t jn, int steps) {
     return jn;
 }
 
-// Address of column c's value in carry node `node` (0-based over all chains).
+// Address of column c's first slot word in carry node `node` (0-based over
+// all chains).  A node stores its words word-major: word k of column c sits at
+// k * WC + c, so the lanes of a column group read each word coalesced.
 template <typename T, int WC>
-__device__ __forceinline__ Q4<T>* slot_ptr(const KernelArgs& a, int64_t node, int c) {
-    return reinterpret_cast<Q4<T>*>(a.desc) + node * WC + c;
+__device__ __forceinline__ SlotWord* slot_ptr(const KernelArgs& a, int64_t node, int c) {
+    return reinterpret_cast<SlotWord*>(a.desc) + node * (WC * slot_words<T>()) + c;
 }
 
 // First-round read attempt, issued right after the tile's data loads so that
@@ -306,7 +343,7 @@ __device__ __forceinline__ bool fenwick_prefetch(const KernelArgs& a, int64_t ch
                                                  Q4<T>* v) {
     const int64_t node = path_node<NW * (64 / WC)>(pos, slot);   // i - 1 = pos
     if (node <= 0) return false;
-    return try_read(a, chain * a.n_tiles + node - 1, slot_ptr<T, WC>(a, chain * a.n_tiles + node - 1, c), v);
+    return try_read<T, WC>(a, slot_ptr<T, WC>(a, chain * a.n_tiles + node - 1, c), v);
 }
 
 // Fenwick look-back for tile `pos` (0-based) of `chain`; called by every
@@ -332,14 +369,12 @@ __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t p
     const int64_t low = i & (-i);
     const int64_t node0 = chain * a.n_tiles;   // node n lives at node0 + n - 1
     const int slot = wave * R + r;
-    const bool wave_lane0 = (threadIdx.x & 63) == 0;
     Q4<T> acc = kProduct ? q_one<T>() : q_zero<T>();
     bool published = (i == a.n_tiles);        // nothing reads the last node
     int64_t jn = i - 1;                       // next node on the query path (block-uniform)
     for (int round = 0;; ++round) {
         if (own_wave && !published && jn <= i - low) {
-            publish(a, node0 + i - 1, slot_ptr<T, WC>(a, node0 + i - 1, c), kProduct ? qmul(own, acc) : qadd(own, acc),
-                    r == 0, wave_lane0);
+            publish<T, WC>(a, slot_ptr<T, WC>(a, node0 + i - 1, c), kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
             published = true;
         }
         if (jn == 0) break;
@@ -347,8 +382,8 @@ __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t p
         if (mine > 0) {
             Q4<T> v = pre_v;
             const int64_t nd = node0 + mine - 1;
-            const bool ok = round == 0 ? (pre_ok || try_read(a, nd, slot_ptr<T, WC>(a, nd, c), &v))
-                                       : try_read(a, nd, slot_ptr<T, WC>(a, nd, c), &v);
+            const bool ok = round == 0 ? (pre_ok || try_read<T, WC>(a, slot_ptr<T, WC>(a, nd, c), &v))
+                                       : try_read<T, WC>(a, slot_ptr<T, WC>(a, nd, c), &v);
             s_nodes[slot][c] = v;
             s_ok[slot][c] = ok ? 1 : 0;
         }
@@ -356,12 +391,10 @@ __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t p
         for (int k = 0; k < PAR && jn > 0; ++k) {
             if (own_wave) {
                 if (!published && jn <= i - low) {
-                    publish(a, node0 + i - 1, slot_ptr<T, WC>(a, node0 + i - 1, c), kProduct ? qmul(own, acc) : qadd(own, acc),
-                    r == 0, wave_lane0);
+                    publish<T, WC>(a, slot_ptr<T, WC>(a, node0 + i - 1, c), kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
                     published = true;
                 }
-                const Q4<T> v = s_ok[k][c] ? s_nodes[k][c]
-                                           : wait_read<T>(a, node0 + jn - 1, slot_ptr<T, WC>(a, node0 + jn - 1, c));
+                const Q4<T> v = s_ok[k][c] ? s_nodes[k][c] : wait_read<T, WC>(a, slot_ptr<T, WC>(a, node0 + jn - 1, c));
                 acc = kProduct ? qmul(acc, v) : qadd(acc, v);
             }
             jn -= jn & (-jn);
