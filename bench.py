@@ -9,6 +9,13 @@ d_init).  Default workload: b=8, s=4096, h=32, j=32, float32 storage
 (33,554,432 quaternions, 512 MiB per [b,s,h,j,4] tensor), seeded unit
 quaternions.
 
+Timing: W untimed warm-up steps, continued until --settle-ms of sustained
+load has passed (the first tens of ms after idle run at unsettled clocks),
+then K timed steps between two device synchronisations.  Inside the timed
+region HIP events bracket every backward launch on its stream (the roofline
+figure); a short loop after it brackets both kernels for the forward /
+backward split.
+
 Reported value: algorithmic bytes per step (32 B/quaternion forward + 48 B
 backward, plus 16 B per column for init and d_init) / wall time per step.
 The last stdout line is one JSON record; diagnostics go to stderr.
@@ -159,8 +166,11 @@ def copy_calibration(nbytes: int, steps: int, warmup: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="keep running untimed warm-up steps until this much time has passed (the GPU's "
+                         "clocks take tens of ms of sustained load to settle)")
     from quaternion_cumprod_autodiff_amd.inputs import CONFIGS, make_config
     ap.add_argument("--config", default="headline", choices=list(CONFIGS))
     ap.add_argument("--path", default=None, choices=["auto", "column", "chunked"])
@@ -168,7 +178,7 @@ def main():
                     help="backward without the saved boundary state (re-derives it from q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
-                    help="time the steps without per-kernel event records (they add a bubble per record)")
+                    help="time the steps without the backward's event records (each adds a few us of idle)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device copy of one [b,s,h,j,4] tensor")
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
@@ -221,27 +231,30 @@ def main():
     def bwd():
         capi.quat_cumprod_bwd(q, init, d_cum, ckpt, d_q=d_q, d_init=d_init, path=args.path)
 
-    for _ in range(args.warmup):
+    # Untimed warm-up: W steps, continued until --settle-ms has passed.
+    warm_steps, t0 = 0, time.perf_counter()
+    while warm_steps < args.warmup or (time.perf_counter() - t0) * 1e3 < args.settle_ms:
         fwd()
         bwd()
+        warm_steps += 1
+        if warm_steps % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     status = capi.default_workspace.status(dev)
     if status != 0:
         raise RuntimeError("a cross-block wait hit its spin limit during warm-up")
 
+    # Timed region: K steps.  Events bracket the backward (the dominant kernel)
+    # on the stream it is launched on (the current stream).
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-    fe = [(ev(), ev()) for _ in range(args.steps)]
     be = [(ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        fwd()
         if args.no_kernel_events:
-            fwd()
             bwd()
             continue
-        fe[k][0].record()
-        fwd()
-        fe[k][1].record()
         be[k][0].record()
         bwd()
         be[k][1].record()
@@ -249,17 +262,29 @@ def main():
     wall = time.perf_counter() - t0
     if capi.default_workspace.status(dev) != 0:
         raise RuntimeError("a cross-block wait hit its spin limit during the timed steps")
+    bwd_ms = None if args.no_kernel_events else float(np.mean([a.elapsed_time(bb) for a, bb in be]))
 
-    if args.no_kernel_events:
-        fwd_ms = bwd_ms = float("nan")
-    else:
-        fwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in fe]))
-        bwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in be]))
+    # Diagnostics after the timed region: forward and backward each bracketed.
+    diag = [((ev(), ev()), (ev(), ev())) for _ in range(20)]
+    for (f0, f1), (b0, b1) in diag:
+        f0.record()
+        fwd()
+        f1.record()
+        b0.record()
+        bwd()
+        b1.record()
+    torch.cuda.synchronize()
+    fwd_ms = float(np.median([f0.elapsed_time(f1) for (f0, f1), _ in diag]))
+    bwd_ms_diag = float(np.median([b0.elapsed_time(b1) for _, (b0, b1) in diag]))
+
     ms_step = wall / args.steps * 1e3
     fwd_bytes = 2 * io_bytes * n + io_bytes * cols
     bwd_bytes = 3 * io_bytes * n + 2 * io_bytes * cols
     value = (fwd_bytes + bwd_bytes) / (ms_step * 1e-3) / 1e9
-    bwd_gbps = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+    # Roofline of the backward from its timed-region events (or, with
+    # --no-kernel-events, from the diagnostic loop).
+    bwd_ms_roof = bwd_ms if bwd_ms is not None else bwd_ms_diag
+    bwd_gbps = bwd_bytes / (bwd_ms_roof * 1e-3) / 1e9
     workload = f"{args.config} b{b} s{s} h{h} j{j} {io} I/O, forward + backward"
     traffic = load_traffic(workload) if (args.path in (None, "auto", "chunked") and not args.leaves_only) else None
 
@@ -281,9 +306,11 @@ def main():
                    "backward": "leaves-only" if args.leaves_only else "saved boundary state"},
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "elements_per_s": round(n / (ms_step * 1e-3), 1),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
-        "fwd_GBps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 2),
+        "untimed_steps": warm_steps,
+        "bwd_ms": round(bwd_ms, 4) if bwd_ms is not None else None,
+        "diag_fwd_ms": round(fwd_ms, 4),
+        "diag_bwd_ms": round(bwd_ms_diag, 4),
+        "diag_fwd_GBps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "bwd_chunked_kernel", "achieved": round(bwd_gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
