@@ -533,34 +533,45 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 
 // ----------------------------------------------------------- backward, chunked
 //
-// Each lane owns L consecutive steps t0 .. t0+L-1 of one column.  With the
-// local products Lc_t = q_t (x) ... (x) q_{t0} and E = P_{t0-1} (saved
-// boundary state times the products of earlier slices of the tile):
-//   P_t = Lc_t (x) E,   conj(P_t) (x) d_t = conj(E) (x) Xh_t,   Xh_t = conj(Lc_t) (x) d_t
-//   S[t] = conj(E) (x) Sh_t + S_after,   Sh_t = sum_{u >= t, u in slice} Xh_u
-//   G[t] = P_t (x) S[t] / |P_t|^2 = Lc_t (x) (Sh_t + Z) / |Lc_t|^2,   Z = E (x) S_after / |E|^2
-//   cum[t-1] = Lc_{t-1} (x) C,   C = E (x) init,   d_q[t] = G[t] (x) conj(cum[t-1])
-// where S_after (S just past the slice) is the reverse sum of the slices'
-// shares conj(E) (x) sum_t Xh_t over later slices, tiles and column chains.
-// Sweep 1 needs no carry and keeps Lc_t and Xh_t in registers; once the
-// carries are in, sweep 2 costs three products per step.  Long-range
-// quantities enter once per slice and the per-step arithmetic stays in the
-// well-conditioned local frame.
+// Tiles run in reverse time order; lane slice k = wave*R + r of a tile owns
+// steps t0 .. t0+L-1 of one column.  Sweep 1 (ascending) keeps only two
+// quaternions per lane, in the frame of the slice start:
+//   Q_k = q_{t0+L-1} (x) ... (x) q_{t0}                    (slice product)
+//   Y_k = sum_t conj(q_t (x) ... (x) q_{t0}) (x) d_t         (slice's share of S)
+// One LDS exchange then gives every lane, from the (Q, Y) of all slices of its
+// column in the tile:
+//   A_k  = Q_k (x) ... (x) Q_0                 (tile-local prefix through the slice)
+//   R'_k = Y_{k+1} + conj(Q_{k+1}) (x) (Y_{k+2} + conj(Q_{k+2}) (x) ( ... ))
+//          (what later slices of the tile send back to the slice's last step)
+// and the tile's total conj(E) (x) (Y_0 + conj(Q_0) (x) R'_0), E = P before the
+// tile (saved boundary state), enters the reverse look-back over tiles, which
+// returns S_after = sum over later tiles of conj(P_u) (x) d_u.  The cotangent
+// reaching the slice's last step te is then exact for any non-zero inputs:
+//   G[te] = d_te + R'_k + A_k (x) Z / |A_k|^2,     Z = E (x) S_after / |E|^2
+// (the later-tile part is P_te (x) S_after / |P_te|^2 written in the tile frame).
+// Sweep 2 walks the slice downwards with the reverse recurrence
+//   d_q[t] = G[t] (x) conj(cum[t-1]),   G[t-1] = d_{t-1} + conj(q_t) (x) G[t],
+//   cum[t-1] = conj(q_t) (x) cum[t] / |q_t|^2
+// from cum[te] = A_k (x) E (x) init, with cum[t0-1] taken directly as
+// A_{k-1} (x) E (x) init.  Only q and d stay in registers between the sweeps, in
+// storage precision.
 
 template <class IO, int WC, int L, int NW>
-__global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
+__global__ void __launch_bounds__(NW * 64, 3) bwd_chunked_kernel(KernelArgs a) {
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
-    __shared__ Q4<CT> s_wagg[NW][WC];
-    __shared__ Q4<CT> s_wsum[NW][WC];
-    __shared__ Q4<CT> s_nodes[NW * R][WC];
-    __shared__ uint8_t s_ok[NW * R][WC];
+    constexpr int K = NW * R;   // slices per column in a tile
+    __shared__ Q4<CT> s_sq[K][WC];
+    __shared__ Q4<CT> s_sy[K][WC];
+    __shared__ Q4<CT> s_nodes[K][WC];
+    __shared__ uint8_t s_ok[K][WC];
     __shared__ Q4<CT> s_after[WC];
     __shared__ uint32_t s_id;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / WC, c = lane % WC;
+    const int k = wave * R + r;
     if (tid == 0) {
         const uint32_t id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // Every block of this launch has drawn once the last ticket is out:
@@ -573,7 +584,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
         if (tid == 0) __hip_atomic_store(&a.hdr[kHdrStatus], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    const TileCoord tc = tile_coord<WC, L, NW>(a, s_id, true, wave * R + r, c);
+    const TileCoord tc = tile_coord<WC, L, NW>(a, s_id, true, k, c);
 
     Raw qv[L], dv[L];
     if (tc.full) {
@@ -590,8 +601,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
             dv[i] = ok ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M) : IO::zero_raw();
         }
     }
-    // Boundary prefix product at the tile start and the initial carry.
-    const int64_t tile_t0 = tc.t0 - int64_t(wave * R + r) * L;
+    // Prefix product before the tile (saved boundary state) and the initial carry.
+    const int64_t tile_t0 = tc.t0 - int64_t(k) * L;
     Q4<CT> Et = q_one<CT>();
     Raw init_raw = IO::one_raw();
     if (tc.col_ok) {
@@ -599,56 +610,56 @@ __global__ void __launch_bounds__(NW * 64) bwd_chunked_kernel(KernelArgs a) {
         init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
     }
     Q4<CT> pre_v;
-    const bool pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
+    const bool pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, k, c, &pre_v);
 
-    // Sweep 1 (local frame): keep Lc_t and Xh_t; Yh = sum of Xh_t.
-    Q4<CT> Lc[L], Xh[L];
-    Q4<CT> Yh = q_zero<CT>();
+    // Sweep 1: slice product and slice share, frame of the slice start.
+    Q4<CT> Ql = IO::ct(qv[0]);
+    Q4<CT> Yl = qcmul(Ql, IO::ct(dv[0]));
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-        Lc[i] = i == 0 ? IO::ct(qv[0]) : qmul(IO::ct(qv[i]), Lc[i - 1]);
-        Xh[i] = qcmul(Lc[i], IO::ct(dv[i]));
-        Yh = qadd(Yh, Xh[i]);
+    for (int i = 1; i < L; ++i) {
+        Ql = qmul(IO::ct(qv[i]), Ql);
+        Yl = qadd(Yl, qcmul(Ql, IO::ct(dv[i])));
     }
-
-    // Forward prefix inside the tile -> E = P_{t0-1} of this slice.
-    Q4<CT> tile_prod;
-    const Q4<CT> F = tile_scan_product<CT, WC, NW>(Lc[L - 1], s_wagg, wave, r, c, &tile_prod);
-    const Q4<CT> E = qmul(F, Et);
-    const Q4<CT> Y = qcmul(E, Yh);   // this slice's share of S, global frame
-
-    // Reverse (suffix) sums of Y over the slices of the tile.
-    Q4<CT> sinc = Y;   // sum over slices r' >= r of this wave
-#pragma unroll
-    for (int d = 1; d < R; d <<= 1) {
-        const Q4<CT> o = shfl_down_q(sinc, d * WC);
-        if (r + d < R) sinc = qadd(sinc, o);
-    }
-    Q4<CT> later_in_wave = shfl_down_q(sinc, WC);
-    if (r == R - 1) later_in_wave = q_zero<CT>();
-    if (r == 0) s_wsum[wave][c] = sinc;
+    s_sq[k][c] = Ql;
+    s_sy[k][c] = Yl;
     __syncthreads();
-    Q4<CT> later_waves = q_zero<CT>();
-    for (int w2 = wave + 1; w2 < NW; ++w2) later_waves = qadd(later_waves, s_wsum[w2][c]);
-    const Q4<CT> tile_sum = qadd(shfl_q(sinc, c), later_waves);   // valid in wave 0
-    const Q4<CT> Sa = fenwick_exclusive<CT, WC, NW, false>(a, tc.chain, tc.pos, tile_sum, wave == 0, wave, r, c,
-                                                            pre_v, pre_ok, s_nodes, s_ok, s_after);
-    const Q4<CT> S_after = qadd(qadd(later_in_wave, later_waves), Sa);   // S just past the slice
+
+    // Exclusive prefix F (slices before k) and exclusive suffix R' (slices after k).
+    Q4<CT> F = q_one<CT>();
+    if (k > 0) {
+        F = s_sq[0][c];
+        for (int k2 = 1; k2 < k; ++k2) F = qmul(s_sq[k2][c], F);
+    }
+    Q4<CT> Rp = q_zero<CT>();
+    if (k < K - 1) {
+        Rp = s_sy[K - 1][c];
+        for (int k2 = K - 2; k2 > k; --k2) Rp = qadd(s_sy[k2][c], qcmul(s_sq[k2][c], Rp));
+    }
+    const Q4<CT> A = qmul(Ql, F);
+
+    // The tile's share of S in the global frame (meaningful in slice 0, which
+    // publishes it): conj(E) (x) (Y_0 + conj(Q_0) (x) R'_0).
+    Q4<CT> Yg = q_zero<CT>();
+    if (wave == 0) Yg = qcmul(Et, qadd(Yl, qcmul(Ql, Rp)));
+    const Q4<CT> Sa = fenwick_exclusive<CT, WC, NW, false>(a, tc.chain, tc.pos, Yg, wave == 0, wave, r, c, pre_v,
+                                                            pre_ok, s_nodes, s_ok, s_after);
 
     if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok)
-        IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Y, S_after));   // S[0]
+        IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Yg, Sa));   // S[0] (slice 0 of the first tile, E = 1)
 
     if (a.out != nullptr && tc.col_ok) {
-        const Q4<CT> Z = qscale(qmul(E, S_after), recip(qnorm2(E)));
-        const Q4<CT> C = qmul(E, IO::ct(init_raw));   // cum[t0-1]
-        Q4<CT> Sh = Yh;                                // Sh_t
+        const Q4<CT> Z = qscale(qmul(Et, Sa), recip(qnorm2(Et)));
+        const Q4<CT> C = qmul(Et, IO::ct(init_raw));           // cum before the tile
+        const Q4<CT> c0 = qmul(F, C);                          // cum[t0 - 1]
+        Q4<CT> cm = qmul(A, C);                                // cum[t0 + L - 1]
+        Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rp, qscale(qmul(A, Z), recip(qnorm2(A)))));
 #pragma unroll
-        for (int i = 0; i < L; ++i) {
-            if (!tc.full && tc.t0 + i >= a.s) break;
-            const Q4<CT> G = qmul(Lc[i], qadd(Sh, Z));
-            const Q4<CT> cprev = i == 0 ? C : qmul(Lc[i - 1], C);
-            IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qscale(qmulc(G, cprev), recip(qnorm2(Lc[i]))));
-            Sh = qsub(Sh, Xh[i]);
+        for (int i = L - 1; i >= 0; --i) {
+            const Q4<CT> qi = IO::ct_fresh(qv[i]);
+            const Q4<CT> cprev = i == 0 ? c0 : qscale(qcmul(qi, cm), recip(qnorm2(qi)));
+            if (tc.full || tc.t0 + i < a.s) IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qmulc(G, cprev));
+            if (i > 0) G = qadd(IO::ct_fresh(dv[i - 1]), qcmul(qi, G));
+            cm = cprev;
         }
     }
 }
