@@ -47,9 +47,8 @@
  * nothing was enqueued (except QC_ERR_HIP, which means a launch failed).
  *
  * Workspace: a device buffer of at least quat_cumprod_workspace_bytes(...)
- * bytes, holding a block ticket, a status word, self-validating cross-block
- * carries and (for a backward without saved boundary state) re-derived
- * boundary products.  Zero it once after allocation
+ * bytes, holding a status word, self-validating cross-block carries and (for
+ * a backward without saved boundary state) re-derived boundary products.  Zero it once after allocation
  * (quat_cumprod_workspace_init does so on a stream; hipMemset also works);
  * every call leaves it ready for the next one, whatever the shape.  Calls
  * sharing one workspace must be ordered (same stream or synchronised);
@@ -152,10 +151,8 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum,
 
 /* Synchronise `stream`, then read the workspace's device-side status word,
  * which accumulates over the calls since it was last cleared: 0 = every
- * cross-block wait completed; 1 = a wait hit its spin limit; 2 = a block drew
- * a ticket beyond its grid (the workspace was not zeroed after allocation).
- * Non-zero means results of some call since the last clear are invalid.
- * clear != 0 resets the word to 0. */
+ * cross-block wait completed; 1 = a wait hit its spin limit (results of some
+ * call since the last clear are invalid).  clear != 0 resets the word to 0. */
 int quat_cumprod_workspace_status(void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t clear, int32_t* status_out);
 

@@ -106,8 +106,9 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     p->n_cols = b * M;
     p->fwd = make_tiling(b, s, M, kFwdMaxWc, false);
     p->bwd = make_tiling(b, s, M, kBwdMaxWc, true);
-    // One block per tile; the 32-bit ticket and the grid bound the count.
-    const int64_t max_blocks = int64_t(1) << 24;
+    // One block per tile; the grid's work-item count is a 32-bit quantity
+    // (blocks have at most 512 threads).
+    const int64_t max_blocks = int64_t(1) << 22;
     if (!mul_ok(p->fwd.n_chains, p->fwd.n_tiles, max_blocks)) return QC_ERR_SHAPE;
     if (!mul_ok(p->bwd.n_chains, p->bwd.n_tiles, max_blocks)) return QC_ERR_SHAPE;
     if ((p->n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock > max_blocks) return QC_ERR_SHAPE;

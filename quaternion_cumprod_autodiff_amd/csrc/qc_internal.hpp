@@ -15,11 +15,11 @@ constexpr int kCkptStride = 64;
 // Bounded waits: a cross-block wait gives up after this many polls (each poll
 // is a few coherent loads plus a short sleep, about a microsecond, so well
 // under a second in all) and raises the workspace status word instead of
-// spinning forever.  Status 1 = a wait timed out, 2 = a ticket beyond the grid.
+// spinning forever.  Status 1 = a wait timed out.
 constexpr uint32_t kSpinLimit = 1u << 16;
 
 // Workspace header words.
-enum : int { kHdrTicket = 0, kHdrStatus = 2, kHdrWords = 64 };
+enum : int { kHdrStatus = 2, kHdrWords = 64 };
 
 // Tile geometry of the chunked path, by column-group width WC (a power of two
 // <= 64).  A wave holds R = 64/WC time slices of WC adjacent columns; a block

@@ -42,10 +42,16 @@
 // nothing is cleared between launches, and a slot read while it is being
 // written fails unless a 64-bit hash collides.  Publishing is therefore a handful of stores with no wait and
 // reading is one round trip, with no ready flag and no ordering between
-// words.  Block ids come from an atomic ticket, so a block only waits on
-// blocks that started before it; the block that draws the last ticket resets
-// the counter for the next launch.  Every wait is bounded (kSpinLimit) and
-// raises a status word instead of hanging.
+// words.
+//
+// Ordering.  Tile ids are the block index, position-major over the chains
+// (id = position * chains + chain), and a tile only ever waits on tiles of
+// smaller id.  Workgroups are dispatched in increasing id order (the grid is
+// dealt round-robin to the XCDs, and each dispatches its share in order), so
+// every resource a pending tile needs is held by tiles of smaller id, and the
+// smallest unfinished tile never waits on an unstarted one: the waits always
+// drain.  Every wait is still bounded (kSpinLimit) and raises a status word
+// instead of hanging.
 //
 // Arithmetic: float64 for float32 storage, float32 for bfloat16 storage.
 #include "qc_internal.hpp"
@@ -416,8 +422,13 @@ template <int WC, int L, int NW>
 __device__ __forceinline__ TileCoord tile_coord(const KernelArgs& a, uint32_t id, bool reverse, int k, int c) {
     constexpr int T = (64 / WC) * NW * L;
     TileCoord tc;
-    tc.chain = id % a.n_chains;
+    // Position-major ids; within one position the chains are rotated by the
+    // position, so consecutive tiles of a chain land on different XCDs (the
+    // grid is dealt round-robin to them) and no XCD streams a fixed subset of
+    // column groups.  Still monotone in position within a chain.
     tc.pos = id / a.n_chains;
+    const int64_t j = id % a.n_chains, rot = tc.pos % a.n_chains;
+    tc.chain = j >= rot ? j - rot : j - rot + a.n_chains;
     const int64_t tile = reverse ? a.n_tiles - 1 - tc.pos : tc.pos;
     tc.bi = tc.chain / a.n_cg;
     const int64_t cg = tc.chain % a.n_cg;
@@ -464,22 +475,10 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     __shared__ Q4<CT> s_nodes[NW * R][WC];
     __shared__ uint8_t s_ok[NW * R][WC];
     __shared__ Q4<CT> s_carry[WC];
-    __shared__ uint32_t s_id;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / WC, c = lane % WC;
-    if (tid == 0) {
-        const uint32_t id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // Every block of this launch has drawn once the last ticket is out:
-        // reset the counter for the next launch on this workspace.
-        if (id == a.n_blocks - 1) __hip_atomic_store(&a.hdr[kHdrTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_id = id;
-    }
-    __syncthreads();
-    if (s_id >= a.n_blocks) {   // workspace never zeroed: refuse to index with this ticket
-        if (tid == 0) __hip_atomic_store(&a.hdr[kHdrStatus], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
+    const uint32_t s_id = blockIdx.x;
     const TileCoord tc = tile_coord<WC, L, NW>(a, s_id, false, wave * R + r, c);
 
     Raw qv[L];
@@ -567,23 +566,11 @@ __global__ void __launch_bounds__(NW * 64, 3) bwd_chunked_kernel(KernelArgs a) {
     __shared__ Q4<CT> s_nodes[K][WC];
     __shared__ uint8_t s_ok[K][WC];
     __shared__ Q4<CT> s_after[WC];
-    __shared__ uint32_t s_id;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / WC, c = lane % WC;
     const int k = wave * R + r;
-    if (tid == 0) {
-        const uint32_t id = __hip_atomic_fetch_add(&a.hdr[kHdrTicket], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // Every block of this launch has drawn once the last ticket is out:
-        // reset the counter for the next launch on this workspace.
-        if (id == a.n_blocks - 1) __hip_atomic_store(&a.hdr[kHdrTicket], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_id = id;
-    }
-    __syncthreads();
-    if (s_id >= a.n_blocks) {   // workspace never zeroed: refuse to index with this ticket
-        if (tid == 0) __hip_atomic_store(&a.hdr[kHdrStatus], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
+    const uint32_t s_id = blockIdx.x;
     const TileCoord tc = tile_coord<WC, L, NW>(a, s_id, true, k, c);
 
     Raw qv[L], dv[L];

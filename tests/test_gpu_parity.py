@@ -215,8 +215,9 @@ def test_segment_chaining_on_device():
 
 
 def test_workspace_reuse_small_then_large_shapes():
-    """Regression: the flag area of one shape overlaps the carry area of
-    another; every call must clear its own flags before use."""
+    """Regression: the carry slots of one shape overlap other parts of the
+    workspace of another; slots left by earlier launches must never be
+    accepted as this launch's carries."""
     seq = [make_config("medium"), make_config("tiny"), make_config("medium"),
            make_inputs(1, 3000, 2, 8, "unit", "f32", seed=4), make_config("medium")]
     for inp in seq:
