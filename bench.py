@@ -110,7 +110,7 @@ def summarize_traffic(pmc_dir: str, copy_bytes: float):
         out.write("# Commands (run from /tmp, TMPDIR=/tmp, R = repository root):\n")
         for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
             out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $R/gpurun_out/pmc/{ctr} -o run -- "
-                      f"python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline\n")
+                      f"python3 $R/bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline\n")
             out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $R/gpurun_out/pmc/copy_{ctr} -o run -- "
                       f"python3 $R/bench.py --copy-calibration --steps 2 --warmup 1\n")
         out.write(f"#   python3 $R/bench.py --summarize-traffic $R/gpurun_out/pmc\n")
