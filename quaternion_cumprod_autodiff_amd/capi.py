@@ -99,6 +99,8 @@ def _check(rc: int, where: str):
 
 
 def _dims(q: torch.Tensor):
+    if not q.is_cuda:
+        raise ValueError("q must live on the GPU: the scan runs only in the HIP library, there is no CPU path")
     if q.dim() != 5 or q.shape[-1] != 4:
         raise ValueError(f"q must be [b, s, h, j, 4], got {tuple(q.shape)}")
     b, s, h, j, _ = q.shape

@@ -177,3 +177,17 @@ def test_workspace_helpers_validate(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         capi.load(str(tmp_path / "missing.so"))
+
+
+def test_cpu_tensors_are_refused_not_computed():
+    """There is no CPU path: host tensors raise before any library call."""
+    import torch
+    from quaternion_cumprod_autodiff_amd.autograd import quat_cumprod
+    q = torch.zeros(1, 4, 1, 1, 4)
+    init = torch.zeros(1, 1, 1, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        quat_cumprod(q, init)
+    with pytest.raises(ValueError, match="GPU"):
+        capi.quat_cumprod_fwd(q, init)
+    with pytest.raises(ValueError, match="GPU"):
+        capi.quat_cumprod_bwd(q, init, q)
