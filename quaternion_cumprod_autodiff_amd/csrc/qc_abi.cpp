@@ -21,18 +21,16 @@ using qc::kCkptStride;
 thread_local std::string g_last_hip_error;
 
 // Epochs enter the check word of every carry slot a launch writes.  The
-// counter starts at a random value so that slots a different process left in
-// recycled memory are not expected to match, and skips 0.
-uint32_t next_epoch() {
-    static std::atomic<uint32_t> counter{[] {
+// 64-bit counter never wraps in practice, so a slot left by an earlier launch
+// of this process can never carry the current epoch; it starts at a random
+// value so that slots another process left in recycled memory are not
+// expected to match either.
+uint64_t next_epoch() {
+    static std::atomic<uint64_t> counter{[] {
         std::random_device rd;
-        return static_cast<uint32_t>(rd());
+        return (static_cast<uint64_t>(rd()) << 32) ^ static_cast<uint64_t>(rd());
     }()};
-    uint32_t e;
-    do {
-        e = counter.fetch_add(1, std::memory_order_relaxed);
-    } while (e == 0);
-    return e;
+    return counter.fetch_add(1, std::memory_order_relaxed);
 }
 
 int hip_fail(hipError_t e) {
@@ -80,12 +78,12 @@ int column_group_width(int64_t M, int cap) {
     return w;
 }
 
-Tiling make_tiling(int64_t b, int64_t s, int64_t M, int cap, bool backward) {
+Tiling make_tiling(int64_t b, int64_t s, int64_t M, int cap, int dtype, bool backward) {
     Tiling t;
     t.wc = column_group_width(M, cap);
     t.n_cg = (M + t.wc - 1) / t.wc;
     t.n_chains = b * t.n_cg;
-    const int64_t steps = backward ? qc::bwd_tile_steps(t.wc) : qc::fwd_tile_steps(t.wc);
+    const int64_t steps = backward ? qc::bwd_tile_steps(t.wc, dtype) : qc::fwd_tile_steps(t.wc, dtype);
     t.n_tiles = (s + steps - 1) / steps;
     return t;
 }
@@ -104,8 +102,8 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     p->ct_bytes = dtype == QC_DTYPE_F32 ? 32 : 16;
     p->slot_bytes = dtype == QC_DTYPE_F32 ? 40 : 24;
     p->n_cols = b * M;
-    p->fwd = make_tiling(b, s, M, kFwdMaxWc, false);
-    p->bwd = make_tiling(b, s, M, kBwdMaxWc, true);
+    p->fwd = make_tiling(b, s, M, kFwdMaxWc, dtype, false);
+    p->bwd = make_tiling(b, s, M, kBwdMaxWc, dtype, true);
     // One block per tile; the grid's work-item count is a 32-bit quantity
     // (blocks have at most 512 threads).
     const int64_t max_blocks = int64_t(1) << 22;

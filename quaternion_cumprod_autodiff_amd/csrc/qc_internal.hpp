@@ -22,28 +22,43 @@ constexpr uint32_t kSpinLimit = 1u << 16;
 enum : int { kHdrStatus = 2, kHdrWords = 64 };
 
 // Tile geometry of the chunked path, by column-group width WC (a power of two
-// <= 64).  A wave holds R = 64/WC time slices of WC adjacent columns; a block
-// has NW waves; every lane owns L consecutive steps of one column.  A tile is
-// WC columns x (R*NW*L) steps.  The forward tile length is 128 steps and the
-// backward one 64 = kCkptStride, so backward tiles start on saved boundaries.
+// <= 64) and storage dtype.  A wave holds R = 64/WC time slices of WC adjacent
+// columns; a block has NW waves; every lane owns L consecutive steps of one
+// column.  A tile is WC columns x (R*NW*L) steps.  Backward tiles are a
+// multiple of kCkptStride steps, so they start on saved boundaries, and every
+// L divides kCkptStride, so some forward slice starts on each boundary.
+// bfloat16 quaternions are half the size, so their slices are twice as long
+// for the same registers (and half as many tiles share the fixed costs).
 struct Geometry {
     int wc;
     int fwd_l, fwd_nw;
     int bwd_l, bwd_nw;
 };
 
-constexpr Geometry geometry_for(int wc) {
-    return wc == 64 ? Geometry{64, 16, 8, 8, 8}
+constexpr Geometry geometry_for(int wc, int dtype) {
+    return dtype == 0
+        ? (wc == 64 ? Geometry{64, 16, 8, 8, 8}
          : wc == 32 ? Geometry{32, 16, 4, 8, 4}
          : wc == 16 ? Geometry{16, 16, 2, 8, 2}
          : wc == 8  ? Geometry{8, 16, 1, 8, 1}
          : wc == 4  ? Geometry{4, 8, 1, 4, 1}
          : wc == 2  ? Geometry{2, 4, 1, 2, 1}
-         :            Geometry{1, 2, 1, 1, 1};
+         :            Geometry{1, 2, 1, 1, 1})
+        : (wc == 64 ? Geometry{64, 32, 8, 16, 8}
+         : wc == 32 ? Geometry{32, 32, 4, 16, 4}
+         : wc == 16 ? Geometry{16, 32, 2, 16, 2}
+         : wc == 8  ? Geometry{8, 32, 1, 16, 1}
+         : wc == 4  ? Geometry{4, 16, 1, 8, 1}
+         : wc == 2  ? Geometry{2, 8, 1, 4, 1}
+         :            Geometry{1, 4, 1, 2, 1});
 }
 
-constexpr int fwd_tile_steps(int wc) { return (64 / wc) * geometry_for(wc).fwd_nw * geometry_for(wc).fwd_l; }
-constexpr int bwd_tile_steps(int wc) { return (64 / wc) * geometry_for(wc).bwd_nw * geometry_for(wc).bwd_l; }
+constexpr int fwd_tile_steps(int wc, int dtype) {
+    return (64 / wc) * geometry_for(wc, dtype).fwd_nw * geometry_for(wc, dtype).fwd_l;
+}
+constexpr int bwd_tile_steps(int wc, int dtype) {
+    return (64 / wc) * geometry_for(wc, dtype).bwd_nw * geometry_for(wc, dtype).bwd_l;
+}
 
 // Arguments of every scan kernel (passed by value).
 struct KernelArgs {
@@ -60,9 +75,9 @@ struct KernelArgs {
     int64_t n_cg;         // column groups per batch entry
     int64_t n_chains;     // b * n_cg
     int64_t n_tiles;      // tiles per chain
+    uint64_t epoch;       // this launch's epoch, folded into every check word
     uint32_t n_blocks;    // grid size
     uint32_t spin_limit;
-    uint32_t epoch;       // this launch's epoch, folded into every check word (never 0)
 };
 
 hipError_t launch_fwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_t st);

@@ -150,6 +150,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // loads and stores are non-temporal (they would only evict useful lines).
 // float32 storage: one 16-byte vector per quaternion; float64 arithmetic.
 struct IoF32 {
+    static constexpr int kDtype = 0;
     using CT = double;
     using Raw = f32x4;
     static __device__ __forceinline__ Raw load(const void* base, int64_t idx) {
@@ -183,6 +184,7 @@ struct IoF32 {
 
 // bfloat16 storage: 4 x 16-bit patterns (8 B) per quaternion; float32 arithmetic.
 struct IoBF16 {
+    static constexpr int kDtype = 1;
     using CT = float;
     using Raw = u32x2;
     static __device__ __forceinline__ Raw load(const void* base, int64_t idx) {
@@ -246,8 +248,8 @@ constexpr int slot_words() { return SlotLayout<T>::kValueWords + 1; }
 // writes matches with probability about 2^-63 whatever the bit patterns; the
 // low bit is forced to 1 so a zeroed slot never matches.
 template <int NV>
-__device__ __forceinline__ SlotWord check_word(const SlotWord* v, uint32_t epoch) {
-    SlotWord h = SlotWord(epoch) * 0x9E3779B97F4A7C15ull;
+__device__ __forceinline__ SlotWord check_word(const SlotWord* v, uint64_t epoch) {
+    SlotWord h = epoch * 0x9E3779B97F4A7C15ull;   // odd multiplier: distinct epochs, distinct seeds
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         h = (h ^ v[k]) * 0xFF51AFD7ED558CCDull;
@@ -746,7 +748,8 @@ __global__ void zero_words_kernel(uint32_t* p, size_t n) {
 
 template <class IO, int WC>
 hipError_t launch_fwd_wc(const KernelArgs& a, hipStream_t st) {
-    constexpr Geometry g = geometry_for(WC);
+    constexpr Geometry g = geometry_for(WC, IO::kDtype);
+    static_assert(kCkptStride % g.fwd_l == 0, "a forward slice must start on every saved boundary");
     KernelArgs args = a;
     void* params[] = {&args};
     return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw>),
@@ -755,7 +758,8 @@ hipError_t launch_fwd_wc(const KernelArgs& a, hipStream_t st) {
 
 template <class IO, int WC>
 hipError_t launch_bwd_wc(const KernelArgs& a, hipStream_t st) {
-    constexpr Geometry g = geometry_for(WC);
+    constexpr Geometry g = geometry_for(WC, IO::kDtype);
+    static_assert(bwd_tile_steps(WC, IO::kDtype) % kCkptStride == 0, "backward tiles start on saved boundaries");
     KernelArgs args = a;
     void* params[] = {&args};
     return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_l, g.bwd_nw>),
