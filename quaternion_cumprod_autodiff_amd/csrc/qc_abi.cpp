@@ -65,11 +65,20 @@ struct Plan {
 };
 
 // Widest column group each kernel uses.  Groups of 32 columns make 4-wave
-// blocks on wide rows, so that (at 2-3 waves per SIMD for these register
-// counts) two or three blocks share a compute unit and overlap their load,
-// compute and carry-wait phases; wider groups would leave one block per CU.
+// blocks on wide rows, so that (at 3 waves per SIMD for these register
+// counts) three blocks share a compute unit and overlap their load, compute
+// and carry-wait phases.
 constexpr int kFwdMaxWc = 32;
 constexpr int kBwdMaxWc = 32;
+
+// The forward can also take 64-column groups with half-height tiles (same
+// tile size, 1 KiB per row read instead of 512 B, measured a few percent
+// faster), but that doubles the tiles per chain.  It is used only while
+// there are at least this many chains, i.e. few tiles of each chain in
+// flight at once; deep chains keep 32-column groups and their shorter
+// carry look-backs.
+constexpr int kFwdWideWc = 64;
+constexpr int64_t kFwdWideMinChains = 64;
 
 int column_group_width(int64_t M, int cap) {
     if (M >= cap) return cap;
@@ -103,6 +112,8 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     p->slot_bytes = dtype == QC_DTYPE_F32 ? 40 : 24;
     p->n_cols = b * M;
     p->fwd = make_tiling(b, s, M, kFwdMaxWc, dtype, false);
+    if (M >= kFwdWideWc && b * ((M + kFwdWideWc - 1) / kFwdWideWc) >= kFwdWideMinChains)
+        p->fwd = make_tiling(b, s, M, kFwdWideWc, dtype, false);
     p->bwd = make_tiling(b, s, M, kBwdMaxWc, dtype, true);
     // One block per tile; the grid's work-item count is a 32-bit quantity
     // (blocks have at most 512 threads).

@@ -37,14 +37,14 @@ struct Geometry {
 
 constexpr Geometry geometry_for(int wc, int dtype) {
     return dtype == 0
-        ? (wc == 64 ? Geometry{64, 16, 8, 8, 8}
+        ? (wc == 64 ? Geometry{64, 16, 4, 8, 8}
          : wc == 32 ? Geometry{32, 16, 4, 8, 4}
          : wc == 16 ? Geometry{16, 16, 2, 8, 2}
          : wc == 8  ? Geometry{8, 16, 1, 8, 1}
          : wc == 4  ? Geometry{4, 8, 1, 4, 1}
          : wc == 2  ? Geometry{2, 4, 1, 2, 1}
          :            Geometry{1, 2, 1, 1, 1})
-        : (wc == 64 ? Geometry{64, 32, 8, 16, 8}
+        : (wc == 64 ? Geometry{64, 32, 4, 16, 8}
          : wc == 32 ? Geometry{32, 32, 4, 16, 4}
          : wc == 16 ? Geometry{16, 32, 2, 16, 2}
          : wc == 8  ? Geometry{8, 32, 1, 16, 1}

@@ -137,6 +137,17 @@ def test_many_tiles_ragged(s, hj):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("b,s,h,j", [(64, 300, 5, 13), (32, 129, 8, 16), (128, 65, 1, 64)])
+def test_wide_forward_groups(dtype, b, s, h, j):
+    """Many chains switch the forward to 64-column groups with half-height
+    tiles: partial groups (h*j not a multiple of 64) and ragged tails."""
+    inp = make_inputs(b, s, h, j, "unit", dtype, seed=b + s + h * j)
+    print(f"[wide b={b} s={s} h={h} j={j} {dtype}]", flush=True)
+    compare(inp)
+    compare(inp, use_ckpt=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_non_unit_steps(dtype):
     """Off the unit sphere the division by |P_t|^2 keeps the closed form exact."""
     inp = make_inputs(2, 400, 4, 8, "scaled", dtype, seed=3)
