@@ -35,7 +35,9 @@ if ROOT not in sys.path:
 
 METRIC = "quat cumprod fwd+bwd GB/s and % HBM peak, b8·s4096·h32·j32 fp32"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "quaternion_cumprod_autodiff_amd", "csrc", "qc_kernels.hip")
+# Sources that define the kernels and their launch shapes (code, tile geometry, planning).
+KERNEL_SOURCES = [os.path.join(ROOT, "quaternion_cumprod_autodiff_amd", "csrc", f)
+                  for f in ("qc_kernels.hip", "qc_internal.hpp", "qc_abi.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline.txt")
 WORKLOAD_KEY = "headline b8 s4096 h32 j32 f32 I/O, forward + backward"
 
@@ -45,8 +47,11 @@ def log(*a):
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_kv(path: str) -> dict:
