@@ -12,9 +12,10 @@ quaternions.
 Timing: W untimed warm-up steps, continued until --settle-ms of sustained
 load has passed (the first tens of ms after idle run at unsettled clocks),
 then K timed steps between two device synchronisations.  Inside the timed
-region HIP events bracket every backward launch on its stream (the roofline
-figure); a short loop after it brackets both kernels for the forward /
-backward split.
+region HIP events bracket every N-th backward launch on its stream (the
+roofline figure; N = --event-every, 4 by default, since each event pair idles
+the GPU for a few us); a short loop after it brackets both kernels for the
+forward / backward split.
 
 Reported value: algorithmic bytes per step (32 B/quaternion forward + 48 B
 backward, plus 16 B per column for init and d_init) / wall time per step.
@@ -184,6 +185,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the backward's event records (each adds a few us of idle)")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="bracket every N-th timed backward with events (N=1: every one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device copy of one [b,s,h,j,4] tensor")
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
@@ -249,25 +252,29 @@ def main():
     if status != 0:
         raise RuntimeError("a cross-block wait hit its spin limit during warm-up")
 
-    # Timed region: K steps.  Events bracket the backward (the dominant kernel)
-    # on the stream it is launched on (the current stream).
+    # Timed region: K steps.  Events bracket every N-th backward (the dominant
+    # kernel) on the stream it is launched on (the current stream); each event
+    # pair leaves the GPU idle for a few us, so sampling keeps that cost out of
+    # most steps while the average still covers launches across the region.
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-    be = [(ev(), ev()) for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    timed_k = [] if args.no_kernel_events else list(range(every - 1, args.steps, every))
+    be = {k: (ev(), ev()) for k in timed_k}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         fwd()
-        if args.no_kernel_events:
+        if k in be:
+            be[k][0].record()
             bwd()
-            continue
-        be[k][0].record()
-        bwd()
-        be[k][1].record()
+            be[k][1].record()
+        else:
+            bwd()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if capi.default_workspace.status(dev) != 0:
         raise RuntimeError("a cross-block wait hit its spin limit during the timed steps")
-    bwd_ms = None if args.no_kernel_events else float(np.mean([a.elapsed_time(bb) for a, bb in be]))
+    bwd_ms = float(np.mean([a.elapsed_time(bb) for a, bb in be.values()])) if be else None
 
     # Diagnostics after the timed region: forward and backward each bracketed.
     diag = [((ev(), ev()), (ev(), ev())) for _ in range(20)]
@@ -313,6 +320,7 @@ def main():
         "elements_per_s": round(n / (ms_step * 1e-3), 1),
         "untimed_steps": warm_steps,
         "bwd_ms": round(bwd_ms, 4) if bwd_ms is not None else None,
+        "bwd_launches_timed": len(be),
         "diag_fwd_ms": round(fwd_ms, 4),
         "diag_bwd_ms": round(bwd_ms_diag, 4),
         "diag_fwd_GBps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 2),
