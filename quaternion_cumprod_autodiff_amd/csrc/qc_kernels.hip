@@ -146,8 +146,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// The [b,s,h,j,4] tensors are streamed exactly once per kernel, so their
-// loads and stores are non-temporal (they would only evict useful lines).
+// The [b,s,h,j,4] tensors are streamed once per kernel, so their stores and
+// the cotangent loads are non-temporal (they would only evict useful lines).
+// The chunked kernels read q with the default policy: the backward walks the
+// sequence in reverse, so when it runs right after the forward on the same q
+// (a step, or a segment recomputed for its backward) it starts on the tiles
+// the forward read last, which the memory-side cache still holds, and the
+// next forward starts where the backward ended (about 1% per step measured).
 // float32 storage: one 16-byte vector per quaternion; float64 arithmetic.
 struct IoF32 {
     static constexpr int kDtype = 0;
@@ -486,11 +491,11 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     Raw qv[L];
     if (tc.full) {
 #pragma unroll
-        for (int i = 0; i < L; ++i) qv[i] = IO::load_stream(a.q, tc.base + int64_t(i) * a.M);
+        for (int i = 0; i < L; ++i) qv[i] = IO::load(a.q, tc.base + int64_t(i) * a.M);
     } else {
 #pragma unroll
         for (int i = 0; i < L; ++i)
-            qv[i] = (tc.col_ok && tc.t0 + i < a.s) ? IO::load_stream(a.q, tc.base + int64_t(i) * a.M)
+            qv[i] = (tc.col_ok && tc.t0 + i < a.s) ? IO::load(a.q, tc.base + int64_t(i) * a.M)
                                                     : IO::one_raw();
     }
     Raw init_raw = IO::one_raw();
@@ -579,14 +584,14 @@ __global__ void __launch_bounds__(NW * 64, 3) bwd_chunked_kernel(KernelArgs a) {
     if (tc.full) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            qv[i] = IO::load_stream(a.q, tc.base + int64_t(i) * a.M);
+            qv[i] = IO::load(a.q, tc.base + int64_t(i) * a.M);
             dv[i] = IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const bool ok = tc.col_ok && tc.t0 + i < a.s;
-            qv[i] = ok ? IO::load_stream(a.q, tc.base + int64_t(i) * a.M) : IO::one_raw();
+            qv[i] = ok ? IO::load(a.q, tc.base + int64_t(i) * a.M) : IO::one_raw();
             dv[i] = ok ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M) : IO::zero_raw();
         }
     }
