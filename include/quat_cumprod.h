@@ -18,8 +18,9 @@
  * states the closed form for unit quaternions (|P_t| = 1); the division by
  * |P_t|^2 keeps it the exact VJP of the given, rounded inputs, which are never
  * exactly unit.  It requires every prefix product P_t to be non-zero in the
- * working precision (no exactly-zero step q_t); results are not finite
- * otherwise.
+ * working precision (no exactly-zero step q_t); otherwise the backward's
+ * results are not finite and the workspace status reports QC_STATUS_ZERO (the
+ * forward is exact for any input).
  *
  * Any gradient of the final carry cum[:, s-1] must already be added into
  * d_cum[:, s-1]: the page folds it there before the backward node runs, so the
@@ -149,10 +150,20 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum,
                         void* workspace, size_t workspace_bytes, void* stream,
                         const qc_options* opts);
 
-/* Synchronise `stream`, then read the workspace's device-side status word,
- * which accumulates over the calls since it was last cleared: 0 = every
- * cross-block wait completed; 1 = a wait hit its spin limit (results of some
- * call since the last clear are invalid).  clear != 0 resets the word to 0. */
+/* Synchronise `stream`, then read the workspace's device-side status word, a
+ * bit mask accumulated over the calls since it was last cleared:
+ *   0                   every call completed normally;
+ *   QC_STATUS_TIMEOUT   a cross-block wait hit its spin limit: results of some
+ *                       call since the last clear are invalid;
+ *   QC_STATUS_ZERO      a backward met a prefix product that is exactly zero
+ *                       (a zero step q_t, or an underflow to zero), outside the
+ *                       documented precondition: its d_q / d_init hold
+ *                       non-finite values.
+ * clear != 0 resets the word to 0. */
+enum {
+    QC_STATUS_TIMEOUT = 1,
+    QC_STATUS_ZERO = 2
+};
 int quat_cumprod_workspace_status(void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t clear, int32_t* status_out);
 

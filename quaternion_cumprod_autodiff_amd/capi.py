@@ -174,6 +174,8 @@ class Workspace:
         return buf
 
     def status(self, device: torch.device, stream=None, clear: bool = True) -> int:
+        """Sticky status bits of this device's workspace since the last clear
+        (0 = normal; QC_STATUS_TIMEOUT = 1, QC_STATUS_ZERO = 2, see the C header)."""
         idx = device.index if device.index is not None else torch.cuda.current_device()
         buf = self._buf.get(idx)
         if buf is None:

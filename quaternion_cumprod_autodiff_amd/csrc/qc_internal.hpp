@@ -15,11 +15,15 @@ constexpr int kCkptStride = 64;
 // Bounded waits: a cross-block wait gives up after this many polls (each poll
 // is a few coherent loads plus a short sleep, about a microsecond, so well
 // under a second in all) and raises the workspace status word instead of
-// spinning forever.  Status 1 = a wait timed out.
+// spinning forever.
 constexpr uint32_t kSpinLimit = 1u << 16;
 
-// Workspace header words.
+// Workspace header words, and the bits of the sticky status word.
 enum : int { kHdrStatus = 2, kHdrWords = 64 };
+enum : uint32_t {
+    kStatusWaitTimeout = 1u,   // a cross-block wait hit kSpinLimit
+    kStatusZeroPrefix = 2u,    // a prefix product was exactly zero: the backward's results are not finite
+};
 
 // Tile geometry of the chunked path, by column-group width WC (a power of two
 // <= 64) and storage dtype.  A wave holds R = 64/WC time slices of WC adjacent

@@ -323,7 +323,7 @@ __device__ __forceinline__ Q4<T> wait_read(const KernelArgs& a, const SlotWord* 
             __builtin_amdgcn_s_sleep(64);
         }
         if (++polls > a.spin_limit) {
-            __hip_atomic_store(&a.hdr[kHdrStatus], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
     }
@@ -642,11 +642,16 @@ __global__ void __launch_bounds__(NW * 64, 3) bwd_chunked_kernel(KernelArgs a) {
         IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Yg, Sa));   // S[0] (slice 0 of the first tile, E = 1)
 
     if (a.out != nullptr && tc.col_ok) {
-        const Q4<CT> Z = qscale(qmul(Et, Sa), recip(qnorm2(Et)));
+        const CT nE = qnorm2(Et), nA = qnorm2(A);
+        // A zero step makes every later prefix product exactly zero, which shows
+        // up here (E for later tiles, A for its own and later slices of this tile).
+        if (nE == CT(0) || nA == CT(0))
+            __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusZeroPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const Q4<CT> Z = qscale(qmul(Et, Sa), recip(nE));
         const Q4<CT> C = qmul(Et, IO::ct(init_raw));           // cum before the tile
         const Q4<CT> c0 = qmul(F, C);                          // cum[t0 - 1]
         Q4<CT> cm = qmul(A, C);                                // cum[t0 + L - 1]
-        Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rp, qscale(qmul(A, Z), recip(qnorm2(A)))));
+        Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rp, qscale(qmul(A, Z), recip(nA))));
 #pragma unroll
         for (int i = L - 1; i >= 0; --i) {
             const Q4<CT> qi = IO::ct_fresh(qv[i]);
@@ -722,6 +727,7 @@ __global__ void __launch_bounds__(kColumnBlock) bwd_column_kernel(KernelArgs a) 
     // Pass 2: the closed form step by step, S[t+1] = S[t] - conj(P_t) (x) d_t.
     Q4<CT> cm = IO::ct(IO::load(a.init, bi * a.M + m));   // cum[-1] = init
     P = q_one<CT>();
+    bool zero = false;
     for (int64_t t0 = 0; t0 < a.s; t0 += U) {
         Raw qv[U], dv[U];
 #pragma unroll
@@ -736,12 +742,16 @@ __global__ void __launch_bounds__(kColumnBlock) bwd_column_kernel(KernelArgs a) 
             if (t >= a.s) break;
             const Q4<CT> qq = IO::ct(qv[i]);
             P = qmul(qq, P);
-            const Q4<CT> G = qscale(qmul(P, S), recip(qnorm2(P)));
+            const CT nP = qnorm2(P);
+            zero = zero || nP == CT(0);
+            const Q4<CT> G = qscale(qmul(P, S), recip(nP));
             IO::store_stream(a.out, base + t * a.M, qmulc(G, cm));
             S = qsub(S, qcmul(P, IO::ct(dv[i])));
             cm = qmul(qq, cm);
         }
     }
+    if (zero)
+        __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusZeroPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void zero_words_kernel(uint32_t* p, size_t n) {

@@ -234,3 +234,23 @@ def test_workspace_reuse_small_then_large_shapes():
     for inp in seq:
         print(f"[reuse b={inp.b} s={inp.s} h={inp.h} j={inp.j}]", flush=True)
         compare(inp, path="chunked", use_ckpt=False)
+
+
+@pytest.mark.parametrize("path", ["chunked", "column"])
+def test_zero_step_is_reported(path):
+    """A step that is exactly zero makes every later prefix product zero: the
+    forward stays exact, and the backward (whose exact form divides by |P_t|^2)
+    raises the status bit instead of failing silently."""
+    inp = make_inputs(2, 300, 2, 4, "unit", "f32", seed=77)
+    inp.q[1, 170, 1, 2] = 0.0
+    inp.q64[1, 170, 1, 2] = 0.0
+    q, init, d = to_dev(inp.q, "f32"), to_dev(inp.init, "f32"), to_dev(inp.d_cum, "f32")
+    print(f"[zero step {path}]", flush=True)
+    ws = capi.Workspace()
+    ck = capi.new_ckpt(q)
+    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, workspace=ws)
+    assert ws.status(q.device) == 0
+    check("cum", to_f64(cum), oracle.fwd(inp.q64, inp.init64), "f32", inp.s)
+    capi.quat_cumprod_bwd(q, init, d, ck, path=path, workspace=ws)
+    assert ws.status(q.device) == 2            # QC_STATUS_ZERO, and cleared by the read
+    assert ws.status(q.device) == 0
