@@ -33,16 +33,16 @@
 //
 // Publication protocol.  Each column's carry in a node is a slot of 64-bit
 // words: the value bits followed by one check word, a hash of the value words
-// and of the launch epoch.  The slot is written with agent-scope atomic stores and read with
-// agent-scope atomic loads (coherent accesses that bypass the per-XCD L2, so
-// no L2 write-back or invalidate is ever needed: on this chip those cost
-// more than the scan itself).  A reader accepts a slot when its check word
-// matches its value words and the current epoch.  Slots left by earlier
-// launches fail (their epoch differs; a zeroed slot can never match), so
-// nothing is cleared between launches, and a slot read while it is being
-// written fails unless a 64-bit hash collides.  Publishing is therefore a handful of stores with no wait and
-// reading is one round trip, with no ready flag and no ordering between
-// words.
+// and of the launch epoch.  The slot is written with agent-scope atomic stores
+// and read with agent-scope atomic loads (coherent accesses that bypass the
+// per-XCD L2, so no L2 write-back or invalidate is ever needed: on this chip
+// those cost more than the scan itself).  A reader accepts a slot when its
+// check word matches its value words and the current epoch.  Slots left by
+// earlier launches fail (their epoch differs; a zeroed slot can never match),
+// so nothing is cleared between launches, and a slot read while it is being
+// written fails unless a 64-bit hash collides.  Publishing is therefore a
+// handful of stores with no wait, and reading is one round trip, with no
+// ready flag and no ordering between words.
 //
 // Ordering.  Tile ids are the block index, position-major over the chains
 // (id = position * chains + chain), and a tile only ever waits on tiles of
@@ -348,9 +348,9 @@ __device__ __forceinline__ SlotWord* slot_ptr(const KernelArgs& a, int64_t node,
 }
 
 // First-round read attempt, issued right after the tile's data loads so that
-// its latency overlaps them and sweep 1: in steady state the predecessor
-// tiles have already published by then.  Slots are write-once per launch, so
-// an early successful read is final; a failed one is retried later.
+// its latency overlaps theirs; predecessor tiles that started long enough
+// before have published by then.  Slots are write-once per launch, so an
+// early successful read is final; a failed one is retried in the look-back.
 template <typename T, int WC, int NW>
 __device__ __forceinline__ bool fenwick_prefetch(const KernelArgs& a, int64_t chain, int64_t pos, int slot, int c,
                                                  Q4<T>* v) {
