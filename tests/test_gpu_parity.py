@@ -206,6 +206,36 @@ def test_side_stream_and_workspace_reuse_across_shapes():
             check(name, to_f64(g), rr, "f32", inp.s)
 
 
+def test_concurrent_streams_with_separate_workspaces():
+    """Two streams run interleaved forward + backward passes on different
+    inputs at the same time, each with its own workspace (the documented rule
+    for concurrent calls); both must match the oracle."""
+    shapes = [(4, 2048, 16, 16, "unit", "f32", 101), (2, 6000, 4, 8, "drift", "f32", 102)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for (b, s, h, j, recipe, dtype, seed), st in zip(shapes, streams):
+        inp = make_inputs(b, s, h, j, recipe, dtype, seed=seed)
+        q, init, d = to_dev(inp.q, dtype), to_dev(inp.init, dtype), to_dev(inp.d_cum, dtype)
+        runs.append(dict(inp=inp, q=q, init=init, d=d, st=st, ws=capi.Workspace(), out=[]))
+    torch.cuda.synchronize()
+    for it in range(3):
+        for rn in runs:
+            with torch.cuda.stream(rn["st"]):
+                ck = capi.new_ckpt(rn["q"])
+                cum = capi.quat_cumprod_fwd(rn["q"], rn["init"], ckpt=ck, stream=rn["st"], workspace=rn["ws"])
+                d_q, d_init = capi.quat_cumprod_bwd(rn["q"], rn["init"], rn["d"], ck, stream=rn["st"],
+                                                    workspace=rn["ws"])
+                rn["out"].append((cum, d_q, d_init))
+    torch.cuda.synchronize()
+    for rn in runs:
+        assert rn["ws"].status(rn["q"].device, rn["st"]) == 0
+        ref = reference(rn["inp"])
+        print(f"[concurrent b={rn['inp'].b} s={rn['inp'].s}]", flush=True)
+        for outs in rn["out"]:
+            for name, g, r in zip(("cum", "d_q", "d_init"), outs, ref):
+                check(name, to_f64(g), r, "f32", rn["inp"].s)
+
+
 def test_segment_chaining_on_device():
     """The final carry of one segment is the init of the next; the backward of
     the tail hands d_init back into the head's last cotangent."""
