@@ -113,13 +113,13 @@ def summarize_traffic(pmc_dir: str, copy_bytes: float):
         out.write("# HBM traffic per launch of the scan kernels, headline workload (b8 s4096 h32 j32, f32 I/O).\n")
         out.write("# Counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), each\n")
         out.write("# scaled by bytes / reading of the same counter for a plain device copy of one tensor.\n")
-        out.write("# Commands (run from /tmp, TMPDIR=/tmp, R = repository root):\n")
+        out.write("# Commands (run from /tmp, TMPDIR=/tmp, R = repository root, OUT = an output directory):\n")
         for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
-            out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $R/gpurun_out/pmc/{ctr} -o run -- "
+            out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $OUT/pmc/{ctr} -o run -- "
                       f"python3 $R/bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline\n")
-            out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $R/gpurun_out/pmc/copy_{ctr} -o run -- "
+            out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $OUT/pmc/copy_{ctr} -o run -- "
                       f"python3 $R/bench.py --copy-calibration --steps 2 --warmup 1\n")
-        out.write(f"#   python3 $R/bench.py --summarize-traffic $R/gpurun_out/pmc\n")
+        out.write(f"#   python3 $R/bench.py --summarize-traffic $OUT/pmc\n")
         for k, v in rec.items():
             out.write(f"{k} = {v}\n")
     print(json.dumps(rec))
@@ -200,7 +200,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(columns shard across GPUs without communication; see DESIGN.md)", file=sys.stderr)
+              "(columns shard across GPUs without communication)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
