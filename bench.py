@@ -19,6 +19,8 @@ forward / backward split.
 
 Reported value: algorithmic bytes per step (32 B/quaternion forward + 48 B
 backward, plus 16 B per column for init and d_init) / wall time per step.
+The line also reports the leaves-only mode (no saved boundary state; the
+backward re-derives it from q), timed after the main region.
 The last stdout line is one JSON record; diagnostics go to stderr.
 """
 from __future__ import annotations
@@ -185,6 +187,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the backward's event records (each adds a few us of idle)")
+    ap.add_argument("--leaves-steps", type=int, default=50,
+                    help="after the timed region, also time this many leaves-only steps (0: skip)")
     ap.add_argument("--event-every", type=int, default=4,
                     help="bracket every N-th timed backward with events (N=1: every one)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -289,6 +293,31 @@ def main():
     fwd_ms = float(np.median([f0.elapsed_time(f1) for (f0, f1), _ in diag]))
     bwd_ms_diag = float(np.median([b0.elapsed_time(b1) for _, (b0, b1) in diag]))
 
+    # The page-faithful mode, reported beside the timed one: the forward saves
+    # nothing beyond the leaves and the backward re-derives the boundary state
+    # from q (one more read of q).  Same workload, same algorithmic bytes.
+    leaves = None
+    if not args.leaves_only and args.leaves_steps > 0:
+        def fwd_lo():
+            capi.quat_cumprod_fwd(q, init, cum, None, path=args.path)
+
+        def bwd_lo():
+            capi.quat_cumprod_bwd(q, init, d_cum, None, d_q=d_q, d_init=d_init, path=args.path)
+
+        for _ in range(10):
+            fwd_lo()
+            bwd_lo()
+        torch.cuda.synchronize()
+        t_lo = time.perf_counter()
+        for _ in range(args.leaves_steps):
+            fwd_lo()
+            bwd_lo()
+        torch.cuda.synchronize()
+        ms_lo = (time.perf_counter() - t_lo) / args.leaves_steps * 1e3
+        if capi.default_workspace.status(dev) != 0:
+            raise RuntimeError("a cross-block wait hit its spin limit during the leaves-only steps")
+        leaves = ms_lo
+
     ms_step = wall / args.steps * 1e3
     fwd_bytes = 2 * io_bytes * n + io_bytes * cols
     bwd_bytes = 3 * io_bytes * n + 2 * io_bytes * cols
@@ -329,6 +358,11 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    if leaves is not None:
+        rec["leaves_only"] = {
+            "value": round((fwd_bytes + bwd_bytes) / (leaves * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(leaves, 4), "steps": args.leaves_steps,
+            "mode": "forward saves only q and init; backward re-derives the boundary state from q"}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(inp)
