@@ -473,7 +473,9 @@ __device__ __forceinline__ Q4<T> tile_scan_product(const Q4<T>& A, Q4<T> (*s_wag
 
 // ------------------------------------------------------------ forward, chunked
 
-template <class IO, int WC, int L, int NW>
+// kStore = false is the boundary-state pass of a backward without saved
+// state: no cum output, so q is dropped right after sweep 1 (fewer registers).
+template <class IO, int WC, int L, int NW, bool kStore>
 __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
@@ -499,7 +501,7 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
                                                     : IO::one_raw();
     }
     Raw init_raw = IO::one_raw();
-    if (a.out != nullptr && tc.col_ok) init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
+    if (kStore && tc.col_ok) init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
     Q4<CT> pre_v;
     const bool pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
 
@@ -517,7 +519,7 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     if (a.ckpt != nullptr && tc.col_ok && tc.t0 < a.s && (tc.t0 % kCkptStride) == 0)
         reinterpret_cast<Q4<CT>*>(a.ckpt)[(tc.bi * a.n_ck + tc.t0 / kCkptStride) * a.M + tc.m] = Ps;
 
-    if (a.out != nullptr) {
+    if (kStore) {
         Q4<CT> cm = qmul(Ps, IO::ct(init_raw));   // cum[t0-1]
         if (tc.full) {
 #pragma unroll
@@ -767,8 +769,9 @@ hipError_t launch_fwd_wc(const KernelArgs& a, hipStream_t st) {
     static_assert(kCkptStride % g.fwd_l == 0, "a forward slice must start on every saved boundary");
     KernelArgs args = a;
     void* params[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw>),
-                           dim3(a.n_blocks), dim3(g.fwd_nw * 64), params, 0, st);
+    const void* fn = a.out != nullptr ? reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, true>)
+                                      : reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, false>);
+    return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(g.fwd_nw * 64), params, 0, st);
 }
 
 template <class IO, int WC>
