@@ -126,6 +126,25 @@ def test_edge_shapes(dtype, path):
                 compare(inp, path=path)
 
 
+def test_random_shapes():
+    """A seeded sweep of shapes, dtypes, paths and saved-state modes, drawn to
+    reach the combinations the grids above do not (partial column groups of
+    every width, the wide forward groups, one to thousands of tiles)."""
+    rng = np.random.default_rng(2024)
+    for it in range(40):
+        b = int(rng.choice([1, 2, 3, 5, 8, 33, 70]))
+        h, j = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        if b >= 33:
+            h, j = int(rng.integers(8, 17)), int(rng.integers(5, 9))   # 64-column forward groups
+        s = int(rng.integers(1, 3000 if b * h * j < 400 else 300))
+        dtype = "bf16" if rng.random() < 0.3 else "f32"
+        path = "column" if rng.random() < 0.2 else "chunked"
+        use_ckpt = bool(rng.random() < 0.7)
+        inp = make_inputs(b, s, h, j, "unit", dtype, seed=1000 + it)
+        print(f"[random {it}: b={b} s={s} h={h} j={j} {dtype} {path} ckpt={use_ckpt}]", flush=True)
+        compare(inp, path=path, use_ckpt=use_ckpt)
+
+
 @pytest.mark.parametrize("s,hj", [(2048, (1, 1)), (4100, (1, 2)), (8191, (2, 2)), (12345, (1, 64)),
                                   (3000, (33, 3))])
 def test_many_tiles_ragged(s, hj):
