@@ -93,7 +93,10 @@ def summarize_traffic(pmc_dir: str, copy_bytes: float):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = ("bwd" if "bwd_chunked_kernel" in name else "fwd" if "fwd_chunked_kernel" in name
+            # The forward that writes cum (not the boundary-state pass of a
+            # backward without saved state, the ", false>" instantiation).
+            key = ("bwd" if "bwd_chunked_kernel" in name
+                   else "fwd" if "fwd_chunked_kernel" in name and ", false>" not in name
                    else "copy" if "copyBuffer" in name else None)
             if key:
                 vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
@@ -118,7 +121,7 @@ def summarize_traffic(pmc_dir: str, copy_bytes: float):
         out.write("# Commands (run from /tmp, TMPDIR=/tmp, R = repository root, OUT = an output directory):\n")
         for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
             out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $OUT/pmc/{ctr} -o run -- "
-                      f"python3 $R/bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline\n")
+                      f"python3 $R/bench.py --steps 2 --warmup 1 --settle-ms 0 --leaves-steps 0 --no-cpu-baseline\n")
             out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $OUT/pmc/copy_{ctr} -o run -- "
                       f"python3 $R/bench.py --copy-calibration --steps 2 --warmup 1\n")
         out.write(f"#   python3 $R/bench.py --summarize-traffic $OUT/pmc\n")
