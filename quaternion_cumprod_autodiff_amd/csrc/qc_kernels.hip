@@ -564,8 +564,15 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 // A_{k-1} (x) E (x) init.  Only q and d stay in registers between the sweeps, in
 // storage precision.
 
+// Waves per SIMD to ask of the compiler: 3 while the slice's q and d_cum fit
+// in 64 registers, else 2.
+template <class IO, int L>
+constexpr int bwd_min_waves() {
+    return L * 2 * int(sizeof(typename IO::Raw)) / 4 <= 64 ? 3 : 2;
+}
+
 template <class IO, int WC, int L, int NW>
-__global__ void __launch_bounds__(NW * 64, 3) bwd_chunked_kernel(KernelArgs a) {
+__global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked_kernel(KernelArgs a) {
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
@@ -775,13 +782,15 @@ hipError_t launch_fwd_wc(const KernelArgs& a, hipStream_t st) {
 }
 
 template <class IO, int WC>
-hipError_t launch_bwd_wc(const KernelArgs& a, hipStream_t st) {
+hipError_t launch_bwd_wc(bool deep, const KernelArgs& a, hipStream_t st) {
     constexpr Geometry g = geometry_for(WC, IO::kDtype);
-    static_assert(bwd_tile_steps(WC, IO::kDtype) % kCkptStride == 0, "backward tiles start on saved boundaries");
+    static_assert(bwd_tile_steps(WC, IO::kDtype, false) % kCkptStride == 0, "backward tiles start on saved boundaries");
+    static_assert(bwd_tile_steps(WC, IO::kDtype, true) % kCkptStride == 0, "backward tiles start on saved boundaries");
     KernelArgs args = a;
     void* params[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_l, g.bwd_nw>),
-                           dim3(a.n_blocks), dim3(g.bwd_nw * 64), params, 0, st);
+    const void* fn = deep ? reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_deep_l, g.bwd_nw>)
+                          : reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_l, g.bwd_nw>);
+    return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(g.bwd_nw * 64), params, 0, st);
 }
 
 template <class IO>
@@ -799,15 +808,15 @@ hipError_t launch_fwd_io(int wc, const KernelArgs& a, hipStream_t st) {
 }
 
 template <class IO>
-hipError_t launch_bwd_io(int wc, const KernelArgs& a, hipStream_t st) {
+hipError_t launch_bwd_io(int wc, bool deep, const KernelArgs& a, hipStream_t st) {
     switch (wc) {
-        case 64: return launch_bwd_wc<IO, 64>(a, st);
-        case 32: return launch_bwd_wc<IO, 32>(a, st);
-        case 16: return launch_bwd_wc<IO, 16>(a, st);
-        case 8: return launch_bwd_wc<IO, 8>(a, st);
-        case 4: return launch_bwd_wc<IO, 4>(a, st);
-        case 2: return launch_bwd_wc<IO, 2>(a, st);
-        case 1: return launch_bwd_wc<IO, 1>(a, st);
+        case 64: return launch_bwd_wc<IO, 64>(deep, a, st);
+        case 32: return launch_bwd_wc<IO, 32>(deep, a, st);
+        case 16: return launch_bwd_wc<IO, 16>(deep, a, st);
+        case 8: return launch_bwd_wc<IO, 8>(deep, a, st);
+        case 4: return launch_bwd_wc<IO, 4>(deep, a, st);
+        case 2: return launch_bwd_wc<IO, 2>(deep, a, st);
+        case 1: return launch_bwd_wc<IO, 1>(deep, a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -818,8 +827,8 @@ hipError_t launch_fwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_
     return dtype == 0 ? launch_fwd_io<IoF32>(wc, a, st) : launch_fwd_io<IoBF16>(wc, a, st);
 }
 
-hipError_t launch_bwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_t st) {
-    return dtype == 0 ? launch_bwd_io<IoF32>(wc, a, st) : launch_bwd_io<IoBF16>(wc, a, st);
+hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st) {
+    return dtype == 0 ? launch_bwd_io<IoF32>(wc, deep, a, st) : launch_bwd_io<IoBF16>(wc, deep, a, st);
 }
 
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st) {
