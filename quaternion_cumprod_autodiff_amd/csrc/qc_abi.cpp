@@ -48,7 +48,7 @@ struct Tiling {
     int wc = 0;               // columns per group
     int64_t n_cg = 0;         // groups per batch entry
     int64_t n_chains = 0;     // b * n_cg
-    bool deep = false;        // backward only: the deep slice length (few chains)
+    bool deep = false;        // the deep slice length (few chains)
     int64_t n_tiles = 0;      // tiles per chain
 };
 
@@ -88,19 +88,28 @@ int column_group_width(int64_t M, int cap) {
     return w;
 }
 
-// The backward takes its deep (taller) tiles when it has fewer chains than
-// this: each chain then has many tiles in flight at once, and halving the
-// look-backs per byte outweighs the lower occupancy (drift: -2% per step,
-// medium: -5%); with many chains (the headline has 256) it does not.
-constexpr int64_t kBwdDeepMaxChains = 64;
+// Deep (twice-as-tall) tiles when there are fewer chains than this: each
+// chain then has many tiles in flight at once, and halving the look-backs per
+// byte outweighs the lower occupancy.  The backward takes them at any depth
+// (drift -2% per step, medium -5%, long-seq -6%); the forward only when its
+// chains are also long (drift -2.5%, long-seq -4%; medium's 16-tile chains
+// were 2% slower).  With many chains (the headline has 128 and 256) neither
+// kernel does.
+constexpr int64_t kDeepMaxChains = 64;
+constexpr int64_t kFwdDeepMinTiles = 64;
 
 Tiling make_tiling(int64_t b, int64_t s, int64_t M, int cap, int dtype, bool backward) {
     Tiling t;
     t.wc = column_group_width(M, cap);
     t.n_cg = (M + t.wc - 1) / t.wc;
     t.n_chains = b * t.n_cg;
-    t.deep = backward && t.n_chains < kBwdDeepMaxChains;
-    const int64_t steps = backward ? qc::bwd_tile_steps(t.wc, dtype, t.deep) : qc::fwd_tile_steps(t.wc, dtype);
+    if (backward) {
+        t.deep = t.n_chains < kDeepMaxChains;
+    } else {
+        const int64_t steps = qc::fwd_tile_steps(t.wc, dtype, false);
+        t.deep = t.n_chains < kDeepMaxChains && (s + steps - 1) / steps >= kFwdDeepMinTiles;
+    }
+    const int64_t steps = backward ? qc::bwd_tile_steps(t.wc, dtype, t.deep) : qc::fwd_tile_steps(t.wc, dtype, t.deep);
     t.n_tiles = (s + steps - 1) / steps;
     return t;
 }
@@ -200,7 +209,7 @@ int launch_forward(const Plan& p, const void* q, const void* init, void* cum, vo
     qc::KernelArgs a = column ? column_args(p, ws) : base_args(p, ws, p.fwd);
     a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt;
     const hipError_t e = column ? qc::launch_fwd_column(p.dtype, a, st)
-                                : qc::launch_fwd_chunked(p.dtype, p.fwd.wc, a, st);
+                                : qc::launch_fwd_chunked(p.dtype, p.fwd.wc, p.fwd.deep, a, st);
     return e == hipSuccess ? QC_OK : hip_fail(e);
 }
 

@@ -33,37 +33,39 @@ enum : uint32_t {
 // L divides kCkptStride, so some forward slice starts on each boundary.
 // bfloat16 quaternions are half the size, so their slices are twice as long
 // for the same registers (and half as many tiles share the fixed costs).
-// The backward has a second, "deep" slice length (bwd_deep_l) for shapes with
-// few chains: each chain then has many tiles in flight, and twice-as-tall
-// tiles halve the carry look-backs per byte, at the price of more registers
-// (float32: 2 waves per SIMD instead of 3).
+// Both kernels have a second, "deep" slice length for shapes with few
+// chains: each chain then has many tiles in flight, and twice-as-tall tiles
+// halve the carry look-backs per byte, at the price of more registers
+// (float32: 2 waves per SIMD instead of 3).  bfloat16 slices are already as
+// long as the registers allow.
 struct Geometry {
     int wc;
     int fwd_l, fwd_nw;
     int bwd_l, bwd_nw;
-    int bwd_deep_l;
+    int fwd_deep_l, bwd_deep_l;
 };
 
 constexpr Geometry geometry_for(int wc, int dtype) {
     return dtype == 0
-        ? (wc == 64 ? Geometry{64, 16, 4, 8, 8, 16}
-         : wc == 32 ? Geometry{32, 16, 4, 8, 4, 16}
-         : wc == 16 ? Geometry{16, 16, 2, 8, 2, 16}
-         : wc == 8  ? Geometry{8, 16, 1, 8, 1, 16}
-         : wc == 4  ? Geometry{4, 8, 1, 4, 1, 8}
-         : wc == 2  ? Geometry{2, 4, 1, 2, 1, 4}
-         :            Geometry{1, 2, 1, 1, 1, 2})
-        : (wc == 64 ? Geometry{64, 32, 4, 16, 8, 16}
-         : wc == 32 ? Geometry{32, 32, 4, 16, 4, 16}
-         : wc == 16 ? Geometry{16, 32, 2, 16, 2, 16}
-         : wc == 8  ? Geometry{8, 32, 1, 16, 1, 16}
-         : wc == 4  ? Geometry{4, 16, 1, 8, 1, 8}
-         : wc == 2  ? Geometry{2, 8, 1, 4, 1, 4}
-         :            Geometry{1, 4, 1, 2, 1, 2});
+        ? (wc == 64 ? Geometry{64, 16, 4, 8, 8, 32, 16}
+         : wc == 32 ? Geometry{32, 16, 4, 8, 4, 32, 16}
+         : wc == 16 ? Geometry{16, 16, 2, 8, 2, 32, 16}
+         : wc == 8  ? Geometry{8, 16, 1, 8, 1, 32, 16}
+         : wc == 4  ? Geometry{4, 8, 1, 4, 1, 16, 8}
+         : wc == 2  ? Geometry{2, 4, 1, 2, 1, 8, 4}
+         :            Geometry{1, 2, 1, 1, 1, 4, 2})
+        : (wc == 64 ? Geometry{64, 32, 4, 16, 8, 32, 16}
+         : wc == 32 ? Geometry{32, 32, 4, 16, 4, 32, 16}
+         : wc == 16 ? Geometry{16, 32, 2, 16, 2, 32, 16}
+         : wc == 8  ? Geometry{8, 32, 1, 16, 1, 32, 16}
+         : wc == 4  ? Geometry{4, 16, 1, 8, 1, 16, 8}
+         : wc == 2  ? Geometry{2, 8, 1, 4, 1, 8, 4}
+         :            Geometry{1, 4, 1, 2, 1, 4, 2});
 }
 
-constexpr int fwd_tile_steps(int wc, int dtype) {
-    return (64 / wc) * geometry_for(wc, dtype).fwd_nw * geometry_for(wc, dtype).fwd_l;
+constexpr int fwd_tile_steps(int wc, int dtype, bool deep) {
+    return (64 / wc) * geometry_for(wc, dtype).fwd_nw *
+           (deep ? geometry_for(wc, dtype).fwd_deep_l : geometry_for(wc, dtype).fwd_l);
 }
 constexpr int bwd_tile_steps(int wc, int dtype, bool deep) {
     return (64 / wc) * geometry_for(wc, dtype).bwd_nw *
@@ -90,7 +92,7 @@ struct KernelArgs {
     uint32_t spin_limit;
 };
 
-hipError_t launch_fwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_t st);
+hipError_t launch_fwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st);
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);

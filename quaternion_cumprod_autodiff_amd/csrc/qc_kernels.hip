@@ -771,13 +771,18 @@ __global__ void zero_words_kernel(uint32_t* p, size_t n) {
 // ------------------------------------------------------------------ launchers
 
 template <class IO, int WC>
-hipError_t launch_fwd_wc(const KernelArgs& a, hipStream_t st) {
+hipError_t launch_fwd_wc(bool deep, const KernelArgs& a, hipStream_t st) {
     constexpr Geometry g = geometry_for(WC, IO::kDtype);
-    static_assert(kCkptStride % g.fwd_l == 0, "a forward slice must start on every saved boundary");
+    static_assert(kCkptStride % g.fwd_l == 0 && kCkptStride % g.fwd_deep_l == 0,
+                  "a forward slice must start on every saved boundary");
     KernelArgs args = a;
     void* params[] = {&args};
-    const void* fn = a.out != nullptr ? reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, true>)
-                                      : reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, false>);
+    const bool store = a.out != nullptr;
+    const void* fn =
+        deep ? (store ? reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_deep_l, g.fwd_nw, true>)
+                      : reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_deep_l, g.fwd_nw, false>))
+             : (store ? reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, true>)
+                      : reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, false>));
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(g.fwd_nw * 64), params, 0, st);
 }
 
@@ -794,15 +799,15 @@ hipError_t launch_bwd_wc(bool deep, const KernelArgs& a, hipStream_t st) {
 }
 
 template <class IO>
-hipError_t launch_fwd_io(int wc, const KernelArgs& a, hipStream_t st) {
+hipError_t launch_fwd_io(int wc, bool deep, const KernelArgs& a, hipStream_t st) {
     switch (wc) {
-        case 64: return launch_fwd_wc<IO, 64>(a, st);
-        case 32: return launch_fwd_wc<IO, 32>(a, st);
-        case 16: return launch_fwd_wc<IO, 16>(a, st);
-        case 8: return launch_fwd_wc<IO, 8>(a, st);
-        case 4: return launch_fwd_wc<IO, 4>(a, st);
-        case 2: return launch_fwd_wc<IO, 2>(a, st);
-        case 1: return launch_fwd_wc<IO, 1>(a, st);
+        case 64: return launch_fwd_wc<IO, 64>(deep, a, st);
+        case 32: return launch_fwd_wc<IO, 32>(deep, a, st);
+        case 16: return launch_fwd_wc<IO, 16>(deep, a, st);
+        case 8: return launch_fwd_wc<IO, 8>(deep, a, st);
+        case 4: return launch_fwd_wc<IO, 4>(deep, a, st);
+        case 2: return launch_fwd_wc<IO, 2>(deep, a, st);
+        case 1: return launch_fwd_wc<IO, 1>(deep, a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -823,8 +828,8 @@ hipError_t launch_bwd_io(int wc, bool deep, const KernelArgs& a, hipStream_t st)
 
 }  // namespace
 
-hipError_t launch_fwd_chunked(int dtype, int wc, const KernelArgs& a, hipStream_t st) {
-    return dtype == 0 ? launch_fwd_io<IoF32>(wc, a, st) : launch_fwd_io<IoBF16>(wc, a, st);
+hipError_t launch_fwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st) {
+    return dtype == 0 ? launch_fwd_io<IoF32>(wc, deep, a, st) : launch_fwd_io<IoBF16>(wc, deep, a, st);
 }
 
 hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st) {
