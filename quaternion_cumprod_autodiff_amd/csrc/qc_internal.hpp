@@ -37,7 +37,9 @@ enum : uint32_t {
 // chains: each chain then has many tiles in flight, and twice-as-tall tiles
 // halve the carry look-backs per byte, at the price of more registers
 // (float32: 2 waves per SIMD instead of 3).  bfloat16 slices are already as
-// long as the registers allow.
+// long as the registers allow.  float32 16-column groups use 4-wave blocks
+// (16 slices per column): narrow shapes are usually single long chains, where
+// the taller tiles pay for the longer in-tile combines (long-seq: -6% per step).
 struct Geometry {
     int wc;
     int fwd_l, fwd_nw;
@@ -49,7 +51,7 @@ constexpr Geometry geometry_for(int wc, int dtype) {
     return dtype == 0
         ? (wc == 64 ? Geometry{64, 16, 4, 8, 8, 32, 16}
          : wc == 32 ? Geometry{32, 16, 4, 8, 4, 32, 16}
-         : wc == 16 ? Geometry{16, 16, 2, 8, 2, 32, 16}
+         : wc == 16 ? Geometry{16, 16, 4, 8, 4, 32, 16}
          : wc == 8  ? Geometry{8, 16, 1, 8, 1, 32, 16}
          : wc == 4  ? Geometry{4, 8, 1, 4, 1, 16, 8}
          : wc == 2  ? Geometry{2, 4, 1, 2, 1, 8, 4}
