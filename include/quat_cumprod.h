@@ -48,12 +48,21 @@
  * nothing was enqueued (except QC_ERR_HIP, which means a launch failed).
  *
  * Workspace: a device buffer of at least quat_cumprod_workspace_bytes(...)
- * bytes, holding a status word, self-validating cross-block carries and (for
- * a backward without saved boundary state) re-derived boundary products.  Zero it once after allocation
+ * bytes, holding a status word, a launch counter, self-validating cross-block
+ * carries and (for a backward without saved boundary state) re-derived
+ * boundary products.  Zero it once after allocation
  * (quat_cumprod_workspace_init does so on a stream; hipMemset also works);
  * every call leaves it ready for the next one, whatever the shape.  Calls
  * sharing one workspace must be ordered (same stream or synchronised);
  * concurrent calls need separate workspaces.
+ *
+ * HIP graphs: quat_cumprod_fwd/_bwd (and the _ex forms) may be called on a
+ * stream that is capturing.  They then also capture a one-thread kernel that
+ * advances the workspace's launch counter, so every replay of the graph gets
+ * carries of its own; replays must be ordered like any other calls on that
+ * workspace.  Capture calls no HIP function other than kernel launches and
+ * hipStreamIsCapturing; quat_cumprod_workspace_status synchronises and must
+ * not be captured.
  */
 #ifndef QUAT_CUMPROD_H
 #define QUAT_CUMPROD_H

@@ -30,7 +30,11 @@ uint64_t next_epoch() {
         std::random_device rd;
         return (static_cast<uint64_t>(rd()) << 32) ^ static_cast<uint64_t>(rd());
     }()};
-    return counter.fetch_add(1, std::memory_order_relaxed);
+    uint64_t e;
+    do {
+        e = counter.fetch_add(1, std::memory_order_relaxed);
+    } while (e == 0);   // 0 tells the kernels to read the epoch from the workspace header
+    return e;
 }
 
 int hip_fail(hipError_t e) {
@@ -193,8 +197,25 @@ qc::KernelArgs base_args(const Plan& p, void* ws, const Tiling& tl) {
     a.hdr = reinterpret_cast<uint32_t*>(ws);
     a.desc = static_cast<char*>(ws) + p.off_desc;
     a.spin_limit = qc::kSpinLimit;
-    a.epoch = next_epoch();
     return a;
+}
+
+// A launch captured in a HIP graph is replayed with the same arguments, so a
+// host-chosen epoch would repeat and a replay could accept the carries of the
+// previous one.  Captured launches therefore bump a counter in the workspace
+// header (one-thread kernel, captured too) and pass epoch 0, which makes the
+// kernels read the counter: every replay gets a fresh epoch.
+int set_epoch(qc::KernelArgs* a, hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cs == hipStreamCaptureStatusNone) {
+        a->epoch = next_epoch();
+        return QC_OK;
+    }
+    a->epoch = 0;
+    e = qc::launch_bump_epoch(a->hdr, st);
+    return e == hipSuccess ? QC_OK : hip_fail(e);
 }
 
 qc::KernelArgs column_args(const Plan& p, void* ws) {
@@ -208,6 +229,10 @@ int launch_forward(const Plan& p, const void* q, const void* init, void* cum, vo
                    hipStream_t st, bool column) {
     qc::KernelArgs a = column ? column_args(p, ws) : base_args(p, ws, p.fwd);
     a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt;
+    if (!column) {
+        const int rc = set_epoch(&a, st);
+        if (rc != QC_OK) return rc;
+    }
     const hipError_t e = column ? qc::launch_fwd_column(p.dtype, a, st)
                                 : qc::launch_fwd_chunked(p.dtype, p.fwd.wc, p.fwd.deep, a, st);
     return e == hipSuccess ? QC_OK : hip_fail(e);
@@ -307,6 +332,8 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
     }
     qc::KernelArgs a = base_args(p, workspace, p.bwd);
     a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init; a.ckpt = ck;
+    rc = set_epoch(&a, st);
+    if (rc != QC_OK) return rc;
     const hipError_t e = qc::launch_bwd_chunked(p.dtype, p.bwd.wc, p.bwd.deep, a, st);
     return e == hipSuccess ? QC_OK : hip_fail(e);
 }

@@ -19,7 +19,9 @@ constexpr int kCkptStride = 64;
 constexpr uint32_t kSpinLimit = 1u << 16;
 
 // Workspace header words, and the bits of the sticky status word.
-enum : int { kHdrStatus = 2, kHdrWords = 64 };
+// kHdrEpoch holds a 64-bit launch counter (words 4-5) for launches captured
+// in a HIP graph, whose arguments (and so a host-chosen epoch) are frozen.
+enum : int { kHdrStatus = 2, kHdrEpoch = 4, kHdrWords = 64 };
 enum : uint32_t {
     kStatusWaitTimeout = 1u,   // a cross-block wait hit kSpinLimit
     kStatusZeroPrefix = 2u,    // a prefix product was exactly zero: the backward's results are not finite
@@ -89,7 +91,7 @@ struct KernelArgs {
     int64_t n_cg;         // column groups per batch entry
     int64_t n_chains;     // b * n_cg
     int64_t n_tiles;      // tiles per chain
-    uint64_t epoch;       // this launch's epoch, folded into every check word
+    uint64_t epoch;       // this launch's epoch, folded into every check word (0: read it from the header)
     uint32_t n_blocks;    // grid size
     uint32_t spin_limit;
 };
@@ -99,6 +101,7 @@ hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a,
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st);
+hipError_t launch_bump_epoch(uint32_t* hdr, hipStream_t st);
 
 constexpr int kColumnBlock = 256;   // threads per block on the column path
 

@@ -419,6 +419,18 @@ __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t p
     return s_out[c];
 }
 
+// The launch epoch: from the arguments, or (launches captured in a graph,
+// epoch 0) from the header counter that a one-thread kernel bumped just
+// before, read coherently and made wave-uniform.
+__device__ __forceinline__ uint64_t launch_epoch(const KernelArgs& a) {
+    if (a.epoch != 0) return a.epoch;
+    const uint64_t e = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.hdr + kHdrEpoch), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(e));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(e >> 32));
+    return (uint64_t(hi) << 32) | lo;
+}
+
 // Tile coordinates shared by the chunked kernels.
 struct TileCoord {
     int64_t chain, pos, bi, m, t0, base;
@@ -477,6 +489,7 @@ __device__ __forceinline__ Q4<T> tile_scan_product(const Q4<T>& A, Q4<T> (*s_wag
 // state: no cum output, so q is dropped right after sweep 1 (fewer registers).
 template <class IO, int WC, int L, int NW, bool kStore>
 __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
+    a.epoch = launch_epoch(a);
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
@@ -573,6 +586,7 @@ constexpr int bwd_min_waves() {
 
 template <class IO, int WC, int L, int NW>
 __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked_kernel(KernelArgs a) {
+    a.epoch = launch_epoch(a);
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
@@ -763,6 +777,12 @@ __global__ void __launch_bounds__(kColumnBlock) bwd_column_kernel(KernelArgs a) 
         __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusZeroPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__global__ void bump_epoch_kernel(uint32_t* hdr) {
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(hdr + kHdrEpoch), uint64_t(1), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ void zero_words_kernel(uint32_t* p, size_t n) {
     for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
         p[i] = 0u;
@@ -850,6 +870,11 @@ hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st) {
     const void* fn = dtype == 0 ? reinterpret_cast<const void*>(&bwd_column_kernel<IoF32, 8>)
                                 : reinterpret_cast<const void*>(&bwd_column_kernel<IoBF16, 8>);
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(kColumnBlock), params, 0, st);
+}
+
+hipError_t launch_bump_epoch(uint32_t* hdr, hipStream_t st) {
+    void* params[] = {&hdr};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bump_epoch_kernel), dim3(1), dim3(64), params, 0, st);
 }
 
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st) {

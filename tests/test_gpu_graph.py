@@ -1,0 +1,93 @@
+"""Forward + backward captured in a HIP graph and replayed (needs an MI355X).
+
+A captured launch keeps its arguments for every replay, so the library cannot
+hand the chunked kernels a fresh host-chosen launch epoch; it captures a
+one-thread kernel that bumps a counter in the workspace header instead, and
+the kernels read their epoch from there.  These tests replay one graph several
+times on new inputs, with eager launches on the same workspace between the
+replays, and check every replay against the oracle and, bitwise, against an
+eager run of the same inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quaternion_cumprod_autodiff_amd import capi
+from quaternion_cumprod_autodiff_amd.inputs import make_inputs
+from test_gpu_parity import check, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (b, s, h, j, recipe, dtype, path, use_ckpt): chunked with saved boundary
+# state, chunked leaves-only (forward prepass inside the backward), bfloat16,
+# a few long chains (tall tiles) and the per-column path.
+CASES = [
+    (2, 4096, 4, 8, "unit", "f32", "chunked", True),
+    (2, 4096, 4, 8, "unit", "f32", "chunked", False),
+    (2, 3000, 4, 8, "unit", "bf16", "chunked", True),
+    (1, 20000, 1, 4, "drift", "f32", "chunked", True),
+    (4, 700, 8, 8, "unit", "f32", "column", True),
+]
+REPLAYS = 4
+
+
+def _eager(q, init, d, path, use_ckpt, ws):
+    ck = capi.new_ckpt(q) if use_ckpt else None
+    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, workspace=ws)
+    d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ck, path=path, workspace=ws)
+    return cum, d_q, d_init
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"b{c[0]}s{c[1]}h{c[2]}j{c[3]}-{c[4]}-{c[5]}-{c[6]}"
+                         + ("" if c[7] else "-leaves"))
+def test_graph_replays_match_eager_and_oracle(case):
+    b, s, h, j, recipe, dtype, path, use_ckpt = case
+    print(f"[graph {case}]", flush=True)
+    first = make_inputs(b, s, h, j, recipe, dtype, seed=500)
+    q, init, d = to_dev(first.q, dtype), to_dev(first.init, dtype), to_dev(first.d_cum, dtype)
+    cum, d_q, d_init = torch.empty_like(q), torch.empty_like(q), torch.empty_like(init)
+    ck = capi.new_ckpt(q) if use_ckpt else None
+    ws = capi.Workspace()
+    eager_ws = capi.Workspace()
+
+    # Warm-up on the capture workspace (allocates and zeroes it outside the capture).
+    capi.quat_cumprod_fwd(q, init, cum, ck, path=path, workspace=ws)
+    capi.quat_cumprod_bwd(q, init, d, ck, d_q=d_q, d_init=d_init, path=path, workspace=ws)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capi.quat_cumprod_fwd(q, init, cum, ck, path=path, workspace=ws)
+        capi.quat_cumprod_bwd(q, init, d, ck, d_q=d_q, d_init=d_init, path=path, workspace=ws)
+    torch.cuda.synchronize()
+
+    for r in range(REPLAYS):
+        inp = make_inputs(b, s, h, j, recipe, dtype, seed=501 + r)
+        q.copy_(to_dev(inp.q, dtype))
+        init.copy_(to_dev(inp.init, dtype))
+        d.copy_(to_dev(inp.d_cum, dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (cum, d_q, d_init)]
+        assert ws.status(q.device) == 0, f"replay {r}: status bits set"
+
+        # Eager work between replays, on the capture workspace (host epochs)
+        # and on a workspace of its own (the bitwise reference).
+        other = make_inputs(b, s, h, j, recipe, dtype, seed=900 + r)
+        _eager(to_dev(other.q, dtype), to_dev(other.init, dtype), to_dev(other.d_cum, dtype), path, use_ckpt, ws)
+        ref_dev = _eager(q, init, d, path, use_ckpt, eager_ws)
+        torch.cuda.synchronize()
+        assert ws.status(q.device) == 0 and eager_ws.status(q.device) == 0
+
+        for name, gt, et in zip(("cum", "d_q", "d_init"), got, ref_dev):
+            assert torch.equal(gt.view(torch.int16) if dtype == "bf16" else gt.view(torch.int32),
+                               et.view(torch.int16) if dtype == "bf16" else et.view(torch.int32)), \
+                f"replay {r}: {name} differs from the eager run"
+        ref = (oracle.fwd(inp.q64, inp.init64),) + tuple(oracle.bwd(inp.q64, inp.init64, inp.d_cum64))
+        for name, gt, rr in zip(("cum", "d_q", "d_init"), got, ref):
+            check(name, to_f64(gt), rr, dtype, s)
+    del g
