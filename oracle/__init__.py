@@ -127,3 +127,7 @@ def bwd_closed_form(q, init, d_cum, normalise: bool, nthreads: int = 0):
     if rc != 0:
         raise MemoryError("oracle_bwd_closed_form could not allocate scratch")
     return d_q, d_init
+
+
+# Generic scan (bodies "add" and "quat") and its VJP: plain numpy, float64.
+from .generic_scan import BODIES as SCAN_BODIES, scan_bwd, scan_fwd  # noqa: E402
