@@ -30,11 +30,19 @@ EXPORTS = (
     "quat_cumprod_fwd", "quat_cumprod_bwd", "quat_cumprod_fwd_ex", "quat_cumprod_bwd_ex",
     "quat_cumprod_workspace_status", "quat_cumprod_strerror", "quat_cumprod_last_hip_error",
     "quat_cumprod_version",
+    # include/qc_scan.h
+    "qc_scan_width", "qc_scan_schedule_capacity", "qc_scan_schedule", "qc_scan_fwd",
+    "qc_scan_bwd_trajectory", "qc_scan_bwd_checkpointed",
 )
 
 
 class QcOptions(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
+class QcScanPlan(ctypes.Structure):
+    _fields_ = [("n_actions", ctypes.c_int64), ("bwd_start", ctypes.c_int64),
+                ("forward_steps", ctypes.c_int64), ("prefix_steps", ctypes.c_int64)]
 
 
 class QuatCumprodError(RuntimeError):
@@ -88,6 +96,19 @@ def load(path: str | None = None):
         lib.quat_cumprod_last_hip_error.restype = ctypes.c_char_p
         lib.quat_cumprod_version.argtypes = []
         lib.quat_cumprod_version.restype = i32
+        lib.qc_scan_width.argtypes = [i32]
+        lib.qc_scan_width.restype = i32
+        lib.qc_scan_schedule_capacity.argtypes = [i64]
+        lib.qc_scan_schedule_capacity.restype = i64
+        lib.qc_scan_schedule.argtypes = [i64, i32, vp, i64, ctypes.POINTER(QcScanPlan)]
+        lib.qc_scan_schedule.restype = ctypes.c_int
+        lib.qc_scan_fwd.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i64, vp, i32, vp]
+        lib.qc_scan_fwd.restype = ctypes.c_int
+        lib.qc_scan_bwd_trajectory.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.qc_scan_bwd_trajectory.restype = ctypes.c_int
+        lib.qc_scan_bwd_checkpointed.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, i64,
+                                                 vp, i32, vp, vp]
+        lib.qc_scan_bwd_checkpointed.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -247,3 +268,133 @@ def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
                                     _stream(stream), _options(path))
     _check(rc, "quat_cumprod_bwd")
     return d_q, d_init
+
+
+# ---------------------------------------------------------------- generic scan
+# Binding of include/qc_scan.h: a scan with body "add" (c + x, width 1) or
+# "quat" (x (x) c, width 4) over float32 [b, s, m, w] tensors, and its VJP from
+# the whole trajectory or from k snapshots (binomial checkpointing).
+
+SCAN_BODIES = {"add": 0, "quat": 1}
+
+
+def _scan_dims(body: str, xs: torch.Tensor):
+    if body not in SCAN_BODIES:
+        raise ValueError(f"unknown scan body {body!r}")
+    w = int(load().qc_scan_width(SCAN_BODIES[body]))
+    if xs.dim() != 4 or xs.shape[-1] != w:
+        raise ValueError(f"xs must be [b, s, m, {w}] for body {body!r}, got {tuple(xs.shape)}")
+    if xs.dtype != torch.float32 or not xs.is_contiguous():
+        raise ValueError("xs must be contiguous float32")
+    if xs.device.type != "cuda":
+        raise ValueError("the scan runs on the GPU only: xs must be a device tensor")
+    b, s, m, _ = xs.shape
+    return SCAN_BODIES[body], b, s, m, w
+
+
+def _scan_like(name, t, shape, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous float32 {tuple(shape)} on {device}")
+
+
+class ScanSchedule:
+    """Binomial-checkpointing schedule for ``s`` steps and ``k`` snapshot
+    slots, built by the library on the host; ``device(dev)`` returns (and
+    caches) its copy in device memory."""
+
+    def __init__(self, s: int, k: int):
+        lib = load()
+        cap = int(lib.qc_scan_schedule_capacity(s))
+        self.s, self.k = int(s), int(k)
+        self.actions = torch.zeros((max(cap, 1), 4), dtype=torch.int32)
+        plan = QcScanPlan()
+        _check(lib.qc_scan_schedule(s, k, ctypes.c_void_p(self.actions.data_ptr()), cap, ctypes.byref(plan)),
+               "qc_scan_schedule")
+        self.n_actions = int(plan.n_actions)
+        self.bwd_start = int(plan.bwd_start)
+        self.forward_steps = int(plan.forward_steps)
+        self.prefix_steps = int(plan.prefix_steps)
+        self.actions = self.actions[: self.n_actions].clone()
+        self._dev = {}
+
+    def device(self, dev) -> torch.Tensor:
+        dev = torch.device(dev)
+        if dev not in self._dev:
+            self._dev[dev] = self.actions.to(dev)
+        return self._dev[dev]
+
+
+def new_snapshots(body: str, xs: torch.Tensor, k: int) -> torch.Tensor:
+    _, b, s, m, w = _scan_dims(body, xs)
+    return torch.empty((k, b * m, w), dtype=torch.float64, device=xs.device)
+
+
+def scan_fwd(body: str, xs: torch.Tensor, init: torch.Tensor, ys: torch.Tensor | None = None, *,
+             schedule: ScanSchedule | None = None, snaps: torch.Tensor | None = None, want_ys: bool = True,
+             stream=None):
+    """ys[t] = f(ys[t-1], xs[t]) from init.  With ``schedule`` the forward
+    sweep's part of it is carried out too, filling ``snaps``."""
+    code, b, s, m, w = _scan_dims(body, xs)
+    _scan_like("init", init, (b, m, w), xs.device)
+    if want_ys and ys is None:
+        ys = torch.empty_like(xs)
+    if not want_ys:
+        ys = None
+    _scan_like("ys", ys, xs.shape, xs.device)
+    sched = None
+    k = 0
+    start = 0
+    if schedule is not None:
+        if schedule.s != s:
+            raise ValueError("schedule was built for another sequence length")
+        if snaps is None or snaps.shape != (schedule.k, b * m, w) or snaps.dtype != torch.float64:
+            raise ValueError("snaps must be float64 [k, b*m, w] (new_snapshots)")
+        sched, k, start = schedule.device(xs.device), schedule.k, schedule.bwd_start
+    rc = load().qc_scan_fwd(code, _ptr(xs), _ptr(init), _ptr(ys), b, s, m, _ptr(sched), start,
+                            _ptr(snaps) if schedule is not None else None, k, _stream(stream))
+    _check(rc, "qc_scan_fwd")
+    return ys
+
+
+def scan_bwd_trajectory(body: str, xs: torch.Tensor, init: torch.Tensor, ys: torch.Tensor,
+                        upstream: torch.Tensor, *, d_xs: torch.Tensor | None = None,
+                        d_init: torch.Tensor | None = None, stream=None):
+    """VJP from the whole saved trajectory ys; returns (d_xs, d_init)."""
+    code, b, s, m, w = _scan_dims(body, xs)
+    d_xs = torch.empty_like(xs) if d_xs is None else d_xs
+    d_init = torch.empty_like(init) if d_init is None else d_init
+    for name, t, shp in (("init", init, (b, m, w)), ("ys", ys, xs.shape), ("upstream", upstream, xs.shape),
+                         ("d_xs", d_xs, xs.shape), ("d_init", d_init, (b, m, w))):
+        _scan_like(name, t, shp, xs.device)
+    rc = load().qc_scan_bwd_trajectory(code, _ptr(xs), _ptr(init), _ptr(ys), _ptr(upstream), _ptr(d_xs),
+                                       _ptr(d_init), b, s, m, _stream(stream))
+    _check(rc, "qc_scan_bwd_trajectory")
+    return d_xs, d_init
+
+
+def scan_bwd_checkpointed(body: str, xs: torch.Tensor, init: torch.Tensor, upstream: torch.Tensor,
+                          schedule: ScanSchedule, snaps: torch.Tensor, *, after_forward: bool = False,
+                          status: torch.Tensor | None = None, d_xs: torch.Tensor | None = None,
+                          d_init: torch.Tensor | None = None, stream=None):
+    """VJP from k snapshots.  ``after_forward``: scan_fwd with this schedule
+    already filled the snapshots, so the records start at bwd_start."""
+    code, b, s, m, w = _scan_dims(body, xs)
+    if schedule.s != s:
+        raise ValueError("schedule was built for another sequence length")
+    if snaps.shape != (schedule.k, b * m, w) or snaps.dtype != torch.float64 or snaps.device != xs.device:
+        raise ValueError("snaps must be float64 [k, b*m, w] on xs's device (new_snapshots)")
+    d_xs = torch.empty_like(xs) if d_xs is None else d_xs
+    d_init = torch.empty_like(init) if d_init is None else d_init
+    for name, t, shp in (("init", init, (b, m, w)), ("upstream", upstream, xs.shape),
+                         ("d_xs", d_xs, xs.shape), ("d_init", d_init, (b, m, w))):
+        _scan_like(name, t, shp, xs.device)
+    if status is not None and (status.dtype != torch.int32 or status.numel() != 1 or status.device != xs.device):
+        raise ValueError("status must be one int32 on xs's device")
+    start = schedule.bwd_start if after_forward else 0
+    rc = load().qc_scan_bwd_checkpointed(code, _ptr(xs), _ptr(init), _ptr(upstream), _ptr(d_xs), _ptr(d_init),
+                                         b, s, m, _ptr(schedule.device(xs.device)), schedule.n_actions, start,
+                                         _ptr(snaps), schedule.k, _ptr(status), _stream(stream))
+    _check(rc, "qc_scan_bwd_checkpointed")
+    return d_xs, d_init

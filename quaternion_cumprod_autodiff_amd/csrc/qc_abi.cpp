@@ -240,6 +240,8 @@ int launch_forward(const Plan& p, const void* q, const void* init, void* cum, vo
 
 }  // namespace
 
+int qc::record_hip_error(hipError_t e) { return hip_fail(e); }
+
 extern "C" {
 
 size_t quat_cumprod_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype) {

@@ -103,6 +103,9 @@ hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st);
 hipError_t launch_bump_epoch(uint32_t* hdr, hipStream_t st);
 
+// Records a failed HIP call for quat_cumprod_last_hip_error; returns QC_ERR_HIP.
+int record_hip_error(hipError_t e);
+
 constexpr int kColumnBlock = 256;   // threads per block on the column path
 
 }  // namespace qc

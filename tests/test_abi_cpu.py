@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol that
-include/quat_cumprod.h declares, sizes its buffers as documented, and rejects
+include/quat_cumprod.h and include/qc_scan.h declare, sizes its buffers as documented, and rejects
 bad arguments with the documented codes before any HIP call (so fake device
 pointers are safe here)."""
 import ctypes
@@ -13,7 +13,7 @@ from quaternion_cumprod_autodiff_amd import capi
 from quaternion_cumprod_autodiff_amd.build import LIB_PATH
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "quat_cumprod.h")
+HEADERS = [os.path.join(ROOT, "include", "quat_cumprod.h"), os.path.join(ROOT, "include", "qc_scan.h")]
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_ALIAS, E_WS, E_HIP, E_OPT = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
@@ -27,9 +27,11 @@ def lib():
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(quat_cumprod_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:quat_cumprod|qc_scan)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_what_the_binding_uses():
@@ -38,7 +40,7 @@ def test_header_declares_what_the_binding_uses():
 
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (quat_cumprod_\w+)", out))
+    exported = set(re.findall(r"\bT ((?:quat_cumprod|qc_scan)_\w+)", out))
     missing = [f for f in header_functions() if f not in exported]
     assert not missing, missing
     for f in header_functions():
