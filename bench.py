@@ -174,6 +174,228 @@ def copy_calibration(nbytes: int, steps: int, warmup: int):
     return 2.0 * nbytes / dt / 1e9, dt
 
 
+# ------------------------------------------------------------- generic scan
+# The scan VJP of include/qc_scan.h (add or quaternion body, one column per
+# thread).  Workload: the page's scan test length, 129 steps, over enough
+# columns that every lane of the chip has one (2^20 quaternion columns,
+# 2^22 scalar ones: 2.16 GB per [b, s, m, w] tensor either way).
+SCAN_WORKLOADS = {"quat": (1, 129, 1 << 20), "add": (1, 129, 1 << 22)}
+
+
+def scan_schedule_bytes(body: str, sched, lo: int, hi: int, ebytes: int, cols: int, w: int) -> int:
+    """Algorithmic bytes of schedule records [lo, hi): every body evaluation
+    reads one x; a reversed step also reads its upstream cotangent and writes
+    its d_x, and reads x only where the body's VJP depends on it (the
+    quaternion body; the add body's Jacobians are constant); a snapshot store
+    or load moves one float64 carry."""
+    acts = sched.actions[lo:hi].numpy()
+    op = acts[:, 0]
+    adv = int((acts[op == 3, 2] - acts[op == 3, 1]).sum())
+    rev = int((op == 4).sum())
+    snap = int(((op == 1) | (op == 2)).sum())
+    rev_bytes = 3 if body == "quat" else 2
+    return cols * (ebytes * (adv + rev_bytes * rev) + 8 * w * snap)
+
+
+SCAN_SOURCES = [os.path.join(ROOT, "quaternion_cumprod_autodiff_amd", "csrc", "qc_scan.hip")]
+SCAN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scan_quat.txt")
+
+
+def scan_source_sha() -> str:
+    h = hashlib.sha256()
+    for path in SCAN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def summarize_scan_traffic(pmc_dir: str, fetch_scale: float, write_scale: float):
+    """HBM bytes per launch of the quaternion-body scan kernels (trajectory
+    mode) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of ``--scan quat``,
+    scaled like the headline's (the copy calibration's factors)."""
+    import csv
+    import statistics
+
+    def per_kernel(counter):
+        vals = {}
+        path = os.path.join(pmc_dir, counter, "run_counter_collection.csv")
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("bwd" if "scan_bwd_trajectory_kernel" in name
+                   else "fwd" if "scan_fwd_kernel" in name else None)
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    f, w = per_kernel("FETCH_SIZE"), per_kernel("WRITE_SIZE")
+    b, s, m = SCAN_WORKLOADS["quat"]
+    rec = {
+        "workload": f"scan quat b{b} s{s} m{m} f32 I/O, forward + VJP (trajectory)",
+        "kernel_source_sha256": scan_source_sha(),
+        "fetch_scale": f"{fetch_scale:.4f}", "write_scale": f"{write_scale:.4f}",
+        "fwd_fetch_bytes": f"{f['fwd'] * fetch_scale:.0f}", "fwd_write_bytes": f"{w['fwd'] * write_scale:.0f}",
+        "bwd_fetch_bytes": f"{f['bwd'] * fetch_scale:.0f}", "bwd_write_bytes": f"{w['bwd'] * write_scale:.0f}",
+        "fwd_hbm_bytes_per_launch": f"{f['fwd'] * fetch_scale + w['fwd'] * write_scale:.0f}",
+        "bwd_hbm_bytes_per_launch": f"{f['bwd'] * fetch_scale + w['bwd'] * write_scale:.0f}",
+    }
+    with open(SCAN_TRAFFIC_FILE, "w") as out:
+        out.write("# HBM traffic per launch of the generic scan kernels, quaternion body, trajectory mode.\n")
+        out.write("# Counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), scaled by\n")
+        out.write("# the factors of the plain-copy calibration in traffic_headline.txt.\n")
+        out.write("# Commands (run from /tmp, TMPDIR=/tmp, R = repository root, OUT = an output directory):\n")
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $OUT/pmc_scan/{ctr} -o run -- "
+                      f"python3 $R/bench.py --scan quat --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline\n")
+        out.write("#   python3 $R/bench.py --summarize-scan-traffic $OUT/pmc_scan\n")
+        for k, v in rec.items():
+            out.write(f"{k} = {v}\n")
+    print(json.dumps(rec))
+
+
+def load_scan_traffic(workload_key: str):
+    try:
+        rec = read_kv(SCAN_TRAFFIC_FILE)
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != scan_source_sha() or rec.get("workload") != workload_key:
+        return None
+    return float(rec["bwd_hbm_bytes_per_launch"])
+
+
+def scan_cpu_baseline(body: str, xs, init, up, min_seconds: float = 10.0):
+    """The float64 numpy oracle of the generic scan on the first 4096 columns."""
+    import oracle
+    cols = min(4096, xs.shape[2])
+    x = xs[:, :, :cols].double().cpu().numpy()
+    i0 = init[:, :cols].double().cpu().numpy()
+    u = up[:, :, :cols].double().cpu().numpy()
+    w = x.shape[-1]
+    n = x.shape[0] * x.shape[1] * cols
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.scan_fwd(body, x, i0)
+        oracle.scan_bwd(body, x, i0, u)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_pass = t_total / reps
+    per_elem, per_col = (6, 3) if body == "quat" else (4, 2)   # the device leg's trajectory-mode bytes
+    gbps = 4 * w * (per_elem * n + per_col * x.shape[0] * cols) / per_pass / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {cols} columns x {x.shape[1]} steps ({n} elements), float64 numpy forward + "
+                      f"reverse sweep over the saved trajectory, {reps} pass(es), {per_pass:.3f} s per pass"}
+
+
+def scan_bench(args):
+    """One step = the scan's forward (ys, plus the snapshots with --scan-k) and
+    its VJP, from the saved trajectory (--scan-k 0) or from k snapshots."""
+    import numpy as np
+    import torch
+
+    from quaternion_cumprod_autodiff_amd import capi
+    from quaternion_cumprod_autodiff_amd.inputs import SCAN_WIDTH, make_generic_scan_inputs_device
+
+    body, k = args.scan, args.scan_k
+    b, s, m = SCAN_WORKLOADS[body]
+    w = SCAN_WIDTH[body]
+    eb, cols = 4 * w, b * m
+    n = cols * s
+    dev = torch.device("cuda:0")
+    xs, init, up = make_generic_scan_inputs_device(body, b, s, m, 0, dev)
+    ys = torch.empty_like(xs)
+    d_xs, d_init = torch.empty_like(xs), torch.empty_like(init)
+    if k > 0:
+        sch = capi.ScanSchedule(s, k)
+        snaps = capi.new_snapshots(body, xs, k)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        fwd_bytes = 2 * eb * n + eb * cols + scan_schedule_bytes(body, sch, 0, sch.bwd_start, eb, cols, w)
+        bwd_bytes = (scan_schedule_bytes(body, sch, sch.bwd_start, sch.n_actions, eb, cols, w)
+                     + 8 * w * cols + eb * cols)      # resume load, d_init
+        kernel = "scan_bwd_checkpointed_kernel"
+
+        def fwd():
+            capi.scan_fwd(body, xs, init, ys, schedule=sch, snaps=snaps)
+
+        def bwd():
+            capi.scan_bwd_checkpointed(body, xs, init, up, sch, snaps, after_forward=True, status=status,
+                                       d_xs=d_xs, d_init=d_init)
+    else:
+        sch = status = None
+        fwd_bytes = 2 * eb * n + eb * cols
+        # quat: xs, ys[t-1] (init at t = 0), upstream, d_xs, d_init.  add: the
+        # VJP depends on neither x nor the carries, so upstream, d_xs, d_init.
+        bwd_bytes = eb * (4 * n + cols) if body == "quat" else eb * (2 * n + cols)
+        kernel = "scan_bwd_trajectory_kernel"
+
+        def fwd():
+            capi.scan_fwd(body, xs, init, ys)
+
+        def bwd():
+            capi.scan_bwd_trajectory(body, xs, init, ys, up, d_xs=d_xs, d_init=d_init)
+
+    warm, t0 = 0, time.perf_counter()
+    while warm < args.warmup or (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        fwd()
+        bwd()
+        warm += 1
+        if warm % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    every = max(1, args.event_every)
+    be = {i: (ev(), ev()) for i in range(every - 1, args.steps, every)}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fwd()
+        if i in be:
+            be[i][0].record()
+            bwd()
+            be[i][1].record()
+        else:
+            bwd()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if status is not None and int(status.item()) != 0:
+        raise RuntimeError("the device refused a schedule record")
+    bwd_ms = float(np.mean([a.elapsed_time(c) for a, c in be.values()]))
+    diag = [(ev(), ev()) for _ in range(10)]
+    for f0, f1 in diag:
+        f0.record()
+        fwd()
+        f1.record()
+    torch.cuda.synchronize()
+    fwd_ms = float(np.median([a.elapsed_time(c) for a, c in diag]))
+    ms_step = wall / args.steps * 1e3
+    value = (fwd_bytes + bwd_bytes) / (ms_step * 1e-3) / 1e9
+    bwd_gbps = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+    mode = f"checkpointed k={k}" if k > 0 else "trajectory"
+    workload = f"scan {body} b{b} s{s} m{m} f32 I/O, forward + VJP ({mode})"
+    rec = {
+        "metric": f"generic scan fwd+bwd GB/s, {body} body, b{b} s{s} m{m} f32 ({mode})",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": workload,
+                   "b": b, "s": s, "m": m, "body": body, "mode": mode},
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4), "elements_per_s": round(n / (ms_step * 1e-3), 1),
+        "fwd_bytes": fwd_bytes, "bwd_bytes": bwd_bytes,
+        "bwd_ms": round(bwd_ms, 4), "bwd_launches_timed": len(be), "diag_fwd_ms": round(fwd_ms, 4),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(bwd_gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": load_scan_traffic(workload)},
+        "cpu_baseline": None,
+    }
+    if sch is not None:
+        rec["schedule"] = {"k": k, "records": sch.n_actions, "body_evaluations": sch.forward_steps,
+                           "in_forward": sch.prefix_steps}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = scan_cpu_baseline(body, xs, init, up)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,7 +420,17 @@ def main():
                     help="only time a plain device copy of one [b,s,h,j,4] tensor")
     ap.add_argument("--summarize-traffic", metavar="PMC_DIR",
                     help="write profiles/traffic_headline.txt from rocprofv3 FETCH_SIZE/WRITE_SIZE runs")
+    ap.add_argument("--scan", choices=["add", "quat"],
+                    help="measure the generic scan VJP (include/qc_scan.h) with this body instead")
+    ap.add_argument("--scan-k", type=int, default=0,
+                    help="with --scan: VJP from k snapshots (binomial checkpointing); 0 = saved trajectory")
+    ap.add_argument("--summarize-scan-traffic", metavar="PMC_DIR",
+                    help="write profiles/traffic_scan_quat.txt from rocprofv3 runs of --scan quat")
     args = ap.parse_args()
+    if args.summarize_scan_traffic:
+        cal = read_kv(TRAFFIC_FILE)
+        summarize_scan_traffic(args.summarize_scan_traffic, float(cal["fetch_scale"]), float(cal["write_scale"]))
+        return
     if args.summarize_traffic:
         b, s, h, j, _, io = CONFIGS["headline"]
         summarize_traffic(args.summarize_traffic, float(b * s * h * j * 16))
@@ -209,6 +441,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(columns shard across GPUs without communication)", file=sys.stderr)
         sys.exit(2)
+
+    if args.scan:
+        scan_bench(args)
+        return
 
     import numpy as np
     import torch

@@ -153,3 +153,27 @@ def make_inputs(b: int, s: int, h: int, j: int, recipe: str = "unit",
 def make_config(name: str, seed: int = 0, want_f64: bool = True) -> ScanInputs:
     b, s, h, j, recipe, dtype = CONFIGS[name]
     return make_inputs(b, s, h, j, recipe, dtype, seed, want_f64)
+
+
+# ---------------------------------------------------------------------------
+# Generic scan (include/qc_scan.h): xs, upstream [b, s, m, w], init [b, m, w],
+# float32.  Bodies: "add" (w = 1) draws N(0, 1) for xs and init; "quat"
+# (w = 4) draws unit quaternions (N(0,1)^4 / |.|, normalised in float32 on the
+# device).  upstream ~ N(0, 1).  Drawn on the device from a seeded
+# torch.Generator in the order xs, init, upstream, so that launches with
+# millions of columns do not wait on the host.
+
+SCAN_WIDTH = {"add": 1, "quat": 4}
+
+
+def make_generic_scan_inputs_device(body: str, b: int, s: int, m: int, seed: int, device):
+    import torch
+    w = SCAN_WIDTH[body]
+    g = torch.Generator(device=device).manual_seed(seed)
+    xs = torch.randn((b, s, m, w), device=device, generator=g)
+    init = torch.randn((b, m, w), device=device, generator=g)
+    if body == "quat":
+        xs /= xs.norm(dim=-1, keepdim=True)
+        init /= init.norm(dim=-1, keepdim=True)
+    up = torch.randn((b, s, m, w), device=device, generator=g)
+    return xs, init, up

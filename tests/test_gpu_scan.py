@@ -188,3 +188,58 @@ def test_many_columns_sampled():
     check("d_init traj", host(d_init[:, cols]), r_di, 2.0 ** -23, 2.0 ** -21)
     check("d_xs ckpt", host(c_xs[:, :, cols]), r_dx, 2.0 ** -23)
     check("d_init ckpt", host(c_init[:, cols]), r_di, 2.0 ** -23)
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 5])
+def test_page_length_129_sum_of_carries(k):
+    """The rlx-autodiff page's length-129 scan test: an add body over a carry of
+    2 values, loss = the sum of every saved carry, so the upstream cotangent is
+    all ones.  Then x[t] reaches the carries t .. 128, so d_x[t] = 129 - t
+    exactly, d_init = 129, and ys is a running sum.  k = 0 reads the saved
+    trajectory; k > 0 recomputes from k snapshots."""
+    b, s, m = 1, 129, 2
+    rng = np.random.default_rng(129)
+    xs = rng.standard_normal((b, s, m, 1)).astype(np.float32)
+    init = rng.standard_normal((b, m, 1)).astype(np.float32)
+    X, I, U = dev(xs), dev(init), torch.ones((b, s, m, 1), dtype=torch.float32, device=DEV)
+    ys = capi.scan_fwd("add", X, I)
+    if k == 0:
+        d_xs, d_init = capi.scan_bwd_trajectory("add", X, I, ys, U)
+    else:
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        d_xs, d_init = capi.scan_bwd_checkpointed("add", X, I, U, capi.ScanSchedule(s, k),
+                                                  capi.new_snapshots("add", X, k), status=status)
+    torch.cuda.synchronize()
+    want = np.broadcast_to((s - np.arange(s, dtype=np.float64))[None, :, None, None], (b, s, m, 1))
+    assert np.array_equal(host(d_xs), want)
+    assert np.array_equal(host(d_init), np.full((b, m, 1), float(s)))
+    running = init.astype(np.float64)[:, None] + np.cumsum(xs.astype(np.float64), axis=1)
+    check("ys", host(ys), running, 2.0 ** -23)
+    if k:
+        assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("after_forward", [False, True])
+def test_page_griewank_length_4_two_snapshots(after_forward):
+    """The page's Griewank case: body carry + 1 (here x[t] = 1), a carry of 2
+    values, length 4, k = 2 snapshots, an arbitrary upstream.  Closed form:
+    ys[t] = init + t + 1, d_init = sum over t of upstream[t], d_x[t] = the sum
+    of upstream over u >= t."""
+    b, s, m, k = 1, 4, 2, 2
+    rng = np.random.default_rng(4)
+    init = rng.standard_normal((b, m, 1)).astype(np.float32)
+    up = rng.standard_normal((b, s, m, 1)).astype(np.float32)
+    X, I, U = torch.ones((b, s, m, 1), dtype=torch.float32, device=DEV), dev(init), dev(up)
+    sch = capi.ScanSchedule(s, k)
+    snaps = capi.new_snapshots("add", X, k)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ys = capi.scan_fwd("add", X, I, schedule=sch if after_forward else None,
+                       snaps=snaps if after_forward else None)
+    d_xs, d_init = capi.scan_bwd_checkpointed("add", X, I, U, sch, snaps, after_forward=after_forward,
+                                              status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    u64 = up.astype(np.float64)
+    check("ys", host(ys), init.astype(np.float64)[:, None] + np.arange(1, s + 1)[None, :, None, None], 2.0 ** -23)
+    check("d_xs", host(d_xs), np.cumsum(u64[:, ::-1], axis=1)[:, ::-1], 2.0 ** -23)
+    check("d_init", host(d_init), u64.sum(axis=1), 2.0 ** -23)
