@@ -152,9 +152,37 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
         reps += 1
     per_pass = t_total / reps
     gbps = (80.0 * n + 32.0 * cols) / per_pass / 1e9
+    # One thread on 1/16 of the same sample (the first 64 columns), same byte formula.
+    s_len = q.shape[1]
+    q1 = np.ascontiguousarray(q.reshape(1, s_len, cols, 4)[:, :, :64])
+    i1 = np.ascontiguousarray(init.reshape(1, cols, 4)[:, :64])
+    d1 = np.ascontiguousarray(d.reshape(1, s_len, cols, 4)[:, :, :64])
+    n1, reps1, t1 = q1.shape[1] * q1.shape[2], 0, 0.0
+    while t1 < min_seconds / 4 or reps1 == 0:
+        t0 = time.perf_counter()
+        oracle.fwd(q1, i1, 1)
+        oracle.bwd(q1, i1, d1, 1)
+        t1 += time.perf_counter() - t0
+        reps1 += 1
+    gbps1 = (80.0 * n1 + 32.0 * q1.shape[2]) / (t1 / reps1) / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"batch entry 0 of the workload ({cols} columns x {q.shape[1]} steps = {n} quaternions), "
-                      f"float64 forward + reverse-recurrence backward, {reps} pass(es), {per_pass:.2f} s per pass"}
+                      f"float64 forward + reverse-recurrence backward, {reps} pass(es), {per_pass:.2f} s per pass",
+            "cpu_model": cpu_model(),
+            "one_thread": {"value": round(gbps1, 4), "unit": "GB/s", "cores": 1,
+                           "sample": f"the first 64 columns of the same sample ({n1} quaternions), "
+                                     f"{reps1} pass(es), {t1 / reps1:.3f} s per pass"}}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_calibration(nbytes: int, steps: int, warmup: int):
@@ -285,7 +313,8 @@ def scan_cpu_baseline(body: str, xs, init, up, min_seconds: float = 10.0):
     gbps = 4 * w * (per_elem * n + per_col * x.shape[0] * cols) / per_pass / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the first {cols} columns x {x.shape[1]} steps ({n} elements), float64 numpy forward + "
-                      f"reverse sweep over the saved trajectory, {reps} pass(es), {per_pass:.3f} s per pass"}
+                      f"reverse sweep over the saved trajectory, {reps} pass(es), {per_pass:.3f} s per pass",
+            "cpu_model": cpu_model()}
 
 
 def scan_bench(args):
