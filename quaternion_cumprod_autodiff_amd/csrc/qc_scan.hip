@@ -353,7 +353,8 @@ int qc_scan_fwd(int32_t body, const float* xs, const float* init, float* ys, int
     if (rc != QC_OK) return rc;
     if (!xs || !init) return QC_ERR_NULL;
     if (!ys && !schedule) return QC_ERR_NULL;
-    if (schedule && (!snaps || k < 1 || k > 4096 || bwd_start < 1)) return QC_ERR_WORKSPACE;
+    if (schedule && (!snaps || k < 1 || k > 4096)) return QC_ERR_WORKSPACE;
+    if (schedule && (bwd_start < 1 || bwd_start > qc_scan_schedule_capacity(s))) return QC_ERR_SHAPE;
     const size_t eb = size_t(d.w) * 4;
     if (!qc::aligned(xs, eb) || !qc::aligned(init, eb) || (ys && !qc::aligned(ys, eb))) return QC_ERR_ALIGN;
     if ((schedule && !qc::aligned(schedule, 16)) || (snaps && !qc::aligned(snaps, 16))) return QC_ERR_ALIGN;

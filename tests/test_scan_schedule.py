@@ -138,6 +138,9 @@ def test_scan_entry_points_validate_before_launching(lib):
     assert f(1, A + 4, A + GB, A + 2 * GB, 1, 8, 8, None, 0, None, 0, None) == E_ALIGN
     assert f(1, A, A + GB, A + 64, 1, 8, 8, None, 0, None, 0, None) == E_ALIAS
     assert f(1, A, A + GB, A + 2 * GB, 1, 8, 8, A + 3 * GB, 1, None, 2, None) == E_WS
+    # bwd_start must name a record inside a schedule for s steps (at most 4 s + 2 records).
+    assert f(1, A, A + GB, A + 2 * GB, 1, 8, 8, A + 3 * GB, 0, A + 4 * GB, 2, None) == E_SHAPE
+    assert f(1, A, A + GB, A + 2 * GB, 1, 8, 8, A + 3 * GB, 35, A + 4 * GB, 2, None) == E_SHAPE
     t = lib.qc_scan_bwd_trajectory
     assert t(1, A, A + GB, A + 2 * GB, None, A + 3 * GB, None, 1, 8, 8, None) == E_NULL
     assert t(1, A, A + GB, A + 2 * GB, A + 3 * GB, None, None, 1, 8, 8, None) == 0   # nothing wanted
