@@ -61,3 +61,73 @@ def quat_cumprod_with_final(q: torch.Tensor, init: torch.Tensor, *, save_boundar
     autograd folds into the last position of cum's gradient."""
     cum = quat_cumprod(q, init, save_boundary_state=save_boundary_state)
     return cum, cum[:, -1]
+
+
+# ---------------------------------------------------------------------------
+# Generic scan (include/qc_scan.h) as an autograd node, after the Scan op of the
+# rlx-autodiff source page "src/decompose_backward.rs": the forward returns
+# every carry (its save_trajectory case); the backward is the scan VJP, read
+# from the saved trajectory (num_checkpoints = 0) or from k snapshots that the
+# forward takes on the way, recomputing the carries between them (its
+# num_checkpoints = k, "Griewank", case).
+
+_schedules: dict = {}
+
+
+def _schedule(s: int, k: int) -> capi.ScanSchedule:
+    key = (int(s), int(k))
+    if key not in _schedules:
+        _schedules[key] = capi.ScanSchedule(s, k)
+    return _schedules[key]
+
+
+class ScanFunction(torch.autograd.Function):
+    """ys = scan(body, xs, init); backward = the VJP of every saved carry."""
+
+    @staticmethod
+    def forward(ctx, body: str, xs: torch.Tensor, init: torch.Tensor, num_checkpoints: int):
+        xs = xs.contiguous()
+        init = init.contiguous()
+        ctx.body = body
+        ctx.k = int(num_checkpoints)
+        if ctx.k > 0:
+            sched = _schedule(xs.shape[1], ctx.k)
+            snaps = capi.new_snapshots(body, xs, ctx.k)
+            ys = capi.scan_fwd(body, xs, init, schedule=sched, snaps=snaps)
+            ctx.sched = sched
+            ctx.fresh_snapshots = True
+            ctx.save_for_backward(xs, init, snaps)
+        else:
+            ys = capi.scan_fwd(body, xs, init)
+            ctx.save_for_backward(xs, init, ys)
+        return ys
+
+    @staticmethod
+    def backward(ctx, d_ys: torch.Tensor):
+        xs, init, saved = ctx.saved_tensors
+        want_dxs, want_dinit = ctx.needs_input_grad[1], ctx.needs_input_grad[2]
+        if not (want_dxs or want_dinit):
+            return None, None, None, None
+        d_ys = d_ys.contiguous()
+        if ctx.k > 0:
+            # The VJP overwrites the snapshots; a second backward through the
+            # same graph (retain_graph) starts again from init.
+            d_xs, d_init = capi.scan_bwd_checkpointed(ctx.body, xs, init, d_ys, ctx.sched, saved,
+                                                      after_forward=ctx.fresh_snapshots)
+            ctx.fresh_snapshots = False
+        else:
+            d_xs, d_init = capi.scan_bwd_trajectory(ctx.body, xs, init, saved, d_ys)
+        return None, (d_xs if want_dxs else None), (d_init if want_dinit else None), None
+
+
+def scan(body: str, xs: torch.Tensor, init: torch.Tensor, *, num_checkpoints: int = 0) -> torch.Tensor:
+    """Every carry of c[t] = f(c[t-1], xs[t]), c[-1] = init, differentiable in
+    xs and init.  body: "add" (f = c + x, width 1) or "quat" (f = x (x) c,
+    width 4).  xs: [b, s, m, w], init: [b, m, w], float32, on the GPU.
+    num_checkpoints = 0 saves the whole trajectory for the backward; k > 0
+    keeps k snapshots and recomputes the rest (binomial checkpointing)."""
+    if num_checkpoints < 0:
+        raise ValueError("num_checkpoints must be >= 0")
+    if torch.is_grad_enabled() and (xs.requires_grad or init.requires_grad):
+        return ScanFunction.apply(body, xs, init, num_checkpoints)
+    return capi.scan_fwd(body, xs.contiguous(), init.contiguous())

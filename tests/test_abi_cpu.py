@@ -193,3 +193,16 @@ def test_cpu_tensors_are_refused_not_computed():
         capi.quat_cumprod_fwd(q, init)
     with pytest.raises(ValueError, match="GPU"):
         capi.quat_cumprod_bwd(q, init, q)
+
+
+def test_scan_node_refuses_host_tensors():
+    """The generic scan's autograd node has no CPU path: host tensors are
+    refused before anything runs."""
+    import torch
+    from quaternion_cumprod_autodiff_amd.autograd import scan
+    xs = torch.zeros((1, 4, 2, 4), requires_grad=True)
+    init = torch.zeros((1, 2, 4))
+    with pytest.raises(ValueError, match="GPU only"):
+        scan("quat", xs, init)
+    with pytest.raises(ValueError):
+        scan("quat", xs, init, num_checkpoints=-1)
