@@ -243,3 +243,38 @@ def test_page_griewank_length_4_two_snapshots(after_forward):
     check("ys", host(ys), init.astype(np.float64)[:, None] + np.arange(1, s + 1)[None, :, None, None], 2.0 ** -23)
     check("d_xs", host(d_xs), np.cumsum(u64[:, ::-1], axis=1)[:, ::-1], 2.0 ** -23)
     check("d_init", host(d_init), u64.sum(axis=1), 2.0 ** -23)
+
+
+def test_random_shapes_and_snapshot_counts():
+    """A seeded sweep of 24 random (body, b, s, m, k) cases, k = 0 meaning the
+    trajectory VJP, each against the oracle.  s spans 1 .. 2000 (odd lengths,
+    partial load groups), m spans 1 .. 300 (partial blocks), k 0 .. 40."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        body = ["add", "quat"][int(rng.integers(2))]
+        b = int(rng.integers(1, 4))
+        s = int(rng.choice([1, 2, 7, 8, 9, 63, 129, 500, 1001, 2000]))
+        m = int(rng.integers(1, 301))
+        k = int(rng.choice([0, 0, 1, 2, 5, 17, 40]))
+        print(f"[scan sweep {case}: {body} b={b} s={s} m={m} k={k}]", flush=True)
+        xs, init, up = make(body, b, s, m, seed=1000 + case)
+        X, I, U = dev(xs), dev(init), dev(up)
+        r_dx, r_di = oracle.scan_bwd(body, xs, init, up)
+        if k == 0:
+            ys = capi.scan_fwd(body, X, I)
+            d_xs, d_init = capi.scan_bwd_trajectory(body, X, I, ys, U)
+            torch.cuda.synchronize()
+            check("ys", host(ys), oracle.scan_fwd(body, xs, init), 2.0 ** -23)
+            check("d_xs", host(d_xs), r_dx, 2.0 ** -23, 2.0 ** -21)
+            check("d_init", host(d_init), r_di, 2.0 ** -23, 2.0 ** -21)
+        else:
+            sch = capi.ScanSchedule(s, k)
+            snaps = capi.new_snapshots(body, X, k)
+            status = torch.zeros(1, dtype=torch.int32, device=DEV)
+            ys = capi.scan_fwd(body, X, I, schedule=sch, snaps=snaps)
+            d_xs, d_init = capi.scan_bwd_checkpointed(body, X, I, U, sch, snaps, after_forward=True, status=status)
+            torch.cuda.synchronize()
+            assert int(status.item()) == 0
+            check("ys", host(ys), oracle.scan_fwd(body, xs, init), 2.0 ** -23)
+            check("d_xs", host(d_xs), r_dx, 2.0 ** -23)
+            check("d_init", host(d_init), r_di, 2.0 ** -23)
