@@ -131,3 +131,6 @@ def bwd_closed_form(q, init, d_cum, normalise: bool, nthreads: int = 0):
 
 # Generic scan (bodies "add" and "quat") and its VJP: plain numpy, float64.
 from .generic_scan import BODIES as SCAN_BODIES, scan_bwd, scan_fwd  # noqa: E402
+
+# Gated DeltaNet-2 recurrence and its VJP: plain numpy, float64.
+from .gdn2 import gdn2_bwd, gdn2_fwd, gdn2_states  # noqa: E402,F401
