@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libquatcumprod.so")
-SOURCES = ["qc_kernels.hip", "qc_abi.cpp", "qc_scan.hip", "qc_scan_schedule.cpp"]
+SOURCES = ["qc_kernels.hip", "qc_abi.cpp", "qc_scan.hip", "qc_scan_schedule.cpp", "gdn2.hip"]
 ARCH = "gfx950"
 
 

@@ -33,6 +33,8 @@ EXPORTS = (
     # include/qc_scan.h
     "qc_scan_width", "qc_scan_schedule_capacity", "qc_scan_schedule", "qc_scan_fwd",
     "qc_scan_bwd_trajectory", "qc_scan_bwd_checkpointed",
+    # include/gdn2.h
+    "gdn2_boundary_bytes", "gdn2_scratch_bytes", "gdn2_fwd", "gdn2_bwd",
 )
 
 
@@ -109,6 +111,14 @@ def load(path: str | None = None):
         lib.qc_scan_bwd_checkpointed.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, i64,
                                                  vp, i32, vp, vp]
         lib.qc_scan_bwd_checkpointed.restype = ctypes.c_int
+        lib.gdn2_boundary_bytes.argtypes = [i64] * 6
+        lib.gdn2_boundary_bytes.restype = sz
+        lib.gdn2_scratch_bytes.argtypes = [i64] * 6
+        lib.gdn2_scratch_bytes.restype = sz
+        lib.gdn2_fwd.argtypes = [vp] * 10 + [i64] * 6 + [vp]
+        lib.gdn2_fwd.restype = ctypes.c_int
+        lib.gdn2_bwd.argtypes = [vp] * 17 + [sz] + [i64] * 6 + [vp]
+        lib.gdn2_bwd.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -398,3 +408,82 @@ def scan_bwd_checkpointed(body: str, xs: torch.Tensor, init: torch.Tensor, upstr
                                          _ptr(snaps), schedule.k, _ptr(status), _stream(stream))
     _check(rc, "qc_scan_bwd_checkpointed")
     return d_xs, d_init
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet-2 recurrence (include/gdn2.h).  query, key, erase, log_decay
+# [B, H, T, L]; value, write [B, H, T, D]; initial_state [B, H, L, D]; all
+# contiguous float32 on the GPU.
+
+GDN2_INPUTS = ("query", "key", "value", "erase", "write", "log_decay", "initial_state")
+
+
+def _gdn2_dims(query, value, chunk):
+    if query.dim() != 4 or value.dim() != 4:
+        raise ValueError("query must be [B, H, T, L] and value [B, H, T, D]")
+    B, H, T, L = query.shape
+    D = value.shape[3]
+    if tuple(value.shape[:3]) != (B, H, T):
+        raise ValueError("value must share query's [B, H, T]")
+    if query.device.type != "cuda":
+        raise ValueError("Gated DeltaNet-2 runs on the GPU only: inputs must be device tensors")
+    if int(chunk) < 1:
+        raise ValueError("chunk must be >= 1")
+    return int(B), int(H), int(T), int(L), int(D), int(chunk)
+
+
+def _gdn2_check(tensors: dict, B, H, T, L, D, device):
+    shapes = {"query": (B, H, T, L), "key": (B, H, T, L), "erase": (B, H, T, L), "log_decay": (B, H, T, L),
+              "value": (B, H, T, D), "write": (B, H, T, D), "initial_state": (B, H, L, D),
+              "d_context": (B, H, T, D), "d_state": (B, H, L, D)}
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if (tuple(t.shape) != shapes[name] or t.dtype != torch.float32 or t.device != device
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 {shapes[name]} on {device}")
+
+
+def gdn2_fwd(query, key, value, erase, write, log_decay, initial_state, *, chunk: int = 64,
+             want_boundary: bool = True, stream=None):
+    """(context [B, H, T, D], final state [B, H, L, D], boundary states or None)."""
+    B, H, T, L, D, chunk = _gdn2_dims(query, value, chunk)
+    ins = dict(zip(GDN2_INPUTS, (query, key, value, erase, write, log_decay, initial_state)))
+    _gdn2_check(ins, B, H, T, L, D, query.device)
+    lib = load()
+    nb = int(lib.gdn2_boundary_bytes(B, H, T, L, D, chunk))
+    if nb == 0:
+        raise QuatCumprodError(-2, "gdn2_fwd")
+    ctx = torch.empty((B, H, T, D), dtype=torch.float32, device=query.device)
+    state = torch.empty((B, H, L, D), dtype=torch.float32, device=query.device)
+    bnd = torch.empty(nb // 4, dtype=torch.float32, device=query.device) if want_boundary else None
+    rc = lib.gdn2_fwd(*[_ptr(ins[n]) for n in GDN2_INPUTS], _ptr(ctx), _ptr(state), _ptr(bnd),
+                      B, H, T, L, D, chunk, _stream(stream))
+    _check(rc, "gdn2_fwd")
+    return ctx, state, bnd
+
+
+def gdn2_bwd(query, key, value, erase, write, log_decay, boundary, d_context, d_state=None, *, chunk: int = 64,
+             want=GDN2_INPUTS, stream=None):
+    """Cotangents (query, key, value, erase, write, log_decay, initial_state);
+    those not named in ``want`` are None.  ``boundary`` is gdn2_fwd's third
+    output for the same inputs and chunk."""
+    B, H, T, L, D, chunk = _gdn2_dims(query, value, chunk)
+    ins = dict(zip(GDN2_INPUTS[:6], (query, key, value, erase, write, log_decay)))
+    ins["d_context"], ins["d_state"] = d_context, d_state
+    _gdn2_check(ins, B, H, T, L, D, query.device)
+    lib = load()
+    nb = int(lib.gdn2_boundary_bytes(B, H, T, L, D, chunk))
+    if boundary is None or boundary.numel() * 4 != nb or boundary.dtype != torch.float32:
+        raise ValueError("boundary must be gdn2_fwd's boundary states for the same sizes and chunk")
+    nscr = int(lib.gdn2_scratch_bytes(B, H, T, L, D, chunk))
+    scratch = torch.empty(nscr // 4, dtype=torch.float32, device=query.device)
+    outs = {}
+    for name, src in zip(GDN2_INPUTS, (query, key, value, erase, write, log_decay, None)):
+        shp = (B, H, L, D) if name == "initial_state" else tuple(src.shape)
+        outs[name] = torch.empty(shp, dtype=torch.float32, device=query.device) if name in want else None
+    rc = lib.gdn2_bwd(*[_ptr(ins[n]) for n in GDN2_INPUTS[:6]], _ptr(boundary), _ptr(d_context), _ptr(d_state),
+                      *[_ptr(outs[n]) for n in GDN2_INPUTS], _ptr(scratch), nscr, B, H, T, L, D, chunk,
+                      _stream(stream))
+    _check(rc, "gdn2_bwd")
+    return tuple(outs[n] for n in GDN2_INPUTS)

@@ -177,3 +177,53 @@ def make_generic_scan_inputs_device(body: str, b: int, s: int, m: int, seed: int
         init /= init.norm(dim=-1, keepdim=True)
     up = torch.randn((b, s, m, w), device=device, generator=g)
     return xs, init, up
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet-2 (include/gdn2.h): query, key, erase, log_decay [B, H, T, L];
+# value, write [B, H, T, D]; initial_state [B, H, L, D]; float32.
+#
+# The burn_gdn page's tests fill every tensor deterministically, element idx
+# (row-major) -> ((idx * stride) % modulus) / modulus + offset, with a
+# (stride, modulus, offset) per tensor; "output_weight" weights the context
+# in their loss.  The random recipe draws from one default_rng(seed) stream in
+# the order below: query ~ N(0,1), key ~ N(0,1)/sqrt(L), value ~ N(0,1),
+# erase ~ U(0,1), write ~ U(0,1), log_decay ~ U(-1.2, -0.2) (decays 0.30 ..
+# 0.82, the span of the page's data), initial_state ~ N(0,1).
+
+GDN2_PAGE_DATA = {
+    "query": (3, 23, -0.35), "key": (5, 29, -0.25), "value": (7, 31, -0.2), "erase": (11, 37, 0.1),
+    "write": (13, 41, 0.2), "log_decay": (17, 43, -1.2), "initial_state": (19, 47, -0.1),
+    "output_weight": (23, 53, -0.3),
+}
+
+
+def _gdn2_shapes(B, H, T, L, D):
+    return {"query": (B, H, T, L), "key": (B, H, T, L), "value": (B, H, T, D), "erase": (B, H, T, L),
+            "write": (B, H, T, D), "log_decay": (B, H, T, L), "initial_state": (B, H, L, D),
+            "output_weight": (B, H, T, D)}
+
+
+def gdn2_page_tensor(shape, stride: int, modulus: int, offset: float) -> np.ndarray:
+    idx = np.arange(int(np.prod(shape)), dtype=np.int64)
+    return (((idx * stride) % modulus).astype(np.float32) / np.float32(modulus) + np.float32(offset)).reshape(shape)
+
+
+def make_gdn2_page_inputs(B: int, H: int, T: int, L: int, D: int) -> dict:
+    shapes = _gdn2_shapes(B, H, T, L, D)
+    return {n: gdn2_page_tensor(shapes[n], *GDN2_PAGE_DATA[n]) for n in GDN2_PAGE_DATA}
+
+
+def make_gdn2_random_inputs(B: int, H: int, T: int, L: int, D: int, seed: int = 0) -> dict:
+    rng = np.random.default_rng(seed)
+    s = _gdn2_shapes(B, H, T, L, D)
+    out = {
+        "query": rng.standard_normal(s["query"]),
+        "key": rng.standard_normal(s["key"]) / np.sqrt(L),
+        "value": rng.standard_normal(s["value"]),
+        "erase": rng.uniform(0.0, 1.0, s["erase"]),
+        "write": rng.uniform(0.0, 1.0, s["write"]),
+        "log_decay": rng.uniform(-1.2, -0.2, s["log_decay"]),
+        "initial_state": rng.standard_normal(s["initial_state"]),
+    }
+    return {n: v.astype(np.float32) for n, v in out.items()}

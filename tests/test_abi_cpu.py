@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol that
-include/quat_cumprod.h and include/qc_scan.h declare, sizes its buffers as documented, and rejects
+include/quat_cumprod.h, include/qc_scan.h and include/gdn2.h declare, sizes its buffers as documented, and rejects
 bad arguments with the documented codes before any HIP call (so fake device
 pointers are safe here)."""
 import ctypes
@@ -13,7 +13,7 @@ from quaternion_cumprod_autodiff_amd import capi
 from quaternion_cumprod_autodiff_amd.build import LIB_PATH
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", "quat_cumprod.h"), os.path.join(ROOT, "include", "qc_scan.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("quat_cumprod.h", "qc_scan.h", "gdn2.h")]
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_ALIAS, E_WS, E_HIP, E_OPT = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
@@ -30,7 +30,7 @@ def header_functions():
     names = set()
     for h in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b((?:quat_cumprod|qc_scan)_\w+)\s*\(", text))
+        names |= set(re.findall(r"\b((?:quat_cumprod|qc_scan|gdn2)_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -40,7 +40,7 @@ def test_header_declares_what_the_binding_uses():
 
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT ((?:quat_cumprod|qc_scan)_\w+)", out))
+    exported = set(re.findall(r"\bT ((?:quat_cumprod|qc_scan|gdn2)_\w+)", out))
     missing = [f for f in header_functions() if f not in exported]
     assert not missing, missing
     for f in header_functions():
@@ -206,3 +206,32 @@ def test_scan_node_refuses_host_tensors():
         scan("quat", xs, init)
     with pytest.raises(ValueError):
         scan("quat", xs, init, num_checkpoints=-1)
+
+
+def test_gdn2_sizes_and_validation(lib):
+    """Gated DeltaNet-2 entry points: documented buffer sizes, and bad
+    arguments refused before any HIP call (fake device pointers)."""
+    assert lib.gdn2_boundary_bytes(1, 2, 5, 3, 4, 2) == 2 * 3 * 3 * 4 * 4       # heads x chunks x L x D floats
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 2) == 2 * 2 * 3 * 4 * 4        # heads x chunk x L x D
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 64) == 2 * 5 * 3 * 4 * 4       # a chunk longer than T
+    assert lib.gdn2_boundary_bytes(1, 1, 1, 65, 4, 1) == 0                      # L > 64
+    assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 257, 1) == 0                     # D > 256
+    assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 4, 0) == 0
+    G = 1 << 30
+    A = 1 << 44
+    ins = [A + i * G for i in range(7)]
+    f = lib.gdn2_fwd
+    assert f(*ins, A + 7 * G, None, None, 0, 1, 8, 4, 4, 2, None) == E_SHAPE
+    assert f(*ins, A + 7 * G, None, None, 1, 1, 8, 65, 4, 2, None) == E_SHAPE
+    assert f(*ins[:6], None, A + 7 * G, None, None, 1, 1, 8, 4, 4, 2, None) == E_NULL
+    assert f(*ins, None, None, None, 1, 1, 8, 4, 4, 2, None) == E_NULL
+    assert f(*ins, A + 7 * G + 2, None, None, 1, 1, 8, 4, 4, 2, None) == E_ALIGN
+    assert f(*ins, A + 64, None, None, 1, 1, 8, 4, 4, 2, None) == E_ALIAS        # context over query
+    b = lib.gdn2_bwd
+    outs = [A + (10 + i) * G for i in range(7)]
+    base = ins[:6] + [A + 8 * G, A + 9 * G, None] + outs
+    assert b(*base, A + 20 * G, 0, 1, 1, 8, 4, 4, 2, None) == E_WS               # scratch too small
+    assert b(*base, None, 1 << 20, 1, 1, 8, 4, 4, 2, None) == E_WS
+    assert b(*(ins[:6] + [None, A + 9 * G, None] + outs), A + 20 * G, 1 << 20, 1, 1, 8, 4, 4, 2, None) == E_NULL
+    assert b(*(ins[:6] + [A + 8 * G, A + 9 * G, None] + [None] * 7), None, 0, 1, 1, 8, 4, 4, 2, None) == OK
+    assert b(*(base[:9] + [A + 64] + outs[1:]), A + 20 * G, 1 << 20, 1, 1, 8, 4, 4, 2, None) == E_ALIAS

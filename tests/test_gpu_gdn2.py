@@ -1,0 +1,110 @@
+"""Parity of the Gated DeltaNet-2 kernels (include/gdn2.h) with the float64
+oracle (oracle/gdn2.py), through the C ABI (needs an MI355X).
+
+Tolerance: the burn_gdn page's own test bound, max |gpu - ref| <= 3e-3 +
+3e-3 max|ref| per tensor (its assert_close), for the context, the final
+state and all seven cotangents.  The device computes in float32 from float32
+inputs; the oracle takes the same float32 values widened to float64.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quaternion_cumprod_autodiff_amd import capi
+from quaternion_cumprod_autodiff_amd.inputs import make_gdn2_page_inputs, make_gdn2_random_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NAMES = capi.GDN2_INPUTS
+
+
+def close(label, got, ref):
+    got = got.detach().cpu().numpy().astype(np.float64)
+    scale = float(np.abs(ref).max())
+    err = float(np.abs(got - ref).max())
+    assert err <= 3e-3 + 3e-3 * scale, f"{label}: max diff {err:.3e} (ref max {scale:.3e})"
+    return err / max(scale, 1e-30)
+
+
+def run_case(arrays, chunk, d_ctx, d_state=None):
+    dev = {n: torch.from_numpy(arrays[n]).to(DEV) for n in NAMES}
+    ctx, state, bnd = capi.gdn2_fwd(*[dev[n] for n in NAMES], chunk=chunk)
+    D_ctx = torch.from_numpy(d_ctx).to(DEV)
+    D_st = torch.from_numpy(d_state).to(DEV) if d_state is not None else None
+    grads = capi.gdn2_bwd(*[dev[n] for n in NAMES[:6]], bnd, D_ctx, D_st, chunk=chunk)
+    torch.cuda.synchronize()
+    r_ctx, r_state = oracle.gdn2_fwd(*[arrays[n] for n in NAMES])
+    r_grads = oracle.gdn2_bwd(*[arrays[n] for n in NAMES], d_ctx, d_state)
+    rel = {"context": close("context", ctx, r_ctx), "state": close("state", state, r_state)}
+    for n, g, r in zip(NAMES, grads, r_grads):
+        rel["d_" + n] = close("d_" + n, g, r)
+    return rel
+
+
+# The page's test geometries (batch, heads, time, latent, dense, chunk) and data.
+PAGE = [(1, 2, 5, 3, 4, 2), (1, 2, 9, 5, 37, 4), (1, 4, 12, 64, 128, 6), (1, 2, 64, 16, 32, 64)]
+
+
+@pytest.mark.parametrize("geom", PAGE, ids=lambda g: "b%dh%dt%dl%dd%dc%d" % g)
+def test_page_geometries_and_data(geom):
+    B, H, T, L, D, chunk = geom
+    print(f"[gdn2 page {geom}]", flush=True)
+    arrays = make_gdn2_page_inputs(B, H, T, L, D)
+    rel = run_case(arrays, chunk, arrays["output_weight"])
+    print("  relative max errors:", {k: f"{v:.1e}" for k, v in rel.items()}, flush=True)
+
+
+@pytest.mark.parametrize("geom", [(2, 3, 50, 7, 100, 8), (1, 1, 200, 64, 256, 32), (3, 2, 33, 33, 65, 1),
+                                  (1, 2, 40, 1, 1, 7), (2, 1, 17, 16, 200, 100), (1, 3, 128, 64, 64, 16)],
+                         ids=lambda g: "b%dh%dt%dl%dd%dc%d" % g)
+def test_random_shapes_with_final_state_cotangent(geom):
+    B, H, T, L, D, chunk = geom
+    print(f"[gdn2 random {geom}]", flush=True)
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=sum(geom))
+    rng = np.random.default_rng(1)
+    d_ctx = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    d_state = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    rel = run_case(arrays, chunk, d_ctx, d_state)
+    print("  relative max errors:", {k: f"{v:.1e}" for k, v in rel.items()}, flush=True)
+
+
+def test_chunk_size_does_not_change_results_beyond_rounding():
+    """The chunk only sets where boundary states are saved: the forward is the
+    same arithmetic for every chunk (bitwise), and the backward recomputes
+    the same states (bitwise too, since each chunk restarts from a state the
+    forward stored exactly)."""
+    arrays = make_gdn2_random_inputs(1, 2, 90, 16, 48, seed=4)
+    dev = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
+    d_ctx = torch.randn((1, 2, 90, 48), device=DEV, generator=torch.Generator(device=DEV).manual_seed(2))
+    outs = []
+    for chunk in (1, 7, 30, 90, 500):
+        ctx, state, bnd = capi.gdn2_fwd(*dev, chunk=chunk)
+        grads = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=chunk)
+        outs.append((ctx, state) + grads)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for x, y in zip(outs[0], o):
+            assert torch.equal(x, y)
+
+
+def test_optional_outputs_and_determinism():
+    arrays = make_gdn2_random_inputs(2, 2, 30, 8, 70, seed=5)
+    dev = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
+    d_ctx = torch.randn((2, 2, 30, 70), device=DEV, generator=torch.Generator(device=DEV).manual_seed(3))
+    ctx, state, bnd = capi.gdn2_fwd(*dev, chunk=4)
+    ctx2, _, none = capi.gdn2_fwd(*dev, chunk=4, want_boundary=False)
+    full = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=4)
+    again = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=4)
+    part = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=4, want=("key", "initial_state"))
+    zero_state = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, torch.zeros_like(state), chunk=4)
+    torch.cuda.synchronize()
+    assert none is None and torch.equal(ctx, ctx2)
+    for x, y, z in zip(full, again, zero_state):
+        assert torch.equal(x, y) and torch.equal(x, z)
+    for n, x, p in zip(NAMES, full, part):
+        if n in ("key", "initial_state"):
+            assert torch.equal(x, p)
+        else:
+            assert p is None
