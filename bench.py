@@ -425,6 +425,119 @@ def scan_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+# -------------------------------------------------------- Gated DeltaNet-2
+# The recurrence of include/gdn2.h at the page's training head shape (latent
+# 64, dense 128) over 8 x 16 heads and 2048 steps, chunk 64.
+GDN2_WORKLOAD = (8, 16, 2048, 64, 128, 64)
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def gdn2_bytes_and_flops(B, H, T, L, D):
+    """Algorithmic bytes and flops per forward and per VJP (float32).  Bytes:
+    every input read once, every output written once (the boundary states and
+    the backward's scratch are the method's recompute and are not counted).
+    Flops per (head, step, latent row, dense column): forward 7 (decay 1,
+    erased read-out 2, write 2, read-out 2); VJP 23 (the step recomputed, 5,
+    and its reverse, 18), counting an FMA as 2."""
+    heads = B * H
+    fwd_bytes = 4 * heads * (T * (4 * L + 2 * D) + L * D + T * D + L * D)
+    bwd_bytes = 4 * heads * (T * (4 * L + 3 * D) + T * (4 * L + 2 * D) + L * D)
+    return fwd_bytes, bwd_bytes, 7 * heads * T * L * D, 23 * heads * T * L * D
+
+
+def gdn2_bench(args):
+    import numpy as np
+    import torch
+
+    from quaternion_cumprod_autodiff_amd import capi
+
+    B, H, T, L, D, chunk = GDN2_WORKLOAD
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    ins = [torch.randn((B, H, T, L), device=dev, generator=g),
+           torch.randn((B, H, T, L), device=dev, generator=g) / L ** 0.5,
+           torch.randn((B, H, T, D), device=dev, generator=g),
+           torch.rand((B, H, T, L), device=dev, generator=g),
+           torch.rand((B, H, T, D), device=dev, generator=g),
+           torch.rand((B, H, T, L), device=dev, generator=g) - 1.2,
+           torch.randn((B, H, L, D), device=dev, generator=g)]
+    d_ctx = torch.randn((B, H, T, D), device=dev, generator=g)
+    out = {}
+
+    def fwd():
+        out["f"] = capi.gdn2_fwd(*ins, chunk=chunk)
+
+    def bwd():
+        capi.gdn2_bwd(*ins[:6], out["f"][2], d_ctx, chunk=chunk)
+
+    warm, t0 = 0, time.perf_counter()
+    while warm < args.warmup or (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        fwd()
+        bwd()
+        warm += 1
+        torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    steps = max(1, args.steps)
+    evs = [(ev(), ev(), ev()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in evs:
+        e0.record()
+        fwd()
+        e1.record()
+        bwd()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in evs]))
+    bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in evs]))
+    fb, bb, ff, bf = gdn2_bytes_and_flops(B, H, T, L, D)
+    dominant = ("gdn2_bwd_kernel", bf, bwd_ms) if bwd_ms >= fwd_ms else ("gdn2_fwd_kernel", ff, fwd_ms)
+    tflops = dominant[1] / (dominant[2] * 1e-3) / 1e12
+    rec = {
+        "metric": f"Gated DeltaNet-2 fwd+bwd GB/s, b{B} h{H} t{T} latent{L} dense{D} fp32",
+        "value": round((fb + bb) / wall / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"gdn2 b{B} h{H} t{T} latent{L} dense{D} chunk{chunk} f32, forward + VJP",
+                   "B": B, "H": H, "T": T, "L": L, "D": D, "chunk": chunk},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "fwd_bytes": fb, "bwd_bytes": bb, "fwd_flops": ff, "bwd_flops": bf,
+        "head_steps_per_s": round(B * H * T / wall, 1),
+        "roofline": {"bound": "alu", "kernel": dominant[0], "achieved": round(tflops, 3),
+                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 5), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = gdn2_cpu_baseline([x.cpu().numpy() for x in ins], d_ctx.cpu().numpy(), (fb + bb))
+    print(json.dumps(rec), flush=True)
+
+
+def gdn2_cpu_baseline(arrays, d_ctx, total_bytes, min_seconds: float = 10.0):
+    """The float64 numpy oracle (forward + VJP) on the first head's first
+    256 steps, scaled to the same byte count per head-step."""
+    import oracle
+    B, H, T, L = arrays[0].shape
+    ts = min(T, 256)
+    sample = [a[:1, :1, :ts] if a.ndim == 4 and a.shape[2] == T else a[:1, :1] for a in arrays]
+    dc = d_ctx[:1, :1, :ts]
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.gdn2_fwd(*sample)
+        oracle.gdn2_bwd(*sample, dc)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_pass = t_total / reps
+    bytes_per_head_step = total_bytes / (B * H * T)
+    return {"value": round(bytes_per_head_step * ts / per_pass / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"one head, the first {ts} steps, float64 numpy forward + VJP over the saved states, "
+                      f"{reps} pass(es), {per_pass:.3f} s per pass"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,6 +568,8 @@ def main():
                     help="with --scan: VJP from k snapshots (binomial checkpointing); 0 = saved trajectory")
     ap.add_argument("--summarize-scan-traffic", metavar="PMC_DIR",
                     help="write profiles/traffic_scan_quat.txt from rocprofv3 runs of --scan quat")
+    ap.add_argument("--gdn2", action="store_true",
+                    help="measure the Gated DeltaNet-2 forward + VJP (include/gdn2.h) instead")
     args = ap.parse_args()
     if args.summarize_scan_traffic:
         cal = read_kv(TRAFFIC_FILE)
@@ -473,6 +588,9 @@ def main():
 
     if args.scan:
         scan_bench(args)
+        return
+    if args.gdn2:
+        gdn2_bench(args)
         return
 
     import numpy as np
