@@ -17,9 +17,12 @@
  * and returns the cotangents of all seven inputs.
  *
  * Layout (row-major float32): query, key, erase, log_decay [B, H, T, L];
- * value, write, context [B, H, T, D]; initial_state, final state [B, H, L, D];
- * boundary states [B, H, ceil(T / chunk), L, D] (entry c = the state before
- * step c * chunk).
+ * value, write, context [B, H, T, D]; initial_state, final state [B, H, L, D].
+ * The boundary states (entry c = the state before step c * chunk) and the
+ * backward's scratch are internal formats, [B, H, ceil(T / chunk), D, LP] and
+ * [B, H, min(chunk, T), D, LP] with LP = L rounded up to 8, 16, 32 or 64 (each
+ * dense column's rows contiguous, rows past L zero); both must be 16-byte
+ * aligned.
  *
  * Device design: the forward gives each thread one dense column of a head's
  * state (columns evolve independently), in registers, with the step's latent
@@ -30,14 +33,15 @@
  * log_decay) are sums over the dense axis, reduced across the block every step.
  * Arithmetic is float32.
  *
- * Limits: B, H, T, D, chunk >= 1; 1 <= L <= 64; D <= 1024; element counts
+ * Limits: B, H, T, D, chunk >= 1; 1 <= L <= 64; D <= 256; element counts
  * below 2^40.
  *
  * Conventions: device pointers owned by the caller; the library never
  * allocates, frees or keeps a pointer.  Validation happens on the host before
  * any HIP call; the return value is 0 or a negative QC_ERR_* code of
  * quat_cumprod.h (QC_ERR_NULL for a missing required pointer, QC_ERR_SHAPE for
- * sizes out of range, QC_ERR_ALIGN for a pointer not 4-byte aligned,
+ * sizes out of range, QC_ERR_ALIGN for a tensor pointer not 4-byte aligned or
+ * a boundary or scratch pointer not 16-byte aligned,
  * QC_ERR_ALIAS for an output overlapping another buffer, QC_ERR_WORKSPACE for
  * a too-small scratch, QC_ERR_HIP for a failed launch).  Launches are
  * asynchronous on `stream` (a hipStream_t as void*).

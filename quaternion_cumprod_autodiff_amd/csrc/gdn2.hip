@@ -105,6 +105,30 @@ constexpr int row_shift() {
     return LM == 64 ? 0 : LM == 32 ? 1 : LM == 16 ? 2 : 3;
 }
 
+// The boundary states and the backward's scratch keep each dense column's LM
+// rows contiguous ([.., d, LM]), so a column moves as LM/4 float4 at
+// immediate offsets from one per-thread address (a [L, D] layout would need
+// a separate uniform base per row).
+template <int LM>
+__device__ __forceinline__ void store_column(float* p, const float (&x)[LM]) {
+    float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+    for (int i = 0; i < LM / 4; ++i) q[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+}
+
+template <int LM>
+__device__ __forceinline__ void load_column(const float* p, float (&x)[LM]) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < LM / 4; ++i) {
+        const float4 v = q[i];
+        x[4 * i] = v.x;
+        x[4 * i + 1] = v.y;
+        x[4 * i + 2] = v.z;
+        x[4 * i + 3] = v.w;
+    }
+}
+
 // ------------------------------------------------------------------ forward
 
 template <int LM>
@@ -130,12 +154,8 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
         const int buf = int(t & 1);
         const bool more = t + 1 < a.T;
         if (more && lane < LM) load_step_row(a, bh, t + 1, lane, r);   // in flight during this step
-        if (a.bnd != nullptr && t % a.chunk == 0 && dok) {
-            float* p = a.bnd + ((bh * a.n_chunks + t / a.chunk) * a.L) * a.D + d;
-#pragma unroll
-            for (int l = 0; l < LM; ++l)
-                if (l < a.L) p[int64_t(l) * a.D] = S[l];
-        }
+        if (a.bnd != nullptr && t % a.chunk == 0 && dok)
+            store_column<LM>(a.bnd + ((bh * a.n_chunks + t / a.chunk) * a.D + d) * LM, S);
         const int64_t e = (bh * a.T + t) * a.D + d;
         const float vv = dok ? a.v[e] : 0.0f, ww = dok ? a.w[e] : 0.0f;
         float read = 0.0f;
@@ -183,69 +203,90 @@ __global__ void __launch_bounds__(kMaxDense) gdn2_bwd_kernel(Gdn2Args a) {
     for (int l = 0; l < LM; ++l)
         G[l] = (a.dstate != nullptr && dok && l < a.L) ? a.dstate[(bh * a.L + l) * a.D + d] : 0.0f;
 
-    float* scr = a.scratch + bh * a.scratch_steps * a.L * a.D + d;
+    // Per-head scratch: the state before each step of the current chunk.
+    float* scr = a.scratch + (bh * a.scratch_steps * a.D + (dok ? d : 0)) * LM;
+    const int64_t scr_step = a.D * LM;
     int it = 0;   // step counter over both sweeps: alternates the LDS buffers
     for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
         const int64_t t0 = c * a.chunk;
         const int64_t t1 = t0 + a.chunk < a.T ? t0 + a.chunk : a.T;
 
-        // Recompute the chunk from its boundary; keep the state before each step.
+        // Recompute the chunk from its boundary; keep the state before each
+        // step.  The next step's vectors and dense values load while this one
+        // computes.
         float S[LM];
-        {
-            const float* p = a.bnd_in + ((bh * a.n_chunks + c) * a.L) * a.D + d;
+        if (dok) {
+            load_column<LM>(a.bnd_in + ((bh * a.n_chunks + c) * a.D + d) * LM, S);
+        } else {
 #pragma unroll
-            for (int l = 0; l < LM; ++l) S[l] = (dok && l < a.L) ? p[int64_t(l) * a.D] : 0.0f;
+            for (int l = 0; l < LM; ++l) S[l] = 0.0f;
+        }
+        float r[4];
+        float vv = 0.0f, ww = 0.0f;
+        if (tid < LM) load_step_row(a, bh, t0, tid, r);
+        if (dok) {
+            vv = a.v[(bh * a.T + t0) * a.D + d];
+            ww = a.w[(bh * a.T + t0) * a.D + d];
         }
         for (int64_t t = t0; t < t1; ++t, ++it) {
             const int buf = it & 1;
-            if (tid < LM) {
-                float r[4];
-                load_step_row(a, bh, t, tid, r);
-                put_step_row<LM>(s_vec[buf], tid, r);
-            }
+            if (tid < LM) put_step_row<LM>(s_vec[buf], tid, r);
             __syncthreads();
-            const int64_t e = (bh * a.T + t) * a.D + d;
-            const float vv = dok ? a.v[e] : 0.0f, ww = dok ? a.w[e] : 0.0f;
-            if (dok) {
-                float* p = scr + (t - t0) * a.L * a.D;
-#pragma unroll
-                for (int l = 0; l < LM; ++l)
-                    if (l < a.L) p[int64_t(l) * a.D] = S[l];
+            const float v_now = vv, w_now = ww;
+            if (t + 1 < t1) {
+                if (tid < LM) load_step_row(a, bh, t + 1, tid, r);
+                if (dok) {
+                    vv = a.v[(bh * a.T + t + 1) * a.D + d];
+                    ww = a.w[(bh * a.T + t + 1) * a.D + d];
+                }
             }
+            if (dok) store_column<LM>(scr + (t - t0) * scr_step, S);
             float read = 0.0f;
 #pragma unroll
             for (int l = 0; l < LM; ++l) {
                 S[l] *= s_vec[buf][kVa][l];
                 read = fmaf(s_vec[buf][kVe][l], S[l], read);
             }
-            const float u = ww * vv - read;
+            const float u = w_now * v_now - read;
 #pragma unroll
             for (int l = 0; l < LM; ++l) S[l] = fmaf(s_vec[buf][kVk][l], u, S[l]);
         }
 
-        // Reverse the chunk.
+        // Reverse the chunk, prefetching one step ahead (downwards) likewise.
+        float dd = 0.0f;
+        if (tid < LM) load_step_row(a, bh, t1 - 1, tid, r);
+        if (dok) {
+            const int64_t e = (bh * a.T + t1 - 1) * a.D + d;
+            vv = a.v[e];
+            ww = a.w[e];
+            dd = a.dctx[e];
+        }
         for (int64_t t = t1 - 1; t >= t0; --t, ++it) {
             const int buf = it & 1;
-            if (tid < LM) {
-                float r[4];
-                load_step_row(a, bh, t, tid, r);
-                put_step_row<LM>(s_vec[buf], tid, r);
-            }
+            if (tid < LM) put_step_row<LM>(s_vec[buf], tid, r);
             __syncthreads();
             const float(*sv)[LM] = s_vec[buf];
             const int64_t e = (bh * a.T + t) * a.D + d;
-            const float vv = dok ? a.v[e] : 0.0f, ww = dok ? a.w[e] : 0.0f;
-            const float dov = dok ? a.dctx[e] * a.scale : 0.0f;
             float Sp[LM];   // state before step t, column d
-            {
-                const float* p = scr + (t - t0) * a.L * a.D;
+            if (dok) {
+                load_column<LM>(scr + (t - t0) * scr_step, Sp);
+            } else {
 #pragma unroll
-                for (int l = 0; l < LM; ++l) Sp[l] = (dok && l < a.L) ? p[int64_t(l) * a.D] : 0.0f;
+                for (int l = 0; l < LM; ++l) Sp[l] = 0.0f;
+            }
+            const float v_now = vv, w_now = ww, dov = dd * a.scale;
+            if (t > t0) {
+                if (tid < LM) load_step_row(a, bh, t - 1, tid, r);
+                if (dok) {
+                    vv = a.v[e - a.D];
+                    ww = a.w[e - a.D];
+                    dd = a.dctx[e - a.D];
+                }
             }
             float read = 0.0f;
 #pragma unroll
             for (int l = 0; l < LM; ++l) read = fmaf(sv[kVe][l], sv[kVa][l] * Sp[l], read);
-            const float u = ww * vv - read;
+            const float u = w_now * v_now - read;
 
             // Read-out: the state after the step, and G += q do^T / sqrt(L).
             float x[LM];
@@ -264,8 +305,8 @@ __global__ void __launch_bounds__(kMaxDense) gdn2_bwd_kernel(Gdn2Args a) {
             }
             const float r_k = wave_row_sum<LM, 32>(x, lane);
             if (dok) {
-                if (a.dw != nullptr) a.dw[e] = du * vv;
-                if (a.dv != nullptr) a.dv[e] = du * ww;
+                if (a.dw != nullptr) a.dw[e] = du * v_now;
+                if (a.dv != nullptr) a.dv[e] = du * w_now;
             }
             // Erased read-out: its cotangent is -du; the erased key gets
             // (decayed state) (-du), the decayed state gets e (-du).
@@ -329,6 +370,8 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
     z->scratch_steps = chunk < T ? chunk : T;
     if (z->BH * z->n_chunks > kMaxElems / (L * D)) return QC_ERR_SHAPE;
     z->lm = L <= 8 ? 8 : L <= 16 ? 16 : L <= 32 ? 32 : 64;
+    if (z->BH * (z->n_chunks > z->scratch_steps ? z->n_chunks : z->scratch_steps) > kMaxElems / (z->lm * D))
+        return QC_ERR_SHAPE;
     return QC_OK;
 }
 
@@ -371,13 +414,13 @@ extern "C" {
 size_t gdn2_boundary_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk) {
     qc::Sizes z;
     if (qc::check_sizes(B, H, T, L, D, chunk, &z) != QC_OK) return 0;
-    return size_t(z.BH * z.n_chunks * L * D) * sizeof(float);
+    return size_t(z.BH * z.n_chunks * D * z.lm) * sizeof(float);
 }
 
 size_t gdn2_scratch_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk) {
     qc::Sizes z;
     if (qc::check_sizes(B, H, T, L, D, chunk, &z) != QC_OK) return 0;
-    return size_t(z.BH * z.scratch_steps * L * D) * sizeof(float);
+    return size_t(z.BH * z.scratch_steps * D * z.lm) * sizeof(float);
 }
 
 int gdn2_fwd(const float* query, const float* key, const float* value, const float* erase, const float* write,
@@ -396,7 +439,8 @@ int gdn2_fwd(const float* query, const float* key, const float* value, const flo
         if (p && !qc::aligned4(p)) return QC_ERR_ALIGN;
     const size_t f = sizeof(float);
     const size_t nl = size_t(z.BH * T * L) * f, nd = size_t(z.BH * T * D) * f, ns = size_t(z.BH * L * D) * f;
-    const size_t nb = size_t(z.BH * z.n_chunks * L * D) * f;
+    const size_t nb = size_t(z.BH * z.n_chunks * D * z.lm) * f;
+    if (boundary && (reinterpret_cast<uintptr_t>(boundary) & 15)) return QC_ERR_ALIGN;
     const qc::Span sp[] = {{context, nd}, {final_state, ns}, {boundary, nb},
                            {query, nl}, {key, nl}, {value, nd}, {erase, nl}, {write, nd}, {log_decay, nl},
                            {initial_state, ns}};
@@ -428,8 +472,10 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     if (!d_query && !d_key && !d_value && !d_erase && !d_write && !d_log_decay && !d_initial_state) return QC_OK;
     const size_t f = sizeof(float);
     const size_t nl = size_t(z.BH * T * L) * f, nd = size_t(z.BH * T * D) * f, ns = size_t(z.BH * L * D) * f;
-    const size_t nb = size_t(z.BH * z.n_chunks * L * D) * f, nscr = size_t(z.BH * z.scratch_steps * L * D) * f;
+    const size_t nb = size_t(z.BH * z.n_chunks * D * z.lm) * f;
+    const size_t nscr = size_t(z.BH * z.scratch_steps * D * z.lm) * f;
     if (!scratch || scratch_bytes < nscr) return QC_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(boundary) & 15) || (reinterpret_cast<uintptr_t>(scratch) & 15)) return QC_ERR_ALIGN;
     for (const void* p : {static_cast<const void*>(query), static_cast<const void*>(key),
                           static_cast<const void*>(value), static_cast<const void*>(erase),
                           static_cast<const void*>(write), static_cast<const void*>(log_decay),

@@ -211,9 +211,11 @@ def test_scan_node_refuses_host_tensors():
 def test_gdn2_sizes_and_validation(lib):
     """Gated DeltaNet-2 entry points: documented buffer sizes, and bad
     arguments refused before any HIP call (fake device pointers)."""
-    assert lib.gdn2_boundary_bytes(1, 2, 5, 3, 4, 2) == 2 * 3 * 3 * 4 * 4       # heads x chunks x L x D floats
-    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 2) == 2 * 2 * 3 * 4 * 4        # heads x chunk x L x D
-    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 64) == 2 * 5 * 3 * 4 * 4       # a chunk longer than T
+    # heads x chunks x D x LP floats, LP = L = 3 rounded up to 8
+    assert lib.gdn2_boundary_bytes(1, 2, 5, 3, 4, 2) == 2 * 3 * 4 * 8 * 4
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 2) == 2 * 2 * 4 * 8 * 4        # heads x chunk x D x LP
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 64) == 2 * 5 * 4 * 8 * 4       # a chunk longer than T
+    assert lib.gdn2_boundary_bytes(1, 1, 4, 33, 2, 4) == 1 * 1 * 2 * 64 * 4     # L = 33 pads to 64
     assert lib.gdn2_boundary_bytes(1, 1, 1, 65, 4, 1) == 0                      # L > 64
     assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 257, 1) == 0                     # D > 256
     assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 4, 0) == 0
@@ -231,6 +233,7 @@ def test_gdn2_sizes_and_validation(lib):
     outs = [A + (10 + i) * G for i in range(7)]
     base = ins[:6] + [A + 8 * G, A + 9 * G, None] + outs
     assert b(*base, A + 20 * G, 0, 1, 1, 8, 4, 4, 2, None) == E_WS               # scratch too small
+    assert b(*base, A + 20 * G + 4, 1 << 20, 1, 1, 8, 4, 4, 2, None) == E_ALIGN   # scratch not 16-byte aligned
     assert b(*base, None, 1 << 20, 1, 1, 8, 4, 4, 2, None) == E_WS
     assert b(*(ins[:6] + [None, A + 9 * G, None] + outs), A + 20 * G, 1 << 20, 1, 1, 8, 4, 4, 2, None) == E_NULL
     assert b(*(ins[:6] + [A + 8 * G, A + 9 * G, None] + [None] * 7), None, 0, 1, 1, 8, 4, 4, 2, None) == OK
