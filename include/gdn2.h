@@ -20,7 +20,7 @@
  * value, write, context [B, H, T, D]; initial_state, final state [B, H, L, D].
  * The boundary states (entry c = the state before step c * chunk) and the
  * backward's scratch are internal formats, [B, H, ceil(T / chunk), D, LP] and
- * [B, H, min(chunk, T), D, LP] with LP = L rounded up to 8, 16, 32 or 64 (each
+ * [B, H, min(chunk, T), D, LP] with LP = L rounded up to 16, 32 or 64 (each
  * dense column's rows contiguous, rows past L zero); both must be 16-byte
  * aligned.
  *
@@ -33,7 +33,7 @@
  * log_decay) are sums over the dense axis, reduced across the block every step.
  * Arithmetic is float32.
  *
- * Limits: B, H, T, D, chunk >= 1; 1 <= L <= 64; D <= 256; element counts
+ * Limits: B, H, T, D, chunk >= 1; 1 <= L <= 64; D <= 128; element counts
  * below 2^40.
  *
  * Conventions: device pointers owned by the caller; the library never

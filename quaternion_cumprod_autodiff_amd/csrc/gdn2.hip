@@ -4,24 +4,25 @@
 // recompute backward: chunk boundary states, in-chunk recompute, per-step
 // reverse sweep).
 //
-// Forward: one thread per dense column d of one (batch, head); the column
-// S[:, d] of the state lives in registers (columns never interact: the
-// read-out u[d] and the write S[:, d] += k u[d] only touch column d).  The
-// step's latent vectors (q, k, decay, erased key) are the same for every
-// column, so one wave stages them in LDS and every lane reads them as
-// broadcasts; the next step's vectors are loaded while this step computes.
+// Mapping: dense columns of a head's [L, D] state never interact in the
+// forward (the read-out u[d] and the write S[:, d] += k u[d] touch column d
+// only), so each column gets a quad of 4 lanes, lane j of the quad holding
+// rows j*R .. j*R+R-1 (R = LP/4, LP = L rounded up to 16, 32 or 64) in
+// registers.  Sums over a column's rows (the erased read-out, the context,
+// d u) are a partial per lane plus two quad shuffles.  A wave holds 16
+// columns.  Every lane loads its own rows of the step's latent vectors
+// (16 lanes share each address) one step ahead of use.
 //
-// Backward: one block per (batch, head), one thread per dense column (D <= 256,
-// so 4 waves at most and the whole register file of a SIMD per wave).  Chunks
-// are taken in reverse; each is recomputed from its saved boundary state, the
-// state before every step going to a per-head scratch slot (each thread
-// writes and reads back only its own column), then reversed step by step.
-// The cotangents of the dense vectors (value, write) and of the state are
-// per column; those of the latent vectors (query, key, erase, log_decay) are
-// sums over the dense axis: every lane holds one contribution per latent row,
-// a transpose-reduce across the wave (log2(64) shuffle stages that halve the
-// rows each lane carries) leaves every lane with one row's wave sum, and the
-// waves' sums meet in LDS.
+// Forward: one lane per column instead (below); the state is saved every
+// `chunk` steps.  Backward: one block per (batch, head), ceil(D/16) waves.  Chunks are
+// taken in reverse; each is recomputed from its saved boundary state, the
+// state before every step going to a per-head scratch slot (each lane writes
+// and reads back only its own rows), then reversed step by step.  The
+// cotangents of value, write and the state are per column; those of query,
+// key, erase and log_decay are sums over the dense axis: the lanes holding
+// the same rows of the wave's 16 columns reduce them by a transpose-reduce
+// (each stage halves the rows a lane carries), and the waves' sums meet in
+// LDS.
 #include "gdn2.h"
 #include "qc_internal.hpp"
 #include "quat_cumprod.h"
@@ -34,7 +35,9 @@ namespace qc {
 namespace {
 
 constexpr int kMaxLatent = 64;
-constexpr int kMaxDense = 256;
+constexpr int kMaxDense = 128;
+constexpr int kColsPerWave = 16;
+constexpr int kMaxWaves = kMaxDense / kColsPerWave;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 struct Gdn2Args {
@@ -48,79 +51,95 @@ struct Gdn2Args {
     float scale;
 };
 
-// Step vectors in LDS, by row l: query, key, erase, decay = exp(log_decay),
-// erased key = erase * key.  Rows L .. LM-1 are zero (decay 1), so padded
-// rows of the state stay zero and contribute nothing.
-enum { kVq = 0, kVk = 1, kVb = 2, kVa = 3, kVe = 4, kNVec = 5 };
-
-// Loads row `row` (< LM) of step t's vectors into r[0..3] (q, k, b, g).
-__device__ __forceinline__ void load_step_row(const Gdn2Args& a, int64_t bh, int64_t t, int row, float* r) {
-    if (row < a.L) {
-        const int64_t i = (bh * a.T + t) * a.L + row;
-        r[0] = a.q[i];
-        r[1] = a.k[i];
-        r[2] = a.b[i];
-        r[3] = a.g[i];
-    } else {
-        r[0] = r[1] = r[2] = r[3] = 0.0f;
-    }
+// Sum over the 4 lanes of a quad (one column's row blocks).
+__device__ __forceinline__ float quad_sum(float x) {
+    x += __shfl_xor(x, 1);
+    return x + __shfl_xor(x, 2);
 }
 
-template <int LM>
-__device__ __forceinline__ void put_step_row(float (*s)[LM], int row, const float* r) {
-    s[kVq][row] = r[0];
-    s[kVk][row] = r[1];
-    s[kVb][row] = r[2];
-    s[kVa][row] = expf(r[3]);
-    s[kVe][row] = r[2] * r[1];
-}
-
-// Sum of x[0..N) over the wave's lanes, transposed: stage by stage (xor
-// offsets O = 32, 16, ...), each lane keeps the half of its rows selected by
-// its lane bit O and adds the partner's copy of those rows, so after
-// log2(N) stages it holds one row; the remaining offsets sum the lanes that
-// hold the same row.  Lane l ends with the sum of row l >> (6 - log2(LM)).
+// Sum of x[0..N) over the 16 lanes that hold the same rows of the wave's 16
+// columns (lane bits 2..5), transposed: each stage (xor offset O = 32, 16,
+// ...) keeps the half of the rows selected by lane bit O and adds the
+// partner's copy of them; once one row is left, the remaining offsets down to
+// 4 add up the lanes holding the same row.  Lane l ends with row
+// (l >> (6 - log2 N)) & (N - 1) of its quad position's block.
 template <int N, int O>
-__device__ __forceinline__ float wave_row_sum(const float (&x)[N], int lane) {
+__device__ __forceinline__ float cols_row_sum(const float (&x)[N], int lane) {
     if constexpr (N == 1) {
         float s = x[0];
 #pragma unroll
-        for (int o = O; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+        for (int o = O; o >= 4; o >>= 1) s += __shfl_xor(s, o);
         return s;
     } else {
         float y[N / 2];
         const bool up = (lane & O) != 0;
 #pragma unroll
-        for (int j = 0; j < N / 2; ++j) {
-            const float keep = up ? x[j + N / 2] : x[j];
-            const float send = up ? x[j] : x[j + N / 2];
-            y[j] = keep + __shfl_xor(send, O);
+        for (int i = 0; i < N / 2; ++i) {
+            const float keep = up ? x[i + N / 2] : x[i];
+            const float send = up ? x[i] : x[i + N / 2];
+            y[i] = keep + __shfl_xor(send, O);
         }
-        return wave_row_sum<N / 2, O / 2>(y, lane);
+        return cols_row_sum<N / 2, O / 2>(y, lane);
     }
 }
 
-template <int LM>
-constexpr int row_shift() {
-    return LM == 64 ? 0 : LM == 32 ? 1 : LM == 16 ? 2 : 3;
+template <int R>
+constexpr int log2_rows() {
+    return R == 16 ? 4 : R == 8 ? 3 : 2;
 }
 
-// The boundary states and the backward's scratch keep each dense column's LM
-// rows contiguous ([.., d, LM]), so a column moves as LM/4 float4 at
-// immediate offsets from one per-thread address (a [L, D] layout would need
-// a separate uniform base per row).
-template <int LM>
-__device__ __forceinline__ void store_column(float* p, const float (&x)[LM]) {
+// The step's latent vectors at this lane's rows: q, k, b, g.
+template <int R>
+struct StepRows {
+    float q[R], k[R], b[R], g[R];
+};
+
+// Rows r0 .. r0+R-1 of one step's vector: as float4 when L is a multiple of 4
+// (the rows then start 16-byte aligned and every group of 4 is whole), else
+// one by one; rows past L read as zero.
+template <int R>
+__device__ __forceinline__ void load_vec_rows(const float* p, int64_t base, int r0, int64_t L, float (&x)[R]) {
+    if ((L & 3) == 0) {
+        const float4* q = reinterpret_cast<const float4*>(p + base + r0);
+#pragma unroll
+        for (int i = 0; i < R / 4; ++i) {
+            const float4 v = r0 + 4 * i < L ? q[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            x[4 * i] = v.x;
+            x[4 * i + 1] = v.y;
+            x[4 * i + 2] = v.z;
+            x[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) x[i] = r0 + i < L ? p[base + r0 + i] : 0.0f;
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void load_rows(const Gdn2Args& a, int64_t bh, int64_t t, int r0, bool with_q,
+                                          StepRows<R>& s) {
+    const int64_t base = (bh * a.T + t) * a.L;
+    load_vec_rows<R>(a.k, base, r0, a.L, s.k);
+    load_vec_rows<R>(a.b, base, r0, a.L, s.b);
+    load_vec_rows<R>(a.g, base, r0, a.L, s.g);
+    if (with_q) load_vec_rows<R>(a.q, base, r0, a.L, s.q);
+}
+
+// The boundary states and the backward's scratch keep each dense column's LP
+// rows contiguous ([.., d, LP]); a lane's R rows move as R/4 float4 from one
+// per-lane address.
+template <int R>
+__device__ __forceinline__ void store_rows(float* p, const float (&x)[R]) {
     float4* q = reinterpret_cast<float4*>(p);
 #pragma unroll
-    for (int i = 0; i < LM / 4; ++i) q[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+    for (int i = 0; i < R / 4; ++i) q[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
 }
 
-template <int LM>
-__device__ __forceinline__ void load_column(const float* p, float (&x)[LM]) {
+template <int R>
+__device__ __forceinline__ void load_rows_of(const float* p, float (&x)[R]) {
     const float4* q = reinterpret_cast<const float4*>(p);
 #pragma unroll
-    for (int i = 0; i < LM / 4; ++i) {
+    for (int i = 0; i < R / 4; ++i) {
         const float4 v = q[i];
         x[4 * i] = v.x;
         x[4 * i + 1] = v.y;
@@ -130,181 +149,224 @@ __device__ __forceinline__ void load_column(const float* p, float (&x)[LM]) {
 }
 
 // ------------------------------------------------------------------ forward
+//
+// The forward has no sum over the dense axis, so it takes the column-per-lane
+// mapping: each lane holds all LP rows of one column, and the wave's 64
+// columns share the step's latent vectors, which lanes < LP load one step
+// ahead and stage in LDS (q, k, decay, erased key) for broadcast reads.  Its
+// long per-lane row loops hide that one-step-ahead load.
 
-template <int LM>
+enum { kVq = 0, kVk = 1, kVa = 2, kVe = 3, kNVec = 4 };
+
+template <int LP>
 __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
-    __shared__ float s_vec[2][kNVec][LM];
+    __shared__ float s_vec[2][kNVec][LP];
     const int lane = threadIdx.x;
     const int64_t n_db = (a.D + 63) / 64;
     const int64_t bh = blockIdx.x / n_db;
     const int64_t d = (blockIdx.x % n_db) * 64 + lane;
     const bool dok = d < a.D;
 
-    float S[LM];
+    float S[LP];
 #pragma unroll
-    for (int l = 0; l < LM; ++l) S[l] = (dok && l < a.L) ? a.s0[(bh * a.L + l) * a.D + d] : 0.0f;
+    for (int l = 0; l < LP; ++l) S[l] = (dok && l < a.L) ? a.s0[(bh * a.L + l) * a.D + d] : 0.0f;
 
+    // Row `lane` of a step's q, k, b, g (zero past L: decay 1, erased key 0).
     float r[4];
-    if (lane < LM) {
-        load_step_row(a, bh, 0, lane, r);
-        put_step_row<LM>(s_vec[0], lane, r);
+    auto load_row = [&](int64_t t) {
+        if (lane < a.L) {
+            const int64_t i = (bh * a.T + t) * a.L + lane;
+            r[0] = a.q[i];
+            r[1] = a.k[i];
+            r[2] = a.b[i];
+            r[3] = a.g[i];
+        } else {
+            r[0] = r[1] = r[2] = r[3] = 0.0f;
+        }
+    };
+    auto put_row = [&](int buf) {
+        s_vec[buf][kVq][lane] = r[0];
+        s_vec[buf][kVk][lane] = r[1];
+        s_vec[buf][kVa][lane] = expf(r[3]);
+        s_vec[buf][kVe][lane] = r[2] * r[1];
+    };
+    if (lane < LP) {
+        load_row(0);
+        put_row(0);
     }
     __syncthreads();
     for (int64_t t = 0; t < a.T; ++t) {
         const int buf = int(t & 1);
         const bool more = t + 1 < a.T;
-        if (more && lane < LM) load_step_row(a, bh, t + 1, lane, r);   // in flight during this step
+        if (more && lane < LP) load_row(t + 1);   // in flight during this step
         if (a.bnd != nullptr && t % a.chunk == 0 && dok)
-            store_column<LM>(a.bnd + ((bh * a.n_chunks + t / a.chunk) * a.D + d) * LM, S);
+            store_rows<LP>(a.bnd + ((bh * a.n_chunks + t / a.chunk) * a.D + d) * LP, S);
         const int64_t e = (bh * a.T + t) * a.D + d;
         const float vv = dok ? a.v[e] : 0.0f, ww = dok ? a.w[e] : 0.0f;
-        float read = 0.0f;
+        // The erased read-out in the backward's association (four partial
+        // sums over row blocks of LP/4, combined as its quad shuffles do), so
+        // the backward's recomputed states equal the saved ones bit for bit.
+        constexpr int R = LP / 4;
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int l = 0; l < LM; ++l) {
+        for (int l = 0; l < LP; ++l) {
             S[l] *= s_vec[buf][kVa][l];
-            read = fmaf(s_vec[buf][kVe][l], S[l], read);
+            part[l / R] = fmaf(s_vec[buf][kVe][l], S[l], part[l / R]);
         }
-        const float u = ww * vv - read;
+        const float u = ww * vv - ((part[0] + part[1]) + (part[2] + part[3]));
         float o = 0.0f;
 #pragma unroll
-        for (int l = 0; l < LM; ++l) {
+        for (int l = 0; l < LP; ++l) {
             S[l] = fmaf(s_vec[buf][kVk][l], u, S[l]);
             o = fmaf(s_vec[buf][kVq][l], S[l], o);
         }
         if (dok) a.ctx[e] = o * a.scale;
-        if (more && lane < LM) put_step_row<LM>(s_vec[buf ^ 1], lane, r);
+        if (more && lane < LP) put_row(buf ^ 1);
         __syncthreads();
     }
     if (a.state != nullptr && dok) {
 #pragma unroll
-        for (int l = 0; l < LM; ++l)
+        for (int l = 0; l < LP; ++l)
             if (l < a.L) a.state[(bh * a.L + l) * a.D + d] = S[l];
     }
 }
 
 // ----------------------------------------------------------------- backward
 
-template <int LM>
-__global__ void __launch_bounds__(kMaxDense) gdn2_bwd_kernel(Gdn2Args a) {
-    constexpr int kWaves = kMaxDense / 64;
-    __shared__ float s_vec[2][kNVec][LM];
-    __shared__ float s_red[2][kWaves][4][LM];   // per wave: query, key (outer part), erased key, decay
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int LP>
+__global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
+    constexpr int R = LP / 4;
+    constexpr int kLog = log2_rows<R>();
+    __shared__ float s_red[2][kMaxWaves][4][LP];   // per wave: query, key (outer part), erased key, decay
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane & 3;
     const int n_waves = int(blockDim.x >> 6);
+    const int r0 = j * R;
     const int64_t bh = blockIdx.x;
-    const int64_t d = tid;
+    const int64_t d = int64_t(wave) * kColsPerWave + (lane >> 2);
     const bool dok = d < a.D;
-    constexpr int kShift = row_shift<LM>();
-    const int row = lane >> kShift;
-    const bool row_writer = (lane & ((1 << kShift) - 1)) == 0;
+    // After the column reduction this lane holds row r0 + idx; lanes that
+    // differ only in the bits summed by the final butterfly hold copies.
+    const int idx = (lane >> (6 - kLog)) & (R - 1);
+    const bool row_writer = ((lane >> 2) & ((1 << (4 - kLog)) - 1)) == 0;
 
-    float G[LM];   // cotangent reaching the current state, column d
+    float G[R];   // cotangent reaching the current state, this lane's rows of column d
 #pragma unroll
-    for (int l = 0; l < LM; ++l)
-        G[l] = (a.dstate != nullptr && dok && l < a.L) ? a.dstate[(bh * a.L + l) * a.D + d] : 0.0f;
+    for (int i = 0; i < R; ++i)
+        G[i] = (a.dstate != nullptr && dok && r0 + i < a.L) ? a.dstate[(bh * a.L + r0 + i) * a.D + d] : 0.0f;
 
-    // Per-head scratch: the state before each step of the current chunk.
-    float* scr = a.scratch + (bh * a.scratch_steps * a.D + (dok ? d : 0)) * LM;
-    const int64_t scr_step = a.D * LM;
-    int it = 0;   // step counter over both sweeps: alternates the LDS buffers
+    float* scr = a.scratch + (bh * a.scratch_steps * a.D + (dok ? d : 0)) * LP + r0;
+    const int64_t scr_step = a.D * LP;
+    int it = 0;   // reverse steps so far: alternates the LDS buffers
     for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
         const int64_t t0 = c * a.chunk;
         const int64_t t1 = t0 + a.chunk < a.T ? t0 + a.chunk : a.T;
 
-        // Recompute the chunk from its boundary; keep the state before each
-        // step.  The next step's vectors and dense values load while this one
-        // computes.
-        float S[LM];
+        // Recompute the chunk from its boundary; keep the state before each step.
+        float S[R];
         if (dok) {
-            load_column<LM>(a.bnd_in + ((bh * a.n_chunks + c) * a.D + d) * LM, S);
+            load_rows_of<R>(a.bnd_in + ((bh * a.n_chunks + c) * a.D + d) * LP + r0, S);
         } else {
 #pragma unroll
-            for (int l = 0; l < LM; ++l) S[l] = 0.0f;
+            for (int i = 0; i < R; ++i) S[i] = 0.0f;
         }
-        float r[4];
+        StepRows<R> cur, nxt;
+        load_rows<R>(a, bh, t0, r0, false, cur);
         float vv = 0.0f, ww = 0.0f;
-        if (tid < LM) load_step_row(a, bh, t0, tid, r);
         if (dok) {
             vv = a.v[(bh * a.T + t0) * a.D + d];
             ww = a.w[(bh * a.T + t0) * a.D + d];
         }
-        for (int64_t t = t0; t < t1; ++t, ++it) {
-            const int buf = it & 1;
-            if (tid < LM) put_step_row<LM>(s_vec[buf], tid, r);
-            __syncthreads();
+        for (int64_t t = t0; t < t1; ++t) {
+            const int64_t e = (bh * a.T + t) * a.D + d;
             const float v_now = vv, w_now = ww;
             if (t + 1 < t1) {
-                if (tid < LM) load_step_row(a, bh, t + 1, tid, r);
+                load_rows<R>(a, bh, t + 1, r0, false, nxt);
                 if (dok) {
-                    vv = a.v[(bh * a.T + t + 1) * a.D + d];
-                    ww = a.w[(bh * a.T + t + 1) * a.D + d];
+                    vv = a.v[e + a.D];
+                    ww = a.w[e + a.D];
                 }
             }
-            if (dok) store_column<LM>(scr + (t - t0) * scr_step, S);
+            if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
             float read = 0.0f;
 #pragma unroll
-            for (int l = 0; l < LM; ++l) {
-                S[l] *= s_vec[buf][kVa][l];
-                read = fmaf(s_vec[buf][kVe][l], S[l], read);
+            for (int i = 0; i < R; ++i) {
+                S[i] *= expf(cur.g[i]);
+                read = fmaf(cur.b[i] * cur.k[i], S[i], read);
             }
-            const float u = w_now * v_now - read;
+            const float u = w_now * v_now - quad_sum(read);
 #pragma unroll
-            for (int l = 0; l < LM; ++l) S[l] = fmaf(s_vec[buf][kVk][l], u, S[l]);
+            for (int i = 0; i < R; ++i) S[i] = fmaf(cur.k[i], u, S[i]);
+            cur = nxt;
         }
 
-        // Reverse the chunk, prefetching one step ahead (downwards) likewise.
+        // Reverse the chunk, loading one step ahead (downwards) likewise;
+        // threads tid < L also fetch row tid of k, b, g for the outputs.
+        load_rows<R>(a, bh, t1 - 1, r0, true, cur);
+        float ok_k = 0.0f, ok_b = 0.0f, ok_g = 0.0f;
+        if (tid < a.L) {
+            const int64_t i = (bh * a.T + t1 - 1) * a.L + tid;
+            ok_k = a.k[i];
+            ok_b = a.b[i];
+            ok_g = a.g[i];
+        }
+        float Sp[R], Sn[R];   // state before step t (this lane's rows), and before step t - 1
         float dd = 0.0f;
-        if (tid < LM) load_step_row(a, bh, t1 - 1, tid, r);
         if (dok) {
             const int64_t e = (bh * a.T + t1 - 1) * a.D + d;
             vv = a.v[e];
             ww = a.w[e];
             dd = a.dctx[e];
+            load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, Sp);
+        } else {
+#pragma unroll
+            for (int i = 0; i < R; ++i) Sp[i] = 0.0f;
         }
         for (int64_t t = t1 - 1; t >= t0; --t, ++it) {
             const int buf = it & 1;
-            if (tid < LM) put_step_row<LM>(s_vec[buf], tid, r);
-            __syncthreads();
-            const float(*sv)[LM] = s_vec[buf];
             const int64_t e = (bh * a.T + t) * a.D + d;
-            float Sp[LM];   // state before step t, column d
-            if (dok) {
-                load_column<LM>(scr + (t - t0) * scr_step, Sp);
-            } else {
-#pragma unroll
-                for (int l = 0; l < LM; ++l) Sp[l] = 0.0f;
-            }
             const float v_now = vv, w_now = ww, dov = dd * a.scale;
+            const float out_k = ok_k, out_b = ok_b, out_g = ok_g;
             if (t > t0) {
-                if (tid < LM) load_step_row(a, bh, t - 1, tid, r);
+                load_rows<R>(a, bh, t - 1, r0, true, nxt);
+                if (tid < a.L) {
+                    const int64_t i = (bh * a.T + t - 1) * a.L + tid;
+                    ok_k = a.k[i];
+                    ok_b = a.b[i];
+                    ok_g = a.g[i];
+                }
                 if (dok) {
                     vv = a.v[e - a.D];
                     ww = a.w[e - a.D];
                     dd = a.dctx[e - a.D];
+                    load_rows_of<R>(scr + (t - 1 - t0) * scr_step, Sn);
                 }
+            }
+            // In place: g -> decay a = exp(g), b -> erased key e = b * k.
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                cur.g[i] = expf(cur.g[i]);
+                cur.b[i] *= cur.k[i];
             }
             float read = 0.0f;
 #pragma unroll
-            for (int l = 0; l < LM; ++l) read = fmaf(sv[kVe][l], sv[kVa][l] * Sp[l], read);
-            const float u = w_now * v_now - read;
+            for (int i = 0; i < R; ++i) read = fmaf(cur.b[i], cur.g[i] * Sp[i], read);
+            const float u = w_now * v_now - quad_sum(read);
 
-            // Read-out: the state after the step, and G += q do^T / sqrt(L).
-            float x[LM];
-#pragma unroll
-            for (int l = 0; l < LM; ++l) {
-                x[l] = fmaf(sv[kVa][l], Sp[l], sv[kVk][l] * u) * dov;   // S_t[l] * do / sqrt(L)
-                G[l] = fmaf(sv[kVq][l], dov, G[l]);
-            }
-            const float r_q = wave_row_sum<LM, 32>(x, lane);
-            // Rank-1 write: d u = G^T k, and G u (the key's outer-product part).
+            // Read-out: the state after the step, and G += q do^T / sqrt(L);
+            // then the rank-1 write: d u = G^T k and G u (the key's outer part).
+            float x1[R], x2[R];
             float du = 0.0f;
 #pragma unroll
-            for (int l = 0; l < LM; ++l) {
-                du = fmaf(G[l], sv[kVk][l], du);
-                x[l] = G[l] * u;
+            for (int i = 0; i < R; ++i) {
+                x1[i] = fmaf(cur.g[i], Sp[i], cur.k[i] * u) * dov;   // S_t * do / sqrt(L)
+                G[i] = fmaf(cur.q[i], dov, G[i]);
+                du = fmaf(G[i], cur.k[i], du);
+                x2[i] = G[i] * u;
             }
-            const float r_k = wave_row_sum<LM, 32>(x, lane);
-            if (dok) {
+            const float r_q = cols_row_sum<R, 32>(x1, lane);
+            const float r_k = cols_row_sum<R, 32>(x2, lane);
+            du = quad_sum(du);
+            if (dok && j == 0) {
                 if (a.dw != nullptr) a.dw[e] = du * v_now;
                 if (a.dv != nullptr) a.dv[e] = du * w_now;
             }
@@ -312,20 +374,19 @@ __global__ void __launch_bounds__(kMaxDense) gdn2_bwd_kernel(Gdn2Args a) {
             // (decayed state) (-du), the decayed state gets e (-du).
             const float dr = -du;
 #pragma unroll
-            for (int l = 0; l < LM; ++l) x[l] = sv[kVa][l] * Sp[l] * dr;
-            const float r_e = wave_row_sum<LM, 32>(x, lane);
-#pragma unroll
-            for (int l = 0; l < LM; ++l) {
-                const float dD = fmaf(sv[kVe][l], dr, G[l]);   // cotangent of the decayed state
-                x[l] = dD * Sp[l];
-                G[l] = sv[kVa][l] * dD;                         // cotangent of the state before step t
+            for (int i = 0; i < R; ++i) {
+                x1[i] = cur.g[i] * Sp[i] * dr;
+                const float dD = fmaf(cur.b[i], dr, G[i]);   // cotangent of the decayed state
+                x2[i] = dD * Sp[i];
+                G[i] = cur.g[i] * dD;                        // cotangent of the state before step t
             }
-            const float r_a = wave_row_sum<LM, 32>(x, lane);
+            const float r_e = cols_row_sum<R, 32>(x1, lane);
+            const float r_a = cols_row_sum<R, 32>(x2, lane);
             if (row_writer) {
-                s_red[buf][wave][0][row] = r_q;
-                s_red[buf][wave][1][row] = r_k;
-                s_red[buf][wave][2][row] = r_e;
-                s_red[buf][wave][3][row] = r_a;
+                s_red[buf][wave][0][r0 + idx] = r_q;
+                s_red[buf][wave][1][r0 + idx] = r_k;
+                s_red[buf][wave][2][r0 + idx] = r_e;
+                s_red[buf][wave][3][r0 + idx] = r_a;
             }
             __syncthreads();
             if (tid < a.L) {
@@ -338,16 +399,21 @@ __global__ void __launch_bounds__(kMaxDense) gdn2_bwd_kernel(Gdn2Args a) {
                 }
                 const int64_t i = (bh * a.T + t) * a.L + tid;
                 if (a.dq != nullptr) a.dq[i] = sq;
-                if (a.dk != nullptr) a.dk[i] = fmaf(se, sv[kVb][tid], sk);
-                if (a.db != nullptr) a.db[i] = se * sv[kVk][tid];
-                if (a.dg != nullptr) a.dg[i] = sa * sv[kVa][tid];
+                if (a.dk != nullptr) a.dk[i] = fmaf(se, out_b, sk);
+                if (a.db != nullptr) a.db[i] = se * out_k;
+                if (a.dg != nullptr) a.dg[i] = sa * expf(out_g);
+            }
+            if (t > t0) {
+                cur = nxt;
+#pragma unroll
+                for (int i = 0; i < R; ++i) Sp[i] = Sn[i];
             }
         }
     }
     if (a.ds0 != nullptr && dok) {
 #pragma unroll
-        for (int l = 0; l < LM; ++l)
-            if (l < a.L) a.ds0[(bh * a.L + l) * a.D + d] = G[l];
+        for (int i = 0; i < R; ++i)
+            if (r0 + i < a.L) a.ds0[(bh * a.L + r0 + i) * a.D + d] = G[i];
     }
 }
 
@@ -363,13 +429,13 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
     if (L > kMaxLatent || D > kMaxDense) return QC_ERR_SHAPE;
     if (B > kMaxElems / H) return QC_ERR_SHAPE;
     z->BH = B * H;
-    if (z->BH > (int64_t(1) << 31) / ((D + 63) / 64)) return QC_ERR_SHAPE;
+    if (z->BH > (int64_t(1) << 31) / ((D + kColsPerWave - 1) / kColsPerWave)) return QC_ERR_SHAPE;
     if (T > kMaxElems / z->BH || z->BH * T > kMaxElems / (L > D ? L : D)) return QC_ERR_SHAPE;
     z->T = T; z->L = L; z->D = D; z->chunk = chunk;
     z->n_chunks = (T + chunk - 1) / chunk;
     z->scratch_steps = chunk < T ? chunk : T;
     if (z->BH * z->n_chunks > kMaxElems / (L * D)) return QC_ERR_SHAPE;
-    z->lm = L <= 8 ? 8 : L <= 16 ? 16 : L <= 32 ? 32 : 64;
+    z->lm = L <= 16 ? 16 : L <= 32 ? 32 : 64;
     if (z->BH * (z->n_chunks > z->scratch_steps ? z->n_chunks : z->scratch_steps) > kMaxElems / (z->lm * D))
         return QC_ERR_SHAPE;
     return QC_OK;
@@ -399,7 +465,6 @@ bool any_overlap(const Span* s, int n_out, int n) {
 template <class F>
 hipError_t by_latent(int lm, F&& f) {
     switch (lm) {
-        case 8: return f(std::integral_constant<int, 8>{});
         case 16: return f(std::integral_constant<int, 16>{});
         case 32: return f(std::integral_constant<int, 32>{});
         default: return f(std::integral_constant<int, 64>{});
@@ -498,7 +563,7 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     a.ds0 = d_initial_state; a.scratch = scratch;
     a.T = T; a.L = L; a.D = D; a.chunk = chunk; a.n_chunks = z.n_chunks; a.scratch_steps = z.scratch_steps;
     a.scale = 1.0f / sqrtf(float(L));
-    const unsigned threads = unsigned((D + 63) / 64 * 64);
+    const unsigned threads = unsigned((D + qc::kColsPerWave - 1) / qc::kColsPerWave * 64);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
         void* params[] = {&a};

@@ -211,13 +211,13 @@ def test_scan_node_refuses_host_tensors():
 def test_gdn2_sizes_and_validation(lib):
     """Gated DeltaNet-2 entry points: documented buffer sizes, and bad
     arguments refused before any HIP call (fake device pointers)."""
-    # heads x chunks x D x LP floats, LP = L = 3 rounded up to 8
-    assert lib.gdn2_boundary_bytes(1, 2, 5, 3, 4, 2) == 2 * 3 * 4 * 8 * 4
-    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 2) == 2 * 2 * 4 * 8 * 4        # heads x chunk x D x LP
-    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 64) == 2 * 5 * 4 * 8 * 4       # a chunk longer than T
+    # heads x chunks x D x LP floats, LP = L = 3 rounded up to 16
+    assert lib.gdn2_boundary_bytes(1, 2, 5, 3, 4, 2) == 2 * 3 * 4 * 16 * 4
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 2) == 2 * 2 * 4 * 16 * 4       # heads x chunk x D x LP
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 64) == 2 * 5 * 4 * 16 * 4      # a chunk longer than T
     assert lib.gdn2_boundary_bytes(1, 1, 4, 33, 2, 4) == 1 * 1 * 2 * 64 * 4     # L = 33 pads to 64
     assert lib.gdn2_boundary_bytes(1, 1, 1, 65, 4, 1) == 0                      # L > 64
-    assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 257, 1) == 0                     # D > 256
+    assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 129, 1) == 0                     # D > 128
     assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 4, 0) == 0
     G = 1 << 30
     A = 1 << 44
