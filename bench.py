@@ -427,8 +427,9 @@ def scan_bench(args):
 
 # -------------------------------------------------------- Gated DeltaNet-2
 # The recurrence of include/gdn2.h at the page's training head shape (latent
-# 64, dense 128) over 8 x 16 heads and 2048 steps, chunk 64.
-GDN2_WORKLOAD = (8, 16, 2048, 64, 128, 64)
+# 64, dense 128) over 8 x 16 heads and 2048 steps; boundary states every 32
+# steps (measured fastest of 4 .. 64, within 8% of each other).
+GDN2_WORKLOAD = (8, 16, 2048, 64, 128, 32)
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
@@ -452,6 +453,8 @@ def gdn2_bench(args):
     from quaternion_cumprod_autodiff_amd import capi
 
     B, H, T, L, D, chunk = GDN2_WORKLOAD
+    if args.gdn2_chunk:
+        chunk = args.gdn2_chunk
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(0)
     ins = [torch.randn((B, H, T, L), device=dev, generator=g),
@@ -570,6 +573,8 @@ def main():
                     help="write profiles/traffic_scan_quat.txt from rocprofv3 runs of --scan quat")
     ap.add_argument("--gdn2", action="store_true",
                     help="measure the Gated DeltaNet-2 forward + VJP (include/gdn2.h) instead")
+    ap.add_argument("--gdn2-chunk", type=int, default=0,
+                    help="with --gdn2: steps between saved boundary states (default: the workload's)")
     args = ap.parse_args()
     if args.summarize_scan_traffic:
         cal = read_kv(TRAFFIC_FILE)
