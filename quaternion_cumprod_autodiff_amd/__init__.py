@@ -13,7 +13,8 @@ def __getattr__(name):
     if name in ("quat_cumprod_fwd", "quat_cumprod_bwd", "new_ckpt", "workspace_bytes", "ckpt_bytes"):
         from . import capi
         return getattr(capi, name)
-    if name in ("quat_cumprod", "quat_cumprod_with_final", "QuatCumprodFunction", "scan", "ScanFunction"):
+    if name in ("quat_cumprod", "quat_cumprod_with_final", "QuatCumprodFunction", "scan", "ScanFunction",
+                "gated_deltanet2", "GatedDeltaNet2Function"):
         from . import autograd
         return getattr(autograd, name)
     raise AttributeError(name)

@@ -131,3 +131,45 @@ def scan(body: str, xs: torch.Tensor, init: torch.Tensor, *, num_checkpoints: in
     if torch.is_grad_enabled() and (xs.requires_grad or init.requires_grad):
         return ScanFunction.apply(body, xs, init, num_checkpoints)
     return capi.scan_fwd(body, xs.contiguous(), init.contiguous())
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet-2 (include/gdn2.h) as an autograd node, after the custom
+# backward node of the burn_gdn source page "src/chunk_wy/custom_backward.rs":
+# the forward returns the context and the final state and keeps the inputs and
+# the boundary states; the backward recomputes in-chunk states from them and
+# returns a cotangent for each tracked input only.  Here the final state's
+# cotangent is used too when the loss reaches the state.
+
+class GatedDeltaNet2Function(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, query, key, value, erase, write, log_decay, initial_state, chunk: int):
+        ins = [t.contiguous() for t in (query, key, value, erase, write, log_decay, initial_state)]
+        context, state, boundary = capi.gdn2_fwd(*ins, chunk=chunk)
+        ctx.chunk = int(chunk)
+        ctx.save_for_backward(*ins[:6], boundary)
+        return context, state
+
+    @staticmethod
+    def backward(ctx, d_context, d_state):
+        *ins, boundary = ctx.saved_tensors
+        want = tuple(n for n, need in zip(capi.GDN2_INPUTS, ctx.needs_input_grad[:7]) if need)
+        if not want:
+            return (None,) * 8
+        if d_context is None:
+            d_context = torch.zeros_like(ins[2])
+        grads = capi.gdn2_bwd(*ins, boundary, d_context.contiguous(),
+                              None if d_state is None else d_state.contiguous(), chunk=ctx.chunk, want=want)
+        return (*grads, None)
+
+
+def gated_deltanet2(query, key, value, erase, write, log_decay, initial_state, *, chunk: int = 32):
+    """(context [B, H, T, D], final state [B, H, L, D]) of the gated delta-rule
+    recurrence, differentiable in all seven inputs; float32 tensors on the GPU
+    (query, key, erase, log_decay [B, H, T, L]; value, write [B, H, T, D];
+    initial_state [B, H, L, D])."""
+    ins = (query, key, value, erase, write, log_decay, initial_state)
+    if torch.is_grad_enabled() and any(t.requires_grad for t in ins):
+        return GatedDeltaNet2Function.apply(*ins, chunk)
+    context, state, _ = capi.gdn2_fwd(*[t.contiguous() for t in ins], chunk=chunk, want_boundary=False)
+    return context, state

@@ -238,3 +238,12 @@ def test_gdn2_sizes_and_validation(lib):
     assert b(*(ins[:6] + [None, A + 9 * G, None] + outs), A + 20 * G, 1 << 20, 1, 1, 8, 4, 4, 2, None) == E_NULL
     assert b(*(ins[:6] + [A + 8 * G, A + 9 * G, None] + [None] * 7), None, 0, 1, 1, 8, 4, 4, 2, None) == OK
     assert b(*(base[:9] + [A + 64] + outs[1:]), A + 20 * G, 1 << 20, 1, 1, 8, 4, 4, 2, None) == E_ALIAS
+
+
+def test_gdn2_node_refuses_host_tensors():
+    import torch
+    from quaternion_cumprod_autodiff_amd.autograd import gated_deltanet2
+    q = torch.zeros((1, 1, 3, 4), requires_grad=True)
+    v = torch.zeros((1, 1, 3, 5))
+    with pytest.raises(ValueError, match="GPU only"):
+        gated_deltanet2(q, q, v, q, v, q, torch.zeros((1, 1, 4, 5)))

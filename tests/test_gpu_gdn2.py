@@ -108,3 +108,34 @@ def test_optional_outputs_and_determinism():
             assert torch.equal(x, p)
         else:
             assert p is None
+
+
+def test_autograd_node_against_oracle():
+    """autograd.gated_deltanet2: a loss on both outputs (context and final
+    state); gradients for all seven inputs, then for a tracked subset only."""
+    from quaternion_cumprod_autodiff_amd.autograd import gated_deltanet2
+    B, H, T, L, D = 2, 2, 40, 12, 24
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=8)
+    rng = np.random.default_rng(9)
+    wc = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    ws = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    ts = [torch.from_numpy(arrays[n]).to(DEV).requires_grad_() for n in NAMES]
+    context, state = gated_deltanet2(*ts, chunk=7)
+    ((context * torch.from_numpy(wc).to(DEV)).sum() + (state * torch.from_numpy(ws).to(DEV)).sum()).backward()
+    torch.cuda.synchronize()
+    ref = oracle.gdn2_bwd(*[arrays[n] for n in NAMES], wc, ws)
+    for n, t, r in zip(NAMES, ts, ref):
+        close("grad " + n, t.grad, r)
+    # Only key and initial_state tracked: the others get no gradient.
+    ts2 = [torch.from_numpy(arrays[n]).to(DEV).requires_grad_(n in ("key", "initial_state")) for n in NAMES]
+    context2, _ = gated_deltanet2(*ts2, chunk=7)
+    (context2 * torch.from_numpy(wc).to(DEV)).sum().backward()
+    ref2 = oracle.gdn2_bwd(*[arrays[n] for n in NAMES], wc)
+    for n, t, r in zip(NAMES, ts2, ref2):
+        if n in ("key", "initial_state"):
+            close("grad " + n, t.grad, r)
+        else:
+            assert t.grad is None
+    with torch.no_grad():
+        c3, s3 = gated_deltanet2(*ts, chunk=7)
+    assert c3.grad_fn is None and torch.equal(c3, context.detach()) and torch.equal(s3, state.detach())
