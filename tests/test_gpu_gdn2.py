@@ -139,3 +139,33 @@ def test_autograd_node_against_oracle():
     with torch.no_grad():
         c3, s3 = gated_deltanet2(*ts, chunk=7)
     assert c3.grad_fn is None and torch.equal(c3, context.detach()) and torch.equal(s3, state.detach())
+
+
+def test_bench_workload_sampled_heads():
+    """The bench's launch configuration (8 x 16 heads, 2048 steps, latent 64,
+    dense 128, chunk 32), checked on sampled heads: heads are independent, so
+    the oracle on a head's inputs alone gives that head's exact outputs."""
+    import bench
+    B, H, T, L, D, chunk = bench.GDN2_WORKLOAD
+    g = torch.Generator(device=DEV).manual_seed(0)
+    ins = [torch.randn((B, H, T, L), device=DEV, generator=g),
+           torch.randn((B, H, T, L), device=DEV, generator=g) / L ** 0.5,
+           torch.randn((B, H, T, D), device=DEV, generator=g),
+           torch.rand((B, H, T, L), device=DEV, generator=g),
+           torch.rand((B, H, T, D), device=DEV, generator=g),
+           torch.rand((B, H, T, L), device=DEV, generator=g) - 1.2,
+           torch.randn((B, H, L, D), device=DEV, generator=g)]
+    d_ctx = torch.randn((B, H, T, D), device=DEV, generator=g)
+    ctx, state, bnd = capi.gdn2_fwd(*ins, chunk=chunk)
+    grads = capi.gdn2_bwd(*ins[:6], bnd, d_ctx, chunk=chunk)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H - 1), (3, 7)):
+        print(f"[gdn2 bench workload, head ({b}, {h})]", flush=True)
+        host = [x[b:b + 1, h:h + 1].cpu().numpy() for x in ins]
+        dc = d_ctx[b:b + 1, h:h + 1].cpu().numpy()
+        r_ctx, r_state = oracle.gdn2_fwd(*host)
+        r_grads = oracle.gdn2_bwd(*host, dc)
+        close("context", ctx[b:b + 1, h:h + 1], r_ctx)
+        close("state", state[b:b + 1, h:h + 1], r_state)
+        for n, gr, r in zip(NAMES, grads, r_grads):
+            close("d_" + n, gr[b:b + 1, h:h + 1], r)

@@ -278,3 +278,34 @@ def test_random_shapes_and_snapshot_counts():
             check("ys", host(ys), oracle.scan_fwd(body, xs, init), 2.0 ** -23)
             check("d_xs", host(d_xs), r_dx, 2.0 ** -23)
             check("d_init", host(d_init), r_di, 2.0 ** -23)
+
+
+@pytest.mark.parametrize("k", [0, 8])
+def test_bench_workload_sampled_columns(k):
+    """The scan bench's launch configuration (quaternion body, b1 s129 m2^20,
+    trajectory or 8 snapshots) on sampled columns against the oracle; columns
+    are independent, so a column's oracle result is exact."""
+    import bench
+    from quaternion_cumprod_autodiff_amd.inputs import make_generic_scan_inputs_device
+    b, s, m = bench.SCAN_WORKLOADS["quat"]
+    X, I, U = make_generic_scan_inputs_device("quat", b, s, m, 0, DEV)
+    if k == 0:
+        ys = capi.scan_fwd("quat", X, I)
+        d_xs, d_init = capi.scan_bwd_trajectory("quat", X, I, ys, U)
+        rel_norm = 2.0 ** -21
+    else:
+        sch = capi.ScanSchedule(s, k)
+        snaps = capi.new_snapshots("quat", X, k)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        ys = capi.scan_fwd("quat", X, I, schedule=sch, snaps=snaps)
+        d_xs, d_init = capi.scan_bwd_checkpointed("quat", X, I, U, sch, snaps, after_forward=True, status=status)
+        rel_norm = 0.0
+    torch.cuda.synchronize()
+    if k:
+        assert int(status.item()) == 0
+    cols = np.array([0, 1, 255, 256, 65537, 524287, 524288, m - 1])
+    xs_s, init_s, up_s = host(X[:, :, cols]), host(I[:, cols]), host(U[:, :, cols])
+    check("ys", host(ys[:, :, cols]), oracle.scan_fwd("quat", xs_s, init_s), 2.0 ** -23)
+    r_dx, r_di = oracle.scan_bwd("quat", xs_s, init_s, up_s)
+    check("d_xs", host(d_xs[:, :, cols]), r_dx, 2.0 ** -23, rel_norm)
+    check("d_init", host(d_init[:, cols]), r_di, 2.0 ** -23, rel_norm)
