@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
     auto put_row = [&](int buf) {
         s_vec[buf][kVq][lane] = r[0];
         s_vec[buf][kVk][lane] = r[1];
-        s_vec[buf][kVa][lane] = expf(r[3]);
+        s_vec[buf][kVa][lane] = __expf(r[3]);
         s_vec[buf][kVe][lane] = r[2] * r[1];
     };
     if (lane < LP) {
@@ -248,6 +248,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
     // differ only in the bits summed by the final butterfly hold copies.
     const int idx = (lane >> (6 - kLog)) & (R - 1);
     const bool row_writer = ((lane >> 2) & ((1 << (4 - kLog)) - 1)) == 0;
+    const bool out_lane = tid < a.L;
 
     float G[R];   // cotangent reaching the current state, this lane's rows of column d
 #pragma unroll
@@ -256,6 +257,37 @@ __global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
 
     float* scr = a.scratch + (bh * a.scratch_steps * a.D + (dok ? d : 0)) * LP + r0;
     const int64_t scr_step = a.D * LP;
+    const int64_t col0 = bh * a.T * a.D + d;   // element (t = 0, d) of the dense tensors
+    // Two register sets for a step's inputs, used in turn: one holds the
+    // step being computed, the other receives the next step's loads, and the
+    // step loops are unrolled by two so the roles swap without copies.
+    struct Dense {
+        float v, w, dc;
+    };
+    struct OutRow {
+        float k, b, g;
+    };
+    StepRows<R> rowsA, rowsB;
+    Dense denA{0.0f, 0.0f, 0.0f}, denB{0.0f, 0.0f, 0.0f};
+    float SpA[R], SpB[R];
+    OutRow outA{0.0f, 0.0f, 0.0f}, outB{0.0f, 0.0f, 0.0f};
+
+    auto load_dense = [&](int64_t t, bool with_dc, Dense& dn) {
+        if (dok) {
+            dn.v = a.v[col0 + t * a.D];
+            dn.w = a.w[col0 + t * a.D];
+            if (with_dc) dn.dc = a.dctx[col0 + t * a.D];
+        }
+    };
+    auto load_out = [&](int64_t t, OutRow& o) {
+        if (out_lane) {
+            const int64_t i = (bh * a.T + t) * a.L + tid;
+            o.k = a.k[i];
+            o.b = a.b[i];
+            o.g = a.g[i];
+        }
+    };
+
     int it = 0;   // reverse steps so far: alternates the LDS buffers
     for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
         const int64_t t0 = c * a.chunk;
@@ -269,88 +301,53 @@ __global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
 #pragma unroll
             for (int i = 0; i < R; ++i) S[i] = 0.0f;
         }
-        StepRows<R> cur, nxt;
-        load_rows<R>(a, bh, t0, r0, false, cur);
-        float vv = 0.0f, ww = 0.0f;
-        if (dok) {
-            vv = a.v[(bh * a.T + t0) * a.D + d];
-            ww = a.w[(bh * a.T + t0) * a.D + d];
-        }
-        for (int64_t t = t0; t < t1; ++t) {
-            const int64_t e = (bh * a.T + t) * a.D + d;
-            const float v_now = vv, w_now = ww;
+        auto rec_step = [&](int64_t t, StepRows<R>& cur, Dense& dcur, StepRows<R>& nxt, Dense& dnxt) {
             if (t + 1 < t1) {
                 load_rows<R>(a, bh, t + 1, r0, false, nxt);
-                if (dok) {
-                    vv = a.v[e + a.D];
-                    ww = a.w[e + a.D];
-                }
+                load_dense(t + 1, false, dnxt);
             }
             if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
             float read = 0.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                S[i] *= expf(cur.g[i]);
+                S[i] *= __expf(cur.g[i]);
                 read = fmaf(cur.b[i] * cur.k[i], S[i], read);
             }
-            const float u = w_now * v_now - quad_sum(read);
+            const float u = dcur.w * dcur.v - quad_sum(read);
 #pragma unroll
             for (int i = 0; i < R; ++i) S[i] = fmaf(cur.k[i], u, S[i]);
-            cur = nxt;
+        };
+        load_rows<R>(a, bh, t0, r0, false, rowsA);
+        load_dense(t0, false, denA);
+        for (int64_t t = t0; t < t1; t += 2) {
+            rec_step(t, rowsA, denA, rowsB, denB);
+            if (t + 1 < t1) rec_step(t + 1, rowsB, denB, rowsA, denA);
         }
 
         // Reverse the chunk, loading one step ahead (downwards) likewise;
         // threads tid < L also fetch row tid of k, b, g for the outputs.
-        load_rows<R>(a, bh, t1 - 1, r0, true, cur);
-        float ok_k = 0.0f, ok_b = 0.0f, ok_g = 0.0f;
-        if (tid < a.L) {
-            const int64_t i = (bh * a.T + t1 - 1) * a.L + tid;
-            ok_k = a.k[i];
-            ok_b = a.b[i];
-            ok_g = a.g[i];
-        }
-        float Sp[R], Sn[R];   // state before step t (this lane's rows), and before step t - 1
-        float dd = 0.0f;
-        if (dok) {
-            const int64_t e = (bh * a.T + t1 - 1) * a.D + d;
-            vv = a.v[e];
-            ww = a.w[e];
-            dd = a.dctx[e];
-            load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, Sp);
-        } else {
-#pragma unroll
-            for (int i = 0; i < R; ++i) Sp[i] = 0.0f;
-        }
-        for (int64_t t = t1 - 1; t >= t0; --t, ++it) {
+        auto rev_step = [&](int64_t t, StepRows<R>& cur, Dense& dcur, float (&Sp)[R], OutRow& ocur,
+                            StepRows<R>& nxt, Dense& dnxt, float (&Sn)[R], OutRow& onxt) {
             const int buf = it & 1;
-            const int64_t e = (bh * a.T + t) * a.D + d;
-            const float v_now = vv, w_now = ww, dov = dd * a.scale;
-            const float out_k = ok_k, out_b = ok_b, out_g = ok_g;
+            ++it;
+            const int64_t e = col0 + t * a.D;
             if (t > t0) {
                 load_rows<R>(a, bh, t - 1, r0, true, nxt);
-                if (tid < a.L) {
-                    const int64_t i = (bh * a.T + t - 1) * a.L + tid;
-                    ok_k = a.k[i];
-                    ok_b = a.b[i];
-                    ok_g = a.g[i];
-                }
-                if (dok) {
-                    vv = a.v[e - a.D];
-                    ww = a.w[e - a.D];
-                    dd = a.dctx[e - a.D];
-                    load_rows_of<R>(scr + (t - 1 - t0) * scr_step, Sn);
-                }
+                load_dense(t - 1, true, dnxt);
+                load_out(t - 1, onxt);
+                if (dok) load_rows_of<R>(scr + (t - 1 - t0) * scr_step, Sn);
             }
+            const float dov = dcur.dc * a.scale;
             // In place: g -> decay a = exp(g), b -> erased key e = b * k.
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                cur.g[i] = expf(cur.g[i]);
+                cur.g[i] = __expf(cur.g[i]);
                 cur.b[i] *= cur.k[i];
             }
             float read = 0.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i) read = fmaf(cur.b[i], cur.g[i] * Sp[i], read);
-            const float u = w_now * v_now - quad_sum(read);
+            const float u = dcur.w * dcur.v - quad_sum(read);
 
             // Read-out: the state after the step, and G += q do^T / sqrt(L);
             // then the rank-1 write: d u = G^T k and G u (the key's outer part).
@@ -367,8 +364,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
             const float r_k = cols_row_sum<R, 32>(x2, lane);
             du = quad_sum(du);
             if (dok && j == 0) {
-                if (a.dw != nullptr) a.dw[e] = du * v_now;
-                if (a.dv != nullptr) a.dv[e] = du * w_now;
+                if (a.dw != nullptr) a.dw[e] = du * dcur.v;
+                if (a.dv != nullptr) a.dv[e] = du * dcur.w;
             }
             // Erased read-out: its cotangent is -du; the erased key gets
             // (decayed state) (-du), the decayed state gets e (-du).
@@ -389,7 +386,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
                 s_red[buf][wave][3][r0 + idx] = r_a;
             }
             __syncthreads();
-            if (tid < a.L) {
+            if (out_lane) {
                 float sq = 0.0f, sk = 0.0f, se = 0.0f, sa = 0.0f;
                 for (int wv = 0; wv < n_waves; ++wv) {
                     sq += s_red[buf][wv][0][tid];
@@ -399,15 +396,23 @@ __global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
                 }
                 const int64_t i = (bh * a.T + t) * a.L + tid;
                 if (a.dq != nullptr) a.dq[i] = sq;
-                if (a.dk != nullptr) a.dk[i] = fmaf(se, out_b, sk);
-                if (a.db != nullptr) a.db[i] = se * out_k;
-                if (a.dg != nullptr) a.dg[i] = sa * expf(out_g);
+                if (a.dk != nullptr) a.dk[i] = fmaf(se, ocur.b, sk);
+                if (a.db != nullptr) a.db[i] = se * ocur.k;
+                if (a.dg != nullptr) a.dg[i] = sa * __expf(ocur.g);
             }
-            if (t > t0) {
-                cur = nxt;
+        };
+        load_rows<R>(a, bh, t1 - 1, r0, true, rowsA);
+        load_dense(t1 - 1, true, denA);
+        load_out(t1 - 1, outA);
+        if (dok) {
+            load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
+        } else {
 #pragma unroll
-                for (int i = 0; i < R; ++i) Sp[i] = Sn[i];
-            }
+            for (int i = 0; i < R; ++i) SpA[i] = SpB[i] = 0.0f;
+        }
+        for (int64_t t = t1 - 1; t >= t0; t -= 2) {
+            rev_step(t, rowsA, denA, SpA, outA, rowsB, denB, SpB, outB);
+            if (t - 1 >= t0) rev_step(t - 1, rowsB, denB, SpB, outB, rowsA, denA, SpA, outA);
         }
     }
     if (a.ds0 != nullptr && dok) {
