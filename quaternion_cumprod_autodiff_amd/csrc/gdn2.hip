@@ -49,6 +49,7 @@ struct Gdn2Args {
     float* scratch;
     int64_t T, L, D, chunk, n_chunks, scratch_steps;
     float scale;
+    int vec_rows;   // 1: L % 4 == 0 and q, k, b, g 16-byte aligned, so rows load as float4
 };
 
 // Sum over the 4 lanes of a quad (one column's row blocks).
@@ -94,12 +95,13 @@ struct StepRows {
     float q[R], k[R], b[R], g[R];
 };
 
-// Rows r0 .. r0+R-1 of one step's vector: as float4 when L is a multiple of 4
-// (the rows then start 16-byte aligned and every group of 4 is whole), else
-// one by one; rows past L read as zero.
+// Rows r0 .. r0+R-1 of one step's vector: as float4 when `vec` (L a multiple
+// of 4 and the tensor 16-byte aligned, so the rows start aligned and every
+// group of 4 is whole), else one by one; rows past L read as zero.
 template <int R>
-__device__ __forceinline__ void load_vec_rows(const float* p, int64_t base, int r0, int64_t L, float (&x)[R]) {
-    if ((L & 3) == 0) {
+__device__ __forceinline__ void load_vec_rows(const float* p, int64_t base, int r0, int64_t L, bool vec,
+                                              float (&x)[R]) {
+    if (vec) {
         const float4* q = reinterpret_cast<const float4*>(p + base + r0);
 #pragma unroll
         for (int i = 0; i < R / 4; ++i) {
@@ -119,10 +121,11 @@ template <int R>
 __device__ __forceinline__ void load_rows(const Gdn2Args& a, int64_t bh, int64_t t, int r0, bool with_q,
                                           StepRows<R>& s) {
     const int64_t base = (bh * a.T + t) * a.L;
-    load_vec_rows<R>(a.k, base, r0, a.L, s.k);
-    load_vec_rows<R>(a.b, base, r0, a.L, s.b);
-    load_vec_rows<R>(a.g, base, r0, a.L, s.g);
-    if (with_q) load_vec_rows<R>(a.q, base, r0, a.L, s.q);
+    const bool vec = a.vec_rows != 0;
+    load_vec_rows<R>(a.k, base, r0, a.L, vec, s.k);
+    load_vec_rows<R>(a.b, base, r0, a.L, vec, s.b);
+    load_vec_rows<R>(a.g, base, r0, a.L, vec, s.g);
+    if (with_q) load_vec_rows<R>(a.q, base, r0, a.L, vec, s.q);
 }
 
 // The boundary states and the backward's scratch keep each dense column's LP
@@ -447,6 +450,7 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 struct Span {
     const void* p;
@@ -565,6 +569,8 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     a.q = query; a.k = key; a.v = value; a.b = erase; a.w = write; a.g = log_decay; a.bnd_in = boundary;
     a.dctx = d_context; a.dstate = d_state;
     a.dq = d_query; a.dk = d_key; a.dv = d_value; a.db = d_erase; a.dw = d_write; a.dg = d_log_decay;
+    a.vec_rows = (L % 4 == 0) && qc::aligned16(query) && qc::aligned16(key) && qc::aligned16(erase) &&
+                 qc::aligned16(log_decay);
     a.ds0 = d_initial_state; a.scratch = scratch;
     a.T = T; a.L = L; a.D = D; a.chunk = chunk; a.n_chunks = z.n_chunks; a.scratch_steps = z.scratch_steps;
     a.scale = 1.0f / sqrtf(float(L));

@@ -169,3 +169,29 @@ def test_bench_workload_sampled_heads():
         close("state", state[b:b + 1, h:h + 1], r_state)
         for n, gr, r in zip(NAMES, grads, r_grads):
             close("d_" + n, gr[b:b + 1, h:h + 1], r)
+
+
+def test_latent_tensors_only_4_byte_aligned():
+    """Latent-vector tensors that are 4- but not 16-byte aligned (views one
+    float into a buffer) take the scalar row loads and give the same results."""
+    arrays = make_gdn2_random_inputs(1, 2, 30, 16, 20, seed=12)
+    base = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
+    shifted = []
+    for n, t in zip(NAMES, base):
+        if n in ("query", "key", "erase", "log_decay"):
+            buf = torch.empty(t.numel() + 1, dtype=torch.float32, device=DEV)
+            v = buf[1:].view(t.shape)
+            v.copy_(t)
+            assert v.data_ptr() % 16 != 0
+            shifted.append(v)
+        else:
+            shifted.append(t)
+    d_ctx = torch.randn((1, 2, 30, 20), device=DEV, generator=torch.Generator(device=DEV).manual_seed(4))
+    c1, s1, b1 = capi.gdn2_fwd(*base, chunk=8)
+    c2, s2, b2 = capi.gdn2_fwd(*shifted, chunk=8)
+    g1 = capi.gdn2_bwd(*base[:6], b1, d_ctx, chunk=8)
+    g2 = capi.gdn2_bwd(*shifted[:6], b2, d_ctx, chunk=8)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
