@@ -19,21 +19,24 @@
  * Layout (row-major float32): query, key, erase, log_decay [B, H, T, L];
  * value, write, context [B, H, T, D]; initial_state, final state [B, H, L, D].
  * The boundary states (entry c = the state before step c * chunk) and the
- * backward's scratch are internal formats, [B, H, ceil(T / chunk), D, LP] and
- * [B, H, min(chunk, T), D, LP] with LP = L rounded up to 16, 32 or 64 (each
+ * backward's scratch are internal formats: [B, H, ceil(T / chunk), D, LP], and
+ * [B, H, min(chunk, T), D, LP] followed (D > 64) by the blocks' shares
+ * [B, H, T, ceil(D / 64), 4, L], with LP = L rounded up to 16, 32 or 64 (each
  * dense column's rows contiguous, rows past L zero); both must be 16-byte
  * aligned.
  *
  * Device design: the forward gives each thread one dense column of a head's
  * state (columns evolve independently), in registers, with the step's latent
  * vectors broadcast through LDS; it saves the state every `chunk` steps.  The
- * backward runs one block per head: it walks the chunks in reverse, recomputes
- * each chunk's states from its saved boundary into `scratch`, then reverses
- * the chunk step by step.  The latent-vector cotangents (query, key, erase,
- * log_decay) are sums over the dense axis, reduced across the block every step.
+ * backward runs ceil(D / 64) blocks per head, each over 64 dense columns: it
+ * walks the chunks in reverse, recomputes each chunk's states from its saved
+ * boundary into `scratch`, then reverses the chunk step by step.  The
+ * latent-vector cotangents (query, key, erase, log_decay) are sums over the
+ * dense axis, reduced across each block every step; with several blocks per
+ * head their shares go through `scratch` and a second kernel adds them.
  * Arithmetic is float32.
  *
- * Limits: B, H, T, D, chunk >= 1; 1 <= L <= 64; D <= 128; element counts
+ * Limits: B, H, T, D, chunk >= 1; 1 <= L <= 64; D <= 1024; element counts
  * below 2^40.
  *
  * Conventions: device pointers owned by the caller; the library never

@@ -4,25 +4,26 @@
 // recompute backward: chunk boundary states, in-chunk recompute, per-step
 // reverse sweep).
 //
-// Mapping: dense columns of a head's [L, D] state never interact in the
-// forward (the read-out u[d] and the write S[:, d] += k u[d] touch column d
-// only), so each column gets a quad of 4 lanes, lane j of the quad holding
-// rows j*R .. j*R+R-1 (R = LP/4, LP = L rounded up to 16, 32 or 64) in
-// registers.  Sums over a column's rows (the erased read-out, the context,
-// d u) are a partial per lane plus two quad shuffles.  A wave holds 16
-// columns.  Every lane loads its own rows of the step's latent vectors
-// (16 lanes share each address) one step ahead of use.
+// Forward: dense columns of a head's [L, D] state never interact (the
+// read-out u[d] and the write S[:, d] += k u[d] touch column d only), so each
+// lane holds one column's rows in registers (below); the state is saved every
+// `chunk` steps.
 //
-// Forward: one lane per column instead (below); the state is saved every
-// `chunk` steps.  Backward: one block per (batch, head), ceil(D/16) waves.  Chunks are
-// taken in reverse; each is recomputed from its saved boundary state, the
-// state before every step going to a per-head scratch slot (each lane writes
-// and reads back only its own rows), then reversed step by step.  The
-// cotangents of value, write and the state are per column; those of query,
-// key, erase and log_decay are sums over the dense axis: the lanes holding
-// the same rows of the wave's 16 columns reduce them by a transpose-reduce
-// (each stage halves the rows a lane carries), and the waves' sums meet in
-// LDS.
+// Backward: each dense column gets a quad of 4 lanes, lane j of the quad
+// holding rows j*R .. j*R+R-1 (R = LP/4, LP = L rounded up to 16, 32 or 64) in
+// registers.  Sums over a column's rows (the erased read-out, d u) are a
+// partial per lane plus two quad shuffles.  A wave holds 16 columns, a block
+// 64 (4 waves, one per SIMD); a head takes ceil(D/64) blocks.  Every lane
+// loads its own rows of the step's latent vectors (16 lanes share each
+// address) one step ahead of use.  Chunks are taken in reverse; each is
+// recomputed from its saved boundary state, the state before every step
+// going to a per-head scratch slot (each lane writes and reads back only its
+// own rows), then reversed step by step.  The cotangents of value, write and
+// the state are per column; those of query, key, erase and log_decay are
+// sums over the dense axis: the lanes holding the same rows of the wave's 16
+// columns reduce them by a transpose-reduce (each stage halves the rows a
+// lane carries), the waves' sums meet in LDS, and with several blocks per
+// head a small kernel adds the blocks' shares in block order.
 #include "gdn2.h"
 #include "qc_internal.hpp"
 #include "quat_cumprod.h"
@@ -35,9 +36,10 @@ namespace qc {
 namespace {
 
 constexpr int kMaxLatent = 64;
-constexpr int kMaxDense = 128;
+constexpr int kMaxDense = 1024;
 constexpr int kColsPerWave = 16;
-constexpr int kMaxWaves = kMaxDense / kColsPerWave;
+constexpr int kColsPerBlock = 64;                          // backward: a head's columns in blocks of 64
+constexpr int kBlockWaves = kColsPerBlock / kColsPerWave;  // 4 waves, one per SIMD
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 struct Gdn2Args {
@@ -50,6 +52,8 @@ struct Gdn2Args {
     int64_t T, L, D, chunk, n_chunks, scratch_steps;
     float scale;
     int vec_rows;   // 1: L % 4 == 0 and q, k, b, g 16-byte aligned, so rows load as float4
+    int n_blk;      // backward blocks per head (ceil(D / 64))
+    float* part;    // with n_blk > 1: per-block sums of the latent-vector cotangents, [BH, T, n_blk, 4, L]
 };
 
 // Sum over the 4 lanes of a quad (one column's row blocks).
@@ -237,15 +241,16 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
 // ----------------------------------------------------------------- backward
 
 template <int LP>
-__global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
+__global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
     constexpr int R = LP / 4;
     constexpr int kLog = log2_rows<R>();
-    __shared__ float s_red[2][kMaxWaves][4][LP];   // per wave: query, key (outer part), erased key, decay
+    __shared__ float s_red[2][kBlockWaves][4][LP];   // per wave: query, key (outer part), erased key, decay
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane & 3;
     const int n_waves = int(blockDim.x >> 6);
     const int r0 = j * R;
-    const int64_t bh = blockIdx.x;
-    const int64_t d = int64_t(wave) * kColsPerWave + (lane >> 2);
+    const int64_t bh = blockIdx.x / a.n_blk;
+    const int blk = int(blockIdx.x % a.n_blk);
+    const int64_t d = int64_t(blk) * kColsPerBlock + wave * kColsPerWave + (lane >> 2);
     const bool dok = d < a.D;
     // After the column reduction this lane holds row r0 + idx; lanes that
     // differ only in the bits summed by the final butterfly hold copies.
@@ -397,11 +402,20 @@ __global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
                     se += s_red[buf][wv][2][tid];
                     sa += s_red[buf][wv][3][tid];
                 }
-                const int64_t i = (bh * a.T + t) * a.L + tid;
-                if (a.dq != nullptr) a.dq[i] = sq;
-                if (a.dk != nullptr) a.dk[i] = fmaf(se, ocur.b, sk);
-                if (a.db != nullptr) a.db[i] = se * ocur.k;
-                if (a.dg != nullptr) a.dg[i] = sa * __expf(ocur.g);
+                if (a.n_blk == 1) {
+                    const int64_t i = (bh * a.T + t) * a.L + tid;
+                    if (a.dq != nullptr) a.dq[i] = sq;
+                    if (a.dk != nullptr) a.dk[i] = fmaf(se, ocur.b, sk);
+                    if (a.db != nullptr) a.db[i] = se * ocur.k;
+                    if (a.dg != nullptr) a.dg[i] = sa * __expf(ocur.g);
+                } else if (a.part != nullptr) {
+                    // This block's share; gdn2_sum_kernel adds the blocks of the head.
+                    float* p = a.part + (((bh * a.T + t) * a.n_blk + blk) * 4) * a.L + tid;
+                    p[0] = sq;
+                    p[a.L] = sk;
+                    p[2 * a.L] = se;
+                    p[3 * a.L] = sa;
+                }
             }
         };
         load_rows<R>(a, bh, t1 - 1, r0, true, rowsA);
@@ -425,11 +439,33 @@ __global__ void __launch_bounds__(kMaxWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
     }
 }
 
+// With several blocks per head: the latent-vector cotangents are the sums of
+// the blocks' shares, taken in block order (so the result is deterministic).
+__global__ void __launch_bounds__(256) gdn2_sum_kernel(Gdn2Args a, int64_t n_rows) {
+    const int64_t n = n_rows * a.L;   // n_rows = BH * T
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+        const int64_t row = i / a.L, l = i - row * a.L;
+        const float* p = a.part + row * a.n_blk * 4 * a.L + l;
+        float sq = 0.0f, sk = 0.0f, se = 0.0f, sa = 0.0f;
+        for (int b = 0; b < a.n_blk; ++b, p += 4 * a.L) {
+            sq += p[0];
+            sk += p[a.L];
+            se += p[2 * a.L];
+            sa += p[3 * a.L];
+        }
+        if (a.dq != nullptr) a.dq[i] = sq;
+        if (a.dk != nullptr) a.dk[i] = fmaf(se, a.b[i], sk);
+        if (a.db != nullptr) a.db[i] = se * a.k[i];
+        if (a.dg != nullptr) a.dg[i] = sa * __expf(a.g[i]);
+    }
+}
+
 // ------------------------------------------------------------ host helpers
 
 struct Sizes {
     int64_t BH, T, L, D, chunk, n_chunks, scratch_steps;
-    int lm;
+    int lm, n_blk;
+    size_t state_scratch, part_bytes, scratch_bytes;   // the backward's scratch: states, then block shares
 };
 
 int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk, Sizes* z) {
@@ -446,6 +482,12 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
     z->lm = L <= 16 ? 16 : L <= 32 ? 32 : 64;
     if (z->BH * (z->n_chunks > z->scratch_steps ? z->n_chunks : z->scratch_steps) > kMaxElems / (z->lm * D))
         return QC_ERR_SHAPE;
+    z->n_blk = int((D + kColsPerBlock - 1) / kColsPerBlock);
+    if (z->BH > (int64_t(1) << 31) / z->n_blk) return QC_ERR_SHAPE;
+    if (z->BH * T > kMaxElems / (4 * L * z->n_blk)) return QC_ERR_SHAPE;
+    z->state_scratch = (size_t(z->BH * z->scratch_steps * D * z->lm) * sizeof(float) + 255) / 256 * 256;
+    z->part_bytes = z->n_blk > 1 ? size_t(z->BH * T * z->n_blk * 4 * L) * sizeof(float) : 0;
+    z->scratch_bytes = z->state_scratch + z->part_bytes;
     return QC_OK;
 }
 
@@ -494,7 +536,7 @@ size_t gdn2_boundary_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D
 size_t gdn2_scratch_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk) {
     qc::Sizes z;
     if (qc::check_sizes(B, H, T, L, D, chunk, &z) != QC_OK) return 0;
-    return size_t(z.BH * z.scratch_steps * D * z.lm) * sizeof(float);
+    return z.scratch_bytes;
 }
 
 int gdn2_fwd(const float* query, const float* key, const float* value, const float* erase, const float* write,
@@ -547,7 +589,7 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     const size_t f = sizeof(float);
     const size_t nl = size_t(z.BH * T * L) * f, nd = size_t(z.BH * T * D) * f, ns = size_t(z.BH * L * D) * f;
     const size_t nb = size_t(z.BH * z.n_chunks * D * z.lm) * f;
-    const size_t nscr = size_t(z.BH * z.scratch_steps * D * z.lm) * f;
+    const size_t nscr = z.scratch_bytes;
     if (!scratch || scratch_bytes < nscr) return QC_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(boundary) & 15) || (reinterpret_cast<uintptr_t>(scratch) & 15)) return QC_ERR_ALIGN;
     for (const void* p : {static_cast<const void*>(query), static_cast<const void*>(key),
@@ -574,13 +616,26 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     a.ds0 = d_initial_state; a.scratch = scratch;
     a.T = T; a.L = L; a.D = D; a.chunk = chunk; a.n_chunks = z.n_chunks; a.scratch_steps = z.scratch_steps;
     a.scale = 1.0f / sqrtf(float(L));
-    const unsigned threads = unsigned((D + qc::kColsPerWave - 1) / qc::kColsPerWave * 64);
+    a.n_blk = z.n_blk;
+    const bool want_latent = d_query || d_key || d_erase || d_log_decay;
+    a.part = (z.n_blk > 1 && want_latent) ? reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + z.state_scratch)
+                                          : nullptr;
+    const unsigned threads = z.n_blk > 1 ? unsigned(qc::kBlockWaves * 64)
+                                         : unsigned((D + qc::kColsPerWave - 1) / qc::kColsPerWave * 64);
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
+    hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
         void* params[] = {&a};
         return hipLaunchKernel(reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<decltype(lm)::value>),
-                               dim3(unsigned(z.BH)), dim3(threads), params, 0, st);
+                               dim3(unsigned(z.BH * z.n_blk)), dim3(threads), params, 0, st);
     });
+    if (e == hipSuccess && a.part != nullptr) {
+        int64_t rows = z.BH * T;
+        const int64_t want = (rows * L + 255) / 256;
+        const unsigned blocks = unsigned(want < (int64_t(1) << 20) ? want : (int64_t(1) << 20));
+        void* params[] = {&a, &rows};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&qc::gdn2_sum_kernel), dim3(blocks), dim3(256), params, 0,
+                            st);
+    }
     return e == hipSuccess ? QC_OK : qc::record_hip_error(e);
 }
 

@@ -217,7 +217,11 @@ def test_gdn2_sizes_and_validation(lib):
     assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 4, 64) == 2 * 5 * 4 * 16 * 4      # a chunk longer than T
     assert lib.gdn2_boundary_bytes(1, 1, 4, 33, 2, 4) == 1 * 1 * 2 * 64 * 4     # L = 33 pads to 64
     assert lib.gdn2_boundary_bytes(1, 1, 1, 65, 4, 1) == 0                      # L > 64
-    assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 129, 1) == 0                     # D > 128
+    assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 1025, 1) == 0                    # D > 1024
+    # D = 100: two 64-column blocks per head; the scratch also holds their shares of the
+    # four latent-vector cotangents, [heads, T, blocks, 4, L], after the states (256-byte aligned).
+    states = 2 * 2 * 100 * 16 * 4
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 100, 2) == (states + 255) // 256 * 256 + 2 * 5 * 2 * 4 * 3 * 4
     assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 4, 0) == 0
     G = 1 << 30
     A = 1 << 44
