@@ -4,18 +4,18 @@
 // recompute backward: chunk boundary states, in-chunk recompute, per-step
 // reverse sweep).
 //
-// Forward: dense columns of a head's [L, D] state never interact (the
-// read-out u[d] and the write S[:, d] += k u[d] touch column d only), so each
-// lane holds one column's rows in registers (below); the state is saved every
-// `chunk` steps.
+// Dense columns of a head's [L, D] state never interact in the forward (the
+// read-out u[d] and the write S[:, d] += k u[d] touch column d only); the
+// forward saves the state every `chunk` steps.
 //
-// Backward: each dense column gets a quad of 4 lanes, lane j of the quad
+// Both kernels give each dense column a quad of 4 lanes, lane j of the quad
 // holding rows j*R .. j*R+R-1 (R = LP/4, LP = L rounded up to 16, 32 or 64) in
 // registers.  Sums over a column's rows (the erased read-out, d u) are a
-// partial per lane plus two quad shuffles.  A wave holds 16 columns, a block
-// 64 (4 waves, one per SIMD); a head takes ceil(D/64) blocks.  Every lane
-// loads its own rows of the step's latent vectors (16 lanes share each
-// address) one step ahead of use.  Chunks are taken in reverse; each is
+// partial per lane plus two quad shuffles.  A wave holds 16 columns.  In the
+// backward a block holds 64 (4 waves, one per SIMD), a head takes
+// ceil(D/64) blocks, and every lane loads its own rows of the step's latent
+// vectors (16 lanes share each address) one step ahead of use.  Chunks are
+// taken in reverse; each is
 // recomputed from its saved boundary state, the state before every step
 // going to a per-head scratch slot (each lane writes and reads back only its
 // own rows), then reversed step by step.  The cotangents of value, write and
@@ -157,26 +157,29 @@ __device__ __forceinline__ void load_rows_of(const float* p, float (&x)[R]) {
 
 // ------------------------------------------------------------------ forward
 //
-// The forward has no sum over the dense axis, so it takes the column-per-lane
-// mapping: each lane holds all LP rows of one column, and the wave's 64
-// columns share the step's latent vectors, which lanes < LP load one step
-// ahead and stage in LDS (q, k, decay, erased key) for broadcast reads.  Its
-// long per-lane row loops hide that one-step-ahead load.
+// Same quad-per-column mapping as the backward (a wave holds 16 columns, lane j
+// of a quad rows j*R ..), so the forward's sums are the backward recompute's
+// arithmetic exactly and the recomputed states equal the saved ones bit for
+// bit.  Lanes < LP load the next step's latent vectors while the step
+// computes and stage them in LDS (q, k, decay, erased key), which every lane
+// reads at its own rows.
 
 enum { kVq = 0, kVk = 1, kVa = 2, kVe = 3, kNVec = 4 };
 
 template <int LP>
 __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
+    constexpr int R = LP / 4;
     __shared__ float s_vec[2][kNVec][LP];
-    const int lane = threadIdx.x;
-    const int64_t n_db = (a.D + 63) / 64;
-    const int64_t bh = blockIdx.x / n_db;
-    const int64_t d = (blockIdx.x % n_db) * 64 + lane;
+    const int lane = threadIdx.x, j = lane & 3;
+    const int r0 = j * R;
+    const int64_t n_cb = (a.D + kColsPerWave - 1) / kColsPerWave;
+    const int64_t bh = blockIdx.x / n_cb;
+    const int64_t d = (blockIdx.x % n_cb) * kColsPerWave + (lane >> 2);
     const bool dok = d < a.D;
 
-    float S[LP];
+    float S[R];
 #pragma unroll
-    for (int l = 0; l < LP; ++l) S[l] = (dok && l < a.L) ? a.s0[(bh * a.L + l) * a.D + d] : 0.0f;
+    for (int i = 0; i < R; ++i) S[i] = (dok && r0 + i < a.L) ? a.s0[(bh * a.L + r0 + i) * a.D + d] : 0.0f;
 
     // Row `lane` of a step's q, k, b, g (zero past L: decay 1, erased key 0).
     float r[4];
@@ -201,40 +204,45 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
         load_row(0);
         put_row(0);
     }
+    const int64_t col0 = bh * a.T * a.D + d;
+    float vv = dok ? a.v[col0] : 0.0f, ww = dok ? a.w[col0] : 0.0f;
     __syncthreads();
     for (int64_t t = 0; t < a.T; ++t) {
         const int buf = int(t & 1);
         const bool more = t + 1 < a.T;
-        if (more && lane < LP) load_row(t + 1);   // in flight during this step
-        if (a.bnd != nullptr && t % a.chunk == 0 && dok)
-            store_rows<LP>(a.bnd + ((bh * a.n_chunks + t / a.chunk) * a.D + d) * LP, S);
-        const int64_t e = (bh * a.T + t) * a.D + d;
-        const float vv = dok ? a.v[e] : 0.0f, ww = dok ? a.w[e] : 0.0f;
-        // The erased read-out in the backward's association (four partial
-        // sums over row blocks of LP/4, combined as its quad shuffles do), so
-        // the backward's recomputed states equal the saved ones bit for bit.
-        constexpr int R = LP / 4;
-        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int l = 0; l < LP; ++l) {
-            S[l] *= s_vec[buf][kVa][l];
-            part[l / R] = fmaf(s_vec[buf][kVe][l], S[l], part[l / R]);
+        const float v_now = vv, w_now = ww;
+        if (more) {                                   // in flight during this step
+            if (lane < LP) load_row(t + 1);
+            if (dok) {
+                vv = a.v[col0 + (t + 1) * a.D];
+                ww = a.w[col0 + (t + 1) * a.D];
+            }
         }
-        const float u = ww * vv - ((part[0] + part[1]) + (part[2] + part[3]));
+        if (a.bnd != nullptr && t % a.chunk == 0 && dok)
+            store_rows<R>(a.bnd + ((bh * a.n_chunks + t / a.chunk) * a.D + d) * LP + r0, S);
+        const float(*sv)[LP] = s_vec[buf];
+        float read = 0.0f;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            S[i] *= sv[kVa][r0 + i];
+            read = fmaf(sv[kVe][r0 + i], S[i], read);
+        }
+        const float u = w_now * v_now - quad_sum(read);
         float o = 0.0f;
 #pragma unroll
-        for (int l = 0; l < LP; ++l) {
-            S[l] = fmaf(s_vec[buf][kVk][l], u, S[l]);
-            o = fmaf(s_vec[buf][kVq][l], S[l], o);
+        for (int i = 0; i < R; ++i) {
+            S[i] = fmaf(sv[kVk][r0 + i], u, S[i]);
+            o = fmaf(sv[kVq][r0 + i], S[i], o);
         }
-        if (dok) a.ctx[e] = o * a.scale;
+        o = quad_sum(o);
+        if (dok && j == 0) a.ctx[col0 + t * a.D] = o * a.scale;
         if (more && lane < LP) put_row(buf ^ 1);
         __syncthreads();
     }
     if (a.state != nullptr && dok) {
 #pragma unroll
-        for (int l = 0; l < LP; ++l)
-            if (l < a.L) a.state[(bh * a.L + l) * a.D + d] = S[l];
+        for (int i = 0; i < R; ++i)
+            if (r0 + i < a.L) a.state[(bh * a.L + r0 + i) * a.D + d] = S[i];
     }
 }
 
@@ -566,7 +574,7 @@ int gdn2_fwd(const float* query, const float* key, const float* value, const flo
     a.ctx = context; a.state = final_state; a.bnd = boundary;
     a.T = T; a.L = L; a.D = D; a.chunk = chunk; a.n_chunks = z.n_chunks; a.scratch_steps = z.scratch_steps;
     a.scale = 1.0f / sqrtf(float(L));
-    const unsigned blocks = unsigned(z.BH * ((D + 63) / 64));
+    const unsigned blocks = unsigned(z.BH * ((D + qc::kColsPerWave - 1) / qc::kColsPerWave));
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
         void* params[] = {&a};
