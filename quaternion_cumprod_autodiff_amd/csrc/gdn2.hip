@@ -11,11 +11,11 @@
 // Both kernels give each dense column a quad of 4 lanes, lane j of the quad
 // holding rows j*R .. j*R+R-1 (R = LP/4, LP = L rounded up to 16, 32 or 64) in
 // registers.  Sums over a column's rows (the erased read-out, d u) are a
-// partial per lane plus two quad shuffles.  A wave holds 16 columns.  In the
-// backward a block holds 64 (4 waves, one per SIMD), a head takes
-// ceil(D/64) blocks, and every lane loads its own rows of the step's latent
-// vectors (16 lanes share each address) one step ahead of use.  Chunks are
-// taken in reverse; each is
+// partial per lane plus two quad shuffles.  A wave holds 16 columns.  The
+// step's latent vectors are loaded one step ahead by one thread per row and
+// staged in LDS, where every lane reads its own rows.  In the backward a
+// block holds 64 columns (4 waves, one per SIMD) and a head takes ceil(D/64)
+// blocks.  Chunks are taken in reverse; each is
 // recomputed from its saved boundary state, the state before every step
 // going to a per-head scratch slot (each lane writes and reads back only its
 // own rows), then reversed step by step.  The cotangents of value, write and
@@ -51,7 +51,6 @@ struct Gdn2Args {
     float* scratch;
     int64_t T, L, D, chunk, n_chunks, scratch_steps;
     float scale;
-    int vec_rows;   // 1: L % 4 == 0 and q, k, b, g 16-byte aligned, so rows load as float4
     int n_blk;      // backward blocks per head (ceil(D / 64))
     float* part;    // with n_blk > 1: per-block sums of the latent-vector cotangents, [BH, T, n_blk, 4, L]
 };
@@ -91,45 +90,6 @@ __device__ __forceinline__ float cols_row_sum(const float (&x)[N], int lane) {
 template <int R>
 constexpr int log2_rows() {
     return R == 16 ? 4 : R == 8 ? 3 : 2;
-}
-
-// The step's latent vectors at this lane's rows: q, k, b, g.
-template <int R>
-struct StepRows {
-    float q[R], k[R], b[R], g[R];
-};
-
-// Rows r0 .. r0+R-1 of one step's vector: as float4 when `vec` (L a multiple
-// of 4 and the tensor 16-byte aligned, so the rows start aligned and every
-// group of 4 is whole), else one by one; rows past L read as zero.
-template <int R>
-__device__ __forceinline__ void load_vec_rows(const float* p, int64_t base, int r0, int64_t L, bool vec,
-                                              float (&x)[R]) {
-    if (vec) {
-        const float4* q = reinterpret_cast<const float4*>(p + base + r0);
-#pragma unroll
-        for (int i = 0; i < R / 4; ++i) {
-            const float4 v = r0 + 4 * i < L ? q[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            x[4 * i] = v.x;
-            x[4 * i + 1] = v.y;
-            x[4 * i + 2] = v.z;
-            x[4 * i + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < R; ++i) x[i] = r0 + i < L ? p[base + r0 + i] : 0.0f;
-    }
-}
-
-template <int R>
-__device__ __forceinline__ void load_rows(const Gdn2Args& a, int64_t bh, int64_t t, int r0, bool with_q,
-                                          StepRows<R>& s) {
-    const int64_t base = (bh * a.T + t) * a.L;
-    const bool vec = a.vec_rows != 0;
-    load_vec_rows<R>(a.k, base, r0, a.L, vec, s.k);
-    load_vec_rows<R>(a.b, base, r0, a.L, vec, s.b);
-    load_vec_rows<R>(a.g, base, r0, a.L, vec, s.g);
-    if (with_q) load_vec_rows<R>(a.q, base, r0, a.L, vec, s.q);
 }
 
 // The boundary states and the backward's scratch keep each dense column's LP
@@ -274,20 +234,41 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
     float* scr = a.scratch + (bh * a.scratch_steps * a.D + (dok ? d : 0)) * LP + r0;
     const int64_t scr_step = a.D * LP;
     const int64_t col0 = bh * a.T * a.D + d;   // element (t = 0, d) of the dense tensors
-    // Two register sets for a step's inputs, used in turn: one holds the
-    // step being computed, the other receives the next step's loads, and the
-    // step loops are unrolled by two so the roles swap without copies.
+
+    // Step vectors staged in LDS, two buffers used in turn: threads < LP load
+    // row tid of the next step while the current one computes and publish it
+    // with the step's barrier.  They keep the raw row too (threads < L finish
+    // the latent-vector outputs with k, b and g of their row).
+    __shared__ float s_rows[2][kNVec][LP];
+    const bool loader = tid < LP;
+    auto load_row = [&](int64_t t, float (&r)[4]) {
+        if (loader) {
+            if (tid < a.L) {
+                const int64_t i = (bh * a.T + t) * a.L + tid;
+                r[0] = a.q[i];
+                r[1] = a.k[i];
+                r[2] = a.b[i];
+                r[3] = a.g[i];
+            } else {
+                r[0] = r[1] = r[2] = r[3] = 0.0f;
+            }
+        }
+    };
+    auto put_row = [&](int buf, const float (&r)[4]) {
+        if (loader) {
+            s_rows[buf][kVq][tid] = r[0];
+            s_rows[buf][kVk][tid] = r[1];
+            s_rows[buf][kVa][tid] = __expf(r[3]);
+            s_rows[buf][kVe][tid] = r[2] * r[1];
+        }
+    };
+    // A step's dense inputs in two register sets used in turn (the step loops
+    // are unrolled by two so the roles swap without copies).
     struct Dense {
         float v, w, dc;
     };
-    struct OutRow {
-        float k, b, g;
-    };
-    StepRows<R> rowsA, rowsB;
     Dense denA{0.0f, 0.0f, 0.0f}, denB{0.0f, 0.0f, 0.0f};
     float SpA[R], SpB[R];
-    OutRow outA{0.0f, 0.0f, 0.0f}, outB{0.0f, 0.0f, 0.0f};
-
     auto load_dense = [&](int64_t t, bool with_dc, Dense& dn) {
         if (dok) {
             dn.v = a.v[col0 + t * a.D];
@@ -295,16 +276,10 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             if (with_dc) dn.dc = a.dctx[col0 + t * a.D];
         }
     };
-    auto load_out = [&](int64_t t, OutRow& o) {
-        if (out_lane) {
-            const int64_t i = (bh * a.T + t) * a.L + tid;
-            o.k = a.k[i];
-            o.b = a.b[i];
-            o.g = a.g[i];
-        }
-    };
+    float rl[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // raw row being staged
+    float rc[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // raw row of the step being reversed
 
-    int it = 0;   // reverse steps so far: alternates the LDS buffers
+    int it = 0;   // steps so far (both sweeps): alternates the LDS buffers
     for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
         const int64_t t0 = c * a.chunk;
         const int64_t t1 = t0 + a.chunk < a.T ? t0 + a.chunk : a.T;
@@ -317,52 +292,53 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
 #pragma unroll
             for (int i = 0; i < R; ++i) S[i] = 0.0f;
         }
-        auto rec_step = [&](int64_t t, StepRows<R>& cur, Dense& dcur, StepRows<R>& nxt, Dense& dnxt) {
-            if (t + 1 < t1) {
-                load_rows<R>(a, bh, t + 1, r0, false, nxt);
+        auto rec_step = [&](int64_t t, Dense& dcur, Dense& dnxt) {
+            const int buf = it & 1;
+            ++it;
+            const bool more = t + 1 < t1;
+            if (more) {
+                load_row(t + 1, rl);
                 load_dense(t + 1, false, dnxt);
             }
             if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
+            const float(*sv)[LP] = s_rows[buf];
             float read = 0.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                S[i] *= __expf(cur.g[i]);
-                read = fmaf(cur.b[i] * cur.k[i], S[i], read);
+                S[i] *= sv[kVa][r0 + i];
+                read = fmaf(sv[kVe][r0 + i], S[i], read);
             }
             const float u = dcur.w * dcur.v - quad_sum(read);
 #pragma unroll
-            for (int i = 0; i < R; ++i) S[i] = fmaf(cur.k[i], u, S[i]);
+            for (int i = 0; i < R; ++i) S[i] = fmaf(sv[kVk][r0 + i], u, S[i]);
+            if (more) put_row(buf ^ 1, rl);
+            __syncthreads();
         };
-        load_rows<R>(a, bh, t0, r0, false, rowsA);
+        load_row(t0, rl);
+        put_row(it & 1, rl);
         load_dense(t0, false, denA);
+        __syncthreads();
         for (int64_t t = t0; t < t1; t += 2) {
-            rec_step(t, rowsA, denA, rowsB, denB);
-            if (t + 1 < t1) rec_step(t + 1, rowsB, denB, rowsA, denA);
+            rec_step(t, denA, denB);
+            if (t + 1 < t1) rec_step(t + 1, denB, denA);
         }
 
-        // Reverse the chunk, loading one step ahead (downwards) likewise;
-        // threads tid < L also fetch row tid of k, b, g for the outputs.
-        auto rev_step = [&](int64_t t, StepRows<R>& cur, Dense& dcur, float (&Sp)[R], OutRow& ocur,
-                            StepRows<R>& nxt, Dense& dnxt, float (&Sn)[R], OutRow& onxt) {
+        // Reverse the chunk, loading one step ahead (downwards) likewise.
+        auto rev_step = [&](int64_t t, Dense& dcur, float (&Sp)[R], Dense& dnxt, float (&Sn)[R]) {
             const int buf = it & 1;
             ++it;
+            const bool more = t > t0;
             const int64_t e = col0 + t * a.D;
-            if (t > t0) {
-                load_rows<R>(a, bh, t - 1, r0, true, nxt);
+            if (more) {
+                load_row(t - 1, rl);
                 load_dense(t - 1, true, dnxt);
-                load_out(t - 1, onxt);
                 if (dok) load_rows_of<R>(scr + (t - 1 - t0) * scr_step, Sn);
             }
+            const float(*sv)[LP] = s_rows[buf];
             const float dov = dcur.dc * a.scale;
-            // In place: g -> decay a = exp(g), b -> erased key e = b * k.
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                cur.g[i] = __expf(cur.g[i]);
-                cur.b[i] *= cur.k[i];
-            }
             float read = 0.0f;
 #pragma unroll
-            for (int i = 0; i < R; ++i) read = fmaf(cur.b[i], cur.g[i] * Sp[i], read);
+            for (int i = 0; i < R; ++i) read = fmaf(sv[kVe][r0 + i], sv[kVa][r0 + i] * Sp[i], read);
             const float u = dcur.w * dcur.v - quad_sum(read);
 
             // Read-out: the state after the step, and G += q do^T / sqrt(L);
@@ -371,9 +347,9 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             float du = 0.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                x1[i] = fmaf(cur.g[i], Sp[i], cur.k[i] * u) * dov;   // S_t * do / sqrt(L)
-                G[i] = fmaf(cur.q[i], dov, G[i]);
-                du = fmaf(G[i], cur.k[i], du);
+                x1[i] = fmaf(sv[kVa][r0 + i], Sp[i], sv[kVk][r0 + i] * u) * dov;   // S_t * do / sqrt(L)
+                G[i] = fmaf(sv[kVq][r0 + i], dov, G[i]);
+                du = fmaf(G[i], sv[kVk][r0 + i], du);
                 x2[i] = G[i] * u;
             }
             const float r_q = cols_row_sum<R, 32>(x1, lane);
@@ -388,10 +364,11 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             const float dr = -du;
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                x1[i] = cur.g[i] * Sp[i] * dr;
-                const float dD = fmaf(cur.b[i], dr, G[i]);   // cotangent of the decayed state
+                const float av = sv[kVa][r0 + i];
+                x1[i] = av * Sp[i] * dr;
+                const float dD = fmaf(sv[kVe][r0 + i], dr, G[i]);   // cotangent of the decayed state
                 x2[i] = dD * Sp[i];
-                G[i] = cur.g[i] * dD;                        // cotangent of the state before step t
+                G[i] = av * dD;                                      // cotangent of the state before step t
             }
             const float r_e = cols_row_sum<R, 32>(x1, lane);
             const float r_a = cols_row_sum<R, 32>(x2, lane);
@@ -401,6 +378,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 s_red[buf][wave][2][r0 + idx] = r_e;
                 s_red[buf][wave][3][r0 + idx] = r_a;
             }
+            if (more) put_row(buf ^ 1, rl);
             __syncthreads();
             if (out_lane) {
                 float sq = 0.0f, sk = 0.0f, se = 0.0f, sa = 0.0f;
@@ -413,9 +391,9 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 if (a.n_blk == 1) {
                     const int64_t i = (bh * a.T + t) * a.L + tid;
                     if (a.dq != nullptr) a.dq[i] = sq;
-                    if (a.dk != nullptr) a.dk[i] = fmaf(se, ocur.b, sk);
-                    if (a.db != nullptr) a.db[i] = se * ocur.k;
-                    if (a.dg != nullptr) a.dg[i] = sa * __expf(ocur.g);
+                    if (a.dk != nullptr) a.dk[i] = fmaf(se, rc[2], sk);
+                    if (a.db != nullptr) a.db[i] = se * rc[1];
+                    if (a.dg != nullptr) a.dg[i] = sa * __expf(rc[3]);
                 } else if (a.part != nullptr) {
                     // This block's share; gdn2_sum_kernel adds the blocks of the head.
                     float* p = a.part + (((bh * a.T + t) * a.n_blk + blk) * 4) * a.L + tid;
@@ -425,19 +403,26 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                     p[3 * a.L] = sa;
                 }
             }
+            if (more) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) rc[q] = rl[q];
+            }
         };
-        load_rows<R>(a, bh, t1 - 1, r0, true, rowsA);
+        load_row(t1 - 1, rl);
+        put_row(it & 1, rl);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rc[q] = rl[q];
         load_dense(t1 - 1, true, denA);
-        load_out(t1 - 1, outA);
         if (dok) {
             load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
         } else {
 #pragma unroll
             for (int i = 0; i < R; ++i) SpA[i] = SpB[i] = 0.0f;
         }
+        __syncthreads();
         for (int64_t t = t1 - 1; t >= t0; t -= 2) {
-            rev_step(t, rowsA, denA, SpA, outA, rowsB, denB, SpB, outB);
-            if (t - 1 >= t0) rev_step(t - 1, rowsB, denB, SpB, outB, rowsA, denA, SpA, outA);
+            rev_step(t, denA, SpA, denB, SpB);
+            if (t - 1 >= t0) rev_step(t - 1, denB, SpB, denA, SpA);
         }
     }
     if (a.ds0 != nullptr && dok) {
@@ -500,7 +485,6 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 struct Span {
     const void* p;
@@ -619,8 +603,6 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     a.q = query; a.k = key; a.v = value; a.b = erase; a.w = write; a.g = log_decay; a.bnd_in = boundary;
     a.dctx = d_context; a.dstate = d_state;
     a.dq = d_query; a.dk = d_key; a.dv = d_value; a.db = d_erase; a.dw = d_write; a.dg = d_log_decay;
-    a.vec_rows = (L % 4 == 0) && qc::aligned16(query) && qc::aligned16(key) && qc::aligned16(erase) &&
-                 qc::aligned16(log_decay);
     a.ds0 = d_initial_state; a.scratch = scratch;
     a.T = T; a.L = L; a.D = D; a.chunk = chunk; a.n_chunks = z.n_chunks; a.scratch_steps = z.scratch_steps;
     a.scale = 1.0f / sqrtf(float(L));

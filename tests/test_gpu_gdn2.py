@@ -173,8 +173,8 @@ def test_bench_workload_sampled_heads():
 
 
 def test_latent_tensors_only_4_byte_aligned():
-    """Latent-vector tensors that are 4- but not 16-byte aligned (views one
-    float into a buffer) take the scalar row loads and give the same results."""
+    """Tensors that are 4- but not 16-byte aligned (views one float into a
+    buffer; the API asks for 4) give the same results bit for bit."""
     arrays = make_gdn2_random_inputs(1, 2, 30, 16, 20, seed=12)
     base = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
     shifted = []
