@@ -58,7 +58,8 @@ def test_page_geometries_and_data(geom):
 
 @pytest.mark.parametrize("geom", [(2, 3, 50, 7, 100, 8), (1, 1, 200, 64, 128, 32), (3, 2, 33, 33, 65, 1),
                                   (1, 2, 40, 1, 1, 7), (2, 1, 17, 16, 100, 100), (1, 3, 128, 64, 64, 16),
-                                  (1, 2, 50, 32, 300, 16)],
+                                  (1, 2, 50, 32, 300, 16), (1, 1, 1, 4, 4, 1), (1, 1, 3, 64, 1024, 2),
+                                  (2, 1, 9, 64, 65, 4), (1, 1, 20, 64, 1, 3)],
                          ids=lambda g: "b%dh%dt%dl%dd%dc%d" % g)
 def test_random_shapes_with_final_state_cotangent(geom):
     B, H, T, L, D, chunk = geom
