@@ -160,3 +160,14 @@ def test_scan_entry_points_validate_before_launching(lib):
     assert c(*args(sched=A + 5 * GB + 4)) == E_ALIGN
     assert c(*args(snaps=A + 3 * GB)) == E_ALIAS
     assert c(*args(dxs=None, dinit=None)) == 0
+
+
+def test_spread_block_map_is_a_bijection():
+    """The scan kernels deal blocks to 16 slices of the column range (block b
+    takes position b // 16 of slice b % 16, slices of q + 1 blocks first);
+    this restatement of that map must permute every grid size."""
+    def spread(b, nb, slices=16):
+        q, r, i, k = nb // slices, nb % slices, b % slices, b // slices
+        return i * q + min(i, r) + k
+    for nb in list(range(1, 200)) + [4095, 4096, 4097, 65537]:
+        assert sorted(spread(b, nb) for b in range(nb)) == list(range(nb))
