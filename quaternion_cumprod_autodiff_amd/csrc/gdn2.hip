@@ -37,9 +37,15 @@ namespace {
 
 constexpr int kMaxLatent = 64;
 constexpr int kMaxDense = 1024;
-constexpr int kColsPerWave = 16;
-constexpr int kColsPerBlock = 64;                          // backward: a head's columns in blocks of 64
-constexpr int kBlockWaves = kColsPerBlock / kColsPerWave;  // 4 waves, one per SIMD
+constexpr int kBlockWaves = 4;   // backward blocks: 4 waves, one per SIMD
+
+// Lanes per dense column: 8 when that still leaves each lane 4 or more of
+// the LP padded rows (LP >= 32), else 4; each lane holds LP / Q contiguous rows.
+constexpr int lanes_per_col(int lp) { return lp >= 32 ? 8 : 4; }
+constexpr int cols_per_wave(int lp) { return 64 / lanes_per_col(lp); }
+constexpr int cols_per_block(int lp) { return kBlockWaves * cols_per_wave(lp); }
+constexpr int padded_rows(int64_t L) { return L <= 16 ? 16 : L <= 32 ? 32 : 64; }
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 struct Gdn2Args {
@@ -55,24 +61,27 @@ struct Gdn2Args {
     float* part;    // with n_blk > 1: per-block sums of the latent-vector cotangents, [BH, T, n_blk, 4, L]
 };
 
-// Sum over the 4 lanes of a quad (one column's row blocks).
-__device__ __forceinline__ float quad_sum(float x) {
-    x += __shfl_xor(x, 1);
-    return x + __shfl_xor(x, 2);
+// Sum over the Q lanes of one column (its row blocks), by xor butterfly:
+// every lane of the group gets the same bits (additions commute).
+template <int Q>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int o = 1; o < Q; o <<= 1) x += __shfl_xor(x, o);
+    return x;
 }
 
-// Sum of x[0..N) over the 16 lanes that hold the same rows of the wave's 16
-// columns (lane bits 2..5), transposed: each stage (xor offset O = 32, 16,
-// ...) keeps the half of the rows selected by lane bit O and adds the
+// Sum of x[0..N) over the lanes that hold the same rows of the wave's 64/Q
+// columns (lane bits log2 Q .. 5), transposed: each stage (xor offset O = 32,
+// 16, ...) keeps the half of the rows selected by lane bit O and adds the
 // partner's copy of them; once one row is left, the remaining offsets down to
-// 4 add up the lanes holding the same row.  Lane l ends with row
-// (l >> (6 - log2 N)) & (N - 1) of its quad position's block.
-template <int N, int O>
+// Q add up the lanes holding the same row.  Lane l ends with row
+// (l >> (6 - log2 N)) & (N - 1) of its position's block.
+template <int N, int O, int Q>
 __device__ __forceinline__ float cols_row_sum(const float (&x)[N], int lane) {
     if constexpr (N == 1) {
         float s = x[0];
 #pragma unroll
-        for (int o = O; o >= 4; o >>= 1) s += __shfl_xor(s, o);
+        for (int o = O; o >= Q; o >>= 1) s += __shfl_xor(s, o);
         return s;
     } else {
         float y[N / 2];
@@ -83,13 +92,8 @@ __device__ __forceinline__ float cols_row_sum(const float (&x)[N], int lane) {
             const float send = up ? x[i] : x[i + N / 2];
             y[i] = keep + __shfl_xor(send, O);
         }
-        return cols_row_sum<N / 2, O / 2>(y, lane);
+        return cols_row_sum<N / 2, O / 2, Q>(y, lane);
     }
-}
-
-template <int R>
-constexpr int log2_rows() {
-    return R == 16 ? 4 : R == 8 ? 3 : 2;
 }
 
 // The boundary states and the backward's scratch keep each dense column's LP
@@ -128,13 +132,13 @@ enum { kVq = 0, kVk = 1, kVa = 2, kVe = 3, kNVec = 4 };
 
 template <int LP>
 __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
-    constexpr int R = LP / 4;
+    constexpr int Q = lanes_per_col(LP), R = LP / Q, CPW = cols_per_wave(LP);
     __shared__ float s_vec[2][kNVec][LP];
-    const int lane = threadIdx.x, j = lane & 3;
+    const int lane = threadIdx.x, j = lane & (Q - 1);
     const int r0 = j * R;
-    const int64_t n_cb = (a.D + kColsPerWave - 1) / kColsPerWave;
+    const int64_t n_cb = (a.D + CPW - 1) / CPW;
     const int64_t bh = blockIdx.x / n_cb;
-    const int64_t d = (blockIdx.x % n_cb) * kColsPerWave + (lane >> 2);
+    const int64_t d = (blockIdx.x % n_cb) * CPW + (lane >> ilog2(Q));
     const bool dok = d < a.D;
 
     float S[R];
@@ -187,14 +191,14 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
             S[i] *= sv[kVa][r0 + i];
             read = fmaf(sv[kVe][r0 + i], S[i], read);
         }
-        const float u = w_now * v_now - quad_sum(read);
+        const float u = w_now * v_now - group_sum<Q>(read);
         float o = 0.0f;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             S[i] = fmaf(sv[kVk][r0 + i], u, S[i]);
             o = fmaf(sv[kVq][r0 + i], S[i], o);
         }
-        o = quad_sum(o);
+        o = group_sum<Q>(o);
         if (dok && j == 0) a.ctx[col0 + t * a.D] = o * a.scale;
         if (more && lane < LP) put_row(buf ^ 1);
         __syncthreads();
@@ -210,20 +214,20 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
 
 template <int LP>
 __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
-    constexpr int R = LP / 4;
-    constexpr int kLog = log2_rows<R>();
+    constexpr int Q = lanes_per_col(LP), R = LP / Q, CPW = cols_per_wave(LP), CPB = cols_per_block(LP);
+    constexpr int kLogR = ilog2(R), kLogQ = ilog2(Q);
     __shared__ float s_red[2][kBlockWaves][4][LP];   // per wave: query, key (outer part), erased key, decay
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane & 3;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane & (Q - 1);
     const int n_waves = int(blockDim.x >> 6);
     const int r0 = j * R;
     const int64_t bh = blockIdx.x / a.n_blk;
     const int blk = int(blockIdx.x % a.n_blk);
-    const int64_t d = int64_t(blk) * kColsPerBlock + wave * kColsPerWave + (lane >> 2);
+    const int64_t d = int64_t(blk) * CPB + wave * CPW + (lane >> kLogQ);
     const bool dok = d < a.D;
     // After the column reduction this lane holds row r0 + idx; lanes that
     // differ only in the bits summed by the final butterfly hold copies.
-    const int idx = (lane >> (6 - kLog)) & (R - 1);
-    const bool row_writer = ((lane >> 2) & ((1 << (4 - kLog)) - 1)) == 0;
+    const int idx = (lane >> (6 - kLogR)) & (R - 1);
+    const bool row_writer = ((lane >> kLogQ) & ((1 << (6 - kLogR - kLogQ)) - 1)) == 0;
     const bool out_lane = tid < a.L;
 
     float G[R];   // cotangent reaching the current state, this lane's rows of column d
@@ -308,7 +312,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 S[i] *= sv[kVa][r0 + i];
                 read = fmaf(sv[kVe][r0 + i], S[i], read);
             }
-            const float u = dcur.w * dcur.v - quad_sum(read);
+            const float u = dcur.w * dcur.v - group_sum<Q>(read);
 #pragma unroll
             for (int i = 0; i < R; ++i) S[i] = fmaf(sv[kVk][r0 + i], u, S[i]);
             if (more) put_row(buf ^ 1, rl);
@@ -339,7 +343,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             float read = 0.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i) read = fmaf(sv[kVe][r0 + i], sv[kVa][r0 + i] * Sp[i], read);
-            const float u = dcur.w * dcur.v - quad_sum(read);
+            const float u = dcur.w * dcur.v - group_sum<Q>(read);
 
             // Read-out: the state after the step, and G += q do^T / sqrt(L);
             // then the rank-1 write: d u = G^T k and G u (the key's outer part).
@@ -352,9 +356,9 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 du = fmaf(G[i], sv[kVk][r0 + i], du);
                 x2[i] = G[i] * u;
             }
-            const float r_q = cols_row_sum<R, 32>(x1, lane);
-            const float r_k = cols_row_sum<R, 32>(x2, lane);
-            du = quad_sum(du);
+            const float r_q = cols_row_sum<R, 32, Q>(x1, lane);
+            const float r_k = cols_row_sum<R, 32, Q>(x2, lane);
+            du = group_sum<Q>(du);
             if (dok && j == 0) {
                 if (a.dw != nullptr) a.dw[e] = du * dcur.v;
                 if (a.dv != nullptr) a.dv[e] = du * dcur.w;
@@ -370,8 +374,8 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 x2[i] = dD * Sp[i];
                 G[i] = av * dD;                                      // cotangent of the state before step t
             }
-            const float r_e = cols_row_sum<R, 32>(x1, lane);
-            const float r_a = cols_row_sum<R, 32>(x2, lane);
+            const float r_e = cols_row_sum<R, 32, Q>(x1, lane);
+            const float r_a = cols_row_sum<R, 32, Q>(x2, lane);
             if (row_writer) {
                 s_red[buf][wave][0][r0 + idx] = r_q;
                 s_red[buf][wave][1][r0 + idx] = r_k;
@@ -457,7 +461,7 @@ __global__ void __launch_bounds__(256) gdn2_sum_kernel(Gdn2Args a, int64_t n_row
 
 struct Sizes {
     int64_t BH, T, L, D, chunk, n_chunks, scratch_steps;
-    int lm, n_blk;
+    int lm, cpw, n_blk;   // padded rows, columns per wave, backward blocks per head
     size_t state_scratch, part_bytes, scratch_bytes;   // the backward's scratch: states, then block shares
 };
 
@@ -466,16 +470,17 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
     if (L > kMaxLatent || D > kMaxDense) return QC_ERR_SHAPE;
     if (B > kMaxElems / H) return QC_ERR_SHAPE;
     z->BH = B * H;
-    if (z->BH > (int64_t(1) << 31) / ((D + kColsPerWave - 1) / kColsPerWave)) return QC_ERR_SHAPE;
+    z->lm = padded_rows(L);
+    z->cpw = cols_per_wave(z->lm);
+    if (z->BH > (int64_t(1) << 31) / ((D + z->cpw - 1) / z->cpw)) return QC_ERR_SHAPE;
     if (T > kMaxElems / z->BH || z->BH * T > kMaxElems / (L > D ? L : D)) return QC_ERR_SHAPE;
     z->T = T; z->L = L; z->D = D; z->chunk = chunk;
     z->n_chunks = (T + chunk - 1) / chunk;
     z->scratch_steps = chunk < T ? chunk : T;
     if (z->BH * z->n_chunks > kMaxElems / (L * D)) return QC_ERR_SHAPE;
-    z->lm = L <= 16 ? 16 : L <= 32 ? 32 : 64;
     if (z->BH * (z->n_chunks > z->scratch_steps ? z->n_chunks : z->scratch_steps) > kMaxElems / (z->lm * D))
         return QC_ERR_SHAPE;
-    z->n_blk = int((D + kColsPerBlock - 1) / kColsPerBlock);
+    z->n_blk = int((D + cols_per_block(z->lm) - 1) / cols_per_block(z->lm));
     if (z->BH > (int64_t(1) << 31) / z->n_blk) return QC_ERR_SHAPE;
     if (z->BH * T > kMaxElems / (4 * L * z->n_blk)) return QC_ERR_SHAPE;
     z->state_scratch = (size_t(z->BH * z->scratch_steps * D * z->lm) * sizeof(float) + 255) / 256 * 256;
@@ -558,7 +563,7 @@ int gdn2_fwd(const float* query, const float* key, const float* value, const flo
     a.ctx = context; a.state = final_state; a.bnd = boundary;
     a.T = T; a.L = L; a.D = D; a.chunk = chunk; a.n_chunks = z.n_chunks; a.scratch_steps = z.scratch_steps;
     a.scale = 1.0f / sqrtf(float(L));
-    const unsigned blocks = unsigned(z.BH * ((D + qc::kColsPerWave - 1) / qc::kColsPerWave));
+    const unsigned blocks = unsigned(z.BH * ((D + z.cpw - 1) / z.cpw));
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
         void* params[] = {&a};
@@ -611,7 +616,7 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     a.part = (z.n_blk > 1 && want_latent) ? reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + z.state_scratch)
                                           : nullptr;
     const unsigned threads = z.n_blk > 1 ? unsigned(qc::kBlockWaves * 64)
-                                         : unsigned((D + qc::kColsPerWave - 1) / qc::kColsPerWave * 64);
+                                         : unsigned((D + z.cpw - 1) / z.cpw * 64);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
         void* params[] = {&a};
