@@ -171,6 +171,7 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
     const int64_t col0 = bh * a.T * a.D + d;
     float vv = dok ? a.v[col0] : 0.0f, ww = dok ? a.w[col0] : 0.0f;
     __syncthreads();
+    int64_t until_bnd = 0, n_bnd = 0;   // steps to the next saved boundary, boundaries saved
     for (int64_t t = 0; t < a.T; ++t) {
         const int buf = int(t & 1);
         const bool more = t + 1 < a.T;
@@ -182,8 +183,12 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
                 ww = a.w[col0 + (t + 1) * a.D];
             }
         }
-        if (a.bnd != nullptr && t % a.chunk == 0 && dok)
-            store_rows<R>(a.bnd + ((bh * a.n_chunks + t / a.chunk) * a.D + d) * LP + r0, S);
+        if (until_bnd == 0) {   // t is a multiple of the chunk
+            if (a.bnd != nullptr && dok) store_rows<R>(a.bnd + ((bh * a.n_chunks + n_bnd) * a.D + d) * LP + r0, S);
+            ++n_bnd;
+            until_bnd = a.chunk;
+        }
+        --until_bnd;
         const float(*sv)[LP] = s_vec[buf];
         float read = 0.0f;
 #pragma unroll
