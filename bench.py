@@ -754,6 +754,11 @@ def main():
             "value": round((fwd_bytes + bwd_bytes) / (leaves * 1e-3) / 1e9, 2), "unit": "GB/s",
             "ms_per_step": round(leaves, 4), "steps": args.leaves_steps,
             "mode": "forward saves only q and init; backward re-derives the boundary state from q"}
+    # Practical ceiling beside the roofline: a plain device copy of one tensor
+    # of the workload (read + write), after the timed region.
+    cgbps, cdt = copy_calibration(n * io_bytes, 20, 5)
+    rec["copy_ceiling"] = {"value": round(cgbps, 1), "unit": "GB/s", "ms": round(cdt * 1e3, 4),
+                           "kind": f"torch device-to-device copy of one {n * io_bytes} B tensor, 20 timed"}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(inp)
