@@ -91,3 +91,84 @@ def test_graph_replays_match_eager_and_oracle(case):
         for name, gt, rr in zip(("cum", "d_q", "d_init"), got, ref):
             check(name, to_f64(gt), rr, dtype, s)
     del g
+
+
+def test_gdn2_graph_replays_match_eager():
+    """Gated DeltaNet-2 forward + VJP (two blocks per head, so the summing
+    kernel runs too) captured once and replayed on new inputs, with eager
+    calls between the replays; every replay equals an eager run bit for bit
+    and the first also matches the oracle within the page's tolerance."""
+    from quaternion_cumprod_autodiff_amd.inputs import make_gdn2_random_inputs
+    names = capi.GDN2_INPUTS
+    B, H, T, L, D, chunk = 1, 2, 60, 32, 100, 8
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=20)
+    ins = [torch.from_numpy(arrays[n]).to(DEV) for n in names]
+    d_ctx = torch.randn((B, H, T, D), device=DEV, generator=torch.Generator(device=DEV).manual_seed(21))
+    ctx0, _, bnd0 = capi.gdn2_fwd(*ins, chunk=chunk)   # warm-up outside the capture
+    capi.gdn2_bwd(*ins[:6], bnd0, d_ctx, chunk=chunk)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ctx, state, bnd = capi.gdn2_fwd(*ins, chunk=chunk)
+        grads = capi.gdn2_bwd(*ins[:6], bnd, d_ctx, chunk=chunk)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        new = make_gdn2_random_inputs(B, H, T, L, D, seed=30 + r)
+        for t, n in zip(ins, names):
+            t.copy_(torch.from_numpy(new[n]).to(DEV))
+        d_ctx.copy_(torch.randn((B, H, T, D), device=DEV, generator=torch.Generator(device=DEV).manual_seed(40 + r)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (ctx, state) + tuple(grads)]
+        e_ctx, e_state, e_bnd = capi.gdn2_fwd(*ins, chunk=chunk)
+        e_grads = capi.gdn2_bwd(*ins[:6], e_bnd, d_ctx, chunk=chunk)
+        torch.cuda.synchronize()
+        for x, y in zip(got, (e_ctx, e_state) + tuple(e_grads)):
+            assert torch.equal(x, y), f"replay {r} differs from the eager run"
+        if r == 0:
+            r_ctx, _ = oracle.gdn2_fwd(*[new[n] for n in names])
+            r_grads = oracle.gdn2_bwd(*[new[n] for n in names], d_ctx.cpu().numpy())
+            for gt, rr in zip([got[0]] + got[2:], [r_ctx] + list(r_grads)):
+                err = float(np.abs(gt.cpu().numpy().astype(np.float64) - rr).max())
+                assert err <= 3e-3 + 3e-3 * float(np.abs(rr).max())
+    del g
+
+
+def test_generic_scan_graph_replays_match_eager():
+    """The generic scan's forward and both VJPs (trajectory, and 5 snapshots
+    after the forward) captured once and replayed on new inputs; every replay
+    equals an eager run bit for bit."""
+    b, s, m, k = 2, 300, 70, 5
+    rng = np.random.default_rng(50)
+    X = torch.nn.functional.normalize(torch.from_numpy(rng.standard_normal((b, s, m, 4)).astype(np.float32)),
+                                      dim=-1).to(DEV)
+    I = torch.nn.functional.normalize(torch.from_numpy(rng.standard_normal((b, m, 4)).astype(np.float32)),
+                                      dim=-1).to(DEV)
+    U = torch.from_numpy(rng.standard_normal((b, s, m, 4)).astype(np.float32)).to(DEV)
+    sch = capi.ScanSchedule(s, k)
+    sch.device(DEV)                                   # device copy made outside the capture
+    snaps = capi.new_snapshots("quat", X, k)
+    ys = capi.scan_fwd("quat", X, I, schedule=sch, snaps=snaps)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ys = capi.scan_fwd("quat", X, I, schedule=sch, snaps=snaps)
+        t_dx, t_di = capi.scan_bwd_trajectory("quat", X, I, ys, U)
+        c_dx, c_di = capi.scan_bwd_checkpointed("quat", X, I, U, sch, snaps, after_forward=True)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        X.copy_(torch.nn.functional.normalize(torch.randn(X.shape, device=DEV), dim=-1))
+        U.copy_(torch.randn(U.shape, device=DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (ys, t_dx, t_di, c_dx, c_di)]
+        e_snaps = capi.new_snapshots("quat", X, k)
+        e_ys = capi.scan_fwd("quat", X, I, schedule=sch, snaps=e_snaps)
+        e_t = capi.scan_bwd_trajectory("quat", X, I, e_ys, U)
+        e_c = capi.scan_bwd_checkpointed("quat", X, I, U, sch, e_snaps, after_forward=True)
+        torch.cuda.synchronize()
+        for x, y in zip(got, (e_ys,) + e_t + e_c):
+            assert torch.equal(x, y), f"replay {r} differs from the eager run"
+    del g
