@@ -285,8 +285,19 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             if (with_dc) dn.dc = a.dctx[col0 + t * a.D];
         }
     };
-    float rl[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // raw row being staged
+    // Rows are loaded two steps ahead of their LDS store, so a whole step of
+    // work covers each load: rl holds the row staged at the end of this step,
+    // rn the one loading now.
+    float rl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float rn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float rc[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // raw row of the step being reversed
+    auto shift_rows = [&]() {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            rc[q] = rl[q];
+            rl[q] = rn[q];
+        }
+    };
 
     int it = 0;   // steps so far (both sweeps): alternates the LDS buffers
     for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
@@ -305,10 +316,8 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             const int buf = it & 1;
             ++it;
             const bool more = t + 1 < t1;
-            if (more) {
-                load_row(t + 1, rl);
-                load_dense(t + 1, false, dnxt);
-            }
+            if (t + 2 < t1) load_row(t + 2, rn);
+            if (more) load_dense(t + 1, false, dnxt);
             if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
             const float(*sv)[LP] = s_rows[buf];
             float read = 0.0f;
@@ -322,9 +331,11 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             for (int i = 0; i < R; ++i) S[i] = fmaf(sv[kVk][r0 + i], u, S[i]);
             if (more) put_row(buf ^ 1, rl);
             __syncthreads();
+            shift_rows();
         };
         load_row(t0, rl);
         put_row(it & 1, rl);
+        if (t0 + 1 < t1) load_row(t0 + 1, rl);
         load_dense(t0, false, denA);
         __syncthreads();
         for (int64_t t = t0; t < t1; t += 2) {
@@ -338,8 +349,8 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             ++it;
             const bool more = t > t0;
             const int64_t e = col0 + t * a.D;
+            if (t - 2 >= t0) load_row(t - 2, rn);
             if (more) {
-                load_row(t - 1, rl);
                 load_dense(t - 1, true, dnxt);
                 if (dok) load_rows_of<R>(scr + (t - 1 - t0) * scr_step, Sn);
             }
@@ -412,15 +423,13 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                     p[3 * a.L] = sa;
                 }
             }
-            if (more) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) rc[q] = rl[q];
-            }
+            shift_rows();
         };
         load_row(t1 - 1, rl);
         put_row(it & 1, rl);
 #pragma unroll
         for (int q = 0; q < 4; ++q) rc[q] = rl[q];
+        if (t1 - 2 >= t0) load_row(t1 - 2, rl);
         load_dense(t1 - 1, true, denA);
         if (dok) {
             load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
