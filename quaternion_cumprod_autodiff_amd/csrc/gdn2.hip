@@ -61,12 +61,43 @@ struct Gdn2Args {
     float* part;    // with n_blk > 1: per-block sums of the latent-vector cotangents, [BH, T, n_blk, 4, L]
 };
 
-// Sum over the Q lanes of one column (its row blocks), by xor butterfly:
-// every lane of the group gets the same bits (additions commute).
+// Lane exchanges inside a wave without the LDS crossbar (ds_bpermute costs an
+// LDS round trip per call, on the critical path of every step).  dpp_xor<O>
+// returns x from lane ^ O for O <= 8: quad permutations for 1 and 2; for 4 a
+// mirror of each 8-lane half-row (lane ^ 7) composed with the quad reversal
+// (lane ^ 3); for 8 a rotation of each 16-lane row by 8.  None of them reads
+// outside its row, so every lane gets a defined value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadXor3 = 0x1B;     // quad_perm [3, 2, 1, 0]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane ^ 7 within 8
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8: lane ^ 8 within 16
+
+template <int O>
+__device__ __forceinline__ float dpp_xor(float x) {
+    static_assert(O == 1 || O == 2 || O == 4 || O == 8, "DPP exchange offsets are 1, 2, 4 and 8");
+    if constexpr (O == 1) return dpp_mov<kDppQuadXor1>(x);
+    if constexpr (O == 2) return dpp_mov<kDppQuadXor2>(x);
+    if constexpr (O == 4) return dpp_mov<kDppQuadXor3>(dpp_mov<kDppHalfMirror>(x));
+    if constexpr (O == 8) return dpp_mov<kDppRowRor8>(x);
+    return x;
+}
+
+// Sum over the Q lanes of one column (its row blocks), by xor butterfly
+// (offsets 1, 2, 4): every lane of the group gets the same bits (additions
+// commute).  After the first two stages the four lanes of a quad agree, so
+// the last stage may take the 8-lane mirror instead of lane ^ 4.
 template <int Q>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int o = 1; o < Q; o <<= 1) x += __shfl_xor(x, o);
+    static_assert(Q == 4 || Q == 8, "a column spans 4 or 8 lanes");
+    x += dpp_mov<kDppQuadXor1>(x);
+    x += dpp_mov<kDppQuadXor2>(x);
+    if constexpr (Q == 8) x += dpp_mov<kDppHalfMirror>(x);
     return x;
 }
 
@@ -76,21 +107,36 @@ __device__ __forceinline__ float group_sum(float x) {
 // partner's copy of them; once one row is left, the remaining offsets down to
 // Q add up the lanes holding the same row.  Lane l ends with row
 // (l >> (6 - log2 N)) & (N - 1) of its position's block.
+//
+// For O = 32 and 16 one gfx950 permlane swap does a stage for a pair of rows:
+// with A = x[i] and B = x[i + N/2], swapping A's upper half (odd 16-lane rows)
+// with B's lower half (even rows) leaves A' + B' = A[l] + A[l ^ O] in the lower
+// lanes and B[l ^ O] + B[l] in the upper ones, which is the stage's sum.
 template <int N, int O, int Q>
 __device__ __forceinline__ float cols_row_sum(const float (&x)[N], int lane) {
     if constexpr (N == 1) {
         float s = x[0];
-#pragma unroll
-        for (int o = O; o >= Q; o >>= 1) s += __shfl_xor(s, o);
+        if constexpr (O >= Q) {
+            s += dpp_xor<O>(s);
+            return cols_row_sum<1, O / 2, Q>({s}, lane);
+        }
         return s;
     } else {
         float y[N / 2];
-        const bool up = (lane & O) != 0;
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) {
-            const float keep = up ? x[i + N / 2] : x[i];
-            const float send = up ? x[i] : x[i + N / 2];
-            y[i] = keep + __shfl_xor(send, O);
+            if constexpr (O == 32 || O == 16) {
+                const auto p = O == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]),
+                                                                         __float_as_uint(x[i + N / 2]), false, false)
+                                       : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]),
+                                                                         __float_as_uint(x[i + N / 2]), false, false);
+                y[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+            } else {
+                const bool up = (lane & O) != 0;
+                const float keep = up ? x[i + N / 2] : x[i];
+                const float send = up ? x[i] : x[i + N / 2];
+                y[i] = keep + dpp_xor<O>(send);
+            }
         }
         return cols_row_sum<N / 2, O / 2, Q>(y, lane);
     }
