@@ -464,10 +464,11 @@ def gdn2_fwd(query, key, value, erase, write, log_decay, initial_state, *, chunk
 
 
 def gdn2_bwd(query, key, value, erase, write, log_decay, boundary, d_context, d_state=None, *, chunk: int = 64,
-             want=GDN2_INPUTS, stream=None):
+             want=GDN2_INPUTS, stream=None, scratch=None):
     """Cotangents (query, key, value, erase, write, log_decay, initial_state);
     those not named in ``want`` are None.  ``boundary`` is gdn2_fwd's third
-    output for the same inputs and chunk."""
+    output for the same inputs and chunk.  ``scratch`` (optional) is a float32
+    device tensor of at least gdn2_scratch_bytes; by default one is allocated."""
     B, H, T, L, D, chunk = _gdn2_dims(query, value, chunk)
     ins = dict(zip(GDN2_INPUTS[:6], (query, key, value, erase, write, log_decay)))
     ins["d_context"], ins["d_state"] = d_context, d_state
@@ -477,7 +478,11 @@ def gdn2_bwd(query, key, value, erase, write, log_decay, boundary, d_context, d_
     if boundary is None or boundary.numel() * 4 != nb or boundary.dtype != torch.float32:
         raise ValueError("boundary must be gdn2_fwd's boundary states for the same sizes and chunk")
     nscr = int(lib.gdn2_scratch_bytes(B, H, T, L, D, chunk))
-    scratch = torch.empty(nscr // 4, dtype=torch.float32, device=query.device)
+    if scratch is None:
+        scratch = torch.empty(nscr // 4, dtype=torch.float32, device=query.device)
+    elif (scratch.dtype != torch.float32 or scratch.device != query.device or not scratch.is_contiguous()
+          or scratch.numel() * 4 < nscr):
+        raise ValueError(f"scratch must be a contiguous float32 tensor of at least {nscr} bytes on {query.device}")
     outs = {}
     for name, src in zip(GDN2_INPUTS, (query, key, value, erase, write, log_decay, None)):
         shp = (B, H, L, D) if name == "initial_state" else tuple(src.shape)

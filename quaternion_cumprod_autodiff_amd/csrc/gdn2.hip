@@ -88,6 +88,14 @@ __device__ __forceinline__ float dpp_xor(float x) {
     return x;
 }
 
+// A product the compiler may not fuse into a later add or subtract: the
+// update's write * value is rounded on its own, the same way in the forward
+// and in the backward's recompute, wherever the compiler schedules it.
+__device__ __forceinline__ float mul_unfused(float x, float y) {
+#pragma clang fp contract(off)
+    return x * y;
+}
+
 // Sum over the Q lanes of one column (its row blocks), by xor butterfly
 // (offsets 1, 2, 4): every lane of the group gets the same bits (additions
 // commute).  After the first two stages the four lanes of a quad agree, so
@@ -167,14 +175,26 @@ __device__ __forceinline__ void load_rows_of(const float* p, float (&x)[R]) {
 
 // ------------------------------------------------------------------ forward
 //
-// Same quad-per-column mapping as the backward (a wave holds 16 columns, lane j
-// of a quad rows j*R ..), so the forward's sums are the backward recompute's
+// Same mapping as the backward (Q lanes per column, lane j of a column's group
+// holding rows j*R ..), so the forward's sums are the backward recompute's
 // arithmetic exactly and the recomputed states equal the saved ones bit for
-// bit.  Lanes < LP load the next step's latent vectors while the step
-// computes and stage them in LDS (q, k, decay, erased key), which every lane
-// reads at its own rows.
+// bit.  The step's latent vectors are staged in LDS (q, k, decay, erased key,
+// and for the backward the raw erase), where every lane reads its own rows.
+//
+// Loads run two steps ahead, into two register sets taken in turn by the
+// two-step unrolled loops, so a load has a whole step to land before its
+// value is used and is never copied while in flight.  Every lane loads every
+// step: rows past L read row L-1, columns past D read column D-1 and steps
+// past the range repeat its last step (values that are then masked or
+// unused), so the loads are unconditional and the compiler's wait counts
+// stay exact.
 
-enum { kVq = 0, kVk = 1, kVa = 2, kVe = 3, kNVec = 4 };
+enum { kVq = 0, kVk = 1, kVa = 2, kVe = 3, kVb = 4, kNVec = 4, kNRow = 5 };
+
+// One latent row of a step: raw query, key, erase and log-decay.
+struct Row {
+    float q, k, b, g;
+};
 
 template <int LP>
 __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
@@ -186,49 +206,49 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
     const int64_t bh = blockIdx.x / n_cb;
     const int64_t d = (blockIdx.x % n_cb) * CPW + (lane >> ilog2(Q));
     const bool dok = d < a.D;
+    const bool live = lane < a.L;                       // this lane's staged row is a real one
+    const int64_t row0 = bh * a.T * a.L + (live ? lane : a.L - 1);
+    const int64_t col0 = bh * a.T * a.D + (dok ? d : a.D - 1);
 
     float S[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) S[i] = (dok && r0 + i < a.L) ? a.s0[(bh * a.L + r0 + i) * a.D + d] : 0.0f;
 
-    // Row `lane` of a step's q, k, b, g (zero past L: decay 1, erased key 0).
-    float r[4];
-    auto load_row = [&](int64_t t) {
-        if (lane < a.L) {
-            const int64_t i = (bh * a.T + t) * a.L + lane;
-            r[0] = a.q[i];
-            r[1] = a.k[i];
-            r[2] = a.b[i];
-            r[3] = a.g[i];
-        } else {
-            r[0] = r[1] = r[2] = r[3] = 0.0f;
+    // A step's inputs as this lane loads them: its row and its column's value and write.
+    struct In {
+        Row r;
+        float v, w;
+    };
+    auto load_in = [&](int64_t t, In& x) {
+        const int64_t tl = t < a.T ? t : a.T - 1;
+        const int64_t i = row0 + tl * a.L, e = col0 + tl * a.D;
+        x.r.q = a.q[i];
+        x.r.k = a.k[i];
+        x.r.b = a.b[i];
+        x.r.g = a.g[i];
+        x.v = a.v[e];
+        x.w = a.w[e];
+    };
+    auto put_row = [&](int buf, const Row& r) {
+        if (lane < LP) {
+            s_vec[buf][kVq][lane] = live ? r.q : 0.0f;
+            s_vec[buf][kVk][lane] = live ? r.k : 0.0f;
+            s_vec[buf][kVa][lane] = live ? __expf(r.g) : 1.0f;
+            s_vec[buf][kVe][lane] = live ? r.b * r.k : 0.0f;
         }
     };
-    auto put_row = [&](int buf) {
-        s_vec[buf][kVq][lane] = r[0];
-        s_vec[buf][kVk][lane] = r[1];
-        s_vec[buf][kVa][lane] = __expf(r[3]);
-        s_vec[buf][kVe][lane] = r[2] * r[1];
-    };
-    if (lane < LP) {
-        load_row(0);
-        put_row(0);
-    }
-    const int64_t col0 = bh * a.T * a.D + d;
-    float vv = dok ? a.v[col0] : 0.0f, ww = dok ? a.w[col0] : 0.0f;
-    __syncthreads();
+
     int64_t until_bnd = 0, n_bnd = 0;   // steps to the next saved boundary, boundaries saved
-    for (int64_t t = 0; t < a.T; ++t) {
+    // Step t: `cur` holds its inputs (its row already staged), `nxt` those of t + 1.
+    auto step = [&](int64_t t, In& cur, In& nxt) {
         const int buf = int(t & 1);
-        const bool more = t + 1 < a.T;
-        const float v_now = vv, w_now = ww;
-        if (more) {                                   // in flight during this step
-            if (lane < LP) load_row(t + 1);
-            if (dok) {
-                vv = a.v[col0 + (t + 1) * a.D];
-                ww = a.w[col0 + (t + 1) * a.D];
-            }
-        }
+        // The update's product is formed before the set is reloaded, so no
+        // old value outlives the load that replaces it (the compiler would
+        // copy it, and wait for the load to do so).
+        float wv = mul_unfused(cur.w, cur.v);
+        asm volatile("" : "+v"(wv));          // the product is formed here (no instruction) ...
+        __builtin_amdgcn_sched_barrier(0);    // ... and the reload is issued after it
+        load_in(t + 2, cur);
         if (until_bnd == 0) {   // t is a multiple of the chunk
             if (a.bnd != nullptr && dok) store_rows<R>(a.bnd + ((bh * a.n_chunks + n_bnd) * a.D + d) * LP + r0, S);
             ++n_bnd;
@@ -242,7 +262,7 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
             S[i] *= sv[kVa][r0 + i];
             read = fmaf(sv[kVe][r0 + i], S[i], read);
         }
-        const float u = w_now * v_now - group_sum<Q>(read);
+        const float u = wv - group_sum<Q>(read);
         float o = 0.0f;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -250,10 +270,24 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
             o = fmaf(sv[kVq][r0 + i], S[i], o);
         }
         o = group_sum<Q>(o);
-        if (dok && j == 0) a.ctx[col0 + t * a.D] = o * a.scale;
-        if (more && lane < LP) put_row(buf ^ 1);
+        if (dok && j == 0) a.ctx[bh * a.T * a.D + d + t * a.D] = o * a.scale;
+        put_row(buf ^ 1, nxt.r);   // past the last step: staged but never read
         __syncthreads();
+    };
+    In x0, x1;
+    load_in(0, x0);
+    load_in(1, x1);
+    put_row(0, x0.r);
+    __syncthreads();
+    // Whole pairs in the loop, an odd last step after it: every iteration
+    // runs both steps, so the sets come back to their registers at the loop's
+    // end without copies.
+    int64_t t = 0;
+    for (; t + 1 < a.T; t += 2) {
+        step(t, x0, x1);
+        step(t + 1, x1, x0);
     }
+    if (t < a.T) step(t, x0, x1);
     if (a.state != nullptr && dok) {
 #pragma unroll
         for (int i = 0; i < R; ++i)
@@ -288,62 +322,49 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
 
     float* scr = a.scratch + (bh * a.scratch_steps * a.D + (dok ? d : 0)) * LP + r0;
     const int64_t scr_step = a.D * LP;
-    const int64_t col0 = bh * a.T * a.D + d;   // element (t = 0, d) of the dense tensors
+    const int64_t col0 = bh * a.T * a.D + d;               // element (t = 0, d) of the dense tensors
+    const int64_t lcol0 = bh * a.T * a.D + (dok ? d : a.D - 1);   // the column this lane loads
 
-    // Step vectors staged in LDS, two buffers used in turn: threads < LP load
-    // row tid of the next step while the current one computes and publish it
-    // with the step's barrier.  They keep the raw row too (threads < L finish
-    // the latent-vector outputs with k, b and g of their row).
-    __shared__ float s_rows[2][kNVec][LP];
-    const bool loader = tid < LP;
-    auto load_row = [&](int64_t t, float (&r)[4]) {
-        if (loader) {
-            if (tid < a.L) {
-                const int64_t i = (bh * a.T + t) * a.L + tid;
-                r[0] = a.q[i];
-                r[1] = a.k[i];
-                r[2] = a.b[i];
-                r[3] = a.g[i];
-            } else {
-                r[0] = r[1] = r[2] = r[3] = 0.0f;
-            }
-        }
+    // Step vectors staged in LDS, two buffers used in turn; threads < LP stage
+    // row tid, which threads < L read back raw (key, erase, decay) to finish
+    // the latent-vector outputs.  Every thread loads a row (clamped as in the
+    // forward) so that the loads stay unconditional.
+    __shared__ float s_rows[2][kNRow][LP];
+    const bool live = tid < a.L;
+    const int64_t row0 = bh * a.T * a.L + ((tid & (LP - 1)) < a.L ? (tid & (LP - 1)) : a.L - 1);
+    auto load_row = [&](int64_t t, Row& r) {
+        const int64_t i = row0 + t * a.L;
+        r.q = a.q[i];
+        r.k = a.k[i];
+        r.b = a.b[i];
+        r.g = a.g[i];
     };
-    auto put_row = [&](int buf, const float (&r)[4]) {
-        if (loader) {
-            s_rows[buf][kVq][tid] = r[0];
-            s_rows[buf][kVk][tid] = r[1];
-            s_rows[buf][kVa][tid] = __expf(r[3]);
-            s_rows[buf][kVe][tid] = r[2] * r[1];
+    auto put_row = [&](int buf, const Row& r) {
+        if (tid < LP) {
+            s_rows[buf][kVq][tid] = live ? r.q : 0.0f;
+            s_rows[buf][kVk][tid] = live ? r.k : 0.0f;
+            s_rows[buf][kVa][tid] = live ? __expf(r.g) : 1.0f;
+            s_rows[buf][kVe][tid] = live ? r.b * r.k : 0.0f;
+            s_rows[buf][kVb][tid] = live ? r.b : 0.0f;
         }
     };
     // A step's dense inputs in two register sets used in turn (the step loops
-    // are unrolled by two so the roles swap without copies).
+    // are unrolled by two so the roles swap without copies).  Columns past D
+    // load column D - 1; their context cotangent is taken as zero.
     struct Dense {
         float v, w, dc;
     };
     Dense denA{0.0f, 0.0f, 0.0f}, denB{0.0f, 0.0f, 0.0f};
     float SpA[R], SpB[R];
     auto load_dense = [&](int64_t t, bool with_dc, Dense& dn) {
-        if (dok) {
-            dn.v = a.v[col0 + t * a.D];
-            dn.w = a.w[col0 + t * a.D];
-            if (with_dc) dn.dc = a.dctx[col0 + t * a.D];
-        }
+        dn.v = a.v[lcol0 + t * a.D];
+        dn.w = a.w[lcol0 + t * a.D];
+        if (with_dc) dn.dc = a.dctx[lcol0 + t * a.D];
     };
-    // Rows are loaded two steps ahead of their LDS store, so a whole step of
-    // work covers each load: rl holds the row staged at the end of this step,
-    // rn the one loading now.
-    float rl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float rn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float rc[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // raw row of the step being reversed
-    auto shift_rows = [&]() {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            rc[q] = rl[q];
-            rl[q] = rn[q];
-        }
-    };
+    // Rows load two steps ahead of their use, into two sets used in turn: the
+    // step that stages row t' +- 1 at its end loads row t' +- 2 into the set
+    // that held its own row.
+    Row rX{0.0f, 0.0f, 0.0f, 0.0f}, rY{0.0f, 0.0f, 0.0f, 0.0f};
 
     int it = 0;   // steps so far (both sweeps): alternates the LDS buffers
     for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
@@ -358,12 +379,13 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
 #pragma unroll
             for (int i = 0; i < R; ++i) S[i] = 0.0f;
         }
-        auto rec_step = [&](int64_t t, Dense& dcur, Dense& dnxt) {
+        // Step t (upwards): rl is the set to load row t + 2 into (it held row
+        // t), rs holds row t + 1, staged at the end of the step.
+        auto rec_step = [&](int64_t t, Dense& dcur, Dense& dnxt, Row& rl, const Row& rs) {
             const int buf = it & 1;
             ++it;
-            const bool more = t + 1 < t1;
-            if (t + 2 < t1) load_row(t + 2, rn);
-            if (more) load_dense(t + 1, false, dnxt);
+            load_row(t + 2 < t1 ? t + 2 : t1 - 1, rl);
+            load_dense(t + 1 < t1 ? t + 1 : t1 - 1, false, dnxt);
             if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
             const float(*sv)[LP] = s_rows[buf];
             float read = 0.0f;
@@ -372,40 +394,47 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 S[i] *= sv[kVa][r0 + i];
                 read = fmaf(sv[kVe][r0 + i], S[i], read);
             }
-            const float u = dcur.w * dcur.v - group_sum<Q>(read);
+            const float u = mul_unfused(dcur.w, dcur.v) - group_sum<Q>(read);
 #pragma unroll
             for (int i = 0; i < R; ++i) S[i] = fmaf(sv[kVk][r0 + i], u, S[i]);
-            if (more) put_row(buf ^ 1, rl);
+            put_row(buf ^ 1, rs);   // after the chunk's last step: staged but never read
             __syncthreads();
-            shift_rows();
         };
-        load_row(t0, rl);
-        put_row(it & 1, rl);
-        if (t0 + 1 < t1) load_row(t0 + 1, rl);
+        load_row(t0, rX);
+        put_row(it & 1, rX);
+        load_row(t0 + 1 < t1 ? t0 + 1 : t1 - 1, rY);
         load_dense(t0, false, denA);
         __syncthreads();
         for (int64_t t = t0; t < t1; t += 2) {
-            rec_step(t, denA, denB);
-            if (t + 1 < t1) rec_step(t + 1, denB, denA);
+            rec_step(t, denA, denB, rX, rY);
+            if (t + 1 < t1) rec_step(t + 1, denB, denA, rY, rX);
         }
 
-        // Reverse the chunk, loading one step ahead (downwards) likewise.
-        auto rev_step = [&](int64_t t, Dense& dcur, float (&Sp)[R], Dense& dnxt, float (&Sn)[R]) {
+        // Reverse the chunk (downwards): the dense inputs and the state
+        // before the step load one step ahead, rows two ahead as above (rl
+        // takes row t - 2, rs holds row t - 1).  Lanes past D load from
+        // column 0's scratch slot, which another block may not have written
+        // yet: they zero what they loaded, and with a zero context cotangent
+        // their state cotangent stays zero, so they add nothing to the sums.
+        auto rev_step = [&](int64_t t, Dense& dcur, float (&Sp)[R], Dense& dnxt, float (&Sn)[R], Row& rl,
+                            const Row& rs) {
             const int buf = it & 1;
             ++it;
-            const bool more = t > t0;
+            const int64_t tp = t > t0 ? t - 1 : t0;
             const int64_t e = col0 + t * a.D;
-            if (t - 2 >= t0) load_row(t - 2, rn);
-            if (more) {
-                load_dense(t - 1, true, dnxt);
-                if (dok) load_rows_of<R>(scr + (t - 1 - t0) * scr_step, Sn);
-            }
+            load_row(t - 2 >= t0 ? t - 2 : t0, rl);
+            load_dense(tp, true, dnxt);
+            load_rows_of<R>(scr + (tp - t0) * scr_step, Sn);
             const float(*sv)[LP] = s_rows[buf];
-            const float dov = dcur.dc * a.scale;
+            const float dov = dok ? dcur.dc * a.scale : 0.0f;
+            if (!dok) {
+#pragma unroll
+                for (int i = 0; i < R; ++i) Sp[i] = 0.0f;
+            }
             float read = 0.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i) read = fmaf(sv[kVe][r0 + i], sv[kVa][r0 + i] * Sp[i], read);
-            const float u = dcur.w * dcur.v - group_sum<Q>(read);
+            const float u = mul_unfused(dcur.w, dcur.v) - group_sum<Q>(read);
 
             // Read-out: the state after the step, and G += q do^T / sqrt(L);
             // then the rank-1 write: d u = G^T k and G u (the key's outer part).
@@ -444,7 +473,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 s_red[buf][wave][2][r0 + idx] = r_e;
                 s_red[buf][wave][3][r0 + idx] = r_a;
             }
-            if (more) put_row(buf ^ 1, rl);
+            put_row(buf ^ 1, rs);   // after the chunk's first step: staged but never read
             __syncthreads();
             if (out_lane) {
                 float sq = 0.0f, sk = 0.0f, se = 0.0f, sa = 0.0f;
@@ -457,9 +486,9 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 if (a.n_blk == 1) {
                     const int64_t i = (bh * a.T + t) * a.L + tid;
                     if (a.dq != nullptr) a.dq[i] = sq;
-                    if (a.dk != nullptr) a.dk[i] = fmaf(se, rc[2], sk);
-                    if (a.db != nullptr) a.db[i] = se * rc[1];
-                    if (a.dg != nullptr) a.dg[i] = sa * __expf(rc[3]);
+                    if (a.dk != nullptr) a.dk[i] = fmaf(se, s_rows[buf][kVb][tid], sk);
+                    if (a.db != nullptr) a.db[i] = se * s_rows[buf][kVk][tid];
+                    if (a.dg != nullptr) a.dg[i] = sa * s_rows[buf][kVa][tid];
                 } else if (a.part != nullptr) {
                     // This block's share; gdn2_sum_kernel adds the blocks of the head.
                     float* p = a.part + (((bh * a.T + t) * a.n_blk + blk) * 4) * a.L + tid;
@@ -469,24 +498,16 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                     p[3 * a.L] = sa;
                 }
             }
-            shift_rows();
         };
-        load_row(t1 - 1, rl);
-        put_row(it & 1, rl);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) rc[q] = rl[q];
-        if (t1 - 2 >= t0) load_row(t1 - 2, rl);
+        load_row(t1 - 1, rX);
+        put_row(it & 1, rX);
+        load_row(t1 - 2 >= t0 ? t1 - 2 : t0, rY);
         load_dense(t1 - 1, true, denA);
-        if (dok) {
-            load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
-        } else {
-#pragma unroll
-            for (int i = 0; i < R; ++i) SpA[i] = SpB[i] = 0.0f;
-        }
+        load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
         __syncthreads();
         for (int64_t t = t1 - 1; t >= t0; t -= 2) {
-            rev_step(t, denA, SpA, denB, SpB);
-            if (t - 1 >= t0) rev_step(t - 1, denB, SpB, denA, SpA);
+            rev_step(t, denA, SpA, denB, SpB, rX, rY);
+            if (t - 1 >= t0) rev_step(t - 1, denB, SpB, denA, SpA, rY, rX);
         }
     }
     if (a.ds0 != nullptr && dok) {

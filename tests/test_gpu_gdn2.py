@@ -197,3 +197,29 @@ def test_latent_tensors_only_4_byte_aligned():
     assert torch.equal(c1, c2) and torch.equal(s1, s2)
     for x, y in zip(g1, g2):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("geom", [(1, 2, 60, 32, 100, 8), (1, 1, 37, 64, 65, 5), (2, 1, 21, 16, 70, 4)],
+                         ids=lambda g: "b%dh%dt%dl%dd%dc%d" % g)
+def test_backward_ignores_scratch_contents(geom):
+    """Dense sizes that leave a head's last block partly empty (so lanes past
+    D exist) with several blocks per head: the backward's results do not
+    depend on what its scratch held before the call (NaN-filled against
+    zero-filled, bit for bit), and match the oracle."""
+    B, H, T, L, D, chunk = geom
+    print(f"[gdn2 scratch {geom}]", flush=True)
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=7 + sum(geom))
+    dev = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
+    d_ctx = torch.randn((B, H, T, D), device=DEV, generator=torch.Generator(device=DEV).manual_seed(5))
+    ctx, _, bnd = capi.gdn2_fwd(*dev, chunk=chunk)
+    nscr = int(capi.load().gdn2_scratch_bytes(B, H, T, L, D, chunk))
+    runs = []
+    for fill in (float("nan"), 0.0):
+        scratch = torch.full((nscr // 4,), fill, dtype=torch.float32, device=DEV)
+        runs.append(capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=chunk, scratch=scratch))
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, *runs):
+        assert torch.equal(x, y), f"d_{n} depends on the scratch's previous contents"
+    r_grads = oracle.gdn2_bwd(*[arrays[n] for n in NAMES], d_ctx.cpu().numpy())
+    for n, g, r in zip(NAMES, runs[0], r_grads):
+        close("d_" + n, g, r)
