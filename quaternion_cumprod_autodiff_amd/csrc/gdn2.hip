@@ -38,6 +38,7 @@ namespace {
 constexpr int kMaxLatent = 64;
 constexpr int kMaxDense = 1024;
 constexpr int kBlockWaves = 4;   // backward blocks: 4 waves, one per SIMD
+constexpr int kRegChunk = 8;     // chunk size whose pre-step states the backward keeps in registers
 
 // Lanes per dense column: 8 when that still leaves each lane 4 or more of
 // the LP padded rows (LP >= 32), else 4; each lane holds LP / Q contiguous rows.
@@ -297,8 +298,12 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
 
 // ----------------------------------------------------------------- backward
 
-template <int LP>
+// KC > 0: chunks of exactly KC steps keep their pre-step states in registers
+// (the recompute stores nothing, the reverse loads nothing); a shorter last
+// chunk, and every chunk when KC = 0, goes through the per-head scratch.
+template <int LP, int KC>
 __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
+    static_assert(KC == 0 || (KC >= 2 && KC % 2 == 0), "register chunks are whole step pairs");
     constexpr int Q = lanes_per_col(LP), R = LP / Q, CPW = cols_per_wave(LP), CPB = cols_per_block(LP);
     constexpr int kLogR = ilog2(R), kLogQ = ilog2(Q);
     __shared__ float s_red[2][kBlockWaves][4][LP];   // per wave: query, key (outer part), erased key, decay
@@ -381,12 +386,20 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         }
         // Step t (upwards): rl is the set to load row t + 2 into (it held row
         // t), rs holds row t + 1, staged at the end of the step.
-        auto rec_step = [&](int64_t t, Dense& dcur, Dense& dnxt, Row& rl, const Row& rs) {
+        // The state before the step goes to the scratch (to_scratch) or to
+        // the registers `keep`.
+        auto rec_step = [&](int64_t t, Dense& dcur, Dense& dnxt, Row& rl, const Row& rs, float (&keep)[R],
+                            bool to_scratch) {
             const int buf = it & 1;
             ++it;
             load_row(t + 2 < t1 ? t + 2 : t1 - 1, rl);
             load_dense(t + 1 < t1 ? t + 1 : t1 - 1, false, dnxt);
-            if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
+            if (to_scratch) {
+                if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
+            } else {
+#pragma unroll
+                for (int i = 0; i < R; ++i) keep[i] = S[i];
+            }
             const float(*sv)[LP] = s_rows[buf];
             float read = 0.0f;
 #pragma unroll
@@ -400,31 +413,23 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             put_row(buf ^ 1, rs);   // after the chunk's last step: staged but never read
             __syncthreads();
         };
-        load_row(t0, rX);
-        put_row(it & 1, rX);
-        load_row(t0 + 1 < t1 ? t0 + 1 : t1 - 1, rY);
-        load_dense(t0, false, denA);
-        __syncthreads();
-        for (int64_t t = t0; t < t1; t += 2) {
-            rec_step(t, denA, denB, rX, rY);
-            if (t + 1 < t1) rec_step(t + 1, denB, denA, rY, rX);
-        }
-
         // Reverse the chunk (downwards): the dense inputs and the state
         // before the step load one step ahead, rows two ahead as above (rl
         // takes row t - 2, rs holds row t - 1).  Lanes past D load from
         // column 0's scratch slot, which another block may not have written
         // yet: they zero what they loaded, and with a zero context cotangent
         // their state cotangent stays zero, so they add nothing to the sums.
+        // Sp is the state before step t; with from_scratch, Sn receives the
+        // one before step t - 1 from the scratch.
         auto rev_step = [&](int64_t t, Dense& dcur, float (&Sp)[R], Dense& dnxt, float (&Sn)[R], Row& rl,
-                            const Row& rs) {
+                            const Row& rs, bool from_scratch) {
             const int buf = it & 1;
             ++it;
             const int64_t tp = t > t0 ? t - 1 : t0;
             const int64_t e = col0 + t * a.D;
             load_row(t - 2 >= t0 ? t - 2 : t0, rl);
             load_dense(tp, true, dnxt);
-            load_rows_of<R>(scr + (tp - t0) * scr_step, Sn);
+            if (from_scratch) load_rows_of<R>(scr + (tp - t0) * scr_step, Sn);
             const float(*sv)[LP] = s_rows[buf];
             const float dov = dok ? dcur.dc * a.scale : 0.0f;
             if (!dok) {
@@ -499,15 +504,45 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 }
             }
         };
-        load_row(t1 - 1, rX);
-        put_row(it & 1, rX);
-        load_row(t1 - 2 >= t0 ? t1 - 2 : t0, rY);
-        load_dense(t1 - 1, true, denA);
+        // Each sweep starts with its first row staged and the next loading.
+        auto start_sweep = [&](int64_t t_first, int64_t t_second, bool with_dc) {
+            load_row(t_first, rX);
+            put_row(it & 1, rX);
+            load_row(t_second, rY);
+            load_dense(t_first, with_dc, denA);
+        };
+        if constexpr (KC > 0) {
+            if (t1 - t0 == KC) {   // whole chunk: states in registers
+                float Sst[KC][R];
+                start_sweep(t0, t0 + 1, false);
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < KC; k += 2) {
+                    rec_step(t0 + k, denA, denB, rX, rY, Sst[k], false);
+                    rec_step(t0 + k + 1, denB, denA, rY, rX, Sst[k + 1], false);
+                }
+                start_sweep(t1 - 1, t1 - 2, true);
+                __syncthreads();
+#pragma unroll
+                for (int k = KC - 1; k > 0; k -= 2) {
+                    rev_step(t0 + k, denA, Sst[k], denB, SpB, rX, rY, false);
+                    rev_step(t0 + k - 1, denB, Sst[k - 1], denA, SpB, rY, rX, false);
+                }
+                continue;
+            }
+        }
+        start_sweep(t0, t0 + 1 < t1 ? t0 + 1 : t1 - 1, false);
+        __syncthreads();
+        for (int64_t t = t0; t < t1; t += 2) {
+            rec_step(t, denA, denB, rX, rY, SpA, true);
+            if (t + 1 < t1) rec_step(t + 1, denB, denA, rY, rX, SpA, true);
+        }
+        start_sweep(t1 - 1, t1 - 2 >= t0 ? t1 - 2 : t0, true);
         load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
         __syncthreads();
         for (int64_t t = t1 - 1; t >= t0; t -= 2) {
-            rev_step(t, denA, SpA, denB, SpB, rX, rY);
-            if (t - 1 >= t0) rev_step(t - 1, denB, SpB, denA, SpA, rY, rX);
+            rev_step(t, denA, SpA, denB, SpB, rX, rY, true);
+            if (t - 1 >= t0) rev_step(t - 1, denB, SpB, denA, SpA, rY, rX, true);
         }
     }
     if (a.ds0 != nullptr && dok) {
@@ -700,9 +735,11 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
                                          : unsigned((D + z.cpw - 1) / z.cpw * 64);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
+        constexpr int kLP = decltype(lm)::value;
         void* params[] = {&a};
-        return hipLaunchKernel(reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<decltype(lm)::value>),
-                               dim3(unsigned(z.BH * z.n_blk)), dim3(threads), params, 0, st);
+        const void* kern = chunk == qc::kRegChunk ? reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<kLP, qc::kRegChunk>)
+                                                  : reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<kLP, 0>);
+        return hipLaunchKernel(kern, dim3(unsigned(z.BH * z.n_blk)), dim3(threads), params, 0, st);
     });
     if (e == hipSuccess && a.part != nullptr) {
         int64_t rows = z.BH * T;

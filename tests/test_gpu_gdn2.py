@@ -59,7 +59,8 @@ def test_page_geometries_and_data(geom):
 @pytest.mark.parametrize("geom", [(2, 3, 50, 7, 100, 8), (1, 1, 200, 64, 128, 32), (3, 2, 33, 33, 65, 1),
                                   (1, 2, 40, 1, 1, 7), (2, 1, 17, 16, 100, 100), (1, 3, 128, 64, 64, 16),
                                   (1, 2, 50, 32, 300, 16), (1, 1, 1, 4, 4, 1), (1, 1, 3, 64, 1024, 2),
-                                  (2, 1, 9, 64, 65, 4), (1, 1, 20, 64, 1, 3)],
+                                  (2, 1, 9, 64, 65, 4), (1, 1, 20, 64, 1, 3), (1, 2, 45, 64, 96, 8),
+                                  (1, 1, 24, 16, 70, 8), (1, 1, 19, 32, 40, 8)],
                          ids=lambda g: "b%dh%dt%dl%dd%dc%d" % g)
 def test_random_shapes_with_final_state_cotangent(geom):
     B, H, T, L, D, chunk = geom
@@ -72,16 +73,21 @@ def test_random_shapes_with_final_state_cotangent(geom):
     print("  relative max errors:", {k: f"{v:.1e}" for k, v in rel.items()}, flush=True)
 
 
-def test_chunk_size_does_not_change_results_beyond_rounding():
+@pytest.mark.parametrize("shape,chunks", [((1, 2, 90, 16, 48), (1, 7, 8, 30, 90, 500)),
+                                          ((1, 1, 42, 64, 96), (8, 13, 42))],
+                         ids=["l16", "l64"])
+def test_chunk_size_does_not_change_results_beyond_rounding(shape, chunks):
     """The chunk only sets where boundary states are saved: the forward is the
     same arithmetic for every chunk (bitwise), and the backward recomputes
     the same states (bitwise too, since each chunk restarts from a state the
-    forward stored exactly)."""
-    arrays = make_gdn2_random_inputs(1, 2, 90, 16, 48, seed=4)
+    forward stored exactly).  Chunk 8 keeps whole chunks' states in registers
+    and its ragged last chunk in the scratch; the others use the scratch."""
+    B, H, T, L, D = shape
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=4)
     dev = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
-    d_ctx = torch.randn((1, 2, 90, 48), device=DEV, generator=torch.Generator(device=DEV).manual_seed(2))
+    d_ctx = torch.randn((B, H, T, D), device=DEV, generator=torch.Generator(device=DEV).manual_seed(2))
     outs = []
-    for chunk in (1, 7, 30, 90, 500):
+    for chunk in chunks:
         ctx, state, bnd = capi.gdn2_fwd(*dev, chunk=chunk)
         grads = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=chunk)
         outs.append((ctx, state) + grads)
@@ -145,7 +151,7 @@ def test_autograd_node_against_oracle():
 
 def test_bench_workload_sampled_heads():
     """The bench's launch configuration (8 x 16 heads, 2048 steps, latent 64,
-    dense 128, chunk 32), checked on sampled heads: heads are independent, so
+    dense 128, chunk 8: the register path), checked on sampled heads: heads are independent, so
     the oracle on a head's inputs alone gives that head's exact outputs."""
     import bench
     B, H, T, L, D, chunk = bench.GDN2_WORKLOAD
