@@ -306,7 +306,11 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
     static_assert(KC == 0 || (KC >= 2 && KC % 2 == 0), "register chunks are whole step pairs");
     constexpr int Q = lanes_per_col(LP), R = LP / Q, CPW = cols_per_wave(LP), CPB = cols_per_block(LP);
     constexpr int kLogR = ilog2(R), kLogQ = ilog2(Q);
-    __shared__ float s_red[2][kBlockWaves][4][LP];   // per wave: query, key (outer part), erased key, decay
+    // Per step slot and wave: the column sums of query, key (outer part),
+    // erased key and decay.  Two slots used in turn, each summed over the
+    // waves right after its step; with register chunks, one slot per step of
+    // the chunk, summed at the chunk's end.
+    __shared__ float s_red[KC > 0 ? KC : 2][kBlockWaves][4][LP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane & (Q - 1);
     const int n_waves = int(blockDim.x >> 6);
     const int r0 = j * R;
@@ -371,6 +375,35 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
     // that held its own row.
     Row rX{0.0f, 0.0f, 0.0f, 0.0f}, rY{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // The latent-vector outputs of step t for row l from the block's sums
+    // (key, erase and decay of that row given): final values with one block
+    // per head, else this block's share, which gdn2_sum_kernel adds up.
+    auto emit = [&](int64_t t, int l, float sq, float sk, float se, float sa, float kv, float bv, float av) {
+        if (a.n_blk == 1) {
+            const int64_t i = (bh * a.T + t) * a.L + l;
+            if (a.dq != nullptr) a.dq[i] = sq;
+            if (a.dk != nullptr) a.dk[i] = fmaf(se, bv, sk);
+            if (a.db != nullptr) a.db[i] = se * kv;
+            if (a.dg != nullptr) a.dg[i] = sa * av;
+        } else if (a.part != nullptr) {
+            float* p = a.part + (((bh * a.T + t) * a.n_blk + blk) * 4) * a.L + l;
+            p[0] = sq;
+            p[a.L] = sk;
+            p[2 * a.L] = se;
+            p[3 * a.L] = sa;
+        }
+    };
+    // Sum of the waves' shares in slot `slot`, row l, in wave order.
+    auto wave_sums = [&](int slot, int l, float& sq, float& sk, float& se, float& sa) {
+        sq = sk = se = sa = 0.0f;
+        for (int wv = 0; wv < n_waves; ++wv) {
+            sq += s_red[slot][wv][0][l];
+            sk += s_red[slot][wv][1][l];
+            se += s_red[slot][wv][2][l];
+            sa += s_red[slot][wv][3][l];
+        }
+    };
+
     int it = 0;   // steps so far (both sweeps): alternates the LDS buffers
     for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
         const int64_t t0 = c * a.chunk;
@@ -421,8 +454,10 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         // their state cotangent stays zero, so they add nothing to the sums.
         // Sp is the state before step t; with from_scratch, Sn receives the
         // one before step t - 1 from the scratch.
+        // The step's column sums go to s_red slot `slot`; with sum_now the
+        // block adds them up after the step's barrier.
         auto rev_step = [&](int64_t t, Dense& dcur, float (&Sp)[R], Dense& dnxt, float (&Sn)[R], Row& rl,
-                            const Row& rs, bool from_scratch) {
+                            const Row& rs, bool from_scratch, int slot, bool sum_now) {
             const int buf = it & 1;
             ++it;
             const int64_t tp = t > t0 ? t - 1 : t0;
@@ -473,35 +508,17 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             const float r_e = cols_row_sum<R, 32, Q>(x1, lane);
             const float r_a = cols_row_sum<R, 32, Q>(x2, lane);
             if (row_writer) {
-                s_red[buf][wave][0][r0 + idx] = r_q;
-                s_red[buf][wave][1][r0 + idx] = r_k;
-                s_red[buf][wave][2][r0 + idx] = r_e;
-                s_red[buf][wave][3][r0 + idx] = r_a;
+                s_red[slot][wave][0][r0 + idx] = r_q;
+                s_red[slot][wave][1][r0 + idx] = r_k;
+                s_red[slot][wave][2][r0 + idx] = r_e;
+                s_red[slot][wave][3][r0 + idx] = r_a;
             }
             put_row(buf ^ 1, rs);   // after the chunk's first step: staged but never read
             __syncthreads();
-            if (out_lane) {
-                float sq = 0.0f, sk = 0.0f, se = 0.0f, sa = 0.0f;
-                for (int wv = 0; wv < n_waves; ++wv) {
-                    sq += s_red[buf][wv][0][tid];
-                    sk += s_red[buf][wv][1][tid];
-                    se += s_red[buf][wv][2][tid];
-                    sa += s_red[buf][wv][3][tid];
-                }
-                if (a.n_blk == 1) {
-                    const int64_t i = (bh * a.T + t) * a.L + tid;
-                    if (a.dq != nullptr) a.dq[i] = sq;
-                    if (a.dk != nullptr) a.dk[i] = fmaf(se, s_rows[buf][kVb][tid], sk);
-                    if (a.db != nullptr) a.db[i] = se * s_rows[buf][kVk][tid];
-                    if (a.dg != nullptr) a.dg[i] = sa * s_rows[buf][kVa][tid];
-                } else if (a.part != nullptr) {
-                    // This block's share; gdn2_sum_kernel adds the blocks of the head.
-                    float* p = a.part + (((bh * a.T + t) * a.n_blk + blk) * 4) * a.L + tid;
-                    p[0] = sq;
-                    p[a.L] = sk;
-                    p[2 * a.L] = se;
-                    p[3 * a.L] = sa;
-                }
+            if (sum_now && out_lane) {
+                float sq, sk, se, sa;
+                wave_sums(slot, tid, sq, sk, se, sa);
+                emit(t, tid, sq, sk, se, sa, s_rows[buf][kVk][tid], s_rows[buf][kVb][tid], s_rows[buf][kVa][tid]);
             }
         };
         // Each sweep starts with its first row staged and the next loading.
@@ -525,8 +542,23 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 __syncthreads();
 #pragma unroll
                 for (int k = KC - 1; k > 0; k -= 2) {
-                    rev_step(t0 + k, denA, Sst[k], denB, SpB, rX, rY, false);
-                    rev_step(t0 + k - 1, denB, Sst[k - 1], denA, SpB, rY, rX, false);
+                    rev_step(t0 + k, denA, Sst[k], denB, SpB, rX, rY, false, k, false);
+                    rev_step(t0 + k - 1, denB, Sst[k - 1], denA, SpB, rY, rX, false, k - 1, false);
+                }
+                // The chunk's sums, its steps dealt over the waves (the last
+                // step's barrier published every slot; the next chunk's
+                // recompute barriers come before any slot is written again).
+                if (lane < a.L) {
+                    for (int k = wave; k < KC; k += n_waves) {
+                        const int64_t t = t0 + k;
+                        const int64_t i = (bh * a.T + t) * a.L + lane;
+                        float sq, sk, se, sa;
+                        wave_sums(k, lane, sq, sk, se, sa);
+                        if (a.n_blk == 1)
+                            emit(t, lane, sq, sk, se, sa, a.k[i], a.b[i], __expf(a.g[i]));
+                        else
+                            emit(t, lane, sq, sk, se, sa, 0.0f, 0.0f, 0.0f);
+                    }
                 }
                 continue;
             }
@@ -541,8 +573,8 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
         __syncthreads();
         for (int64_t t = t1 - 1; t >= t0; t -= 2) {
-            rev_step(t, denA, SpA, denB, SpB, rX, rY, true);
-            if (t - 1 >= t0) rev_step(t - 1, denB, SpB, denA, SpA, rY, rX, true);
+            rev_step(t, denA, SpA, denB, SpB, rX, rY, true, it & 1, true);
+            if (t - 1 >= t0) rev_step(t - 1, denB, SpB, denA, SpA, rY, rX, true, it & 1, true);
         }
     }
     if (a.ds0 != nullptr && dok) {
