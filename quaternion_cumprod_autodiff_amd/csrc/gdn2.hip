@@ -405,28 +405,35 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
     };
 
     int it = 0;   // steps so far (both sweeps): alternates the LDS buffers
-    for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
-        const int64_t t0 = c * a.chunk;
-        const int64_t t1 = t0 + a.chunk < a.T ? t0 + a.chunk : a.T;
-
-        // Recompute the chunk from its boundary; keep the state before each step.
-        float S[R];
+    // The chunk's boundary state, and whether the previous (register) chunk
+    // already loaded it with the chunk's first rows and dense inputs.
+    float S[R];
+    auto load_boundary = [&](int64_t c) {
         if (dok) {
             load_rows_of<R>(a.bnd_in + ((bh * a.n_chunks + c) * a.D + d) * LP + r0, S);
         } else {
 #pragma unroll
             for (int i = 0; i < R; ++i) S[i] = 0.0f;
         }
-        // Step t (upwards): rl is the set to load row t + 2 into (it held row
-        // t), rs holds row t + 1, staged at the end of the step.
+    };
+    bool primed = false;
+    for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
+        const int64_t t0 = c * a.chunk;
+        const int64_t t1 = t0 + a.chunk < a.T ? t0 + a.chunk : a.T;
+
+        // Recompute the chunk from its boundary; keep the state before each step.
+        if (!primed) load_boundary(c);
+        // Step t (upwards): rl is the set to load row row_t into (it held row
+        // t; row_t is t + 2 inside the chunk), rs holds row t + 1, staged at
+        // the end of the step; dnxt receives the dense inputs of dense_t.
         // The state before the step goes to the scratch (to_scratch) or to
         // the registers `keep`.
         auto rec_step = [&](int64_t t, Dense& dcur, Dense& dnxt, Row& rl, const Row& rs, float (&keep)[R],
-                            bool to_scratch) {
+                            bool to_scratch, int64_t row_t, int64_t dense_t, bool dense_dc) {
             const int buf = it & 1;
             ++it;
-            load_row(t + 2 < t1 ? t + 2 : t1 - 1, rl);
-            load_dense(t + 1 < t1 ? t + 1 : t1 - 1, false, dnxt);
+            load_row(row_t, rl);
+            load_dense(dense_t, dense_dc, dnxt);
             if (to_scratch) {
                 if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
             } else {
@@ -456,14 +463,17 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         // one before step t - 1 from the scratch.
         // The step's column sums go to s_red slot `slot`; with sum_now the
         // block adds them up after the step's barrier.
+        // row_t and dense_t (t - 2 and t - 1 inside the chunk) are the row
+        // and dense inputs this step loads.
         auto rev_step = [&](int64_t t, Dense& dcur, float (&Sp)[R], Dense& dnxt, float (&Sn)[R], Row& rl,
-                            const Row& rs, bool from_scratch, int slot, bool sum_now) {
+                            const Row& rs, bool from_scratch, int slot, bool sum_now, int64_t row_t,
+                            int64_t dense_t) {
             const int buf = it & 1;
             ++it;
             const int64_t tp = t > t0 ? t - 1 : t0;
             const int64_t e = col0 + t * a.D;
-            load_row(t - 2 >= t0 ? t - 2 : t0, rl);
-            load_dense(tp, true, dnxt);
+            load_row(row_t, rl);
+            load_dense(dense_t, true, dnxt);
             if (from_scratch) load_rows_of<R>(scr + (tp - t0) * scr_step, Sn);
             const float(*sv)[LP] = s_rows[buf];
             const float dov = dok ? dcur.dc * a.scale : 0.0f;
@@ -530,20 +540,44 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         };
         if constexpr (KC > 0) {
             if (t1 - t0 == KC) {   // whole chunk: states in registers
+                // Loads run ahead across the sweeps: the recompute's last two
+                // steps load what the reverse starts with (rows t1 - 1, t1 - 2,
+                // the dense inputs of t1 - 1 with the context cotangent), and
+                // the reverse's last two load the next chunk's start (its
+                // boundary state, rows and dense inputs), so no sweep starts
+                // by waiting for memory.
                 float Sst[KC][R];
-                start_sweep(t0, t0 + 1, false);
+                if (primed)
+                    put_row(it & 1, rX);
+                else
+                    start_sweep(t0, t0 + 1, false);
                 __syncthreads();
 #pragma unroll
                 for (int k = 0; k < KC; k += 2) {
-                    rec_step(t0 + k, denA, denB, rX, rY, Sst[k], false);
-                    rec_step(t0 + k + 1, denB, denA, rY, rX, Sst[k + 1], false);
+                    const int64_t t = t0 + k;
+                    if (k + 2 < KC) {
+                        rec_step(t, denA, denB, rX, rY, Sst[k], false, t + 2, t + 1, false);
+                        rec_step(t + 1, denB, denA, rY, rX, Sst[k + 1], false, t + 3, t + 2, false);
+                    } else {
+                        rec_step(t, denA, denB, rX, rY, Sst[k], false, t1 - 1, t1 - 1, false);
+                        rec_step(t + 1, denB, denA, rY, rX, Sst[k + 1], false, t1 - 2, t1 - 1, true);
+                    }
                 }
-                start_sweep(t1 - 1, t1 - 2, true);
+                if (c > 0) load_boundary(c - 1);   // S is not read again in this chunk
+                put_row(it & 1, rX);
                 __syncthreads();
+                const int64_t n0 = c > 0 ? t0 - KC : t0;   // next chunk's first step (or a repeat)
 #pragma unroll
                 for (int k = KC - 1; k > 0; k -= 2) {
-                    rev_step(t0 + k, denA, Sst[k], denB, SpB, rX, rY, false, k, false);
-                    rev_step(t0 + k - 1, denB, Sst[k - 1], denA, SpB, rY, rX, false, k - 1, false);
+                    const int64_t t = t0 + k;
+                    if (k > 1) {
+                        rev_step(t, denA, Sst[k], denB, SpB, rX, rY, false, k, false, t - 2, t - 1);
+                        rev_step(t - 1, denB, Sst[k - 1], denA, SpB, rY, rX, false, k - 1, false, t - 3, t - 2);
+                    } else {
+                        rev_step(t, denA, Sst[k], denB, SpB, rX, rY, false, k, false, n0, t - 1);
+                        rev_step(t - 1, denB, Sst[k - 1], denA, SpB, rY, rX, false, k - 1, false,
+                                 c > 0 ? n0 + 1 : t0, n0);
+                    }
                 }
                 // The chunk's sums, its steps dealt over the waves (the last
                 // step's barrier published every slot; the next chunk's
@@ -560,22 +594,30 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                             emit(t, lane, sq, sk, se, sa, 0.0f, 0.0f, 0.0f);
                     }
                 }
+                primed = c > 0;
                 continue;
             }
         }
         start_sweep(t0, t0 + 1 < t1 ? t0 + 1 : t1 - 1, false);
         __syncthreads();
         for (int64_t t = t0; t < t1; t += 2) {
-            rec_step(t, denA, denB, rX, rY, SpA, true);
-            if (t + 1 < t1) rec_step(t + 1, denB, denA, rY, rX, SpA, true);
+            rec_step(t, denA, denB, rX, rY, SpA, true, t + 2 < t1 ? t + 2 : t1 - 1, t + 1 < t1 ? t + 1 : t1 - 1,
+                     false);
+            if (t + 1 < t1)
+                rec_step(t + 1, denB, denA, rY, rX, SpA, true, t + 3 < t1 ? t + 3 : t1 - 1,
+                         t + 2 < t1 ? t + 2 : t1 - 1, false);
         }
         start_sweep(t1 - 1, t1 - 2 >= t0 ? t1 - 2 : t0, true);
         load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
         __syncthreads();
         for (int64_t t = t1 - 1; t >= t0; t -= 2) {
-            rev_step(t, denA, SpA, denB, SpB, rX, rY, true, it & 1, true);
-            if (t - 1 >= t0) rev_step(t - 1, denB, SpB, denA, SpA, rY, rX, true, it & 1, true);
+            rev_step(t, denA, SpA, denB, SpB, rX, rY, true, it & 1, true, t - 2 >= t0 ? t - 2 : t0,
+                     t - 1 >= t0 ? t - 1 : t0);
+            if (t - 1 >= t0)
+                rev_step(t - 1, denB, SpB, denA, SpA, rY, rX, true, it & 1, true, t - 3 >= t0 ? t - 3 : t0,
+                         t - 2 >= t0 ? t - 2 : t0);
         }
+        primed = false;
     }
     if (a.ds0 != nullptr && dok) {
 #pragma unroll
