@@ -8,22 +8,25 @@
 // read-out u[d] and the write S[:, d] += k u[d] touch column d only); the
 // forward saves the state every `chunk` steps.
 //
-// Both kernels give each dense column a quad of 4 lanes, lane j of the quad
-// holding rows j*R .. j*R+R-1 (R = LP/4, LP = L rounded up to 16, 32 or 64) in
-// registers.  Sums over a column's rows (the erased read-out, d u) are a
-// partial per lane plus two quad shuffles.  A wave holds 16 columns.  The
-// step's latent vectors are loaded one step ahead by one thread per row and
-// staged in LDS, where every lane reads its own rows.  In the backward a
-// block holds 64 columns (4 waves, one per SIMD) and a head takes ceil(D/64)
-// blocks.  Chunks are taken in reverse; each is
-// recomputed from its saved boundary state, the state before every step
-// going to a per-head scratch slot (each lane writes and reads back only its
-// own rows), then reversed step by step.  The cotangents of value, write and
-// the state are per column; those of query, key, erase and log_decay are
-// sums over the dense axis: the lanes holding the same rows of the wave's 16
-// columns reduce them by a transpose-reduce (each stage halves the rows a
-// lane carries), the waves' sums meet in LDS, and with several blocks per
-// head a small kernel adds the blocks' shares in block order.
+// Both kernels give each dense column Q lanes (8 when L rounds up to 32 or
+// 64, else 4), lane j of the group holding rows j*R .. j*R+R-1 (R = LP/Q, LP
+// = L rounded up to 16, 32 or 64) in registers; a wave holds 64/Q columns.
+// Sums over a column's rows (the erased read-out, the context, d u) are a
+// partial per lane plus a DPP butterfly.  The step's latent vectors are
+// loaded two steps ahead and staged in LDS, where every lane reads its own
+// rows.
+//
+// The backward runs blocks of 4 waves (one per SIMD) over 4 * 64/Q columns,
+// ceil(D / (4 * 64/Q)) blocks per head.  Chunks are taken in reverse; each
+// is recomputed from its saved boundary state, keeping the state before
+// every step (in registers for chunks of 8 steps, else in a per-head scratch
+// where each lane writes and reads back only its own rows), then reversed
+// step by step.  The cotangents of value, write and the state are per
+// column; those of query, key, erase and log_decay are sums over the dense
+// axis: the lanes holding the same rows of the wave's columns reduce them by
+// a transpose-reduce (gfx950 permlane swaps and DPP), the waves' sums meet in
+// LDS, and with several blocks per head a small kernel adds the blocks'
+// shares in block order.
 #include "gdn2.h"
 #include "qc_internal.hpp"
 #include "quat_cumprod.h"
@@ -58,7 +61,7 @@ struct Gdn2Args {
     float* scratch;
     int64_t T, L, D, chunk, n_chunks, scratch_steps;
     float scale;
-    int n_blk;      // backward blocks per head (ceil(D / 64))
+    int n_blk;      // backward blocks per head (ceil(D / columns per block))
     float* part;    // with n_blk > 1: per-block sums of the latent-vector cotangents, [BH, T, n_blk, 4, L]
 };
 
