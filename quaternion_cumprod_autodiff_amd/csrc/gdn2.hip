@@ -200,7 +200,12 @@ struct Row {
     float q, k, b, g;
 };
 
-template <int LP>
+// kFull: D is a multiple of the columns per wave, so every lane has a column
+// and the per-step context store is made by all lanes of the column (the same
+// value to the same address): an unconditional store keeps the compiler's
+// wait counts exact, where a conditional one makes the next step wait for a
+// load issued during this one.
+template <int LP, bool kFull>
 __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
     constexpr int Q = lanes_per_col(LP), R = LP / Q, CPW = cols_per_wave(LP);
     __shared__ float s_vec[2][kNVec][LP];
@@ -209,7 +214,7 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
     const int64_t n_cb = (a.D + CPW - 1) / CPW;
     const int64_t bh = blockIdx.x / n_cb;
     const int64_t d = (blockIdx.x % n_cb) * CPW + (lane >> ilog2(Q));
-    const bool dok = d < a.D;
+    const bool dok = kFull || d < a.D;
     const bool live = lane < a.L;                       // this lane's staged row is a real one
     const int64_t row0 = bh * a.T * a.L + (live ? lane : a.L - 1);
     const int64_t col0 = bh * a.T * a.D + (dok ? d : a.D - 1);
@@ -274,7 +279,10 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
             o = fmaf(sv[kVq][r0 + i], S[i], o);
         }
         o = group_sum<Q>(o);
-        if (dok && j == 0) a.ctx[bh * a.T * a.D + d + t * a.D] = o * a.scale;
+        if constexpr (kFull)
+            a.ctx[bh * a.T * a.D + d + t * a.D] = o * a.scale;
+        else if (dok && j == 0)
+            a.ctx[bh * a.T * a.D + d + t * a.D] = o * a.scale;
         put_row(buf ^ 1, nxt.r);   // past the last step: staged but never read
         __syncthreads();
     };
@@ -285,8 +293,15 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
     __syncthreads();
     // Whole pairs in the loop, an odd last step after it: every iteration
     // runs both steps, so the sets come back to their registers at the loop's
-    // end without copies.
+    // end without copies.  The first pair runs before the loop, so the loop is
+    // entered with the same loads and stores in flight as at its back edge and
+    // its wait counts need not allow for the prologue.
     int64_t t = 0;
+    if (a.T >= 2) {
+        step(0, x0, x1);
+        step(1, x1, x0);
+        t = 2;
+    }
     for (; t + 1 < a.T; t += 2) {
         step(t, x0, x1);
         step(t + 1, x1, x0);
@@ -758,10 +773,13 @@ int gdn2_fwd(const float* query, const float* key, const float* value, const flo
     a.scale = 1.0f / sqrtf(float(L));
     const unsigned blocks = unsigned(z.BH * ((D + z.cpw - 1) / z.cpw));
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool full = D % z.cpw == 0;
     const hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
+        constexpr int kLP = decltype(lm)::value;
         void* params[] = {&a};
-        return hipLaunchKernel(reinterpret_cast<const void*>(&qc::gdn2_fwd_kernel<decltype(lm)::value>),
-                               dim3(blocks), dim3(64), params, 0, st);
+        const void* kern = full ? reinterpret_cast<const void*>(&qc::gdn2_fwd_kernel<kLP, true>)
+                                : reinterpret_cast<const void*>(&qc::gdn2_fwd_kernel<kLP, false>);
+        return hipLaunchKernel(kern, dim3(blocks), dim3(64), params, 0, st);
     });
     return e == hipSuccess ? QC_OK : qc::record_hip_error(e);
 }
