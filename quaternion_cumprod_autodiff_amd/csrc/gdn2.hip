@@ -319,7 +319,8 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
 // KC > 0: chunks of exactly KC steps keep their pre-step states in registers
 // (the recompute stores nothing, the reverse loads nothing); a shorter last
 // chunk, and every chunk when KC = 0, goes through the per-head scratch.
-template <int LP, int KC>
+// kFull: D is a multiple of the block's columns, so every lane has a column.
+template <int LP, int KC, bool kFull>
 __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) {
     static_assert(KC == 0 || (KC >= 2 && KC % 2 == 0), "register chunks are whole step pairs");
     constexpr int Q = lanes_per_col(LP), R = LP / Q, CPW = cols_per_wave(LP), CPB = cols_per_block(LP);
@@ -335,7 +336,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
     const int64_t bh = blockIdx.x / a.n_blk;
     const int blk = int(blockIdx.x % a.n_blk);
     const int64_t d = int64_t(blk) * CPB + wave * CPW + (lane >> kLogQ);
-    const bool dok = d < a.D;
+    const bool dok = kFull || d < a.D;
     // After the column reduction this lane holds row r0 + idx; lanes that
     // differ only in the bits summed by the final butterfly hold copies.
     const int idx = (lane >> (6 - kLogR)) & (R - 1);
@@ -832,8 +833,12 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
         constexpr int kLP = decltype(lm)::value;
         void* params[] = {&a};
-        const void* kern = chunk == qc::kRegChunk ? reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<kLP, qc::kRegChunk>)
-                                                  : reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<kLP, 0>);
+        const bool reg = chunk == qc::kRegChunk, full = D % qc::cols_per_block(kLP) == 0;
+        const void* kern =
+            reg ? (full ? reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<kLP, qc::kRegChunk, true>)
+                        : reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<kLP, qc::kRegChunk, false>))
+                : (full ? reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<kLP, 0, true>)
+                        : reinterpret_cast<const void*>(&qc::gdn2_bwd_kernel<kLP, 0, false>));
         return hipLaunchKernel(kern, dim3(unsigned(z.BH * z.n_blk)), dim3(threads), params, 0, st);
     });
     if (e == hipSuccess && a.part != nullptr) {
