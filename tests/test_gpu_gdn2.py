@@ -229,3 +229,19 @@ def test_backward_ignores_scratch_contents(geom):
     r_grads = oracle.gdn2_bwd(*[arrays[n] for n in NAMES], d_ctx.cpu().numpy())
     for n, g, r in zip(NAMES, runs[0], r_grads):
         close("d_" + n, g, r)
+
+
+@pytest.mark.parametrize("T", [8, 9, 16, 17, 31])
+@pytest.mark.parametrize("L,D", [(64, 64), (5, 20)])
+def test_register_chunk_orderings(T, L, D):
+    """Chunk 8 around its boundaries: one register chunk alone (T = 8), a
+    ragged scratch chunk followed by a register chunk (9, 17), register chunks
+    handing their next chunk's inputs over (16, 31), against the oracle, with
+    two heads so the hand-over's indexing is per head."""
+    B, H = 1, 2
+    print(f"[gdn2 register chunks T={T} L={L} D={D}]", flush=True)
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=100 + T + L)
+    rng = np.random.default_rng(T)
+    d_ctx = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    d_state = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    run_case(arrays, 8, d_ctx, d_state)
