@@ -21,7 +21,7 @@
  * The boundary states (entry c = the state before step c * chunk) and the
  * backward's scratch are internal formats: [B, H, ceil(T / chunk), D, LP], and
  * [B, H, min(chunk, T), D, LP] followed, when a head spans several backward
- * blocks (D > 32 for L > 16, D > 64 for L <= 16), by the blocks' shares
+ * blocks (D > 64 for L > 16, D > 128 for L <= 16), by the blocks' shares
  * [B, H, T, n_blocks, 4, L], with LP = L rounded up to 16, 32 or 64 (each
  * dense column's rows contiguous, rows past L zero); both must be 16-byte
  * aligned.  gdn2_scratch_bytes gives the size.
@@ -29,8 +29,8 @@
  * Device design: a dense column's rows are spread over 8 lanes (4 when L <=
  * 16) and columns evolve independently, so the forward runs one-wave blocks
  * over a head's columns, with the step's latent vectors broadcast through LDS;
- * it saves the state every `chunk` steps.  The backward runs blocks of 4
- * waves (32 columns, 64 when L <= 16), several per head: it walks the chunks
+ * it saves the state every `chunk` steps.  The backward runs blocks of 8
+ * waves (64 columns, 128 when L <= 16), several per head: it walks the chunks
  * in reverse, recomputes each chunk's states from its saved boundary (in
  * registers when chunk is 8, else into `scratch`), then reverses the chunk
  * step by step.  The latent-vector cotangents (query, key, erase, log_decay)

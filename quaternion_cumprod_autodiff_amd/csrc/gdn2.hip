@@ -16,8 +16,8 @@
 // loaded two steps ahead and staged in LDS, where every lane reads its own
 // rows.
 //
-// The backward runs blocks of 4 waves (one per SIMD) over 4 * 64/Q columns,
-// ceil(D / (4 * 64/Q)) blocks per head.  Chunks are taken in reverse; each
+// The backward runs blocks of 8 waves (two per SIMD) over 8 * 64/Q columns,
+// ceil(D / (8 * 64/Q)) blocks per head.  Chunks are taken in reverse; each
 // is recomputed from its saved boundary state, keeping the state before
 // every step (in registers for chunks of 8 steps, else in a per-head scratch
 // where each lane writes and reads back only its own rows), then reversed
@@ -40,7 +40,7 @@ namespace {
 
 constexpr int kMaxLatent = 64;
 constexpr int kMaxDense = 1024;
-constexpr int kBlockWaves = 4;   // backward blocks: 4 waves, one per SIMD
+constexpr int kBlockWaves = 8;   // backward blocks: 8 waves, two per SIMD
 constexpr int kRegChunk = 8;     // chunk size whose pre-step states the backward keeps in registers
 
 // Lanes per dense column: 8 when that still leaves each lane 4 or more of

@@ -218,10 +218,15 @@ def test_gdn2_sizes_and_validation(lib):
     assert lib.gdn2_boundary_bytes(1, 1, 4, 33, 2, 4) == 1 * 1 * 2 * 64 * 4     # L = 33 pads to 64
     assert lib.gdn2_boundary_bytes(1, 1, 1, 65, 4, 1) == 0                      # L > 64
     assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 1025, 1) == 0                    # D > 1024
-    # D = 100: two 64-column blocks per head; the scratch also holds their shares of the
-    # four latent-vector cotangents, [heads, T, blocks, 4, L], after the states (256-byte aligned).
-    states = 2 * 2 * 100 * 16 * 4
-    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 100, 2) == (states + 255) // 256 * 256 + 2 * 5 * 2 * 4 * 3 * 4
+    # L = 3 (16 padded rows, 4 lanes per column): backward blocks of 8 waves x 16 columns.  D = 100
+    # fits one block, and the scratch holds the states alone; D = 200 takes two blocks per head, and
+    # the scratch also holds their shares of the four latent-vector cotangents, [heads, T, blocks, 4,
+    # L], after the states (256-byte aligned).  L = 40 (64 padded rows, 8 lanes): 64-column blocks.
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 100, 2) == 2 * 2 * 100 * 16 * 4
+    states = 2 * 2 * 200 * 16 * 4
+    assert lib.gdn2_scratch_bytes(1, 2, 5, 3, 200, 2) == (states + 255) // 256 * 256 + 2 * 5 * 2 * 4 * 3 * 4
+    states = 1 * 3 * 100 * 64 * 4
+    assert lib.gdn2_scratch_bytes(1, 1, 7, 40, 100, 3) == (states + 255) // 256 * 256 + 1 * 7 * 2 * 4 * 40 * 4
     assert lib.gdn2_boundary_bytes(1, 1, 1, 4, 4, 0) == 0
     G = 1 << 30
     A = 1 << 44
