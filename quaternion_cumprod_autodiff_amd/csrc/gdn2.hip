@@ -42,6 +42,7 @@ constexpr int kMaxLatent = 64;
 constexpr int kMaxDense = 1024;
 constexpr int kBlockWaves = 8;   // backward blocks: 8 waves, two per SIMD
 constexpr int kRegChunk = 8;     // chunk size whose pre-step states the backward keeps in registers
+constexpr int kFwdSets = 4;      // forward input sets in flight: loads run this many steps ahead
 
 // Lanes per dense column: 8 when that still leaves each lane 4 or more of
 // the LP padded rows (LP >= 32), else 4; each lane holds LP / Q contiguous rows.
@@ -257,7 +258,7 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
         float wv = mul_unfused(cur.w, cur.v);
         asm volatile("" : "+v"(wv));          // the product is formed here (no instruction) ...
         __builtin_amdgcn_sched_barrier(0);    // ... and the reload is issued after it
-        load_in(t + 2, cur);
+        load_in(t + kFwdSets, cur);
         if (until_bnd == 0) {   // t is a multiple of the chunk
             if (a.bnd != nullptr && dok) store_rows<R>(a.bnd + ((bh * a.n_chunks + n_bnd) * a.D + d) * LP + r0, S);
             ++n_bnd;
@@ -286,27 +287,36 @@ __global__ void __launch_bounds__(64) gdn2_fwd_kernel(Gdn2Args a) {
         put_row(buf ^ 1, nxt.r);   // past the last step: staged but never read
         __syncthreads();
     };
-    In x0, x1;
+    // Four input sets in turn (set i holds the steps congruent to i mod 4):
+    // step t stages the row of t + 1 from its set and reloads its own set with
+    // step t + 4, so a load has three steps to land.  Whole groups of four run
+    // in the loop and the last steps after it, so the sets come back to their
+    // registers without copies; the first group runs before the loop, so the
+    // loop is entered with the same loads and stores in flight as at its back
+    // edge and its wait counts need not allow for the prologue.
+    static_assert(kFwdSets == 4, "the step calls below name four sets");
+    In x0, x1, x2, x3;
     load_in(0, x0);
     load_in(1, x1);
+    load_in(2, x2);
+    load_in(3, x3);
     put_row(0, x0.r);
     __syncthreads();
-    // Whole pairs in the loop, an odd last step after it: every iteration
-    // runs both steps, so the sets come back to their registers at the loop's
-    // end without copies.  The first pair runs before the loop, so the loop is
-    // entered with the same loads and stores in flight as at its back edge and
-    // its wait counts need not allow for the prologue.
-    int64_t t = 0;
-    if (a.T >= 2) {
-        step(0, x0, x1);
-        step(1, x1, x0);
-        t = 2;
-    }
-    for (; t + 1 < a.T; t += 2) {
+    auto group = [&](int64_t t) {
         step(t, x0, x1);
-        step(t + 1, x1, x0);
+        step(t + 1, x1, x2);
+        step(t + 2, x2, x3);
+        step(t + 3, x3, x0);
+    };
+    int64_t t = 0;
+    if (a.T >= 4) {
+        group(0);
+        t = 4;
     }
+    for (; t + 4 <= a.T; t += 4) group(t);
     if (t < a.T) step(t, x0, x1);
+    if (t + 1 < a.T) step(t + 1, x1, x2);
+    if (t + 2 < a.T) step(t + 2, x2, x3);
     if (a.state != nullptr && dok) {
 #pragma unroll
         for (int i = 0; i < R; ++i)
