@@ -186,13 +186,13 @@ __device__ __forceinline__ void load_rows_of(const float* p, float (&x)[R]) {
 // bit.  The step's latent vectors are staged in LDS (q, k, decay, erased key,
 // and for the backward the raw erase), where every lane reads its own rows.
 //
-// Loads run two steps ahead, into two register sets taken in turn by the
-// two-step unrolled loops, so a load has a whole step to land before its
-// value is used and is never copied while in flight.  Every lane loads every
-// step: rows past L read row L-1, columns past D read column D-1 and steps
-// past the range repeat its last step (values that are then masked or
-// unused), so the loads are unconditional and the compiler's wait counts
-// stay exact.
+// Loads run ahead into register sets taken in turn by loops unrolled over the
+// sets (four in the forward, two in the backward), so a load has whole steps
+// to land before its value is used and is never copied while in flight.
+// Every lane loads every step: rows past L read row L-1, columns past D read
+// column D-1 and steps past the range repeat its last step (values that are
+// then masked or unused), so the loads are unconditional and the compiler's
+// wait counts stay exact.
 
 enum { kVq = 0, kVk = 1, kVa = 2, kVe = 3, kVb = 4, kNVec = 4, kNRow = 5 };
 
