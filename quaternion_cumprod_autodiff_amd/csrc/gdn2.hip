@@ -393,6 +393,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         float v, w, dc;
     };
     Dense denA{0.0f, 0.0f, 0.0f}, denB{0.0f, 0.0f, 0.0f};
+    Dense denC{0.0f, 0.0f, 0.0f}, denD{0.0f, 0.0f, 0.0f};   // register chunks: four sets
     float SpA[R], SpB[R];
     auto load_dense = [&](int64_t t, bool with_dc, Dense& dn) {
         dn.v = a.v[lcol0 + t * a.D];
@@ -570,44 +571,44 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         if constexpr (KC > 0) {
             if (t1 - t0 == KC) {   // whole chunk: states in registers
                 // Loads run ahead across the sweeps: the recompute's last two
-                // steps load what the reverse starts with (rows t1 - 1, t1 - 2,
-                // the dense inputs of t1 - 1 with the context cotangent), and
+                // steps load what the reverse starts with (rows and dense
+                // inputs, with the context cotangent, of t1 - 1 and t1 - 2), and
                 // the reverse's last two load the next chunk's start (its
                 // boundary state, rows and dense inputs), so no sweep starts
                 // by waiting for memory.
+                // Dense inputs run two steps ahead here, through four sets
+                // (step k of the chunk reads set k mod 4 and loads step k + 2
+                // into set k + 2 mod 4, downwards in the reverse).
+                static_assert(KC == 8, "the step calls below spell out a chunk of 8");
                 float Sst[KC][R];
-                if (primed)
+                if (primed) {
                     put_row(it & 1, rX);
-                else
+                } else {
                     start_sweep(t0, t0 + 1, false);
-                __syncthreads();
-#pragma unroll
-                for (int k = 0; k < KC; k += 2) {
-                    const int64_t t = t0 + k;
-                    if (k + 2 < KC) {
-                        rec_step(t, denA, denB, rX, rY, Sst[k], false, t + 2, t + 1, false);
-                        rec_step(t + 1, denB, denA, rY, rX, Sst[k + 1], false, t + 3, t + 2, false);
-                    } else {
-                        rec_step(t, denA, denB, rX, rY, Sst[k], false, t1 - 1, t1 - 1, false);
-                        rec_step(t + 1, denB, denA, rY, rX, Sst[k + 1], false, t1 - 2, t1 - 1, true);
-                    }
+                    load_dense(t0 + 1, false, denB);
                 }
+                __syncthreads();
+                rec_step(t0, denA, denC, rX, rY, Sst[0], false, t0 + 2, t0 + 2, false);
+                rec_step(t0 + 1, denB, denD, rY, rX, Sst[1], false, t0 + 3, t0 + 3, false);
+                rec_step(t0 + 2, denC, denA, rX, rY, Sst[2], false, t0 + 4, t0 + 4, false);
+                rec_step(t0 + 3, denD, denB, rY, rX, Sst[3], false, t0 + 5, t0 + 5, false);
+                rec_step(t0 + 4, denA, denC, rX, rY, Sst[4], false, t0 + 6, t0 + 6, false);
+                rec_step(t0 + 5, denB, denD, rY, rX, Sst[5], false, t0 + 7, t0 + 7, false);
+                rec_step(t0 + 6, denC, denA, rX, rY, Sst[6], false, t1 - 1, t1 - 1, true);
+                rec_step(t0 + 7, denD, denB, rY, rX, Sst[7], false, t1 - 2, t1 - 2, true);
                 if (c > 0) load_boundary(c - 1);   // S is not read again in this chunk
                 put_row(it & 1, rX);
                 __syncthreads();
                 const int64_t n0 = c > 0 ? t0 - KC : t0;   // next chunk's first step (or a repeat)
-#pragma unroll
-                for (int k = KC - 1; k > 0; k -= 2) {
-                    const int64_t t = t0 + k;
-                    if (k > 1) {
-                        rev_step(t, denA, Sst[k], denB, SpB, rX, rY, false, k, false, t - 2, t - 1);
-                        rev_step(t - 1, denB, Sst[k - 1], denA, SpB, rY, rX, false, k - 1, false, t - 3, t - 2);
-                    } else {
-                        rev_step(t, denA, Sst[k], denB, SpB, rX, rY, false, k, false, n0, t - 1);
-                        rev_step(t - 1, denB, Sst[k - 1], denA, SpB, rY, rX, false, k - 1, false,
-                                 c > 0 ? n0 + 1 : t0, n0);
-                    }
-                }
+                const int64_t n1 = c > 0 ? n0 + 1 : t0;
+                rev_step(t0 + 7, denA, Sst[7], denC, SpB, rX, rY, false, 7, false, t0 + 5, t0 + 5);
+                rev_step(t0 + 6, denB, Sst[6], denD, SpB, rY, rX, false, 6, false, t0 + 4, t0 + 4);
+                rev_step(t0 + 5, denC, Sst[5], denA, SpB, rX, rY, false, 5, false, t0 + 3, t0 + 3);
+                rev_step(t0 + 4, denD, Sst[4], denB, SpB, rY, rX, false, 4, false, t0 + 2, t0 + 2);
+                rev_step(t0 + 3, denA, Sst[3], denC, SpB, rX, rY, false, 3, false, t0 + 1, t0 + 1);
+                rev_step(t0 + 2, denB, Sst[2], denD, SpB, rY, rX, false, 2, false, t0, t0);
+                rev_step(t0 + 1, denC, Sst[1], denA, SpB, rX, rY, false, 1, false, n0, n0);
+                rev_step(t0, denD, Sst[0], denB, SpB, rY, rX, false, 0, false, n1, n1);
                 // The chunk's sums, its steps dealt over the waves (the last
                 // step's barrier published every slot; the next chunk's
                 // recompute barriers come before any slot is written again).
