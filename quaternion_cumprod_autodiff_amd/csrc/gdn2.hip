@@ -447,6 +447,9 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         }
     };
     bool primed = false;
+    // Register chunks of full blocks: a whole chunk's staged rows, two buffers used in turn.
+    __shared__ float s_chunk[KC > 0 && kFull ? 2 : 1][KC > 0 ? KC : 1][kNVec][LP];
+    int cb = 0;
     for (int64_t c = a.n_chunks - 1; c >= 0; --c) {
         const int64_t t0 = c * a.chunk;
         const int64_t t1 = t0 + a.chunk < a.T ? t0 + a.chunk : a.T;
@@ -458,11 +461,17 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         // the end of the step; dnxt receives the dense inputs of dense_t.
         // The state before the step goes to the scratch (to_scratch) or to
         // the registers `keep`.
+        // With svx set, the step's rows come from there (a chunk staged
+        // whole) and the step neither loads nor stages rows nor waits at a
+        // barrier.
         auto rec_step = [&](int64_t t, Dense& dcur, Dense& dnxt, Row& rl, const Row& rs, float (&keep)[R],
-                            bool to_scratch, int64_t row_t, int64_t dense_t, bool dense_dc) {
+                            bool to_scratch, int64_t row_t, int64_t dense_t, bool dense_dc,
+                            const float (*svx)[LP]) {
             const int buf = it & 1;
-            ++it;
-            load_row(row_t, rl);
+            if (svx == nullptr) {
+                ++it;
+                load_row(row_t, rl);
+            }
             load_dense(dense_t, dense_dc, dnxt);
             if (to_scratch) {
                 if (dok) store_rows<R>(scr + (t - t0) * scr_step, S);
@@ -470,7 +479,7 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
 #pragma unroll
                 for (int i = 0; i < R; ++i) keep[i] = S[i];
             }
-            const float(*sv)[LP] = s_rows[buf];
+            const float(*sv)[LP] = svx != nullptr ? svx : s_rows[buf];
             float read = 0.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i) {
@@ -480,8 +489,10 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             const float u = mul_unfused(dcur.w, dcur.v) - group_sum<Q>(read);
 #pragma unroll
             for (int i = 0; i < R; ++i) S[i] = fmaf(sv[kVk][r0 + i], u, S[i]);
-            put_row(buf ^ 1, rs);   // after the chunk's last step: staged but never read
-            __syncthreads();
+            if (svx == nullptr) {
+                put_row(buf ^ 1, rs);   // after the chunk's last step: staged but never read
+                __syncthreads();
+            }
         };
         // Reverse the chunk (downwards): the dense inputs and the state
         // before the step load one step ahead, rows two ahead as above (rl
@@ -497,15 +508,17 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         // and dense inputs this step loads.
         auto rev_step = [&](int64_t t, Dense& dcur, float (&Sp)[R], Dense& dnxt, float (&Sn)[R], Row& rl,
                             const Row& rs, bool from_scratch, int slot, bool sum_now, int64_t row_t,
-                            int64_t dense_t) {
+                            int64_t dense_t, const float (*svx)[LP]) {
             const int buf = it & 1;
-            ++it;
+            if (svx == nullptr) {
+                ++it;
+                load_row(row_t, rl);
+            }
             const int64_t tp = t > t0 ? t - 1 : t0;
             const int64_t e = col0 + t * a.D;
-            load_row(row_t, rl);
             load_dense(dense_t, true, dnxt);
             if (from_scratch) load_rows_of<R>(scr + (tp - t0) * scr_step, Sn);
-            const float(*sv)[LP] = s_rows[buf];
+            const float(*sv)[LP] = svx != nullptr ? svx : s_rows[buf];
             const float dov = dok ? dcur.dc * a.scale : 0.0f;
             if (!dok) {
 #pragma unroll
@@ -553,8 +566,10 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                 s_red[slot][wave][2][r0 + idx] = r_e;
                 s_red[slot][wave][3][r0 + idx] = r_a;
             }
-            put_row(buf ^ 1, rs);   // after the chunk's first step: staged but never read
-            __syncthreads();
+            if (svx == nullptr) {
+                put_row(buf ^ 1, rs);   // after the chunk's first step: staged but never read
+                __syncthreads();
+            }
             if (sum_now && out_lane) {
                 float sq, sk, se, sa;
                 wave_sums(slot, tid, sq, sk, se, sa);
@@ -568,6 +583,86 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
             load_row(t_second, rY);
             load_dense(t_first, with_dc, denA);
         };
+        if constexpr (KC > 0 && kFull) {
+            if (t1 - t0 == KC) {   // whole chunk, rows staged whole: no barrier inside the chunk
+                // Every thread stages one (step, row) pair of a chunk: the
+                // chunk's latent vectors go to LDS at once, loaded a whole
+                // chunk ahead, so the steps neither load nor stage rows and
+                // each wave runs the chunk's 16 steps without a barrier (its
+                // column sums go to per-step slots, added at the chunk's end).
+                // The dense inputs run two steps ahead through four sets as
+                // below, and the reverse's last two steps load the next
+                // chunk's first dense inputs.
+                static_assert(KC == 8 && KC * 64 <= kBlockWaves * 64, "one (step, row) pair per thread");
+                const int pk = tid / LP, pr = tid % LP;
+                const bool pair = tid < KC * LP, plive = pr < a.L;
+                const int64_t prow = bh * a.T * a.L + (plive ? pr : a.L - 1);
+                auto load_chunk_row = [&](int64_t cc, Row& r) {
+                    const int64_t i = prow + (cc * KC + (pair ? pk : 0)) * a.L;
+                    r.q = a.q[i];
+                    r.k = a.k[i];
+                    r.b = a.b[i];
+                    r.g = a.g[i];
+                };
+                auto stage_chunk_row = [&](int buf, const Row& r) {
+                    if (pair) {
+                        s_chunk[buf][pk][kVq][pr] = plive ? r.q : 0.0f;
+                        s_chunk[buf][pk][kVk][pr] = plive ? r.k : 0.0f;
+                        s_chunk[buf][pk][kVa][pr] = plive ? __expf(r.g) : 1.0f;
+                        s_chunk[buf][pk][kVe][pr] = plive ? r.b * r.k : 0.0f;
+                    }
+                };
+                if (!primed) {
+                    Row first{0.0f, 0.0f, 0.0f, 0.0f};
+                    load_chunk_row(c, first);
+                    stage_chunk_row(cb, first);
+                    load_dense(t0, false, denA);
+                    load_dense(t0 + 1, false, denB);
+                    __syncthreads();
+                }
+                Row nxt{0.0f, 0.0f, 0.0f, 0.0f};
+                if (c > 0) load_chunk_row(c - 1, nxt);
+                const float(*sc)[kNVec][LP] = s_chunk[cb];
+                float Sst[KC][R];
+                rec_step(t0, denA, denC, rX, rY, Sst[0], false, 0, t0 + 2, false, sc[0]);
+                rec_step(t0 + 1, denB, denD, rY, rX, Sst[1], false, 0, t0 + 3, false, sc[1]);
+                rec_step(t0 + 2, denC, denA, rX, rY, Sst[2], false, 0, t0 + 4, false, sc[2]);
+                rec_step(t0 + 3, denD, denB, rY, rX, Sst[3], false, 0, t0 + 5, false, sc[3]);
+                rec_step(t0 + 4, denA, denC, rX, rY, Sst[4], false, 0, t0 + 6, false, sc[4]);
+                rec_step(t0 + 5, denB, denD, rY, rX, Sst[5], false, 0, t0 + 7, false, sc[5]);
+                rec_step(t0 + 6, denC, denA, rX, rY, Sst[6], false, 0, t1 - 1, true, sc[6]);
+                rec_step(t0 + 7, denD, denB, rY, rX, Sst[7], false, 0, t1 - 2, true, sc[7]);
+                if (c > 0) load_boundary(c - 1);   // S is not read again in this chunk
+                const int64_t n0 = c > 0 ? t0 - KC : t0;   // next chunk's first step (or a repeat)
+                const int64_t n1 = c > 0 ? n0 + 1 : t0;
+                rev_step(t0 + 7, denA, Sst[7], denC, SpB, rX, rY, false, 7, false, 0, t0 + 5, sc[7]);
+                rev_step(t0 + 6, denB, Sst[6], denD, SpB, rY, rX, false, 6, false, 0, t0 + 4, sc[6]);
+                rev_step(t0 + 5, denC, Sst[5], denA, SpB, rX, rY, false, 5, false, 0, t0 + 3, sc[5]);
+                rev_step(t0 + 4, denD, Sst[4], denB, SpB, rY, rX, false, 4, false, 0, t0 + 2, sc[4]);
+                rev_step(t0 + 3, denA, Sst[3], denC, SpB, rX, rY, false, 3, false, 0, t0 + 1, sc[3]);
+                rev_step(t0 + 2, denB, Sst[2], denD, SpB, rY, rX, false, 2, false, 0, t0, sc[2]);
+                rev_step(t0 + 1, denC, Sst[1], denA, SpB, rX, rY, false, 1, false, 0, n0, sc[1]);
+                rev_step(t0, denD, Sst[0], denB, SpB, rY, rX, false, 0, false, 0, n1, sc[0]);
+                __syncthreads();   // every slot written; this chunk's staged rows no longer read
+                if (lane < a.L) {
+                    for (int k = wave; k < KC; k += n_waves) {
+                        const int64_t t = t0 + k;
+                        const int64_t i = (bh * a.T + t) * a.L + lane;
+                        float sq, sk, se, sa;
+                        wave_sums(k, lane, sq, sk, se, sa);
+                        if (a.n_blk == 1)
+                            emit(t, lane, sq, sk, se, sa, a.k[i], a.b[i], __expf(a.g[i]));
+                        else
+                            emit(t, lane, sq, sk, se, sa, 0.0f, 0.0f, 0.0f);
+                    }
+                }
+                if (c > 0) stage_chunk_row(cb ^ 1, nxt);
+                __syncthreads();   // the sums read before any slot is written again; next rows staged
+                cb ^= 1;
+                primed = c > 0;
+                continue;
+            }
+        }
         if constexpr (KC > 0) {
             if (t1 - t0 == KC) {   // whole chunk: states in registers
                 // Loads run ahead across the sweeps: the recompute's last two
@@ -588,27 +683,27 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
                     load_dense(t0 + 1, false, denB);
                 }
                 __syncthreads();
-                rec_step(t0, denA, denC, rX, rY, Sst[0], false, t0 + 2, t0 + 2, false);
-                rec_step(t0 + 1, denB, denD, rY, rX, Sst[1], false, t0 + 3, t0 + 3, false);
-                rec_step(t0 + 2, denC, denA, rX, rY, Sst[2], false, t0 + 4, t0 + 4, false);
-                rec_step(t0 + 3, denD, denB, rY, rX, Sst[3], false, t0 + 5, t0 + 5, false);
-                rec_step(t0 + 4, denA, denC, rX, rY, Sst[4], false, t0 + 6, t0 + 6, false);
-                rec_step(t0 + 5, denB, denD, rY, rX, Sst[5], false, t0 + 7, t0 + 7, false);
-                rec_step(t0 + 6, denC, denA, rX, rY, Sst[6], false, t1 - 1, t1 - 1, true);
-                rec_step(t0 + 7, denD, denB, rY, rX, Sst[7], false, t1 - 2, t1 - 2, true);
+                rec_step(t0, denA, denC, rX, rY, Sst[0], false, t0 + 2, t0 + 2, false, nullptr);
+                rec_step(t0 + 1, denB, denD, rY, rX, Sst[1], false, t0 + 3, t0 + 3, false, nullptr);
+                rec_step(t0 + 2, denC, denA, rX, rY, Sst[2], false, t0 + 4, t0 + 4, false, nullptr);
+                rec_step(t0 + 3, denD, denB, rY, rX, Sst[3], false, t0 + 5, t0 + 5, false, nullptr);
+                rec_step(t0 + 4, denA, denC, rX, rY, Sst[4], false, t0 + 6, t0 + 6, false, nullptr);
+                rec_step(t0 + 5, denB, denD, rY, rX, Sst[5], false, t0 + 7, t0 + 7, false, nullptr);
+                rec_step(t0 + 6, denC, denA, rX, rY, Sst[6], false, t1 - 1, t1 - 1, true, nullptr);
+                rec_step(t0 + 7, denD, denB, rY, rX, Sst[7], false, t1 - 2, t1 - 2, true, nullptr);
                 if (c > 0) load_boundary(c - 1);   // S is not read again in this chunk
                 put_row(it & 1, rX);
                 __syncthreads();
                 const int64_t n0 = c > 0 ? t0 - KC : t0;   // next chunk's first step (or a repeat)
                 const int64_t n1 = c > 0 ? n0 + 1 : t0;
-                rev_step(t0 + 7, denA, Sst[7], denC, SpB, rX, rY, false, 7, false, t0 + 5, t0 + 5);
-                rev_step(t0 + 6, denB, Sst[6], denD, SpB, rY, rX, false, 6, false, t0 + 4, t0 + 4);
-                rev_step(t0 + 5, denC, Sst[5], denA, SpB, rX, rY, false, 5, false, t0 + 3, t0 + 3);
-                rev_step(t0 + 4, denD, Sst[4], denB, SpB, rY, rX, false, 4, false, t0 + 2, t0 + 2);
-                rev_step(t0 + 3, denA, Sst[3], denC, SpB, rX, rY, false, 3, false, t0 + 1, t0 + 1);
-                rev_step(t0 + 2, denB, Sst[2], denD, SpB, rY, rX, false, 2, false, t0, t0);
-                rev_step(t0 + 1, denC, Sst[1], denA, SpB, rX, rY, false, 1, false, n0, n0);
-                rev_step(t0, denD, Sst[0], denB, SpB, rY, rX, false, 0, false, n1, n1);
+                rev_step(t0 + 7, denA, Sst[7], denC, SpB, rX, rY, false, 7, false, t0 + 5, t0 + 5, nullptr);
+                rev_step(t0 + 6, denB, Sst[6], denD, SpB, rY, rX, false, 6, false, t0 + 4, t0 + 4, nullptr);
+                rev_step(t0 + 5, denC, Sst[5], denA, SpB, rX, rY, false, 5, false, t0 + 3, t0 + 3, nullptr);
+                rev_step(t0 + 4, denD, Sst[4], denB, SpB, rY, rX, false, 4, false, t0 + 2, t0 + 2, nullptr);
+                rev_step(t0 + 3, denA, Sst[3], denC, SpB, rX, rY, false, 3, false, t0 + 1, t0 + 1, nullptr);
+                rev_step(t0 + 2, denB, Sst[2], denD, SpB, rY, rX, false, 2, false, t0, t0, nullptr);
+                rev_step(t0 + 1, denC, Sst[1], denA, SpB, rX, rY, false, 1, false, n0, n0, nullptr);
+                rev_step(t0, denD, Sst[0], denB, SpB, rY, rX, false, 0, false, n1, n1, nullptr);
                 // The chunk's sums, its steps dealt over the waves (the last
                 // step's barrier published every slot; the next chunk's
                 // recompute barriers come before any slot is written again).
@@ -632,20 +727,20 @@ __global__ void __launch_bounds__(kBlockWaves * 64) gdn2_bwd_kernel(Gdn2Args a) 
         __syncthreads();
         for (int64_t t = t0; t < t1; t += 2) {
             rec_step(t, denA, denB, rX, rY, SpA, true, t + 2 < t1 ? t + 2 : t1 - 1, t + 1 < t1 ? t + 1 : t1 - 1,
-                     false);
+                     false, nullptr);
             if (t + 1 < t1)
                 rec_step(t + 1, denB, denA, rY, rX, SpA, true, t + 3 < t1 ? t + 3 : t1 - 1,
-                         t + 2 < t1 ? t + 2 : t1 - 1, false);
+                         t + 2 < t1 ? t + 2 : t1 - 1, false, nullptr);
         }
         start_sweep(t1 - 1, t1 - 2 >= t0 ? t1 - 2 : t0, true);
         load_rows_of<R>(scr + (t1 - 1 - t0) * scr_step, SpA);
         __syncthreads();
         for (int64_t t = t1 - 1; t >= t0; t -= 2) {
             rev_step(t, denA, SpA, denB, SpB, rX, rY, true, it & 1, true, t - 2 >= t0 ? t - 2 : t0,
-                     t - 1 >= t0 ? t - 1 : t0);
+                     t - 1 >= t0 ? t - 1 : t0, nullptr);
             if (t - 1 >= t0)
                 rev_step(t - 1, denB, SpB, denA, SpA, rY, rX, true, it & 1, true, t - 3 >= t0 ? t - 3 : t0,
-                         t - 2 >= t0 ? t - 2 : t0);
+                         t - 2 >= t0 ? t - 2 : t0, nullptr);
         }
         primed = false;
     }
