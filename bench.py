@@ -428,7 +428,7 @@ def scan_bench(args):
 # -------------------------------------------------------- Gated DeltaNet-2
 # The recurrence of include/gdn2.h at the page's training head shape (latent
 # 64, dense 128) over 8 x 16 heads and 2048 steps; boundary states every 8
-# steps, the chunk whose states the backward keeps in registers (3.9 ms per
+# steps, the chunk whose states the backward keeps in registers (3.7 ms per
 # step against 6.0 at chunk 32).
 GDN2_WORKLOAD = (8, 16, 2048, 64, 128, 8)
 FP32_VECTOR_PEAK_TFLOPS = 157.3

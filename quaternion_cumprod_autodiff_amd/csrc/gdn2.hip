@@ -13,8 +13,8 @@
 // = L rounded up to 16, 32 or 64) in registers; a wave holds 64/Q columns.
 // Sums over a column's rows (the erased read-out, the context, d u) are a
 // partial per lane plus a DPP butterfly.  The step's latent vectors are
-// loaded two steps ahead and staged in LDS, where every lane reads its own
-// rows.
+// loaded ahead and staged in LDS, where every lane reads its own rows (the
+// backward's full blocks stage a whole register chunk's rows at once).
 //
 // The backward runs blocks of 8 waves (two per SIMD) over 8 * 64/Q columns,
 // ceil(D / (8 * 64/Q)) blocks per head.  Chunks are taken in reverse; each
