@@ -202,6 +202,37 @@ def copy_calibration(nbytes: int, steps: int, warmup: int):
     return 2.0 * nbytes / dt / 1e9, dt
 
 
+def copy_ceiling(nbytes: int, steps: int = 20):
+    """The hand-written streaming copy (include/qc_bench.h) of one nbytes
+    tensor: best rate over a few grid sizes (blocks per compute unit), each
+    timed over `steps` copies between device synchronisations."""
+    import torch
+
+    from quaternion_cumprod_autodiff_amd import capi
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    best = None
+    for bpc in (2, 4, 8, 16):
+        for _ in range(5):
+            capi.stream_copy(src, dst, blocks_per_cu=bpc)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            capi.stream_copy(src, dst, blocks_per_cu=bpc)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        gbps = 2.0 * nbytes / dt / 1e9
+        if best is None or gbps > best[0]:
+            best = (gbps, dt, bpc)
+    if not torch.equal(src, dst):
+        raise RuntimeError("the streaming copy produced a different tensor")
+    torch_gbps, torch_dt = copy_calibration(nbytes, steps, 5)
+    return {"value": round(best[0], 1), "unit": "GB/s", "ms": round(best[1] * 1e3, 4),
+            "kind": f"qc_stream_copy of one {nbytes} B tensor (read + write), {best[2]} blocks per CU, "
+                    f"best of 2/4/8/16, {steps} timed",
+            "torch_copy": {"value": round(torch_gbps, 1), "ms": round(torch_dt * 1e3, 4)}}
+
+
 # ------------------------------------------------------------- generic scan
 # The scan VJP of include/qc_scan.h (add or quaternion body, one column per
 # thread).  Workload: the page's scan test length, 129 steps, over enough
@@ -542,6 +573,150 @@ def gdn2_cpu_baseline(arrays, d_ctx, total_bytes, min_seconds: float = 10.0):
                       f"{reps} pass(es), {per_pass:.3f} s per pass"}
 
 
+# ---------------------------------------------------------------- per config
+def all_configs_bench(args):
+    """One JSON line per named workload and backward mode: forward, backward
+    and whole-step rates (algorithmic bytes / time), elements per second and
+    fractions of 8 TB/s.  Step time is wall time over --steps steps between
+    device synchronisations; the forward and backward times are medians of
+    20 event-bracketed launches each, after the timed steps."""
+    import numpy as np
+    import torch
+
+    from quaternion_cumprod_autodiff_amd import capi
+    from quaternion_cumprod_autodiff_amd.inputs import CONFIGS, make_config
+
+    dev = torch.device("cuda:0")
+    names = args.configs.split(",") if args.configs else list(CONFIGS)
+    for name in names:
+        b, s, h, j, recipe, io = CONFIGS[name]
+        n, cols = b * s * h * j, b * h * j
+        io_bytes = 16 if io == "f32" else 8
+        inp = make_config(name, want_f64=False)
+
+        def up(a):
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if io == "bf16" else np.float32)).to(dev)
+            return t.view(torch.bfloat16) if io == "bf16" else t
+
+        q, init, d_cum = up(inp.q), up(inp.init), up(inp.d_cum)
+        del inp
+        cum, d_q, d_init = torch.empty_like(q), torch.empty_like(q), torch.empty_like(init)
+        fwd_bytes = 2 * io_bytes * n + io_bytes * cols
+        bwd_bytes = 3 * io_bytes * n + 2 * io_bytes * cols
+        for mode in ("saved boundary state", "leaves-only"):
+            ckpt = capi.new_ckpt(q) if mode == "saved boundary state" else None
+
+            def fwd():
+                capi.quat_cumprod_fwd(q, init, cum, ckpt)
+
+            def bwd():
+                capi.quat_cumprod_bwd(q, init, d_cum, ckpt, d_q=d_q, d_init=d_init)
+
+            warm, t0 = 0, time.perf_counter()
+            while warm < args.warmup or (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+                fwd()
+                bwd()
+                warm += 1
+                if warm % 16 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                fwd()
+                bwd()
+            torch.cuda.synchronize()
+            step_ms = (time.perf_counter() - t0) / args.steps * 1e3
+            ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+            diag = [((ev(), ev()), (ev(), ev())) for _ in range(20)]
+            for (f0, f1), (b0, b1) in diag:
+                f0.record()
+                fwd()
+                f1.record()
+                b0.record()
+                bwd()
+                b1.record()
+            torch.cuda.synchronize()
+            if capi.default_workspace.status(dev) != 0:
+                raise RuntimeError(f"{name}: a cross-block wait hit its spin limit")
+            fwd_ms = float(np.median([a.elapsed_time(c) for (a, c), _ in diag]))
+            bwd_ms = float(np.median([a.elapsed_time(c) for _, (a, c) in diag]))
+            gb = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9   # noqa: E731
+            rec = {
+                "metric": "quat cumprod fwd+bwd GB/s and % HBM peak, per workload",
+                "config": {"workload": f"{name} b{b} s{s} h{h} j{j} {io} I/O, forward + backward", "b": b,
+                           "s": s, "h": h, "j": j, "io_dtype": io, "recipe": recipe},
+                "backward": mode, "steps": args.steps,
+                "cache_resident": fwd_bytes < 256 * 2 ** 20,
+                "step_us": round(step_ms * 1e3, 2), "fwd_us": round(fwd_ms * 1e3, 2),
+                "bwd_us": round(bwd_ms * 1e3, 2),
+                "GBps": round(gb(fwd_bytes + bwd_bytes, step_ms), 1),
+                "fwd_GBps": round(gb(fwd_bytes, fwd_ms), 1), "bwd_GBps": round(gb(bwd_bytes, bwd_ms), 1),
+                "hbm_frac": round(gb(fwd_bytes + bwd_bytes, step_ms) / HBM_PEAK_GBPS, 4),
+                "fwd_hbm_frac": round(gb(fwd_bytes, fwd_ms) / HBM_PEAK_GBPS, 4),
+                "bwd_hbm_frac": round(gb(bwd_bytes, bwd_ms) / HBM_PEAK_GBPS, 4),
+                "elements_per_s": round(n / (step_ms * 1e-3), 1),
+                "fwd_bytes": fwd_bytes, "bwd_bytes": bwd_bytes,
+            }
+            print(json.dumps(rec), flush=True)
+        del q, init, d_cum, cum, d_q, d_init
+        torch.cuda.empty_cache()
+
+
+def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command: str):
+    """Write profiles/kernels_<config>.txt from a rocprofv3 --kernel-trace
+    --stats run (and, with pmc_dir, its FETCH_SIZE / WRITE_SIZE runs scaled by
+    the plain-copy calibration factors of traffic_headline.txt)."""
+    import csv
+    import statistics
+
+    from quaternion_cumprod_autodiff_amd.inputs import CONFIGS
+    b, s, h, j, recipe, io = CONFIGS[config]
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    lines = [f"# Kernel durations and HBM traffic, workload {config} (b{b} s{s} h{h} j{j}, {io} I/O, "
+             f"recipe {recipe}), one MI355X.",
+             "# Commands (from /tmp, TMPDIR=/tmp, R = repository root, OUT = an output directory):"]
+    lines += ["#   " + c for c in command.split(" ;; ")]
+    lines.append("#")
+    lines.append("# rocprofv3 run_kernel_stats.csv (every dispatch of the traced run)")
+    lines.append(f"# {'kernel':60s} {'calls':>6s} {'avg ns':>10s} {'min ns':>10s} {'max ns':>10s}")
+    for r in rows:
+        name = r["Name"]
+        lines.append(f"{name[:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']):10.0f} "
+                     f"{float(r['MinNs']):10.0f} {float(r['MaxNs']):10.0f}")
+    if pmc_dir:
+        cal = read_kv(TRAFFIC_FILE)
+        fs, ws = float(cal["fetch_scale"]), float(cal["write_scale"])
+
+        def per_kernel(counter):
+            vals = {}
+            for r in csv.DictReader(open(os.path.join(pmc_dir, counter, "run_counter_collection.csv"))):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+            return {k: statistics.median(v) for k, v in vals.items()}
+
+        f, w = per_kernel("FETCH_SIZE"), per_kernel("WRITE_SIZE")
+        n, cols = b * s * h * j, b * h * j
+        io_bytes = 16 if io == "f32" else 8
+        alg = {"fwd_chunked_kernel": 2 * io_bytes * n + io_bytes * cols,
+               "fwd_column_kernel": 2 * io_bytes * n + io_bytes * cols,
+               "bwd_chunked_kernel": 3 * io_bytes * n + 2 * io_bytes * cols}
+        lines.append("#")
+        lines.append(f"# HBM bytes per launch: FETCH_SIZE x {fs:.4f} + WRITE_SIZE x {ws:.4f} (the plain-copy "
+                     "calibration factors of traffic_headline.txt), median over the run's launches")
+        lines.append(f"# {'kernel':60s} {'fetch B':>14s} {'write B':>14s} {'algorithmic B':>14s} {'ratio':>6s}")
+        for k in sorted(set(f) & set(w)):
+            if "zero_words" in k or "bump_epoch" in k:
+                continue
+            base = next((v for key, v in alg.items() if key in k and ", false>" not in k), None)
+            tot = f[k] * fs + w[k] * ws
+            lines.append(f"{k[:62]:62s} {f[k] * fs:14.0f} {w[k] * ws:14.0f} "
+                         f"{(base if base else 0):14d} {(tot / base if base else 0):6.3f}")
+    path = os.path.join(ROOT, "profiles", f"kernels_{config}.txt")
+    with open(path, "w") as out:
+        out.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -576,7 +751,20 @@ def main():
                     help="measure the Gated DeltaNet-2 forward + VJP (include/gdn2.h) instead")
     ap.add_argument("--gdn2-chunk", type=int, default=0,
                     help="with --gdn2: steps between saved boundary states (default: the workload's)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one JSON line per named workload and backward mode (forward, backward, step rates)")
+    ap.add_argument("--configs", default="",
+                    help="with --all-configs: comma-separated workload names (default: all)")
+    ap.add_argument("--summarize-profile", metavar="TRACE_DIR",
+                    help="write profiles/kernels_<config>.txt from a rocprofv3 kernel-trace run of --config")
+    ap.add_argument("--pmc-dir", default=None,
+                    help="with --summarize-profile: directory holding FETCH_SIZE/ and WRITE_SIZE/ counter runs")
+    ap.add_argument("--profile-command", default="",
+                    help="with --summarize-profile: the commands that made the runs (' ;; '-separated)")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.config, args.pmc_dir, args.profile_command)
+        return
     if args.summarize_scan_traffic:
         cal = read_kv(TRAFFIC_FILE)
         summarize_scan_traffic(args.summarize_scan_traffic, float(cal["fetch_scale"]), float(cal["write_scale"]))
@@ -597,6 +785,9 @@ def main():
         return
     if args.gdn2:
         gdn2_bench(args)
+        return
+    if args.all_configs:
+        all_configs_bench(args)
         return
 
     import numpy as np
@@ -755,11 +946,12 @@ def main():
             "value": round((fwd_bytes + bwd_bytes) / (leaves * 1e-3) / 1e9, 2), "unit": "GB/s",
             "ms_per_step": round(leaves, 4), "steps": args.leaves_steps,
             "mode": "forward saves only q and init; backward re-derives the boundary state from q"}
-    # Practical ceiling beside the roofline: a plain device copy of one tensor
-    # of the workload (read + write), after the timed region.
-    cgbps, cdt = copy_calibration(n * io_bytes, 20, 5)
-    rec["copy_ceiling"] = {"value": round(cgbps, 1), "unit": "GB/s", "ms": round(cdt * 1e3, 4),
-                           "kind": f"torch device-to-device copy of one {n * io_bytes} B tensor, 20 timed"}
+    # Practical ceiling beside the roofline: the library's hand-written
+    # streaming copy of one tensor of the workload (read + write), after the
+    # timed region, at its best grid of a short sweep.
+    ceil = copy_ceiling(n * io_bytes)
+    rec["copy_ceiling"] = ceil
+    rec["roofline"]["frac_of_copy_ceiling"] = round(bwd_gbps / ceil["value"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(inp)

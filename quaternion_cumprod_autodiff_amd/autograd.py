@@ -23,16 +23,30 @@ import torch
 from . import capi
 
 
+_STATUS_MODES = ("deferred", "sync")
+
+
 class QuatCumprodFunction(torch.autograd.Function):
-    """cum = quat_cumprod(q, init); backward = the recompute-based VJP."""
+    """cum = quat_cumprod(q, init); backward = the recompute-based VJP.
+
+    Device-side conditions (a cross-block wait at its spin limit, a zero
+    prefix product in the backward) are read from the workspace's status word
+    without stalling the stream: each call queues an asynchronous copy of the
+    word, and the next call through this node raises QuatCumprodStatusError
+    for any copy that has completed with a bit set (capi.check_status() waits
+    for all of them: a synchronisation point).  status_check="sync" waits
+    after the backward instead and raises from it."""
 
     @staticmethod
-    def forward(ctx, q: torch.Tensor, init: torch.Tensor, save_boundary_state: bool):
+    def forward(ctx, q: torch.Tensor, init: torch.Tensor, save_boundary_state: bool, status_check: str):
+        capi.default_workspace.poll()
         q = q.contiguous()
         init = init.contiguous()
         ckpt = capi.new_ckpt(q) if save_boundary_state else None
         cum = capi.quat_cumprod_fwd(q, init, ckpt=ckpt)
+        capi.default_workspace.watch(q.device, None, "quat_cumprod forward")
         ctx.save_for_backward(q, init, ckpt)
+        ctx.status_check = status_check
         return cum
 
     @staticmethod
@@ -40,26 +54,39 @@ class QuatCumprodFunction(torch.autograd.Function):
         q, init, ckpt = ctx.saved_tensors
         want_dq, want_dinit = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if not (want_dq or want_dinit):
-            return None, None, None
+            return None, None, None, None
+        capi.default_workspace.poll()
         d_q, d_init = capi.quat_cumprod_bwd(q, init, d_cum.contiguous(), ckpt,
                                             want_dq=want_dq, want_dinit=want_dinit)
-        return d_q, d_init, None
+        capi.default_workspace.watch(q.device, None, "quat_cumprod backward")
+        if ctx.status_check == "sync":
+            capi.default_workspace.poll(wait=True)
+        return d_q, d_init, None, None
 
 
-def quat_cumprod(q: torch.Tensor, init: torch.Tensor, *, save_boundary_state: bool = True) -> torch.Tensor:
+def quat_cumprod(q: torch.Tensor, init: torch.Tensor, *, save_boundary_state: bool = True,
+                 status_check: str = "deferred") -> torch.Tensor:
     """cum[t] = q_t (x) cum[t-1] with cum[-1] = init, differentiable in q and init.
 
     q: [b, s, h, j, 4], init: [b, h, j, 4], float32 or bfloat16, on the GPU.
+    status_check: "deferred" (default) raises a device-side failure at the
+    next call or at capi.check_status(); "sync" raises it from the backward.
     """
+    if status_check not in _STATUS_MODES:
+        raise ValueError(f"status_check must be one of {_STATUS_MODES}")
     if torch.is_grad_enabled() and (q.requires_grad or init.requires_grad):
-        return QuatCumprodFunction.apply(q, init, save_boundary_state)
-    return capi.quat_cumprod_fwd(q.contiguous(), init.contiguous())
+        return QuatCumprodFunction.apply(q, init, save_boundary_state, status_check)
+    capi.default_workspace.poll()
+    cum = capi.quat_cumprod_fwd(q.contiguous(), init.contiguous())
+    capi.default_workspace.watch(q.device, None, "quat_cumprod forward")
+    return cum
 
 
-def quat_cumprod_with_final(q: torch.Tensor, init: torch.Tensor, *, save_boundary_state: bool = True):
+def quat_cumprod_with_final(q: torch.Tensor, init: torch.Tensor, *, save_boundary_state: bool = True,
+                            status_check: str = "deferred"):
     """(cum, final_carry) with final_carry = cum[:, -1], a view whose gradient
     autograd folds into the last position of cum's gradient."""
-    cum = quat_cumprod(q, init, save_boundary_state=save_boundary_state)
+    cum = quat_cumprod(q, init, save_boundary_state=save_boundary_state, status_check=status_check)
     return cum, cum[:, -1]
 
 
@@ -111,9 +138,15 @@ class ScanFunction(torch.autograd.Function):
         d_ys = d_ys.contiguous()
         if ctx.k > 0:
             # The VJP overwrites the snapshots; a second backward through the
-            # same graph (retain_graph) starts again from init.
+            # same graph (retain_graph) starts again from init.  A schedule
+            # record the device refuses stops its column and sets `status`,
+            # watched like the scan's workspace status (raised at the next
+            # call or at capi.check_status()).
+            capi.default_workspace.poll()
+            status = torch.zeros(1, dtype=torch.int32, device=xs.device)
             d_xs, d_init = capi.scan_bwd_checkpointed(ctx.body, xs, init, d_ys, ctx.sched, saved,
-                                                      after_forward=ctx.fresh_snapshots)
+                                                      after_forward=ctx.fresh_snapshots, status=status)
+            capi.default_workspace.watch(xs.device, None, "scan checkpointed backward", word=status)
             ctx.fresh_snapshots = False
         else:
             d_xs, d_init = capi.scan_bwd_trajectory(ctx.body, xs, init, saved, d_ys)

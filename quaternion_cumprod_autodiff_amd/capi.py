@@ -35,6 +35,8 @@ EXPORTS = (
     "qc_scan_bwd_trajectory", "qc_scan_bwd_checkpointed",
     # include/gdn2.h
     "gdn2_boundary_bytes", "gdn2_scratch_bytes", "gdn2_fwd", "gdn2_bwd",
+    # include/qc_bench.h
+    "qc_stream_copy",
 )
 
 
@@ -119,6 +121,8 @@ def load(path: str | None = None):
         lib.gdn2_fwd.restype = ctypes.c_int
         lib.gdn2_bwd.argtypes = [vp] * 17 + [sz] + [i64] * 6 + [vp]
         lib.gdn2_bwd.restype = ctypes.c_int
+        lib.qc_stream_copy.argtypes = [vp, vp, sz, i32, vp]
+        lib.qc_stream_copy.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -187,28 +191,69 @@ def ckpt_bytes(b, s, h, j, dtype=torch.float32) -> int:
     return int(load().quat_cumprod_ckpt_bytes(b, s, h, j, _DTYPES[dtype]))
 
 
-class Workspace:
-    """A zero-initialised device workspace that grows on demand (per device)."""
+class QuatCumprodStatusError(RuntimeError):
+    """A device-side condition reported through a workspace's status word:
+    QC_STATUS_TIMEOUT (1, a cross-block wait hit its spin limit: results of
+    the call are invalid) or QC_STATUS_ZERO (2, a backward met a prefix
+    product that is exactly zero: its gradients are not finite)."""
 
-    def __init__(self):
-        self._buf: dict[int, torch.Tensor] = {}
+    def __init__(self, bits: int, where: str):
+        names = [n for b, n in ((1, "QC_STATUS_TIMEOUT"), (2, "QC_STATUS_ZERO")) if bits & b]
+        super().__init__(f"{where}: device status {bits} ({', '.join(names) or 'unknown bits'})")
+        self.bits = bits
+
+
+# Byte offset of the sticky status word in a workspace (header word 2).
+_STATUS_OFFSET = 8
+
+
+class Workspace:
+    """A zero-initialised device workspace that grows on demand.
+
+    ``per_stream=False`` (an explicitly created workspace): one buffer per
+    device; calls that share it must be ordered, as the C header requires.
+    ``per_stream=True`` (the default workspace): one buffer per (device,
+    stream), so calls on different streams never share carry slots or the
+    leaves-only boundary scratch.  A buffer is allocated while its stream is
+    current, so the caching allocator hands it (and, after growth, the old
+    one) only to work ordered on that stream.
+
+    Status: after a call, ``watch`` copies the buffer's status word into
+    pinned host memory on the call's stream (no synchronisation); ``poll``
+    raises QuatCumprodStatusError once such a copy has completed with a set
+    bit (``wait=True`` waits for every pending copy first) and clears the
+    word."""
+
+    def __init__(self, per_stream: bool = False):
+        self.per_stream = per_stream
+        self._buf: dict = {}
+        self._pending: list = []
+
+    def _key(self, device: torch.device, stream):
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        if not self.per_stream:
+            return idx
+        st = stream if stream is not None else torch.cuda.current_stream(idx)
+        return (idx, int(st.cuda_stream))
 
     def get(self, nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
-        idx = device.index if device.index is not None else torch.cuda.current_device()
-        buf = self._buf.get(idx)
+        key = self._key(device, stream)
+        buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
             nbytes = max(nbytes, 1 << 20)
-            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-            _check(load().quat_cumprod_workspace_init(_ptr(buf), buf.numel(), _stream(stream)),
+            st = stream if stream is not None else torch.cuda.current_stream(device)
+            with torch.cuda.stream(st):
+                buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            _check(load().quat_cumprod_workspace_init(_ptr(buf), buf.numel(), _stream(st)),
                    "quat_cumprod_workspace_init")
-            self._buf[idx] = buf
+            self._buf[key] = buf
         return buf
 
     def status(self, device: torch.device, stream=None, clear: bool = True) -> int:
-        """Sticky status bits of this device's workspace since the last clear
-        (0 = normal; QC_STATUS_TIMEOUT = 1, QC_STATUS_ZERO = 2, see the C header)."""
-        idx = device.index if device.index is not None else torch.cuda.current_device()
-        buf = self._buf.get(idx)
+        """Sticky status bits of this workspace (for ``stream`` when per
+        stream) since the last clear; synchronises the stream.  0 = normal;
+        QC_STATUS_TIMEOUT = 1, QC_STATUS_ZERO = 2 (see the C header)."""
+        buf = self._buf.get(self._key(device, stream))
         if buf is None:
             return 0
         out = ctypes.c_int32(0)
@@ -216,8 +261,63 @@ class Workspace:
                                                     ctypes.byref(out)), "quat_cumprod_workspace_status")
         return int(out.value)
 
+    def watch(self, device: torch.device, stream, where: str, word: torch.Tensor | None = None):
+        """Queue an asynchronous copy of the status word after the work just
+        enqueued on ``stream`` with this workspace.  ``word`` (one device
+        int32) watches another status word instead, e.g. the generic scan's;
+        a set word is cleared when it is reported."""
+        st = stream if stream is not None else torch.cuda.current_stream(device)
+        if word is None:
+            buf = self._buf.get(self._key(device, st))
+            if buf is None:
+                return
+            src = buf[_STATUS_OFFSET:_STATUS_OFFSET + 4].view(torch.int32)
 
-default_workspace = Workspace()
+            def clear():
+                self.status(device, st, clear=True)
+        else:
+            src = word.view(torch.int32).reshape(1)
+
+            def clear():
+                with torch.cuda.stream(st):
+                    src.zero_()
+                st.synchronize()
+        host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+        with torch.cuda.stream(st):
+            host.copy_(src, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(st)
+        self._pending.append((ev, host, clear, st, where))
+
+    def poll(self, wait: bool = False):
+        """Raise for a completed status copy that shows a set bit."""
+        keep, bad = [], None
+        for item in self._pending:
+            ev, host, clear, st, where = item
+            if wait:
+                ev.synchronize()
+            elif not ev.query():
+                keep.append(item)
+                continue
+            bits = int(host.item())
+            if bits and bad is None:
+                bad = (bits, clear, st, where)
+        self._pending = keep
+        if bad is not None:
+            bits, clear, st, where = bad
+            clear()
+            self._pending = [it for it in self._pending if it[3] != st]
+            raise QuatCumprodStatusError(bits, where)
+
+
+default_workspace = Workspace(per_stream=True)
+
+
+def check_status(wait: bool = True):
+    """Raise QuatCumprodStatusError if any watched call on the default
+    workspace reported a device-side condition (``wait``: first wait for the
+    pending status copies; a synchronisation point)."""
+    default_workspace.poll(wait=wait)
 
 
 def new_ckpt(q: torch.Tensor) -> torch.Tensor:
@@ -278,6 +378,16 @@ def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
                                     _stream(stream), _options(path))
     _check(rc, "quat_cumprod_bwd")
     return d_q, d_init
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor, *, blocks_per_cu: int = 8, stream=None):
+    """Plain streaming copy of src into dst (include/qc_bench.h): the
+    practical bandwidth ceiling the scan kernels are measured against."""
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(load().qc_stream_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(), int(blocks_per_cu),
+                                 _stream(stream)), "qc_stream_copy")
+    return dst
 
 
 # ---------------------------------------------------------------- generic scan

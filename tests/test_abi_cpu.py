@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol that
-include/quat_cumprod.h, include/qc_scan.h and include/gdn2.h declare, sizes its buffers as documented, and rejects
+include/quat_cumprod.h, include/qc_scan.h, include/gdn2.h and include/qc_bench.h declare, sizes its buffers as documented, and rejects
 bad arguments with the documented codes before any HIP call (so fake device
 pointers are safe here)."""
 import ctypes
@@ -13,7 +13,7 @@ from quaternion_cumprod_autodiff_amd import capi
 from quaternion_cumprod_autodiff_amd.build import LIB_PATH
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("quat_cumprod.h", "qc_scan.h", "gdn2.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("quat_cumprod.h", "qc_scan.h", "gdn2.h", "qc_bench.h")]
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_ALIAS, E_WS, E_HIP, E_OPT = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
@@ -30,7 +30,7 @@ def header_functions():
     names = set()
     for h in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b((?:quat_cumprod|qc_scan|gdn2)_\w+)\s*\(", text))
+        names |= set(re.findall(r"\b((?:quat_cumprod|qc_scan|gdn2|qc_stream)_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -40,7 +40,7 @@ def test_header_declares_what_the_binding_uses():
 
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT ((?:quat_cumprod|qc_scan|gdn2)_\w+)", out))
+    exported = set(re.findall(r"\bT ((?:quat_cumprod|qc_scan|gdn2|qc_stream)_\w+)", out))
     missing = [f for f in header_functions() if f not in exported]
     assert not missing, missing
     for f in header_functions():
@@ -256,3 +256,15 @@ def test_gdn2_node_refuses_host_tensors():
     v = torch.zeros((1, 1, 3, 5))
     with pytest.raises(ValueError, match="GPU only"):
         gated_deltanet2(q, q, v, q, v, q, torch.zeros((1, 1, 4, 5)))
+
+
+def test_stream_copy_validates_before_any_hip_call(lib):
+    a, b = ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 31)
+    assert lib.qc_stream_copy(a, b, 0, 8, None) == OK                 # empty: no-op
+    assert lib.qc_stream_copy(None, b, 64, 8, None) == E_NULL
+    assert lib.qc_stream_copy(a, None, 64, 8, None) == E_NULL
+    assert lib.qc_stream_copy(ctypes.c_void_p((1 << 30) + 4), b, 64, 8, None) == E_ALIGN
+    assert lib.qc_stream_copy(a, b, 60, 8, None) == E_ALIGN
+    assert lib.qc_stream_copy(a, ctypes.c_void_p((1 << 30) + 32), 64, 8, None) == E_ALIAS
+    assert lib.qc_stream_copy(a, b, 64, 0, None) == E_OPT
+    assert lib.qc_stream_copy(a, b, 64, 65, None) == E_OPT

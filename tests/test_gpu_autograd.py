@@ -114,8 +114,71 @@ def test_bf16_gradients():
     inp = make_inputs(2, 400, 4, 4, "drift", "bf16", seed=30)
     q, init = dev(inp.q, "bf16", grad=True), dev(inp.init, "bf16", grad=True)
     wd = dev(inp.d_cum, "bf16")
-    cum = QuatCumprodFunction.apply(q, init, True)
+    cum = QuatCumprodFunction.apply(q, init, True, "deferred")
     (cum.float() * wd.float()).sum().backward()
     r_dq, r_di = oracle.bwd(inp.q64, inp.init64, inp.d_cum64)
     close(f64(q.grad), r_dq, "bf16")
     close(f64(init.grad), r_di, "bf16")
+
+
+@pytest.mark.parametrize("save", [True, False])
+def test_zero_step_raises_from_backward(save):
+    """A zero step makes the backward's prefix products zero: with
+    status_check="sync" the backward itself raises, instead of handing
+    non-finite gradients to the optimiser."""
+    inp = make_inputs(2, 300, 2, 4, "unit", "f32", seed=31)
+    inp.q[1, 120, 0, 3] = 0.0
+    q, init = dev(inp.q, grad=True), dev(inp.init, grad=True)
+    cum = quat_cumprod(q, init, save_boundary_state=save, status_check="sync")
+    with pytest.raises(capi.QuatCumprodStatusError) as ei:
+        cum.sum().backward()
+    assert ei.value.bits == 2
+    capi.check_status()                       # reported once, then cleared
+
+
+def test_zero_step_raises_at_next_call_when_deferred():
+    """Deferred mode (the default): the status copy is queued after the
+    backward, and the next call through the node (or capi.check_status())
+    raises."""
+    inp = make_inputs(1, 200, 2, 2, "unit", "f32", seed=32)
+    inp.q[0, 50, 1, 1] = 0.0
+    q, init = dev(inp.q, grad=True), dev(inp.init, grad=True)
+    quat_cumprod(q, init).sum().backward()
+    torch.cuda.synchronize()
+    with pytest.raises(capi.QuatCumprodStatusError):
+        quat_cumprod(q.detach(), init.detach())
+    capi.check_status()
+    good = make_inputs(1, 200, 2, 2, "unit", "f32", seed=33)
+    q2, i2 = dev(good.q, grad=True), dev(good.init, grad=True)
+    quat_cumprod(q2, i2).sum().backward()
+    capi.check_status()
+
+
+def test_two_streams_share_the_default_workspace():
+    """Two streams run leaves-only forward + backward through the autograd
+    node concurrently on the default workspace: it keeps a buffer per stream,
+    so neither the carry slots nor the re-derived boundary state are shared,
+    and both match the oracle."""
+    shapes = [(4, 2048, 16, 16, "unit", 41), (2, 6000, 4, 8, "drift", 42)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for (b, s, h, j, recipe, seed), st in zip(shapes, streams):
+        inp = make_inputs(b, s, h, j, recipe, "f32", seed=seed)
+        w = np.random.default_rng(seed + 100).standard_normal(inp.q.shape).astype(np.float32)
+        runs.append(dict(inp=inp, w=w, st=st, grads=[]))
+    torch.cuda.synchronize()
+    for it in range(3):
+        for rn in runs:
+            with torch.cuda.stream(rn["st"]):
+                q, init = dev(rn["inp"].q, grad=True), dev(rn["inp"].init, grad=True)
+                (quat_cumprod(q, init, save_boundary_state=False) * dev(rn["w"])).sum().backward()
+                rn["grads"].append((q.grad, init.grad))
+    torch.cuda.synchronize()
+    capi.check_status()
+    for rn in runs:
+        inp = rn["inp"]
+        r_dq, r_di = oracle.bwd(inp.q64, inp.init64, rn["w"].astype(np.float64))
+        print(f"[default workspace, stream of b={inp.b} s={inp.s}]", flush=True)
+        for gq, gi in rn["grads"]:
+            close(f64(gq), r_dq)
+            close(f64(gi), r_di)

@@ -1,10 +1,19 @@
 """Parity of the Gated DeltaNet-2 kernels (include/gdn2.h) with the float64
 oracle (oracle/gdn2.py), through the C ABI (needs an MI355X).
 
-Tolerance: the burn_gdn page's own test bound, max |gpu - ref| <= 3e-3 +
-3e-3 max|ref| per tensor (its assert_close), for the context, the final
-state and all seven cotangents.  The device computes in float32 from float32
-inputs; the oracle takes the same float32 values widened to float64.
+Tolerances, per output tensor (the context, the final state and all seven
+cotangents), both asserted:
+  * the burn_gdn page's own test bound, max |gpu - ref| <= 3e-3 + 3e-3
+    max|ref| (its assert_close);
+  * a float32 bound derived from the arithmetic: normwise
+    max |gpu - ref| / max |ref| <= 1e-5.  Every output is a sum of at most
+    L + D + chunk products per step, in float32 (unit roundoff 2^-24), and
+    the decays (<= 0.82 on these inputs) forget a rounding error after a few
+    steps, so the probabilistic rounding model gives about
+    sqrt(6 (L + D + chunk)) 2^-24 <= 5e-6 at the largest sizes here; the
+    bound leaves a factor 2 above that.
+The device computes in float32 from float32 inputs; the oracle takes the
+same float32 values widened to float64.
 """
 import numpy as np
 import pytest
@@ -18,6 +27,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 NAMES = capi.GDN2_INPUTS
+NORMWISE_TOL = 1e-5
 
 
 def close(label, got, ref):
@@ -25,7 +35,9 @@ def close(label, got, ref):
     scale = float(np.abs(ref).max())
     err = float(np.abs(got - ref).max())
     assert err <= 3e-3 + 3e-3 * scale, f"{label}: max diff {err:.3e} (ref max {scale:.3e})"
-    return err / max(scale, 1e-30)
+    rel = err / max(scale, 1e-30)
+    assert rel <= NORMWISE_TOL, f"{label}: normwise error {rel:.3e} > {NORMWISE_TOL} (ref max {scale:.3e})"
+    return rel
 
 
 def run_case(arrays, chunk, d_ctx, d_state=None):

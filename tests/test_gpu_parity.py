@@ -81,9 +81,9 @@ def check(name, got, ref, dtype, s, report=None):
         assert rel <= BF16_NORMWISE_TOL, f"{name}: normwise rel err {rel:.3e} > {BF16_NORMWISE_TOL}"
 
 
-def compare(inp, path=None, use_ckpt=True):
+def compare(inp, path=None, use_ckpt=True, ref=None):
     cum, d_q, d_init = run_device(inp, path=path, use_ckpt=use_ckpt)
-    r_cum, r_dq, r_di = reference(inp)
+    r_cum, r_dq, r_di = ref if ref is not None else reference(inp)
     rep = {}
     check("cum", to_f64(cum), r_cum, inp.dtype, inp.s, rep)
     check("d_q", to_f64(d_q), r_dq, inp.dtype, inp.s, rep)
@@ -94,12 +94,29 @@ def compare(inp, path=None, use_ckpt=True):
 
 # --------------------------------------------------------------- the configs
 
+_config_cache = {}
+
+
+def config_and_reference(name):
+    """Inputs and oracle results of one named workload, kept for the next
+    test of the same workload only (the full-size arrays are large)."""
+    if name not in _config_cache:
+        _config_cache.clear()
+        inp = make_config(name)
+        _config_cache[name] = (inp, reference(inp))
+    return _config_cache[name]
+
+
+@pytest.mark.parametrize("use_ckpt", [True, False], ids=["saved-state", "leaves-only"])
 @pytest.mark.parametrize("name", list(CONFIGS))
-def test_config_full_parity(name):
+def test_config_full_parity(name, use_ckpt):
     """Every named workload at full size, in the launch configuration the
-    benchmark times (default path, saved boundary state)."""
-    print(f"[config {name}]", flush=True)
-    compare(make_config(name))
+    benchmark times (default path, saved boundary state), and in the
+    page-faithful leaves-only mode (the backward re-derives the boundary
+    state from q)."""
+    print(f"[config {name} {'saved state' if use_ckpt else 'leaves only'}]", flush=True)
+    inp, ref = config_and_reference(name)
+    compare(inp, use_ckpt=use_ckpt, ref=ref)
 
 
 @pytest.mark.parametrize("name", ["tiny", "medium"])
