@@ -159,6 +159,31 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum,
                         void* workspace, size_t workspace_bytes, void* stream,
                         const qc_options* opts);
 
+/* Backward without a caller workspace, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as quat_cumprod_bwd, bit for bit,
+ * except that the workspace is a fixed device array of this library: 64 MiB
+ * per GPU, held by each GPU the library runs on until the process ends.  It
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   status   optional out (NULL = not wanted): a device int32 that receives
+ *            the QC_STATUS_* bits raised by this call (0 = normal), written
+ *            on `stream` after the backward; 4-byte aligned, not overlapping
+ *            any tensor of the call.
+ * Shapes whose quat_cumprod_workspace_bytes exceeds 64 MiB are rejected with
+ * QC_ERR_WORKSPACE before any HIP call (the largest float32 shapes of about
+ * 60 million quaternions with a saved ckpt fit, depending on the column
+ * count).  The first call on a device (with that device current) looks up
+ * the array's device address and zeroes its header on `stream`; make it
+ * outside a graph capture to keep that fill out of the graph.  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU race
+ * (order them on one stream, or synchronise).  Each call leaves the array's
+ * status word cleared. */
+int quat_cumprod_bwd_noalloc(const void* q, const void* init, const void* d_cum,
+                             const void* ckpt, size_t ckpt_bytes,
+                             void* d_q, void* d_init,
+                             int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                             int32_t* status, void* stream);
+
 /* Synchronise `stream`, then read the workspace's device-side status word, a
  * bit mask accumulated over the calls since it was last cleared:
  *   0                   every call completed normally;

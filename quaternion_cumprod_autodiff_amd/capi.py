@@ -29,7 +29,7 @@ EXPORTS = (
     "quat_cumprod_workspace_bytes", "quat_cumprod_ckpt_bytes", "quat_cumprod_workspace_init",
     "quat_cumprod_fwd", "quat_cumprod_bwd", "quat_cumprod_fwd_ex", "quat_cumprod_bwd_ex",
     "quat_cumprod_workspace_status", "quat_cumprod_strerror", "quat_cumprod_last_hip_error",
-    "quat_cumprod_version",
+    "quat_cumprod_version", "quat_cumprod_bwd_noalloc",
     # include/qc_scan.h
     "qc_scan_width", "qc_scan_schedule_capacity", "qc_scan_schedule", "qc_scan_fwd",
     "qc_scan_bwd_trajectory", "qc_scan_bwd_checkpointed",
@@ -92,6 +92,8 @@ def load(path: str | None = None):
         lib.quat_cumprod_fwd_ex.restype = ctypes.c_int
         lib.quat_cumprod_bwd_ex.argtypes = bwd + [ctypes.POINTER(QcOptions)]
         lib.quat_cumprod_bwd_ex.restype = ctypes.c_int
+        lib.quat_cumprod_bwd_noalloc.argtypes = [vp, vp, vp, vp, sz, vp, vp] + dims + [vp, vp]
+        lib.quat_cumprod_bwd_noalloc.restype = ctypes.c_int
         lib.quat_cumprod_workspace_status.argtypes = [vp, sz, vp, i32, ctypes.POINTER(i32)]
         lib.quat_cumprod_workspace_status.restype = ctypes.c_int
         lib.quat_cumprod_strerror.argtypes = [i32]
@@ -388,6 +390,28 @@ def stream_copy(src: torch.Tensor, dst: torch.Tensor, *, blocks_per_cu: int = 8,
     _check(load().qc_stream_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(), int(blocks_per_cu),
                                  _stream(stream)), "qc_stream_copy")
     return dst
+
+
+def quat_cumprod_bwd_noalloc(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
+                             d_q: torch.Tensor | None, d_init: torch.Tensor | None,
+                             ckpt: torch.Tensor | None = None, status: torch.Tensor | None = None, *, stream=None):
+    """VJP of the scan into caller-provided outputs, with the library's fixed
+    device array as workspace (quat_cumprod_bwd_noalloc): nothing is
+    allocated.  ``status`` (optional) is one device int32 that receives the
+    call's status bits."""
+    b, s, h, j = _dims(q)
+    dt = _dtype_code(q)
+    _check_like("init", init, (b, h, j, 4), q.dtype, q.device)
+    _check_like("d_cum", d_cum, q.shape, q.dtype, q.device)
+    _check_like("d_q", d_q, q.shape, q.dtype, q.device)
+    _check_like("d_init", d_init, (b, h, j, 4), q.dtype, q.device)
+    if status is not None and (status.dtype != torch.int32 or status.numel() != 1 or status.device != q.device):
+        raise ValueError("status must be one int32 on q's device")
+    rc = load().quat_cumprod_bwd_noalloc(_ptr(q), _ptr(init), _ptr(d_cum), _ptr(ckpt),
+                                         0 if ckpt is None else ckpt.numel() * ckpt.element_size(),
+                                         _ptr(d_q), _ptr(d_init), b, s, h, j, dt, _ptr(status), _stream(stream))
+    _check(rc, "quat_cumprod_bwd_noalloc")
+    return d_q, d_init
 
 
 # ---------------------------------------------------------------- generic scan

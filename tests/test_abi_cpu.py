@@ -268,3 +268,18 @@ def test_stream_copy_validates_before_any_hip_call(lib):
     assert lib.qc_stream_copy(a, ctypes.c_void_p((1 << 30) + 32), 64, 8, None) == E_ALIAS
     assert lib.qc_stream_copy(a, b, 64, 0, None) == E_OPT
     assert lib.qc_stream_copy(a, b, 64, 65, None) == E_OPT
+
+
+def test_noalloc_validates_before_any_hip_call(lib):
+    """Shapes beyond the fixed 64 MiB array, bad shapes, a misaligned or
+    aliasing status word and a call with no output are all decided on the
+    host (fake device pointers are never dereferenced)."""
+    q, init, d = ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 31), ctypes.c_void_p(1 << 32)
+    dq, di = ctypes.c_void_p(1 << 33), ctypes.c_void_p(1 << 34)
+    f = lib.quat_cumprod_bwd_noalloc
+    assert f(q, init, d, None, 0, dq, di, 64, 4096, 32, 32, 0, None, None) == E_WS     # 288 MiB of workspace
+    assert f(q, init, d, None, 0, dq, di, 0, 8, 1, 1, 0, None, None) == E_SHAPE
+    assert f(q, init, d, None, 0, dq, di, 1, 8, 1, 1, 5, None, None) == E_DTYPE
+    assert f(q, init, d, None, 0, None, None, 1, 8, 1, 1, 0, None, None) == OK          # nothing wanted
+    assert f(q, init, d, None, 0, dq, di, 1, 8, 1, 1, 0, ctypes.c_void_p((1 << 35) + 2), None) == E_ALIGN
+    assert f(q, init, d, None, 0, dq, di, 1, 8, 1, 1, 0, ctypes.c_void_p((1 << 33) + 16), None) == E_ALIAS
