@@ -461,7 +461,7 @@ def scan_bench(args):
 # 64, dense 128) over 8 x 16 heads and 2048 steps; boundary states every 8
 # steps, the chunk whose states the backward keeps in registers (3.7 ms per
 # step against 6.0 at chunk 32).
-GDN2_WORKLOAD = (8, 16, 2048, 64, 128, 8)
+GDN2_WORKLOAD = (8, 16, 2048, 64, 128, 32)
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 

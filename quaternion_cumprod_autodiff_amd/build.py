@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libquatcumprod.so")
-SOURCES = ["qc_kernels.hip", "qc_abi.cpp", "qc_scan.hip", "qc_scan_schedule.cpp", "gdn2.hip", "qc_copy.hip", "qc_noalloc.hip"]
+SOURCES = ["qc_kernels.hip", "qc_abi.cpp", "qc_scan.hip", "qc_scan_schedule.cpp", "gdn2.hip", "gdn2_wy.hip", "qc_copy.hip", "qc_noalloc.hip"]
 ARCH = "gfx950"
 NOISE = "is not a recognized feature for this target"
 

@@ -28,6 +28,7 @@
 // LDS, and with several blocks per head a small kernel adds the blocks'
 // shares in block order.
 #include "gdn2.h"
+#include "gdn2_internal.hpp"
 #include "qc_internal.hpp"
 #include "quat_cumprod.h"
 
@@ -801,6 +802,13 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
     z->state_scratch = (size_t(z->BH * z->scratch_steps * D * z->lm) * sizeof(float) + 255) / 256 * 256;
     z->part_bytes = z->n_blk > 1 ? size_t(z->BH * T * z->n_blk * 4 * L) * sizeof(float) : 0;
     z->scratch_bytes = z->state_scratch + z->part_bytes;
+    if (wy_chunk(chunk)) {
+        // Chunk-WY path: grids of BH * n_chunks and BH * ceil(D / kWyDense)
+        // blocks; the scratch holds the state cotangent entering each chunk.
+        if (z->BH > (int64_t(1) << 31) / z->n_chunks) return QC_ERR_SHAPE;
+        if (z->BH > (int64_t(1) << 31) / ((D + kWyDense - 1) / kWyDense)) return QC_ERR_SHAPE;
+        z->scratch_bytes = size_t(z->BH * z->n_chunks * z->lm * D) * sizeof(float);
+    }
     return QC_OK;
 }
 
@@ -873,13 +881,23 @@ int gdn2_fwd(const float* query, const float* key, const float* value, const flo
                            {query, nl}, {key, nl}, {value, nd}, {erase, nl}, {write, nd}, {log_decay, nl},
                            {initial_state, ns}};
     if (qc::any_overlap(sp, 3, 10)) return QC_ERR_ALIAS;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (qc::wy_chunk(chunk)) {
+        qc::WyArgs w{};
+        w.q = query; w.k = key; w.v = value; w.b = erase; w.w = write; w.g = log_decay; w.s0 = initial_state;
+        w.ctx = context; w.state = final_state; w.bnd = boundary;
+        w.BH = z.BH; w.T = T; w.L = L; w.D = D; w.n_chunks = z.n_chunks;
+        w.n_dt = int((D + qc::kWyDense - 1) / qc::kWyDense);
+        w.scale = 1.0f / sqrtf(float(L));
+        const hipError_t e = qc::launch_wy_forward(int(chunk), z.lm, w, st);
+        return e == hipSuccess ? QC_OK : qc::record_hip_error(e);
+    }
     qc::Gdn2Args a{};
     a.q = query; a.k = key; a.v = value; a.b = erase; a.w = write; a.g = log_decay; a.s0 = initial_state;
     a.ctx = context; a.state = final_state; a.bnd = boundary;
     a.T = T; a.L = L; a.D = D; a.chunk = chunk; a.n_chunks = z.n_chunks; a.scratch_steps = z.scratch_steps;
     a.scale = 1.0f / sqrtf(float(L));
     const unsigned blocks = unsigned(z.BH * ((D + z.cpw - 1) / z.cpw));
-    const hipStream_t st = static_cast<hipStream_t>(stream);
     const bool full = D % z.cpw == 0;
     const hipError_t e = qc::by_latent(z.lm, [&](auto lm) {
         constexpr int kLP = decltype(lm)::value;
@@ -922,6 +940,18 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
                            {query, nl}, {key, nl}, {value, nd}, {erase, nl}, {write, nd}, {log_decay, nl},
                            {boundary, nb}, {d_context, nd}, {d_state, ns}};
     if (qc::any_overlap(sp, 8, 17)) return QC_ERR_ALIAS;
+    if (qc::wy_chunk(chunk)) {
+        qc::WyArgs w{};
+        w.q = query; w.k = key; w.v = value; w.b = erase; w.w = write; w.g = log_decay;
+        w.bnd_in = boundary; w.dctx = d_context; w.dstate = d_state;
+        w.dq = d_query; w.dk = d_key; w.dv = d_value; w.db = d_erase; w.dw = d_write; w.dg = d_log_decay;
+        w.ds0 = d_initial_state; w.dbnd = scratch;
+        w.BH = z.BH; w.T = T; w.L = L; w.D = D; w.n_chunks = z.n_chunks;
+        w.n_dt = int((D + qc::kWyDense - 1) / qc::kWyDense);
+        w.scale = 1.0f / sqrtf(float(L));
+        const hipError_t e = qc::launch_wy_backward(int(chunk), z.lm, w, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? QC_OK : qc::record_hip_error(e);
+    }
     qc::Gdn2Args a{};
     a.q = query; a.k = key; a.v = value; a.b = erase; a.w = write; a.g = log_decay; a.bnd_in = boundary;
     a.dctx = d_context; a.dstate = d_state;

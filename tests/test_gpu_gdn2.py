@@ -166,7 +166,8 @@ def test_bench_workload_sampled_heads():
     dense 128, chunk 8: the register path), checked on sampled heads: heads are independent, so
     the oracle on a head's inputs alone gives that head's exact outputs."""
     import bench
-    B, H, T, L, D, chunk = bench.GDN2_WORKLOAD
+    B, H, T, L, D, _ = bench.GDN2_WORKLOAD
+    chunk = 8
     g = torch.Generator(device=DEV).manual_seed(0)
     ins = [torch.randn((B, H, T, L), device=DEV, generator=g),
            torch.randn((B, H, T, L), device=DEV, generator=g) / L ** 0.5,
@@ -257,3 +258,92 @@ def test_register_chunk_orderings(T, L, D):
     d_ctx = rng.standard_normal((B, H, T, D)).astype(np.float32)
     d_state = rng.standard_normal((B, H, L, D)).astype(np.float32)
     run_case(arrays, 8, d_ctx, d_state)
+
+
+# ----------------------------------------------------------- chunk-WY path
+# Chunks of 16 or 32 steps select the chunk-WY kernels (float32 MFMA); the
+# result does not depend on the chunk, so the page's geometries and data run
+# through them at those chunks too.
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("geom", PAGE, ids=lambda g: "b%dh%dt%dl%dd%dc%d" % g)
+def test_page_geometries_and_data_chunk_wy(geom, chunk):
+    B, H, T, L, D, _ = geom
+    print(f"[gdn2 wy page {geom} chunk {chunk}]", flush=True)
+    arrays = make_gdn2_page_inputs(B, H, T, L, D)
+    rel = run_case(arrays, chunk, arrays["output_weight"])
+    print("  relative max errors:", {k: f"{v:.1e}" for k, v in rel.items()}, flush=True)
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("geom", [(2, 3, 50, 7, 100, 0), (1, 1, 200, 64, 128, 0), (3, 2, 33, 33, 65, 0),
+                                  (1, 2, 40, 1, 1, 0), (2, 1, 17, 16, 100, 0), (1, 3, 128, 64, 64, 0),
+                                  (1, 2, 50, 32, 300, 0), (1, 1, 1, 4, 4, 0), (1, 1, 3, 64, 1024, 0),
+                                  (2, 1, 9, 64, 65, 0), (1, 1, 20, 64, 1, 0), (1, 2, 45, 64, 96, 0),
+                                  (1, 1, 31, 17, 31, 0), (1, 1, 97, 48, 33, 0)],
+                         ids=lambda g: "b%dh%dt%dl%dd%d" % g[:5])
+def test_random_shapes_chunk_wy(geom, chunk):
+    """Ragged last chunks (T not a multiple of the chunk, T below it), latent
+    sizes that pad to 16, 32 or 64 rows, dense sizes that leave the last
+    32-column tile partly empty, and a final-state cotangent."""
+    B, H, T, L, D, _ = geom
+    print(f"[gdn2 wy random {geom[:5]} chunk {chunk}]", flush=True)
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=sum(geom) + chunk)
+    rng = np.random.default_rng(chunk)
+    d_ctx = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    d_state = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    rel = run_case(arrays, chunk, d_ctx, d_state)
+    print("  relative max errors:", {k: f"{v:.1e}" for k, v in rel.items()}, flush=True)
+
+
+def test_chunk_wy_optional_outputs_and_determinism():
+    arrays = make_gdn2_random_inputs(2, 2, 70, 20, 40, seed=15)
+    dev = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
+    d_ctx = torch.randn((2, 2, 70, 40), device=DEV, generator=torch.Generator(device=DEV).manual_seed(6))
+    ctx, state, bnd = capi.gdn2_fwd(*dev, chunk=32)
+    ctx2, state2, none = capi.gdn2_fwd(*dev, chunk=32, want_boundary=False)
+    full = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=32)
+    again = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=32)
+    part = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, chunk=32, want=("log_decay", "initial_state"))
+    zero_state = capi.gdn2_bwd(*dev[:6], bnd, d_ctx, torch.zeros_like(state), chunk=32)
+    torch.cuda.synchronize()
+    assert none is None and torch.equal(ctx, ctx2) and torch.equal(state, state2)
+    for x, y, z in zip(full, again, zero_state):
+        assert torch.equal(x, y) and torch.equal(x, z)
+    for n, x, p in zip(NAMES, full, part):
+        if n in ("log_decay", "initial_state"):
+            assert torch.equal(x, p)
+        else:
+            assert p is None
+
+
+def test_bench_workload_sampled_heads_chunk_wy():
+    """The bench's launch configuration (8 x 16 heads, 2048 steps, latent 64,
+    dense 128, chunk-WY at its chunk), checked on sampled heads against the
+    oracle on that head's inputs alone."""
+    import bench
+    B, H, T, L, D, chunk = bench.GDN2_WORKLOAD
+    assert chunk in (16, 32)
+    g = torch.Generator(device=DEV).manual_seed(0)
+    ins = [torch.randn((B, H, T, L), device=DEV, generator=g),
+           torch.randn((B, H, T, L), device=DEV, generator=g) / L ** 0.5,
+           torch.randn((B, H, T, D), device=DEV, generator=g),
+           torch.rand((B, H, T, L), device=DEV, generator=g),
+           torch.rand((B, H, T, D), device=DEV, generator=g),
+           torch.rand((B, H, T, L), device=DEV, generator=g) - 1.2,
+           torch.randn((B, H, L, D), device=DEV, generator=g)]
+    d_ctx = torch.randn((B, H, T, D), device=DEV, generator=g)
+    ctx, state, bnd = capi.gdn2_fwd(*ins, chunk=chunk)
+    grads = capi.gdn2_bwd(*ins[:6], bnd, d_ctx, chunk=chunk)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H - 1), (5, 2)):
+        print(f"[gdn2 wy bench workload, head ({b}, {h})]", flush=True)
+        host = [x[b:b + 1, h:h + 1].cpu().numpy() for x in ins]
+        dc = d_ctx[b:b + 1, h:h + 1].cpu().numpy()
+        r_ctx, r_state = oracle.gdn2_fwd(*host)
+        r_grads = oracle.gdn2_bwd(*host, dc)
+        rel = {"context": close("context", ctx[b:b + 1, h:h + 1], r_ctx),
+               "state": close("state", state[b:b + 1, h:h + 1], r_state)}
+        for n, gr, r in zip(NAMES, grads, r_grads):
+            rel["d_" + n] = close("d_" + n, gr[b:b + 1, h:h + 1], r)
+        print("  relative max errors:", {k: f"{v:.1e}" for k, v in rel.items()}, flush=True)
