@@ -779,6 +779,7 @@ struct Sizes {
     int64_t BH, T, L, D, chunk, n_chunks, scratch_steps;
     int lm, cpw, n_blk;   // padded rows, columns per wave, backward blocks per head
     size_t state_scratch, part_bytes, scratch_bytes;   // the backward's scratch: states, then block shares
+    size_t bnd_bytes;   // the forward's saved state: boundary states (and, chunk-WY, the factor records)
 };
 
 int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk, Sizes* z) {
@@ -802,12 +803,15 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
     z->state_scratch = (size_t(z->BH * z->scratch_steps * D * z->lm) * sizeof(float) + 255) / 256 * 256;
     z->part_bytes = z->n_blk > 1 ? size_t(z->BH * T * z->n_blk * 4 * L) * sizeof(float) : 0;
     z->scratch_bytes = z->state_scratch + z->part_bytes;
+    z->bnd_bytes = size_t(z->BH * z->n_chunks * D * z->lm) * sizeof(float);
     if (wy_chunk(chunk)) {
         // Chunk-WY path: grids of BH * n_chunks and BH * ceil(D / kWyDense)
         // blocks; the scratch holds the state cotangent entering each chunk.
         if (z->BH > (int64_t(1) << 31) / z->n_chunks) return QC_ERR_SHAPE;
         if (z->BH > (int64_t(1) << 31) / ((D + kWyDense - 1) / kWyDense)) return QC_ERR_SHAPE;
         z->scratch_bytes = size_t(z->BH * z->n_chunks * z->lm * D) * sizeof(float);
+        if (z->BH * z->n_chunks > kMaxElems / wy_record_floats(chunk, z->lm)) return QC_ERR_SHAPE;
+        z->bnd_bytes += size_t(z->BH * z->n_chunks * wy_record_floats(chunk, z->lm)) * sizeof(float);
     }
     return QC_OK;
 }
@@ -850,7 +854,7 @@ extern "C" {
 size_t gdn2_boundary_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk) {
     qc::Sizes z;
     if (qc::check_sizes(B, H, T, L, D, chunk, &z) != QC_OK) return 0;
-    return size_t(z.BH * z.n_chunks * D * z.lm) * sizeof(float);
+    return z.bnd_bytes;
 }
 
 size_t gdn2_scratch_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk) {
@@ -875,7 +879,7 @@ int gdn2_fwd(const float* query, const float* key, const float* value, const flo
         if (p && !qc::aligned4(p)) return QC_ERR_ALIGN;
     const size_t f = sizeof(float);
     const size_t nl = size_t(z.BH * T * L) * f, nd = size_t(z.BH * T * D) * f, ns = size_t(z.BH * L * D) * f;
-    const size_t nb = size_t(z.BH * z.n_chunks * D * z.lm) * f;
+    const size_t nb = z.bnd_bytes;
     if (boundary && (reinterpret_cast<uintptr_t>(boundary) & 15)) return QC_ERR_ALIGN;
     const qc::Span sp[] = {{context, nd}, {final_state, ns}, {boundary, nb},
                            {query, nl}, {key, nl}, {value, nd}, {erase, nl}, {write, nd}, {log_decay, nl},
@@ -886,6 +890,7 @@ int gdn2_fwd(const float* query, const float* key, const float* value, const flo
         qc::WyArgs w{};
         w.q = query; w.k = key; w.v = value; w.b = erase; w.w = write; w.g = log_decay; w.s0 = initial_state;
         w.ctx = context; w.state = final_state; w.bnd = boundary;
+        w.rec = boundary ? boundary + z.BH * z.n_chunks * z.lm * D : nullptr;
         w.BH = z.BH; w.T = T; w.L = L; w.D = D; w.n_chunks = z.n_chunks;
         w.n_dt = int((D + qc::kWyDense - 1) / qc::kWyDense);
         w.scale = 1.0f / sqrtf(float(L));
@@ -921,7 +926,7 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
     if (!d_query && !d_key && !d_value && !d_erase && !d_write && !d_log_decay && !d_initial_state) return QC_OK;
     const size_t f = sizeof(float);
     const size_t nl = size_t(z.BH * T * L) * f, nd = size_t(z.BH * T * D) * f, ns = size_t(z.BH * L * D) * f;
-    const size_t nb = size_t(z.BH * z.n_chunks * D * z.lm) * f;
+    const size_t nb = z.bnd_bytes;
     const size_t nscr = z.scratch_bytes;
     if (!scratch || scratch_bytes < nscr) return QC_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(boundary) & 15) || (reinterpret_cast<uintptr_t>(scratch) & 15)) return QC_ERR_ALIGN;
@@ -944,6 +949,7 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
         qc::WyArgs w{};
         w.q = query; w.k = key; w.v = value; w.b = erase; w.w = write; w.g = log_decay;
         w.bnd_in = boundary; w.dctx = d_context; w.dstate = d_state;
+        w.rec = const_cast<float*>(boundary) + z.BH * z.n_chunks * z.lm * D;
         w.dq = d_query; w.dk = d_key; w.dv = d_value; w.db = d_erase; w.dw = d_write; w.dg = d_log_decay;
         w.ds0 = d_initial_state; w.dbnd = scratch;
         w.BH = z.BH; w.T = T; w.L = L; w.D = D; w.n_chunks = z.n_chunks;

@@ -28,23 +28,31 @@
 // Kernels (256 threads = 4 waves; chunks of CP = 16 or 32 steps; latent
 // rows padded to LP = 16, 32 or 64; every matrix product is 16x16 output
 // tiles of the f32 MFMA, operands read from LDS):
+//   wy_factor_kernel    one block per (head, chunk), all chunks at once: the
+//                       chunk's factors M, Qc, Kt, T, Bq and c_last, written
+//                       as one record per chunk after the boundary states
+//                       (the forward's saved state for the backward).
 //   wy_fwd_kernel       one block per (head, 32 dense columns): the chunks in
-//                       order, the state tile in LDS; saves the state at every
-//                       chunk start (the boundary states).
+//                       order, streaming their records; the state tile stays
+//                       in LDS; saves the state at every chunk start.  Without
+//                       a boundary buffer (no backward to follow) a fused
+//                       variant builds each chunk's factors itself.
 //   wy_bwd_carry_kernel one block per (head, 32 dense columns): the chunks in
 //                       reverse, carrying dS; saves the dS entering every
 //                       chunk from later ones (scratch), and d initial_state.
 //   wy_bwd_grad_kernel  one block per (head, chunk), all chunks at once: from
-//                       the chunk's boundary state and its dS, every
+//                       the chunk's record, boundary state and dS, every
 //                       cotangent of the chunk's steps; the sums over the
 //                       dense axis stay in MFMA accumulators across the
 //                       block's walk over 32-column dense tiles.
-// Each kernel recomputes the chunk's factors (c, Qc, M, Wb, Kt, A, T, Bq)
-// from the inputs with the same code, so all three see the same bits.
+// The sequential kernels deal their blocks so that all dense tiles of a head
+// run on one XCD (block % 8), where they share the head's records in L2.
 // Padded steps (past T in the last chunk) have k = q = b = v = w = g = 0: they
 // leave the state unchanged and get no output.
 #include "gdn2_internal.hpp"
 #include "qc_internal.hpp"
+
+#include <type_traits>
 
 namespace qc {
 namespace {
@@ -53,22 +61,45 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kDN = kWyDense;   // dense columns per tile
-constexpr int kDS = kDN + 4;    // LDS row stride of [rows][kDN] tiles
+constexpr int kDS = kDN + 4;    // LDS row stride of [rows][kDN] tiles read both ways (gradient kernel)
+constexpr int kSeqDS = kDN + 16;  // the same for tiles read only as row-major B operands: conflict-free
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // acc += A(m0 + 0..15, k0 + 0..K) B(k0 + 0..K, n0 + 0..15) on one wave, K a
-// multiple of 4.  `a` points at A(m0, k0) and `b` at B(k0, n0); A(m, k) is
-// a[m * SAM + k * SAK] and B(k, n) is b[k * SBK + n * SBN] (strides select
-// transposes).  Lane l feeds A(l % 16, 4i + l / 16) and B(4i + l / 16, l % 16)
-// to step i and ends with rows 4 (l / 16) + r, column l % 16 in acc[r].
-template <int SAM, int SAK, int SBK, int SBN>
-__device__ __forceinline__ void mma(f32x4& acc, const float* a, const float* b, int K, int lane) {
+// multiple of 4 known at compile time, so that every operand read is issued
+// ahead of the MFMA chain.  `a` points at A(m0, k0) and `b` at B(k0, n0);
+// A(m, k) is a[m * SAM + k * SAK] and B(k, n) is b[k * SBK + n * SBN]
+// (strides select transposes).  Lane l feeds A(l % 16, 4i + l / 16) and
+// B(4i + l / 16, l % 16) to step i and ends with rows 4 (l / 16) + r, column
+// l % 16 in acc[r].
+template <int K, int SAM, int SAK, int SBK, int SBN>
+__device__ __forceinline__ void mma(f32x4& acc, const float* a, const float* b, int lane) {
     const int i = lane & 15, kq = lane >> 4;
     a += i * SAM + kq * SAK;
     b += kq * SBK + i * SBN;
-#pragma unroll 4
-    for (int k = 0; k < K; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k * SAK], b[k * SBK], acc, 0, 0, 0);
+    float av[K / 4], bv[K / 4];
+#pragma unroll
+    for (int k = 0; k < K / 4; ++k) {
+        av[k] = a[4 * k * SAK];
+        bv[k] = b[4 * k * SBK];
+    }
+#pragma unroll
+    for (int k = 0; k < K / 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k], bv[k], acc, 0, 0, 0);
+}
+
+// The same with K = 16 * k16, k16 wave-uniform in 1 .. KMAX / 16 (the
+// triangular ranges of the chunk's lower-triangular factors; KMAX <= 32).
+template <int KMAX, int SAM, int SAK, int SBK, int SBN>
+__device__ __forceinline__ void mma16(f32x4& acc, const float* a, const float* b, int k16, int lane) {
+    static_assert(KMAX == 16 || KMAX == 32, "chunk of 16 or 32 steps");
+    if constexpr (KMAX == 32) {
+        if (k16 == 2) {
+            mma<32, SAM, SAK, SBK, SBN>(acc, a, b, lane);
+            return;
+        }
+    }
+    mma<16, SAM, SAK, SBK, SBN>(acc, a, b, lane);
 }
 
 __device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 4) + r; }
@@ -84,47 +115,94 @@ __device__ __forceinline__ void lower_tile(int j, int& ti, int& tj) {
     tj = j;
 }
 
+// Row stride of the LDS [CP][LP] factor matrices.  Latent rows are read both
+// row-major (A operands) and transposed (A^T operands); with 64 LDS banks a
+// stride of 76 for 64 rows keeps the first conflict-free and the second at
+// two-way, where 68 would make the second four-way.
+constexpr int factor_stride(int lp) { return lp == 64 ? 76 : lp + 4; }
+
 // One chunk's factors in LDS.  Thread (rg, l), rg = tid / LP, owns latent row
-// l of the chunk's steps rg*RPT .. rg*RPT + RPT - 1.
-template <int CP, int LP, bool kKt>
-struct Factors {
-    static constexpr int LS = LP + 4;    // row stride of [CP][LP]
-    static constexpr int CS = CP + 4;    // row stride of [CP][CP]
+// l of the chunk's steps rg*RPT .. rg*RPT + RPT - 1.  kWb, kKt: whether Wb
+// and Kt are held; kScratch: the group sums and the inversion scratch (for
+// building the factors).
+template <int CP, int LP, int LSV, bool kWb, bool kKt, bool kScratch>
+struct alignas(16) FactorsT {
+    static constexpr int LS = LSV;        // row stride of [CP][LP]
+    static constexpr int CS = CP + 4;     // row stride of [CP][CP]
     static constexpr int RG = kThreads / LP;
     static constexpr int RPT = CP / RG;
     static constexpr int NT = CP / 16;
-    float Qc[CP * LS], M[CP * LS], Wb[CP * LS];
-    float Kt[kKt ? CP * LS : 1];
+    static constexpr bool kHasKt = kKt;
+    float Qc[CP * LS], M[CP * LS];
+    float Wb[kWb ? CP * LS : 4];
+    float Kt[kKt ? CP * LS : 4];
     float Tm[CP * CS];     // A, then T = (I + A)^-1 (upper part zero)
     float Bq[CP * CS];     // lower part of Qc Wb^T (upper part zero)
-    float tot[RG * LP];    // per-group sums of log_decay
+    float tot[kScratch ? RG * LP : 4];    // per-group sums of log_decay
     float clast[LP];       // c at the chunk's last (padded) step
-    float tmp[16 * 20];
+    float tmp[kScratch ? 16 * 20 : 4];
 };
+template <int CP, int LP>
+using BuildFactors = FactorsT<CP, LP, factor_stride(LP), true, true, true>;     // factor kernel, fused forward
+template <int CP, int LP>
+using StagedFactors = FactorsT<CP, LP, factor_stride(LP), false, true, false>;  // record-streaming kernels
 
 template <int RPT>
 struct LatIn {
     float q[RPT], k[RPT], b[RPT], g[RPT];
 };
 
-// Latent inputs of chunk rows rg*RPT + i (zero past T or past L).
+// Loads are unconditional, from indices clamped into range; the values are
+// masked only where they are consumed.  A load under a branch makes the
+// compiler wait for every outstanding load where the branch rejoins, and any
+// use of a loaded register (a masking select included) waits for it, either
+// of which would turn the prefetches below into synchronous loads.
+
+// Latent inputs of chunk rows rg*RPT + i (rows past T and columns past L
+// hold clamped copies: mask with latent_ok).
 template <int CP, int LP, int RPT>
 __device__ __forceinline__ void load_latent(const WyArgs& a, int64_t head, int64_t t0, int tid, LatIn<RPT>& in) {
     constexpr int RG = kThreads / LP;
     static_assert(RG * RPT == CP, "rows per thread");
     const int l = tid % LP, rg = tid / LP;
+    const int64_t lc = l < a.L ? l : a.L - 1;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int64_t t = t0 + rg * RPT + i;
-        in.q[i] = in.k[i] = in.b[i] = in.g[i] = 0.f;
-        if (t < a.T && l < a.L) {
-            const int64_t idx = (head * a.T + t) * a.L + l;
-            in.q[i] = a.q[idx];
-            in.k[i] = a.k[idx];
-            in.b[i] = a.b[idx];
-            in.g[i] = a.g[idx];
-        }
+        const int64_t idx = (head * a.T + (t < a.T ? t : a.T - 1)) * a.L + lc;
+        in.q[i] = a.q[idx];
+        in.k[i] = a.k[idx];
+        in.b[i] = a.b[idx];
+        in.g[i] = a.g[idx];
     }
+}
+
+// Whether this thread's latent row i of the chunk at t0 is a real entry.
+template <int CP, int LP, int RPT>
+__device__ __forceinline__ bool latent_ok(const WyArgs& a, int64_t t0, int tid, int i) {
+    return t0 + (tid / LP) * RPT + i < a.T && tid % LP < a.L;
+}
+
+// One or two [B, H, T, D] tensors' values of a chunk's dense tile, element
+// tid + i * kThreads of the [CP][kDN] tile (clamped copies past T or past D:
+// mask with dense_ok).
+template <int CP, bool kTwo>
+__device__ __forceinline__ void load_dense(const float* x, const float* y, const WyArgs& a, int64_t head, int64_t t0,
+                                           int64_t d0, int tid, float* xv, float* yv) {
+    constexpr int EPT = CP * kDN / kThreads;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
+        const int64_t t = t0 + row, d = d0 + n;
+        const int64_t gi = (head * a.T + (t < a.T ? t : a.T - 1)) * a.D + (d < a.D ? d : a.D - 1);
+        xv[i] = x[gi];
+        if constexpr (kTwo) yv[i] = y[gi];
+    }
+}
+
+__device__ __forceinline__ bool dense_ok(const WyArgs& a, int64_t t0, int64_t d0, int tid, int i) {
+    const int idx = tid + i * kThreads;
+    return t0 + idx / kDN < a.T && d0 + idx % kDN < a.D;
 }
 
 // Builds Qc, M, Wb (and Kt), A, Bq in LDS, then T in place of A (wave 0,
@@ -132,12 +210,20 @@ __device__ __forceinline__ void load_latent(const WyArgs& a, int64_t head, int64
 // receive c and 1/c of this thread's rows.  Starts and ends reading nothing
 // that the caller may still be writing: the first barrier comes after the
 // group sums are stored.
-template <int CP, int LP, bool kKt, int RPT>
-__device__ void make_factors(Factors<CP, LP, kKt>& f, const LatIn<RPT>& in, int tid, float* e, float* ie) {
-    using F = Factors<CP, LP, kKt>;
+template <int CP, int LP, class F, int RPT>
+__device__ void make_factors(F& f, const LatIn<RPT>& raw, const WyArgs& a, int64_t t0, int tid, float* e, float* ie) {
     constexpr int LS = F::LS, CS = F::CS, RG = F::RG, NT = F::NT;
     const int lane = tid & 63, wave = tid >> 6;
     const int l = tid % LP, rg = tid / LP;
+    LatIn<RPT> in;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const bool ok = latent_ok<CP, LP, RPT>(a, t0, tid, i);
+        in.q[i] = ok ? raw.q[i] : 0.f;
+        in.k[i] = ok ? raw.k[i] : 0.f;
+        in.b[i] = ok ? raw.b[i] : 0.f;
+        in.g[i] = ok ? raw.g[i] : 0.f;
+    }
 
     float G[RPT];
     float run = 0.f;
@@ -164,7 +250,7 @@ __device__ void make_factors(Factors<CP, LP, kKt>& f, const LatIn<RPT>& in, int 
         f.Qc[row * LS + l] = in.q[i] * e[i];
         f.M[row * LS + l] = (in.b[i] * in.k[i]) * e[i];
         f.Wb[row * LS + l] = in.k[i] * ie[i];
-        if constexpr (kKt) f.Kt[row * LS + l] = in.k[i] * __expf(Gl - Gt);
+        if constexpr (F::kHasKt) f.Kt[row * LS + l] = in.k[i] * __expf(Gl - Gt);
     }
     if (rg == 0) f.clast[l] = __expf(Gl);
     __syncthreads();
@@ -176,7 +262,7 @@ __device__ void make_factors(Factors<CP, LP, kKt>& f, const LatIn<RPT>& in, int 
         int ti, tj;
         lower_tile(isA ? job - NJ : job, ti, tj);
         f32x4 acc = zero4();
-        mma<LS, 1, 1, LS>(acc, (isA ? f.M : f.Qc) + ti * 16 * LS, f.Wb + tj * 16 * LS, LP, lane);
+        mma<LP, LS, 1, 1, LS>(acc, (isA ? f.M : f.Qc) + ti * 16 * LS, f.Wb + tj * 16 * LS, lane);
         float* dst = (isA ? f.Tm : f.Bq) + ti * 16 * CS + tj * 16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -199,37 +285,121 @@ __device__ void make_factors(Factors<CP, LP, kKt>& f, const LatIn<RPT>& in, int 
     if (wave == 0) {
         const int blk = lane >> 4, j = lane & 15;
         if (blk < NT) {
+            // Column-oriented (right-looking): once x[k] is final it updates
+            // every later row, so the dependent chain is 16 steps long.
             float x[16];
             const float* arow = f.Tm + blk * 16 * CS + blk * 16;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = i == j ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = i == j ? 1.f : 0.f;
 #pragma unroll
-                for (int kk = 0; kk < i; ++kk) s -= arow[i * CS + kk] * x[kk];
-                x[i] = s;
-            }
+            for (int kk = 0; kk < 15; ++kk)
+#pragma unroll
+                for (int i = kk + 1; i < 16; ++i) x[i] -= arow[i * CS + kk] * x[kk];
             float* trow = f.Tm + blk * 16 * CS + blk * 16;
 #pragma unroll
             for (int i = 0; i < 16; ++i) trow[i * CS + j] = x[i];
         }
         if constexpr (NT == 2) {
             f32x4 acc = zero4();
-            mma<CS, 1, CS, 1>(acc, f.Tm + 16 * CS, f.Tm, 16, lane);             // A10 T00
+            mma<16, CS, 1, CS, 1>(acc, f.Tm + 16 * CS, f.Tm, lane);             // A10 T00
 #pragma unroll
             for (int r = 0; r < 4; ++r) f.tmp[acc_row(lane, r) * 20 + acc_col(lane)] = acc[r];
             f32x4 acc2 = zero4();
-            mma<CS, 1, 20, 1>(acc2, f.Tm + 16 * CS + 16, f.tmp, 16, lane);     // T11 (A10 T00)
+            mma<16, CS, 1, 20, 1>(acc2, f.Tm + 16 * CS + 16, f.tmp, lane);     // T11 (A10 T00)
 #pragma unroll
             for (int r = 0; r < 4; ++r) f.Tm[(16 + acc_row(lane, r)) * CS + acc_col(lane)] = -acc2[r];
         }
     }
 }
 
-// --------------------------------------------------------------- forward
+// ---------------------------------------------------------- factor records
+//
+// One chunk's record, floats: M, Qc, Kt [CP][LP] (row = step, unpadded),
+// T, Bq [CP][CP], c_last [LP]; kSize rounds it up to 256 bytes.
+template <int CP, int LP>
+struct Rec {
+    static constexpr int kM = 0, kQc = CP * LP, kKt = 2 * CP * LP, kT = 3 * CP * LP;
+    static constexpr int kBq = kT + CP * CP, kCl = kBq + CP * CP, kUsed = kCl + LP;
+    static constexpr int kSize = wy_record_floats(CP, LP);
+    static constexpr int kN4 = kUsed / 4;                          // float4 per record
+    static constexpr int kPer = (kN4 + kThreads - 1) / kThreads;   // float4 per thread
+    static_assert(kUsed <= kSize && LP % 4 == 0 && CP % 4 == 0, "record layout");
+};
+
+// LDS address of record element e (a multiple of 4: a float4 never spans two
+// rows or two sections).
+template <int CP, int LP, class F>
+__device__ __forceinline__ float* rec_lds(F& f, int e) {
+    using R = Rec<CP, LP>;
+    constexpr int LS = F::LS, CS = F::CS;
+    if (e < R::kQc) return f.M + (e / LP) * LS + e % LP;
+    if (e < R::kKt) return f.Qc + ((e - R::kQc) / LP) * LS + (e - R::kQc) % LP;
+    if (e < R::kT) return f.Kt + ((e - R::kKt) / LP) * LS + (e - R::kKt) % LP;
+    if (e < R::kBq) return f.Tm + ((e - R::kT) / CP) * CS + (e - R::kT) % CP;
+    if (e < R::kCl) return f.Bq + ((e - R::kBq) / CP) * CS + (e - R::kBq) % CP;
+    return f.clast + (e - R::kCl);
+}
 
 template <int CP, int LP>
+struct RecRegs {
+    f32x4 v[Rec<CP, LP>::kPer];
+};
+
+template <int CP, int LP>
+__device__ __forceinline__ void load_rec(RecRegs<CP, LP>& r, const float* rec, int tid) {
+    using R = Rec<CP, LP>;
+#pragma unroll
+    for (int i = 0; i < R::kPer; ++i) {
+        const int j = tid + i * kThreads;
+        r.v[i] = reinterpret_cast<const f32x4*>(rec)[j < R::kN4 ? j : R::kN4 - 1];   // unconditional (see load_latent)
+    }
+}
+
+template <int CP, int LP, class F>
+__device__ __forceinline__ void stage_rec(F& f, const RecRegs<CP, LP>& r, int tid) {
+    using R = Rec<CP, LP>;
+#pragma unroll
+    for (int i = 0; i < R::kPer; ++i) {
+        const int j = tid + i * kThreads;
+        if (j < R::kN4) *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, 4 * j)) = r.v[i];
+    }
+}
+
+template <int CP, int LP>
+__global__ void __launch_bounds__(kThreads, 2) wy_factor_kernel(WyArgs a) {
+    using F = BuildFactors<CP, LP>;
+    using R = Rec<CP, LP>;
+    __shared__ F f;
+    const int tid = threadIdx.x;
+    const int64_t head = blockIdx.x / a.n_chunks, c = blockIdx.x % a.n_chunks;
+    LatIn<F::RPT> in;
+    load_latent<CP, LP>(a, head, c * CP, tid, in);
+    float e[F::RPT], ie[F::RPT];
+    make_factors<CP, LP>(f, in, a, c * CP, tid, e, ie);
+    __syncthreads();
+    f32x4* rec = reinterpret_cast<f32x4*>(a.rec + (head * a.n_chunks + c) * R::kSize);
+    for (int j = tid; j < R::kN4; j += kThreads) rec[j] = *reinterpret_cast<const f32x4*>(rec_lds<CP, LP>(f, 4 * j));
+}
+
+// Blocks of the sequential kernels: block b runs dense tile dt of head
+// (b / 8 / n_dt) * 8 + b % 8, so a head's tiles share one XCD (b % 8) and its
+// records in that XCD's L2.  Returns false for the grid's padding blocks.
+__device__ __forceinline__ bool seq_block(const WyArgs& a, int64_t* head, int64_t* d0) {
+    const int64_t xcd = blockIdx.x % 8, rest = blockIdx.x / 8;
+    *d0 = (rest % a.n_dt) * kDN;
+    *head = (rest / a.n_dt) * 8 + xcd;
+    return *head < a.BH;
+}
+
+// --------------------------------------------------------------- forward
+
+// kRec: stream the chunks' records (written by wy_factor_kernel); else build
+// each chunk's factors here (no boundary buffer, so nowhere to keep them).
+template <int CP, int LP, bool kRec>
 __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
-    using F = Factors<CP, LP, true>;
+    using F = std::conditional_t<kRec, StagedFactors<CP, LP>, BuildFactors<CP, LP>>;
+    using R = Rec<CP, LP>;
+    constexpr int kDS = kSeqDS;   // dense tiles here are read only as row-major B operands
     constexpr int LS = F::LS, CS = F::CS, NT = F::NT, RPT = F::RPT;
     constexpr int NS = (LP / 16) * (kDN / 16);        // state tiles
     constexpr int NSW = (NS + 3) / 4;                   // state tiles per wave
@@ -237,8 +407,8 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
     __shared__ float sX[CP * kDS], sU[CP * kDS], sS[LP * kDS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t head = blockIdx.x / a.n_dt;
-    const int64_t d0 = int64_t(blockIdx.x % a.n_dt) * kDN;
+    int64_t head, d0;
+    if (!seq_block(a, &head, &d0)) return;
     const int64_t nb = a.n_chunks;
 
     for (int idx = tid; idx < LP * kDN; idx += kThreads) {
@@ -251,38 +421,47 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
         sS[l * kDS + n] = v;
     }
 
+    // The next chunk's inputs are loaded into registers while this chunk
+    // computes (barriers wait for LDS traffic only, not for these loads).
+    constexpr int EPT = CP * kDN / kThreads;
+    LatIn<kRec ? 1 : RPT> in;
+    RecRegs<CP, LP> rr;
+    float vv[EPT], ww[EPT];
+    if constexpr (kRec)
+        load_rec<CP, LP>(rr, a.rec + head * nb * R::kSize, tid);
+    else
+        load_latent<CP, LP>(a, head, 0, tid, in);
+    load_dense<CP, true>(a.v, a.w, a, head, 0, d0, tid, vv, ww);
     for (int64_t c = 0; c < nb; ++c) {
         const int64_t t0 = c * CP;
-        LatIn<RPT> in;
-        load_latent<CP, LP>(a, head, t0, tid, in);
-        constexpr int EPT = CP * kDN / kThreads;
-        float wv[EPT];
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-            const int64_t t = t0 + row;
-            wv[i] = 0.f;
-            if (t < a.T && d0 + n < a.D) {
-                const int64_t gi = (head * a.T + t) * a.D + d0 + n;
-                wv[i] = a.w[gi] * a.v[gi];
-            }
-        }
-        float e[RPT], ie[RPT];
-        // sX (this chunk's w.v) is free: its last reader (the previous U) is
-        // behind the previous chunk's barriers, and make_factors' first
-        // barrier orders this store before the rhs below.
+        // sX (this chunk's w.v) and the factors are free: their last readers
+        // are behind the previous chunk's final barrier.
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int idx = tid + i * kThreads;
-            sX[(idx / kDN) * kDS + idx % kDN] = wv[i];
+            sX[(idx / kDN) * kDS + idx % kDN] = dense_ok(a, t0, d0, tid, i) ? ww[i] * vv[i] : 0.f;
         }
-        make_factors<CP, LP, true>(f, in, tid, e, ie);
+        // Prefetches are unconditional: the last chunk reloads its own record
+        // (and dense loads past T are clamped and masked); a branch around
+        // them would make the compiler wait for them where it rejoins.
+        const int64_t cn = c + 1 < nb ? c + 1 : c;
+        if constexpr (kRec) {
+            stage_rec<CP, LP>(f, rr, tid);
+            __syncthreads();
+            load_rec<CP, LP>(rr, a.rec + (head * nb + cn) * R::kSize, tid);
+        } else {
+            float e[RPT], ie[RPT];
+            make_factors<CP, LP>(f, in, a, t0, tid, e, ie);   // its barriers also order the stores above
+            load_latent<CP, LP>(a, head, cn * CP, tid, in);
+        }
+        load_dense<CP, true>(a.v, a.w, a, head, cn * CP, d0, tid, vv, ww);
 
-        // rhs = w.v - M S0 (in place in sX), while wave 0 finishes T.
+        // rhs = w.v - M S0 (in place in sX); in the fused variant wave 0 may
+        // still be finishing T.
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
             f32x4 acc = zero4();
-            mma<LS, 1, kDS, 1>(acc, f.M + ti * 16 * LS, sS + tj * 16, LP, lane);
+            mma<LP, LS, 1, kDS, 1>(acc, f.M + ti * 16 * LS, sS + tj * 16, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float* p = sX + (ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane);
@@ -294,7 +473,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
             f32x4 acc = zero4();
-            mma<CS, 1, kDS, 1>(acc, f.Tm + ti * 16 * CS, sX + tj * 16, (ti + 1) * 16, lane);
+            mma16<CP, CS, 1, kDS, 1>(acc, f.Tm + ti * 16 * CS, sX + tj * 16, ti + 1, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sU[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
         }
@@ -303,8 +482,8 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
             f32x4 acc = zero4();
-            mma<LS, 1, kDS, 1>(acc, f.Qc + ti * 16 * LS, sS + tj * 16, LP, lane);
-            mma<CS, 1, kDS, 1>(acc, f.Bq + ti * 16 * CS, sU + tj * 16, (ti + 1) * 16, lane);
+            mma<LP, LS, 1, kDS, 1>(acc, f.Qc + ti * 16 * LS, sS + tj * 16, lane);
+            mma16<CP, CS, 1, kDS, 1>(acc, f.Bq + ti * 16 * CS, sU + tj * 16, ti + 1, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t t = t0 + ti * 16 + acc_row(lane, r), d = d0 + tj * 16 + acc_col(lane);
@@ -324,7 +503,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
                     const int l = ti * 16 + acc_row(lane, r);
                     acc[r] = f.clast[l] * sS[l * kDS + tj * 16 + acc_col(lane)];
                 }
-                mma<1, LS, kDS, 1>(acc, f.Kt + ti * 16, sU + tj * 16, CP, lane);
+                mma<CP, 1, LS, kDS, 1>(acc, f.Kt + ti * 16, sU + tj * 16, lane);
                 snew[s] = acc;
             }
         }
@@ -355,16 +534,18 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
 
 template <int CP, int LP>
 __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
-    using F = Factors<CP, LP, false>;
-    constexpr int LS = F::LS, CS = F::CS, NT = F::NT, RPT = F::RPT;
+    using F = StagedFactors<CP, LP>;
+    using R = Rec<CP, LP>;
+    constexpr int kDS = kSeqDS;   // dense tiles here are read only as row-major B operands
+    constexpr int LS = F::LS, CS = F::CS, NT = F::NT;
     constexpr int NS = (LP / 16) * (kDN / 16);
     constexpr int NSW = (NS + 3) / 4;
     __shared__ F f;
     __shared__ float sX[CP * kDS], sU[CP * kDS], sR[CP * kDS], sS[LP * kDS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t head = blockIdx.x / a.n_dt;
-    const int64_t d0 = int64_t(blockIdx.x % a.n_dt) * kDN;
+    int64_t head, d0;
+    if (!seq_block(a, &head, &d0)) return;
     const int64_t nb = a.n_chunks;
     const float s = a.scale;
 
@@ -378,35 +559,29 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
         sS[l * kDS + n] = v;
     }
 
+    constexpr int EPT = CP * kDN / kThreads;
+    RecRegs<CP, LP> rr;
+    float oo[EPT];
+    load_rec<CP, LP>(rr, a.rec + (head * nb + nb - 1) * R::kSize, tid);
+    load_dense<CP, false>(a.dctx, nullptr, a, head, (nb - 1) * CP, d0, tid, oo, nullptr);
     for (int64_t c = nb - 1; c >= 0; --c) {
         const int64_t t0 = c * CP;
-        LatIn<RPT> in;
-        load_latent<CP, LP>(a, head, t0, tid, in);
-        constexpr int EPT = CP * kDN / kThreads;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-            const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-            const int64_t t = t0 + row;
-            float v = 0.f;
-            if (t < a.T && d0 + n < a.D) v = a.dctx[(head * a.T + t) * a.D + d0 + n];
-            sX[row * kDS + n] = v;
+            const int idx = tid + i * kThreads;
+            sX[(idx / kDN) * kDS + idx % kDN] = dense_ok(a, t0, d0, tid, i) ? oo[i] : 0.f;
         }
-        float e[RPT], ie[RPT];
-        make_factors<CP, LP, false>(f, in, tid, e, ie);
-
-        // dSc = diag(c_last) dS, in place (sS was last read before the previous
-        // chunk's final barrier); the barrier after it also publishes T.
-        for (int idx = tid; idx < LP * kDN; idx += kThreads) {
-            const int l = idx / kDN, n = idx % kDN;
-            sS[l * kDS + n] *= f.clast[l];
-        }
+        stage_rec<CP, LP>(f, rr, tid);
         __syncthreads();
-        // dU = Bq^T dO / sqrt(L) + Wb dSc.
+        const int64_t cn = c > 0 ? c - 1 : c;   // unconditional prefetch (see the forward)
+        load_rec<CP, LP>(rr, a.rec + (head * nb + cn) * R::kSize, tid);
+        load_dense<CP, false>(a.dctx, nullptr, a, head, cn * CP, d0, tid, oo, nullptr);
+        // dU = Bq^T dO / sqrt(L) + Wb dSc, with Wb dSc = Kt dS (Kt = Wb diag(c_last)).
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
             f32x4 a1 = zero4(), a2 = zero4();
-            mma<1, CS, kDS, 1>(a1, f.Bq + ti * 16 * CS + ti * 16, sX + ti * 16 * kDS + tj * 16, CP - ti * 16, lane);
-            mma<LS, 1, kDS, 1>(a2, f.Wb + ti * 16 * LS, sS + tj * 16, LP, lane);
+            mma16<CP, 1, CS, kDS, 1>(a1, f.Bq + ti * 16 * CS + ti * 16, sX + ti * 16 * kDS + tj * 16, NT - ti, lane);
+            mma<LP, LS, 1, kDS, 1>(a2, f.Kt + ti * 16 * LS, sS + tj * 16, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 sU[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = a1[r] * s + a2[r];
@@ -416,12 +591,12 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
             f32x4 acc = zero4();
-            mma<1, CS, kDS, 1>(acc, f.Tm + ti * 16 * CS + ti * 16, sU + ti * 16 * kDS + tj * 16, CP - ti * 16, lane);
+            mma16<CP, 1, CS, kDS, 1>(acc, f.Tm + ti * 16 * CS + ti * 16, sU + ti * 16 * kDS + tj * 16, NT - ti, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sR[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
         }
         __syncthreads();
-        // dS0 = Qc^T dO / sqrt(L) + dSc - M^T drhs.
+        // dS0 = Qc^T dO / sqrt(L) + diag(c_last) dS - M^T drhs.
         f32x4 dnew[NSW];
 #pragma unroll
         for (int sl = 0; sl < NSW; ++sl) {
@@ -429,12 +604,12 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
             if (job < NS) {
                 const int ti = job >> 1, tj = job & 1;
                 f32x4 aq = zero4(), am = zero4();
-                mma<1, LS, kDS, 1>(aq, f.Qc + ti * 16, sX + tj * 16, CP, lane);
-                mma<1, LS, kDS, 1>(am, f.M + ti * 16, sR + tj * 16, CP, lane);
+                mma<CP, 1, LS, kDS, 1>(aq, f.Qc + ti * 16, sX + tj * 16, lane);
+                mma<CP, 1, LS, kDS, 1>(am, f.M + ti * 16, sR + tj * 16, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int l = ti * 16 + acc_row(lane, r);
-                    dnew[sl][r] = sS[l * kDS + tj * 16 + acc_col(lane)] + aq[r] * s - am[r];
+                    dnew[sl][r] = f.clast[l] * sS[l * kDS + tj * 16 + acc_col(lane)] + aq[r] * s - am[r];
                 }
             }
         }
@@ -476,7 +651,7 @@ struct GradTiles {
             float R[CP * kDS];    // drhs
         } t;
         struct {
-            float dQc[CP * (LP + 4)], dM[CP * (LP + 4)], dWb[CP * (LP + 4)], P[CP * (LP + 4)];
+            float dQc[CP * LP], dM[CP * LP], dWb[CP * LP], P[CP * LP];
             float xl[kThreads];
             float red[2 * kThreads];
         } m;
@@ -485,7 +660,7 @@ struct GradTiles {
 
 template <int CP, int LP>
 __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
-    using F = Factors<CP, LP, false>;
+    using F = FactorsT<CP, LP, LP + 4, true, false, true>;   // no Kt: the record's Kt is skipped
     constexpr int LS = F::LS, CS = F::CS, NT = F::NT, RPT = F::RPT, RG = F::RG;
     constexpr int NJ = NT * (NT + 1) / 2;            // lower tiles of a CP x CP matrix
     constexpr int NL = NT * (LP / 16);               // tiles of a CP x LP matrix
@@ -503,8 +678,48 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
 
     LatIn<RPT> in;
     load_latent<CP, LP>(a, head, t0, tid, in);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const bool ok = latent_ok<CP, LP, RPT>(a, t0, tid, i);
+        in.q[i] = ok ? in.q[i] : 0.f;
+        in.k[i] = ok ? in.k[i] : 0.f;
+        in.b[i] = ok ? in.b[i] : 0.f;
+        in.g[i] = ok ? in.g[i] : 0.f;
+    }
+    // The chunk's record (M, Qc, T, Bq, c_last; Kt is not needed here).
+    {
+        using R = Rec<CP, LP>;
+        const f32x4* rec = reinterpret_cast<const f32x4*>(a.rec + (head * nb + c) * R::kSize);
+        for (int j = tid; j < R::kN4; j += kThreads) {
+            const int e4 = 4 * j;
+            if (e4 < R::kKt || e4 >= R::kT) *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, e4)) = rec[j];
+        }
+    }
+    // Wb = k / c, and c, 1/c of this thread's rows, as the factor kernel forms them.
     float e[RPT], ie[RPT];
-    make_factors<CP, LP, false>(f, in, tid, e, ie);
+    {
+        const int l = tid % LP, rg = tid / LP;
+        float G[RPT];
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            run += in.g[i];
+            G[i] = run;
+        }
+        f.tot[rg * LP + l] = run;
+        __syncthreads();
+        float off = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+            if (r < rg) off += f.tot[r * LP + l];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float Gt = off + G[i];
+            e[i] = __expf(Gt);
+            ie[i] = __expf(-Gt);
+            f.Wb[(rg * RPT + i) * LS + l] = in.k[i] * ie[i];
+        }
+    }
 
     f32x4 accC[NCC], accQ[NCL], accM[NCL], accP[NCL];
 #pragma unroll
@@ -517,49 +732,54 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     float xl = 0.f;
 
     constexpr int EPT = CP * kDN / kThreads;
+    // One dense tile's loads, in registers: S0 and dS (this thread's row
+    // l = tid / TPL, EPL columns), v, w and dO (elements tid + i * kThreads of
+    // the [CP][kDN] tile).  The next tile's are issued while this one computes.
+    float sv[EPL], dsv[EPL], vv[EPT], ww[EPT], oo[EPT];
+    const int xl_l = tid / TPL, xl_n0 = (tid % TPL) * EPL;
+    auto load_tile = [&](int64_t d0) {   // raw (clamped) values, masked where consumed
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int64_t d = d0 + xl_n0 + i;
+            const int64_t gi = ((head * nb + c) * LP + (xl_l < a.L ? xl_l : a.L - 1)) * a.D + (d < a.D ? d : a.D - 1);
+            sv[i] = a.bnd_in[gi];
+            dsv[i] = a.dbnd[gi];
+        }
+        load_dense<CP, true>(a.v, a.w, a, head, t0, d0, tid, vv, ww);
+        load_dense<CP, false>(a.dctx, nullptr, a, head, t0, d0, tid, oo, nullptr);
+    };
+    load_tile(0);
+    __syncthreads();   // the record and Wb are in LDS
     for (int dt = 0; dt < a.n_dt; ++dt) {
         const int64_t d0 = int64_t(dt) * kDN;
-        // Loads: S0 and dS (scaled by c_last), w.v, dO, and v, w for this thread's drhs elements.
-        {
-            const int l = tid / TPL, n0 = (tid % TPL) * EPL;
+        float vc[EPT], wc[EPT];
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const int n = n0 + i;
-                float sv = 0.f, dv = 0.f;
-                if (l < a.L && d0 + n < a.D) {
-                    const int64_t gi = ((head * nb + c) * LP + l) * a.D + d0 + n;
-                    sv = a.bnd_in[gi];
-                    dv = a.dbnd[gi];
-                }
-                dv *= f.clast[l];
-                g.t.S[l * kDS + n] = sv;
-                g.t.D[l * kDS + n] = dv;
-                xl += dv * sv;
-            }
+        for (int i = 0; i < EPL; ++i) {
+            const int n = xl_n0 + i;
+            const bool ok = xl_l < a.L && d0 + n < a.D;
+            const float sx = ok ? sv[i] : 0.f;
+            const float dv = ok ? dsv[i] * f.clast[xl_l] : 0.f;
+            g.t.S[xl_l * kDS + n] = sx;
+            g.t.D[xl_l * kDS + n] = dv;
+            xl += dv * sx;
         }
-        float vv[EPT], ww[EPT];
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-            const int64_t t = t0 + row;
-            float o = 0.f;
-            vv[i] = ww[i] = 0.f;
-            if (t < a.T && d0 + n < a.D) {
-                const int64_t gi = (head * a.T + t) * a.D + d0 + n;
-                vv[i] = a.v[gi];
-                ww[i] = a.w[gi];
-                o = a.dctx[gi];
-            }
-            g.t.X[row * kDS + n] = ww[i] * vv[i];
-            g.t.O[row * kDS + n] = o;
+            const bool ok = dense_ok(a, t0, d0, tid, i);
+            vc[i] = ok ? vv[i] : 0.f;
+            wc[i] = ok ? ww[i] : 0.f;
+            g.t.X[row * kDS + n] = wc[i] * vc[i];
+            g.t.O[row * kDS + n] = ok ? oo[i] : 0.f;
         }
+        load_tile(dt + 1 < a.n_dt ? d0 + kDN : d0);   // unconditional prefetch (see the forward)
         __syncthreads();
         // rhs = w.v - M S0;  dU = Bq^T dO / sqrt(L) + Wb dSc.
         for (int job = wave; job < NT * 4; job += 4) {
             const int ti = (job >> 1) % NT, tj = job & 1;
             if (job < NT * 2) {
                 f32x4 acc = zero4();
-                mma<LS, 1, kDS, 1>(acc, f.M + ti * 16 * LS, g.t.S + tj * 16, LP, lane);
+                mma<LP, LS, 1, kDS, 1>(acc, f.M + ti * 16 * LS, g.t.S + tj * 16, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float* p = g.t.X + (ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane);
@@ -567,9 +787,8 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
                 }
             } else {
                 f32x4 a1 = zero4(), a2 = zero4();
-                mma<1, CS, kDS, 1>(a1, f.Bq + ti * 16 * CS + ti * 16, g.t.O + ti * 16 * kDS + tj * 16, CP - ti * 16,
-                                   lane);
-                mma<LS, 1, kDS, 1>(a2, f.Wb + ti * 16 * LS, g.t.D + tj * 16, LP, lane);
+                mma16<CP, 1, CS, kDS, 1>(a1, f.Bq + ti * 16 * CS + ti * 16, g.t.O + ti * 16 * kDS + tj * 16, NT - ti, lane);
+                mma<LP, LS, 1, kDS, 1>(a2, f.Wb + ti * 16 * LS, g.t.D + tj * 16, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     g.t.dU[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = a1[r] * s + a2[r];
@@ -581,12 +800,11 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             const int ti = (job >> 1) % NT, tj = job & 1;
             f32x4 acc = zero4();
             if (job < NT * 2) {
-                mma<CS, 1, kDS, 1>(acc, f.Tm + ti * 16 * CS, g.t.X + tj * 16, (ti + 1) * 16, lane);
+                mma16<CP, CS, 1, kDS, 1>(acc, f.Tm + ti * 16 * CS, g.t.X + tj * 16, ti + 1, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) g.t.U[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
             } else {
-                mma<1, CS, kDS, 1>(acc, f.Tm + ti * 16 * CS + ti * 16, g.t.dU + ti * 16 * kDS + tj * 16, CP - ti * 16,
-                                   lane);
+                mma16<CP, 1, CS, kDS, 1>(acc, f.Tm + ti * 16 * CS + ti * 16, g.t.dU + ti * 16 * kDS + tj * 16, NT - ti, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) g.t.R[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
             }
@@ -600,8 +818,8 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             if (t < a.T && d0 + n < a.D) {
                 const int64_t gi = (head * a.T + t) * a.D + d0 + n;
                 const float r = g.t.R[row * kDS + n];
-                if (a.dw) a.dw[gi] = r * vv[i];
-                if (a.dv) a.dv[gi] = r * ww[i];
+                if (a.dw) a.dw[gi] = r * vc[i];
+                if (a.dv) a.dv[gi] = r * wc[i];
             }
         }
         // Sums over the dense axis: dO U^T, drhs U^T (lower tiles), dO S0^T, drhs S0^T, U dSc^T.
@@ -612,7 +830,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
                 const bool isA = job >= NJ;
                 int ti, tj;
                 lower_tile(isA ? job - NJ : job, ti, tj);
-                mma<kDS, 1, 1, kDS>(accC[sl], (isA ? g.t.R : g.t.O) + ti * 16 * kDS, g.t.U + tj * 16 * kDS, kDN, lane);
+                mma<kDN, kDS, 1, 1, kDS>(accC[sl], (isA ? g.t.R : g.t.O) + ti * 16 * kDS, g.t.U + tj * 16 * kDS, lane);
             }
         }
 #pragma unroll
@@ -620,9 +838,9 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             const int job = wave + 4 * sl;
             if (job < NL) {
                 const int ti = job / (LP / 16), lj = job % (LP / 16);
-                mma<kDS, 1, 1, kDS>(accQ[sl], g.t.O + ti * 16 * kDS, g.t.S + lj * 16 * kDS, kDN, lane);
-                mma<kDS, 1, 1, kDS>(accM[sl], g.t.R + ti * 16 * kDS, g.t.S + lj * 16 * kDS, kDN, lane);
-                mma<kDS, 1, 1, kDS>(accP[sl], g.t.U + ti * 16 * kDS, g.t.D + lj * 16 * kDS, kDN, lane);
+                mma<kDN, kDS, 1, 1, kDS>(accQ[sl], g.t.O + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
+                mma<kDN, kDS, 1, 1, kDS>(accM[sl], g.t.R + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
+                mma<kDN, kDS, 1, 1, kDS>(accP[sl], g.t.U + ti * 16 * kDS, g.t.D + lj * 16 * kDS, lane);
             }
         }
         __syncthreads();
@@ -662,17 +880,17 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
                 m4[r] = -accM[sl][r];
             }
             w4 = accP[sl];
-            mma<CS, 1, LS, 1>(q4, f.Bq + ti * 16 * CS, f.Wb + lj * 16, (ti + 1) * 16, lane);
-            mma<CS, 1, LS, 1>(m4, f.Tm + ti * 16 * CS, f.Wb + lj * 16, (ti + 1) * 16, lane);
-            mma<1, CS, LS, 1>(w4, f.Bq + ti * 16 * CS + ti * 16, f.Qc + ti * 16 * LS + lj * 16, CP - ti * 16, lane);
-            mma<1, CS, LS, 1>(w4, f.Tm + ti * 16 * CS + ti * 16, f.M + ti * 16 * LS + lj * 16, CP - ti * 16, lane);
+            mma16<CP, CS, 1, LS, 1>(q4, f.Bq + ti * 16 * CS, f.Wb + lj * 16, ti + 1, lane);
+            mma16<CP, CS, 1, LS, 1>(m4, f.Tm + ti * 16 * CS, f.Wb + lj * 16, ti + 1, lane);
+            mma16<CP, 1, CS, LS, 1>(w4, f.Bq + ti * 16 * CS + ti * 16, f.Qc + ti * 16 * LS + lj * 16, NT - ti, lane);
+            mma16<CP, 1, CS, LS, 1>(w4, f.Tm + ti * 16 * CS + ti * 16, f.M + ti * 16 * LS + lj * 16, NT - ti, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = ti * 16 + acc_row(lane, r), col = lj * 16 + acc_col(lane);
-                g.m.dQc[row * LS + col] = q4[r];
-                g.m.dM[row * LS + col] = m4[r];
-                g.m.dWb[row * LS + col] = w4[r];
-                g.m.P[row * LS + col] = accP[sl][r];
+                g.m.dQc[row * LP + col] = q4[r];
+                g.m.dM[row * LP + col] = m4[r];
+                g.m.dWb[row * LP + col] = w4[r];
+                g.m.P[row * LP + col] = accP[sl][r];
             }
         }
     }
@@ -685,10 +903,10 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int row = rg * RPT + i;
-            const float dQc = g.m.dQc[row * LS + l], dM = g.m.dM[row * LS + l], dWb = g.m.dWb[row * LS + l];
+            const float dQc = g.m.dQc[row * LP + l], dM = g.m.dM[row * LP + l], dWb = g.m.dWb[row * LP + l];
             const float Qc = f.Qc[row * LS + l], M = f.M[row * LS + l], Wb = f.Wb[row * LS + l];
             dcc[i] = dQc * Qc + dM * M - dWb * Wb;
-            pp += Wb * g.m.P[row * LS + l];
+            pp += Wb * g.m.P[row * LP + l];
             const int64_t t = t0 + row;
             if (t < a.T && l < a.L) {
                 const int64_t gi = (head * a.T + t) * a.L + l;
@@ -728,11 +946,19 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     }
 }
 
+unsigned seq_blocks(const WyArgs& a) { return unsigned((a.BH + 7) / 8 * 8 * a.n_dt); }
+
 template <int CP, int LP>
 hipError_t launch_fwd_t(const WyArgs& a, hipStream_t st) {
     WyArgs args = a;
     void* params[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&wy_fwd_kernel<CP, LP>), dim3(unsigned(a.BH * a.n_dt)),
+    if (a.rec == nullptr)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&wy_fwd_kernel<CP, LP, false>), dim3(seq_blocks(a)),
+                               dim3(kThreads), params, 0, st);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wy_factor_kernel<CP, LP>),
+                                   dim3(unsigned(a.BH * a.n_chunks)), dim3(kThreads), params, 0, st);
+    if (e != hipSuccess) return e;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&wy_fwd_kernel<CP, LP, true>), dim3(seq_blocks(a)),
                            dim3(kThreads), params, 0, st);
 }
 
@@ -740,9 +966,10 @@ template <int CP, int LP>
 hipError_t launch_bwd_t(const WyArgs& a, hipStream_t st) {
     WyArgs args = a;
     void* params[] = {&args};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wy_bwd_carry_kernel<CP, LP>),
-                                   dim3(unsigned(a.BH * a.n_dt)), dim3(kThreads), params, 0, st);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wy_bwd_carry_kernel<CP, LP>), dim3(seq_blocks(a)),
+                                   dim3(kThreads), params, 0, st);
     if (e != hipSuccess) return e;
+    if (!a.dq && !a.dk && !a.dv && !a.db && !a.dw && !a.dg) return hipSuccess;
     return hipLaunchKernel(reinterpret_cast<const void*>(&wy_bwd_grad_kernel<CP, LP>),
                            dim3(unsigned(a.BH * a.n_chunks)), dim3(kThreads), params, 0, st);
 }
