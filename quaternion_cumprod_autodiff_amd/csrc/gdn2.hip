@@ -809,9 +809,14 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t c
         // blocks; the scratch holds the state cotangent entering each chunk.
         if (z->BH > (int64_t(1) << 31) / z->n_chunks) return QC_ERR_SHAPE;
         if (z->BH > (int64_t(1) << 31) / ((D + kWyDense - 1) / kWyDense)) return QC_ERR_SHAPE;
-        z->scratch_bytes = size_t(z->BH * z->n_chunks * z->lm * D) * sizeof(float);
+        // Scratch: the state cotangent entering each chunk, then drhs of every
+        // padded step.  Saved state: boundary states, factor records, then U of
+        // every padded step.
+        const int64_t tp = z->n_chunks * chunk;
         if (z->BH * z->n_chunks > kMaxElems / wy_record_floats(chunk, z->lm)) return QC_ERR_SHAPE;
-        z->bnd_bytes += size_t(z->BH * z->n_chunks * wy_record_floats(chunk, z->lm)) * sizeof(float);
+        if (z->BH * tp > kMaxElems / D) return QC_ERR_SHAPE;
+        z->scratch_bytes = size_t(z->BH * z->n_chunks * z->lm * D + z->BH * tp * D) * sizeof(float);
+        z->bnd_bytes += size_t(z->BH * z->n_chunks * wy_record_floats(chunk, z->lm) + z->BH * tp * D) * sizeof(float);
     }
     return QC_OK;
 }
@@ -891,6 +896,7 @@ int gdn2_fwd(const float* query, const float* key, const float* value, const flo
         w.q = query; w.k = key; w.v = value; w.b = erase; w.w = write; w.g = log_decay; w.s0 = initial_state;
         w.ctx = context; w.state = final_state; w.bnd = boundary;
         w.rec = boundary ? boundary + z.BH * z.n_chunks * z.lm * D : nullptr;
+        w.ubuf = boundary ? w.rec + z.BH * z.n_chunks * qc::wy_record_floats(chunk, z.lm) : nullptr;
         w.BH = z.BH; w.T = T; w.L = L; w.D = D; w.n_chunks = z.n_chunks;
         w.n_dt = int((D + qc::kWyDense - 1) / qc::kWyDense);
         w.scale = 1.0f / sqrtf(float(L));
@@ -950,6 +956,8 @@ int gdn2_bwd(const float* query, const float* key, const float* value, const flo
         w.q = query; w.k = key; w.v = value; w.b = erase; w.w = write; w.g = log_decay;
         w.bnd_in = boundary; w.dctx = d_context; w.dstate = d_state;
         w.rec = const_cast<float*>(boundary) + z.BH * z.n_chunks * z.lm * D;
+        w.ubuf = w.rec + z.BH * z.n_chunks * qc::wy_record_floats(chunk, z.lm);
+        w.drhs = scratch + z.BH * z.n_chunks * z.lm * D;
         w.dq = d_query; w.dk = d_key; w.dv = d_value; w.db = d_erase; w.dw = d_write; w.dg = d_log_decay;
         w.ds0 = d_initial_state; w.dbnd = scratch;
         w.BH = z.BH; w.T = T; w.L = L; w.D = D; w.n_chunks = z.n_chunks;

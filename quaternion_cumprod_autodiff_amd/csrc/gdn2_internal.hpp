@@ -24,6 +24,8 @@ struct WyArgs {
     const float *q, *k, *v, *b, *w, *g, *s0;   // inputs
     float *ctx, *state, *bnd;                   // forward outputs (bnd: [BH, n_chunks, LP, D])
     float* rec;                                 // factor records [BH, n_chunks, wy_record_floats] (after the states), or null
+    float* ubuf;                                // the chunks' updates U [BH, n_chunks * chunk, D] (after the records), or null
+    float* drhs;                                // backward scratch after dbnd: drhs [BH, n_chunks * chunk, D]
     const float *bnd_in, *dctx, *dstate;        // backward inputs
     float *dq, *dk, *dv, *db, *dw, *dg, *ds0;   // backward outputs (each may be null)
     float* dbnd;                                // backward scratch: [BH, n_chunks, LP, D], the state cotangent entering each chunk from later ones

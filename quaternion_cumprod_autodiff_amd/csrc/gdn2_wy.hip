@@ -475,7 +475,12 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
             f32x4 acc = zero4();
             mma16<CP, CS, 1, kDS, 1>(acc, f.Tm + ti * 16 * CS, sX + tj * 16, ti + 1, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sU[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
+            for (int r = 0; r < 4; ++r) {
+                const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
+                sU[row * kDS + col] = acc[r];
+                // U is kept for the backward (rows of the padded chunk, columns < D).
+                if (kRec && d0 + col < a.D) a.ubuf[(head * nb * CP + t0 + row) * a.D + d0 + col] = acc[r];
+            }
         }
         __syncthreads();
         // O = (Qc S0 + Bq U) / sqrt(L).
@@ -562,8 +567,24 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
     constexpr int EPT = CP * kDN / kThreads;
     RecRegs<CP, LP> rr;
     float oo[EPT];
+    // v and w at this lane's elements of its drhs tile (job = wave: one
+    // 16x16 tile per wave when CP = 32, waves 0 and 1 when CP = 16), for
+    // dv = drhs . w and dw = drhs . v.
+    const bool has_tile = wave < NT * 2;
+    const int my_ti = (wave >> 1) % NT, my_tj = wave & 1;
+    float vt[4], wt[4];
+    auto load_vw = [&](int64_t tc0) {   // raw (clamped), masked where consumed
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t t = tc0 + my_ti * 16 + acc_row(lane, r), d = d0 + my_tj * 16 + acc_col(lane);
+            const int64_t gi = (head * a.T + (t < a.T ? t : a.T - 1)) * a.D + (d < a.D ? d : a.D - 1);
+            vt[r] = a.v[gi];
+            wt[r] = a.w[gi];
+        }
+    };
     load_rec<CP, LP>(rr, a.rec + (head * nb + nb - 1) * R::kSize, tid);
     load_dense<CP, false>(a.dctx, nullptr, a, head, (nb - 1) * CP, d0, tid, oo, nullptr);
+    load_vw((nb - 1) * CP);
     for (int64_t c = nb - 1; c >= 0; --c) {
         const int64_t t0 = c * CP;
 #pragma unroll
@@ -574,8 +595,15 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
         stage_rec<CP, LP>(f, rr, tid);
         __syncthreads();
         const int64_t cn = c > 0 ? c - 1 : c;   // unconditional prefetch (see the forward)
+        float vc[4], wc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vc[r] = vt[r];
+            wc[r] = wt[r];
+        }
         load_rec<CP, LP>(rr, a.rec + (head * nb + cn) * R::kSize, tid);
         load_dense<CP, false>(a.dctx, nullptr, a, head, cn * CP, d0, tid, oo, nullptr);
+        load_vw(cn * CP);
         // dU = Bq^T dO / sqrt(L) + Wb dSc, with Wb dSc = Kt dS (Kt = Wb diag(c_last)).
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
@@ -593,7 +621,19 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
             f32x4 acc = zero4();
             mma16<CP, 1, CS, kDS, 1>(acc, f.Tm + ti * 16 * CS + ti * 16, sU + ti * 16 * kDS + tj * 16, NT - ti, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sR[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
+            for (int r = 0; r < 4; ++r) {
+                const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
+                sR[row * kDS + col] = acc[r];
+                const int64_t t = t0 + row, d = d0 + col;
+                if (d < a.D) {
+                    const int64_t gi = (head * a.T + t) * a.D + d;
+                    a.drhs[(head * nb * CP + t) * a.D + d] = acc[r];   // for the gradient kernel
+                    if (t < a.T) {
+                        if (a.dw) a.dw[gi] = acc[r] * vc[r];
+                        if (a.dv) a.dv[gi] = acc[r] * wc[r];
+                    }
+                }
+            }
         }
         __syncthreads();
         // dS0 = Qc^T dO / sqrt(L) + diag(c_last) dS - M^T drhs.
@@ -644,11 +684,9 @@ struct GradTiles {
         struct {
             float S[LP * kDS];    // boundary state tile S0
             float D[LP * kDS];    // dSc = diag(c_last) dS tile
-            float X[CP * kDS];    // w.v, then rhs
             float O[CP * kDS];    // dO
-            float U[CP * kDS];    // U, then (after drhs) free
-            float dU[CP * kDS];   // dU
-            float R[CP * kDS];    // drhs
+            float U[CP * kDS];    // U (saved by the forward)
+            float R[CP * kDS];    // drhs (from the carry kernel)
         } t;
         struct {
             float dQc[CP * LP], dM[CP * LP], dWb[CP * LP], P[CP * LP];
@@ -686,13 +724,13 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
         in.b[i] = ok ? in.b[i] : 0.f;
         in.g[i] = ok ? in.g[i] : 0.f;
     }
-    // The chunk's record (M, Qc, T, Bq, c_last; Kt is not needed here).
+    // The chunk's record: M, Qc and c_last (U and drhs come ready-made).
     {
         using R = Rec<CP, LP>;
         const f32x4* rec = reinterpret_cast<const f32x4*>(a.rec + (head * nb + c) * R::kSize);
         for (int j = tid; j < R::kN4; j += kThreads) {
             const int e4 = 4 * j;
-            if (e4 < R::kKt || e4 >= R::kT) *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, e4)) = rec[j];
+            if (e4 < R::kKt || e4 >= R::kCl) *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, e4)) = rec[j];
         }
     }
     // Wb = k / c, and c, 1/c of this thread's rows, as the factor kernel forms them.
@@ -733,11 +771,13 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
 
     constexpr int EPT = CP * kDN / kThreads;
     // One dense tile's loads, in registers: S0 and dS (this thread's row
-    // l = tid / TPL, EPL columns), v, w and dO (elements tid + i * kThreads of
-    // the [CP][kDN] tile).  The next tile's are issued while this one computes.
-    float sv[EPL], dsv[EPL], vv[EPT], ww[EPT], oo[EPT];
+    // l = tid / TPL, EPL columns), and U (saved by the forward), drhs (written
+    // by the carry kernel) and dO (elements tid + i * kThreads of the
+    // [CP][kDN] tile).  The next tile's are issued while this one computes;
+    // values are raw (clamped) and masked where consumed.
+    float sv[EPL], dsv[EPL], uu[EPT], rv[EPT], oo[EPT];
     const int xl_l = tid / TPL, xl_n0 = (tid % TPL) * EPL;
-    auto load_tile = [&](int64_t d0) {   // raw (clamped) values, masked where consumed
+    auto load_tile = [&](int64_t d0) {
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int64_t d = d0 + xl_n0 + i;
@@ -745,14 +785,20 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             sv[i] = a.bnd_in[gi];
             dsv[i] = a.dbnd[gi];
         }
-        load_dense<CP, true>(a.v, a.w, a, head, t0, d0, tid, vv, ww);
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int idx = tid + i * kThreads;
+            const int64_t d = d0 + idx % kDN;
+            const int64_t gi = (head * nb * CP + t0 + idx / kDN) * a.D + (d < a.D ? d : a.D - 1);
+            uu[i] = a.ubuf[gi];
+            rv[i] = a.drhs[gi];
+        }
         load_dense<CP, false>(a.dctx, nullptr, a, head, t0, d0, tid, oo, nullptr);
     };
     load_tile(0);
     __syncthreads();   // the record and Wb are in LDS
     for (int dt = 0; dt < a.n_dt; ++dt) {
         const int64_t d0 = int64_t(dt) * kDN;
-        float vc[EPT], wc[EPT];
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int n = xl_n0 + i;
@@ -766,62 +812,13 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-            const bool ok = dense_ok(a, t0, d0, tid, i);
-            vc[i] = ok ? vv[i] : 0.f;
-            wc[i] = ok ? ww[i] : 0.f;
-            g.t.X[row * kDS + n] = wc[i] * vc[i];
-            g.t.O[row * kDS + n] = ok ? oo[i] : 0.f;
+            const bool okd = d0 + n < a.D;
+            g.t.U[row * kDS + n] = okd ? uu[i] : 0.f;
+            g.t.R[row * kDS + n] = okd ? rv[i] : 0.f;
+            g.t.O[row * kDS + n] = dense_ok(a, t0, d0, tid, i) ? oo[i] : 0.f;
         }
         load_tile(dt + 1 < a.n_dt ? d0 + kDN : d0);   // unconditional prefetch (see the forward)
         __syncthreads();
-        // rhs = w.v - M S0;  dU = Bq^T dO / sqrt(L) + Wb dSc.
-        for (int job = wave; job < NT * 4; job += 4) {
-            const int ti = (job >> 1) % NT, tj = job & 1;
-            if (job < NT * 2) {
-                f32x4 acc = zero4();
-                mma<LP, LS, 1, kDS, 1>(acc, f.M + ti * 16 * LS, g.t.S + tj * 16, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float* p = g.t.X + (ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane);
-                    *p = *p - acc[r];
-                }
-            } else {
-                f32x4 a1 = zero4(), a2 = zero4();
-                mma16<CP, 1, CS, kDS, 1>(a1, f.Bq + ti * 16 * CS + ti * 16, g.t.O + ti * 16 * kDS + tj * 16, NT - ti, lane);
-                mma<LP, LS, 1, kDS, 1>(a2, f.Wb + ti * 16 * LS, g.t.D + tj * 16, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    g.t.dU[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = a1[r] * s + a2[r];
-            }
-        }
-        __syncthreads();
-        // U = T rhs;  drhs = T^T dU.
-        for (int job = wave; job < NT * 4; job += 4) {
-            const int ti = (job >> 1) % NT, tj = job & 1;
-            f32x4 acc = zero4();
-            if (job < NT * 2) {
-                mma16<CP, CS, 1, kDS, 1>(acc, f.Tm + ti * 16 * CS, g.t.X + tj * 16, ti + 1, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) g.t.U[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
-            } else {
-                mma16<CP, 1, CS, kDS, 1>(acc, f.Tm + ti * 16 * CS + ti * 16, g.t.dU + ti * 16 * kDS + tj * 16, NT - ti, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) g.t.R[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
-            }
-        }
-        __syncthreads();
-        // dw = drhs . v, dv = drhs . w.
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-            const int64_t t = t0 + row;
-            if (t < a.T && d0 + n < a.D) {
-                const int64_t gi = (head * a.T + t) * a.D + d0 + n;
-                const float r = g.t.R[row * kDS + n];
-                if (a.dw) a.dw[gi] = r * vc[i];
-                if (a.dv) a.dv[gi] = r * wc[i];
-            }
-        }
         // Sums over the dense axis: dO U^T, drhs U^T (lower tiles), dO S0^T, drhs S0^T, U dSc^T.
 #pragma unroll
         for (int sl = 0; sl < NCC; ++sl) {
@@ -847,7 +844,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     }
 
     // dBq = lower(dO U^T) / sqrt(L) into f.Bq, dA = -strictly lower(drhs U^T) into f.Tm
-    // (their upper tiles are already zero).
+    // (their buffers are free: this kernel reads neither T nor Bq).
 #pragma unroll
     for (int sl = 0; sl < NCC; ++sl) {
         const int job = wave + 4 * sl;
@@ -862,6 +859,12 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
                 const bool keep = isA ? gi > gj : gi >= gj;
                 dst[acc_row(lane, r) * CS + acc_col(lane)] = keep ? (isA ? -accC[sl][r] : accC[sl][r] * s) : 0.f;
             }
+        }
+    }
+    if constexpr (NT > 1) {   // their upper tile (0, 1) is zero
+        for (int idx = tid; idx < 256; idx += kThreads) {
+            f.Tm[(idx / 16) * CS + 16 + idx % 16] = 0.f;
+            f.Bq[(idx / 16) * CS + 16 + idx % 16] = 0.f;
         }
     }
     g.m.xl[tid] = xl;
