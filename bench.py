@@ -458,24 +458,98 @@ def scan_bench(args):
 
 # -------------------------------------------------------- Gated DeltaNet-2
 # The recurrence of include/gdn2.h at the page's training head shape (latent
-# 64, dense 128) over 8 x 16 heads and 2048 steps; boundary states every 8
-# steps, the chunk whose states the backward keeps in registers (3.7 ms per
-# step against 6.0 at chunk 32).
+# 64, dense 128) over 8 x 16 heads and 2048 steps, in chunk-WY form on fp32
+# MFMA at chunks of 32 steps (chunks of 16 or 32 select that form; any other
+# chunk runs the step-by-step recurrent kernels).
 GDN2_WORKLOAD = (8, 16, 2048, 64, 128, 32)
-FP32_VECTOR_PEAK_TFLOPS = 157.3
+FP32_MFMA_PEAK_TFLOPS = 157.3
+GDN2_SOURCES = [os.path.join(ROOT, "quaternion_cumprod_autodiff_amd", "csrc", f)
+                for f in ("gdn2.hip", "gdn2_wy.hip", "gdn2_internal.hpp")]
+GDN2_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gdn2.txt")
 
 
-def gdn2_bytes_and_flops(B, H, T, L, D):
-    """Algorithmic bytes and flops per forward and per VJP (float32).  Bytes:
-    every input read once, every output written once (the boundary states and
-    the backward's scratch are the method's recompute and are not counted).
-    Flops per (head, step, latent row, dense column): forward 7 (decay 1,
-    erased read-out 2, write 2, read-out 2); VJP 23 (the step recomputed, 5,
-    and its reverse, 18), counting an FMA as 2."""
+def gdn2_source_sha() -> str:
+    h = hashlib.sha256()
+    for path in GDN2_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def gdn2_bytes_and_flops(B, H, T, L, D, C):
+    """Algorithmic bytes and flops of one forward and one VJP (float32).
+
+    Bytes: every input read once, every output written once (the saved
+    boundary states, factor records and updates, and the backward's scratch,
+    are the method's own state and are not counted).
+
+    Flops: the chunk-WY form at chunk C, counted per chunk of every head as
+    multiply-adds (2 flops each), a triangular product as half its dense size:
+      forward  A = M Wb^T and Bq = Qc Wb^T: C^2 L;  T = (I + A)^-1: C^3 / 6;
+               M S0, Qc S0, Kt^T U: 3 C L D;  T rhs and Bq U: C^2 D
+      VJP      Bq^T dO, T^T dU, dO U^T, drhs U^T: 2 C^2 D;
+               Kt dS, Qc^T dO, M^T drhs, dO S0^T, drhs S0^T, U dSc^T: 6 C L D;
+               dBq Wb, dA Wb, dBq^T Qc, dA^T M: 2 C^2 L
+    with ceil(T / C) chunks per head."""
     heads = B * H
+    chunks = heads * ((T + C - 1) // C)
     fwd_bytes = 4 * heads * (T * (4 * L + 2 * D) + L * D + T * D + L * D)
     bwd_bytes = 4 * heads * (T * (4 * L + 3 * D) + T * (4 * L + 2 * D) + L * D)
-    return fwd_bytes, bwd_bytes, 7 * heads * T * L * D, 23 * heads * T * L * D
+    fwd_mac = C * C * L + C ** 3 / 6 + 3 * C * L * D + C * C * D
+    bwd_mac = 2 * C * C * D + 6 * C * L * D + 2 * C * C * L
+    return fwd_bytes, bwd_bytes, int(2 * fwd_mac * chunks), int(2 * bwd_mac * chunks)
+
+
+def load_gdn2_traffic(workload_key: str):
+    """HBM bytes per VJP (both backward launches) from the committed counter
+    summary, or None when missing or taken on different kernel sources."""
+    try:
+        rec = read_kv(GDN2_TRAFFIC_FILE)
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != gdn2_source_sha() or rec.get("workload") != workload_key:
+        return None
+    return float(rec["bwd_hbm_bytes"])
+
+
+def summarize_gdn2_traffic(pmc_dir: str, workload_key: str):
+    """profiles/traffic_gdn2.txt from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of
+    --gdn2, scaled by the plain-copy calibration of traffic_headline.txt."""
+    import csv
+    import statistics
+    cal = read_kv(TRAFFIC_FILE)
+    fs, ws = float(cal["fetch_scale"]), float(cal["write_scale"])
+
+    def per_kernel(counter):
+        vals = {}
+        for r in csv.DictReader(open(os.path.join(pmc_dir, counter, "run_counter_collection.csv"))):
+            if r["Counter_Name"] != counter or "wy_" not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].split("(anonymous namespace)::")[-1].split("(")[0]
+            vals.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    f, w = per_kernel("FETCH_SIZE"), per_kernel("WRITE_SIZE")
+    B, H, T, L, D, C = GDN2_WORKLOAD
+    fb, bb, _, _ = gdn2_bytes_and_flops(B, H, T, L, D, C)
+    fwd = sum(f[k] * fs + w.get(k, 0.0) * ws for k in f if "fwd" in k or "factor" in k)
+    bwd = sum(f[k] * fs + w.get(k, 0.0) * ws for k in f if "bwd" in k)
+    with open(GDN2_TRAFFIC_FILE, "w") as out:
+        out.write("# HBM traffic of the Gated DeltaNet-2 chunk-WY kernels, bench workload.\n")
+        out.write("# Counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), scaled by\n")
+        out.write("# the factors of the plain-copy calibration in traffic_headline.txt; median over the run.\n")
+        out.write("# Commands (run from /tmp, TMPDIR=/tmp, R = repository root, OUT = an output directory):\n")
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            out.write(f"#   rocprofv3 --pmc {ctr} --output-format csv -d $OUT/pmc_gdn2/{ctr} -o run -- "
+                      f"python3 $R/bench.py --gdn2 --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline\n")
+        out.write("#   python3 $R/bench.py --summarize-gdn2-traffic $OUT/pmc_gdn2\n")
+        out.write(f"workload = {workload_key}\n")
+        out.write(f"kernel_source_sha256 = {gdn2_source_sha()}\n")
+        for k in sorted(f):
+            out.write(f"{k}_fetch_bytes = {f[k] * fs:.0f}\n{k}_write_bytes = {w.get(k, 0.0) * ws:.0f}\n")
+        out.write(f"fwd_hbm_bytes = {fwd:.0f}\nfwd_algorithmic_bytes = {fb}\nfwd_ratio = {fwd / fb:.3f}\n")
+        out.write(f"bwd_hbm_bytes = {bwd:.0f}\nbwd_algorithmic_bytes = {bb}\nbwd_ratio = {bwd / bb:.3f}\n")
+    print(open(GDN2_TRAFFIC_FILE).read())
 
 
 def gdn2_bench(args):
@@ -526,22 +600,27 @@ def gdn2_bench(args):
     wall = (time.perf_counter() - t0) / steps
     fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in evs]))
     bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in evs]))
-    fb, bb, ff, bf = gdn2_bytes_and_flops(B, H, T, L, D)
-    dominant = ("gdn2_bwd_kernel", bf, bwd_ms) if bwd_ms >= fwd_ms else ("gdn2_fwd_kernel", ff, fwd_ms)
-    tflops = dominant[1] / (dominant[2] * 1e-3) / 1e12
+    fb, bb, ff, bf = gdn2_bytes_and_flops(B, H, T, L, D, chunk)
+    wy = chunk in (16, 32)
+    tflops = bf / (bwd_ms * 1e-3) / 1e12
+    workload = f"gdn2 b{B} h{H} t{T} latent{L} dense{D} chunk{chunk} f32, forward + VJP"
     rec = {
         "metric": f"Gated DeltaNet-2 fwd+bwd GB/s, b{B} h{H} t{T} latent{L} dense{D} fp32",
         "value": round((fb + bb) / wall / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"gdn2 b{B} h{H} t{T} latent{L} dense{D} chunk{chunk} f32, forward + VJP",
-                   "B": B, "H": H, "T": T, "L": L, "D": D, "chunk": chunk},
+        "config": {"workload": workload, "B": B, "H": H, "T": T, "L": L, "D": D, "chunk": chunk,
+                   "form": "chunk-WY, fp32 MFMA" if wy else "step-by-step recurrence"},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "fwd_bytes": fb, "bwd_bytes": bb, "fwd_flops": ff, "bwd_flops": bf,
+        "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 3),
         "head_steps_per_s": round(B * H * T / wall, 1),
-        "roofline": {"bound": "alu", "kernel": dominant[0], "achieved": round(tflops, 3),
-                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 5), "traffic": None},
+        "roofline": {"bound": "mfma" if wy else "alu",
+                     "kernel": "gdn2_bwd (wy_bwd_carry_kernel + wy_bwd_grad_kernel)" if wy else "gdn2_bwd_kernel",
+                     "achieved": round(tflops, 3), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 5),
+                     "flops_per_launch": bf,
+                     "traffic": load_gdn2_traffic(workload) if wy else None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -749,6 +828,8 @@ def main():
                     help="write profiles/traffic_scan_quat.txt from rocprofv3 runs of --scan quat")
     ap.add_argument("--gdn2", action="store_true",
                     help="measure the Gated DeltaNet-2 forward + VJP (include/gdn2.h) instead")
+    ap.add_argument("--summarize-gdn2-traffic", metavar="PMC_DIR",
+                    help="write profiles/traffic_gdn2.txt from rocprofv3 runs of --gdn2")
     ap.add_argument("--gdn2-chunk", type=int, default=0,
                     help="with --gdn2: steps between saved boundary states (default: the workload's)")
     ap.add_argument("--all-configs", action="store_true",
@@ -762,6 +843,11 @@ def main():
     ap.add_argument("--profile-command", default="",
                     help="with --summarize-profile: the commands that made the runs (' ;; '-separated)")
     args = ap.parse_args()
+    if args.summarize_gdn2_traffic:
+        B, H, T, L, D, C = GDN2_WORKLOAD
+        summarize_gdn2_traffic(args.summarize_gdn2_traffic,
+                               f"gdn2 b{B} h{H} t{T} latent{L} dense{D} chunk{C} f32, forward + VJP")
+        return
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.config, args.pmc_dir, args.profile_command)
         return

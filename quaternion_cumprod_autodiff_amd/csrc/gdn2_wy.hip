@@ -88,6 +88,32 @@ __device__ __forceinline__ void mma(f32x4& acc, const float* a, const float* b, 
     for (int k = 0; k < K / 4; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k], bv[k], acc, 0, 0, 0);
 }
 
+// acc += A B over K with both operands stored contiguously along K:
+// A(m, k) = a[m * SA + k], B(k, n) = bt[n * SB + k] (a and bt point at row
+// m0 and row n0).  Lane group kq = l / 16 takes k = kq * K/4 + j at step j,
+// so a lane's operands for four steps are one 16-byte LDS read each (the
+// same reordering of the sum for A and B, so the product is unchanged up to
+// rounding).  SA and SB multiples of 4 with SA / 4 and SB / 4 odd keep the
+// 16 lanes of a row group on distinct banks.
+template <int K, int SA, int SB>
+__device__ __forceinline__ void mma_kc(f32x4& acc, const float* a, const float* bt, int lane) {
+    static_assert(K % 16 == 0 && SA % 4 == 0 && SB % 4 == 0, "16-byte operand reads");
+    constexpr int KQ = K / 4;
+    const int i = lane & 15, kq = lane >> 4;
+    const f32x4* pa = reinterpret_cast<const f32x4*>(a + i * SA + kq * KQ);
+    const f32x4* pb = reinterpret_cast<const f32x4*>(bt + i * SB + kq * KQ);
+    f32x4 av[KQ / 4], bv[KQ / 4];
+#pragma unroll
+    for (int j = 0; j < KQ / 4; ++j) {
+        av[j] = pa[j];
+        bv[j] = pb[j];
+    }
+#pragma unroll
+    for (int j = 0; j < KQ / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][e], bv[j][e], acc, 0, 0, 0);
+}
+
 // The same with K = 16 * k16, k16 wave-uniform in 1 .. KMAX / 16 (the
 // triangular ranges of the chunk's lower-triangular factors; KMAX <= 32).
 template <int KMAX, int SAM, int SAK, int SBK, int SBN>
@@ -262,7 +288,7 @@ __device__ void make_factors(F& f, const LatIn<RPT>& raw, const WyArgs& a, int64
         int ti, tj;
         lower_tile(isA ? job - NJ : job, ti, tj);
         f32x4 acc = zero4();
-        mma<LP, LS, 1, 1, LS>(acc, (isA ? f.M : f.Qc) + ti * 16 * LS, f.Wb + tj * 16 * LS, lane);
+        mma_kc<LP, LS, LS>(acc, (isA ? f.M : f.Qc) + ti * 16 * LS, f.Wb + tj * 16 * LS, lane);
         float* dst = (isA ? f.Tm : f.Bq) + ti * 16 * CS + tj * 16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -678,7 +704,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
 // ------------------------------------------------ backward: the gradients
 
 template <int CP, int LP>
-struct GradTiles {
+struct alignas(16) GradTiles {
     // The walk over dense tiles; reused for the final per-chunk matrices.
     union {
         struct {
@@ -714,61 +740,9 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     const int64_t nb = a.n_chunks;
     const float s = a.scale;
 
-    LatIn<RPT> in;
-    load_latent<CP, LP>(a, head, t0, tid, in);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const bool ok = latent_ok<CP, LP, RPT>(a, t0, tid, i);
-        in.q[i] = ok ? in.q[i] : 0.f;
-        in.k[i] = ok ? in.k[i] : 0.f;
-        in.b[i] = ok ? in.b[i] : 0.f;
-        in.g[i] = ok ? in.g[i] : 0.f;
-    }
-    // The chunk's record: M, Qc and c_last (U and drhs come ready-made).
-    {
-        using R = Rec<CP, LP>;
-        const f32x4* rec = reinterpret_cast<const f32x4*>(a.rec + (head * nb + c) * R::kSize);
-        for (int j = tid; j < R::kN4; j += kThreads) {
-            const int e4 = 4 * j;
-            if (e4 < R::kKt || e4 >= R::kCl) *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, e4)) = rec[j];
-        }
-    }
-    // Wb = k / c, and c, 1/c of this thread's rows, as the factor kernel forms them.
-    float e[RPT], ie[RPT];
-    {
-        const int l = tid % LP, rg = tid / LP;
-        float G[RPT];
-        float run = 0.f;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            run += in.g[i];
-            G[i] = run;
-        }
-        f.tot[rg * LP + l] = run;
-        __syncthreads();
-        float off = 0.f;
-#pragma unroll
-        for (int r = 0; r < RG; ++r)
-            if (r < rg) off += f.tot[r * LP + l];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const float Gt = off + G[i];
-            e[i] = __expf(Gt);
-            ie[i] = __expf(-Gt);
-            f.Wb[(rg * RPT + i) * LS + l] = in.k[i] * ie[i];
-        }
-    }
-
-    f32x4 accC[NCC], accQ[NCL], accM[NCL], accP[NCL];
-#pragma unroll
-    for (int i = 0; i < NCC; ++i) accC[i] = zero4();
-#pragma unroll
-    for (int i = 0; i < NCL; ++i) accQ[i] = accM[i] = accP[i] = zero4();
     // rowsum(dSc . S0) partials: thread (l = tid / (256 / LP) ...) over its elements.
     constexpr int TPL = kThreads / LP;               // threads per latent row
     constexpr int EPL = kDN / TPL;                   // elements per thread per tile
-    float xl = 0.f;
-
     constexpr int EPT = CP * kDN / kThreads;
     // One dense tile's loads, in registers: S0 and dS (this thread's row
     // l = tid / TPL, EPL columns), and U (saved by the forward), drhs (written
@@ -795,7 +769,85 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
         }
         load_dense<CP, false>(a.dctx, nullptr, a, head, t0, d0, tid, oo, nullptr);
     };
+
+    // Prologue: every load of the block is issued before the first wait
+    // (latent inputs, the record's M, Qc and c_last, the first dense tile), so
+    // their latencies overlap.
+    using R = Rec<CP, LP>;
+    constexpr int NR4 = R::kKt / 4 + LP / 4;        // float4 of M, Qc and c_last
+    constexpr int RPER = (NR4 + kThreads - 1) / kThreads;
+    LatIn<RPT> in;
+    {
+        const int l = tid % LP, rg = tid / LP;
+        const int64_t lc = l < a.L ? l : a.L - 1;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int64_t t = t0 + rg * RPT + i;
+            const int64_t idx = (head * a.T + (t < a.T ? t : a.T - 1)) * a.L + lc;
+            in.k[i] = a.k[idx];
+            in.b[i] = a.b[idx];
+            in.g[i] = a.g[idx];
+        }
+    }
+    f32x4 recv[RPER];
+    {
+        const f32x4* rec4 = reinterpret_cast<const f32x4*>(a.rec + (head * nb + c) * R::kSize);
+#pragma unroll
+        for (int i = 0; i < RPER; ++i) {
+            const int j = tid + i * kThreads;
+            const int jj = j < NR4 ? j : NR4 - 1;
+            recv[i] = rec4[jj < R::kKt / 4 ? jj : R::kCl / 4 + (jj - R::kKt / 4)];
+        }
+    }
     load_tile(0);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const bool ok = latent_ok<CP, LP, RPT>(a, t0, tid, i);
+        in.k[i] = ok ? in.k[i] : 0.f;
+        in.b[i] = ok ? in.b[i] : 0.f;
+        in.g[i] = ok ? in.g[i] : 0.f;
+    }
+    // Wb = k / c, and c, 1/c of this thread's rows, as the factor kernel forms them.
+    float e[RPT], ie[RPT];
+    {
+        const int l = tid % LP, rg = tid / LP;
+        float G[RPT];
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            run += in.g[i];
+            G[i] = run;
+        }
+        f.tot[rg * LP + l] = run;
+        __syncthreads();
+        float off = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+            if (r < rg) off += f.tot[r * LP + l];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float Gt = off + G[i];
+            e[i] = __expf(Gt);
+            ie[i] = __expf(-Gt);
+            f.Wb[(rg * RPT + i) * LS + l] = in.k[i] * ie[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RPER; ++i) {
+        const int j = tid + i * kThreads;
+        if (j < NR4) {
+            const int e4 = j < R::kKt / 4 ? 4 * j : R::kCl + 4 * (j - R::kKt / 4);
+            *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, e4)) = recv[i];
+        }
+    }
+
+    f32x4 accC[NCC], accQ[NCL], accM[NCL], accP[NCL];
+#pragma unroll
+    for (int i = 0; i < NCC; ++i) accC[i] = zero4();
+#pragma unroll
+    for (int i = 0; i < NCL; ++i) accQ[i] = accM[i] = accP[i] = zero4();
+    float xl = 0.f;
+
     __syncthreads();   // the record and Wb are in LDS
     for (int dt = 0; dt < a.n_dt; ++dt) {
         const int64_t d0 = int64_t(dt) * kDN;
@@ -827,7 +879,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
                 const bool isA = job >= NJ;
                 int ti, tj;
                 lower_tile(isA ? job - NJ : job, ti, tj);
-                mma<kDN, kDS, 1, 1, kDS>(accC[sl], (isA ? g.t.R : g.t.O) + ti * 16 * kDS, g.t.U + tj * 16 * kDS, lane);
+                mma_kc<kDN, kDS, kDS>(accC[sl], (isA ? g.t.R : g.t.O) + ti * 16 * kDS, g.t.U + tj * 16 * kDS, lane);
             }
         }
 #pragma unroll
@@ -835,9 +887,9 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             const int job = wave + 4 * sl;
             if (job < NL) {
                 const int ti = job / (LP / 16), lj = job % (LP / 16);
-                mma<kDN, kDS, 1, 1, kDS>(accQ[sl], g.t.O + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
-                mma<kDN, kDS, 1, 1, kDS>(accM[sl], g.t.R + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
-                mma<kDN, kDS, 1, 1, kDS>(accP[sl], g.t.U + ti * 16 * kDS, g.t.D + lj * 16 * kDS, lane);
+                mma_kc<kDN, kDS, kDS>(accQ[sl], g.t.O + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
+                mma_kc<kDN, kDS, kDS>(accM[sl], g.t.R + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
+                mma_kc<kDN, kDS, kDS>(accP[sl], g.t.U + ti * 16 * kDS, g.t.D + lj * 16 * kDS, lane);
             }
         }
         __syncthreads();
