@@ -806,7 +806,7 @@ def main():
                          "clocks take tens of ms of sustained load to settle)")
     from quaternion_cumprod_autodiff_amd.inputs import CONFIGS, make_config
     ap.add_argument("--config", default="headline", choices=list(CONFIGS))
-    ap.add_argument("--path", default=None, choices=["auto", "column", "chunked"])
+    ap.add_argument("--path", default=None, choices=["auto", "column", "chunked", "rscan"])
     ap.add_argument("--leaves-only", action="store_true",
                     help="backward without the saved boundary state (re-derives it from q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -97,7 +97,9 @@ enum {
 enum {
     QC_PATH_AUTO = 0,       /* library heuristic */
     QC_PATH_COLUMN = 1,     /* one lane walks a whole column sequentially */
-    QC_PATH_CHUNKED = 2     /* sequence-parallel tiles with cross-block carries */
+    QC_PATH_CHUNKED = 2,    /* sequence-parallel tiles with cross-block carries (one pass, look-back) */
+    QC_PATH_RSCAN = 3       /* the same tiles, reduce-then-scan: tile aggregates, a scan of them, a
+                               fix-up pass that re-reads the tile's inputs (never chosen by AUTO) */
 };
 
 typedef struct {

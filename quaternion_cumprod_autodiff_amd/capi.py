@@ -20,7 +20,8 @@ QC_DTYPE_BF16 = 1
 QC_PATH_AUTO = 0
 QC_PATH_COLUMN = 1
 QC_PATH_CHUNKED = 2
-PATHS = {"auto": QC_PATH_AUTO, "column": QC_PATH_COLUMN, "chunked": QC_PATH_CHUNKED}
+QC_PATH_RSCAN = 3
+PATHS = {"auto": QC_PATH_AUTO, "column": QC_PATH_COLUMN, "chunked": QC_PATH_CHUNKED, "rscan": QC_PATH_RSCAN}
 
 _DTYPES = {torch.float32: QC_DTYPE_F32, torch.bfloat16: QC_DTYPE_BF16}
 

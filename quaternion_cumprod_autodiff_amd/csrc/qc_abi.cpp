@@ -147,8 +147,11 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     const size_t slots_fwd = size_t(p->fwd.n_chains * p->fwd.n_tiles) * size_t(p->fwd.wc);
     const size_t slots_bwd = size_t(p->bwd.n_chains * p->bwd.n_tiles) * size_t(p->bwd.wc);
     const size_t slots = slots_fwd > slots_bwd ? slots_fwd : slots_bwd;
+    // The carry region holds the look-back's slots, or the reduce-then-scan
+    // variant's tile aggregates and scanned carries (one internal quaternion each).
+    const size_t desc = slots * p->slot_bytes > 2 * slots * p->ct_bytes ? slots * p->slot_bytes : 2 * slots * p->ct_bytes;
     p->off_desc = round_up(size_t(qc::kHdrWords) * 4, kAlignWs);
-    p->off_ckpt = round_up(p->off_desc + slots * p->slot_bytes, kAlignWs);
+    p->off_ckpt = round_up(p->off_desc + desc, kAlignWs);
     p->ws_bytes = round_up(p->off_ckpt + p->ckpt_bytes, kAlignWs);
     return QC_OK;
 }
@@ -177,7 +180,7 @@ bool any_alias(const Range* r, const bool* is_out, int n) {
 int check_options(const qc_options* o, int* path) {
     *path = QC_PATH_AUTO;
     if (!o) return QC_OK;
-    if (o->path < QC_PATH_AUTO || o->path > QC_PATH_CHUNKED) return QC_ERR_OPTION;
+    if (o->path < QC_PATH_AUTO || o->path > QC_PATH_RSCAN) return QC_ERR_OPTION;
     for (int i = 0; i < 7; ++i)
         if (o->reserved[i] != 0) return QC_ERR_OPTION;
     *path = o->path;
@@ -225,16 +228,23 @@ qc::KernelArgs column_args(const Plan& p, void* ws) {
     return a;
 }
 
+// The reduce-then-scan variant (three passes: tile aggregates, a scan of them,
+// a fix-up that re-reads the tile's inputs) runs only when asked for.  It has
+// no cross-block waits, but moves one more read of the inputs than the
+// look-back, and on the long single-chain shapes where its waits-free passes
+// could pay it measured slower than the look-back, so AUTO never takes it.
+bool use_rscan(int path) { return path == QC_PATH_RSCAN; }
+
 int launch_forward(const Plan& p, const void* q, const void* init, void* cum, void* ckpt, void* ws,
-                   hipStream_t st, bool column) {
+                   hipStream_t st, bool column, bool rscan) {
     qc::KernelArgs a = column ? column_args(p, ws) : base_args(p, ws, p.fwd);
     a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt;
-    if (!column) {
+    if (!column && !rscan) {
         const int rc = set_epoch(&a, st);
         if (rc != QC_OK) return rc;
     }
     const hipError_t e = column ? qc::launch_fwd_column(p.dtype, a, st)
-                                : qc::launch_fwd_chunked(p.dtype, p.fwd.wc, p.fwd.deep, a, st);
+                                : qc::launch_fwd_chunked(p.dtype, p.fwd.wc, p.fwd.deep, rscan, a, st);
     return e == hipSuccess ? QC_OK : hip_fail(e);
 }
 
@@ -284,7 +294,8 @@ int quat_cumprod_fwd_ex(const void* q, const void* init, void* cum, void* ckpt, 
     if (any_alias(rs, out, 5)) return QC_ERR_ALIAS;
 
     const bool column = path == QC_PATH_COLUMN || (path == QC_PATH_AUTO && p.n_cols >= kColumnPathMinColumns);
-    return launch_forward(p, q, init, cum, ckpt, workspace, static_cast<hipStream_t>(stream), column);
+    return launch_forward(p, q, init, cum, ckpt, workspace, static_cast<hipStream_t>(stream), column,
+                          !column && use_rscan(path));
 }
 
 int quat_cumprod_fwd(const void* q, const void* init, void* cum, void* ckpt, size_t ckpt_bytes,
@@ -329,14 +340,17 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
     if (!ck) {
         // Leaves-only backward: re-derive the boundary prefix products from q.
         ck = static_cast<char*>(workspace) + p.off_ckpt;
-        rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false);
+        rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false, use_rscan(path));
         if (rc != QC_OK) return rc;
     }
     qc::KernelArgs a = base_args(p, workspace, p.bwd);
     a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init; a.ckpt = ck;
-    rc = set_epoch(&a, st);
-    if (rc != QC_OK) return rc;
-    const hipError_t e = qc::launch_bwd_chunked(p.dtype, p.bwd.wc, p.bwd.deep, a, st);
+    const bool rscan = use_rscan(path);
+    if (!rscan) {
+        rc = set_epoch(&a, st);
+        if (rc != QC_OK) return rc;
+    }
+    const hipError_t e = qc::launch_bwd_chunked(p.dtype, p.bwd.wc, p.bwd.deep, rscan, a, st);
     return e == hipSuccess ? QC_OK : hip_fail(e);
 }
 

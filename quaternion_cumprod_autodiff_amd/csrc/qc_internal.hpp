@@ -96,8 +96,10 @@ struct KernelArgs {
     uint32_t spin_limit;
 };
 
-hipError_t launch_fwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st);
-hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st);
+// rscan: the reduce-then-scan variant (tile aggregates, a scan of them per
+// chain, a fix-up pass) instead of the single pass with the look-back.
+hipError_t launch_fwd_chunked(int dtype, int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st);
+hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st);
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st);

@@ -485,11 +485,29 @@ __device__ __forceinline__ Q4<T> tile_scan_product(const Q4<T>& A, Q4<T> (*s_wag
 
 // ------------------------------------------------------------ forward, chunked
 
+// Carries of the reduce-then-scan variant, in the workspace's carry region:
+// per (chain, tile position, column) one compute-type quaternion, the tile
+// aggregates first, then the scanned carries.
+template <typename CT, int WC>
+__device__ __forceinline__ Q4<CT>* rscan_agg(const KernelArgs& a, int64_t chain, int64_t pos, int c) {
+    return reinterpret_cast<Q4<CT>*>(a.desc) + (chain * a.n_tiles + pos) * WC + c;
+}
+template <typename CT, int WC>
+__device__ __forceinline__ Q4<CT>* rscan_carry(const KernelArgs& a, int64_t chain, int64_t pos, int c) {
+    return reinterpret_cast<Q4<CT>*>(a.desc) + (a.n_chains * a.n_tiles + chain * a.n_tiles + pos) * WC + c;
+}
+
 // kStore = false is the boundary-state pass of a backward without saved
 // state: no cum output, so q is dropped right after sweep 1 (fewer registers).
-template <class IO, int WC, int L, int NW, bool kStore>
+// kMode selects how a tile learns the product of the tiles before it:
+//   kLookback  the Fenwick look-back over published carries, in one pass;
+//   kAggregate reduce-then-scan, pass 1: only the tile's product, stored;
+//   kFixup     reduce-then-scan, pass 3: the scanned carry, read.
+enum : int { kLookback = 0, kAggregate = 1, kFixup = 2 };
+
+template <class IO, int WC, int L, int NW, bool kStore, int kMode>
 __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
-    a.epoch = launch_epoch(a);
+    if constexpr (kMode == kLookback) a.epoch = launch_epoch(a);
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
@@ -515,8 +533,11 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     }
     Raw init_raw = IO::one_raw();
     if (kStore && tc.col_ok) init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
-    Q4<CT> pre_v;
-    const bool pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
+    Q4<CT> pre_v = q_one<CT>();
+    bool pre_ok = false;
+    if constexpr (kMode == kLookback) pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
+    Q4<CT> Et = q_one<CT>();
+    if constexpr (kMode == kFixup) Et = *rscan_carry<CT, WC>(a, tc.chain, tc.pos, c);
 
     // Slice product: A = q_{t0+L-1} (x) ... (x) q_{t0}.
     Q4<CT> A = IO::ct(qv[0]);
@@ -525,8 +546,13 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 
     Q4<CT> tile_agg;
     const Q4<CT> F = tile_scan_product<CT, WC, NW>(A, s_wagg, wave, r, c, &tile_agg);
-    const Q4<CT> Et = fenwick_exclusive<CT, WC, NW, true>(a, tc.chain, tc.pos, tile_agg, wave == NW - 1, wave, r, c,
-                                                           pre_v, pre_ok, s_nodes, s_ok, s_carry);
+    if constexpr (kMode == kAggregate) {
+        if (wave == NW - 1 && r == 0) *rscan_agg<CT, WC>(a, tc.chain, tc.pos, c) = tile_agg;
+        return;
+    }
+    if constexpr (kMode == kLookback)
+        Et = fenwick_exclusive<CT, WC, NW, true>(a, tc.chain, tc.pos, tile_agg, wave == NW - 1, wave, r, c, pre_v,
+                                                 pre_ok, s_nodes, s_ok, s_carry);
     const Q4<CT> Ps = qmul(F, Et);   // P_{t0-1}: prefix product before this slice
 
     if (a.ckpt != nullptr && tc.col_ok && tc.t0 < a.s && (tc.t0 % kCkptStride) == 0)
@@ -584,9 +610,9 @@ constexpr int bwd_min_waves() {
     return L * 2 * int(sizeof(typename IO::Raw)) / 4 <= 64 ? 3 : 2;
 }
 
-template <class IO, int WC, int L, int NW>
+template <class IO, int WC, int L, int NW, int kMode>
 __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked_kernel(KernelArgs a) {
-    a.epoch = launch_epoch(a);
+    if constexpr (kMode == kLookback) a.epoch = launch_epoch(a);
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
@@ -608,14 +634,18 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             qv[i] = IO::load(a.q, tc.base + int64_t(i) * a.M);
-            dv[i] = IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M);
+            // The reduce-then-scan passes read d_cum twice: keep it cached.
+            dv[i] = kMode == kLookback ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M)
+                                       : IO::load(a.d_cum, tc.base + int64_t(i) * a.M);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const bool ok = tc.col_ok && tc.t0 + i < a.s;
             qv[i] = ok ? IO::load(a.q, tc.base + int64_t(i) * a.M) : IO::one_raw();
-            dv[i] = ok ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M) : IO::zero_raw();
+            dv[i] = ok ? (kMode == kLookback ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M)
+                                             : IO::load(a.d_cum, tc.base + int64_t(i) * a.M))
+                       : IO::zero_raw();
         }
     }
     // Prefix product before the tile (saved boundary state) and the initial carry.
@@ -626,8 +656,11 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
         Et = reinterpret_cast<const Q4<CT>*>(a.ckpt)[(tc.bi * a.n_ck + tile_t0 / kCkptStride) * a.M + tc.m];
         init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
     }
-    Q4<CT> pre_v;
-    const bool pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, k, c, &pre_v);
+    Q4<CT> pre_v = q_zero<CT>();
+    bool pre_ok = false;
+    if constexpr (kMode == kLookback) pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, k, c, &pre_v);
+    Q4<CT> Sa = q_zero<CT>();
+    if constexpr (kMode == kFixup) Sa = *rscan_carry<CT, WC>(a, tc.chain, tc.pos, c);
 
     // Sweep 1: slice product and slice share, frame of the slice start.
     Q4<CT> Ql = IO::ct(qv[0]);
@@ -658,8 +691,13 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
     // publishes it): conj(E) (x) (Y_0 + conj(Q_0) (x) R'_0).
     Q4<CT> Yg = q_zero<CT>();
     if (wave == 0) Yg = qcmul(Et, qadd(Yl, qcmul(Ql, Rp)));
-    const Q4<CT> Sa = fenwick_exclusive<CT, WC, NW, false>(a, tc.chain, tc.pos, Yg, wave == 0, wave, r, c, pre_v,
-                                                            pre_ok, s_nodes, s_ok, s_after);
+    if constexpr (kMode == kAggregate) {
+        if (wave == 0 && r == 0) *rscan_agg<CT, WC>(a, tc.chain, tc.pos, c) = Yg;
+        return;
+    }
+    if constexpr (kMode == kLookback)
+        Sa = fenwick_exclusive<CT, WC, NW, false>(a, tc.chain, tc.pos, Yg, wave == 0, wave, r, c, pre_v, pre_ok,
+                                                  s_nodes, s_ok, s_after);
 
     if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok)
         IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Yg, Sa));   // S[0] (slice 0 of the first tile, E = 1)
@@ -777,6 +815,53 @@ __global__ void __launch_bounds__(kColumnBlock) bwd_column_kernel(KernelArgs a) 
         __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusZeroPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Reduce-then-scan, pass 2: one block per chain scans its tiles' aggregates
+// into exclusive carries.  Thread (segment, column) walks a contiguous run of
+// tiles for its column, loading them in batches so that the loads overlap;
+// the runs' totals meet in LDS.  Forward: products in left-multiply order
+// (later factor on the left), identity first.  Backward: plain sums (the
+// tiles are already in reverse time order), zero first.
+template <int WC>
+constexpr int rscan_segments() { return WC >= 16 ? 1024 / WC : 64; }
+
+template <typename CT, int WC, bool kProduct>
+__global__ void __launch_bounds__(rscan_segments<WC>() * WC) rscan_kernel(KernelArgs a) {
+    constexpr int NSEG = rscan_segments<WC>();
+    constexpr int B = 8;
+    __shared__ Q4<CT> s_run[NSEG][WC];
+    const int c = threadIdx.x % WC, seg = threadIdx.x / WC;
+    const int64_t chain = blockIdx.x;
+    const int64_t per = (a.n_tiles + NSEG - 1) / NSEG;
+    const int64_t lo = seg * per < a.n_tiles ? seg * per : a.n_tiles;
+    const int64_t hi = lo + per < a.n_tiles ? lo + per : a.n_tiles;
+    const Q4<CT> id = kProduct ? q_one<CT>() : q_zero<CT>();
+    Q4<CT> run = id;
+    for (int64_t i0 = lo; i0 < hi; i0 += B) {
+        Q4<CT> v[B];
+#pragma unroll
+        for (int k = 0; k < B; ++k) v[k] = *rscan_agg<CT, WC>(a, chain, i0 + k < hi ? i0 + k : hi - 1, c);
+#pragma unroll
+        for (int k = 0; k < B; ++k)
+            if (i0 + k < hi) run = kProduct ? qmul(v[k], run) : qadd(run, v[k]);
+    }
+    s_run[seg][c] = run;
+    __syncthreads();
+    Q4<CT> p = id;
+    for (int k = 0; k < seg; ++k) p = kProduct ? qmul(s_run[k][c], p) : qadd(p, s_run[k][c]);
+    for (int64_t i0 = lo; i0 < hi; i0 += B) {
+        Q4<CT> v[B];
+#pragma unroll
+        for (int k = 0; k < B; ++k) v[k] = *rscan_agg<CT, WC>(a, chain, i0 + k < hi ? i0 + k : hi - 1, c);
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+            if (i0 + k < hi) {
+                *rscan_carry<CT, WC>(a, chain, i0 + k, c) = p;
+                p = kProduct ? qmul(v[k], p) : qadd(p, v[k]);
+            }
+        }
+    }
+}
+
 __global__ void bump_epoch_kernel(uint32_t* hdr) {
     if (threadIdx.x == 0)
         __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(hdr + kHdrEpoch), uint64_t(1), __ATOMIC_RELAXED,
@@ -790,8 +875,8 @@ __global__ void zero_words_kernel(uint32_t* p, size_t n) {
 
 // ------------------------------------------------------------------ launchers
 
-template <class IO, int WC>
-hipError_t launch_fwd_wc(bool deep, const KernelArgs& a, hipStream_t st) {
+template <class IO, int WC, int kMode>
+hipError_t launch_fwd_mode(bool deep, const KernelArgs& a, hipStream_t st) {
     constexpr Geometry g = geometry_for(WC, IO::kDtype);
     static_assert(kCkptStride % g.fwd_l == 0 && kCkptStride % g.fwd_deep_l == 0,
                   "a forward slice must start on every saved boundary");
@@ -799,61 +884,88 @@ hipError_t launch_fwd_wc(bool deep, const KernelArgs& a, hipStream_t st) {
     void* params[] = {&args};
     const bool store = a.out != nullptr;
     const void* fn =
-        deep ? (store ? reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_deep_l, g.fwd_nw, true>)
-                      : reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_deep_l, g.fwd_nw, false>))
-             : (store ? reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, true>)
-                      : reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, false>));
+        deep ? (store ? reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_deep_l, g.fwd_nw, true, kMode>)
+                      : reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_deep_l, g.fwd_nw, false, kMode>))
+             : (store ? reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, true, kMode>)
+                      : reinterpret_cast<const void*>(&fwd_chunked_kernel<IO, WC, g.fwd_l, g.fwd_nw, false, kMode>));
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(g.fwd_nw * 64), params, 0, st);
 }
 
-template <class IO, int WC>
-hipError_t launch_bwd_wc(bool deep, const KernelArgs& a, hipStream_t st) {
+template <class IO, int WC, int kMode>
+hipError_t launch_bwd_mode(bool deep, const KernelArgs& a, hipStream_t st) {
     constexpr Geometry g = geometry_for(WC, IO::kDtype);
     static_assert(bwd_tile_steps(WC, IO::kDtype, false) % kCkptStride == 0, "backward tiles start on saved boundaries");
     static_assert(bwd_tile_steps(WC, IO::kDtype, true) % kCkptStride == 0, "backward tiles start on saved boundaries");
     KernelArgs args = a;
     void* params[] = {&args};
-    const void* fn = deep ? reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_deep_l, g.bwd_nw>)
-                          : reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_l, g.bwd_nw>);
+    const void* fn = deep ? reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_deep_l, g.bwd_nw, kMode>)
+                          : reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_l, g.bwd_nw, kMode>);
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(g.bwd_nw * 64), params, 0, st);
 }
 
+template <class IO, int WC, bool kProduct>
+hipError_t launch_rscan(const KernelArgs& a, hipStream_t st) {
+    KernelArgs args = a;
+    void* params[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&rscan_kernel<typename IO::CT, WC, kProduct>),
+                           dim3(unsigned(a.n_chains)), dim3(rscan_segments<WC>() * WC), params, 0, st);
+}
+
+// One pass with the look-back, or the three reduce-then-scan passes.
+template <class IO, int WC>
+hipError_t launch_fwd_wc(bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
+    if (!rscan) return launch_fwd_mode<IO, WC, kLookback>(deep, a, st);
+    hipError_t e = launch_fwd_mode<IO, WC, kAggregate>(deep, a, st);
+    if (e == hipSuccess) e = launch_rscan<IO, WC, true>(a, st);
+    if (e == hipSuccess) e = launch_fwd_mode<IO, WC, kFixup>(deep, a, st);
+    return e;
+}
+
+template <class IO, int WC>
+hipError_t launch_bwd_wc(bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
+    if (!rscan) return launch_bwd_mode<IO, WC, kLookback>(deep, a, st);
+    hipError_t e = launch_bwd_mode<IO, WC, kAggregate>(deep, a, st);
+    if (e == hipSuccess) e = launch_rscan<IO, WC, false>(a, st);
+    if (e == hipSuccess) e = launch_bwd_mode<IO, WC, kFixup>(deep, a, st);
+    return e;
+}
+
 template <class IO>
-hipError_t launch_fwd_io(int wc, bool deep, const KernelArgs& a, hipStream_t st) {
+hipError_t launch_fwd_io(int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
     switch (wc) {
-        case 64: return launch_fwd_wc<IO, 64>(deep, a, st);
-        case 32: return launch_fwd_wc<IO, 32>(deep, a, st);
-        case 16: return launch_fwd_wc<IO, 16>(deep, a, st);
-        case 8: return launch_fwd_wc<IO, 8>(deep, a, st);
-        case 4: return launch_fwd_wc<IO, 4>(deep, a, st);
-        case 2: return launch_fwd_wc<IO, 2>(deep, a, st);
-        case 1: return launch_fwd_wc<IO, 1>(deep, a, st);
+        case 64: return launch_fwd_wc<IO, 64>(deep, rscan, a, st);
+        case 32: return launch_fwd_wc<IO, 32>(deep, rscan, a, st);
+        case 16: return launch_fwd_wc<IO, 16>(deep, rscan, a, st);
+        case 8: return launch_fwd_wc<IO, 8>(deep, rscan, a, st);
+        case 4: return launch_fwd_wc<IO, 4>(deep, rscan, a, st);
+        case 2: return launch_fwd_wc<IO, 2>(deep, rscan, a, st);
+        case 1: return launch_fwd_wc<IO, 1>(deep, rscan, a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <class IO>
-hipError_t launch_bwd_io(int wc, bool deep, const KernelArgs& a, hipStream_t st) {
+hipError_t launch_bwd_io(int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
     switch (wc) {
-        case 64: return launch_bwd_wc<IO, 64>(deep, a, st);
-        case 32: return launch_bwd_wc<IO, 32>(deep, a, st);
-        case 16: return launch_bwd_wc<IO, 16>(deep, a, st);
-        case 8: return launch_bwd_wc<IO, 8>(deep, a, st);
-        case 4: return launch_bwd_wc<IO, 4>(deep, a, st);
-        case 2: return launch_bwd_wc<IO, 2>(deep, a, st);
-        case 1: return launch_bwd_wc<IO, 1>(deep, a, st);
+        case 64: return launch_bwd_wc<IO, 64>(deep, rscan, a, st);
+        case 32: return launch_bwd_wc<IO, 32>(deep, rscan, a, st);
+        case 16: return launch_bwd_wc<IO, 16>(deep, rscan, a, st);
+        case 8: return launch_bwd_wc<IO, 8>(deep, rscan, a, st);
+        case 4: return launch_bwd_wc<IO, 4>(deep, rscan, a, st);
+        case 2: return launch_bwd_wc<IO, 2>(deep, rscan, a, st);
+        case 1: return launch_bwd_wc<IO, 1>(deep, rscan, a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st) {
-    return dtype == 0 ? launch_fwd_io<IoF32>(wc, deep, a, st) : launch_fwd_io<IoBF16>(wc, deep, a, st);
+hipError_t launch_fwd_chunked(int dtype, int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
+    return dtype == 0 ? launch_fwd_io<IoF32>(wc, deep, rscan, a, st) : launch_fwd_io<IoBF16>(wc, deep, rscan, a, st);
 }
 
-hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st) {
-    return dtype == 0 ? launch_bwd_io<IoF32>(wc, deep, a, st) : launch_bwd_io<IoBF16>(wc, deep, a, st);
+hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
+    return dtype == 0 ? launch_bwd_io<IoF32>(wc, deep, rscan, a, st) : launch_bwd_io<IoBF16>(wc, deep, rscan, a, st);
 }
 
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st) {

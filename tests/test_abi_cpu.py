@@ -160,7 +160,7 @@ def test_aliasing(lib):
 
 def test_options(lib):
     o = capi.QcOptions()
-    o.path = 3
+    o.path = 4
     assert fwd(lib, opts=ctypes.byref(o)) == E_OPT
     o.path = 0
     o.reserved[2] = 1

@@ -30,6 +30,8 @@ CASES = [
     (2, 3000, 4, 8, "unit", "bf16", "chunked", True),
     (1, 20000, 1, 4, "drift", "f32", "chunked", True),
     (4, 700, 8, 8, "unit", "f32", "column", True),
+    (1, 30000, 2, 8, "unit", "f32", "rscan", True),
+    (1, 30000, 2, 8, "unit", "f32", "rscan", False),
 ]
 REPLAYS = 4
 

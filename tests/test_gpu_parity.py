@@ -120,7 +120,8 @@ def test_config_full_parity(name, use_ckpt):
 
 
 @pytest.mark.parametrize("name", ["tiny", "medium"])
-@pytest.mark.parametrize("path,use_ckpt", [("chunked", False), ("column", True), ("column", False)])
+@pytest.mark.parametrize("path,use_ckpt", [("chunked", False), ("column", True), ("column", False),
+                                           ("rscan", True), ("rscan", False)])
 def test_config_other_paths(name, path, use_ckpt):
     print(f"[config {name} path={path} ckpt={use_ckpt}]", flush=True)
     compare(make_config(name), path=path, use_ckpt=use_ckpt)
@@ -133,7 +134,7 @@ EDGE_HJ = [(1, 1), (1, 3), (4, 4), (4, 8), (8, 8), (5, 13), (10, 10)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("path", ["chunked", "column"])
+@pytest.mark.parametrize("path", ["chunked", "column", "rscan"])
 def test_edge_shapes(dtype, path):
     for s in EDGE_S:
         for (h, j) in EDGE_HJ:
@@ -168,8 +169,10 @@ def test_many_tiles_ragged(s, hj):
     """Chains of many tiles (deep carry trees) with ragged tails and partial column groups."""
     inp = make_inputs(2, s, hj[0], hj[1], "unit", "f32", seed=s)
     print(f"[ragged s={s} hj={hj}]", flush=True)
-    compare(inp, path="chunked")
-    compare(inp, path="chunked", use_ckpt=False)
+    ref = reference(inp)
+    for path in ("chunked", "rscan"):
+        compare(inp, path=path, ref=ref)
+        compare(inp, path=path, use_ckpt=False, ref=ref)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -179,8 +182,10 @@ def test_wide_forward_groups(dtype, b, s, h, j):
     tiles: partial groups (h*j not a multiple of 64) and ragged tails."""
     inp = make_inputs(b, s, h, j, "unit", dtype, seed=b + s + h * j)
     print(f"[wide b={b} s={s} h={h} j={j} {dtype}]", flush=True)
-    compare(inp)
-    compare(inp, use_ckpt=False)
+    ref = reference(inp)
+    compare(inp, ref=ref)
+    compare(inp, use_ckpt=False, ref=ref)
+    compare(inp, path="rscan", ref=ref)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -302,7 +307,7 @@ def test_workspace_reuse_small_then_large_shapes():
         compare(inp, path="chunked", use_ckpt=False)
 
 
-@pytest.mark.parametrize("path", ["chunked", "column"])
+@pytest.mark.parametrize("path", ["chunked", "column", "rscan"])
 def test_zero_step_is_reported(path):
     """A step that is exactly zero makes every later prefix product zero: the
     forward stays exact, and the backward (whose exact form divides by |P_t|^2)
@@ -320,3 +325,17 @@ def test_zero_step_is_reported(path):
     capi.quat_cumprod_bwd(q, init, d, ck, path=path, workspace=ws)
     assert ws.status(q.device) == 2            # QC_STATUS_ZERO, and cleared by the read
     assert ws.status(q.device) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rscan_and_lookback_agree_on_long_chains(dtype):
+    """Few long chains (the long-sequence shape, scaled down): the
+    reduce-then-scan passes and the one-pass look-back give the same results
+    to rounding, and both match the oracle, with and without saved state."""
+    for (b, s, h, j) in [(1, 70000, 2, 8), (2, 40000, 1, 3), (3, 33333, 1, 1)]:
+        inp = make_inputs(b, s, h, j, "unit", dtype, seed=s + h * j)
+        print(f"[long chains b={b} s={s} h={h} j={j} {dtype}]", flush=True)
+        ref = reference(inp)
+        for path in ("rscan", "chunked"):
+            for use_ckpt in (True, False):
+                compare(inp, path=path, use_ckpt=use_ckpt, ref=ref)
