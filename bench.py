@@ -807,6 +807,7 @@ def main():
     from quaternion_cumprod_autodiff_amd.inputs import CONFIGS, make_config
     ap.add_argument("--config", default="headline", choices=list(CONFIGS))
     ap.add_argument("--path", default=None, choices=["auto", "column", "chunked", "rscan"])
+    ap.add_argument("--lookback", default=None, choices=["auto", "fenwick", "grouped"])
     ap.add_argument("--leaves-only", action="store_true",
                     help="backward without the saved boundary state (re-derives it from q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -907,10 +908,10 @@ def main():
     ckpt = None if args.leaves_only else capi.new_ckpt(q)
 
     def fwd():
-        capi.quat_cumprod_fwd(q, init, cum, ckpt, path=args.path)
+        capi.quat_cumprod_fwd(q, init, cum, ckpt, path=args.path, lookback=args.lookback)
 
     def bwd():
-        capi.quat_cumprod_bwd(q, init, d_cum, ckpt, d_q=d_q, d_init=d_init, path=args.path)
+        capi.quat_cumprod_bwd(q, init, d_cum, ckpt, d_q=d_q, d_init=d_init, path=args.path, lookback=args.lookback)
 
     # Untimed warm-up: W steps, continued until --settle-ms has passed.
     warm_steps, t0 = 0, time.perf_counter()
@@ -968,10 +969,10 @@ def main():
     leaves = None
     if not args.leaves_only and args.leaves_steps > 0:
         def fwd_lo():
-            capi.quat_cumprod_fwd(q, init, cum, None, path=args.path)
+            capi.quat_cumprod_fwd(q, init, cum, None, path=args.path, lookback=args.lookback)
 
         def bwd_lo():
-            capi.quat_cumprod_bwd(q, init, d_cum, None, d_q=d_q, d_init=d_init, path=args.path)
+            capi.quat_cumprod_bwd(q, init, d_cum, None, d_q=d_q, d_init=d_init, path=args.path, lookback=args.lookback)
 
         for _ in range(10):
             fwd_lo()
@@ -996,7 +997,8 @@ def main():
     bwd_ms_roof = bwd_ms if bwd_ms is not None else bwd_ms_diag
     bwd_gbps = bwd_bytes / (bwd_ms_roof * 1e-3) / 1e9
     workload = f"{args.config} b{b} s{s} h{h} j{j} {io} I/O, forward + backward"
-    traffic = load_traffic(workload) if (args.path in (None, "auto", "chunked") and not args.leaves_only) else None
+    traffic = (load_traffic(workload) if (args.path in (None, "auto", "chunked") and args.lookback in (None, "auto")
+                                          and not args.leaves_only) else None)
 
     rec = {
         "metric": METRIC,
@@ -1012,7 +1014,7 @@ def main():
         "dtype": "f64" if io == "f32" else "f32",
         "data": "synthetic",
         "config": {"workload": workload, "b": b, "s": s, "h": h, "j": j, "io_dtype": io, "recipe": recipe,
-                   "path": args.path or "auto",
+                   "path": args.path or "auto", "lookback": args.lookback or "auto",
                    "backward": "leaves-only" if args.leaves_only else "saved boundary state"},
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "elements_per_s": round(n / (ms_step * 1e-3), 1),

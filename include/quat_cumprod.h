@@ -102,9 +102,20 @@ enum {
                                fix-up pass that re-reads the tile's inputs (never chosen by AUTO) */
 };
 
+/* Cross-tile carry scheme of the look-back path (QC_PATH_AUTO / QC_PATH_CHUNKED). */
+enum {
+    QC_LOOKBACK_AUTO = 0,     /* library heuristic */
+    QC_LOOKBACK_FENWICK = 1,  /* each tile reads about log2(position) published partial products */
+    QC_LOOKBACK_GROUPED = 2   /* tiles and groups of about sqrt(tiles) publish their aggregates; a
+                                 tile reads its group's earlier tiles and the earlier groups (two
+                                 publish-to-read round trips deep; AUTO takes it for launches of
+                                 at most a few thousand tiles) */
+};
+
 typedef struct {
     int32_t path;           /* QC_PATH_* */
-    int32_t reserved[7];    /* must be zero */
+    int32_t lookback;       /* QC_LOOKBACK_*; ignored by the other paths */
+    int32_t reserved[6];    /* must be zero */
 } qc_options;
 
 /* Bytes of workspace that quat_cumprod_fwd and quat_cumprod_bwd need for this

@@ -22,6 +22,8 @@ QC_PATH_COLUMN = 1
 QC_PATH_CHUNKED = 2
 QC_PATH_RSCAN = 3
 PATHS = {"auto": QC_PATH_AUTO, "column": QC_PATH_COLUMN, "chunked": QC_PATH_CHUNKED, "rscan": QC_PATH_RSCAN}
+# Cross-tile carry scheme of the look-back path (QC_LOOKBACK_*).
+LOOKBACKS = {"auto": 0, "fenwick": 1, "grouped": 2}
 
 _DTYPES = {torch.float32: QC_DTYPE_F32, torch.bfloat16: QC_DTYPE_BF16}
 
@@ -42,7 +44,7 @@ EXPORTS = (
 
 
 class QcOptions(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("path", ctypes.c_int32), ("lookback", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
 
 
 class QcScanPlan(ctypes.Structure):
@@ -178,11 +180,12 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _options(path: str | None):
-    if path is None:
+def _options(path: str | None, lookback: str | None = None):
+    if path is None and lookback is None:
         return None
     o = QcOptions()
-    o.path = PATHS[path]
+    o.path = PATHS[path or "auto"]
+    o.lookback = LOOKBACKS[lookback or "auto"]
     return ctypes.byref(o)
 
 
@@ -330,8 +333,8 @@ def new_ckpt(q: torch.Tensor) -> torch.Tensor:
 
 
 def quat_cumprod_fwd(q: torch.Tensor, init: torch.Tensor, cum: torch.Tensor | None = None,
-                     ckpt: torch.Tensor | None = None, *, path: str | None = None, stream=None,
-                     workspace: Workspace | None = None) -> torch.Tensor:
+                     ckpt: torch.Tensor | None = None, *, path: str | None = None, lookback: str | None = None,
+                     stream=None, workspace: Workspace | None = None) -> torch.Tensor:
     """cum[t] = q_t (x) cum[t-1], cum[-1] = init (device computation).
 
     If ``ckpt`` (from :func:`new_ckpt`) is given, the boundary state for the
@@ -348,7 +351,7 @@ def quat_cumprod_fwd(q: torch.Tensor, init: torch.Tensor, cum: torch.Tensor | No
     ws = (workspace or default_workspace).get(workspace_bytes(b, s, h, j, q.dtype), q.device, stream)
     rc = load().quat_cumprod_fwd_ex(_ptr(q), _ptr(init), _ptr(cum), _ptr(ckpt),
                                     0 if ckpt is None else ckpt.numel() * ckpt.element_size(),
-                                    b, s, h, j, dt, _ptr(ws), ws.numel(), _stream(stream), _options(path))
+                                    b, s, h, j, dt, _ptr(ws), ws.numel(), _stream(stream), _options(path, lookback))
     _check(rc, "quat_cumprod_fwd")
     return cum
 
@@ -356,7 +359,8 @@ def quat_cumprod_fwd(q: torch.Tensor, init: torch.Tensor, cum: torch.Tensor | No
 def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
                      ckpt: torch.Tensor | None = None, *, want_dq: bool = True, want_dinit: bool = True,
                      d_q: torch.Tensor | None = None, d_init: torch.Tensor | None = None,
-                     path: str | None = None, stream=None, workspace: Workspace | None = None):
+                     path: str | None = None, lookback: str | None = None, stream=None,
+                     workspace: Workspace | None = None):
     """VJP of the scan: returns (d_q, d_init); an unwanted output is None."""
     b, s, h, j = _dims(q)
     dt = _dtype_code(q)
@@ -378,7 +382,7 @@ def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
     rc = load().quat_cumprod_bwd_ex(_ptr(q), _ptr(init), _ptr(d_cum), _ptr(ckpt),
                                     0 if ckpt is None else ckpt.numel() * ckpt.element_size(),
                                     _ptr(d_q), _ptr(d_init), b, s, h, j, dt, _ptr(ws), ws.numel(),
-                                    _stream(stream), _options(path))
+                                    _stream(stream), _options(path, lookback))
     _check(rc, "quat_cumprod_bwd")
     return d_q, d_init
 

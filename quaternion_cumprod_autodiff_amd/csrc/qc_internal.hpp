@@ -91,6 +91,8 @@ struct KernelArgs {
     int64_t n_cg;         // column groups per batch entry
     int64_t n_chains;     // b * n_cg
     int64_t n_tiles;      // tiles per chain
+    int64_t group;        // grouped look-back: tiles per group (0: the Fenwick look-back)
+    int64_t n_groups;     // groups per chain (grouped look-back)
     uint64_t epoch;       // this launch's epoch, folded into every check word (0: read it from the header)
     uint32_t n_blocks;    // grid size
     uint32_t spin_limit;

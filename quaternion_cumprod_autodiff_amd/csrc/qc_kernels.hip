@@ -419,6 +419,103 @@ __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t p
     return s_out[c];
 }
 
+// Grouped look-back, for chains whose tiles are mostly in flight at once
+// (few, long chains), where the Fenwick query's depth of about log2(tiles)
+// publish-then-poll round trips is exposed instead of hidden behind other
+// tiles' streaming.  Tiles form groups of G = a.group consecutive positions.
+// Every tile publishes its own aggregate as soon as it has it; the last tile
+// of each group (unless it is in the chain's last group) also publishes the
+// group's aggregate once it has read the rest of its group.  Tile p = gG + k
+// then combines, nearest first, the aggregates of tiles p-1 .. gG and of
+// groups g-1 .. 0: two round trips deep, at the price of up to
+// (G - 1) + (groups - 1) node reads per tile instead of about log2(p).
+// Node layout: tile aggregates at chain * n_tiles + p (as the Fenwick nodes),
+// group aggregates after all of those, at n_chains * n_tiles + chain * n_groups + g.
+// Item t of tile p's read list is the tile node p-1-t for t < k, else the
+// group node g-1-(t-k).
+template <typename T, int WC>
+__device__ __forceinline__ SlotWord* grouped_node(const KernelArgs& a, int64_t chain, int64_t pos, int64_t t, int c) {
+    const int64_t k = pos % a.group;
+    const int64_t node = t < k ? chain * a.n_tiles + pos - 1 - t
+                               : a.n_chains * a.n_tiles + chain * a.n_groups + pos / a.group - 1 - (t - k);
+    return slot_ptr<T, WC>(a, node, c);
+}
+
+// First-round read attempt of the Fenwick look-back (the grouped one reads
+// its nodes when it gets there).
+template <typename T, int WC, int NW, bool kGrouped>
+__device__ __forceinline__ bool lookback_prefetch(const KernelArgs& a, int64_t chain, int64_t pos, int slot, int c,
+                                                  Q4<T>* v) {
+    if constexpr (kGrouped) return false;
+    return fenwick_prefetch<T, WC, NW>(a, chain, pos, slot, c, v);
+}
+
+// Combination, in list order, of items [lo, hi) of the read list: this lane
+// slot takes a contiguous run of them (a few items), waiting for each in turn.
+template <typename T, int WC, int PAR, bool kProduct>
+__device__ Q4<T> grouped_run(const KernelArgs& a, int64_t chain, int64_t pos, int64_t lo, int64_t hi, int slot,
+                             int c) {
+    const int64_t per = (hi - lo + PAR - 1) / PAR;
+    const int64_t r0 = lo + slot * per < hi ? lo + slot * per : hi;
+    const int64_t r1 = r0 + per < hi ? r0 + per : hi;
+    Q4<T> part = kProduct ? q_one<T>() : q_zero<T>();
+    for (int64_t t = r0; t < r1; ++t) {
+        const Q4<T> v = wait_read<T, WC>(a, grouped_node<T, WC>(a, chain, pos, t, c));
+        part = kProduct ? qmul(part, v) : qadd(part, v);
+    }
+    return part;
+}
+
+// Same contract as fenwick_exclusive (pre_v / pre_ok unused).
+template <typename T, int WC, int NW, bool kProduct>
+__device__ Q4<T> grouped_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const Q4<T>& own,
+                                   bool own_wave, int wave, int r, int c, Q4<T> (*s_nodes)[WC], Q4<T>* s_out) {
+    constexpr int R = 64 / WC;
+    constexpr int PAR = NW * R;
+    const int64_t k = pos % a.group, g = pos / a.group;
+    const int slot = wave * R + r;
+    // Nothing reads the chain's last tile, nor the last group.
+    if (own_wave && pos + 1 < a.n_tiles) publish<T, WC>(a, slot_ptr<T, WC>(a, chain * a.n_tiles + pos, c), own, r == 0);
+    // Phase 1, the group's earlier tiles: the group's last tile publishes the
+    // group aggregate from them before it waits on anything else.
+    s_nodes[slot][c] = grouped_run<T, WC, PAR, kProduct>(a, chain, pos, 0, k, slot, c);
+    __syncthreads();
+    Q4<T> acc = kProduct ? q_one<T>() : q_zero<T>();
+    if (own_wave) {
+#pragma unroll 2
+        for (int j = 0; j < PAR; ++j) acc = kProduct ? qmul(acc, s_nodes[j][c]) : qadd(acc, s_nodes[j][c]);
+        if (k == a.group - 1 && g + 1 < a.n_groups)
+            publish<T, WC>(a, slot_ptr<T, WC>(a, a.n_chains * a.n_tiles + chain * a.n_groups + g, c),
+                           kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
+    }
+    __syncthreads();
+    // Phase 2, the earlier groups.
+    s_nodes[slot][c] = grouped_run<T, WC, PAR, kProduct>(a, chain, pos, k, k + g, slot, c);
+    __syncthreads();
+    if (own_wave) {
+#pragma unroll 2
+        for (int j = 0; j < PAR; ++j) acc = kProduct ? qmul(acc, s_nodes[j][c]) : qadd(acc, s_nodes[j][c]);
+        if (r == 0) s_out[c] = acc;
+    }
+    __syncthreads();
+    return s_out[c];
+}
+
+// The two look-backs are separate kernel instances: the scan kernels hold
+// their tile in registers across the look-back, and code for both would
+// raise every instance's register count.
+template <typename T, int WC, int NW, bool kProduct, bool kGrouped>
+__device__ __forceinline__ Q4<T> lookback_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const Q4<T>& own,
+                                                    bool own_wave, int wave, int r, int c, const Q4<T>& pre_v,
+                                                    bool pre_ok, Q4<T> (*s_nodes)[WC], uint8_t (*s_ok)[WC],
+                                                    Q4<T>* s_out) {
+    if constexpr (kGrouped)
+        return grouped_exclusive<T, WC, NW, kProduct>(a, chain, pos, own, own_wave, wave, r, c, s_nodes, s_out);
+    else
+        return fenwick_exclusive<T, WC, NW, kProduct>(a, chain, pos, own, own_wave, wave, r, c, pre_v, pre_ok,
+                                                      s_nodes, s_ok, s_out);
+}
+
 // The launch epoch: from the arguments, or (launches captured in a graph,
 // epoch 0) from the header counter that a one-thread kernel bumped just
 // before, read coherently and made wave-uniform.
@@ -501,13 +598,15 @@ __device__ __forceinline__ Q4<CT>* rscan_carry(const KernelArgs& a, int64_t chai
 // state: no cum output, so q is dropped right after sweep 1 (fewer registers).
 // kMode selects how a tile learns the product of the tiles before it:
 //   kLookback  the Fenwick look-back over published carries, in one pass;
+//   kGrouped   the grouped look-back, in one pass;
 //   kAggregate reduce-then-scan, pass 1: only the tile's product, stored;
 //   kFixup     reduce-then-scan, pass 3: the scanned carry, read.
-enum : int { kLookback = 0, kAggregate = 1, kFixup = 2 };
+enum : int { kLookback = 0, kAggregate = 1, kFixup = 2, kGrouped = 3 };
+constexpr bool one_pass(int mode) { return mode == kLookback || mode == kGrouped; }
 
 template <class IO, int WC, int L, int NW, bool kStore, int kMode>
 __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
-    if constexpr (kMode == kLookback) a.epoch = launch_epoch(a);
+    if constexpr (one_pass(kMode)) a.epoch = launch_epoch(a);
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
@@ -535,7 +634,8 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     if (kStore && tc.col_ok) init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
     Q4<CT> pre_v = q_one<CT>();
     bool pre_ok = false;
-    if constexpr (kMode == kLookback) pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
+    if constexpr (one_pass(kMode))
+        pre_ok = lookback_prefetch<CT, WC, NW, kMode == kGrouped>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
     Q4<CT> Et = q_one<CT>();
     if constexpr (kMode == kFixup) Et = *rscan_carry<CT, WC>(a, tc.chain, tc.pos, c);
 
@@ -550,8 +650,8 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
         if (wave == NW - 1 && r == 0) *rscan_agg<CT, WC>(a, tc.chain, tc.pos, c) = tile_agg;
         return;
     }
-    if constexpr (kMode == kLookback)
-        Et = fenwick_exclusive<CT, WC, NW, true>(a, tc.chain, tc.pos, tile_agg, wave == NW - 1, wave, r, c, pre_v,
+    if constexpr (one_pass(kMode))
+        Et = lookback_exclusive<CT, WC, NW, true, kMode == kGrouped>(a, tc.chain, tc.pos, tile_agg, wave == NW - 1, wave, r, c, pre_v,
                                                  pre_ok, s_nodes, s_ok, s_carry);
     const Q4<CT> Ps = qmul(F, Et);   // P_{t0-1}: prefix product before this slice
 
@@ -612,7 +712,7 @@ constexpr int bwd_min_waves() {
 
 template <class IO, int WC, int L, int NW, int kMode>
 __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked_kernel(KernelArgs a) {
-    if constexpr (kMode == kLookback) a.epoch = launch_epoch(a);
+    if constexpr (one_pass(kMode)) a.epoch = launch_epoch(a);
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
     constexpr int R = 64 / WC;
@@ -635,7 +735,7 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
         for (int i = 0; i < L; ++i) {
             qv[i] = IO::load(a.q, tc.base + int64_t(i) * a.M);
             // The reduce-then-scan passes read d_cum twice: keep it cached.
-            dv[i] = kMode == kLookback ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M)
+            dv[i] = one_pass(kMode) ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M)
                                        : IO::load(a.d_cum, tc.base + int64_t(i) * a.M);
         }
     } else {
@@ -643,7 +743,7 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
         for (int i = 0; i < L; ++i) {
             const bool ok = tc.col_ok && tc.t0 + i < a.s;
             qv[i] = ok ? IO::load(a.q, tc.base + int64_t(i) * a.M) : IO::one_raw();
-            dv[i] = ok ? (kMode == kLookback ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M)
+            dv[i] = ok ? (one_pass(kMode) ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M)
                                              : IO::load(a.d_cum, tc.base + int64_t(i) * a.M))
                        : IO::zero_raw();
         }
@@ -658,7 +758,7 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
     }
     Q4<CT> pre_v = q_zero<CT>();
     bool pre_ok = false;
-    if constexpr (kMode == kLookback) pre_ok = fenwick_prefetch<CT, WC, NW>(a, tc.chain, tc.pos, k, c, &pre_v);
+    if constexpr (one_pass(kMode)) pre_ok = lookback_prefetch<CT, WC, NW, kMode == kGrouped>(a, tc.chain, tc.pos, k, c, &pre_v);
     Q4<CT> Sa = q_zero<CT>();
     if constexpr (kMode == kFixup) Sa = *rscan_carry<CT, WC>(a, tc.chain, tc.pos, c);
 
@@ -695,8 +795,8 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
         if (wave == 0 && r == 0) *rscan_agg<CT, WC>(a, tc.chain, tc.pos, c) = Yg;
         return;
     }
-    if constexpr (kMode == kLookback)
-        Sa = fenwick_exclusive<CT, WC, NW, false>(a, tc.chain, tc.pos, Yg, wave == 0, wave, r, c, pre_v, pre_ok,
+    if constexpr (one_pass(kMode))
+        Sa = lookback_exclusive<CT, WC, NW, false, kMode == kGrouped>(a, tc.chain, tc.pos, Yg, wave == 0, wave, r, c, pre_v, pre_ok,
                                                   s_nodes, s_ok, s_after);
 
     if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok)
@@ -911,10 +1011,13 @@ hipError_t launch_rscan(const KernelArgs& a, hipStream_t st) {
                            dim3(unsigned(a.n_chains)), dim3(rscan_segments<WC>() * WC), params, 0, st);
 }
 
-// One pass with the look-back, or the three reduce-then-scan passes.
+// One pass with either look-back (a.group != 0: the grouped one), or the
+// three reduce-then-scan passes.
 template <class IO, int WC>
 hipError_t launch_fwd_wc(bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
-    if (!rscan) return launch_fwd_mode<IO, WC, kLookback>(deep, a, st);
+    if (!rscan)
+        return a.group != 0 ? launch_fwd_mode<IO, WC, kGrouped>(deep, a, st)
+                            : launch_fwd_mode<IO, WC, kLookback>(deep, a, st);
     hipError_t e = launch_fwd_mode<IO, WC, kAggregate>(deep, a, st);
     if (e == hipSuccess) e = launch_rscan<IO, WC, true>(a, st);
     if (e == hipSuccess) e = launch_fwd_mode<IO, WC, kFixup>(deep, a, st);
@@ -923,7 +1026,9 @@ hipError_t launch_fwd_wc(bool deep, bool rscan, const KernelArgs& a, hipStream_t
 
 template <class IO, int WC>
 hipError_t launch_bwd_wc(bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
-    if (!rscan) return launch_bwd_mode<IO, WC, kLookback>(deep, a, st);
+    if (!rscan)
+        return a.group != 0 ? launch_bwd_mode<IO, WC, kGrouped>(deep, a, st)
+                            : launch_bwd_mode<IO, WC, kLookback>(deep, a, st);
     hipError_t e = launch_bwd_mode<IO, WC, kAggregate>(deep, a, st);
     if (e == hipSuccess) e = launch_rscan<IO, WC, false>(a, st);
     if (e == hipSuccess) e = launch_bwd_mode<IO, WC, kFixup>(deep, a, st);

@@ -163,6 +163,9 @@ def test_options(lib):
     o.path = 4
     assert fwd(lib, opts=ctypes.byref(o)) == E_OPT
     o.path = 0
+    o.lookback = 3
+    assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
+    o.lookback = 0
     o.reserved[2] = 1
     assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
 

@@ -23,7 +23,10 @@ DEV = "cuda:0"
 
 # (b, s, h, j, recipe, dtype, path, use_ckpt): chunked with saved boundary
 # state, chunked leaves-only (forward prepass inside the backward), bfloat16,
-# a few long chains (tall tiles) and the per-column path.
+# a few long chains (tall tiles), the per-column path, the reduce-then-scan
+# passes, and each look-back scheme forced ("fenwick", "grouped": the chunked
+# path with that scheme; AUTO takes the grouped one for the first and the
+# long-chain shapes).
 CASES = [
     (2, 4096, 4, 8, "unit", "f32", "chunked", True),
     (2, 4096, 4, 8, "unit", "f32", "chunked", False),
@@ -32,14 +35,20 @@ CASES = [
     (4, 700, 8, 8, "unit", "f32", "column", True),
     (1, 30000, 2, 8, "unit", "f32", "rscan", True),
     (1, 30000, 2, 8, "unit", "f32", "rscan", False),
+    (1, 30000, 2, 8, "unit", "f32", "fenwick", True),
+    (3, 5000, 2, 3, "unit", "bf16", "grouped", False),
 ]
 REPLAYS = 4
 
 
+def _opts(path):
+    return dict(path="chunked", lookback=path) if path in ("fenwick", "grouped") else dict(path=path)
+
+
 def _eager(q, init, d, path, use_ckpt, ws):
     ck = capi.new_ckpt(q) if use_ckpt else None
-    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, workspace=ws)
-    d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ck, path=path, workspace=ws)
+    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, workspace=ws, **_opts(path))
+    d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ck, workspace=ws, **_opts(path))
     return cum, d_q, d_init
 
 
@@ -56,14 +65,14 @@ def test_graph_replays_match_eager_and_oracle(case):
     eager_ws = capi.Workspace()
 
     # Warm-up on the capture workspace (allocates and zeroes it outside the capture).
-    capi.quat_cumprod_fwd(q, init, cum, ck, path=path, workspace=ws)
-    capi.quat_cumprod_bwd(q, init, d, ck, d_q=d_q, d_init=d_init, path=path, workspace=ws)
+    capi.quat_cumprod_fwd(q, init, cum, ck, workspace=ws, **_opts(path))
+    capi.quat_cumprod_bwd(q, init, d, ck, d_q=d_q, d_init=d_init, workspace=ws, **_opts(path))
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        capi.quat_cumprod_fwd(q, init, cum, ck, path=path, workspace=ws)
-        capi.quat_cumprod_bwd(q, init, d, ck, d_q=d_q, d_init=d_init, path=path, workspace=ws)
+        capi.quat_cumprod_fwd(q, init, cum, ck, workspace=ws, **_opts(path))
+        capi.quat_cumprod_bwd(q, init, d, ck, d_q=d_q, d_init=d_init, workspace=ws, **_opts(path))
     torch.cuda.synchronize()
 
     for r in range(REPLAYS):

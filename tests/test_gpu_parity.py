@@ -47,12 +47,19 @@ def to_f64(t):
     return t.float().cpu().numpy().astype(np.float64) if t is not None else None
 
 
+def path_options(path):
+    """A test's path name as (path, lookback): "fenwick" and "grouped" are the
+    look-back path with that carry scheme forced."""
+    return ("chunked", path) if path in ("fenwick", "grouped") else (path, None)
+
+
 def run_device(inp, path=None, use_ckpt=True, want_dq=True, want_dinit=True, stream=None):
     q, init, d = to_dev(inp.q, inp.dtype), to_dev(inp.init, inp.dtype), to_dev(inp.d_cum, inp.dtype)
     ck = capi.new_ckpt(q) if use_ckpt else None
-    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, stream=stream)
+    path, lookback = path_options(path)
+    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, lookback=lookback, stream=stream)
     d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ckpt=ck, want_dq=want_dq, want_dinit=want_dinit,
-                                        path=path, stream=stream)
+                                        path=path, lookback=lookback, stream=stream)
     assert capi.default_workspace.status(q.device, stream) == 0, "a cross-block wait hit its spin limit"
     return cum, d_q, d_init
 
@@ -121,7 +128,8 @@ def test_config_full_parity(name, use_ckpt):
 
 @pytest.mark.parametrize("name", ["tiny", "medium"])
 @pytest.mark.parametrize("path,use_ckpt", [("chunked", False), ("column", True), ("column", False),
-                                           ("rscan", True), ("rscan", False)])
+                                           ("rscan", True), ("rscan", False), ("fenwick", True),
+                                           ("fenwick", False), ("grouped", True)])
 def test_config_other_paths(name, path, use_ckpt):
     print(f"[config {name} path={path} ckpt={use_ckpt}]", flush=True)
     compare(make_config(name), path=path, use_ckpt=use_ckpt)
@@ -134,7 +142,7 @@ EDGE_HJ = [(1, 1), (1, 3), (4, 4), (4, 8), (8, 8), (5, 13), (10, 10)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("path", ["chunked", "column", "rscan"])
+@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "fenwick", "grouped"])
 def test_edge_shapes(dtype, path):
     for s in EDGE_S:
         for (h, j) in EDGE_HJ:
@@ -170,7 +178,7 @@ def test_many_tiles_ragged(s, hj):
     inp = make_inputs(2, s, hj[0], hj[1], "unit", "f32", seed=s)
     print(f"[ragged s={s} hj={hj}]", flush=True)
     ref = reference(inp)
-    for path in ("chunked", "rscan"):
+    for path in ("chunked", "rscan", "fenwick", "grouped"):
         compare(inp, path=path, ref=ref)
         compare(inp, path=path, use_ckpt=False, ref=ref)
 
@@ -186,6 +194,7 @@ def test_wide_forward_groups(dtype, b, s, h, j):
     compare(inp, ref=ref)
     compare(inp, use_ckpt=False, ref=ref)
     compare(inp, path="rscan", ref=ref)
+    compare(inp, path="grouped", ref=ref)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -307,7 +316,7 @@ def test_workspace_reuse_small_then_large_shapes():
         compare(inp, path="chunked", use_ckpt=False)
 
 
-@pytest.mark.parametrize("path", ["chunked", "column", "rscan"])
+@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "grouped"])
 def test_zero_step_is_reported(path):
     """A step that is exactly zero makes every later prefix product zero: the
     forward stays exact, and the backward (whose exact form divides by |P_t|^2)
@@ -319,10 +328,11 @@ def test_zero_step_is_reported(path):
     print(f"[zero step {path}]", flush=True)
     ws = capi.Workspace()
     ck = capi.new_ckpt(q)
-    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, workspace=ws)
+    path, lookback = path_options(path)
+    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, lookback=lookback, workspace=ws)
     assert ws.status(q.device) == 0
     check("cum", to_f64(cum), oracle.fwd(inp.q64, inp.init64), "f32", inp.s)
-    capi.quat_cumprod_bwd(q, init, d, ck, path=path, workspace=ws)
+    capi.quat_cumprod_bwd(q, init, d, ck, path=path, lookback=lookback, workspace=ws)
     assert ws.status(q.device) == 2            # QC_STATUS_ZERO, and cleared by the read
     assert ws.status(q.device) == 0
 
@@ -336,6 +346,6 @@ def test_rscan_and_lookback_agree_on_long_chains(dtype):
         inp = make_inputs(b, s, h, j, "unit", dtype, seed=s + h * j)
         print(f"[long chains b={b} s={s} h={h} j={j} {dtype}]", flush=True)
         ref = reference(inp)
-        for path in ("rscan", "chunked"):
+        for path in ("rscan", "chunked", "fenwick", "grouped"):
             for use_ckpt in (True, False):
                 compare(inp, path=path, use_ckpt=use_ckpt, ref=ref)
