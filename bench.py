@@ -741,10 +741,18 @@ def all_configs_bench(args):
         torch.cuda.empty_cache()
 
 
-def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command: str):
+def short_kernel_name(name: str) -> str:
+    for pre in ("void ", "qc::(anonymous namespace)::", "(anonymous namespace)::", "qc::"):
+        name = name.replace(pre, "")
+    return name.replace("(KernelArgs)", "")
+
+
+def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command: str, bench_log: str | None = None):
     """Write profiles/kernels_<config>.txt from a rocprofv3 --kernel-trace
     --stats run (and, with pmc_dir, its FETCH_SIZE / WRITE_SIZE runs scaled by
-    the plain-copy calibration factors of traffic_headline.txt)."""
+    the plain-copy calibration factors of traffic_headline.txt).  Kernel
+    template arguments: <IO, column-group width, steps per lane, waves, ...,
+    mode>, mode 0 = Fenwick look-back, 3 = grouped look-back."""
     import csv
     import statistics
 
@@ -756,11 +764,19 @@ def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command:
              "# Commands (from /tmp, TMPDIR=/tmp, R = repository root, OUT = an output directory):"]
     lines += ["#   " + c for c in command.split(" ;; ")]
     lines.append("#")
-    lines.append("# rocprofv3 run_kernel_stats.csv (every dispatch of the traced run)")
-    lines.append(f"# {'kernel':60s} {'calls':>6s} {'avg ns':>10s} {'min ns':>10s} {'max ns':>10s}")
+    if bench_log:
+        recs = [json.loads(x) for x in open(bench_log) if x.startswith("{")]
+        if recs:
+            d = recs[-1]
+            lines.append(f"# The traced bench run's own line (profiler attached): {d['ms_per_step']} ms per step, "
+                         f"{d['value']} GB/s ({d['hbm_frac']:.3f} of 8 TB/s); diagnostic fwd "
+                         f"{d.get('diag_fwd_ms')} ms, bwd {d.get('diag_bwd_ms')} ms.")
+            lines.append("#")
+    lines.append("# rocprofv3 run_kernel_stats.csv (every dispatch of the traced run, untimed settle steps included)")
+    lines.append(f"# {'kernel':70s} {'calls':>6s} {'avg ns':>10s} {'min ns':>10s} {'max ns':>10s}")
     for r in rows:
-        name = r["Name"]
-        lines.append(f"{name[:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']):10.0f} "
+        name = short_kernel_name(r["Name"])
+        lines.append(f"{name[:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']):10.0f} "
                      f"{float(r['MinNs']):10.0f} {float(r['MaxNs']):10.0f}")
     if pmc_dir:
         cal = read_kv(TRAFFIC_FILE)
@@ -782,13 +798,13 @@ def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command:
         lines.append("#")
         lines.append(f"# HBM bytes per launch: FETCH_SIZE x {fs:.4f} + WRITE_SIZE x {ws:.4f} (the plain-copy "
                      "calibration factors of traffic_headline.txt), median over the run's launches")
-        lines.append(f"# {'kernel':60s} {'fetch B':>14s} {'write B':>14s} {'algorithmic B':>14s} {'ratio':>6s}")
+        lines.append(f"# {'kernel':70s} {'fetch B':>14s} {'write B':>14s} {'algorithmic B':>14s} {'ratio':>6s}")
         for k in sorted(set(f) & set(w)):
-            if "zero_words" in k or "bump_epoch" in k:
+            if "zero_words" in k or "bump_epoch" in k or "at::native" in k or "rocclr" in k:
                 continue
             base = next((v for key, v in alg.items() if key in k and ", false>" not in k), None)
             tot = f[k] * fs + w[k] * ws
-            lines.append(f"{k[:62]:62s} {f[k] * fs:14.0f} {w[k] * ws:14.0f} "
+            lines.append(f"{short_kernel_name(k)[:72]:72s} {f[k] * fs:14.0f} {w[k] * ws:14.0f} "
                          f"{(base if base else 0):14d} {(tot / base if base else 0):6.3f}")
     path = os.path.join(ROOT, "profiles", f"kernels_{config}.txt")
     with open(path, "w") as out:
@@ -841,6 +857,8 @@ def main():
                     help="write profiles/kernels_<config>.txt from a rocprofv3 kernel-trace run of --config")
     ap.add_argument("--pmc-dir", default=None,
                     help="with --summarize-profile: directory holding FETCH_SIZE/ and WRITE_SIZE/ counter runs")
+    ap.add_argument("--bench-log", default=None,
+                    help="with --summarize-profile: the traced bench run's output, for its JSON line")
     ap.add_argument("--profile-command", default="",
                     help="with --summarize-profile: the commands that made the runs (' ;; '-separated)")
     args = ap.parse_args()
@@ -850,7 +868,7 @@ def main():
                                f"gdn2 b{B} h{H} t{T} latent{L} dense{D} chunk{C} f32, forward + VJP")
         return
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.config, args.pmc_dir, args.profile_command)
+        summarize_profile(args.summarize_profile, args.config, args.pmc_dir, args.profile_command, args.bench_log)
         return
     if args.summarize_scan_traffic:
         cal = read_kv(TRAFFIC_FILE)
