@@ -18,25 +18,40 @@
  *
  * Layout (row-major float32): query, key, erase, log_decay [B, H, T, L];
  * value, write, context [B, H, T, D]; initial_state, final state [B, H, L, D].
- * The boundary states (entry c = the state before step c * chunk) and the
- * backward's scratch are internal formats: [B, H, ceil(T / chunk), D, LP], and
- * [B, H, min(chunk, T), D, LP] followed, when a head spans several backward
- * blocks (D > 64 for L > 16, D > 128 for L <= 16), by the blocks' shares
- * [B, H, T, n_blocks, 4, L], with LP = L rounded up to 16, 32 or 64 (each
- * dense column's rows contiguous, rows past L zero); both must be 16-byte
- * aligned.  gdn2_scratch_bytes gives the size.
+ * The saved state for the backward (`boundary`) and the backward's scratch
+ * are internal formats whose sizes gdn2_boundary_bytes and gdn2_scratch_bytes
+ * give; both must be 16-byte aligned.  LP is L rounded up to 16, 32 or 64.
  *
- * Device design: a dense column's rows are spread over 8 lanes (4 when L <=
- * 16) and columns evolve independently, so the forward runs one-wave blocks
- * over a head's columns, with the step's latent vectors broadcast through LDS;
- * it saves the state every `chunk` steps.  The backward runs blocks of 8
+ * Two device forms, selected by `chunk`; the results agree to rounding.
+ *
+ * chunk 16 or 32: the chunk-WY form (the same page's tensor-core backward,
+ * backward_chunk_wy_tensor_core_impl, and the factors it consumes), on
+ * float32 MFMA.  Within a chunk, with c_t the cumulative decay from the chunk
+ * start, the updates solve the unit-lower-triangular system
+ * (I + A) U = write.value - M S0 (A = strictly lower (b k c)(k / c)^T); the
+ * context, the end state and the VJP are chunk-sized matrix products.  The
+ * forward writes, in `boundary`: the state before every chunk [B, H, chunks,
+ * LP, D], one factor record per chunk, and the chunks' updates U [B, H,
+ * chunks * chunk, D].  The backward carries the state cotangent through the
+ * chunks in reverse (saving it per chunk in `scratch`, with the chunks' solved
+ * right-hand sides), then forms every cotangent of every chunk in parallel.
+ * Requires each chunk's cumulative decay to stay above about 1e-37 per latent
+ * row (float32 range), as the page's form does.
+ *
+ * Any other chunk: the step-by-step recurrence.  A dense column's rows are
+ * spread over 8 lanes (4 when L <= 16) and columns evolve independently, so
+ * the forward runs one-wave blocks over a head's columns, with the step's
+ * latent vectors broadcast through LDS; it saves the state every `chunk`
+ * steps ([B, H, ceil(T / chunk), D, LP]).  The backward runs blocks of 8
  * waves (64 columns, 128 when L <= 16), several per head: it walks the chunks
  * in reverse, recomputes each chunk's states from its saved boundary (in
  * registers when chunk is 8, else into `scratch`), then reverses the chunk
  * step by step.  The latent-vector cotangents (query, key, erase, log_decay)
  * are sums over the dense axis, reduced across each block; with several
  * blocks per head their shares go through `scratch` and a second kernel adds
- * them in block order.  Results do not depend on the chunk, bit for bit.
+ * them in block order.  Results of this form do not depend on the chunk, bit
+ * for bit.
+ *
  * Arithmetic is float32.
  *
  * Limits: B, H, T, D, chunk >= 1; 1 <= L <= 64; D <= 1024; element counts
@@ -62,10 +77,12 @@
 extern "C" {
 #endif
 
-/* Bytes of the saved boundary states for these sizes (0 if out of range). */
+/* Bytes of the saved state the forward writes for the backward (boundary
+ * states, and for the chunk-WY form also the factor records and updates;
+ * 0 if out of range). */
 size_t gdn2_boundary_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk);
 
-/* Bytes of the backward's scratch (one chunk of states per head; 0 if out of range). */
+/* Bytes of the backward's scratch (0 if out of range). */
 size_t gdn2_scratch_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int64_t D, int64_t chunk);
 
 /* context (required), final_state (may be NULL) and the boundary states the
