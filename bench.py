@@ -824,6 +824,8 @@ def main():
     ap.add_argument("--config", default="headline", choices=list(CONFIGS))
     ap.add_argument("--path", default=None, choices=["auto", "column", "chunked", "rscan"])
     ap.add_argument("--lookback", default=None, choices=["auto", "fenwick", "grouped"])
+    ap.add_argument("--leaves", default=None, choices=["auto", "prepass", "coresident"],
+                    help="how the leaves-only backward re-derives the boundary products")
     ap.add_argument("--leaves-only", action="store_true",
                     help="backward without the saved boundary state (re-derives it from q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -929,7 +931,8 @@ def main():
         capi.quat_cumprod_fwd(q, init, cum, ckpt, path=args.path, lookback=args.lookback)
 
     def bwd():
-        capi.quat_cumprod_bwd(q, init, d_cum, ckpt, d_q=d_q, d_init=d_init, path=args.path, lookback=args.lookback)
+        capi.quat_cumprod_bwd(q, init, d_cum, ckpt, d_q=d_q, d_init=d_init, path=args.path, lookback=args.lookback,
+                              leaves=args.leaves)
 
     # Untimed warm-up: W steps, continued until --settle-ms has passed.
     warm_steps, t0 = 0, time.perf_counter()
@@ -990,7 +993,8 @@ def main():
             capi.quat_cumprod_fwd(q, init, cum, None, path=args.path, lookback=args.lookback)
 
         def bwd_lo():
-            capi.quat_cumprod_bwd(q, init, d_cum, None, d_q=d_q, d_init=d_init, path=args.path, lookback=args.lookback)
+            capi.quat_cumprod_bwd(q, init, d_cum, None, d_q=d_q, d_init=d_init, path=args.path, lookback=args.lookback,
+                                  leaves=args.leaves)
 
         for _ in range(10):
             fwd_lo()
@@ -1033,6 +1037,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "b": b, "s": s, "h": h, "j": j, "io_dtype": io, "recipe": recipe,
                    "path": args.path or "auto", "lookback": args.lookback or "auto",
+                   "leaves": args.leaves or "auto",
                    "backward": "leaves-only" if args.leaves_only else "saved boundary state"},
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "elements_per_s": round(n / (ms_step * 1e-3), 1),

@@ -112,10 +112,24 @@ enum {
                                  at most a few thousand tiles) */
 };
 
+/* How a backward without saved boundary state (ckpt = NULL) obtains the
+ * prefix products before its tiles (QC_PATH_AUTO / QC_PATH_CHUNKED). */
+enum {
+    QC_LEAVES_AUTO = 0,       /* library heuristic */
+    QC_LEAVES_PREPASS = 1,    /* a forward pass over q writes them into the workspace first (one more
+                                 read of q) */
+    QC_LEAVES_CORESIDENT = 2  /* one cooperative pass: groups of blocks that hold a whole chain's tiles
+                                 at once also run a forward look-back among themselves, so q is read
+                                 once.  Taken when at least one chain fits on the device at once and
+                                 the stream is not capturing a graph; otherwise the pre-pass runs.
+                                 Never chosen by AUTO (slower than the pre-pass where measured). */
+};
+
 typedef struct {
     int32_t path;           /* QC_PATH_* */
     int32_t lookback;       /* QC_LOOKBACK_*; ignored by the other paths */
-    int32_t reserved[6];    /* must be zero */
+    int32_t leaves;         /* QC_LEAVES_*; ignored when a ckpt is given */
+    int32_t reserved[5];    /* must be zero */
 } qc_options;
 
 /* Bytes of workspace that quat_cumprod_fwd and quat_cumprod_bwd need for this

@@ -24,6 +24,8 @@ QC_PATH_RSCAN = 3
 PATHS = {"auto": QC_PATH_AUTO, "column": QC_PATH_COLUMN, "chunked": QC_PATH_CHUNKED, "rscan": QC_PATH_RSCAN}
 # Cross-tile carry scheme of the look-back path (QC_LOOKBACK_*).
 LOOKBACKS = {"auto": 0, "fenwick": 1, "grouped": 2}
+# How a backward without saved state gets its boundary products (QC_LEAVES_*).
+LEAVES = {"auto": 0, "prepass": 1, "coresident": 2}
 
 _DTYPES = {torch.float32: QC_DTYPE_F32, torch.bfloat16: QC_DTYPE_BF16}
 
@@ -44,7 +46,8 @@ EXPORTS = (
 
 
 class QcOptions(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("lookback", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+    _fields_ = [("path", ctypes.c_int32), ("lookback", ctypes.c_int32), ("leaves", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
 
 
 class QcScanPlan(ctypes.Structure):
@@ -180,12 +183,13 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _options(path: str | None, lookback: str | None = None):
-    if path is None and lookback is None:
+def _options(path: str | None, lookback: str | None = None, leaves: str | None = None):
+    if path is None and lookback is None and leaves is None:
         return None
     o = QcOptions()
     o.path = PATHS[path or "auto"]
     o.lookback = LOOKBACKS[lookback or "auto"]
+    o.leaves = LEAVES[leaves or "auto"]
     return ctypes.byref(o)
 
 
@@ -359,9 +363,11 @@ def quat_cumprod_fwd(q: torch.Tensor, init: torch.Tensor, cum: torch.Tensor | No
 def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
                      ckpt: torch.Tensor | None = None, *, want_dq: bool = True, want_dinit: bool = True,
                      d_q: torch.Tensor | None = None, d_init: torch.Tensor | None = None,
-                     path: str | None = None, lookback: str | None = None, stream=None,
-                     workspace: Workspace | None = None):
-    """VJP of the scan: returns (d_q, d_init); an unwanted output is None."""
+                     path: str | None = None, lookback: str | None = None, leaves: str | None = None,
+                     stream=None, workspace: Workspace | None = None):
+    """VJP of the scan: returns (d_q, d_init); an unwanted output is None.
+    Without ``ckpt``, ``leaves`` chooses how the boundary products are
+    re-derived ("prepass", "coresident"; see QC_LEAVES_* in the C header)."""
     b, s, h, j = _dims(q)
     dt = _dtype_code(q)
     if want_dq and d_q is None:
@@ -382,7 +388,7 @@ def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
     rc = load().quat_cumprod_bwd_ex(_ptr(q), _ptr(init), _ptr(d_cum), _ptr(ckpt),
                                     0 if ckpt is None else ckpt.numel() * ckpt.element_size(),
                                     _ptr(d_q), _ptr(d_init), b, s, h, j, dt, _ptr(ws), ws.numel(),
-                                    _stream(stream), _options(path, lookback))
+                                    _stream(stream), _options(path, lookback, leaves))
     _check(rc, "quat_cumprod_bwd")
     return d_q, d_init
 
@@ -583,9 +589,14 @@ def _gdn2_check(tensors: dict, B, H, T, L, D, device):
             raise ValueError(f"{name} must be contiguous float32 {shapes[name]} on {device}")
 
 
-def gdn2_fwd(query, key, value, erase, write, log_decay, initial_state, *, chunk: int = 64,
+def gdn2_fwd(query, key, value, erase, write, log_decay, initial_state, *, chunk: int = 32,
              want_boundary: bool = True, stream=None):
-    """(context [B, H, T, D], final state [B, H, L, D], boundary states or None)."""
+    """(context [B, H, T, D], final state [B, H, L, D], boundary states or None).
+
+    Chunks of 16 and 32 run the chunk-WY form (the fastest; 32 is the
+    default), every other chunk the step-by-step recurrence.  The returned
+    saved state is tagged with its chunk (``gdn2_chunk``), and gdn2_bwd
+    refuses it for another chunk."""
     B, H, T, L, D, chunk = _gdn2_dims(query, value, chunk)
     ins = dict(zip(GDN2_INPUTS, (query, key, value, erase, write, log_decay, initial_state)))
     _gdn2_check(ins, B, H, T, L, D, query.device)
@@ -599,10 +610,12 @@ def gdn2_fwd(query, key, value, erase, write, log_decay, initial_state, *, chunk
     rc = lib.gdn2_fwd(*[_ptr(ins[n]) for n in GDN2_INPUTS], _ptr(ctx), _ptr(state), _ptr(bnd),
                       B, H, T, L, D, chunk, _stream(stream))
     _check(rc, "gdn2_fwd")
+    if bnd is not None:
+        bnd.gdn2_chunk = chunk
     return ctx, state, bnd
 
 
-def gdn2_bwd(query, key, value, erase, write, log_decay, boundary, d_context, d_state=None, *, chunk: int = 64,
+def gdn2_bwd(query, key, value, erase, write, log_decay, boundary, d_context, d_state=None, *, chunk: int = 32,
              want=GDN2_INPUTS, stream=None, scratch=None):
     """Cotangents (query, key, value, erase, write, log_decay, initial_state);
     those not named in ``want`` are None.  ``boundary`` is gdn2_fwd's third
@@ -616,6 +629,9 @@ def gdn2_bwd(query, key, value, erase, write, log_decay, boundary, d_context, d_
     nb = int(lib.gdn2_boundary_bytes(B, H, T, L, D, chunk))
     if boundary is None or boundary.numel() * 4 != nb or boundary.dtype != torch.float32:
         raise ValueError("boundary must be gdn2_fwd's boundary states for the same sizes and chunk")
+    made_with = getattr(boundary, "gdn2_chunk", None)
+    if made_with is not None and made_with != chunk:
+        raise ValueError(f"boundary was written by gdn2_fwd with chunk {made_with}, not {chunk}")
     nscr = int(lib.gdn2_scratch_bytes(B, H, T, L, D, chunk))
     if scratch is None:
         scratch = torch.empty(nscr // 4, dtype=torch.float32, device=query.device)

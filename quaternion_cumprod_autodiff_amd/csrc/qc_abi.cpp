@@ -9,10 +9,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <random>
 #include <string>
+#include <tuple>
 
 namespace {
 
@@ -166,7 +170,9 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     const size_t tiles_bwd = size_t(p->bwd.n_chains * p->bwd.n_tiles) * size_t(p->bwd.wc);
     const size_t nodes_fwd = tiles_fwd + size_t(p->fwd.n_chains * p->fwd.n_groups) * size_t(p->fwd.wc);
     const size_t nodes_bwd = tiles_bwd + size_t(p->bwd.n_chains * p->bwd.n_groups) * size_t(p->bwd.wc);
-    const size_t look = (nodes_fwd > nodes_bwd ? nodes_fwd : nodes_bwd) * p->slot_bytes;
+    // The co-resident leaves-only backward keeps two sets of tile nodes, one per look-back.
+    const size_t nodes = std::max(std::max(nodes_fwd, nodes_bwd), 2 * tiles_bwd);
+    const size_t look = nodes * p->slot_bytes;
     const size_t agg = 2 * (tiles_fwd > tiles_bwd ? tiles_fwd : tiles_bwd) * p->ct_bytes;
     const size_t desc = look > agg ? look : agg;
     p->off_desc = round_up(size_t(qc::kHdrWords) * 4, kAlignWs);
@@ -199,6 +205,7 @@ bool any_alias(const Range* r, const bool* is_out, int n) {
 struct Options {
     int path = QC_PATH_AUTO;
     int lookback = QC_LOOKBACK_AUTO;
+    int leaves = QC_LEAVES_AUTO;
 };
 
 int check_options(const qc_options* o, Options* out) {
@@ -206,10 +213,12 @@ int check_options(const qc_options* o, Options* out) {
     if (!o) return QC_OK;
     if (o->path < QC_PATH_AUTO || o->path > QC_PATH_RSCAN) return QC_ERR_OPTION;
     if (o->lookback < QC_LOOKBACK_AUTO || o->lookback > QC_LOOKBACK_GROUPED) return QC_ERR_OPTION;
-    for (int i = 0; i < 6; ++i)
+    if (o->leaves < QC_LEAVES_AUTO || o->leaves > QC_LEAVES_CORESIDENT) return QC_ERR_OPTION;
+    for (int i = 0; i < 5; ++i)
         if (o->reserved[i] != 0) return QC_ERR_OPTION;
     out->path = o->path;
     out->lookback = o->lookback;
+    out->leaves = o->leaves;
     return QC_OK;
 }
 
@@ -263,6 +272,65 @@ qc::KernelArgs column_args(const Plan& p, void* ws) {
 // look-back, and on the long single-chain shapes where its waits-free passes
 // could pay it measured slower than the look-back, so AUTO never takes it.
 bool use_rscan(int path) { return path == QC_PATH_RSCAN; }
+
+// The leaves-only backward in one co-resident pass (no pre-pass over q) runs
+// only when asked for (QC_LEAVES_CORESIDENT) and at least one chain fits on
+// the device at once.  It reads q once, but each group of blocks walks its
+// chains in lockstep with two look-backs per chain, which the other groups'
+// streaming does not hide: measured slower than the pre-pass at every
+// workload (headline backward 613 us against 392, medium 45.5 against 34.5,
+// drift 781 against 423), so AUTO keeps the pre-pass.
+
+// Chains the co-resident backward can hold at once on the current device
+// (occupancy of its kernel, cached per device and instance).
+int64_t coresident_groups(const Plan& p) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, bool>, int64_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const auto key = std::make_tuple(dev, p.dtype, p.bwd.wc, p.bwd.deep);
+    int64_t blocks = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) {
+            blocks = it->second;
+        } else {
+            blocks = qc::coresident_blocks(p.dtype, p.bwd.wc, p.bwd.deep);
+            cache[key] = blocks;
+        }
+    }
+    return std::min(blocks / p.bwd.n_tiles, p.bwd.n_chains);
+}
+
+// Launches the co-resident leaves-only backward if the options and the shape
+// allow it; *done tells whether it did.
+int try_bwd_coresident(const Plan& p, const Options& o, const void* q, const void* init, const void* d_cum,
+                       void* d_q, void* d_init, void* ws, hipStream_t st, bool* done) {
+    *done = false;
+    if (o.leaves != QC_LEAVES_CORESIDENT || use_rscan(o.path)) return QC_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t ce = hipStreamIsCapturing(st, &cs);
+    if (ce != hipSuccess) return hip_fail(ce);
+    if (cs != hipStreamCaptureStatusNone) return QC_OK;   // graphs keep the pre-pass's plain launches
+    const int64_t groups = coresident_groups(p);
+    if (groups < 1) return QC_OK;
+    qc::KernelArgs a = base_args(p, ws, p.bwd, QC_LOOKBACK_FENWICK);
+    a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init;
+    a.desc2 = static_cast<char*>(a.desc) + size_t(p.bwd.n_chains * p.bwd.n_tiles) * size_t(p.bwd.wc) * p.slot_bytes;
+    a.n_coop = groups;
+    a.n_blocks = uint32_t(groups * p.bwd.n_tiles);
+    const int rc = set_epoch(&a, st);
+    if (rc != QC_OK) return rc;
+    const hipError_t e = qc::launch_bwd_coresident(p.dtype, p.bwd.wc, p.bwd.deep, a, st);
+    if (e == hipErrorCooperativeLaunchTooLarge) {
+        (void)hipGetLastError();   // the device holds fewer blocks than its occupancy said: use the pre-pass
+        return QC_OK;
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    *done = true;
+    return QC_OK;
+}
 
 int launch_forward(const Plan& p, const void* q, const void* init, void* cum, void* ckpt, void* ws,
                    hipStream_t st, bool column, bool rscan, int lookback) {
@@ -368,6 +436,11 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
         return e == hipSuccess ? QC_OK : hip_fail(e);
     }
     void* ck = const_cast<void*>(ckpt);
+    if (!ck) {
+        bool done = false;
+        rc = try_bwd_coresident(p, o, q, init, d_cum, d_q, d_init, workspace, st, &done);
+        if (rc != QC_OK || done) return rc;
+    }
     if (!ck) {
         // Leaves-only backward: re-derive the boundary prefix products from q.
         ck = static_cast<char*>(workspace) + p.off_ckpt;

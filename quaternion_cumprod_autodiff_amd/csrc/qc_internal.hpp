@@ -93,6 +93,8 @@ struct KernelArgs {
     int64_t n_tiles;      // tiles per chain
     int64_t group;        // grouped look-back: tiles per group (0: the Fenwick look-back)
     int64_t n_groups;     // groups per chain (grouped look-back)
+    void* desc2;          // co-resident leaves-only backward: the forward look-back's carry nodes
+    int64_t n_coop;       // co-resident leaves-only backward: chains in flight at once (groups of n_tiles blocks)
     uint64_t epoch;       // this launch's epoch, folded into every check word (0: read it from the header)
     uint32_t n_blocks;    // grid size
     uint32_t spin_limit;
@@ -102,6 +104,11 @@ struct KernelArgs {
 // chain, a fix-up pass) instead of the single pass with the look-back.
 hipError_t launch_fwd_chunked(int dtype, int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st);
+// Co-resident leaves-only backward (cooperative launch of a.n_coop groups of
+// a.n_tiles blocks), and how many of its blocks the current device holds at
+// once (0 if that cannot be told).
+hipError_t launch_bwd_coresident(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st);
+int64_t coresident_blocks(int dtype, int wc, bool deep);
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_bwd_column(int dtype, const KernelArgs& a, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t st);

@@ -824,6 +824,140 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
     }
 }
 
+// Leaves-only backward in one pass, for shapes whose chains fit on the chip
+// a group of blocks at a time (the page's contract: only q and init are
+// saved, and no pre-pass re-reads q to rebuild the boundary products).  The
+// grid is cooperative: a.n_coop groups of a.n_tiles blocks, all resident at
+// once, and group g walks chains g, g + n_coop, ...  Block b of a group owns
+// tile b (time order) of its chain.  A tile learns the prefix product E
+// before it from a forward Fenwick look-back among its own group (nodes in
+// a.desc2: the tile's product of all its slices), then runs the backward's
+// reverse look-back and sweep 2 as bwd_chunked_kernel does with E from the
+// saved boundary state.  Every wait is on a block of the same group in the
+// same chain; the group is resident, and a block leaves a chain only after
+// publishing all of its nodes of that chain, so every wait ends.
+template <int WC, int L, int NW>
+__device__ __forceinline__ TileCoord tile_at(const KernelArgs& a, int64_t chain, int64_t tile, int k, int c) {
+    constexpr int T = (64 / WC) * NW * L;
+    TileCoord tc;
+    tc.chain = chain;
+    tc.pos = a.n_tiles - 1 - tile;   // the reverse look-back's position
+    tc.bi = chain / a.n_cg;
+    const int64_t cg = chain % a.n_cg;
+    tc.m = cg * WC + c;
+    tc.col_ok = tc.m < a.M;
+    tc.t0 = tile * T + int64_t(k) * L;
+    tc.base = (tc.bi * a.s + tc.t0) * a.M + tc.m;
+    tc.full = (tile + 1) * T <= a.s && (cg + 1) * WC <= a.M;
+    return tc;
+}
+
+template <class IO, int WC, int L, int NW>
+__global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_coresident_kernel(KernelArgs a) {
+    a.epoch = launch_epoch(a);
+    using CT = typename IO::CT;
+    using Raw = typename IO::Raw;
+    constexpr int R = 64 / WC;
+    constexpr int K = NW * R;
+    __shared__ Q4<CT> s_sq[K][WC];
+    __shared__ Q4<CT> s_sy[K][WC];
+    __shared__ Q4<CT> s_nodes[K][WC];
+    __shared__ uint8_t s_ok[K][WC];
+    __shared__ Q4<CT> s_before[WC];
+    __shared__ Q4<CT> s_after[WC];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane / WC, c = lane % WC;
+    const int k = wave * R + r;
+    const int64_t group = blockIdx.x / a.n_tiles, tile = blockIdx.x % a.n_tiles;
+    KernelArgs af = a;
+    af.desc = a.desc2;
+
+    for (int64_t chain = group; chain < a.n_chains; chain += a.n_coop) {
+        const TileCoord tc = tile_at<WC, L, NW>(a, chain, tile, k, c);
+        Raw qv[L], dv[L];
+        if (tc.full) {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                qv[i] = IO::load(a.q, tc.base + int64_t(i) * a.M);
+                dv[i] = IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const bool ok = tc.col_ok && tc.t0 + i < a.s;
+                qv[i] = ok ? IO::load(a.q, tc.base + int64_t(i) * a.M) : IO::one_raw();
+                dv[i] = ok ? IO::load_stream(a.d_cum, tc.base + int64_t(i) * a.M) : IO::zero_raw();
+            }
+        }
+        Raw init_raw = IO::one_raw();
+        if (tc.col_ok) init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
+
+        // Sweep 1 and the tile's exchange, as in bwd_chunked_kernel.
+        Q4<CT> Ql = IO::ct(qv[0]);
+        Q4<CT> Yl = qcmul(Ql, IO::ct(dv[0]));
+#pragma unroll
+        for (int i = 1; i < L; ++i) {
+            Ql = qmul(IO::ct(qv[i]), Ql);
+            Yl = qadd(Yl, qcmul(Ql, IO::ct(dv[i])));
+        }
+        s_sq[k][c] = Ql;
+        s_sy[k][c] = Yl;
+        __syncthreads();
+        Q4<CT> F = q_one<CT>();
+        if (k > 0) {
+            F = s_sq[0][c];
+            for (int k2 = 1; k2 < k; ++k2) F = qmul(s_sq[k2][c], F);
+        }
+        Q4<CT> Rp = q_zero<CT>();
+        if (k < K - 1) {
+            Rp = s_sy[K - 1][c];
+            for (int k2 = K - 2; k2 > k; --k2) Rp = qadd(s_sy[k2][c], qcmul(s_sq[k2][c], Rp));
+        }
+        const Q4<CT> A = qmul(Ql, F);
+
+        // The tile's product (all K slices; wave 0 publishes it) and the
+        // forward look-back for E, the prefix product before the tile.
+        Q4<CT> Pt = q_one<CT>();
+        if (wave == 0) {
+            Pt = s_sq[0][c];
+            for (int k2 = 1; k2 < K; ++k2) Pt = qmul(s_sq[k2][c], Pt);
+        }
+        // (No first-round prefetch: its value would be held across sweep 1,
+        // and the tile's registers are full.)
+        const Q4<CT> Et = fenwick_exclusive<CT, WC, NW, true>(af, chain, tile, Pt, wave == 0, wave, r, c, q_one<CT>(),
+                                                              false, s_nodes, s_ok, s_before);
+
+        Q4<CT> Yg = q_zero<CT>();
+        if (wave == 0) Yg = qcmul(Et, qadd(Yl, qcmul(Ql, Rp)));
+        const Q4<CT> Sa = fenwick_exclusive<CT, WC, NW, false>(a, chain, tc.pos, Yg, wave == 0, wave, r, c,
+                                                               q_zero<CT>(), false, s_nodes, s_ok, s_after);
+
+        if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok) IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Yg, Sa));
+
+        if (a.out != nullptr && tc.col_ok) {
+            const CT nE = qnorm2(Et), nA = qnorm2(A);
+            if (nE == CT(0) || nA == CT(0))
+                __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusZeroPrefix, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            const Q4<CT> Z = qscale(qmul(Et, Sa), recip(nE));
+            const Q4<CT> C = qmul(Et, IO::ct(init_raw));
+            const Q4<CT> c0 = qmul(F, C);
+            Q4<CT> cm = qmul(A, C);
+            Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rp, qscale(qmul(A, Z), recip(nA))));
+#pragma unroll
+            for (int i = L - 1; i >= 0; --i) {
+                const Q4<CT> qi = IO::ct_fresh(qv[i]);
+                const Q4<CT> cprev = i == 0 ? c0 : qscale(qcmul(qi, cm), recip(qnorm2(qi)));
+                if (tc.full || tc.t0 + i < a.s) IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qmulc(G, cprev));
+                if (i > 0) G = qadd(IO::ct_fresh(dv[i - 1]), qcmul(qi, G));
+                cm = cprev;
+            }
+        }
+        __syncthreads();   // s_sq / s_sy are rewritten for the next chain
+    }
+}
+
 // ------------------------------------------------------------- column path
 
 template <class IO, int U>
@@ -1071,6 +1205,59 @@ hipError_t launch_fwd_chunked(int dtype, int wc, bool deep, bool rscan, const Ke
 
 hipError_t launch_bwd_chunked(int dtype, int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
     return dtype == 0 ? launch_bwd_io<IoF32>(wc, deep, rscan, a, st) : launch_bwd_io<IoBF16>(wc, deep, rscan, a, st);
+}
+
+namespace {
+
+template <class IO, int WC>
+const void* coresident_fn(bool deep) {
+    constexpr Geometry g = geometry_for(WC, IO::kDtype);
+    return deep ? reinterpret_cast<const void*>(&bwd_coresident_kernel<IO, WC, g.bwd_deep_l, g.bwd_nw>)
+                : reinterpret_cast<const void*>(&bwd_coresident_kernel<IO, WC, g.bwd_l, g.bwd_nw>);
+}
+
+template <class IO>
+const void* coresident_fn_io(int wc, bool deep) {
+    switch (wc) {
+        case 64: return coresident_fn<IO, 64>(deep);
+        case 32: return coresident_fn<IO, 32>(deep);
+        case 16: return coresident_fn<IO, 16>(deep);
+        case 8: return coresident_fn<IO, 8>(deep);
+        case 4: return coresident_fn<IO, 4>(deep);
+        case 2: return coresident_fn<IO, 2>(deep);
+        case 1: return coresident_fn<IO, 1>(deep);
+        default: return nullptr;
+    }
+}
+
+const void* coresident_kernel(int dtype, int wc, bool deep) {
+    return dtype == 0 ? coresident_fn_io<IoF32>(wc, deep) : coresident_fn_io<IoBF16>(wc, deep);
+}
+
+int bwd_threads(int dtype, int wc) {
+    const Geometry g = dtype == 0 ? geometry_for(wc, 0) : geometry_for(wc, 1);
+    return g.bwd_nw * 64;
+}
+
+}  // namespace
+
+int64_t coresident_blocks(int dtype, int wc, bool deep) {
+    const void* fn = coresident_kernel(dtype, wc, deep);
+    if (fn == nullptr) return 0;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, bwd_threads(dtype, wc), 0) != hipSuccess) return 0;
+    return int64_t(per_cu) * cus;
+}
+
+hipError_t launch_bwd_coresident(int dtype, int wc, bool deep, const KernelArgs& a, hipStream_t st) {
+    const void* fn = coresident_kernel(dtype, wc, deep);
+    if (fn == nullptr) return hipErrorInvalidValue;
+    KernelArgs args = a;
+    void* params[] = {&args};
+    return hipLaunchCooperativeKernel(fn, dim3(unsigned(a.n_coop * a.n_tiles)), dim3(bwd_threads(dtype, wc)), params, 0,
+                                      st);
 }
 
 hipError_t launch_fwd_column(int dtype, const KernelArgs& a, hipStream_t st) {

@@ -166,6 +166,9 @@ def test_options(lib):
     o.lookback = 3
     assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
     o.lookback = 0
+    o.leaves = 3
+    assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
+    o.leaves = 0
     o.reserved[2] = 1
     assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
 

@@ -347,3 +347,18 @@ def test_bench_workload_sampled_heads_chunk_wy():
         for n, gr, r in zip(NAMES, grads, r_grads):
             rel["d_" + n] = close("d_" + n, gr[b:b + 1, h:h + 1], r)
         print("  relative max errors:", {k: f"{v:.1e}" for k, v in rel.items()}, flush=True)
+
+
+def test_boundary_of_another_chunk_is_refused():
+    """The saved state is tagged with the chunk that wrote it: chunks 4 and 5
+    at T = 11 give states of the same size, and the backward must not take
+    one for the other."""
+    arrays = make_gdn2_random_inputs(1, 2, 11, 8, 16, seed=3)
+    dev = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
+    d_ctx = torch.ones((1, 2, 11, 16), device=DEV)
+    _, _, bnd4 = capi.gdn2_fwd(*dev, chunk=4)
+    assert bnd4.numel() == capi.load().gdn2_boundary_bytes(1, 2, 11, 8, 16, 5) // 4
+    with pytest.raises(ValueError, match="chunk 4"):
+        capi.gdn2_bwd(*dev[:6], bnd4, d_ctx, chunk=5)
+    capi.gdn2_bwd(*dev[:6], bnd4, d_ctx, chunk=4)
+    torch.cuda.synchronize()

@@ -47,19 +47,30 @@ def to_f64(t):
     return t.float().cpu().numpy().astype(np.float64) if t is not None else None
 
 
+# Backward modes without saved state, forced: the forward pre-pass over q, or
+# the co-resident single pass.
+LEAVES_MODES = ("prepass", "coresident")
+
+
 def path_options(path):
-    """A test's path name as (path, lookback): "fenwick" and "grouped" are the
-    look-back path with that carry scheme forced."""
-    return ("chunked", path) if path in ("fenwick", "grouped") else (path, None)
+    """A test's path name as binding options: "fenwick" and "grouped" are the
+    look-back path with that carry scheme forced, "prepass" and "coresident"
+    the look-back path with that leaves-only backward forced (they matter only
+    without saved state)."""
+    if path in ("fenwick", "grouped"):
+        return dict(path="chunked", lookback=path), {}
+    if path in LEAVES_MODES:
+        return dict(path="chunked"), dict(leaves=path)
+    return dict(path=path), {}
 
 
 def run_device(inp, path=None, use_ckpt=True, want_dq=True, want_dinit=True, stream=None):
     q, init, d = to_dev(inp.q, inp.dtype), to_dev(inp.init, inp.dtype), to_dev(inp.d_cum, inp.dtype)
     ck = capi.new_ckpt(q) if use_ckpt else None
-    path, lookback = path_options(path)
-    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, lookback=lookback, stream=stream)
+    opts, bwd_only = path_options(path)
+    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, stream=stream, **opts)
     d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ckpt=ck, want_dq=want_dq, want_dinit=want_dinit,
-                                        path=path, lookback=lookback, stream=stream)
+                                        stream=stream, **opts, **bwd_only)
     assert capi.default_workspace.status(q.device, stream) == 0, "a cross-block wait hit its spin limit"
     return cum, d_q, d_init
 
@@ -129,7 +140,8 @@ def test_config_full_parity(name, use_ckpt):
 @pytest.mark.parametrize("name", ["tiny", "medium"])
 @pytest.mark.parametrize("path,use_ckpt", [("chunked", False), ("column", True), ("column", False),
                                            ("rscan", True), ("rscan", False), ("fenwick", True),
-                                           ("fenwick", False), ("grouped", True)])
+                                           ("fenwick", False), ("grouped", True), ("prepass", False),
+                                           ("coresident", False)])
 def test_config_other_paths(name, path, use_ckpt):
     print(f"[config {name} path={path} ckpt={use_ckpt}]", flush=True)
     compare(make_config(name), path=path, use_ckpt=use_ckpt)
@@ -142,14 +154,14 @@ EDGE_HJ = [(1, 1), (1, 3), (4, 4), (4, 8), (8, 8), (5, 13), (10, 10)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "fenwick", "grouped"])
+@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "fenwick", "grouped", "prepass", "coresident"])
 def test_edge_shapes(dtype, path):
     for s in EDGE_S:
         for (h, j) in EDGE_HJ:
             for b in (1, 3):
                 inp = make_inputs(b, s, h, j, "unit", dtype, seed=s * 131 + h * 7 + j + b)
                 print(f"[edge b={b} s={s} h={h} j={j} {dtype} {path}]", flush=True)
-                compare(inp, path=path)
+                compare(inp, path=path, use_ckpt=path not in LEAVES_MODES)
 
 
 def test_random_shapes():
@@ -166,6 +178,8 @@ def test_random_shapes():
         dtype = "bf16" if rng.random() < 0.3 else "f32"
         path = "column" if rng.random() < 0.2 else "chunked"
         use_ckpt = bool(rng.random() < 0.7)
+        if not use_ckpt and path == "chunked":
+            path = LEAVES_MODES[it % 2]
         inp = make_inputs(b, s, h, j, "unit", dtype, seed=1000 + it)
         print(f"[random {it}: b={b} s={s} h={h} j={j} {dtype} {path} ckpt={use_ckpt}]", flush=True)
         compare(inp, path=path, use_ckpt=use_ckpt)
@@ -180,6 +194,8 @@ def test_many_tiles_ragged(s, hj):
     ref = reference(inp)
     for path in ("chunked", "rscan", "fenwick", "grouped"):
         compare(inp, path=path, ref=ref)
+        compare(inp, path=path, use_ckpt=False, ref=ref)
+    for path in LEAVES_MODES:
         compare(inp, path=path, use_ckpt=False, ref=ref)
 
 
@@ -214,12 +230,21 @@ def test_drift_bf16_column_path():
 
 # ------------------------------------------------------------- API semantics
 
-def test_checkpoint_and_leaves_only_agree_bitwise():
+def test_checkpoint_and_prepass_leaves_only_agree_bitwise():
+    """The pre-pass (the default leaves-only backward) writes exactly the
+    boundary state the forward saves, so that leaves-only backward equals the
+    saved-state one bit for bit.  The co-resident pass combines the tiles'
+    products in another order: it matches to rounding, and the oracle."""
     inp = make_config("medium")
     a = run_device(inp, use_ckpt=True)
-    b = run_device(inp, use_ckpt=False)
+    b = run_device(inp, path="prepass", use_ckpt=False)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+    ref = reference(inp)
+    c = run_device(inp, path="coresident", use_ckpt=False)
+    for name, x, y, r in zip(("cum", "d_q", "d_init"), a, c, ref):
+        check(name, to_f64(y), r, inp.dtype, inp.s)
+        assert torch.allclose(x, y, rtol=1e-6, atol=1e-6)
 
 
 def test_optional_gradients():
@@ -316,7 +341,7 @@ def test_workspace_reuse_small_then_large_shapes():
         compare(inp, path="chunked", use_ckpt=False)
 
 
-@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "grouped"])
+@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "grouped", "coresident"])
 def test_zero_step_is_reported(path):
     """A step that is exactly zero makes every later prefix product zero: the
     forward stays exact, and the backward (whose exact form divides by |P_t|^2)
@@ -327,12 +352,12 @@ def test_zero_step_is_reported(path):
     q, init, d = to_dev(inp.q, "f32"), to_dev(inp.init, "f32"), to_dev(inp.d_cum, "f32")
     print(f"[zero step {path}]", flush=True)
     ws = capi.Workspace()
-    ck = capi.new_ckpt(q)
-    path, lookback = path_options(path)
-    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path, lookback=lookback, workspace=ws)
+    ck = None if path in LEAVES_MODES else capi.new_ckpt(q)
+    opts, bwd_only = path_options(path)
+    cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, workspace=ws, **opts)
     assert ws.status(q.device) == 0
     check("cum", to_f64(cum), oracle.fwd(inp.q64, inp.init64), "f32", inp.s)
-    capi.quat_cumprod_bwd(q, init, d, ck, path=path, lookback=lookback, workspace=ws)
+    capi.quat_cumprod_bwd(q, init, d, ck, workspace=ws, **opts, **bwd_only)
     assert ws.status(q.device) == 2            # QC_STATUS_ZERO, and cleared by the read
     assert ws.status(q.device) == 0
 
@@ -349,3 +374,5 @@ def test_rscan_and_lookback_agree_on_long_chains(dtype):
         for path in ("rscan", "chunked", "fenwick", "grouped"):
             for use_ckpt in (True, False):
                 compare(inp, path=path, use_ckpt=use_ckpt, ref=ref)
+        for path in LEAVES_MODES:
+            compare(inp, path=path, use_ckpt=False, ref=ref)
