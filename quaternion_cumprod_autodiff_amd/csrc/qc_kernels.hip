@@ -704,10 +704,11 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 // storage precision.
 
 // Waves per SIMD to ask of the compiler: 3 while the slice's q and d_cum fit
-// in 64 registers, else 2.
+// in 64 registers, else 2; bfloat16 slices (float32 arithmetic) fit 4.
 template <class IO, int L>
 constexpr int bwd_min_waves() {
-    return L * 2 * int(sizeof(typename IO::Raw)) / 4 <= 64 ? 3 : 2;
+    return IO::kDtype == 1 && L * 2 * int(sizeof(typename IO::Raw)) / 4 <= 64 ? 4
+         : L * 2 * int(sizeof(typename IO::Raw)) / 4 <= 64 ? 3 : 2;
 }
 
 template <class IO, int WC, int L, int NW, int kMode>
@@ -853,7 +854,8 @@ __device__ __forceinline__ TileCoord tile_at(const KernelArgs& a, int64_t chain,
 }
 
 template <class IO, int WC, int L, int NW>
-__global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_coresident_kernel(KernelArgs a) {
+__global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>() < 3 ? bwd_min_waves<IO, L>() : 3))
+    bwd_coresident_kernel(KernelArgs a) {
     a.epoch = launch_epoch(a);
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
