@@ -212,17 +212,35 @@ __device__ __forceinline__ bool latent_ok(const WyArgs& a, int64_t t0, int tid, 
 // One or two [B, H, T, D] tensors' values of a chunk's dense tile, element
 // tid + i * kThreads of the [CP][kDN] tile (clamped copies past T or past D:
 // mask with dense_ok).
+// Addressing of the per-chunk tiles: one block-uniform 64-bit base (the
+// tile's first element), then 32-bit offsets row * D + column per element,
+// clamped in 32 bits.  Per-element 64-bit index arithmetic (multiplies,
+// compares, selects) had made issuing a chunk's prefetch take about as long
+// as the chunk's first matrix product.
+__device__ __forceinline__ int64_t tile_base(const WyArgs& a, int64_t head, int64_t t0, int64_t d0) {
+    return (head * a.T + t0) * a.D + d0;
+}
+__device__ __forceinline__ int last_row(const WyArgs& a, int64_t t0, int rows) {
+    return a.T - t0 < rows ? int(a.T - t0) - 1 : rows - 1;
+}
+__device__ __forceinline__ int last_col(const WyArgs& a, int64_t d0) {
+    return a.D - d0 < kDN ? int(a.D - d0) - 1 : kDN - 1;
+}
+
 template <int CP, bool kTwo>
 __device__ __forceinline__ void load_dense(const float* x, const float* y, const WyArgs& a, int64_t head, int64_t t0,
                                            int64_t d0, int tid, float* xv, float* yv) {
     constexpr int EPT = CP * kDN / kThreads;
+    const int64_t base = tile_base(a, head, t0, d0);
+    const float* xb = x + base;
+    const float* yb = kTwo ? y + base : nullptr;
+    const int lr = last_row(a, t0, CP), lc = last_col(a, d0), D = int(a.D);
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-        const int64_t t = t0 + row, d = d0 + n;
-        const int64_t gi = (head * a.T + (t < a.T ? t : a.T - 1)) * a.D + (d < a.D ? d : a.D - 1);
-        xv[i] = x[gi];
-        if constexpr (kTwo) yv[i] = y[gi];
+        const int off = (row < lr ? row : lr) * D + (n < lc ? n : lc);
+        xv[i] = xb[off];
+        if constexpr (kTwo) yv[i] = yb[off];
     }
 }
 
@@ -496,6 +514,8 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
         }
         __syncthreads();
         // U = T rhs (T lower triangular).
+        const int lr = last_row(a, t0, CP), lc = last_col(a, d0), D = int(a.D);
+        float* ub = kRec ? a.ubuf + (head * nb * CP + t0) * a.D + d0 : nullptr;
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
             f32x4 acc = zero4();
@@ -505,11 +525,12 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
                 const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
                 sU[row * kDS + col] = acc[r];
                 // U is kept for the backward (rows of the padded chunk, columns < D).
-                if (kRec && d0 + col < a.D) a.ubuf[(head * nb * CP + t0 + row) * a.D + d0 + col] = acc[r];
+                if (kRec && col <= lc) ub[row * D + col] = acc[r];
             }
         }
         __syncthreads();
         // O = (Qc S0 + Bq U) / sqrt(L).
+        float* ob = a.ctx + tile_base(a, head, t0, d0);
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
             f32x4 acc = zero4();
@@ -517,8 +538,8 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
             mma16<CP, CS, 1, kDS, 1>(acc, f.Bq + ti * 16 * CS, sU + tj * 16, ti + 1, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t t = t0 + ti * 16 + acc_row(lane, r), d = d0 + tj * 16 + acc_col(lane);
-                if (t < a.T && d < a.D) a.ctx[(head * a.T + t) * a.D + d] = acc[r] * a.scale;
+                const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
+                if (row <= lr && col <= lc) ob[row * D + col] = acc[r] * a.scale;
             }
         }
         // S_end = diag(c_last) S0 + Kt^T U.
@@ -539,6 +560,10 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
             }
         }
         __syncthreads();
+        // The state goes to the next chunk's boundary slot, or (last chunk)
+        // to the final state.
+        float* sb = c + 1 < nb ? (a.bnd ? a.bnd + (head * nb + c + 1) * LP * a.D + d0 : nullptr)
+                               : (a.state ? a.state + head * a.L * a.D + d0 : nullptr);
 #pragma unroll
         for (int s = 0; s < NSW; ++s) {
             const int job = wave + 4 * s;
@@ -548,13 +573,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int l = ti * 16 + acc_row(lane, r), n = tj * 16 + acc_col(lane);
                     sS[l * kDS + n] = snew[s][r];
-                    if (l < a.L && d0 + n < a.D) {
-                        if (c + 1 < nb) {
-                            if (a.bnd) a.bnd[((head * nb + c + 1) * LP + l) * a.D + d0 + n] = snew[s][r];
-                        } else if (a.state) {
-                            a.state[(head * a.L + l) * a.D + d0 + n] = snew[s][r];
-                        }
-                    }
+                    if (sb && l < a.L && n <= lc) sb[l * D + n] = snew[s][r];
                 }
             }
         }
@@ -600,12 +619,16 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
     const int my_ti = (wave >> 1) % NT, my_tj = wave & 1;
     float vt[4], wt[4];
     auto load_vw = [&](int64_t tc0) {   // raw (clamped), masked where consumed
+        const int64_t base = tile_base(a, head, tc0, d0);
+        const float* vb = a.v + base;
+        const float* wb = a.w + base;
+        const int lr = last_row(a, tc0, CP), lc = last_col(a, d0), D = int(a.D);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t t = tc0 + my_ti * 16 + acc_row(lane, r), d = d0 + my_tj * 16 + acc_col(lane);
-            const int64_t gi = (head * a.T + (t < a.T ? t : a.T - 1)) * a.D + (d < a.D ? d : a.D - 1);
-            vt[r] = a.v[gi];
-            wt[r] = a.w[gi];
+            const int row = my_ti * 16 + acc_row(lane, r), col = my_tj * 16 + acc_col(lane);
+            const int off = (row < lr ? row : lr) * D + (col < lc ? col : lc);
+            vt[r] = vb[off];
+            wt[r] = wb[off];
         }
     };
     load_rec<CP, LP>(rr, a.rec + (head * nb + nb - 1) * R::kSize, tid);
@@ -642,6 +665,11 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
         }
         __syncthreads();
         // drhs = T^T dU.
+        const int lr = last_row(a, t0, CP), lc = last_col(a, d0), D = int(a.D);
+        float* rb = a.drhs + (head * nb * CP + t0) * a.D + d0;
+        const int64_t gbase = tile_base(a, head, t0, d0);
+        float* dwb = a.dw ? a.dw + gbase : nullptr;
+        float* dvb = a.dv ? a.dv + gbase : nullptr;
         for (int job = wave; job < NT * 2; job += 4) {
             const int ti = job >> 1, tj = job & 1;
             f32x4 acc = zero4();
@@ -650,13 +678,12 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
                 sR[row * kDS + col] = acc[r];
-                const int64_t t = t0 + row, d = d0 + col;
-                if (d < a.D) {
-                    const int64_t gi = (head * a.T + t) * a.D + d;
-                    a.drhs[(head * nb * CP + t) * a.D + d] = acc[r];   // for the gradient kernel
-                    if (t < a.T) {
-                        if (a.dw) a.dw[gi] = acc[r] * vc[r];
-                        if (a.dv) a.dv[gi] = acc[r] * wc[r];
+                if (col <= lc) {
+                    const int off = row * D + col;
+                    rb[off] = acc[r];   // for the gradient kernel
+                    if (row <= lr) {
+                        if (dwb) dwb[off] = acc[r] * vc[r];
+                        if (dvb) dvb[off] = acc[r] * wc[r];
                     }
                 }
             }
@@ -680,6 +707,10 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
             }
         }
         __syncthreads();
+        // dS entering this chunk: the previous chunk's slot, or (first chunk)
+        // d initial_state.
+        float* db = c > 0 ? a.dbnd + (head * nb + c - 1) * LP * a.D + d0
+                          : (a.ds0 ? a.ds0 + head * a.L * a.D + d0 : nullptr);
 #pragma unroll
         for (int sl = 0; sl < NSW; ++sl) {
             const int job = wave + 4 * sl;
@@ -689,12 +720,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int l = ti * 16 + acc_row(lane, r), n = tj * 16 + acc_col(lane);
                     sS[l * kDS + n] = dnew[sl][r];
-                    if (l < a.L && d0 + n < a.D) {
-                        if (c > 0)
-                            a.dbnd[((head * nb + c - 1) * LP + l) * a.D + d0 + n] = dnew[sl][r];
-                        else if (a.ds0)
-                            a.ds0[(head * a.L + l) * a.D + d0 + n] = dnew[sl][r];
-                    }
+                    if (db && l < a.L && n <= lc) db[l * D + n] = dnew[sl][r];
                 }
             }
         }
@@ -751,21 +777,29 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     // values are raw (clamped) and masked where consumed.
     float sv[EPL], dsv[EPL], uu[EPT], rv[EPT], oo[EPT];
     const int xl_l = tid / TPL, xl_n0 = (tid % TPL) * EPL;
+    const int xl_lc = xl_l < a.L ? xl_l : int(a.L) - 1, D = int(a.D);
     auto load_tile = [&](int64_t d0) {
+        // Block-uniform bases and 32-bit clamped offsets (see tile_base).
+        const int lc = last_col(a, d0);
+        const int64_t sbase = (head * nb + c) * LP * a.D + d0;
+        const float* sb = a.bnd_in + sbase;
+        const float* dsb = a.dbnd + sbase;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            const int64_t d = d0 + xl_n0 + i;
-            const int64_t gi = ((head * nb + c) * LP + (xl_l < a.L ? xl_l : a.L - 1)) * a.D + (d < a.D ? d : a.D - 1);
-            sv[i] = a.bnd_in[gi];
-            dsv[i] = a.dbnd[gi];
+            const int n = xl_n0 + i;
+            const int off = xl_lc * D + (n < lc ? n : lc);
+            sv[i] = sb[off];
+            dsv[i] = dsb[off];
         }
+        const int64_t ubase = (head * nb * CP + t0) * a.D + d0;
+        const float* ub = a.ubuf + ubase;
+        const float* rb = a.drhs + ubase;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-            const int idx = tid + i * kThreads;
-            const int64_t d = d0 + idx % kDN;
-            const int64_t gi = (head * nb * CP + t0 + idx / kDN) * a.D + (d < a.D ? d : a.D - 1);
-            uu[i] = a.ubuf[gi];
-            rv[i] = a.drhs[gi];
+            const int idx = tid + i * kThreads, n = idx % kDN;
+            const int off = (idx / kDN) * D + (n < lc ? n : lc);
+            uu[i] = ub[off];
+            rv[i] = rb[off];
         }
         load_dense<CP, false>(a.dctx, nullptr, a, head, t0, d0, tid, oo, nullptr);
     };
