@@ -273,14 +273,6 @@ qc::KernelArgs column_args(const Plan& p, void* ws) {
 // could pay it measured slower than the look-back, so AUTO never takes it.
 bool use_rscan(int path) { return path == QC_PATH_RSCAN; }
 
-// The leaves-only backward in one co-resident pass (no pre-pass over q) runs
-// only when asked for (QC_LEAVES_CORESIDENT) and at least one chain fits on
-// the device at once.  It reads q once, but each group of blocks walks its
-// chains in lockstep with two look-backs per chain, which the other groups'
-// streaming does not hide: measured slower than the pre-pass at every
-// workload (headline backward 613 us against 392, medium 45.5 against 34.5,
-// drift 781 against 423), so AUTO keeps the pre-pass.
-
 // Chains the co-resident backward can hold at once on the current device
 // (occupancy of its kernel, cached per device and instance).
 int64_t coresident_groups(const Plan& p) {
@@ -304,7 +296,13 @@ int64_t coresident_groups(const Plan& p) {
 }
 
 // Launches the co-resident leaves-only backward if the options and the shape
-// allow it; *done tells whether it did.
+// allow it; *done tells whether it did.  It runs only when asked for
+// (QC_LEAVES_CORESIDENT), outside graph capture, and when at least one chain
+// fits on the device at once.  It reads q once, but each group of blocks
+// walks its chains in lockstep with two look-backs per chain, which the other
+// groups' streaming does not hide: measured slower than the pre-pass at every
+// workload (headline backward 613 us against 392, medium 45.5 against 34.5,
+// drift 781 against 423), so AUTO keeps the pre-pass.
 int try_bwd_coresident(const Plan& p, const Options& o, const void* q, const void* init, const void* d_cum,
                        void* d_q, void* d_init, void* ws, hipStream_t st, bool* done) {
     *done = false;
