@@ -143,15 +143,19 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
     cols = q.shape[2] * q.shape[3]
     threads = oracle.threads(0)
     oracle.fwd(q[:, :64], init)             # load and warm up
-    reps, t_total = 0, 0.0
+    reps, t_total, each = 0, 0.0, []
     while t_total < min_seconds or reps == 0:
         t0 = time.perf_counter()
         oracle.fwd(q, init, threads)
+        t1 = time.perf_counter()
         oracle.bwd(q, init, d, threads)
         t_total += time.perf_counter() - t0
+        each.append((t1 - t0, time.perf_counter() - t1))
         reps += 1
     per_pass = t_total / reps
     gbps = (80.0 * n + 32.0 * cols) / per_pass / 1e9
+    fwd_med = float(np.median([f for f, _ in each]))    # forward and backward separately, medians
+    bwd_med = float(np.median([b for _, b in each]))
     # One thread on 1/16 of the same sample (the first 64 columns), same byte formula.
     s_len = q.shape[1]
     q1 = np.ascontiguousarray(q.reshape(1, s_len, cols, 4)[:, :, :64])
@@ -169,6 +173,9 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
             "sample": f"batch entry 0 of the workload ({cols} columns x {q.shape[1]} steps = {n} quaternions), "
                       f"float64 forward + reverse-recurrence backward, {reps} pass(es), {per_pass:.2f} s per pass",
             "cpu_model": cpu_model(),
+            "fwd_GBps": round((32.0 * n + 16.0 * cols) / fwd_med / 1e9, 4),
+            "bwd_GBps": round((48.0 * n + 32.0 * cols) / bwd_med / 1e9, 4),
+            "fwd_s_median": round(fwd_med, 5), "bwd_s_median": round(bwd_med, 5),
             "one_thread": {"value": round(gbps1, 4), "unit": "GB/s", "cores": 1,
                            "sample": f"the first 64 columns of the same sample ({n1} quaternions), "
                                      f"{reps1} pass(es), {t1 / reps1:.3f} s per pass"}}
