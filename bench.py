@@ -19,8 +19,10 @@ forward / backward split.
 
 Reported value: algorithmic bytes per step (32 B/quaternion forward + 48 B
 backward, plus 16 B per column for init and d_init) / wall time per step.
-The line also reports the leaves-only mode (no saved boundary state; the
-backward re-derives it from q), timed after the main region.
+The line also reports, timed after the main region, the final-carry mode
+(the forward saves only cum[:, s-1] per column and the backward rebuilds the
+rest from the end of the sequence) and the leaves-only mode (nothing saved;
+the backward re-derives the boundary state from q).
 The last stdout line is one JSON record; diagnostics go to stderr.
 """
 from __future__ import annotations
@@ -29,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -689,8 +692,9 @@ def all_configs_bench(args):
         cum, d_q, d_init = torch.empty_like(q), torch.empty_like(q), torch.empty_like(init)
         fwd_bytes = 2 * io_bytes * n + io_bytes * cols
         bwd_bytes = 3 * io_bytes * n + 2 * io_bytes * cols
-        for mode in ("saved boundary state", "leaves-only"):
-            ckpt = capi.new_ckpt(q) if mode == "saved boundary state" else None
+        for mode in ("saved boundary state", "final carry", "leaves-only"):
+            ckpt = {"saved boundary state": lambda: capi.new_ckpt(q), "final carry": lambda: capi.new_ckpt(q, "final"),
+                    "leaves-only": lambda: None}[mode]()
 
             def fwd():
                 capi.quat_cumprod_fwd(q, init, cum, ckpt)
@@ -758,8 +762,9 @@ def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command:
     """Write profiles/kernels_<config>.txt from a rocprofv3 --kernel-trace
     --stats run (and, with pmc_dir, its FETCH_SIZE / WRITE_SIZE runs scaled by
     the plain-copy calibration factors of traffic_headline.txt).  Kernel
-    template arguments: <IO, column-group width, steps per lane, waves, ...,
-    mode>, mode 0 = Fenwick look-back, 3 = grouped look-back."""
+    template arguments: forward <IO, column-group width, steps per lane,
+    waves, stores cum, mode>, backward <IO, width, steps per lane, waves, mode,
+    from the final carry>; mode 0 = Fenwick look-back, 3 = grouped look-back."""
     import csv
     import statistics
 
@@ -809,7 +814,9 @@ def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command:
         for k in sorted(set(f) & set(w)):
             if "zero_words" in k or "bump_epoch" in k or "at::native" in k or "rocclr" in k:
                 continue
-            base = next((v for key, v in alg.items() if key in k and ", false>" not in k), None)
+            # (no algorithmic share for the boundary pre-pass: a forward that stores no cum)
+            prepass = re.search(r"fwd_chunked_kernel<.*, false, \d+>", k) is not None
+            base = None if prepass else next((v for key, v in alg.items() if key in k), None)
             tot = f[k] * fs + w[k] * ws
             lines.append(f"{short_kernel_name(k)[:72]:72s} {f[k] * fs:14.0f} {w[k] * ws:14.0f} "
                          f"{(base if base else 0):14d} {(tot / base if base else 0):6.3f}")
@@ -833,13 +840,15 @@ def main():
     ap.add_argument("--lookback", default=None, choices=["auto", "fenwick", "grouped"])
     ap.add_argument("--leaves", default=None, choices=["auto", "prepass", "coresident"],
                     help="how the leaves-only backward re-derives the boundary products")
+    ap.add_argument("--saved", default="boundary", choices=["boundary", "final"],
+                    help="what the timed forward saves for its backward (with --leaves-only: nothing)")
     ap.add_argument("--leaves-only", action="store_true",
                     help="backward without the saved boundary state (re-derives it from q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the backward's event records (each adds a few us of idle)")
-    ap.add_argument("--leaves-steps", type=int, default=50,
-                    help="after the timed region, also time this many leaves-only steps (0: skip)")
+    ap.add_argument("--leaves-steps", type=int, default=100,
+                    help="after the timed region, also time this many steps of each other backward mode (0: skip)")
     ap.add_argument("--event-every", type=int, default=4,
                     help="bracket every N-th timed backward with events (N=1: every one)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -932,7 +941,9 @@ def main():
     cum = torch.empty_like(q)
     d_q = torch.empty_like(q)
     d_init = torch.empty_like(init)
-    ckpt = None if args.leaves_only else capi.new_ckpt(q)
+    ckpt = None if args.leaves_only else capi.new_ckpt(q, args.saved)
+    timed_mode = "leaves-only" if args.leaves_only else {"boundary": "saved boundary state",
+                                                         "final": "final carry"}[args.saved]
 
     def fwd():
         capi.quat_cumprod_fwd(q, init, cum, ckpt, path=args.path, lookback=args.lookback)
@@ -991,31 +1002,46 @@ def main():
     fwd_ms = float(np.median([f0.elapsed_time(f1) for (f0, f1), _ in diag]))
     bwd_ms_diag = float(np.median([b0.elapsed_time(b1) for _, (b0, b1) in diag]))
 
-    # The page-faithful mode, reported beside the timed one: the forward saves
-    # nothing beyond the leaves and the backward re-derives the boundary state
-    # from q (one more read of q).  Same workload, same algorithmic bytes.
-    leaves = None
-    if not args.leaves_only and args.leaves_steps > 0:
-        def fwd_lo():
-            capi.quat_cumprod_fwd(q, init, cum, None, path=args.path, lookback=args.lookback)
+    # The other backward modes, reported beside the timed one on the same
+    # workload with the same algorithmic bytes: the page-faithful leaves-only
+    # mode (the forward saves nothing beyond the leaves and the backward
+    # re-derives the boundary state from q, one more read of q), and the
+    # final-carry mode (the forward saves only cum[:, s-1]; the backward reads
+    # q and d_cum once and rebuilds cum from the end of the sequence).
+    def time_mode(state):
+        def fwd_m():
+            capi.quat_cumprod_fwd(q, init, cum, state, path=args.path, lookback=args.lookback)
 
-        def bwd_lo():
-            capi.quat_cumprod_bwd(q, init, d_cum, None, d_q=d_q, d_init=d_init, path=args.path, lookback=args.lookback,
-                                  leaves=args.leaves)
+        def bwd_m():
+            capi.quat_cumprod_bwd(q, init, d_cum, state, d_q=d_q, d_init=d_init, path=args.path,
+                                  lookback=args.lookback, leaves=args.leaves)
 
-        for _ in range(10):
-            fwd_lo()
-            bwd_lo()
+        # Its own settle phase: a mode timed right after a change of kernels
+        # otherwise reads a few percent slow for its first tens of steps.
+        warm, t_w = 0, time.perf_counter()
+        while warm < 10 or (time.perf_counter() - t_w) * 1e3 < args.settle_ms / 2:
+            fwd_m()
+            bwd_m()
+            warm += 1
+            if warm % 16 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
-        t_lo = time.perf_counter()
+        t_m = time.perf_counter()
         for _ in range(args.leaves_steps):
-            fwd_lo()
-            bwd_lo()
+            fwd_m()
+            bwd_m()
         torch.cuda.synchronize()
-        ms_lo = (time.perf_counter() - t_lo) / args.leaves_steps * 1e3
+        ms_m = (time.perf_counter() - t_m) / args.leaves_steps * 1e3
         if capi.default_workspace.status(dev) != 0:
-            raise RuntimeError("a cross-block wait hit its spin limit during the leaves-only steps")
-        leaves = ms_lo
+            raise RuntimeError("a cross-block wait hit its spin limit during the extra steps")
+        return ms_m
+
+    other_modes = {}
+    if args.leaves_steps > 0:
+        if timed_mode != "final carry" and args.path != "rscan":   # (no final-carry reduce-then-scan)
+            other_modes["final_carry"] = time_mode(capi.new_ckpt(q, "final"))
+        if timed_mode != "leaves-only":
+            other_modes["leaves_only"] = time_mode(None)
 
     ms_step = wall / args.steps * 1e3
     fwd_bytes = 2 * io_bytes * n + io_bytes * cols
@@ -1027,7 +1053,7 @@ def main():
     bwd_gbps = bwd_bytes / (bwd_ms_roof * 1e-3) / 1e9
     workload = f"{args.config} b{b} s{s} h{h} j{j} {io} I/O, forward + backward"
     traffic = (load_traffic(workload) if (args.path in (None, "auto", "chunked") and args.lookback in (None, "auto")
-                                          and not args.leaves_only) else None)
+                                          and timed_mode == "saved boundary state") else None)
 
     rec = {
         "metric": METRIC,
@@ -1044,8 +1070,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "b": b, "s": s, "h": h, "j": j, "io_dtype": io, "recipe": recipe,
                    "path": args.path or "auto", "lookback": args.lookback or "auto",
-                   "leaves": args.leaves or "auto",
-                   "backward": "leaves-only" if args.leaves_only else "saved boundary state"},
+                   "leaves": args.leaves or "auto", "backward": timed_mode},
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "elements_per_s": round(n / (ms_step * 1e-3), 1),
         "untimed_steps": warm_steps,
@@ -1059,11 +1084,12 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
-    if leaves is not None:
-        rec["leaves_only"] = {
-            "value": round((fwd_bytes + bwd_bytes) / (leaves * 1e-3) / 1e9, 2), "unit": "GB/s",
-            "ms_per_step": round(leaves, 4), "steps": args.leaves_steps,
-            "mode": "forward saves only q and init; backward re-derives the boundary state from q"}
+    mode_text = {"leaves_only": "forward saves only q and init; backward re-derives the boundary state from q",
+                 "final_carry": "forward saves only its final carry per column; backward reads q and d_cum once"}
+    for key, ms_m in other_modes.items():
+        rec[key] = {"value": round((fwd_bytes + bwd_bytes) / (ms_m * 1e-3) / 1e9, 2), "unit": "GB/s",
+                    "hbm_frac": round((fwd_bytes + bwd_bytes) / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "ms_per_step": round(ms_m, 4), "steps": args.leaves_steps, "mode": mode_text[key]}
     # Practical ceiling beside the roofline: the library's hand-written
     # streaming copy of one tensor of the workload (read + write), after the
     # timed region, at its best grid of a short sweep.

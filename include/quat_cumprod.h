@@ -125,11 +125,29 @@ enum {
                                  Never chosen by AUTO (slower than the pre-pass where measured). */
 };
 
+/* What the forward saves into the ckpt buffer and the backward reads from it.
+ * Forward and backward of one scan must use the same kind.  The backward's
+ * formula is the one stated at the top either way; with QC_SAVED_FINAL it is
+ * evaluated from the end of the sequence: G[t] by the page's reverse
+ * recurrence G[t] = d_cum[t] + conj(q_{t+1}) (x) G[t+1], and cum[t-1] as
+ * q_t^-1 (x) cum[t] from the final carry (products over later steps, inverted;
+ * the same non-zero precondition as above). */
+enum {
+    QC_SAVED_BOUNDARY = 0,  /* the prefix products at a fixed stride of steps (quat_cumprod_ckpt_bytes):
+                               the backward reads q and d_cum once */
+    QC_SAVED_FINAL = 1      /* only the final carry cum[:, s-1] of every column, in the internal
+                               precision (b*h*j quaternions): the backward still reads q and d_cum
+                               once, from this alone (look-back paths; with QC_PATH_COLUMN the
+                               column backward recomputes from q and ignores it; QC_PATH_RSCAN
+                               refuses it) */
+};
+
 typedef struct {
     int32_t path;           /* QC_PATH_* */
     int32_t lookback;       /* QC_LOOKBACK_*; ignored by the other paths */
     int32_t leaves;         /* QC_LEAVES_*; ignored when a ckpt is given */
-    int32_t reserved[5];    /* must be zero */
+    int32_t saved;          /* QC_SAVED_*: the kind of the ckpt buffer, if one is given */
+    int32_t reserved[4];    /* must be zero */
 } qc_options;
 
 /* Bytes of workspace that quat_cumprod_fwd and quat_cumprod_bwd need for this
@@ -144,14 +162,21 @@ size_t quat_cumprod_workspace_bytes(int64_t b, int64_t s, int64_t h, int64_t j, 
  * invalid arguments. */
 size_t quat_cumprod_ckpt_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype);
 
+/* Same for the ckpt kind that opts->saved names (opts may be NULL = the
+ * boundary state); QC_SAVED_FINAL needs b*h*j quaternions in the internal
+ * precision, whatever s.  Returns 0 for invalid arguments or options. */
+size_t quat_cumprod_ckpt_bytes_ex(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
+                                  const qc_options* opts);
+
 /* Zero a workspace on `stream` with a fill kernel (so it may be captured in a
  * HIP graph).  Needed once per allocation. */
 int quat_cumprod_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Forward scan (the page's Mamba3QuatScanBackendExt::quat_cumprod).
  *   q      [b,s,h,j,4] in      init [b,h,j,4] in      cum [b,s,h,j,4] out
- *   ckpt   optional out (NULL = none): saved boundary state for the
- *          backward, ckpt_bytes >= quat_cumprod_ckpt_bytes(...). */
+ *   ckpt   optional out (NULL = none): saved state for the backward,
+ *          ckpt_bytes >= quat_cumprod_ckpt_bytes(...) (the _ex form: of the
+ *          kind opts->saved, sized by quat_cumprod_ckpt_bytes_ex). */
 int quat_cumprod_fwd(const void* q, const void* init, void* cum,
                      void* ckpt, size_t ckpt_bytes,
                      int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype,
@@ -160,11 +185,12 @@ int quat_cumprod_fwd(const void* q, const void* init, void* cum,
 /* Backward (the page's quat_scan_backward): recomputes the prefix products
  * from the saved leaves q and init, never from stored scan intermediates.
  *   q, init, d_cum   in
- *   ckpt             optional in (NULL = none): the boundary state written by
- *                    quat_cumprod_fwd for the same q, shape and dtype.  With
- *                    it the backward reads q and d_cum once; without it the
- *                    backward first re-derives the boundary prefix products
- *                    from q (one more read of q).
+ *   ckpt             optional in (NULL = none): the state written by
+ *                    quat_cumprod_fwd for the same q, init, shape, dtype (and,
+ *                    for the _ex forms, the same opts->saved).  With it the
+ *                    backward reads q and d_cum once; without it the backward
+ *                    first re-derives the boundary prefix products from q (one
+ *                    more read of q).
  *   d_q [b,s,h,j,4], d_init [b,h,j,4]   out, each optional (NULL = not
  *                    wanted, as for an untracked input); both NULL is a no-op. */
 int quat_cumprod_bwd(const void* q, const void* init, const void* d_cum,

@@ -5,9 +5,12 @@ Mirrors the custom autodiff node of the burn-mamba source page
 of ``quat_cumprod`` and its ``Backward`` node):
 
 * the node keeps only its leaves q and init, never scan intermediates; here it
-  may also keep the O(N/64) saved boundary state the forward writes, so the
-  backward reads q and d_cum once (``save_boundary_state=False`` keeps the
-  leaves only, and the backward re-derives that state from q);
+  may also keep a small state the forward writes, so that the backward reads
+  q and d_cum once: ``saved="boundary"`` (default) the prefix products every
+  64 steps, O(N/64); ``saved="final"`` only the final carry of every column,
+  O(b*h*j), from which the backward rebuilds cum backwards; ``saved="none"``
+  keeps the leaves only, and the backward re-derives the boundary products
+  from q (one more read of q);
 * the backward recomputes the prefix products and returns the VJP;
 * a gradient is produced only for an input that requires one;
 * the final carry is a slice of cum, so its gradient reaches the node folded
@@ -24,6 +27,7 @@ from . import capi
 
 
 _STATUS_MODES = ("deferred", "sync")
+_SAVED_MODES = ("boundary", "final", "none")
 
 
 class QuatCumprodFunction(torch.autograd.Function):
@@ -38,14 +42,15 @@ class QuatCumprodFunction(torch.autograd.Function):
     after the backward instead and raises from it."""
 
     @staticmethod
-    def forward(ctx, q: torch.Tensor, init: torch.Tensor, save_boundary_state: bool, status_check: str):
+    def forward(ctx, q: torch.Tensor, init: torch.Tensor, saved: str, status_check: str):
         capi.default_workspace.poll()
         q = q.contiguous()
         init = init.contiguous()
-        ckpt = capi.new_ckpt(q) if save_boundary_state else None
+        ckpt = None if saved == "none" else capi.new_ckpt(q, saved)
         cum = capi.quat_cumprod_fwd(q, init, ckpt=ckpt)
         capi.default_workspace.watch(q.device, None, "quat_cumprod forward")
         ctx.save_for_backward(q, init, ckpt)
+        ctx.saved_kind = saved
         ctx.status_check = status_check
         return cum
 
@@ -56,37 +61,42 @@ class QuatCumprodFunction(torch.autograd.Function):
         if not (want_dq or want_dinit):
             return None, None, None, None
         capi.default_workspace.poll()
-        d_q, d_init = capi.quat_cumprod_bwd(q, init, d_cum.contiguous(), ckpt,
-                                            want_dq=want_dq, want_dinit=want_dinit)
+        d_q, d_init = capi.quat_cumprod_bwd(q, init, d_cum.contiguous(), ckpt, want_dq=want_dq,
+                                            want_dinit=want_dinit,
+                                            saved=None if ckpt is None else ctx.saved_kind)
         capi.default_workspace.watch(q.device, None, "quat_cumprod backward")
         if ctx.status_check == "sync":
             capi.default_workspace.poll(wait=True)
         return d_q, d_init, None, None
 
 
-def quat_cumprod(q: torch.Tensor, init: torch.Tensor, *, save_boundary_state: bool = True,
+def quat_cumprod(q: torch.Tensor, init: torch.Tensor, *, saved: str = "boundary",
                  status_check: str = "deferred") -> torch.Tensor:
     """cum[t] = q_t (x) cum[t-1] with cum[-1] = init, differentiable in q and init.
 
     q: [b, s, h, j, 4], init: [b, h, j, 4], float32 or bfloat16, on the GPU.
+    saved: what the node keeps beside q and init for its backward, "boundary"
+    (default), "final" or "none" (see the module docstring).
     status_check: "deferred" (default) raises a device-side failure at the
     next call or at capi.check_status(); "sync" raises it from the backward.
     """
     if status_check not in _STATUS_MODES:
         raise ValueError(f"status_check must be one of {_STATUS_MODES}")
+    if saved not in _SAVED_MODES:
+        raise ValueError(f"saved must be one of {_SAVED_MODES}")
     if torch.is_grad_enabled() and (q.requires_grad or init.requires_grad):
-        return QuatCumprodFunction.apply(q, init, save_boundary_state, status_check)
+        return QuatCumprodFunction.apply(q, init, saved, status_check)
     capi.default_workspace.poll()
     cum = capi.quat_cumprod_fwd(q.contiguous(), init.contiguous())
     capi.default_workspace.watch(q.device, None, "quat_cumprod forward")
     return cum
 
 
-def quat_cumprod_with_final(q: torch.Tensor, init: torch.Tensor, *, save_boundary_state: bool = True,
+def quat_cumprod_with_final(q: torch.Tensor, init: torch.Tensor, *, saved: str = "boundary",
                             status_check: str = "deferred"):
     """(cum, final_carry) with final_carry = cum[:, -1], a view whose gradient
     autograd folds into the last position of cum's gradient."""
-    cum = quat_cumprod(q, init, save_boundary_state=save_boundary_state, status_check=status_check)
+    cum = quat_cumprod(q, init, saved=saved, status_check=status_check)
     return cum, cum[:, -1]
 
 

@@ -26,12 +26,16 @@ PATHS = {"auto": QC_PATH_AUTO, "column": QC_PATH_COLUMN, "chunked": QC_PATH_CHUN
 LOOKBACKS = {"auto": 0, "fenwick": 1, "grouped": 2}
 # How a backward without saved state gets its boundary products (QC_LEAVES_*).
 LEAVES = {"auto": 0, "prepass": 1, "coresident": 2}
+# What a ckpt buffer holds (QC_SAVED_*): the boundary prefix products, or only
+# the final carry of every column.
+SAVED = {"boundary": 0, "final": 1}
 
 _DTYPES = {torch.float32: QC_DTYPE_F32, torch.bfloat16: QC_DTYPE_BF16}
 
 # The exported symbols, as declared in include/quat_cumprod.h.
 EXPORTS = (
-    "quat_cumprod_workspace_bytes", "quat_cumprod_ckpt_bytes", "quat_cumprod_workspace_init",
+    "quat_cumprod_workspace_bytes", "quat_cumprod_ckpt_bytes", "quat_cumprod_ckpt_bytes_ex",
+    "quat_cumprod_workspace_init",
     "quat_cumprod_fwd", "quat_cumprod_bwd", "quat_cumprod_fwd_ex", "quat_cumprod_bwd_ex",
     "quat_cumprod_workspace_status", "quat_cumprod_strerror", "quat_cumprod_last_hip_error",
     "quat_cumprod_version", "quat_cumprod_bwd_noalloc",
@@ -47,7 +51,7 @@ EXPORTS = (
 
 class QcOptions(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("lookback", ctypes.c_int32), ("leaves", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 5)]
+                ("saved", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
 
 
 class QcScanPlan(ctypes.Structure):
@@ -86,6 +90,8 @@ def load(path: str | None = None):
         lib.quat_cumprod_workspace_bytes.restype = sz
         lib.quat_cumprod_ckpt_bytes.argtypes = dims
         lib.quat_cumprod_ckpt_bytes.restype = sz
+        lib.quat_cumprod_ckpt_bytes_ex.argtypes = dims + [ctypes.POINTER(QcOptions)]
+        lib.quat_cumprod_ckpt_bytes_ex.restype = sz
         lib.quat_cumprod_workspace_init.argtypes = [vp, sz, vp]
         lib.quat_cumprod_workspace_init.restype = ctypes.c_int
         fwd = [vp, vp, vp, vp, sz] + dims + [vp, sz, vp]
@@ -183,13 +189,15 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _options(path: str | None, lookback: str | None = None, leaves: str | None = None):
-    if path is None and lookback is None and leaves is None:
+def _options(path: str | None, lookback: str | None = None, leaves: str | None = None,
+             saved: str = "boundary"):
+    if path is None and lookback is None and leaves is None and saved == "boundary":
         return None
     o = QcOptions()
     o.path = PATHS[path or "auto"]
     o.lookback = LOOKBACKS[lookback or "auto"]
     o.leaves = LEAVES[leaves or "auto"]
+    o.saved = SAVED[saved]
     return ctypes.byref(o)
 
 
@@ -197,8 +205,22 @@ def workspace_bytes(b, s, h, j, dtype=torch.float32) -> int:
     return int(load().quat_cumprod_workspace_bytes(b, s, h, j, _DTYPES[dtype]))
 
 
-def ckpt_bytes(b, s, h, j, dtype=torch.float32) -> int:
-    return int(load().quat_cumprod_ckpt_bytes(b, s, h, j, _DTYPES[dtype]))
+def ckpt_bytes(b, s, h, j, dtype=torch.float32, saved: str = "boundary") -> int:
+    """Bytes of a ckpt buffer of the kind ``saved`` ("boundary" or "final")."""
+    if saved not in SAVED:
+        raise ValueError(f"saved must be one of {tuple(SAVED)}")
+    return int(load().quat_cumprod_ckpt_bytes_ex(b, s, h, j, _DTYPES[dtype], _options(None, saved=saved)))
+
+
+def _saved_kind(ckpt: torch.Tensor | None, saved: str | None) -> str:
+    """The kind of a ckpt buffer: its tag from new_ckpt, else ``saved``, else
+    "boundary"; a tag and an explicit ``saved`` must agree."""
+    tag = getattr(ckpt, "qc_saved", None) if ckpt is not None else None
+    if saved is not None and saved not in SAVED:
+        raise ValueError(f"saved must be one of {tuple(SAVED)}")
+    if tag is not None and saved is not None and tag != saved:
+        raise ValueError(f"ckpt holds the {tag!r} state, not {saved!r}")
+    return tag or saved or "boundary"
 
 
 class QuatCumprodStatusError(RuntimeError):
@@ -330,19 +352,25 @@ def check_status(wait: bool = True):
     default_workspace.poll(wait=wait)
 
 
-def new_ckpt(q: torch.Tensor) -> torch.Tensor:
-    """Allocate a buffer for the saved boundary state of a forward over q."""
+def new_ckpt(q: torch.Tensor, saved: str = "boundary") -> torch.Tensor:
+    """Allocate a buffer for the state a forward over q saves for its
+    backward: "boundary" (the prefix products at a fixed stride of steps) or
+    "final" (only the final carry of every column).  The buffer is tagged with
+    its kind, which the forward and the backward then use."""
     b, s, h, j = _dims(q)
-    return torch.empty(ckpt_bytes(b, s, h, j, q.dtype), dtype=torch.uint8, device=q.device)
+    ck = torch.empty(ckpt_bytes(b, s, h, j, q.dtype, saved), dtype=torch.uint8, device=q.device)
+    ck.qc_saved = saved
+    return ck
 
 
 def quat_cumprod_fwd(q: torch.Tensor, init: torch.Tensor, cum: torch.Tensor | None = None,
                      ckpt: torch.Tensor | None = None, *, path: str | None = None, lookback: str | None = None,
-                     stream=None, workspace: Workspace | None = None) -> torch.Tensor:
+                     saved: str | None = None, stream=None, workspace: Workspace | None = None) -> torch.Tensor:
     """cum[t] = q_t (x) cum[t-1], cum[-1] = init (device computation).
 
-    If ``ckpt`` (from :func:`new_ckpt`) is given, the boundary state for the
-    backward is written into it as well.
+    If ``ckpt`` (from :func:`new_ckpt`) is given, the state for the backward
+    is written into it as well (of the kind it was made for; ``saved`` names
+    the kind of an untagged buffer).
     """
     b, s, h, j = _dims(q)
     dt = _dtype_code(q)
@@ -352,10 +380,12 @@ def quat_cumprod_fwd(q: torch.Tensor, init: torch.Tensor, cum: torch.Tensor | No
     _check_like("cum", cum, q.shape, q.dtype, q.device)
     if ckpt is not None and ckpt.device != q.device:
         raise ValueError("ckpt must be on q's device")
+    kind = _saved_kind(ckpt, saved)
     ws = (workspace or default_workspace).get(workspace_bytes(b, s, h, j, q.dtype), q.device, stream)
     rc = load().quat_cumprod_fwd_ex(_ptr(q), _ptr(init), _ptr(cum), _ptr(ckpt),
                                     0 if ckpt is None else ckpt.numel() * ckpt.element_size(),
-                                    b, s, h, j, dt, _ptr(ws), ws.numel(), _stream(stream), _options(path, lookback))
+                                    b, s, h, j, dt, _ptr(ws), ws.numel(), _stream(stream),
+                                    _options(path, lookback, saved=kind))
     _check(rc, "quat_cumprod_fwd")
     return cum
 
@@ -364,10 +394,12 @@ def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
                      ckpt: torch.Tensor | None = None, *, want_dq: bool = True, want_dinit: bool = True,
                      d_q: torch.Tensor | None = None, d_init: torch.Tensor | None = None,
                      path: str | None = None, lookback: str | None = None, leaves: str | None = None,
-                     stream=None, workspace: Workspace | None = None):
+                     saved: str | None = None, stream=None, workspace: Workspace | None = None):
     """VJP of the scan: returns (d_q, d_init); an unwanted output is None.
-    Without ``ckpt``, ``leaves`` chooses how the boundary products are
-    re-derived ("prepass", "coresident"; see QC_LEAVES_* in the C header)."""
+    ``ckpt`` is the state the forward saved (its kind from its tag, else
+    ``saved``).  Without ``ckpt``, ``leaves`` chooses how the boundary
+    products are re-derived ("prepass", "coresident"; see QC_LEAVES_* in the C
+    header)."""
     b, s, h, j = _dims(q)
     dt = _dtype_code(q)
     if want_dq and d_q is None:
@@ -384,11 +416,12 @@ def quat_cumprod_bwd(q: torch.Tensor, init: torch.Tensor, d_cum: torch.Tensor,
     _check_like("d_init", d_init, (b, h, j, 4), q.dtype, q.device)
     if ckpt is not None and ckpt.device != q.device:
         raise ValueError("ckpt must be on q's device")
+    kind = _saved_kind(ckpt, saved)
     ws = (workspace or default_workspace).get(workspace_bytes(b, s, h, j, q.dtype), q.device, stream)
     rc = load().quat_cumprod_bwd_ex(_ptr(q), _ptr(init), _ptr(d_cum), _ptr(ckpt),
                                     0 if ckpt is None else ckpt.numel() * ckpt.element_size(),
                                     _ptr(d_q), _ptr(d_init), b, s, h, j, dt, _ptr(ws), ws.numel(),
-                                    _stream(stream), _options(path, lookback, leaves))
+                                    _stream(stream), _options(path, lookback, leaves, saved=kind))
     _check(rc, "quat_cumprod_bwd")
     return d_q, d_init
 
@@ -409,9 +442,12 @@ def quat_cumprod_bwd_noalloc(q: torch.Tensor, init: torch.Tensor, d_cum: torch.T
     """VJP of the scan into caller-provided outputs, with the library's fixed
     device array as workspace (quat_cumprod_bwd_noalloc): nothing is
     allocated.  ``status`` (optional) is one device int32 that receives the
-    call's status bits."""
+    call's status bits.  ``ckpt`` must be a boundary state (this entry point
+    takes no options)."""
     b, s, h, j = _dims(q)
     dt = _dtype_code(q)
+    if _saved_kind(ckpt, None) != "boundary":
+        raise ValueError("quat_cumprod_bwd_noalloc reads only a boundary-state ckpt")
     _check_like("init", init, (b, h, j, 4), q.dtype, q.device)
     _check_like("d_cum", d_cum, q.shape, q.dtype, q.device)
     _check_like("d_q", d_q, q.shape, q.dtype, q.device)

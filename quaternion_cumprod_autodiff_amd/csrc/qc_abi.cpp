@@ -69,9 +69,11 @@ struct Plan {
     size_t io_bytes = 0;      // bytes per stored quaternion
     size_t ct_bytes = 0;      // bytes per internal quaternion
     size_t slot_bytes = 0;    // bytes per carry slot (value words + check word)
+    size_t pair_slot_bytes = 0;   // the same for the final-carry backward's (product, share) pairs
     Tiling fwd, bwd;
     int64_t n_ck = 0;
     size_t ckpt_bytes = 0;
+    size_t final_bytes = 0;   // saved final carries (QC_SAVED_FINAL)
     size_t off_desc = 0, off_ckpt = 0, ws_bytes = 0;
     int64_t n_cols = 0;
 };
@@ -82,6 +84,7 @@ struct Plan {
 // and carry-wait phases.
 constexpr int kFwdMaxWc = 32;
 constexpr int kBwdMaxWc = 32;
+static_assert(kBwdMaxWc <= 32, "backward kernels exist for column groups of at most 32");
 
 // The forward can also take 64-column groups with half-height tiles (same
 // tile size, 1 KiB per row read instead of 512 B, measured a few percent
@@ -150,6 +153,7 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     p->io_bytes = dtype == QC_DTYPE_F32 ? 16 : 8;
     p->ct_bytes = dtype == QC_DTYPE_F32 ? 32 : 16;
     p->slot_bytes = dtype == QC_DTYPE_F32 ? 40 : 24;
+    p->pair_slot_bytes = dtype == QC_DTYPE_F32 ? 72 : 40;
     p->n_cols = b * M;
     p->fwd = make_tiling(b, s, M, kFwdMaxWc, dtype, false);
     if (M >= kFwdWideWc && b * ((M + kFwdWideWc - 1) / kFwdWideWc) >= kFwdWideMinChains)
@@ -163,6 +167,7 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     if ((p->n_cols + qc::kColumnBlock - 1) / qc::kColumnBlock > max_blocks) return QC_ERR_SHAPE;
     p->n_ck = (s + kCkptStride - 1) / kCkptStride;
     p->ckpt_bytes = size_t(b) * size_t(p->n_ck) * size_t(M) * p->ct_bytes;
+    p->final_bytes = size_t(p->n_cols) * p->ct_bytes;
     // The carry region holds the look-back's slots (one node per tile, then
     // the grouped look-back's group nodes), or the reduce-then-scan variant's
     // tile aggregates and scanned carries (one internal quaternion each).
@@ -170,9 +175,10 @@ int make_plan(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, Plan* p
     const size_t tiles_bwd = size_t(p->bwd.n_chains * p->bwd.n_tiles) * size_t(p->bwd.wc);
     const size_t nodes_fwd = tiles_fwd + size_t(p->fwd.n_chains * p->fwd.n_groups) * size_t(p->fwd.wc);
     const size_t nodes_bwd = tiles_bwd + size_t(p->bwd.n_chains * p->bwd.n_groups) * size_t(p->bwd.wc);
-    // The co-resident leaves-only backward keeps two sets of tile nodes, one per look-back.
-    const size_t nodes = std::max(std::max(nodes_fwd, nodes_bwd), 2 * tiles_bwd);
-    const size_t look = nodes * p->slot_bytes;
+    // The co-resident leaves-only backward keeps two sets of tile nodes, one
+    // per look-back; the final-carry backward's nodes hold pairs.
+    const size_t look = std::max(std::max(std::max(nodes_fwd, nodes_bwd), 2 * tiles_bwd) * p->slot_bytes,
+                                 nodes_bwd * p->pair_slot_bytes);
     const size_t agg = 2 * (tiles_fwd > tiles_bwd ? tiles_fwd : tiles_bwd) * p->ct_bytes;
     const size_t desc = look > agg ? look : agg;
     p->off_desc = round_up(size_t(qc::kHdrWords) * 4, kAlignWs);
@@ -206,6 +212,7 @@ struct Options {
     int path = QC_PATH_AUTO;
     int lookback = QC_LOOKBACK_AUTO;
     int leaves = QC_LEAVES_AUTO;
+    int saved = QC_SAVED_BOUNDARY;
 };
 
 int check_options(const qc_options* o, Options* out) {
@@ -214,12 +221,19 @@ int check_options(const qc_options* o, Options* out) {
     if (o->path < QC_PATH_AUTO || o->path > QC_PATH_RSCAN) return QC_ERR_OPTION;
     if (o->lookback < QC_LOOKBACK_AUTO || o->lookback > QC_LOOKBACK_GROUPED) return QC_ERR_OPTION;
     if (o->leaves < QC_LEAVES_AUTO || o->leaves > QC_LEAVES_CORESIDENT) return QC_ERR_OPTION;
-    for (int i = 0; i < 5; ++i)
+    if (o->saved < QC_SAVED_BOUNDARY || o->saved > QC_SAVED_FINAL) return QC_ERR_OPTION;
+    for (int i = 0; i < 4; ++i)
         if (o->reserved[i] != 0) return QC_ERR_OPTION;
     out->path = o->path;
     out->lookback = o->lookback;
     out->leaves = o->leaves;
+    out->saved = o->saved;
     return QC_OK;
+}
+
+// Size of the ckpt buffer of the kind o.saved names.
+size_t saved_bytes(const Plan& p, const Options& o) {
+    return o.saved == QC_SAVED_FINAL ? p.final_bytes : p.ckpt_bytes;
 }
 
 // The column path wins the forward when enough columns exist to fill the
@@ -330,10 +344,10 @@ int try_bwd_coresident(const Plan& p, const Options& o, const void* q, const voi
     return QC_OK;
 }
 
-int launch_forward(const Plan& p, const void* q, const void* init, void* cum, void* ckpt, void* ws,
+int launch_forward(const Plan& p, const void* q, const void* init, void* cum, void* ckpt, void* fin, void* ws,
                    hipStream_t st, bool column, bool rscan, int lookback) {
     qc::KernelArgs a = column ? column_args(p, ws) : base_args(p, ws, p.fwd, lookback);
-    a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt;
+    a.q = q; a.init = init; a.out = cum; a.ckpt = ckpt; a.fin = fin;
     if (!column && !rscan) {
         const int rc = set_epoch(&a, st);
         if (rc != QC_OK) return rc;
@@ -359,6 +373,13 @@ size_t quat_cumprod_ckpt_bytes(int64_t b, int64_t s, int64_t h, int64_t j, int32
     return make_plan(b, s, h, j, dtype, &p) == QC_OK ? p.ckpt_bytes : 0;
 }
 
+size_t quat_cumprod_ckpt_bytes_ex(int64_t b, int64_t s, int64_t h, int64_t j, int32_t dtype, const qc_options* opts) {
+    Options o;
+    Plan p;
+    if (check_options(opts, &o) != QC_OK || make_plan(b, s, h, j, dtype, &p) != QC_OK) return 0;
+    return saved_bytes(p, o);
+}
+
 int quat_cumprod_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
     if (!workspace) return QC_ERR_NULL;
     if (!aligned(workspace, 16)) return QC_ERR_ALIGN;
@@ -380,18 +401,20 @@ int quat_cumprod_fwd_ex(const void* q, const void* init, void* cum, void* ckpt, 
     if (rc != QC_OK) return rc;
     if (!q || !init || !cum) return QC_ERR_NULL;
     if (!workspace) return QC_ERR_WORKSPACE;
-    if (ckpt && ckpt_bytes < p.ckpt_bytes) return QC_ERR_WORKSPACE;
+    const size_t ck_bytes = saved_bytes(p, o);
+    if (ckpt && ckpt_bytes < ck_bytes) return QC_ERR_WORKSPACE;
     if (workspace_bytes < p.ws_bytes) return QC_ERR_WORKSPACE;
     if (!aligned(q, p.io_bytes) || !aligned(init, p.io_bytes) || !aligned(cum, p.io_bytes)) return QC_ERR_ALIGN;
     if ((ckpt && !aligned(ckpt, 16)) || !aligned(workspace, 16)) return QC_ERR_ALIGN;
     const size_t big = size_t(p.N) * p.io_bytes, small = size_t(p.n_cols) * p.io_bytes;
-    const Range rs[] = {{q, big}, {init, small}, {cum, big}, {ckpt, p.ckpt_bytes}, {workspace, p.ws_bytes}};
+    const Range rs[] = {{q, big}, {init, small}, {cum, big}, {ckpt, ck_bytes}, {workspace, p.ws_bytes}};
     const bool out[] = {false, false, true, true, true};
     if (any_alias(rs, out, 5)) return QC_ERR_ALIAS;
 
     const bool column = path == QC_PATH_COLUMN || (path == QC_PATH_AUTO && p.n_cols >= kColumnPathMinColumns);
-    return launch_forward(p, q, init, cum, ckpt, workspace, static_cast<hipStream_t>(stream), column,
-                          !column && use_rscan(path), o.lookback);
+    const bool final_only = o.saved == QC_SAVED_FINAL;
+    return launch_forward(p, q, init, cum, final_only ? nullptr : ckpt, final_only ? ckpt : nullptr, workspace,
+                          static_cast<hipStream_t>(stream), column, !column && use_rscan(path), o.lookback);
 }
 
 int quat_cumprod_fwd(const void* q, const void* init, void* cum, void* ckpt, size_t ckpt_bytes,
@@ -413,15 +436,18 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
     rc = make_plan(b, s, h, j, dtype, &p);
     if (rc != QC_OK) return rc;
     if (!q || !init || !d_cum) return QC_ERR_NULL;
+    const bool final_only = ckpt && o.saved == QC_SAVED_FINAL;
+    if (final_only && use_rscan(path)) return QC_ERR_OPTION;
     if (!d_q && !d_init) return QC_OK;
     if (!workspace) return QC_ERR_WORKSPACE;
-    if (ckpt && ckpt_bytes < p.ckpt_bytes) return QC_ERR_WORKSPACE;
+    const size_t ck_bytes = saved_bytes(p, o);
+    if (ckpt && ckpt_bytes < ck_bytes) return QC_ERR_WORKSPACE;
     if (workspace_bytes < p.ws_bytes) return QC_ERR_WORKSPACE;
     if (!aligned(q, p.io_bytes) || !aligned(init, p.io_bytes) || !aligned(d_cum, p.io_bytes)) return QC_ERR_ALIGN;
     if ((d_q && !aligned(d_q, p.io_bytes)) || (d_init && !aligned(d_init, p.io_bytes))) return QC_ERR_ALIGN;
     if ((ckpt && !aligned(ckpt, 16)) || !aligned(workspace, 16)) return QC_ERR_ALIGN;
     const size_t big = size_t(p.N) * p.io_bytes, small = size_t(p.n_cols) * p.io_bytes;
-    const Range rs[] = {{q, big}, {init, small}, {d_cum, big}, {ckpt, p.ckpt_bytes},
+    const Range rs[] = {{q, big}, {init, small}, {d_cum, big}, {ckpt, ck_bytes},
                         {d_q, big}, {d_init, small}, {workspace, p.ws_bytes}};
     const bool out[] = {false, false, false, false, true, true, true};
     if (any_alias(rs, out, 7)) return QC_ERR_ALIAS;
@@ -433,20 +459,19 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum, cons
         const hipError_t e = qc::launch_bwd_column(p.dtype, a, st);
         return e == hipSuccess ? QC_OK : hip_fail(e);
     }
-    void* ck = const_cast<void*>(ckpt);
-    if (!ck) {
+    void* ck = final_only ? nullptr : const_cast<void*>(ckpt);
+    if (!ckpt) {
         bool done = false;
         rc = try_bwd_coresident(p, o, q, init, d_cum, d_q, d_init, workspace, st, &done);
         if (rc != QC_OK || done) return rc;
-    }
-    if (!ck) {
         // Leaves-only backward: re-derive the boundary prefix products from q.
         ck = static_cast<char*>(workspace) + p.off_ckpt;
-        rc = launch_forward(p, q, init, nullptr, ck, workspace, st, false, use_rscan(path), o.lookback);
+        rc = launch_forward(p, q, init, nullptr, ck, nullptr, workspace, st, false, use_rscan(path), o.lookback);
         if (rc != QC_OK) return rc;
     }
     qc::KernelArgs a = base_args(p, workspace, p.bwd, o.lookback);
     a.q = q; a.init = init; a.d_cum = d_cum; a.out = d_q; a.d_init = d_init; a.ckpt = ck;
+    if (final_only) a.fin = const_cast<void*>(ckpt);
     const bool rscan = use_rscan(path);
     if (!rscan) {
         rc = set_epoch(&a, st);

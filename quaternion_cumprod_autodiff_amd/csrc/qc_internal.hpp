@@ -84,6 +84,8 @@ struct KernelArgs {
     void* out;            // cum (forward, may be null) or d_q (backward, may be null)
     void* d_init;         // [b][M]              (backward, may be null)
     void* ckpt;           // [b][n_ck][M] quaternions in the compute type (may be null)
+    void* fin;            // [b][M] final carries cum[s-1] in the compute type (forward: written if not
+                          // null; chunked backward: not null selects the backward from them alone)
     uint32_t* hdr;        // workspace header
     void* desc;           // per-tile carry slots, WC columns each (value words + check word)
     int64_t b, s, M;

@@ -245,8 +245,6 @@ using SlotWord = unsigned long long;
 template <typename T> struct SlotLayout;
 template <> struct SlotLayout<double> { static constexpr int kValueWords = 4; };
 template <> struct SlotLayout<float> { static constexpr int kValueWords = 2; };
-template <typename T>
-constexpr int slot_words() { return SlotLayout<T>::kValueWords + 1; }
 
 // Check word of a slot: a multiply-xorshift hash of the value words and the
 // launch epoch.  Being non-linear, a slot that mixes words of two different
@@ -282,13 +280,69 @@ __device__ __forceinline__ Q4<float> unpack_words(const SlotWord* v, float) {
             __uint_as_float(uint32_t(v[1] >> 32))};
 }
 
+// Carries of the look-back, as monoids over ranges of tiles.  combine(x, y)
+// joins two adjacent ranges: x is the one nearer the reading tile (met first
+// on its look-back path), y the farther one.
+//   ProductCarry  forward prefix product P: x is later in time, so x (x) y.
+//   SumCarry      backward reverse sum S (in the global frame): x + y.
+//   PairCarry     backward without boundary products (only the forward's final
+//                 carry saved): a range of steps a..b as (U, Y), its product
+//                 U = q_b (x) ... (x) q_a and its share of S in the frame of its
+//                 first step, Y = sum_t conj(q_t (x) ... (x) q_a) (x) d_t.  The
+//                 reverse look-back meets x earlier in time than y, and
+//                 (U, Y)_xy = (U_y (x) U_x, Y_x + conj(U_x) (x) Y_y).
+template <typename T>
+struct QPair {
+    Q4<T> u, y;
+};
+
+template <typename T>
+struct ProductCarry {
+    using V = Q4<T>;
+    static constexpr int kWords = SlotLayout<T>::kValueWords;
+    static __device__ __forceinline__ V identity() { return q_one<T>(); }
+    static __device__ __forceinline__ V combine(const V& x, const V& y) { return qmul(x, y); }
+    static __device__ __forceinline__ void pack(const V& v, SlotWord* w) { pack_words(v, w); }
+    static __device__ __forceinline__ V unpack(const SlotWord* w) { return unpack_words(w, T()); }
+};
+
+template <typename T>
+struct SumCarry {
+    using V = Q4<T>;
+    static constexpr int kWords = SlotLayout<T>::kValueWords;
+    static __device__ __forceinline__ V identity() { return q_zero<T>(); }
+    static __device__ __forceinline__ V combine(const V& x, const V& y) { return qadd(x, y); }
+    static __device__ __forceinline__ void pack(const V& v, SlotWord* w) { pack_words(v, w); }
+    static __device__ __forceinline__ V unpack(const SlotWord* w) { return unpack_words(w, T()); }
+};
+
+template <typename T>
+struct PairCarry {
+    using V = QPair<T>;
+    static constexpr int kWords = 2 * SlotLayout<T>::kValueWords;
+    static __device__ __forceinline__ V identity() { return {q_one<T>(), q_zero<T>()}; }
+    static __device__ __forceinline__ V combine(const V& x, const V& y) {
+        return {qmul(y.u, x.u), qadd(x.y, qcmul(x.u, y.y))};
+    }
+    static __device__ __forceinline__ void pack(const V& v, SlotWord* w) {
+        pack_words(v.u, w);
+        pack_words(v.y, w + SlotLayout<T>::kValueWords);
+    }
+    static __device__ __forceinline__ V unpack(const SlotWord* w) {
+        return {unpack_words(w, T()), unpack_words(w + SlotLayout<T>::kValueWords, T())};
+    }
+};
+
+template <class C>
+constexpr int carry_slot_words() { return C::kWords + 1; }
+
 // Publish this lane's column of a node (lanes with `writer` set).
-template <typename T, int WC>
-__device__ __forceinline__ void publish(const KernelArgs& a, SlotWord* slot, const Q4<T>& v, bool writer) {
+template <class C, int WC>
+__device__ __forceinline__ void publish(const KernelArgs& a, SlotWord* slot, const typename C::V& v, bool writer) {
     if (writer) {
-        constexpr int NV = SlotLayout<T>::kValueWords;
+        constexpr int NV = C::kWords;
         SlotWord w[NV + 1];
-        pack_words(v, w);
+        C::pack(v, w);
         w[NV] = check_word<NV>(w, a.epoch);
 #pragma unroll
         for (int k = 0; k <= NV; ++k) __hip_atomic_store(slot + k * WC, w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -297,24 +351,24 @@ __device__ __forceinline__ void publish(const KernelArgs& a, SlotWord* slot, con
 
 // One read attempt of this lane's column of a node: true (and *out set) if
 // the slot holds a complete value of this launch.
-template <typename T, int WC>
-__device__ __forceinline__ bool try_read(const KernelArgs& a, const SlotWord* slot, Q4<T>* out) {
-    constexpr int NV = SlotLayout<T>::kValueWords;
+template <class C, int WC>
+__device__ __forceinline__ bool try_read(const KernelArgs& a, const SlotWord* slot, typename C::V* out) {
+    constexpr int NV = C::kWords;
     SlotWord w[NV + 1];
 #pragma unroll
     for (int k = 0; k <= NV; ++k) w[k] = __hip_atomic_load(slot + k * WC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *out = unpack_words(w, T());
+    *out = C::unpack(w);
     return w[NV] == check_word<NV>(w, a.epoch);
 }
 
 // Wait (bounded) until the node is published, then read this lane's column.
 // Polls back off from about 30 ns to about 2 us between attempts, so a slot
 // that many tiles wait on is not hammered with coherent loads.
-template <typename T, int WC>
-__device__ __forceinline__ Q4<T> wait_read(const KernelArgs& a, const SlotWord* slot) {
-    Q4<T> v = q_zero<T>();
+template <class C, int WC>
+__device__ __forceinline__ typename C::V wait_read(const KernelArgs& a, const SlotWord* slot) {
+    typename C::V v = C::identity();
     uint32_t polls = 0;
-    while (!try_read<T, WC>(a, slot, &v)) {
+    while (!try_read<C, WC>(a, slot, &v)) {
         if (polls < 8) {
             __builtin_amdgcn_s_sleep(1);
         } else if (polls < 64) {
@@ -342,73 +396,80 @@ __device__ __forceinline__ int64_t path_node(int64_t jn, int steps) {
 // Address of column c's first slot word in carry node `node` (0-based over
 // all chains).  A node stores its words word-major: word k of column c sits at
 // k * WC + c, so the lanes of a column group read each word coalesced.
-template <typename T, int WC>
+template <class C, int WC>
 __device__ __forceinline__ SlotWord* slot_ptr(const KernelArgs& a, int64_t node, int c) {
-    return reinterpret_cast<SlotWord*>(a.desc) + node * (WC * slot_words<T>()) + c;
+    return reinterpret_cast<SlotWord*>(a.desc) + node * (WC * carry_slot_words<C>()) + c;
 }
 
 // First-round read attempt, issued right after the tile's data loads so that
 // its latency overlaps theirs; predecessor tiles that started long enough
 // before have published by then.  Slots are write-once per launch, so an
 // early successful read is final; a failed one is retried in the look-back.
-template <typename T, int WC, int NW>
+template <class C, int WC, int NW>
 __device__ __forceinline__ bool fenwick_prefetch(const KernelArgs& a, int64_t chain, int64_t pos, int slot, int c,
-                                                 Q4<T>* v) {
+                                                 typename C::V* v) {
     const int64_t node = path_node<NW * (64 / WC)>(pos, slot);   // i - 1 = pos
     if (node <= 0) return false;
-    return try_read<T, WC>(a, slot_ptr<T, WC>(a, chain * a.n_tiles + node - 1, c), v);
+    return try_read<C, WC>(a, slot_ptr<C, WC>(a, chain * a.n_tiles + node - 1, c), v);
 }
 
 // Fenwick look-back for tile `pos` (0-based) of `chain`; called by every
 // thread of the block.  `own` is this tile's aggregate, valid in the wave
-// `own_wave`; (pre_v, pre_ok) is this slot's first-round prefetch.
-// Combine(later, earlier) is
-//   product:  later (x) earlier           (forward carry P)
-//   sum:      later + earlier             (backward carry S, "later" = earlier in time)
-// The query path is walked in rounds of PAR = NW*R nodes: every lane slot
+// `own_wave`; (pre_v, pre_ok) is this slot's first-round prefetch.  Nodes
+// are combined with C::combine, nearest first.  The query path is walked in rounds of PAR = NW*R nodes: every lane slot
 // makes one read attempt of one node for column c (round 0 uses the
 // prefetch), so published nodes cost at most one round trip together; then
 // `own_wave` combines the round in the fixed order, waiting itself (nearest
 // node first) only for nodes that were not yet published, and publishes node
-// i as soon as its children are in.  Returns the exclusive prefix (identity /
-// zero for the first tile) to every thread.
-template <typename T, int WC, int NW, bool kProduct>
-__device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const Q4<T>& own,
-                                   bool own_wave, int wave, int r, int c, const Q4<T>& pre_v, bool pre_ok,
-                                   Q4<T> (*s_nodes)[WC], uint8_t (*s_ok)[WC], Q4<T>* s_out) {
+// i as soon as its children are in.  Returns the exclusive prefix (the
+// identity for the first tile) to every thread.
+template <class C, int WC, int NW, bool kStaged = false>
+__device__ typename C::V fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const typename C::V& own,
+                                           bool own_wave, int wave, int r, int c, const typename C::V& pre_v,
+                                           bool pre_ok, typename C::V (*s_nodes)[WC], uint8_t (*s_ok)[WC],
+                                           typename C::V* s_out) {
+    using V = typename C::V;
     constexpr int R = 64 / WC;
     constexpr int PAR = NW * R;
     const int64_t i = pos + 1;
     const int64_t low = i & (-i);
     const int64_t node0 = chain * a.n_tiles;   // node n lives at node0 + n - 1
     const int slot = wave * R + r;
-    Q4<T> acc = kProduct ? q_one<T>() : q_zero<T>();
+    V acc = C::identity();
     bool published = (i == a.n_tiles);        // nothing reads the last node
     int64_t jn = i - 1;                       // next node on the query path (block-uniform)
     for (int round = 0;; ++round) {
         if (own_wave && !published && jn <= i - low) {
-            publish<T, WC>(a, slot_ptr<T, WC>(a, node0 + i - 1, c), kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
+            publish<C, WC>(a, slot_ptr<C, WC>(a, node0 + i - 1, c), C::combine(own, acc), r == 0);
             published = true;
         }
         if (jn == 0) break;
         const int64_t mine = path_node<PAR>(jn, slot);
         if (mine > 0) {
-            Q4<T> v = pre_v;
             const int64_t nd = node0 + mine - 1;
-            const bool ok = round == 0 ? (pre_ok || try_read<T, WC>(a, slot_ptr<T, WC>(a, nd, c), &v))
-                                       : try_read<T, WC>(a, slot_ptr<T, WC>(a, nd, c), &v);
-            s_nodes[slot][c] = v;
-            s_ok[slot][c] = ok ? 1 : 0;
+            if constexpr (kStaged) {
+                if (round > 0 || !s_ok[slot][c]) {
+                    V v;
+                    s_ok[slot][c] = try_read<C, WC>(a, slot_ptr<C, WC>(a, nd, c), &v) ? 1 : 0;
+                    s_nodes[slot][c] = v;
+                }
+            } else {
+                V v = pre_v;
+                const bool ok = round == 0 ? (pre_ok || try_read<C, WC>(a, slot_ptr<C, WC>(a, nd, c), &v))
+                                           : try_read<C, WC>(a, slot_ptr<C, WC>(a, nd, c), &v);
+                s_nodes[slot][c] = v;
+                s_ok[slot][c] = ok ? 1 : 0;
+            }
         }
         __syncthreads();
         for (int k = 0; k < PAR && jn > 0; ++k) {
             if (own_wave) {
                 if (!published && jn <= i - low) {
-                    publish<T, WC>(a, slot_ptr<T, WC>(a, node0 + i - 1, c), kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
+                    publish<C, WC>(a, slot_ptr<C, WC>(a, node0 + i - 1, c), C::combine(own, acc), r == 0);
                     published = true;
                 }
-                const Q4<T> v = s_ok[k][c] ? s_nodes[k][c] : wait_read<T, WC>(a, slot_ptr<T, WC>(a, node0 + jn - 1, c));
-                acc = kProduct ? qmul(acc, v) : qadd(acc, v);
+                const V v = s_ok[k][c] ? s_nodes[k][c] : wait_read<C, WC>(a, slot_ptr<C, WC>(a, node0 + jn - 1, c));
+                acc = C::combine(acc, v);
             }
             jn -= jn & (-jn);
         }
@@ -433,68 +494,66 @@ __device__ Q4<T> fenwick_exclusive(const KernelArgs& a, int64_t chain, int64_t p
 // group aggregates after all of those, at n_chains * n_tiles + chain * n_groups + g.
 // Item t of tile p's read list is the tile node p-1-t for t < k, else the
 // group node g-1-(t-k).
-template <typename T, int WC>
+template <class C, int WC>
 __device__ __forceinline__ SlotWord* grouped_node(const KernelArgs& a, int64_t chain, int64_t pos, int64_t t, int c) {
     const int64_t k = pos % a.group;
     const int64_t node = t < k ? chain * a.n_tiles + pos - 1 - t
                                : a.n_chains * a.n_tiles + chain * a.n_groups + pos / a.group - 1 - (t - k);
-    return slot_ptr<T, WC>(a, node, c);
+    return slot_ptr<C, WC>(a, node, c);
 }
 
 // First-round read attempt of the Fenwick look-back (the grouped one reads
 // its nodes when it gets there).
-template <typename T, int WC, int NW, bool kGrouped>
+template <class C, int WC, int NW, bool kGrouped>
 __device__ __forceinline__ bool lookback_prefetch(const KernelArgs& a, int64_t chain, int64_t pos, int slot, int c,
-                                                  Q4<T>* v) {
+                                                  typename C::V* v) {
     if constexpr (kGrouped) return false;
-    return fenwick_prefetch<T, WC, NW>(a, chain, pos, slot, c, v);
+    return fenwick_prefetch<C, WC, NW>(a, chain, pos, slot, c, v);
 }
 
 // Combination, in list order, of items [lo, hi) of the read list: this lane
 // slot takes a contiguous run of them (a few items), waiting for each in turn.
-template <typename T, int WC, int PAR, bool kProduct>
-__device__ Q4<T> grouped_run(const KernelArgs& a, int64_t chain, int64_t pos, int64_t lo, int64_t hi, int slot,
-                             int c) {
+template <class C, int WC, int PAR>
+__device__ typename C::V grouped_run(const KernelArgs& a, int64_t chain, int64_t pos, int64_t lo, int64_t hi,
+                                     int slot, int c) {
     const int64_t per = (hi - lo + PAR - 1) / PAR;
     const int64_t r0 = lo + slot * per < hi ? lo + slot * per : hi;
     const int64_t r1 = r0 + per < hi ? r0 + per : hi;
-    Q4<T> part = kProduct ? q_one<T>() : q_zero<T>();
-    for (int64_t t = r0; t < r1; ++t) {
-        const Q4<T> v = wait_read<T, WC>(a, grouped_node<T, WC>(a, chain, pos, t, c));
-        part = kProduct ? qmul(part, v) : qadd(part, v);
-    }
+    typename C::V part = C::identity();
+    for (int64_t t = r0; t < r1; ++t) part = C::combine(part, wait_read<C, WC>(a, grouped_node<C, WC>(a, chain, pos, t, c)));
     return part;
 }
 
 // Same contract as fenwick_exclusive (pre_v / pre_ok unused).
-template <typename T, int WC, int NW, bool kProduct>
-__device__ Q4<T> grouped_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const Q4<T>& own,
-                                   bool own_wave, int wave, int r, int c, Q4<T> (*s_nodes)[WC], Q4<T>* s_out) {
+template <class C, int WC, int NW>
+__device__ typename C::V grouped_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const typename C::V& own,
+                                           bool own_wave, int wave, int r, int c, typename C::V (*s_nodes)[WC],
+                                           typename C::V* s_out) {
     constexpr int R = 64 / WC;
     constexpr int PAR = NW * R;
     const int64_t k = pos % a.group, g = pos / a.group;
     const int slot = wave * R + r;
     // Nothing reads the chain's last tile, nor the last group.
-    if (own_wave && pos + 1 < a.n_tiles) publish<T, WC>(a, slot_ptr<T, WC>(a, chain * a.n_tiles + pos, c), own, r == 0);
+    if (own_wave && pos + 1 < a.n_tiles) publish<C, WC>(a, slot_ptr<C, WC>(a, chain * a.n_tiles + pos, c), own, r == 0);
     // Phase 1, the group's earlier tiles: the group's last tile publishes the
     // group aggregate from them before it waits on anything else.
-    s_nodes[slot][c] = grouped_run<T, WC, PAR, kProduct>(a, chain, pos, 0, k, slot, c);
+    s_nodes[slot][c] = grouped_run<C, WC, PAR>(a, chain, pos, 0, k, slot, c);
     __syncthreads();
-    Q4<T> acc = kProduct ? q_one<T>() : q_zero<T>();
+    typename C::V acc = C::identity();
     if (own_wave) {
 #pragma unroll 2
-        for (int j = 0; j < PAR; ++j) acc = kProduct ? qmul(acc, s_nodes[j][c]) : qadd(acc, s_nodes[j][c]);
+        for (int j = 0; j < PAR; ++j) acc = C::combine(acc, s_nodes[j][c]);
         if (k == a.group - 1 && g + 1 < a.n_groups)
-            publish<T, WC>(a, slot_ptr<T, WC>(a, a.n_chains * a.n_tiles + chain * a.n_groups + g, c),
-                           kProduct ? qmul(own, acc) : qadd(own, acc), r == 0);
+            publish<C, WC>(a, slot_ptr<C, WC>(a, a.n_chains * a.n_tiles + chain * a.n_groups + g, c),
+                           C::combine(own, acc), r == 0);
     }
     __syncthreads();
     // Phase 2, the earlier groups.
-    s_nodes[slot][c] = grouped_run<T, WC, PAR, kProduct>(a, chain, pos, k, k + g, slot, c);
+    s_nodes[slot][c] = grouped_run<C, WC, PAR>(a, chain, pos, k, k + g, slot, c);
     __syncthreads();
     if (own_wave) {
 #pragma unroll 2
-        for (int j = 0; j < PAR; ++j) acc = kProduct ? qmul(acc, s_nodes[j][c]) : qadd(acc, s_nodes[j][c]);
+        for (int j = 0; j < PAR; ++j) acc = C::combine(acc, s_nodes[j][c]);
         if (r == 0) s_out[c] = acc;
     }
     __syncthreads();
@@ -504,16 +563,17 @@ __device__ Q4<T> grouped_exclusive(const KernelArgs& a, int64_t chain, int64_t p
 // The two look-backs are separate kernel instances: the scan kernels hold
 // their tile in registers across the look-back, and code for both would
 // raise every instance's register count.
-template <typename T, int WC, int NW, bool kProduct, bool kGrouped>
-__device__ __forceinline__ Q4<T> lookback_exclusive(const KernelArgs& a, int64_t chain, int64_t pos, const Q4<T>& own,
-                                                    bool own_wave, int wave, int r, int c, const Q4<T>& pre_v,
-                                                    bool pre_ok, Q4<T> (*s_nodes)[WC], uint8_t (*s_ok)[WC],
-                                                    Q4<T>* s_out) {
+template <class C, int WC, int NW, bool kGrouped, bool kStaged = false>
+__device__ __forceinline__ typename C::V lookback_exclusive(const KernelArgs& a, int64_t chain, int64_t pos,
+                                                            const typename C::V& own, bool own_wave, int wave, int r,
+                                                            int c, const typename C::V& pre_v, bool pre_ok,
+                                                            typename C::V (*s_nodes)[WC], uint8_t (*s_ok)[WC],
+                                                            typename C::V* s_out) {
     if constexpr (kGrouped)
-        return grouped_exclusive<T, WC, NW, kProduct>(a, chain, pos, own, own_wave, wave, r, c, s_nodes, s_out);
+        return grouped_exclusive<C, WC, NW>(a, chain, pos, own, own_wave, wave, r, c, s_nodes, s_out);
     else
-        return fenwick_exclusive<T, WC, NW, kProduct>(a, chain, pos, own, own_wave, wave, r, c, pre_v, pre_ok,
-                                                      s_nodes, s_ok, s_out);
+        return fenwick_exclusive<C, WC, NW, kStaged>(a, chain, pos, own, own_wave, wave, r, c, pre_v, pre_ok, s_nodes,
+                                                     s_ok, s_out);
 }
 
 // The launch epoch: from the arguments, or (launches captured in a graph,
@@ -635,7 +695,8 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
     Q4<CT> pre_v = q_one<CT>();
     bool pre_ok = false;
     if constexpr (one_pass(kMode))
-        pre_ok = lookback_prefetch<CT, WC, NW, kMode == kGrouped>(a, tc.chain, tc.pos, wave * R + r, c, &pre_v);
+        pre_ok = lookback_prefetch<ProductCarry<CT>, WC, NW, kMode == kGrouped>(a, tc.chain, tc.pos, wave * R + r, c,
+                                                                                &pre_v);
     Q4<CT> Et = q_one<CT>();
     if constexpr (kMode == kFixup) Et = *rscan_carry<CT, WC>(a, tc.chain, tc.pos, c);
 
@@ -651,8 +712,9 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
         return;
     }
     if constexpr (one_pass(kMode))
-        Et = lookback_exclusive<CT, WC, NW, true, kMode == kGrouped>(a, tc.chain, tc.pos, tile_agg, wave == NW - 1, wave, r, c, pre_v,
-                                                 pre_ok, s_nodes, s_ok, s_carry);
+        Et = lookback_exclusive<ProductCarry<CT>, WC, NW, kMode == kGrouped>(a, tc.chain, tc.pos, tile_agg, wave == NW - 1,
+                                                                             wave, r, c, pre_v, pre_ok, s_nodes, s_ok,
+                                                                             s_carry);
     const Q4<CT> Ps = qmul(F, Et);   // P_{t0-1}: prefix product before this slice
 
     if (a.ckpt != nullptr && tc.col_ok && tc.t0 < a.s && (tc.t0 % kCkptStride) == 0)
@@ -675,6 +737,9 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
                 }
             }
         }
+        // The final carry cum[s-1], for a backward from it alone.
+        if (a.fin != nullptr && tc.col_ok && tc.t0 < a.s && tc.t0 + L >= a.s)
+            reinterpret_cast<Q4<CT>*>(a.fin)[tc.bi * a.M + tc.m] = cm;
     }
 }
 
@@ -702,6 +767,40 @@ __global__ void __launch_bounds__(NW * 64) fwd_chunked_kernel(KernelArgs a) {
 // from cum[te] = A_k (x) E (x) init, with cum[t0-1] taken directly as
 // A_{k-1} (x) E (x) init.  Only q and d stay in registers between the sweeps, in
 // storage precision.
+//
+// kFinal: the same tile without any prefix product saved, only the forward's
+// final carry cum[s-1] (a.fin, per column, internal precision).  G needs no
+// prefix product at all (it is the page's reverse recurrence), only cum does.
+// The reverse look-back carries the frame-free pair of each later range
+// (PairCarry): its product U and its share Y in the frame of its first step,
+// which gives the tile (U_a, Y_a) over all later tiles.  With
+// B_k = Q_{K-1} (x) ... (x) Q_{k+1}, the slices of the tile after k:
+//   G[te]   = d_te + R'_k + conj(B_k) (x) Y_a     (the sum over u > te of
+//             conj(q_u (x) ... (x) q_{te+1}) (x) d_u, which P_te (x) S / |P_te|^2
+//             reduces to: P_u = (q_u (x) ... (x) q_{te+1}) (x) P_te)
+//   cum[te] = B_k^-1 (x) U_a^-1 (x) cum[s-1]      (cum[s-1] = U_a (x) B_k (x) cum[te])
+//   cum[t0 - 1] = Q_k^-1 (x) cum[te],    d_init = S[0] = Y of the whole sequence.
+// Nothing here needs a product from the front of the sequence, so q and
+// d_cum are read once and no boundary state exists.  The inverses need the
+// products over later steps to be non-zero, which holds whenever no step is
+// zero (else the status word reports it, as for a zero prefix product).
+
+// Sweep 2 of a backward slice: from G[te] and cum[te] at its last step te and
+// cum[t0-1] before it, walk down the slice storing d_q[t] = G[t] (x) conj(cum[t-1]).
+template <class IO, int L>
+__device__ __forceinline__ void sweep2_store(const KernelArgs& a, const TileCoord& tc, const typename IO::Raw (&qv)[L],
+                                             const typename IO::Raw (&dv)[L], Q4<typename IO::CT> G,
+                                             Q4<typename IO::CT> cm, const Q4<typename IO::CT>& c0) {
+    using CT = typename IO::CT;
+#pragma unroll
+    for (int i = L - 1; i >= 0; --i) {
+        const Q4<CT> qi = IO::ct_fresh(qv[i]);
+        const Q4<CT> cprev = i == 0 ? c0 : qscale(qcmul(qi, cm), recip(qnorm2(qi)));
+        if (tc.full || tc.t0 + i < a.s) IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qmulc(G, cprev));
+        if (i > 0) G = qadd(IO::ct_fresh(dv[i - 1]), qcmul(qi, G));
+        cm = cprev;
+    }
+}
 
 // Waves per SIMD to ask of the compiler: 3 while the slice's q and d_cum fit
 // in 64 registers, else 2; bfloat16 slices (float32 arithmetic) fit 4.
@@ -711,18 +810,24 @@ constexpr int bwd_min_waves() {
          : L * 2 * int(sizeof(typename IO::Raw)) / 4 <= 64 ? 3 : 2;
 }
 
-template <class IO, int WC, int L, int NW, int kMode>
+template <class IO, int WC, int L, int NW, int kMode, bool kFinal>
 __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked_kernel(KernelArgs a) {
+    static_assert(!kFinal || one_pass(kMode), "the final-carry backward runs only with a look-back");
     if constexpr (one_pass(kMode)) a.epoch = launch_epoch(a);
     using CT = typename IO::CT;
     using Raw = typename IO::Raw;
+    using Carry = std::conditional_t<kFinal, PairCarry<CT>, SumCarry<CT>>;
+    using CV = typename Carry::V;
     constexpr int R = 64 / WC;
     constexpr int K = NW * R;   // slices per column in a tile
     __shared__ Q4<CT> s_sq[K][WC];
     __shared__ Q4<CT> s_sy[K][WC];
-    __shared__ Q4<CT> s_nodes[K][WC];
+    __shared__ CV s_nodes[K][WC];
     __shared__ uint8_t s_ok[K][WC];
-    __shared__ Q4<CT> s_after[WC];
+    __shared__ CV s_after[WC];
+    __shared__ Q4<CT> s_b[kFinal ? K : 1][WC];
+    __shared__ Q4<CT> s_rp[kFinal ? K : 1][WC];
+    __shared__ Q4<CT> s_fin[kFinal ? WC : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane / WC, c = lane % WC;
@@ -749,18 +854,22 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
                        : IO::zero_raw();
         }
     }
-    // Prefix product before the tile (saved boundary state) and the initial carry.
+    // Prefix product before the tile (saved boundary state) and the initial
+    // carry.  (kFinal reads the forward's final carry after the look-back.)
     const int64_t tile_t0 = tc.t0 - int64_t(k) * L;
     Q4<CT> Et = q_one<CT>();
     Raw init_raw = IO::one_raw();
-    if (tc.col_ok) {
+    if (!kFinal && tc.col_ok) {
         Et = reinterpret_cast<const Q4<CT>*>(a.ckpt)[(tc.bi * a.n_ck + tile_t0 / kCkptStride) * a.M + tc.m];
         init_raw = IO::load(a.init, tc.bi * a.M + tc.m);
     }
-    Q4<CT> pre_v = q_zero<CT>();
+    CV pre_v = Carry::identity();
     bool pre_ok = false;
-    if constexpr (one_pass(kMode)) pre_ok = lookback_prefetch<CT, WC, NW, kMode == kGrouped>(a, tc.chain, tc.pos, k, c, &pre_v);
-    Q4<CT> Sa = q_zero<CT>();
+    if constexpr (one_pass(kMode))
+        pre_ok = lookback_prefetch<Carry, WC, NW, kMode == kGrouped>(a, tc.chain, tc.pos, k, c, &pre_v);
+    Q4<CT> fin = q_one<CT>();
+    if (kFinal && k == 0 && tc.col_ok) fin = reinterpret_cast<const Q4<CT>*>(a.fin)[tc.bi * a.M + tc.m];
+    CV Sa = Carry::identity();
     if constexpr (kMode == kFixup) Sa = *rscan_carry<CT, WC>(a, tc.chain, tc.pos, c);
 
     // Sweep 1: slice product and slice share, frame of the slice start.
@@ -773,54 +882,92 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>())) bwd_chunked
     }
     s_sq[k][c] = Ql;
     s_sy[k][c] = Yl;
+    if constexpr (kFinal && kMode == kLookback) {
+        s_nodes[k][c] = pre_v;
+        s_ok[k][c] = pre_ok ? 1 : 0;
+    }
     __syncthreads();
 
-    // Exclusive prefix F (slices before k) and exclusive suffix R' (slices after k).
-    Q4<CT> F = q_one<CT>();
-    if (k > 0) {
-        F = s_sq[0][c];
-        for (int k2 = 1; k2 < k; ++k2) F = qmul(s_sq[k2][c], F);
+    // Exclusive prefix F (slices before k) and exclusive suffix R' (slices
+    // after k); kFinal needs no F, but B = Q_{K-1} (x) ... (x) Q_{k+1}.
+    Q4<CT> F = q_one<CT>(), B = q_one<CT>();
+    if constexpr (!kFinal) {
+        if (k > 0) {
+            F = s_sq[0][c];
+            for (int k2 = 1; k2 < k; ++k2) F = qmul(s_sq[k2][c], F);
+        }
     }
     Q4<CT> Rp = q_zero<CT>();
     if (k < K - 1) {
         Rp = s_sy[K - 1][c];
-        for (int k2 = K - 2; k2 > k; --k2) Rp = qadd(s_sy[k2][c], qcmul(s_sq[k2][c], Rp));
+        if constexpr (kFinal) B = s_sq[K - 1][c];
+        for (int k2 = K - 2; k2 > k; --k2) {
+            Rp = qadd(s_sy[k2][c], qcmul(s_sq[k2][c], Rp));
+            if constexpr (kFinal) B = qmul(B, s_sq[k2][c]);
+        }
     }
-    const Q4<CT> A = qmul(Ql, F);
 
-    // The tile's share of S in the global frame (meaningful in slice 0, which
-    // publishes it): conj(E) (x) (Y_0 + conj(Q_0) (x) R'_0).
-    Q4<CT> Yg = q_zero<CT>();
-    if (wave == 0) Yg = qcmul(Et, qadd(Yl, qcmul(Ql, Rp)));
+    // kFinal parks B and R' in LDS across the look-back, whose pair carries
+    // leave no registers for them (Q_k and Y_k are still in s_sq / s_sy).
+    if constexpr (kFinal) {
+        s_b[k][c] = B;
+        s_rp[k][c] = Rp;
+        if (k == 0) s_fin[c] = fin;
+    }
+
+    // The tile's carry, meaningful in slice 0, which publishes it: its share
+    // of S in the global frame, conj(E) (x) (Y_0 + conj(Q_0) (x) R'_0); kFinal:
+    // the pair (U_t, Y_0 + conj(Q_0) (x) R'_0), U_t = B_0 (x) Q_0.
+    CV own = Carry::identity();
+    if (wave == 0) {
+        if constexpr (kFinal)
+            own = {qmul(B, Ql), qadd(Yl, qcmul(Ql, Rp))};
+        else
+            own = qcmul(Et, qadd(Yl, qcmul(Ql, Rp)));
+    }
     if constexpr (kMode == kAggregate) {
-        if (wave == 0 && r == 0) *rscan_agg<CT, WC>(a, tc.chain, tc.pos, c) = Yg;
+        if (wave == 0 && r == 0) *rscan_agg<CT, WC>(a, tc.chain, tc.pos, c) = own;
         return;
     }
     if constexpr (one_pass(kMode))
-        Sa = lookback_exclusive<CT, WC, NW, false, kMode == kGrouped>(a, tc.chain, tc.pos, Yg, wave == 0, wave, r, c, pre_v, pre_ok,
-                                                  s_nodes, s_ok, s_after);
+        Sa = lookback_exclusive<Carry, WC, NW, kMode == kGrouped, kFinal>(a, tc.chain, tc.pos, own, wave == 0, wave,
+                                                                          r, c, pre_v, pre_ok, s_nodes, s_ok, s_after);
 
-    if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok)
-        IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Yg, Sa));   // S[0] (slice 0 of the first tile, E = 1)
-
-    if (a.out != nullptr && tc.col_ok) {
-        const CT nE = qnorm2(Et), nA = qnorm2(A);
-        // A zero step makes every later prefix product exactly zero, which shows
-        // up here (E for later tiles, A for its own and later slices of this tile).
-        if (nE == CT(0) || nA == CT(0))
-            __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusZeroPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const Q4<CT> Z = qscale(qmul(Et, Sa), recip(nE));
-        const Q4<CT> C = qmul(Et, IO::ct(init_raw));           // cum before the tile
-        const Q4<CT> c0 = qmul(F, C);                          // cum[t0 - 1]
-        Q4<CT> cm = qmul(A, C);                                // cum[t0 + L - 1]
-        Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rp, qscale(qmul(A, Z), recip(nA))));
-#pragma unroll
-        for (int i = L - 1; i >= 0; --i) {
-            const Q4<CT> qi = IO::ct_fresh(qv[i]);
-            const Q4<CT> cprev = i == 0 ? c0 : qscale(qcmul(qi, cm), recip(qnorm2(qi)));
-            if (tc.full || tc.t0 + i < a.s) IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qmulc(G, cprev));
-            if (i > 0) G = qadd(IO::ct_fresh(dv[i - 1]), qcmul(qi, G));
-            cm = cprev;
+    if constexpr (kFinal) {
+        // Sa = (U_a, Y_a) of all later tiles.  At the slice end te,
+        // cum[te] = B^-1 (x) U_a^-1 (x) cum[s-1] and the later steps' part of
+        // G[te] is R' + conj(B) (x) Y_a; S[0] is the whole sequence's Y.
+        const Q4<CT> Bk = s_b[k][c], Rk = s_rp[k][c], Qk = s_sq[k][c];
+        if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok) {
+            const Q4<CT> Ut = qmul(Bk, Qk), Yt = qadd(s_sy[k][c], qcmul(Qk, Rk));
+            IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Yt, qcmul(Ut, Sa.y)));
+        }
+        if (a.out != nullptr && tc.col_ok) {
+            const CT nU = qnorm2(Sa.u), nB = qnorm2(Bk), nQ = qnorm2(Qk);
+            if (nU == CT(0) || nB == CT(0) || nQ == CT(0))
+                __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusZeroPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const Q4<CT> Ce = qscale(qcmul(Sa.u, s_fin[c]), recip(nU));   // cum at the tile's last step
+            const Q4<CT> cm = qscale(qcmul(Bk, Ce), recip(nB));      // cum[t0 + L - 1]
+            const Q4<CT> c0 = qscale(qcmul(Qk, cm), recip(nQ));      // cum[t0 - 1]
+            const Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rk, qcmul(Bk, Sa.y)));
+            sweep2_store<IO, L>(a, tc, qv, dv, G, cm, c0);
+        }
+    } else {
+        const Q4<CT> A = qmul(Ql, F);
+        if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok)
+            IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(own, Sa));   // S[0] (slice 0 of the first tile, E = 1)
+        if (a.out != nullptr && tc.col_ok) {
+            const CT nE = qnorm2(Et), nA = qnorm2(A);
+            // A zero step makes every later prefix product exactly zero, which shows
+            // up here (E for later tiles, A for its own and later slices of this tile).
+            if (nE == CT(0) || nA == CT(0))
+                __hip_atomic_fetch_or(&a.hdr[kHdrStatus], kStatusZeroPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const Q4<CT> Z = qscale(qmul(Et, Sa), recip(nE));
+            const Q4<CT> C = qmul(Et, IO::ct(init_raw));           // cum before the tile
+            const Q4<CT> c0 = qmul(F, C);                          // cum[t0 - 1]
+            const Q4<CT> cm = qmul(A, C);                          // cum[t0 + L - 1]
+            const Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rp, qscale(qmul(A, Z), recip(nA))));
+            sweep2_store<IO, L>(a, tc, qv, dv, G, cm, c0);
         }
     }
 }
@@ -927,13 +1074,13 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>() < 3 ? bwd_min
         }
         // (No first-round prefetch: its value would be held across sweep 1,
         // and the tile's registers are full.)
-        const Q4<CT> Et = fenwick_exclusive<CT, WC, NW, true>(af, chain, tile, Pt, wave == 0, wave, r, c, q_one<CT>(),
-                                                              false, s_nodes, s_ok, s_before);
+        const Q4<CT> Et = fenwick_exclusive<ProductCarry<CT>, WC, NW>(af, chain, tile, Pt, wave == 0, wave, r, c,
+                                                                      q_one<CT>(), false, s_nodes, s_ok, s_before);
 
         Q4<CT> Yg = q_zero<CT>();
         if (wave == 0) Yg = qcmul(Et, qadd(Yl, qcmul(Ql, Rp)));
-        const Q4<CT> Sa = fenwick_exclusive<CT, WC, NW, false>(a, chain, tc.pos, Yg, wave == 0, wave, r, c,
-                                                               q_zero<CT>(), false, s_nodes, s_ok, s_after);
+        const Q4<CT> Sa = fenwick_exclusive<SumCarry<CT>, WC, NW>(a, chain, tc.pos, Yg, wave == 0, wave, r, c,
+                                                                  q_zero<CT>(), false, s_nodes, s_ok, s_after);
 
         if (a.d_init != nullptr && tc.t0 == 0 && tc.col_ok) IO::store(a.d_init, tc.bi * a.M + tc.m, qadd(Yg, Sa));
 
@@ -992,6 +1139,7 @@ __global__ void __launch_bounds__(kColumnBlock) fwd_column_kernel(KernelArgs a) 
             if (a.out != nullptr) IO::store_stream(a.out, base + t * a.M, cm);
         }
     }
+    if (a.fin != nullptr) reinterpret_cast<Q4<CT>*>(a.fin)[col] = cm;
 }
 
 template <class IO, int U>
@@ -1127,15 +1275,16 @@ hipError_t launch_fwd_mode(bool deep, const KernelArgs& a, hipStream_t st) {
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(g.fwd_nw * 64), params, 0, st);
 }
 
-template <class IO, int WC, int kMode>
+template <class IO, int WC, int kMode, bool kFinal = false>
 hipError_t launch_bwd_mode(bool deep, const KernelArgs& a, hipStream_t st) {
     constexpr Geometry g = geometry_for(WC, IO::kDtype);
     static_assert(bwd_tile_steps(WC, IO::kDtype, false) % kCkptStride == 0, "backward tiles start on saved boundaries");
     static_assert(bwd_tile_steps(WC, IO::kDtype, true) % kCkptStride == 0, "backward tiles start on saved boundaries");
     KernelArgs args = a;
     void* params[] = {&args};
-    const void* fn = deep ? reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_deep_l, g.bwd_nw, kMode>)
-                          : reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_l, g.bwd_nw, kMode>);
+    const void* fn =
+        deep ? reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_deep_l, g.bwd_nw, kMode, kFinal>)
+             : reinterpret_cast<const void*>(&bwd_chunked_kernel<IO, WC, g.bwd_l, g.bwd_nw, kMode, kFinal>);
     return hipLaunchKernel(fn, dim3(a.n_blocks), dim3(g.bwd_nw * 64), params, 0, st);
 }
 
@@ -1162,6 +1311,11 @@ hipError_t launch_fwd_wc(bool deep, bool rscan, const KernelArgs& a, hipStream_t
 
 template <class IO, int WC>
 hipError_t launch_bwd_wc(bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
+    if (a.fin != nullptr) {
+        if (rscan) return hipErrorInvalidValue;
+        return a.group != 0 ? launch_bwd_mode<IO, WC, kGrouped, true>(deep, a, st)
+                            : launch_bwd_mode<IO, WC, kLookback, true>(deep, a, st);
+    }
     if (!rscan)
         return a.group != 0 ? launch_bwd_mode<IO, WC, kGrouped>(deep, a, st)
                             : launch_bwd_mode<IO, WC, kLookback>(deep, a, st);
@@ -1185,10 +1339,10 @@ hipError_t launch_fwd_io(int wc, bool deep, bool rscan, const KernelArgs& a, hip
     }
 }
 
+// Backward column groups are at most 32 wide (the dispatcher's cap).
 template <class IO>
 hipError_t launch_bwd_io(int wc, bool deep, bool rscan, const KernelArgs& a, hipStream_t st) {
     switch (wc) {
-        case 64: return launch_bwd_wc<IO, 64>(deep, rscan, a, st);
         case 32: return launch_bwd_wc<IO, 32>(deep, rscan, a, st);
         case 16: return launch_bwd_wc<IO, 16>(deep, rscan, a, st);
         case 8: return launch_bwd_wc<IO, 8>(deep, rscan, a, st);
@@ -1221,7 +1375,6 @@ const void* coresident_fn(bool deep) {
 template <class IO>
 const void* coresident_fn_io(int wc, bool deep) {
     switch (wc) {
-        case 64: return coresident_fn<IO, 64>(deep);
         case 32: return coresident_fn<IO, 32>(deep);
         case 16: return coresident_fn<IO, 16>(deep);
         case 8: return coresident_fn<IO, 8>(deep);

@@ -169,8 +169,51 @@ def test_options(lib):
     o.leaves = 3
     assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
     o.leaves = 0
+    o.saved = 2
+    assert fwd(lib, opts=ctypes.byref(o)) == E_OPT
+    assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
+    o.saved = 0
     o.reserved[2] = 1
     assert bwd(lib, opts=ctypes.byref(o)) == E_OPT
+
+
+def test_final_carry_state(lib):
+    """QC_SAVED_FINAL: the ckpt holds one internal-precision quaternion per
+    column whatever s, is size-checked as such, and is refused by the
+    reduce-then-scan backward (which has no pair carries)."""
+    o = capi.QcOptions()
+    o.saved = 1
+    opt = ctypes.byref(o)
+    for (b, s, h, j) in [(1, 1, 1, 1), (8, 4096, 32, 32), (1, 262144, 2, 8), (2, 65, 3, 5)]:
+        assert lib.quat_cumprod_ckpt_bytes_ex(b, s, h, j, 0, opt) == b * h * j * 32
+        assert lib.quat_cumprod_ckpt_bytes_ex(b, s, h, j, 1, opt) == b * h * j * 16
+        assert lib.quat_cumprod_ckpt_bytes_ex(b, s, h, j, 0, None) == lib.quat_cumprod_ckpt_bytes(b, s, h, j, 0)
+    assert lib.quat_cumprod_ckpt_bytes_ex(0, 1, 1, 1, 0, opt) == 0
+    bad = capi.QcOptions()
+    bad.saved = 5
+    assert lib.quat_cumprod_ckpt_bytes_ex(1, 1, 1, 1, 0, ctypes.byref(bad)) == 0
+    fin = lib.quat_cumprod_ckpt_bytes_ex(*SHAPE, 0, opt)
+    assert fin < lib.quat_cumprod_ckpt_bytes(*SHAPE, 0)
+    assert fwd(lib, ckpt=8, ckb=fin - 1, opts=opt) == E_WS
+    assert bwd(lib, ckpt=8, ckb=fin - 1, opts=opt) == E_WS
+    o.path = 3
+    assert bwd(lib, ckpt=8, ckb=fin, opts=opt) == E_OPT
+
+
+def test_binding_tags_ckpt_kind():
+    """The binding sizes a ckpt by its kind and refuses a kind that
+    disagrees with the buffer's tag (host-side checks only)."""
+    import torch
+    ck = torch.empty(0)
+    ck.qc_saved = "final"
+    assert capi._saved_kind(ck, None) == "final"
+    assert capi._saved_kind(ck, "final") == "final"
+    assert capi._saved_kind(None, None) == "boundary"
+    assert capi._saved_kind(torch.empty(0), "final") == "final"
+    with pytest.raises(ValueError, match="holds"):
+        capi._saved_kind(ck, "boundary")
+    with pytest.raises(ValueError):
+        capi._saved_kind(None, "everything")
 
 
 def test_workspace_helpers_validate(lib):

@@ -40,12 +40,12 @@ def close(got, ref, dtype="f32"):
         assert err / scale <= 2e-2, (err, scale)
 
 
-@pytest.mark.parametrize("save", [True, False])
-def test_gradients_match_oracle(save):
+@pytest.mark.parametrize("saved", ["boundary", "final", "none"])
+def test_gradients_match_oracle(saved):
     inp = make_inputs(2, 700, 4, 8, "unit", "f32", seed=21)
     w = np.random.default_rng(22).standard_normal(inp.q.shape).astype(np.float32)
     q, init = dev(inp.q, grad=True), dev(inp.init, grad=True)
-    cum = quat_cumprod(q, init, save_boundary_state=save)
+    cum = quat_cumprod(q, init, saved=saved)
     (cum * dev(w)).sum().backward()
     r_cum = oracle.fwd(inp.q64, inp.init64)
     r_dq, r_di = oracle.bwd(inp.q64, inp.init64, w.astype(np.float64))
@@ -54,14 +54,15 @@ def test_gradients_match_oracle(save):
     close(f64(init.grad), r_di)
 
 
-def test_final_carry_gradient_is_folded():
+@pytest.mark.parametrize("saved", ["boundary", "final"])
+def test_final_carry_gradient_is_folded(saved):
     """The final carry is a slice of cum: its gradient lands in d_cum[:, -1]."""
     inp = make_inputs(3, 300, 2, 4, "unit", "f32", seed=23)
     rng = np.random.default_rng(24)
     w = rng.standard_normal(inp.q.shape).astype(np.float32)
     w2 = rng.standard_normal(inp.init.shape).astype(np.float32)
     q, init = dev(inp.q, grad=True), dev(inp.init, grad=True)
-    cum, final = quat_cumprod_with_final(q, init)
+    cum, final = quat_cumprod_with_final(q, init, saved=saved)
     ((cum * dev(w)).sum() + (final * dev(w2)).sum()).backward()
     d = w.astype(np.float64)
     d[:, -1] += w2
@@ -114,22 +115,24 @@ def test_bf16_gradients():
     inp = make_inputs(2, 400, 4, 4, "drift", "bf16", seed=30)
     q, init = dev(inp.q, "bf16", grad=True), dev(inp.init, "bf16", grad=True)
     wd = dev(inp.d_cum, "bf16")
-    cum = QuatCumprodFunction.apply(q, init, True, "deferred")
-    (cum.float() * wd.float()).sum().backward()
-    r_dq, r_di = oracle.bwd(inp.q64, inp.init64, inp.d_cum64)
-    close(f64(q.grad), r_dq, "bf16")
-    close(f64(init.grad), r_di, "bf16")
+    for saved in ("boundary", "final"):
+        q.grad = init.grad = None
+        cum = QuatCumprodFunction.apply(q, init, saved, "deferred")
+        (cum.float() * wd.float()).sum().backward()
+        r_dq, r_di = oracle.bwd(inp.q64, inp.init64, inp.d_cum64)
+        close(f64(q.grad), r_dq, "bf16")
+        close(f64(init.grad), r_di, "bf16")
 
 
-@pytest.mark.parametrize("save", [True, False])
-def test_zero_step_raises_from_backward(save):
+@pytest.mark.parametrize("saved", ["boundary", "final", "none"])
+def test_zero_step_raises_from_backward(saved):
     """A zero step makes the backward's prefix products zero: with
     status_check="sync" the backward itself raises, instead of handing
     non-finite gradients to the optimiser."""
     inp = make_inputs(2, 300, 2, 4, "unit", "f32", seed=31)
     inp.q[1, 120, 0, 3] = 0.0
     q, init = dev(inp.q, grad=True), dev(inp.init, grad=True)
-    cum = quat_cumprod(q, init, save_boundary_state=save, status_check="sync")
+    cum = quat_cumprod(q, init, saved=saved, status_check="sync")
     with pytest.raises(capi.QuatCumprodStatusError) as ei:
         cum.sum().backward()
     assert ei.value.bits == 2
@@ -171,7 +174,7 @@ def test_two_streams_share_the_default_workspace():
         for rn in runs:
             with torch.cuda.stream(rn["st"]):
                 q, init = dev(rn["inp"].q, grad=True), dev(rn["inp"].init, grad=True)
-                (quat_cumprod(q, init, save_boundary_state=False) * dev(rn["w"])).sum().backward()
+                (quat_cumprod(q, init, saved="none") * dev(rn["w"])).sum().backward()
                 rn["grads"].append((q.grad, init.grad))
     torch.cuda.synchronize()
     capi.check_status()

@@ -15,7 +15,7 @@ import torch
 import oracle
 from quaternion_cumprod_autodiff_amd import capi
 from quaternion_cumprod_autodiff_amd.inputs import make_inputs
-from test_gpu_parity import check, to_dev, to_f64
+from test_gpu_parity import FINAL, check, new_state, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ DEV = "cuda:0"
 # a few long chains (tall tiles), the per-column path, the reduce-then-scan
 # passes, and each look-back scheme forced ("fenwick", "grouped": the chunked
 # path with that scheme; AUTO takes the grouped one for the first and the
-# long-chain shapes).
+# long-chain shapes); then the backward from the final carry alone.
 CASES = [
     (2, 4096, 4, 8, "unit", "f32", "chunked", True),
     (2, 4096, 4, 8, "unit", "f32", "chunked", False),
@@ -37,6 +37,9 @@ CASES = [
     (1, 30000, 2, 8, "unit", "f32", "rscan", False),
     (1, 30000, 2, 8, "unit", "f32", "fenwick", True),
     (3, 5000, 2, 3, "unit", "bf16", "grouped", False),
+    (2, 4096, 4, 8, "unit", "f32", "chunked", FINAL),
+    (1, 30000, 2, 8, "unit", "f32", "fenwick", FINAL),
+    (3, 5000, 2, 3, "unit", "bf16", "grouped", FINAL),
 ]
 REPLAYS = 4
 
@@ -46,21 +49,21 @@ def _opts(path):
 
 
 def _eager(q, init, d, path, use_ckpt, ws):
-    ck = capi.new_ckpt(q) if use_ckpt else None
+    ck = new_state(q, use_ckpt)
     cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, workspace=ws, **_opts(path))
     d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ck, workspace=ws, **_opts(path))
     return cum, d_q, d_init
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"b{c[0]}s{c[1]}h{c[2]}j{c[3]}-{c[4]}-{c[5]}-{c[6]}"
-                         + ("" if c[7] else "-leaves"))
+                         + ("-final" if c[7] == FINAL else "" if c[7] else "-leaves"))
 def test_graph_replays_match_eager_and_oracle(case):
     b, s, h, j, recipe, dtype, path, use_ckpt = case
     print(f"[graph {case}]", flush=True)
     first = make_inputs(b, s, h, j, recipe, dtype, seed=500)
     q, init, d = to_dev(first.q, dtype), to_dev(first.init, dtype), to_dev(first.d_cum, dtype)
     cum, d_q, d_init = torch.empty_like(q), torch.empty_like(q), torch.empty_like(init)
-    ck = capi.new_ckpt(q) if use_ckpt else None
+    ck = new_state(q, use_ckpt)
     ws = capi.Workspace()
     eager_ws = capi.Workspace()
 

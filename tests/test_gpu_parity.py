@@ -64,9 +64,20 @@ def path_options(path):
     return dict(path=path), {}
 
 
+# use_ckpt: True (the saved boundary state), False (leaves only) or FINAL (the
+# forward saves only its final carry, and the backward runs from it).
+FINAL = "final"
+
+
+def new_state(q, use_ckpt):
+    if use_ckpt == FINAL:
+        return capi.new_ckpt(q, "final")
+    return capi.new_ckpt(q) if use_ckpt else None
+
+
 def run_device(inp, path=None, use_ckpt=True, want_dq=True, want_dinit=True, stream=None):
     q, init, d = to_dev(inp.q, inp.dtype), to_dev(inp.init, inp.dtype), to_dev(inp.d_cum, inp.dtype)
-    ck = capi.new_ckpt(q) if use_ckpt else None
+    ck = new_state(q, use_ckpt)
     opts, bwd_only = path_options(path)
     cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, stream=stream, **opts)
     d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ckpt=ck, want_dq=want_dq, want_dinit=want_dinit,
@@ -125,14 +136,15 @@ def config_and_reference(name):
     return _config_cache[name]
 
 
-@pytest.mark.parametrize("use_ckpt", [True, False], ids=["saved-state", "leaves-only"])
+@pytest.mark.parametrize("use_ckpt", [True, False, FINAL], ids=["saved-state", "leaves-only", "final-carry"])
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_config_full_parity(name, use_ckpt):
     """Every named workload at full size, in the launch configuration the
-    benchmark times (default path, saved boundary state), and in the
+    benchmark times (default path, saved boundary state), in the
     page-faithful leaves-only mode (the backward re-derives the boundary
-    state from q)."""
-    print(f"[config {name} {'saved state' if use_ckpt else 'leaves only'}]", flush=True)
+    state from q), and with only the forward's final carry saved."""
+    mode = {True: "saved state", False: "leaves only", FINAL: "final carry"}[use_ckpt]
+    print(f"[config {name} {mode}]", flush=True)
     inp, ref = config_and_reference(name)
     compare(inp, use_ckpt=use_ckpt, ref=ref)
 
@@ -141,7 +153,8 @@ def test_config_full_parity(name, use_ckpt):
 @pytest.mark.parametrize("path,use_ckpt", [("chunked", False), ("column", True), ("column", False),
                                            ("rscan", True), ("rscan", False), ("fenwick", True),
                                            ("fenwick", False), ("grouped", True), ("prepass", False),
-                                           ("coresident", False)])
+                                           ("coresident", False), ("chunked", FINAL), ("fenwick", FINAL),
+                                           ("grouped", FINAL), ("column", FINAL)])
 def test_config_other_paths(name, path, use_ckpt):
     print(f"[config {name} path={path} ckpt={use_ckpt}]", flush=True)
     compare(make_config(name), path=path, use_ckpt=use_ckpt)
@@ -154,14 +167,18 @@ EDGE_HJ = [(1, 1), (1, 3), (4, 4), (4, 8), (8, 8), (5, 13), (10, 10)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "fenwick", "grouped", "prepass", "coresident"])
+@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "fenwick", "grouped", "prepass", "coresident",
+                                  "final", "final-grouped"])
 def test_edge_shapes(dtype, path):
+    use_ckpt = path not in LEAVES_MODES
+    if path.startswith("final"):
+        path, use_ckpt = ("grouped" if path == "final-grouped" else "chunked"), FINAL
     for s in EDGE_S:
         for (h, j) in EDGE_HJ:
             for b in (1, 3):
                 inp = make_inputs(b, s, h, j, "unit", dtype, seed=s * 131 + h * 7 + j + b)
-                print(f"[edge b={b} s={s} h={h} j={j} {dtype} {path}]", flush=True)
-                compare(inp, path=path, use_ckpt=path not in LEAVES_MODES)
+                print(f"[edge b={b} s={s} h={h} j={j} {dtype} {path} ckpt={use_ckpt}]", flush=True)
+                compare(inp, path=path, use_ckpt=use_ckpt)
 
 
 def test_random_shapes():
@@ -185,6 +202,21 @@ def test_random_shapes():
         compare(inp, path=path, use_ckpt=use_ckpt)
 
 
+def test_random_shapes_final_carry():
+    """The same kind of sweep for the backward from the final carry alone,
+    over both look-backs (forced and AUTO) and both dtypes."""
+    rng = np.random.default_rng(2025)
+    for it in range(30):
+        b = int(rng.choice([1, 2, 3, 5, 8, 33]))
+        h, j = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        s = int(rng.integers(1, 4000 if b * h * j < 400 else 300))
+        dtype = "bf16" if rng.random() < 0.3 else "f32"
+        path = ("chunked", "fenwick", "grouped")[it % 3]
+        inp = make_inputs(b, s, h, j, "unit", dtype, seed=3000 + it)
+        print(f"[random final {it}: b={b} s={s} h={h} j={j} {dtype} {path}]", flush=True)
+        compare(inp, path=path, use_ckpt=FINAL)
+
+
 @pytest.mark.parametrize("s,hj", [(2048, (1, 1)), (4100, (1, 2)), (8191, (2, 2)), (12345, (1, 64)),
                                   (3000, (33, 3))])
 def test_many_tiles_ragged(s, hj):
@@ -195,6 +227,8 @@ def test_many_tiles_ragged(s, hj):
     for path in ("chunked", "rscan", "fenwick", "grouped"):
         compare(inp, path=path, ref=ref)
         compare(inp, path=path, use_ckpt=False, ref=ref)
+        if path != "rscan":
+            compare(inp, path=path, use_ckpt=FINAL, ref=ref)
     for path in LEAVES_MODES:
         compare(inp, path=path, use_ckpt=False, ref=ref)
 
@@ -209,6 +243,7 @@ def test_wide_forward_groups(dtype, b, s, h, j):
     ref = reference(inp)
     compare(inp, ref=ref)
     compare(inp, use_ckpt=False, ref=ref)
+    compare(inp, use_ckpt=FINAL, ref=ref)
     compare(inp, path="rscan", ref=ref)
     compare(inp, path="grouped", ref=ref)
 
@@ -220,6 +255,9 @@ def test_non_unit_steps(dtype):
     print(f"[scaled {dtype}]", flush=True)
     compare(inp)
     compare(inp, path="column")
+    # From the final carry, cum is rebuilt backwards through q_t^-1 = conj(q_t) / |q_t|^2.
+    compare(inp, use_ckpt=FINAL)
+    compare(inp, path="grouped", use_ckpt=FINAL)
 
 
 def test_drift_bf16_column_path():
@@ -247,14 +285,50 @@ def test_checkpoint_and_prepass_leaves_only_agree_bitwise():
         assert torch.allclose(x, y, rtol=1e-6, atol=1e-6)
 
 
-def test_optional_gradients():
+@pytest.mark.parametrize("use_ckpt", [True, FINAL])
+def test_optional_gradients(use_ckpt):
     inp = make_inputs(2, 300, 4, 8, "unit", "f32", seed=5)
-    _, dq_full, di_full = run_device(inp)
-    _, dq_only, none1 = run_device(inp, want_dinit=False)
-    _, none2, di_only = run_device(inp, want_dq=False)
+    _, dq_full, di_full = run_device(inp, use_ckpt=use_ckpt)
+    _, dq_only, none1 = run_device(inp, want_dinit=False, use_ckpt=use_ckpt)
+    _, none2, di_only = run_device(inp, want_dq=False, use_ckpt=use_ckpt)
     assert none1 is None and none2 is None
     assert torch.equal(dq_full, dq_only)
     assert torch.equal(di_full, di_only)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("path", ["chunked", "column"])
+def test_final_carry_state_is_the_last_cum(dtype, path):
+    """The final-carry state is cum[:, s-1] in the internal precision (float64
+    for float32 storage, float32 for bfloat16), whichever forward path wrote
+    it; and a state from the per-column forward serves the chunked backward."""
+    inp = make_inputs(3, 777, 3, 5, "unit", dtype, seed=8)
+    q, init, d = to_dev(inp.q, dtype), to_dev(inp.init, dtype), to_dev(inp.d_cum, dtype)
+    ck = capi.new_ckpt(q, "final")
+    capi.quat_cumprod_fwd(q, init, ckpt=ck, path=path)
+    ct = torch.float64 if dtype == "f32" else torch.float32
+    got = ck.view(ct).reshape(3, 3, 5, 4).cpu().numpy().astype(np.float64)
+    ref = oracle.fwd(inp.q64, inp.init64)[:, -1]
+    tol = 1e-12 if dtype == "f32" else 1e-5
+    assert float(np.abs(got - ref).max()) <= tol * max(1.0, float(np.abs(ref).max()))
+    d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ck, path="chunked")
+    assert capi.default_workspace.status(q.device) == 0
+    _, r_dq, r_di = reference(inp)
+    check("d_q", to_f64(d_q), r_dq, dtype, inp.s)
+    check("d_init", to_f64(d_init), r_di, dtype, inp.s)
+
+
+def test_final_carry_refused_by_rscan_and_noalloc():
+    """The reduce-then-scan backward has no pair carries, and the allocation-free
+    entry point takes no options: both refuse a final-carry state."""
+    inp = make_inputs(1, 100, 2, 2, "unit", "f32", seed=6)
+    q, init, d = to_dev(inp.q, "f32"), to_dev(inp.init, "f32"), to_dev(inp.d_cum, "f32")
+    ck = capi.new_ckpt(q, "final")
+    capi.quat_cumprod_fwd(q, init, ckpt=ck)
+    with pytest.raises(capi.QuatCumprodError, match="option"):
+        capi.quat_cumprod_bwd(q, init, d, ck, path="rscan")
+    with pytest.raises(ValueError, match="boundary"):
+        capi.quat_cumprod_bwd_noalloc(q, init, d, torch.empty_like(q), torch.empty_like(init), ck)
 
 
 def test_determinism_repeated_runs():
@@ -341,7 +415,7 @@ def test_workspace_reuse_small_then_large_shapes():
         compare(inp, path="chunked", use_ckpt=False)
 
 
-@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "grouped", "coresident"])
+@pytest.mark.parametrize("path", ["chunked", "column", "rscan", "grouped", "coresident", "final", "final-grouped"])
 def test_zero_step_is_reported(path):
     """A step that is exactly zero makes every later prefix product zero: the
     forward stays exact, and the backward (whose exact form divides by |P_t|^2)
@@ -352,7 +426,10 @@ def test_zero_step_is_reported(path):
     q, init, d = to_dev(inp.q, "f32"), to_dev(inp.init, "f32"), to_dev(inp.d_cum, "f32")
     print(f"[zero step {path}]", flush=True)
     ws = capi.Workspace()
-    ck = None if path in LEAVES_MODES else capi.new_ckpt(q)
+    if path.startswith("final"):
+        path, ck = ("grouped" if path == "final-grouped" else "chunked"), capi.new_ckpt(q, "final")
+    else:
+        ck = None if path in LEAVES_MODES else capi.new_ckpt(q)
     opts, bwd_only = path_options(path)
     cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, workspace=ws, **opts)
     assert ws.status(q.device) == 0
@@ -374,5 +451,7 @@ def test_rscan_and_lookback_agree_on_long_chains(dtype):
         for path in ("rscan", "chunked", "fenwick", "grouped"):
             for use_ckpt in (True, False):
                 compare(inp, path=path, use_ckpt=use_ckpt, ref=ref)
+            if path != "rscan":
+                compare(inp, path=path, use_ckpt=FINAL, ref=ref)
         for path in LEAVES_MODES:
             compare(inp, path=path, use_ckpt=False, ref=ref)
