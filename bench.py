@@ -758,7 +758,8 @@ def short_kernel_name(name: str) -> str:
     return name.replace("(KernelArgs)", "")
 
 
-def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command: str, bench_log: str | None = None):
+def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command: str, bench_log: str | None = None,
+                      saved: str = "boundary"):
     """Write profiles/kernels_<config>.txt from a rocprofv3 --kernel-trace
     --stats run (and, with pmc_dir, its FETCH_SIZE / WRITE_SIZE runs scaled by
     the plain-copy calibration factors of traffic_headline.txt).  Kernel
@@ -771,8 +772,9 @@ def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command:
     from quaternion_cumprod_autodiff_amd.inputs import CONFIGS
     b, s, h, j, recipe, io = CONFIGS[config]
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    mode = "saved boundary state" if saved == "boundary" else "backward from the final carry alone"
     lines = [f"# Kernel durations and HBM traffic, workload {config} (b{b} s{s} h{h} j{j}, {io} I/O, "
-             f"recipe {recipe}), one MI355X.",
+             f"recipe {recipe}, {mode}), one MI355X.",
              "# Commands (from /tmp, TMPDIR=/tmp, R = repository root, OUT = an output directory):"]
     lines += ["#   " + c for c in command.split(" ;; ")]
     lines.append("#")
@@ -820,7 +822,7 @@ def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command:
             tot = f[k] * fs + w[k] * ws
             lines.append(f"{short_kernel_name(k)[:72]:72s} {f[k] * fs:14.0f} {w[k] * ws:14.0f} "
                          f"{(base if base else 0):14d} {(tot / base if base else 0):6.3f}")
-    path = os.path.join(ROOT, "profiles", f"kernels_{config}.txt")
+    path = os.path.join(ROOT, "profiles", f"kernels_{config}{'' if saved == 'boundary' else '_' + saved}.txt")
     with open(path, "w") as out:
         out.write("\n".join(lines) + "\n")
     print(path)
@@ -886,7 +888,8 @@ def main():
                                f"gdn2 b{B} h{H} t{T} latent{L} dense{D} chunk{C} f32, forward + VJP")
         return
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.config, args.pmc_dir, args.profile_command, args.bench_log)
+        summarize_profile(args.summarize_profile, args.config, args.pmc_dir, args.profile_command, args.bench_log,
+                          args.saved)
         return
     if args.summarize_scan_traffic:
         cal = read_kv(TRAFFIC_FILE)
