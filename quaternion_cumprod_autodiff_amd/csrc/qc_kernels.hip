@@ -616,6 +616,78 @@ __device__ __forceinline__ TileCoord tile_coord(const KernelArgs& a, uint32_t id
     return tc;
 }
 
+// Lane moves by gfx950 permlane swaps (VALU, no LDS crossbar).  For O = 32,
+// lane blocks are the wave's two 32-lane halves; for O = 16, the 16-lane rows
+// of each half.  Given x, *even receives in every lane the value of the even
+// block of its pair (O = 32: the lower half; O = 16: rows 0, 0, 2, 2) and
+// *odd that of the odd block (the upper half; rows 1, 1, 3, 3): the swap
+// exchanges one operand's odd blocks with the other's even blocks, and both
+// operands are x.
+template <int O, typename T>
+__device__ __forceinline__ void q_perm(const Q4<T>& x, Q4<T>* even, Q4<T>* odd) {
+    static_assert(O == 32 || O == 16, "permlane swaps move 32 or 16 lanes");
+    constexpr int N = int(sizeof(Q4<T>) / 4);
+    uint32_t in[N], e[N], o[N];
+    __builtin_memcpy(in, &x, sizeof(in));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const auto p = O == 32 ? __builtin_amdgcn_permlane32_swap(in[i], in[i], false, false)
+                               : __builtin_amdgcn_permlane16_swap(in[i], in[i], false, false);
+        e[i] = p[0];
+        o[i] = p[1];
+    }
+    __builtin_memcpy(even, e, sizeof(e));
+    __builtin_memcpy(odd, o, sizeof(o));
+}
+
+// In-wave scan of the R slice products of a column (slice r holds A), in
+// left-multiply order: *inc = A_r (x) ... (x) A_0, *exw = A_{r-1} (x) ... (x) A_0
+// (identity for r = 0), *last = the wave's total A_{R-1} (x) ... (x) A_0 in every
+// lane.  Two and four slices per wave (32- and 16-column groups) move lanes
+// by permlane swaps; four first scans each 32-lane half, then offsets the
+// upper half by the lower half's total.  Narrower groups (eight or more
+// slices) use a Hillis-Steele scan over ds_bpermute shuffles.
+template <typename T, int WC>
+__device__ __forceinline__ void wave_scan_product(const Q4<T>& A, int r, int c, Q4<T>* inc, Q4<T>* exw,
+                                                  Q4<T>* last) {
+    constexpr int R = 64 / WC;
+    Q4<T> even, odd;
+    if constexpr (R == 1) {
+        *inc = A;
+        *exw = q_one<T>();
+        *last = A;
+    } else if constexpr (R == 2) {
+        q_perm<32>(A, &even, &odd);                   // even: the lower slice's A
+        *inc = r == 1 ? qmul(A, even) : A;
+        *exw = r == 1 ? even : q_one<T>();
+        q_perm<32>(*inc, &even, last);                // odd: the upper slice's inc
+    } else if constexpr (R == 4) {
+        q_perm<16>(A, &even, &odd);                   // even: rows 0, 0, 2, 2 of A
+        const Q4<T> in_half = (r & 1) ? qmul(A, even) : A;
+        const Q4<T> ex_half = (r & 1) ? even : q_one<T>();
+        Q4<T> half_tot, lower_tot;
+        q_perm<16>(in_half, &even, &half_tot);        // odd: each half's total (rows 1, 1, 3, 3)
+        q_perm<32>(half_tot, &lower_tot, &odd);       // even: the lower half's total, everywhere
+        const Q4<T> off = r >= 2 ? lower_tot : q_one<T>();
+        *inc = qmul(in_half, off);
+        *exw = qmul(ex_half, off);
+        Q4<T> row_odd;
+        q_perm<16>(*inc, &even, &row_odd);            // odd: rows 1, 1, 3, 3 of inc
+        q_perm<32>(row_odd, &even, last);             // odd: the upper half's, i.e. row 3's
+    } else {
+        Q4<T> x = A;
+#pragma unroll
+        for (int d = 1; d < R; d <<= 1) {
+            const Q4<T> o = shfl_up_q(x, d * WC);
+            if (r >= d) x = qmul(x, o);
+        }
+        *inc = x;
+        *exw = shfl_up_q(x, WC);
+        if (r == 0) *exw = q_one<T>();
+        *last = shfl_q(x, (R - 1) * WC + c);
+    }
+}
+
 // In-tile exclusive prefix product of slice aggregates (left-multiply order).
 // Slice k = wave*R + r.  Returns F = product of slices before k in this tile;
 // `tile_agg` receives the tile's full product (valid in the last wave).
@@ -623,19 +695,12 @@ template <typename T, int WC, int NW>
 __device__ __forceinline__ Q4<T> tile_scan_product(const Q4<T>& A, Q4<T> (*s_wagg)[WC], int wave, int r, int c,
                                                    Q4<T>* tile_agg) {
     constexpr int R = 64 / WC;
-    Q4<T> inc = A;
-#pragma unroll
-    for (int d = 1; d < R; d <<= 1) {
-        const Q4<T> o = shfl_up_q(inc, d * WC);
-        if (r >= d) inc = qmul(inc, o);
-    }
-    Q4<T> exw = shfl_up_q(inc, WC);
-    if (r == 0) exw = q_one<T>();
+    Q4<T> inc, exw, last;
+    wave_scan_product<T, WC>(A, r, c, &inc, &exw, &last);
     if (r == R - 1) s_wagg[wave][c] = inc;
     __syncthreads();
     Q4<T> wex = q_one<T>();
     for (int w2 = wave - 1; w2 >= 0; --w2) wex = qmul(wex, s_wagg[w2][c]);
-    const Q4<T> last = shfl_q(inc, (R - 1) * WC + c);
     *tile_agg = qmul(last, wex);
     return qmul(exw, wex);
 }
