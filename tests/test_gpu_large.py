@@ -7,7 +7,8 @@ cotangents) and rounded to bfloat16; eight sampled columns are copied back
 and checked, end to end, against the float64 oracle run on exactly those
 columns (the columns are independent, so this is the exact reference for
 the sampled outputs).  Tolerance: normwise relative 2e-2 per output, as for
-every bfloat16 workload.
+every bfloat16 workload.  The backward runs twice: from the saved boundary
+state, then from the forward's final carry alone.
 """
 import numpy as np
 import pytest
@@ -82,5 +83,20 @@ def test_beyond_32bit_indices_sampled_columns():
         print(f"[large] {name}: normwise rel err {rel:.2e}", flush=True)
         assert np.isfinite(g).all(), name
         assert rel <= 2e-2, f"{name}: normwise rel err {rel:.3e}"
-    del q, d, cum, d_q, ck, ws
+
+    # The backward from the final carry alone, same inputs, into the same buffers.
+    print("[large] final-carry backward", flush=True)
+    fin = capi.new_ckpt(q, "final")
+    capi.quat_cumprod_fwd(q, init, cum, ckpt=fin, workspace=ws)
+    capi.quat_cumprod_bwd(q, init, d, fin, d_q=d_q, d_init=d_init, workspace=ws)
+    torch.cuda.synchronize()
+    assert ws.status(q.device) == 0
+    got_dq = np.stack([_col(d_q, m) for m in COLS], axis=1).reshape(r_dq.shape)
+    got_di = d_init.view(B, M, 4)[0, COLS].float().cpu().numpy().astype(np.float64).reshape(r_di.shape)
+    for name, g, r in (("d_q (final carry)", got_dq, r_dq), ("d_init (final carry)", got_di, r_di)):
+        rel = float(np.abs(g - r).max() / np.abs(r).max())
+        print(f"[large] {name}: normwise rel err {rel:.2e}", flush=True)
+        assert np.isfinite(g).all(), name
+        assert rel <= 2e-2, f"{name}: normwise rel err {rel:.3e}"
+    del q, d, cum, d_q, ck, fin, ws
     torch.cuda.empty_cache()
