@@ -673,15 +673,18 @@ def all_configs_bench(args):
     import torch
 
     from quaternion_cumprod_autodiff_amd import capi
-    from quaternion_cumprod_autodiff_amd.inputs import CONFIGS, make_config
+    from quaternion_cumprod_autodiff_amd.inputs import CONFIGS, make_inputs
 
     dev = torch.device("cuda:0")
     names = args.configs.split(",") if args.configs else list(CONFIGS)
+    shards = max(1, args.seq_shards)
     for name in names:
         b, s, h, j, recipe, io = CONFIGS[name]
+        # One GPU's share of a sequence-sharded run: the first s / shards steps.
+        s = -(-s // shards)
         n, cols = b * s * h * j, b * h * j
         io_bytes = 16 if io == "f32" else 8
-        inp = make_config(name, want_f64=False)
+        inp = make_inputs(b, s, h, j, recipe, io, seed=0, want_f64=False)
 
         def up(a):
             t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if io == "bf16" else np.float32)).to(dev)
@@ -733,7 +736,8 @@ def all_configs_bench(args):
             gb = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9   # noqa: E731
             rec = {
                 "metric": "quat cumprod fwd+bwd GB/s and % HBM peak, per workload",
-                "config": {"workload": f"{name} b{b} s{s} h{h} j{j} {io} I/O, forward + backward", "b": b,
+                "config": {"workload": f"{name}{'' if shards == 1 else f' shard 1/{shards}'} b{b} s{s} h{h} j{j} "
+                                       f"{io} I/O, forward + backward", "b": b,
                            "s": s, "h": h, "j": j, "io_dtype": io, "recipe": recipe},
                 "backward": mode, "steps": args.steps,
                 "cache_resident": fwd_bytes < 256 * 2 ** 20,
@@ -871,6 +875,8 @@ def main():
                     help="with --gdn2: steps between saved boundary states (default: the workload's)")
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per named workload and backward mode (forward, backward, step rates)")
+    ap.add_argument("--seq-shards", type=int, default=1,
+                    help="with --all-configs: time one GPU's share of a run sharded N ways along the sequence")
     ap.add_argument("--configs", default="",
                     help="with --all-configs: comma-separated workload names (default: all)")
     ap.add_argument("--summarize-profile", metavar="TRACE_DIR",
