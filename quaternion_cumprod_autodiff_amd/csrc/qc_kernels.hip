@@ -17,10 +17,13 @@
 //            each lane owns L consecutive steps of one column in registers.
 //            The carry of the non-commutative product is combined in
 //            left-multiply order (later factor on the left) across lanes
-//            (ds_bpermute shuffles), across waves (LDS) and across blocks
+//            (permlane swaps, or ds_bpermute shuffles for narrow column
+//            groups), across waves (LDS) and across blocks
 //            (a Fenwick tree of per-tile carries in the workspace, see below).
 //            The backward runs its tiles in reverse time order and carries the
-//            plain (commutative) sum S in the same way.
+//            plain (commutative) sum S in the same way; without saved boundary
+//            products (only the forward's final carry) it carries instead each
+//            range's product and its share of S in the range's own frame.
 //
 // Cross-block carries.  Tiles of one column group form a chain; tile i
 // (1-based, in chain order) publishes node i of a Fenwick tree: the combined
