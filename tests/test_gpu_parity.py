@@ -413,6 +413,9 @@ def test_workspace_reuse_small_then_large_shapes():
     for inp in seq:
         print(f"[reuse b={inp.b} s={inp.s} h={inp.h} j={inp.j}]", flush=True)
         compare(inp, path="chunked", use_ckpt=False)
+        # The final-carry backward's pair slots are larger: slots of other
+        # kinds and shapes lie at other offsets under them.
+        compare(inp, path="chunked", use_ckpt=FINAL)
 
 
 @pytest.mark.parametrize("path", ["chunked", "column", "rscan", "grouped", "coresident", "final", "final-grouped"])
