@@ -223,9 +223,9 @@ int quat_cumprod_bwd_ex(const void* q, const void* init, const void* d_cum,
  *            on `stream` after the backward; 4-byte aligned, not overlapping
  *            any tensor of the call.
  * Shapes whose quat_cumprod_workspace_bytes exceeds 64 MiB are rejected with
- * QC_ERR_WORKSPACE before any HIP call (the largest float32 shapes of about
- * 60 million quaternions with a saved ckpt fit, depending on the column
- * count).  The first call on a device (with that device current) looks up
+ * QC_ERR_WORKSPACE before any HIP call (float32, b8 s4096 h32 j32 with 33.5
+ * million quaternions needs 56.5 MiB; the workspace grows with the number of
+ * quaternions and of columns).  The first call on a device (with that device current) looks up
  * the array's device address and zeroes its header on `stream`; make it
  * outside a graph capture to keep that fill out of the graph.  Every call on
  * one GPU shares that GPU's array: calls that overlap in time on one GPU race
