@@ -129,10 +129,6 @@ __device__ __forceinline__ Q4<T> shfl_up_q(const Q4<T>& v, int delta) {
     return {__shfl_up(v.w, delta), __shfl_up(v.x, delta), __shfl_up(v.y, delta), __shfl_up(v.z, delta)};
 }
 template <typename T>
-__device__ __forceinline__ Q4<T> shfl_down_q(const Q4<T>& v, int delta) {
-    return {__shfl_down(v.w, delta), __shfl_down(v.x, delta), __shfl_down(v.y, delta), __shfl_down(v.z, delta)};
-}
-template <typename T>
 __device__ __forceinline__ Q4<T> shfl_q(const Q4<T>& v, int src) {
     return {__shfl(v.w, src), __shfl(v.x, src), __shfl(v.y, src), __shfl(v.z, src)};
 }
@@ -1160,16 +1156,9 @@ __global__ void __launch_bounds__(NW * 64, (bwd_min_waves<IO, L>() < 3 ? bwd_min
             const Q4<CT> Z = qscale(qmul(Et, Sa), recip(nE));
             const Q4<CT> C = qmul(Et, IO::ct(init_raw));
             const Q4<CT> c0 = qmul(F, C);
-            Q4<CT> cm = qmul(A, C);
-            Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rp, qscale(qmul(A, Z), recip(nA))));
-#pragma unroll
-            for (int i = L - 1; i >= 0; --i) {
-                const Q4<CT> qi = IO::ct_fresh(qv[i]);
-                const Q4<CT> cprev = i == 0 ? c0 : qscale(qcmul(qi, cm), recip(qnorm2(qi)));
-                if (tc.full || tc.t0 + i < a.s) IO::store_stream(a.out, tc.base + int64_t(i) * a.M, qmulc(G, cprev));
-                if (i > 0) G = qadd(IO::ct_fresh(dv[i - 1]), qcmul(qi, G));
-                cm = cprev;
-            }
+            const Q4<CT> cm = qmul(A, C);
+            const Q4<CT> G = qadd(IO::ct_fresh(dv[L - 1]), qadd(Rp, qscale(qmul(A, Z), recip(nA))));
+            sweep2_store<IO, L>(a, tc, qv, dv, G, cm, c0);
         }
         __syncthreads();   // s_sq / s_sy are rewritten for the next chain
     }
