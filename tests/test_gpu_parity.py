@@ -331,14 +331,18 @@ def test_final_carry_refused_by_rscan_and_noalloc():
         capi.quat_cumprod_bwd_noalloc(q, init, d, torch.empty_like(q), torch.empty_like(init), ck)
 
 
-def test_determinism_repeated_runs():
+@pytest.mark.parametrize("use_ckpt,path", [(True, None), (FINAL, None), (FINAL, "fenwick")])
+def test_determinism_repeated_runs(use_ckpt, path):
+    """Every combine has a fixed association, so repeated runs agree bit for
+    bit, with either saved state and either look-back."""
     inp = make_config("medium")
-    first = run_device(inp)
+    first = run_device(inp, path=path, use_ckpt=use_ckpt)
     q, init, d = to_dev(inp.q, "f32"), to_dev(inp.init, "f32"), to_dev(inp.d_cum, "f32")
-    ck = capi.new_ckpt(q)
+    ck = new_state(q, use_ckpt)
+    opts, _ = path_options(path)
     for it in range(100):
-        cum = capi.quat_cumprod_fwd(q, init, ckpt=ck)
-        d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ckpt=ck)
+        cum = capi.quat_cumprod_fwd(q, init, ckpt=ck, **opts)
+        d_q, d_init = capi.quat_cumprod_bwd(q, init, d, ckpt=ck, **opts)
         assert torch.equal(cum, first[0]) and torch.equal(d_q, first[1]) and torch.equal(d_init, first[2]), it
     assert capi.default_workspace.status(q.device) == 0
 
