@@ -763,7 +763,7 @@ def short_kernel_name(name: str) -> str:
 
 
 def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command: str, bench_log: str | None = None,
-                      saved: str = "boundary"):
+                      saved: str = "boundary", out_dir: str | None = None):
     """Write profiles/kernels_<config>.txt from a rocprofv3 --kernel-trace
     --stats run (and, with pmc_dir, its FETCH_SIZE / WRITE_SIZE runs scaled by
     the plain-copy calibration factors of traffic_headline.txt).  Kernel
@@ -826,7 +826,8 @@ def summarize_profile(trace_dir: str, config: str, pmc_dir: str | None, command:
             tot = f[k] * fs + w[k] * ws
             lines.append(f"{short_kernel_name(k)[:72]:72s} {f[k] * fs:14.0f} {w[k] * ws:14.0f} "
                          f"{(base if base else 0):14d} {(tot / base if base else 0):6.3f}")
-    path = os.path.join(ROOT, "profiles", f"kernels_{config}{'' if saved == 'boundary' else '_' + saved}.txt")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"),
+                        f"kernels_{config}{'' if saved == 'boundary' else '_' + saved}.txt")
     with open(path, "w") as out:
         out.write("\n".join(lines) + "\n")
     print(path)
