@@ -40,8 +40,10 @@
 //   wy_bwd_carry_kernel one block per (head, 32 dense columns): the chunks in
 //                       reverse, carrying dS; saves the dS entering every
 //                       chunk from later ones (scratch), and d initial_state.
-//   wy_bwd_grad_kernel  one block per (head, chunk), all chunks at once: from
-//                       the chunk's record, boundary state and dS, every
+//   wy_bwd_grad_kernel  every (head, chunk) independently, as many blocks as
+//                       the device holds at once, each looping over chunks
+//                       and loading the next one's inputs during the current:
+//                       from the chunk's record, boundary state and dS, every
 //                       cotangent of the chunk's steps; the sums over the
 //                       dense axis stay in MFMA accumulators across the
 //                       block's walk over 32-column dense tiles.
@@ -760,10 +762,8 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     __shared__ GradTiles<CP, LP> g;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t head = blockIdx.x / a.n_chunks;
-    const int64_t c = blockIdx.x % a.n_chunks;
-    const int64_t t0 = c * CP;
     const int64_t nb = a.n_chunks;
+    const uint32_t nb32 = uint32_t(nb), n_items = uint32_t(a.BH * nb);   // the launch checks both fit
     const float s = a.scale;
 
     // rowsum(dSc . S0) partials: thread (l = tid / (256 / LP) ...) over its elements.
@@ -773,12 +773,13 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     // One dense tile's loads, in registers: S0 and dS (this thread's row
     // l = tid / TPL, EPL columns), and U (saved by the forward), drhs (written
     // by the carry kernel) and dO (elements tid + i * kThreads of the
-    // [CP][kDN] tile).  The next tile's are issued while this one computes;
-    // values are raw (clamped) and masked where consumed.
+    // [CP][kDN] tile).  The next tile's are issued while this one computes,
+    // the next item's first tile during this item's last; values are raw
+    // (clamped) and masked where consumed.
     float sv[EPL], dsv[EPL], uu[EPT], rv[EPT], oo[EPT];
     const int xl_l = tid / TPL, xl_n0 = (tid % TPL) * EPL;
     const int xl_lc = xl_l < a.L ? xl_l : int(a.L) - 1, D = int(a.D);
-    auto load_tile = [&](int64_t d0) {
+    auto load_tile = [&](int64_t head, int64_t c, int64_t d0) {
         // Block-uniform bases and 32-bit clamped offsets (see tile_base).
         const int lc = last_col(a, d0);
         const int64_t sbase = (head * nb + c) * LP * a.D + d0;
@@ -791,7 +792,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             sv[i] = sb[off];
             dsv[i] = dsb[off];
         }
-        const int64_t ubase = (head * nb * CP + t0) * a.D + d0;
+        const int64_t ubase = (head * nb + c) * CP * a.D + d0;
         const float* ub = a.ubuf + ubase;
         const float* rb = a.drhs + ubase;
 #pragma unroll
@@ -801,30 +802,27 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             uu[i] = ub[off];
             rv[i] = rb[off];
         }
-        load_dense<CP, false>(a.dctx, nullptr, a, head, t0, d0, tid, oo, nullptr);
+        load_dense<CP, false>(a.dctx, nullptr, a, head, c * CP, d0, tid, oo, nullptr);
     };
 
-    // Prologue: every load of the block is issued before the first wait
-    // (latent inputs, the record's M, Qc and c_last, the first dense tile), so
-    // their latencies overlap.
+    // An item's other loads: its latent inputs k, b, g (raw, clamped copies
+    // past T or L) and its record's M, Qc and c_last.
     using R = Rec<CP, LP>;
     constexpr int NR4 = R::kKt / 4 + LP / 4;        // float4 of M, Qc and c_last
     constexpr int RPER = (NR4 + kThreads - 1) / kThreads;
-    LatIn<RPT> in;
-    {
+    LatIn<RPT> raw;
+    f32x4 recv[RPER];
+    auto load_item = [&](int64_t head, int64_t c) {
         const int l = tid % LP, rg = tid / LP;
         const int64_t lc = l < a.L ? l : a.L - 1;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int64_t t = t0 + rg * RPT + i;
+            const int64_t t = c * CP + rg * RPT + i;
             const int64_t idx = (head * a.T + (t < a.T ? t : a.T - 1)) * a.L + lc;
-            in.k[i] = a.k[idx];
-            in.b[i] = a.b[idx];
-            in.g[i] = a.g[idx];
+            raw.k[i] = a.k[idx];
+            raw.b[i] = a.b[idx];
+            raw.g[i] = a.g[idx];
         }
-    }
-    f32x4 recv[RPER];
-    {
         const f32x4* rec4 = reinterpret_cast<const f32x4*>(a.rec + (head * nb + c) * R::kSize);
 #pragma unroll
         for (int i = 0; i < RPER; ++i) {
@@ -832,80 +830,124 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             const int jj = j < NR4 ? j : NR4 - 1;
             recv[i] = rec4[jj < R::kKt / 4 ? jj : R::kCl / 4 + (jj - R::kKt / 4)];
         }
-    }
-    load_tile(0);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const bool ok = latent_ok<CP, LP, RPT>(a, t0, tid, i);
-        in.k[i] = ok ? in.k[i] : 0.f;
-        in.b[i] = ok ? in.b[i] : 0.f;
-        in.g[i] = ok ? in.g[i] : 0.f;
-    }
-    // Wb = k / c, and c, 1/c of this thread's rows, as the factor kernel forms them.
-    float e[RPT], ie[RPT];
-    {
-        const int l = tid % LP, rg = tid / LP;
-        float G[RPT];
-        float run = 0.f;
+    };
+
+    // Items (head, chunk) = (item / n_chunks, item % n_chunks), item =
+    // blockIdx.x, blockIdx.x + gridDim.x, ...: the grid is as many blocks as
+    // the device holds at once, so every load of an item but the first is
+    // issued during the item before (the first: before any wait).
+    uint32_t item = blockIdx.x;
+    load_item(item / nb32, item % nb32);
+    load_tile(item / nb32, item % nb32, 0);
+    for (; item < n_items; item += gridDim.x) {
+        const int64_t head = item / nb32, c = item % nb32, t0 = c * CP;
+        const uint32_t nxt = item + gridDim.x < n_items ? item + gridDim.x : item;
+        const int64_t nhead = nxt / nb32, nc = nxt % nb32;
+        LatIn<RPT> in;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            run += in.g[i];
-            G[i] = run;
+            const bool ok = latent_ok<CP, LP, RPT>(a, t0, tid, i);
+            in.k[i] = ok ? raw.k[i] : 0.f;
+            in.b[i] = ok ? raw.b[i] : 0.f;
+            in.g[i] = ok ? raw.g[i] : 0.f;
         }
-        f.tot[rg * LP + l] = run;
-        __syncthreads();
-        float off = 0.f;
+        // c and 1/c of this thread's rows, as the factor kernel forms them, from
+        // the rows' g and the group sums in f.tot (which stay put until the next
+        // item, so the epilogue forms them again instead of keeping them live).
+        auto row_scales = [&](float* e, float* ie) {
+            const int l = tid % LP, rg = tid / LP;
+            float off = 0.f;
 #pragma unroll
-        for (int r = 0; r < RG; ++r)
-            if (r < rg) off += f.tot[r * LP + l];
+            for (int r = 0; r < RG; ++r)
+                if (r < rg) off += f.tot[r * LP + l];
+            float run = 0.f;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const float Gt = off + G[i];
-            e[i] = __expf(Gt);
-            ie[i] = __expf(-Gt);
-            f.Wb[(rg * RPT + i) * LS + l] = in.k[i] * ie[i];
+            for (int i = 0; i < RPT; ++i) {
+                run += in.g[i];
+                e[i] = __expf(off + run);
+                ie[i] = __expf(-(off + run));
+            }
+        };
+        {
+            const int l = tid % LP, rg = tid / LP;
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) run += in.g[i];
+            f.tot[rg * LP + l] = run;
+            __syncthreads();
+            float e[RPT], ie[RPT];
+            row_scales(e, ie);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) f.Wb[(rg * RPT + i) * LS + l] = in.k[i] * ie[i];   // Wb = k / c
         }
-    }
 #pragma unroll
-    for (int i = 0; i < RPER; ++i) {
-        const int j = tid + i * kThreads;
-        if (j < NR4) {
-            const int e4 = j < R::kKt / 4 ? 4 * j : R::kCl + 4 * (j - R::kKt / 4);
-            *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, e4)) = recv[i];
+        for (int i = 0; i < RPER; ++i) {
+            const int j = tid + i * kThreads;
+            if (j < NR4) {
+                const int e4 = j < R::kKt / 4 ? 4 * j : R::kCl + 4 * (j - R::kKt / 4);
+                *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, e4)) = recv[i];
+            }
         }
-    }
 
-    f32x4 accC[NCC], accQ[NCL], accM[NCL], accP[NCL];
+        f32x4 accC[NCC], accQ[NCL], accM[NCL], accP[NCL];
 #pragma unroll
-    for (int i = 0; i < NCC; ++i) accC[i] = zero4();
+        for (int i = 0; i < NCC; ++i) accC[i] = zero4();
 #pragma unroll
-    for (int i = 0; i < NCL; ++i) accQ[i] = accM[i] = accP[i] = zero4();
-    float xl = 0.f;
+        for (int i = 0; i < NCL; ++i) accQ[i] = accM[i] = accP[i] = zero4();
+        float xl = 0.f;
 
-    __syncthreads();   // the record and Wb are in LDS
-    for (int dt = 0; dt < a.n_dt; ++dt) {
-        const int64_t d0 = int64_t(dt) * kDN;
+        __syncthreads();   // the record and Wb are in LDS
+        for (int dt = 0; dt < a.n_dt; ++dt) {
+            const int64_t d0 = int64_t(dt) * kDN;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int n = xl_n0 + i;
-            const bool ok = xl_l < a.L && d0 + n < a.D;
-            const float sx = ok ? sv[i] : 0.f;
-            const float dv = ok ? dsv[i] * f.clast[xl_l] : 0.f;
-            g.t.S[xl_l * kDS + n] = sx;
-            g.t.D[xl_l * kDS + n] = dv;
-            xl += dv * sx;
-        }
+            for (int i = 0; i < EPL; ++i) {
+                const int n = xl_n0 + i;
+                const bool ok = xl_l < a.L && d0 + n < a.D;
+                const float sx = ok ? sv[i] : 0.f;
+                const float dv = ok ? dsv[i] * f.clast[xl_l] : 0.f;
+                g.t.S[xl_l * kDS + n] = sx;
+                g.t.D[xl_l * kDS + n] = dv;
+                xl += dv * sx;
+            }
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-            const bool okd = d0 + n < a.D;
-            g.t.U[row * kDS + n] = okd ? uu[i] : 0.f;
-            g.t.R[row * kDS + n] = okd ? rv[i] : 0.f;
-            g.t.O[row * kDS + n] = dense_ok(a, t0, d0, tid, i) ? oo[i] : 0.f;
+            for (int i = 0; i < EPT; ++i) {
+                const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
+                const bool okd = d0 + n < a.D;
+                g.t.U[row * kDS + n] = okd ? uu[i] : 0.f;
+                g.t.R[row * kDS + n] = okd ? rv[i] : 0.f;
+                g.t.O[row * kDS + n] = dense_ok(a, t0, d0, tid, i) ? oo[i] : 0.f;
+            }
+            // The next dense tile, or the next item's first (unconditional: see the forward).
+            const bool more = dt + 1 < a.n_dt;
+            load_tile(more ? head : nhead, more ? c : nc, more ? d0 + kDN : 0);
+            __syncthreads();
+            // Sums over the dense axis: dO U^T, drhs U^T (lower tiles), dO S0^T, drhs S0^T, U dSc^T.
+#pragma unroll
+            for (int sl = 0; sl < NCC; ++sl) {
+                const int job = wave + 4 * sl;
+                if (job < 2 * NJ) {
+                    const bool isA = job >= NJ;
+                    int ti, tj;
+                    lower_tile(isA ? job - NJ : job, ti, tj);
+                    mma_kc<kDN, kDS, kDS>(accC[sl], (isA ? g.t.R : g.t.O) + ti * 16 * kDS, g.t.U + tj * 16 * kDS, lane);
+                }
+            }
+#pragma unroll
+            for (int sl = 0; sl < NCL; ++sl) {
+                const int job = wave + 4 * sl;
+                if (job < NL) {
+                    const int ti = job / (LP / 16), lj = job % (LP / 16);
+                    mma_kc<kDN, kDS, kDS>(accQ[sl], g.t.O + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
+                    mma_kc<kDN, kDS, kDS>(accM[sl], g.t.R + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
+                    mma_kc<kDN, kDS, kDS>(accP[sl], g.t.U + ti * 16 * kDS, g.t.D + lj * 16 * kDS, lane);
+                }
+            }
+            __syncthreads();
         }
-        load_tile(dt + 1 < a.n_dt ? d0 + kDN : d0);   // unconditional prefetch (see the forward)
-        __syncthreads();
-        // Sums over the dense axis: dO U^T, drhs U^T (lower tiles), dO S0^T, drhs S0^T, U dSc^T.
+
+        load_item(nhead, nc);   // the next item's latents and record, consumed at its start
+        // dBq = lower(dO U^T) / sqrt(L) into f.Bq, dA = -strictly lower(drhs U^T) into f.Tm
+        // (their buffers are free: this kernel reads neither T nor Bq).
 #pragma unroll
         for (int sl = 0; sl < NCC; ++sl) {
             const int job = wave + 4 * sl;
@@ -913,123 +955,101 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
                 const bool isA = job >= NJ;
                 int ti, tj;
                 lower_tile(isA ? job - NJ : job, ti, tj);
-                mma_kc<kDN, kDS, kDS>(accC[sl], (isA ? g.t.R : g.t.O) + ti * 16 * kDS, g.t.U + tj * 16 * kDS, lane);
+                float* dst = (isA ? f.Tm : f.Bq) + ti * 16 * CS + tj * 16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int gi = ti * 16 + acc_row(lane, r), gj = tj * 16 + acc_col(lane);
+                    const bool keep = isA ? gi > gj : gi >= gj;
+                    dst[acc_row(lane, r) * CS + acc_col(lane)] = keep ? (isA ? -accC[sl][r] : accC[sl][r] * s) : 0.f;
+                }
             }
         }
+        if constexpr (NT > 1) {   // their upper tile (0, 1) is zero
+            for (int idx = tid; idx < 256; idx += kThreads) {
+                f.Tm[(idx / 16) * CS + 16 + idx % 16] = 0.f;
+                f.Bq[(idx / 16) * CS + 16 + idx % 16] = 0.f;
+            }
+        }
+        g.m.xl[tid] = xl;
+        __syncthreads();
+        // dQc = s dO S0^T + dBq Wb;  dM = -drhs S0^T + dA Wb;  dWb = U dSc^T + dBq^T Qc + dA^T M.
+        // P = U dSc^T is kept apart too, for the last step's term sum_tau Wb[tau][l] P[tau][l].
 #pragma unroll
         for (int sl = 0; sl < NCL; ++sl) {
             const int job = wave + 4 * sl;
             if (job < NL) {
                 const int ti = job / (LP / 16), lj = job % (LP / 16);
-                mma_kc<kDN, kDS, kDS>(accQ[sl], g.t.O + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
-                mma_kc<kDN, kDS, kDS>(accM[sl], g.t.R + ti * 16 * kDS, g.t.S + lj * 16 * kDS, lane);
-                mma_kc<kDN, kDS, kDS>(accP[sl], g.t.U + ti * 16 * kDS, g.t.D + lj * 16 * kDS, lane);
+                f32x4 q4, m4, w4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    q4[r] = accQ[sl][r] * s;
+                    m4[r] = -accM[sl][r];
+                }
+                w4 = accP[sl];
+                mma16<CP, CS, 1, LS, 1>(q4, f.Bq + ti * 16 * CS, f.Wb + lj * 16, ti + 1, lane);
+                mma16<CP, CS, 1, LS, 1>(m4, f.Tm + ti * 16 * CS, f.Wb + lj * 16, ti + 1, lane);
+                mma16<CP, 1, CS, LS, 1>(w4, f.Bq + ti * 16 * CS + ti * 16, f.Qc + ti * 16 * LS + lj * 16, NT - ti, lane);
+                mma16<CP, 1, CS, LS, 1>(w4, f.Tm + ti * 16 * CS + ti * 16, f.M + ti * 16 * LS + lj * 16, NT - ti, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = ti * 16 + acc_row(lane, r), col = lj * 16 + acc_col(lane);
+                    g.m.dQc[row * LP + col] = q4[r];
+                    g.m.dM[row * LP + col] = m4[r];
+                    g.m.dWb[row * LP + col] = w4[r];
+                    g.m.P[row * LP + col] = accP[sl][r];
+                }
             }
         }
         __syncthreads();
-    }
-
-    // dBq = lower(dO U^T) / sqrt(L) into f.Bq, dA = -strictly lower(drhs U^T) into f.Tm
-    // (their buffers are free: this kernel reads neither T nor Bq).
-#pragma unroll
-    for (int sl = 0; sl < NCC; ++sl) {
-        const int job = wave + 4 * sl;
-        if (job < 2 * NJ) {
-            const bool isA = job >= NJ;
-            int ti, tj;
-            lower_tile(isA ? job - NJ : job, ti, tj);
-            float* dst = (isA ? f.Tm : f.Bq) + ti * 16 * CS + tj * 16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int gi = ti * 16 + acc_row(lane, r), gj = tj * 16 + acc_col(lane);
-                const bool keep = isA ? gi > gj : gi >= gj;
-                dst[acc_row(lane, r) * CS + acc_col(lane)] = keep ? (isA ? -accC[sl][r] : accC[sl][r] * s) : 0.f;
-            }
-        }
-    }
-    if constexpr (NT > 1) {   // their upper tile (0, 1) is zero
-        for (int idx = tid; idx < 256; idx += kThreads) {
-            f.Tm[(idx / 16) * CS + 16 + idx % 16] = 0.f;
-            f.Bq[(idx / 16) * CS + 16 + idx % 16] = 0.f;
-        }
-    }
-    g.m.xl[tid] = xl;
-    __syncthreads();
-    // dQc = s dO S0^T + dBq Wb;  dM = -drhs S0^T + dA Wb;  dWb = U dSc^T + dBq^T Qc + dA^T M.
-    // P = U dSc^T is kept apart too, for the last step's term sum_tau Wb[tau][l] P[tau][l].
-#pragma unroll
-    for (int sl = 0; sl < NCL; ++sl) {
-        const int job = wave + 4 * sl;
-        if (job < NL) {
-            const int ti = job / (LP / 16), lj = job % (LP / 16);
-            f32x4 q4, m4, w4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                q4[r] = accQ[sl][r] * s;
-                m4[r] = -accM[sl][r];
-            }
-            w4 = accP[sl];
-            mma16<CP, CS, 1, LS, 1>(q4, f.Bq + ti * 16 * CS, f.Wb + lj * 16, ti + 1, lane);
-            mma16<CP, CS, 1, LS, 1>(m4, f.Tm + ti * 16 * CS, f.Wb + lj * 16, ti + 1, lane);
-            mma16<CP, 1, CS, LS, 1>(w4, f.Bq + ti * 16 * CS + ti * 16, f.Qc + ti * 16 * LS + lj * 16, NT - ti, lane);
-            mma16<CP, 1, CS, LS, 1>(w4, f.Tm + ti * 16 * CS + ti * 16, f.M + ti * 16 * LS + lj * 16, NT - ti, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = ti * 16 + acc_row(lane, r), col = lj * 16 + acc_col(lane);
-                g.m.dQc[row * LP + col] = q4[r];
-                g.m.dM[row * LP + col] = m4[r];
-                g.m.dWb[row * LP + col] = w4[r];
-                g.m.P[row * LP + col] = accP[sl][r];
-            }
-        }
-    }
-    __syncthreads();
-    // Per (step, latent row): this thread's rows rg*RPT + i of row l.
-    {
-        const int l = tid % LP, rg = tid / LP;
-        float dcc[RPT];
-        float pp = 0.f;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int row = rg * RPT + i;
-            const float dQc = g.m.dQc[row * LP + l], dM = g.m.dM[row * LP + l], dWb = g.m.dWb[row * LP + l];
-            const float Qc = f.Qc[row * LS + l], M = f.M[row * LS + l], Wb = f.Wb[row * LS + l];
-            dcc[i] = dQc * Qc + dM * M - dWb * Wb;
-            pp += Wb * g.m.P[row * LP + l];
-            const int64_t t = t0 + row;
-            if (t < a.T && l < a.L) {
-                const int64_t gi = (head * a.T + t) * a.L + l;
-                if (a.dq) a.dq[gi] = dQc * e[i];
-                if (a.db) a.db[gi] = dM * in.k[i] * e[i];
-                if (a.dk) a.dk[gi] = dM * in.b[i] * e[i] + dWb * ie[i];
-            }
-        }
-        // Suffix sums of dcc over the chunk: local, then later groups' totals.
-        float suf[RPT];
-        float run = 0.f;
-#pragma unroll
-        for (int i = RPT - 1; i >= 0; --i) {
-            run += dcc[i];
-            suf[i] = run;
-        }
-        g.m.red[rg * LP + l] = run;
-        g.m.red[kThreads + rg * LP + l] = pp;
-        __syncthreads();
-        float later = 0.f, xlt = 0.f;
-#pragma unroll
-        for (int r = RG - 1; r >= 0; --r) {
-            if (r > rg) later += g.m.red[r * LP + l];
-            xlt += g.m.red[kThreads + r * LP + l];
-        }
-        // The end state's term, rowsum(dSc . (S0 + Wb^T U)), enters at the
-        // chunk's last step, so every step of the chunk gets it.
-#pragma unroll
-        for (int r = 0; r < TPL; ++r) xlt += g.m.xl[l * TPL + r];
-        if (a.dg) {
+        // Per (step, latent row): this thread's rows rg*RPT + i of row l.
+        {
+            const int l = tid % LP, rg = tid / LP;
+            float e[RPT], ie[RPT];
+            row_scales(e, ie);
+            float dcc[RPT];
+            float pp = 0.f;
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const int64_t t = t0 + rg * RPT + i;
-                if (t < a.T && l < a.L) a.dg[(head * a.T + t) * a.L + l] = suf[i] + later + xlt;
+                const int row = rg * RPT + i;
+                const float dQc = g.m.dQc[row * LP + l], dM = g.m.dM[row * LP + l], dWb = g.m.dWb[row * LP + l];
+                const float Qc = f.Qc[row * LS + l], M = f.M[row * LS + l], Wb = f.Wb[row * LS + l];
+                dcc[i] = dQc * Qc + dM * M - dWb * Wb;
+                pp += Wb * g.m.P[row * LP + l];
+                const int64_t t = t0 + row;
+                if (t < a.T && l < a.L) {
+                    const int64_t gi = (head * a.T + t) * a.L + l;
+                    if (a.dq) a.dq[gi] = dQc * e[i];
+                    if (a.db) a.db[gi] = dM * in.k[i] * e[i];
+                    if (a.dk) a.dk[gi] = dM * in.b[i] * e[i] + dWb * ie[i];
+                }
+            }
+            // Suffix sums of dcc over the chunk: local, then later groups' totals.
+            float suf[RPT];
+            float run = 0.f;
+#pragma unroll
+            for (int i = RPT - 1; i >= 0; --i) {
+                run += dcc[i];
+                suf[i] = run;
+            }
+            g.m.red[rg * LP + l] = run;
+            g.m.red[kThreads + rg * LP + l] = pp;
+            __syncthreads();
+            float later = 0.f, xlt = 0.f;
+#pragma unroll
+            for (int r = RG - 1; r >= 0; --r) {
+                if (r > rg) later += g.m.red[r * LP + l];
+                xlt += g.m.red[kThreads + r * LP + l];
+            }
+            // The end state's term, rowsum(dSc . (S0 + Wb^T U)), enters at the
+            // chunk's last step, so every step of the chunk gets it.
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) xlt += g.m.xl[l * TPL + r];
+            if (a.dg) {
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int64_t t = t0 + rg * RPT + i;
+                    if (t < a.T && l < a.L) a.dg[(head * a.T + t) * a.L + l] = suf[i] + later + xlt;
+                }
             }
         }
     }
@@ -1059,8 +1079,16 @@ hipError_t launch_bwd_t(const WyArgs& a, hipStream_t st) {
                                    dim3(kThreads), params, 0, st);
     if (e != hipSuccess) return e;
     if (!a.dq && !a.dk && !a.dv && !a.db && !a.dw && !a.dg) return hipSuccess;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&wy_bwd_grad_kernel<CP, LP>),
-                           dim3(unsigned(a.BH * a.n_chunks)), dim3(kThreads), params, 0, st);
+    const void* grad = reinterpret_cast<const void*>(&wy_bwd_grad_kernel<CP, LP>);
+    int dev = 0, cus = 0, per_cu = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grad, kThreads, 0);
+    if (e != hipSuccess) return e;
+    // As many blocks as the device holds at once, each looping over items.
+    const int64_t items = a.BH * a.n_chunks, resident = int64_t(cus) * (per_cu > 0 ? per_cu : 1);
+    if (items > int64_t(UINT32_MAX)) return hipErrorInvalidValue;   // the kernel counts items in 32 bits
+    return hipLaunchKernel(grad, dim3(unsigned(items < resident ? items : resident)), dim3(kThreads), params, 0, st);
 }
 
 template <int CP>
