@@ -778,6 +778,9 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     // (clamped) and masked where consumed.
     float sv[EPL], dsv[EPL], uu[EPT], rv[EPT], oo[EPT];
     const int xl_l = tid / TPL, xl_n0 = (tid % TPL) * EPL;
+    constexpr int SV = EPL < 4 ? EPL : 4;            // floats per LDS vector store of S0 and dSc
+    typedef float svec __attribute__((ext_vector_type(SV)));
+    static_assert(EPL % SV == 0 && kDS % SV == 0, "aligned vector stores");
     const int xl_lc = xl_l < a.L ? xl_l : int(a.L) - 1, D = int(a.D);
     auto load_tile = [&](int64_t head, int64_t c, int64_t d0) {
         // Block-uniform bases and 32-bit clamped offsets (see tile_base).
@@ -899,23 +902,35 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
         __syncthreads();   // the record and Wb are in LDS
         for (int dt = 0; dt < a.n_dt; ++dt) {
             const int64_t d0 = int64_t(dt) * kDN;
+            // Masks in 32 bits against the tile's own extent, c_last read once
+            // and unconditionally (a conditional LDS read had become a branch
+            // and an LDS wait per element), and this thread's EPL adjacent
+            // S0 and dSc columns stored as whole vectors.
+            const int ncols = a.D - d0 < kDN ? int(a.D - d0) : kDN;
+            const int nrows = a.T - t0 < CP ? int(a.T - t0) : CP;
+            const float cl = f.clast[xl_l];
+            const bool lok = xl_l < a.L;
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const int n = xl_n0 + i;
-                const bool ok = xl_l < a.L && d0 + n < a.D;
-                const float sx = ok ? sv[i] : 0.f;
-                const float dv = ok ? dsv[i] * f.clast[xl_l] : 0.f;
-                g.t.S[xl_l * kDS + n] = sx;
-                g.t.D[xl_l * kDS + n] = dv;
-                xl += dv * sx;
+            for (int j = 0; j < EPL / SV; ++j) {
+                svec s4, d4;
+#pragma unroll
+                for (int e = 0; e < SV; ++e) {
+                    const int i = j * SV + e;
+                    const bool ok = lok && xl_n0 + i < ncols;
+                    s4[e] = ok ? sv[i] : 0.f;
+                    d4[e] = ok ? dsv[i] * cl : 0.f;
+                    xl += d4[e] * s4[e];
+                }
+                *reinterpret_cast<svec*>(g.t.S + xl_l * kDS + xl_n0 + j * SV) = s4;
+                *reinterpret_cast<svec*>(g.t.D + xl_l * kDS + xl_n0 + j * SV) = d4;
             }
 #pragma unroll
             for (int i = 0; i < EPT; ++i) {
                 const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-                const bool okd = d0 + n < a.D;
+                const bool okd = n < ncols;
                 g.t.U[row * kDS + n] = okd ? uu[i] : 0.f;
                 g.t.R[row * kDS + n] = okd ? rv[i] : 0.f;
-                g.t.O[row * kDS + n] = dense_ok(a, t0, d0, tid, i) ? oo[i] : 0.f;
+                g.t.O[row * kDS + n] = okd && row < nrows ? oo[i] : 0.f;
             }
             // The next dense tile, or the next item's first (unconditional: see the forward).
             const bool more = dt + 1 < a.n_dt;
