@@ -32,14 +32,18 @@
 //                       chunk's factors M, Qc, Kt, T, Bq and c_last, written
 //                       as one record per chunk after the boundary states
 //                       (the forward's saved state for the backward).
-//   wy_fwd_kernel       one block per (head, 32 dense columns): the chunks in
-//                       order, streaming their records; the state tile stays
-//                       in LDS; saves the state at every chunk start.  Without
-//                       a boundary buffer (no backward to follow) a fused
-//                       variant builds each chunk's factors itself.
-//   wy_bwd_carry_kernel one block per (head, 32 dense columns): the chunks in
+//   wy_fwd_strip_kernel one wave per (head, 16 dense columns), four to a
+//                       block: the chunks in order, streaming their records
+//                       through two LDS copies; each wave carries its strip
+//                       of the state alone; saves the state at every chunk
+//                       start and U.
+//   wy_fwd_kernel       without a boundary buffer (no backward to follow):
+//                       one block per (head, 32 dense columns), building
+//                       each chunk's factors itself.
+//   wy_bwd_carry_strip_kernel  as the forward strip kernel, the chunks in
 //                       reverse, carrying dS; saves the dS entering every
-//                       chunk from later ones (scratch), and d initial_state.
+//                       chunk from later ones and drhs (scratch), dv, dw and
+//                       d initial_state.
 //   wy_bwd_grad_kernel  every (head, chunk) independently, as many blocks as
 //                       the device holds at once, each looping over chunks
 //                       and loading the next one's inputs during the current:
@@ -47,8 +51,8 @@
 //                       cotangent of the chunk's steps; the sums over the
 //                       dense axis stay in MFMA accumulators across the
 //                       block's walk over 32-column dense tiles.
-// The sequential kernels deal their blocks so that all dense tiles of a head
-// run on one XCD (block % 8), where they share the head's records in L2.
+// The sequential kernels deal their blocks so that all dense columns of a
+// head run on one XCD (block % 8), where they share the head's records in L2.
 // Padded steps (past T in the last chunk) have k = q = b = v = w = g = 0: they
 // leave the state unchanged and get no output.
 #include "gdn2_internal.hpp"
@@ -582,150 +586,416 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
     }
 }
 
-// ----------------------------------------------------- backward: the carry
+// The forward over saved records, one wave per 16-column strip of the dense
+// axis: a block of 4 waves takes 64 dense columns of one head, and each wave
+// carries its strip's state S[:, strip] through the chunks alone.  Within a
+// chunk no wave needs another's results: rhs = w.v - M S, U = T rhs, O and
+// S_end of a strip use only that strip's columns.  The chunk's record is the
+// only shared operand; two LDS copies alternate, the next chunk's staged
+// while this one computes, so a chunk costs one barrier.  The strip's S^T,
+// rhs^T and U^T pass through the wave's own LDS area, from the accumulator
+// layout into the K-contiguous operand layout.  LDS operations of one wave
+// complete in order, so wave_sync (wavefront-scope fences around a wave
+// barrier: no instructions, only no compiler reordering) is all the ordering
+// that the exchange needs.
+// Stores without branches.  Loads and stores share one counter on gfx950,
+// and where a store sits under a branch (a lane mask, an optional output) the
+// compiler assumes, when it later waits for a load issued before the store,
+// that the branch skipped it: the wait then also covers every store issued
+// after that load.  A buffer resource over the output region drops stores at
+// offsets past its size, so masked lanes (and an output that is not wanted,
+// a region of size zero) store to an offset out of range instead, and every
+// store instruction issues on every path.
+constexpr int kRsrcWord3 = 0x00020000;     // gfx9 buffer resource: 32-bit elements, no swizzle
+struct OutRegion {
+    static constexpr int kDrop = 0x7ffffffc;   // a byte offset past every region
+    __amdgpu_buffer_rsrc_t r;
+    // floats: the region's size (at most 64 rows of the API's largest D, 1024).
+    __device__ OutRegion(float* base, int64_t floats)
+        : r(__builtin_amdgcn_make_buffer_rsrc(base, 0, base ? int(floats * 4) : 0, kRsrcWord3)) {}
+    __device__ void store(float v, bool ok, int idx) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, ok ? idx * 4 : kDrop, 0, 0);
+    }
+};
+
+constexpr int kStrip = 16;                 // dense columns per wave
+constexpr int kStripBlock = 4 * kStrip;    // dense columns per block
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int CP, int LP>
-__global__ void __launch_bounds__(kThreads, 2) wy_bwd_carry_kernel(WyArgs a) {
+struct alignas(16) StripT {                // one wave's transposes: S^T [16][LP + 4], rhs^T and U^T [16][CP + 4]
+    float st[16 * (LP + 4)], rt[16 * (CP + 4)], ut[16 * (CP + 4)];
+};
+
+template <int CP, int LP>
+__global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
     using F = StagedFactors<CP, LP>;
     using R = Rec<CP, LP>;
-    constexpr int kDS = kSeqDS;   // dense tiles here are read only as row-major B operands
     constexpr int LS = F::LS, CS = F::CS, NT = F::NT;
-    constexpr int NS = (LP / 16) * (kDN / 16);
-    constexpr int NSW = (NS + 3) / 4;
-    __shared__ F f;
-    __shared__ float sX[CP * kDS], sU[CP * kDS], sR[CP * kDS], sS[LP * kDS];
+    constexpr int NL = LP / 16;            // 16-row tiles of the state
+    constexpr int SST = LP + 4;            // row stride of the strip's S^T [16][LP]
+    constexpr int SCT = CP + 4;            // row stride of rhs^T and U^T [16][CP]
+    static_assert((SST / 4) % 2 == 1 && (SCT / 4) % 2 == 1 && (LS / 4) % 2 == 1 && (CS / 4) % 2 == 1,
+                  "16-byte operand reads on distinct banks");
+    __shared__ F f[2];
+    __shared__ StripT<CP, LP> strip[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int64_t head, d0;
-    if (!seq_block(a, &head, &d0)) return;
+    const int g4 = 4 * (lane >> 4), col = lane & 15;   // accumulator rows g4 + r, column col
+    // Blocks as the other sequential kernels deal them: a head's column groups on one XCD.
+    const int64_t n_dg = (a.D + kStripBlock - 1) / kStripBlock;
+    const int64_t xcd = blockIdx.x % 8, rest = blockIdx.x / 8;
+    const int64_t head = (rest / n_dg) * 8 + xcd;
+    if (head >= a.BH) return;
+    const int64_t d0 = (rest % n_dg) * kStripBlock + kStrip * wave;   // this wave's first column
     const int64_t nb = a.n_chunks;
-    const float s = a.scale;
+    const int D = int(a.D);
+    const bool col_ok = d0 + col < a.D;
+    const int cc = int(d0 + col < a.D ? d0 + col : a.D - 1);         // clamped column (absolute)
+    float* myST = strip[wave].st;
+    float* myRT = strip[wave].rt;
+    float* myUT = strip[wave].ut;
 
-    for (int idx = tid; idx < LP * kDN; idx += kThreads) {
-        const int l = idx / kDN, n = idx % kDN;
-        float v = 0.f;
-        if (l < a.L && d0 + n < a.D) {
-            if (a.dstate) v = a.dstate[(head * a.L + l) * a.D + d0 + n];
-            a.dbnd[((head * nb + nb - 1) * LP + l) * a.D + d0 + n] = v;
-        }
-        sS[l * kDS + n] = v;
-    }
-
-    constexpr int EPT = CP * kDN / kThreads;
-    RecRegs<CP, LP> rr;
-    float oo[EPT];
-    // v and w at this lane's elements of its drhs tile (job = wave: one
-    // 16x16 tile per wave when CP = 32, waves 0 and 1 when CP = 16), for
-    // dv = drhs . w and dw = drhs . v.
-    const bool has_tile = wave < NT * 2;
-    const int my_ti = (wave >> 1) % NT, my_tj = wave & 1;
-    float vt[4], wt[4];
-    auto load_vw = [&](int64_t tc0) {   // raw (clamped), masked where consumed
-        const int64_t base = tile_base(a, head, tc0, d0);
-        const float* vb = a.v + base;
-        const float* wb = a.w + base;
-        const int lr = last_row(a, tc0, CP), lc = last_col(a, d0), D = int(a.D);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = my_ti * 16 + acc_row(lane, r), col = my_tj * 16 + acc_col(lane);
-            const int off = (row < lr ? row : lr) * D + (col < lc ? col : lc);
-            vt[r] = vb[off];
-            wt[r] = wb[off];
-        }
-    };
-    load_rec<CP, LP>(rr, a.rec + (head * nb + nb - 1) * R::kSize, tid);
-    load_dense<CP, false>(a.dctx, nullptr, a, head, (nb - 1) * CP, d0, tid, oo, nullptr);
-    load_vw((nb - 1) * CP);
-    for (int64_t c = nb - 1; c >= 0; --c) {
+    // w and v of chunk c at this lane's accumulator elements (raw, clamped;
+    // masked where used).
+    float wv[NT][4], vv[NT][4];
+    auto load_wv = [&](int64_t c) {
         const int64_t t0 = c * CP;
+        const int lr = last_row(a, t0, CP);
+        const float* wb = a.w + (head * a.T + t0) * a.D;
+        const float* vb = a.v + (head * a.T + t0) * a.D;
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int idx = tid + i * kThreads;
-            sX[(idx / kDN) * kDS + idx % kDN] = dense_ok(a, t0, d0, tid, i) ? oo[i] : 0.f;
-        }
-        stage_rec<CP, LP>(f, rr, tid);
-        __syncthreads();
-        const int64_t cn = c > 0 ? c - 1 : c;   // unconditional prefetch (see the forward)
-        float vc[4], wc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            vc[r] = vt[r];
-            wc[r] = wt[r];
-        }
-        load_rec<CP, LP>(rr, a.rec + (head * nb + cn) * R::kSize, tid);
-        load_dense<CP, false>(a.dctx, nullptr, a, head, cn * CP, d0, tid, oo, nullptr);
-        load_vw(cn * CP);
-        // dU = Bq^T dO / sqrt(L) + Wb dSc, with Wb dSc = Kt dS (Kt = Wb diag(c_last)).
-        for (int job = wave; job < NT * 2; job += 4) {
-            const int ti = job >> 1, tj = job & 1;
-            f32x4 a1 = zero4(), a2 = zero4();
-            mma16<CP, 1, CS, kDS, 1>(a1, f.Bq + ti * 16 * CS + ti * 16, sX + ti * 16 * kDS + tj * 16, NT - ti, lane);
-            mma<LP, LS, 1, kDS, 1>(a2, f.Kt + ti * 16 * LS, sS + tj * 16, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sU[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = a1[r] * s + a2[r];
-        }
-        __syncthreads();
-        // drhs = T^T dU.
-        const int lr = last_row(a, t0, CP), lc = last_col(a, d0), D = int(a.D);
-        float* rb = a.drhs + (head * nb * CP + t0) * a.D + d0;
-        const int64_t gbase = tile_base(a, head, t0, d0);
-        float* dwb = a.dw ? a.dw + gbase : nullptr;
-        float* dvb = a.dv ? a.dv + gbase : nullptr;
-        for (int job = wave; job < NT * 2; job += 4) {
-            const int ti = job >> 1, tj = job & 1;
-            f32x4 acc = zero4();
-            mma16<CP, 1, CS, kDS, 1>(acc, f.Tm + ti * 16 * CS + ti * 16, sU + ti * 16 * kDS + tj * 16, NT - ti, lane);
+        for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
-                sR[row * kDS + col] = acc[r];
-                if (col <= lc) {
-                    const int off = row * D + col;
-                    rb[off] = acc[r];   // for the gradient kernel
-                    if (row <= lr) {
-                        if (dwb) dwb[off] = acc[r] * vc[r];
-                        if (dvb) dvb[off] = acc[r] * wc[r];
-                    }
-                }
+                const int row = 16 * ti + g4 + r;
+                const int off = (row < lr ? row : lr) * D + cc;
+                wv[ti][r] = wb[off];
+                vv[ti][r] = vb[off];
             }
-        }
-        __syncthreads();
-        // dS0 = Qc^T dO / sqrt(L) + diag(c_last) dS - M^T drhs.
-        f32x4 dnew[NSW];
+    };
+    auto write_t = [&](float* dstT, int stride, int row0, const f32x4& v) {   // rows row0 + g4 + r, column col
+        *reinterpret_cast<f32x4*>(dstT + col * stride + row0 + g4) = v;
+    };
+
+    // The state entering chunk 0, in accumulator layout: S[16 tl + g4 + r][col].
+    f32x4 sc[NL];
+    {
+        const float* s0 = a.s0 + head * a.L * a.D;
+        const OutRegion b0(a.bnd ? a.bnd + head * nb * LP * a.D : nullptr, LP * a.D);
 #pragma unroll
-        for (int sl = 0; sl < NSW; ++sl) {
-            const int job = wave + 4 * sl;
-            if (job < NS) {
-                const int ti = job >> 1, tj = job & 1;
-                f32x4 aq = zero4(), am = zero4();
-                mma<CP, 1, LS, kDS, 1>(aq, f.Qc + ti * 16, sX + tj * 16, lane);
-                mma<CP, 1, LS, kDS, 1>(am, f.M + ti * 16, sR + tj * 16, lane);
+        for (int tl = 0; tl < NL; ++tl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int l = 16 * tl + g4 + r;
+                sc[tl][r] = s0[(l < a.L ? l : int(a.L) - 1) * D + cc];   // clamped, masked below
+            }
+#pragma unroll
+        for (int tl = 0; tl < NL; ++tl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int l = 16 * tl + g4 + r;
+                const bool ok = l < a.L && col_ok;
+                sc[tl][r] = ok ? sc[tl][r] : 0.f;
+                b0.store(sc[tl][r], ok, l * D + int(d0) + col);
+            }
+    }
+#pragma unroll
+    for (int tl = 0; tl < NL; ++tl) write_t(myST, SST, 16 * tl, sc[tl]);
+
+    RecRegs<CP, LP> rr;
+    const float* recs = a.rec + head * nb * R::kSize;
+    load_rec<CP, LP>(rr, recs, tid);
+    stage_rec<CP, LP>(f[0], rr, tid);
+    load_rec<CP, LP>(rr, recs + (nb > 1 ? 1 : 0) * R::kSize, tid);
+    load_wv(0);
+    __syncthreads();
+
+    for (int64_t c = 0; c < nb; ++c) {
+        const int64_t t0 = c * CP;
+        F& fc = f[c & 1];
+        // x = w.v of this chunk (zero on padded steps), as the negated
+        // initial value of M S - x.
+        f32x4 nr[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = t0 + 16 * ti + g4 + r < a.T && col_ok;
+                nr[ti][r] = ok ? -(wv[ti][r] * vv[ti][r]) : 0.f;
+            }
+        // The next chunk's record into the other copy (its last readers were
+        // behind the previous chunk's barrier), then the loads for later
+        // chunks (unconditional, clamped: see the other kernels).
+        stage_rec<CP, LP>(f[(c + 1) & 1], rr, tid);
+        const int64_t c2 = c + 2 < nb ? c + 2 : nb - 1;
+        load_rec<CP, LP>(rr, recs + c2 * R::kSize, tid);
+        load_wv(c + 1 < nb ? c + 1 : c);
+
+        // M S - x and Qc S, tile rows ti (independent chains).
+        f32x4 o[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            o[ti] = zero4();
+            mma_kc<LP, LS, SST>(nr[ti], fc.M + 16 * ti * LS, myST, lane);
+            mma_kc<LP, LS, SST>(o[ti], fc.Qc + 16 * ti * LS, myST, lane);
+        }
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) write_t(myRT, SCT, 16 * ti, nr[ti]);
+        wave_sync();
+        // U = T rhs = -T (M S - x); T is lower triangular.
+        f32x4 u[NT];
+        u[0] = zero4();
+        mma_kc<16, CS, SCT>(u[0], fc.Tm, myRT, lane);
+        if constexpr (NT == 2) {
+            u[1] = zero4();
+            mma_kc<32, CS, SCT>(u[1], fc.Tm + 16 * CS, myRT, lane);
+        }
+        // U is kept for the backward (rows of the padded chunk, columns < D).
+        const OutRegion ub(a.ubuf ? a.ubuf + (head * nb * CP + t0) * a.D : nullptr, CP * a.D);
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                u[ti][r] = -u[ti][r];
+                ub.store(u[ti][r], col_ok, (16 * ti + g4 + r) * D + int(d0) + col);
+            }
+            write_t(myUT, SCT, 16 * ti, u[ti]);
+        }
+        wave_sync();
+        // O = (Qc S + Bq U) / sqrt(L); Bq is lower triangular.
+        mma_kc<16, CS, SCT>(o[0], fc.Bq, myUT, lane);
+        if constexpr (NT == 2) mma_kc<32, CS, SCT>(o[1], fc.Bq + 16 * CS, myUT, lane);
+        // S_end = diag(c_last) S + Kt^T U.
+#pragma unroll
+        for (int tl = 0; tl < NL; ++tl) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[tl][r] *= fc.clast[16 * tl + g4 + r];
+            mma<CP, 1, LS, 1, SCT>(sc[tl], fc.Kt + 16 * tl, myUT, lane);
+        }
+        const int rows = a.T - t0 < CP ? int(a.T - t0) : CP;
+        const OutRegion ob(a.ctx + (head * a.T + t0) * a.D, rows * a.D);
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * ti + g4 + r;
+                ob.store(o[ti][r] * a.scale, row < rows && col_ok, row * D + int(d0) + col);
+            }
+        // The state goes to the next chunk's boundary slot, or (last chunk)
+        // to the final state.
+        const OutRegion sb = c + 1 < nb
+            ? OutRegion(a.bnd ? a.bnd + (head * nb + c + 1) * LP * a.D : nullptr, LP * a.D)
+            : OutRegion(a.state ? a.state + head * a.L * a.D : nullptr, a.L * a.D);
+#pragma unroll
+        for (int tl = 0; tl < NL; ++tl) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int l = 16 * tl + g4 + r;
+                sb.store(sc[tl][r], l < a.L && col_ok, l * D + int(d0) + col);
+            }
+            write_t(myST, SST, 16 * tl, sc[tl]);
+        }
+        __syncthreads();   // the next record is staged, this one is free for the one after, S^T is written
+    }
+}
+
+// ----------------------------------------------------- backward: the carry
+
+// The reverse carry over saved records, one wave per 16-column strip as in
+// wy_fwd_strip_kernel: each wave carries its strip of dS through the chunks
+// in reverse, the chunk's record the only shared operand (two LDS copies, one
+// barrier per chunk); dO^T, dU^T, drhs^T and dS^T pass through the wave's own
+// LDS area.
+template <int CP, int LP>
+struct alignas(16) CarryStripT {          // one wave's transposes: dS^T [16][LP + 4]; dO^T, dU^T, drhs^T [16][CP + 4]
+    float st[16 * (LP + 4)], ot[16 * (CP + 4)], ut[16 * (CP + 4)], rt[16 * (CP + 4)];
+};
+
+template <int CP, int LP>
+__global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs a) {
+    using F = StagedFactors<CP, LP>;
+    using R = Rec<CP, LP>;
+    constexpr int LS = F::LS, CS = F::CS, NT = F::NT;
+    constexpr int NL = LP / 16;
+    constexpr int SST = LP + 4, SCT = CP + 4;
+    static_assert((SST / 4) % 2 == 1 && (SCT / 4) % 2 == 1 && (LS / 4) % 2 == 1, "16-byte operand reads on distinct banks");
+    __shared__ F f[2];
+    __shared__ CarryStripT<CP, LP> strip[4];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g4 = 4 * (lane >> 4), col = lane & 15;
+    const int64_t n_dg = (a.D + kStripBlock - 1) / kStripBlock;
+    const int64_t xcd = blockIdx.x % 8, rest = blockIdx.x / 8;
+    const int64_t head = (rest / n_dg) * 8 + xcd;
+    if (head >= a.BH) return;
+    const int64_t d0 = (rest % n_dg) * kStripBlock + kStrip * wave;
+    const int64_t nb = a.n_chunks;
+    const int D = int(a.D);
+    const float s = a.scale;
+    const bool col_ok = d0 + col < a.D;
+    const int cc = int(d0 + col < a.D ? d0 + col : a.D - 1);
+    float* myST = strip[wave].st;
+    float* myOT = strip[wave].ot;
+    float* myUT = strip[wave].ut;
+    float* myRT = strip[wave].rt;
+    auto write_t = [&](float* dstT, int stride, int row0, const f32x4& v) {
+        *reinterpret_cast<f32x4*>(dstT + col * stride + row0 + g4) = v;
+    };
+
+    // dO, w and v of chunk c at this lane's accumulator elements (raw, clamped).
+    float ov[NT][4], wv[NT][4], vv[NT][4];
+    auto load_dense3 = [&](int64_t c) {
+        const int64_t t0 = c * CP;
+        const int lr = last_row(a, t0, CP);
+        const int64_t base = (head * a.T + t0) * a.D;
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * ti + g4 + r;
+                const int off = (row < lr ? row : lr) * D + cc;
+                ov[ti][r] = a.dctx[base + off];
+                wv[ti][r] = a.w[base + off];
+                vv[ti][r] = a.v[base + off];
+            }
+    };
+
+    // The cotangent of the final state (zero if none), in accumulator layout,
+    // is what enters the last chunk from later ones.
+    f32x4 sc[NL];
+    {
+        const OutRegion b0(a.dbnd + (head * nb + nb - 1) * LP * a.D, LP * a.D);
+        if (a.dstate) {
+            const float* ds = a.dstate + head * a.L * a.D;
+#pragma unroll
+            for (int tl = 0; tl < NL; ++tl)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int l = ti * 16 + acc_row(lane, r);
-                    dnew[sl][r] = f.clast[l] * sS[l * kDS + tj * 16 + acc_col(lane)] + aq[r] * s - am[r];
+                    const int l = 16 * tl + g4 + r;
+                    sc[tl][r] = ds[(l < a.L ? l : int(a.L) - 1) * D + cc];
                 }
-            }
+        } else {
+#pragma unroll
+            for (int tl = 0; tl < NL; ++tl) sc[tl] = zero4();
         }
-        __syncthreads();
+#pragma unroll
+        for (int tl = 0; tl < NL; ++tl) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int l = 16 * tl + g4 + r;
+                const bool ok = l < a.L && col_ok;
+                sc[tl][r] = ok ? sc[tl][r] : 0.f;
+                b0.store(sc[tl][r], ok, l * D + int(d0) + col);
+            }
+            write_t(myST, SST, 16 * tl, sc[tl]);
+        }
+    }
+
+    RecRegs<CP, LP> rr;
+    const float* recs = a.rec + head * nb * R::kSize;
+    load_rec<CP, LP>(rr, recs + (nb - 1) * R::kSize, tid);
+    stage_rec<CP, LP>(f[(nb - 1) & 1], rr, tid);
+    load_rec<CP, LP>(rr, recs + (nb > 1 ? nb - 2 : 0) * R::kSize, tid);
+    load_dense3(nb - 1);
+    __syncthreads();
+
+    for (int64_t c = nb - 1; c >= 0; --c) {
+        const int64_t t0 = c * CP;
+        F& fc = f[c & 1];
+        const int rows = a.T - t0 < CP ? int(a.T - t0) : CP;
+        // dO of this chunk (zero past T) into its transpose; w and v kept for dw, dv.
+        float wc[NT][4], vc[NT][4];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            f32x4 o4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = 16 * ti + g4 + r < rows && col_ok;
+                o4[r] = ok ? ov[ti][r] : 0.f;
+                wc[ti][r] = wv[ti][r];
+                vc[ti][r] = vv[ti][r];
+            }
+            write_t(myOT, SCT, 16 * ti, o4);
+        }
+        // The previous chunk's record into the other copy, then the loads for
+        // earlier chunks (unconditional, clamped).
+        stage_rec<CP, LP>(f[(c + 1) & 1], rr, tid);
+        load_rec<CP, LP>(rr, recs + (c >= 2 ? c - 2 : 0) * R::kSize, tid);
+        load_dense3(c >= 1 ? c - 1 : 0);
+        wave_sync();
+
+        // dU = Bq^T dO / sqrt(L) + Kt dS  (Bq^T upper triangular: tile ti
+        // sums over steps 16 ti ..).
+        f32x4 du[NT], kd[NT];
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            du[ti] = zero4();
+            kd[ti] = zero4();
+            mma_kc<LP, LS, SST>(kd[ti], fc.Kt + 16 * ti * LS, myST, lane);
+        }
+        mma<CP, 1, CS, 1, SCT>(du[0], fc.Bq, myOT, lane);
+        if constexpr (NT == 2) mma<16, 1, CS, 1, SCT>(du[1], fc.Bq + 16 * CS + 16, myOT + 16, lane);
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) du[ti][r] = du[ti][r] * s + kd[ti][r];
+            write_t(myUT, SCT, 16 * ti, du[ti]);
+        }
+        wave_sync();
+        // drhs = T^T dU (upper triangular as Bq^T); dw = drhs . v, dv = drhs . w.
+        f32x4 dr[NT];
+        dr[0] = zero4();
+        mma<CP, 1, CS, 1, SCT>(dr[0], fc.Tm, myUT, lane);
+        if constexpr (NT == 2) {
+            dr[1] = zero4();
+            mma<16, 1, CS, 1, SCT>(dr[1], fc.Tm + 16 * CS + 16, myUT + 16, lane);
+        }
+        const OutRegion rb(a.drhs + (head * nb * CP + t0) * a.D, CP * a.D);
+        const int64_t gbase = (head * a.T + t0) * a.D;
+        const OutRegion dwb(a.dw ? a.dw + gbase : nullptr, rows * a.D);
+        const OutRegion dvb(a.dv ? a.dv + gbase : nullptr, rows * a.D);
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * ti + g4 + r;
+                const int off = row * D + int(d0) + col;
+                rb.store(dr[ti][r], col_ok, off);   // for the gradient kernel
+                dwb.store(dr[ti][r] * vc[ti][r], col_ok && row < rows, off);
+                dvb.store(dr[ti][r] * wc[ti][r], col_ok && row < rows, off);
+            }
+            write_t(myRT, SCT, 16 * ti, dr[ti]);
+        }
+        wave_sync();
+        // dS0 = Qc^T dO / sqrt(L) + diag(c_last) dS - M^T drhs.
+#pragma unroll
+        for (int tl = 0; tl < NL; ++tl) {
+            f32x4 aq = zero4(), am = zero4();
+            mma<CP, 1, LS, 1, SCT>(aq, fc.Qc + 16 * tl, myOT, lane);
+            mma<CP, 1, LS, 1, SCT>(am, fc.M + 16 * tl, myRT, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[tl][r] = fc.clast[16 * tl + g4 + r] * sc[tl][r] + aq[r] * s - am[r];
+        }
         // dS entering this chunk: the previous chunk's slot, or (first chunk)
         // d initial_state.
-        float* db = c > 0 ? a.dbnd + (head * nb + c - 1) * LP * a.D + d0
-                          : (a.ds0 ? a.ds0 + head * a.L * a.D + d0 : nullptr);
+        const OutRegion db = c > 0 ? OutRegion(a.dbnd + (head * nb + c - 1) * LP * a.D, LP * a.D)
+                                   : OutRegion(a.ds0 ? a.ds0 + head * a.L * a.D : nullptr, a.L * a.D);
 #pragma unroll
-        for (int sl = 0; sl < NSW; ++sl) {
-            const int job = wave + 4 * sl;
-            if (job < NS) {
-                const int ti = job >> 1, tj = job & 1;
+        for (int tl = 0; tl < NL; ++tl) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int l = ti * 16 + acc_row(lane, r), n = tj * 16 + acc_col(lane);
-                    sS[l * kDS + n] = dnew[sl][r];
-                    if (db && l < a.L && n <= lc) db[l * D + n] = dnew[sl][r];
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int l = 16 * tl + g4 + r;
+                db.store(sc[tl][r], l < a.L && col_ok, l * D + int(d0) + col);
             }
+            write_t(myST, SST, 16 * tl, sc[tl]);
         }
+        __syncthreads();   // the previous record is staged, this one is free for the one before
     }
 }
 
@@ -1021,6 +1291,14 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             const int l = tid % LP, rg = tid / LP;
             float e[RPT], ie[RPT];
             row_scales(e, ie);
+            // Branch-free stores (see OutRegion) of the chunk's real steps.
+            const int rows = a.T - t0 < CP ? int(a.T - t0) : CP;
+            const int64_t lbase = (head * a.T + t0) * a.L;
+            const OutRegion dq_out(a.dq ? a.dq + lbase : nullptr, rows * a.L);
+            const OutRegion db_out(a.db ? a.db + lbase : nullptr, rows * a.L);
+            const OutRegion dk_out(a.dk ? a.dk + lbase : nullptr, rows * a.L);
+            const OutRegion dg_out(a.dg ? a.dg + lbase : nullptr, rows * a.L);
+            const int Lr = int(a.L);
             float dcc[RPT];
             float pp = 0.f;
 #pragma unroll
@@ -1030,13 +1308,10 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
                 const float Qc = f.Qc[row * LS + l], M = f.M[row * LS + l], Wb = f.Wb[row * LS + l];
                 dcc[i] = dQc * Qc + dM * M - dWb * Wb;
                 pp += Wb * g.m.P[row * LP + l];
-                const int64_t t = t0 + row;
-                if (t < a.T && l < a.L) {
-                    const int64_t gi = (head * a.T + t) * a.L + l;
-                    if (a.dq) a.dq[gi] = dQc * e[i];
-                    if (a.db) a.db[gi] = dM * in.k[i] * e[i];
-                    if (a.dk) a.dk[gi] = dM * in.b[i] * e[i] + dWb * ie[i];
-                }
+                const bool real = row < rows && l < Lr;
+                dq_out.store(dQc * e[i], real, row * Lr + l);
+                db_out.store(dM * in.k[i] * e[i], real, row * Lr + l);
+                dk_out.store(dM * in.b[i] * e[i] + dWb * ie[i], real, row * Lr + l);
             }
             // Suffix sums of dcc over the chunk: local, then later groups' totals.
             float suf[RPT];
@@ -1059,12 +1334,10 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
             // chunk's last step, so every step of the chunk gets it.
 #pragma unroll
             for (int r = 0; r < TPL; ++r) xlt += g.m.xl[l * TPL + r];
-            if (a.dg) {
 #pragma unroll
-                for (int i = 0; i < RPT; ++i) {
-                    const int64_t t = t0 + rg * RPT + i;
-                    if (t < a.T && l < a.L) a.dg[(head * a.T + t) * a.L + l] = suf[i] + later + xlt;
-                }
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg * RPT + i;
+                dg_out.store(suf[i] + later + xlt, row < rows && l < Lr, row * Lr + l);
             }
         }
     }
@@ -1082,7 +1355,8 @@ hipError_t launch_fwd_t(const WyArgs& a, hipStream_t st) {
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wy_factor_kernel<CP, LP>),
                                    dim3(unsigned(a.BH * a.n_chunks)), dim3(kThreads), params, 0, st);
     if (e != hipSuccess) return e;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&wy_fwd_kernel<CP, LP, true>), dim3(seq_blocks(a)),
+    const unsigned strips = unsigned((a.BH + 7) / 8 * 8 * ((a.D + kStripBlock - 1) / kStripBlock));
+    return hipLaunchKernel(reinterpret_cast<const void*>(&wy_fwd_strip_kernel<CP, LP>), dim3(strips),
                            dim3(kThreads), params, 0, st);
 }
 
@@ -1090,7 +1364,8 @@ template <int CP, int LP>
 hipError_t launch_bwd_t(const WyArgs& a, hipStream_t st) {
     WyArgs args = a;
     void* params[] = {&args};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wy_bwd_carry_kernel<CP, LP>), dim3(seq_blocks(a)),
+    const unsigned strips = unsigned((a.BH + 7) / 8 * 8 * ((a.D + kStripBlock - 1) / kStripBlock));
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wy_bwd_carry_strip_kernel<CP, LP>), dim3(strips),
                                    dim3(kThreads), params, 0, st);
     if (e != hipSuccess) return e;
     if (!a.dq && !a.dk && !a.dv && !a.db && !a.dw && !a.dg) return hipSuccess;
