@@ -626,7 +626,7 @@ def gdn2_bench(args):
         "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 3),
         "head_steps_per_s": round(B * H * T / wall, 1),
         "roofline": {"bound": "mfma" if wy else "alu",
-                     "kernel": "gdn2_bwd (wy_bwd_carry_kernel + wy_bwd_grad_kernel)" if wy else "gdn2_bwd_kernel",
+                     "kernel": "gdn2_bwd (wy_bwd_carry_strip_kernel + wy_bwd_grad_kernel)" if wy else "gdn2_bwd_kernel",
                      "achieved": round(tflops, 3), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 5),
                      "flops_per_launch": bf,

@@ -58,6 +58,7 @@
 #include "gdn2_internal.hpp"
 #include "qc_internal.hpp"
 
+#include <cstddef>
 #include <type_traits>
 
 namespace qc {
@@ -118,6 +119,47 @@ __device__ __forceinline__ void mma_kc(f32x4& acc, const float* a, const float* 
     for (int j = 0; j < KQ / 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][e], bv[j][e], acc, 0, 0, 0);
+}
+
+// N independent products over one B, acc[c] += A_c B, with the MFMAs of the
+// N chains interleaved (no MFMA waits for the one just before it) and B read
+// once: the strided form of mma (A_c(m, k) = a[c][m * SAM + k * SAK]) ...
+template <int N, int K, int SAM, int SAK, int SBK, int SBN>
+__device__ __forceinline__ void mma_n(f32x4 (&acc)[N], const float* const (&a)[N], const float* b, int lane) {
+    const int i = lane & 15, kq = lane >> 4;
+    float bv[K / 4], av[N][K / 4];
+#pragma unroll
+    for (int k = 0; k < K / 4; ++k) {
+        bv[k] = b[(4 * k + kq) * SBK + i * SBN];
+#pragma unroll
+        for (int c = 0; c < N; ++c) av[c][k] = a[c][i * SAM + (4 * k + kq) * SAK];
+    }
+#pragma unroll
+    for (int k = 0; k < K / 4; ++k)
+#pragma unroll
+        for (int c = 0; c < N; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][k], bv[k], acc[c], 0, 0, 0);
+}
+
+// ... and the K-contiguous form of mma_kc (the same reordering of k).
+template <int N, int K, int SA, int SB>
+__device__ __forceinline__ void mma_kc_n(f32x4 (&acc)[N], const float* const (&a)[N], const float* bt, int lane) {
+    static_assert(K % 16 == 0 && SA % 4 == 0 && SB % 4 == 0, "16-byte operand reads");
+    constexpr int KQ = K / 4;
+    const int i = lane & 15, kq = lane >> 4;
+    const f32x4* pb = reinterpret_cast<const f32x4*>(bt + i * SB + kq * KQ);
+    f32x4 bv[KQ / 4], av[N][KQ / 4];
+#pragma unroll
+    for (int j = 0; j < KQ / 4; ++j) {
+        bv[j] = pb[j];
+#pragma unroll
+        for (int c = 0; c < N; ++c) av[c][j] = reinterpret_cast<const f32x4*>(a[c] + i * SA + kq * KQ)[j];
+    }
+#pragma unroll
+    for (int j = 0; j < KQ / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int c = 0; c < N; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][j][e], bv[j][e], acc[c], 0, 0, 0);
 }
 
 // The same with K = 16 * k16, k16 wave-uniform in 1 .. KMAX / 16 (the
@@ -415,6 +457,35 @@ __device__ __forceinline__ void stage_rec(F& f, const RecRegs<CP, LP>& r, int ti
     }
 }
 
+// Where this thread's float4 of a record land in staged factors F: offsets
+// in floats from the start of F (-1: none), formed once per kernel, so that
+// staging a record is a run of 16-byte LDS stores.
+template <int CP, int LP, class F>
+struct RecStage {
+    using R = Rec<CP, LP>;
+    int off[R::kPer];
+    __device__ explicit RecStage(int tid) {
+        constexpr int LS = F::LS, CS = F::CS;
+#pragma unroll
+        for (int i = 0; i < R::kPer; ++i) {
+            const int j = tid + i * kThreads, e = 4 * j;
+            off[i] = j >= R::kN4  ? -1
+                   : e < R::kQc  ? int(offsetof(F, M) / 4) + (e / LP) * LS + e % LP
+                   : e < R::kKt  ? int(offsetof(F, Qc) / 4) + ((e - R::kQc) / LP) * LS + (e - R::kQc) % LP
+                   : e < R::kT   ? int(offsetof(F, Kt) / 4) + ((e - R::kKt) / LP) * LS + (e - R::kKt) % LP
+                   : e < R::kBq  ? int(offsetof(F, Tm) / 4) + ((e - R::kT) / CP) * CS + (e - R::kT) % CP
+                   : e < R::kCl  ? int(offsetof(F, Bq) / 4) + ((e - R::kBq) / CP) * CS + (e - R::kBq) % CP
+                                 : int(offsetof(F, clast) / 4) + (e - R::kCl);
+        }
+    }
+    __device__ void stage(F& f, const RecRegs<CP, LP>& r) const {
+        float* base = reinterpret_cast<float*>(&f);
+#pragma unroll
+        for (int i = 0; i < R::kPer; ++i)
+            if (off[i] >= 0) *reinterpret_cast<f32x4*>(base + off[i]) = r.v[i];
+    }
+};
+
 template <int CP, int LP>
 __global__ void __launch_bounds__(kThreads, 2) wy_factor_kernel(WyArgs a) {
     using F = BuildFactors<CP, LP>;
@@ -709,9 +780,10 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
     for (int tl = 0; tl < NL; ++tl) write_t(myST, SST, 16 * tl, sc[tl]);
 
     RecRegs<CP, LP> rr;
+    const RecStage<CP, LP, F> rs(tid);
     const float* recs = a.rec + head * nb * R::kSize;
     load_rec<CP, LP>(rr, recs, tid);
-    stage_rec<CP, LP>(f[0], rr, tid);
+    rs.stage(f[0], rr);
     load_rec<CP, LP>(rr, recs + (nb > 1 ? 1 : 0) * R::kSize, tid);
     load_wv(0);
     __syncthreads();
@@ -732,29 +804,45 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
         // The next chunk's record into the other copy (its last readers were
         // behind the previous chunk's barrier), then the loads for later
         // chunks (unconditional, clamped: see the other kernels).
-        stage_rec<CP, LP>(f[(c + 1) & 1], rr, tid);
+        rs.stage(f[(c + 1) & 1], rr);
         const int64_t c2 = c + 2 < nb ? c + 2 : nb - 1;
         load_rec<CP, LP>(rr, recs + c2 * R::kSize, tid);
         load_wv(c + 1 < nb ? c + 1 : c);
 
         // M S - x and Qc S, tile rows ti (independent chains).
         f32x4 o[NT];
+        {
+            f32x4 acc[2 * NT];
+            const float* aa[2 * NT];
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
-            o[ti] = zero4();
-            mma_kc<LP, LS, SST>(nr[ti], fc.M + 16 * ti * LS, myST, lane);
-            mma_kc<LP, LS, SST>(o[ti], fc.Qc + 16 * ti * LS, myST, lane);
+            for (int ti = 0; ti < NT; ++ti) {
+                acc[2 * ti] = nr[ti];
+                acc[2 * ti + 1] = zero4();
+                aa[2 * ti] = fc.M + 16 * ti * LS;
+                aa[2 * ti + 1] = fc.Qc + 16 * ti * LS;
+            }
+            mma_kc_n<2 * NT, LP, LS, SST>(acc, aa, myST, lane);
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+                nr[ti] = acc[2 * ti];
+                o[ti] = acc[2 * ti + 1];
+            }
         }
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) write_t(myRT, SCT, 16 * ti, nr[ti]);
         wave_sync();
         // U = T rhs = -T (M S - x); T is lower triangular.
+        // (Row tile 1 sums over steps 0..15 together with row tile 0, then over 16..31.)
         f32x4 u[NT];
-        u[0] = zero4();
-        mma_kc<16, CS, SCT>(u[0], fc.Tm, myRT, lane);
-        if constexpr (NT == 2) {
-            u[1] = zero4();
-            mma_kc<32, CS, SCT>(u[1], fc.Tm + 16 * CS, myRT, lane);
+        {
+            const float* aa[NT];
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+                u[ti] = zero4();
+                aa[ti] = fc.Tm + 16 * ti * CS;
+            }
+            mma_kc_n<NT, 16, CS, SCT>(u, aa, myRT, lane);
+            if constexpr (NT == 2) mma_kc<16, CS, SCT>(u[1], fc.Tm + 16 * CS + 16, myRT + 16, lane);
         }
         // U is kept for the backward (rows of the padded chunk, columns < D).
         const OutRegion ub(a.ubuf ? a.ubuf + (head * nb * CP + t0) * a.D : nullptr, CP * a.D);
@@ -769,14 +857,23 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
         }
         wave_sync();
         // O = (Qc S + Bq U) / sqrt(L); Bq is lower triangular.
-        mma_kc<16, CS, SCT>(o[0], fc.Bq, myUT, lane);
-        if constexpr (NT == 2) mma_kc<32, CS, SCT>(o[1], fc.Bq + 16 * CS, myUT, lane);
+        {
+            const float* aa[NT];
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) aa[ti] = fc.Bq + 16 * ti * CS;
+            mma_kc_n<NT, 16, CS, SCT>(o, aa, myUT, lane);
+            if constexpr (NT == 2) mma_kc<16, CS, SCT>(o[1], fc.Bq + 16 * CS + 16, myUT + 16, lane);
+        }
         // S_end = diag(c_last) S + Kt^T U.
+        {
+            const float* aa[NL];
 #pragma unroll
-        for (int tl = 0; tl < NL; ++tl) {
+            for (int tl = 0; tl < NL; ++tl) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sc[tl][r] *= fc.clast[16 * tl + g4 + r];
-            mma<CP, 1, LS, 1, SCT>(sc[tl], fc.Kt + 16 * tl, myUT, lane);
+                for (int r = 0; r < 4; ++r) sc[tl][r] *= fc.clast[16 * tl + g4 + r];
+                aa[tl] = fc.Kt + 16 * tl;
+            }
+            mma_n<NL, CP, 1, LS, 1, SCT>(sc, aa, myUT, lane);
         }
         const int rows = a.T - t0 < CP ? int(a.T - t0) : CP;
         const OutRegion ob(a.ctx + (head * a.T + t0) * a.D, rows * a.D);
@@ -898,9 +995,10 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
     }
 
     RecRegs<CP, LP> rr;
+    const RecStage<CP, LP, F> rs(tid);
     const float* recs = a.rec + head * nb * R::kSize;
     load_rec<CP, LP>(rr, recs + (nb - 1) * R::kSize, tid);
-    stage_rec<CP, LP>(f[(nb - 1) & 1], rr, tid);
+    rs.stage(f[(nb - 1) & 1], rr);
     load_rec<CP, LP>(rr, recs + (nb > 1 ? nb - 2 : 0) * R::kSize, tid);
     load_dense3(nb - 1);
     __syncthreads();
@@ -925,7 +1023,7 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
         }
         // The previous chunk's record into the other copy, then the loads for
         // earlier chunks (unconditional, clamped).
-        stage_rec<CP, LP>(f[(c + 1) & 1], rr, tid);
+        rs.stage(f[(c + 1) & 1], rr);
         load_rec<CP, LP>(rr, recs + (c >= 2 ? c - 2 : 0) * R::kSize, tid);
         load_dense3(c >= 1 ? c - 1 : 0);
         wave_sync();
