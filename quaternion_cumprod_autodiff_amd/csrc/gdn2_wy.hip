@@ -1118,7 +1118,11 @@ struct alignas(16) GradTiles {
     };
 };
 
-template <int CP, int LP>
+// kVec: dense rows 16-byte aligned (D a multiple of 4, every dense base
+// aligned; chunks of 32, latent rows of 32 or 64): a dense tile's loads are
+// 16-byte vectors, a quarter of the load instructions, and U, drhs and dO
+// are held as one float4 per thread (row tid / 8, columns 4 (tid % 8) ..).
+template <int CP, int LP, bool kVec>
 __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     using F = FactorsT<CP, LP, LP + 4, true, false, true>;   // no Kt: the record's Kt is skipped
     constexpr int LS = F::LS, CS = F::CS, NT = F::NT, RPT = F::RPT, RG = F::RG;
@@ -1150,30 +1154,60 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
     typedef float svec __attribute__((ext_vector_type(SV)));
     static_assert(EPL % SV == 0 && kDS % SV == 0, "aligned vector stores");
     const int xl_lc = xl_l < a.L ? xl_l : int(a.L) - 1, D = int(a.D);
+    static_assert(!kVec || (CP * kDN == 4 * kThreads && EPT == 4 && EPL % 4 == 0), "vector tile layout");
+    const int v_row = tid / (kDN / 4), v_n = 4 * (tid % (kDN / 4));   // kVec: U, drhs, dO element of this thread
     auto load_tile = [&](int64_t head, int64_t c, int64_t d0) {
         // Block-uniform bases and 32-bit clamped offsets (see tile_base).
         const int lc = last_col(a, d0);
         const int64_t sbase = (head * nb + c) * LP * a.D + d0;
         const float* sb = a.bnd_in + sbase;
         const float* dsb = a.dbnd + sbase;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int n = xl_n0 + i;
-            const int off = xl_lc * D + (n < lc ? n : lc);
-            sv[i] = sb[off];
-            dsv[i] = dsb[off];
-        }
         const int64_t ubase = (head * nb + c) * CP * a.D + d0;
         const float* ub = a.ubuf + ubase;
         const float* rb = a.drhs + ubase;
+        if constexpr (kVec) {
+            // lc + 1 is a multiple of 4: a float4 is wholly inside or wholly past D (clamped to the last).
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int idx = tid + i * kThreads, n = idx % kDN;
-            const int off = (idx / kDN) * D + (n < lc ? n : lc);
-            uu[i] = ub[off];
-            rv[i] = rb[off];
+            for (int j = 0; j < EPL / 4; ++j) {
+                const int n = xl_n0 + 4 * j;
+                const int off = xl_lc * D + (n < lc ? n : lc - 3);
+                const f32x4 s4 = *reinterpret_cast<const f32x4*>(sb + off);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsb + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sv[4 * j + e] = s4[e];
+                    dsv[4 * j + e] = d4[e];
+                }
+            }
+            const int off = v_row * D + (v_n < lc ? v_n : lc - 3);
+            const int lr = last_row(a, c * CP, CP);
+            const int ooff = (v_row < lr ? v_row : lr) * D + (v_n < lc ? v_n : lc - 3);
+            const f32x4 u4 = *reinterpret_cast<const f32x4*>(ub + off);
+            const f32x4 r4 = *reinterpret_cast<const f32x4*>(rb + off);
+            const f32x4 o4 = *reinterpret_cast<const f32x4*>(a.dctx + tile_base(a, head, c * CP, d0) + ooff);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uu[e] = u4[e];
+                rv[e] = r4[e];
+                oo[e] = o4[e];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int n = xl_n0 + i;
+                const int off = xl_lc * D + (n < lc ? n : lc);
+                sv[i] = sb[off];
+                dsv[i] = dsb[off];
+            }
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const int idx = tid + i * kThreads, n = idx % kDN;
+                const int off = (idx / kDN) * D + (n < lc ? n : lc);
+                uu[i] = ub[off];
+                rv[i] = rb[off];
+            }
+            load_dense<CP, false>(a.dctx, nullptr, a, head, c * CP, d0, tid, oo, nullptr);
         }
-        load_dense<CP, false>(a.dctx, nullptr, a, head, c * CP, d0, tid, oo, nullptr);
     };
 
     // An item's other loads: its latent inputs k, b, g (raw, clamped copies
@@ -1292,13 +1326,27 @@ __global__ void __launch_bounds__(kThreads, 2) wy_bwd_grad_kernel(WyArgs a) {
                 *reinterpret_cast<svec*>(g.t.S + xl_l * kDS + xl_n0 + j * SV) = s4;
                 *reinterpret_cast<svec*>(g.t.D + xl_l * kDS + xl_n0 + j * SV) = d4;
             }
+            if constexpr (kVec) {
+                const bool okd = v_n < ncols, oko = okd && v_row < nrows;
+                f32x4 u4, r4, o4;
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
-                const bool okd = n < ncols;
-                g.t.U[row * kDS + n] = okd ? uu[i] : 0.f;
-                g.t.R[row * kDS + n] = okd ? rv[i] : 0.f;
-                g.t.O[row * kDS + n] = okd && row < nrows ? oo[i] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    u4[e] = okd ? uu[e] : 0.f;
+                    r4[e] = okd ? rv[e] : 0.f;
+                    o4[e] = oko ? oo[e] : 0.f;
+                }
+                *reinterpret_cast<f32x4*>(g.t.U + v_row * kDS + v_n) = u4;
+                *reinterpret_cast<f32x4*>(g.t.R + v_row * kDS + v_n) = r4;
+                *reinterpret_cast<f32x4*>(g.t.O + v_row * kDS + v_n) = o4;
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) {
+                    const int idx = tid + i * kThreads, row = idx / kDN, n = idx % kDN;
+                    const bool okd = n < ncols;
+                    g.t.U[row * kDS + n] = okd ? uu[i] : 0.f;
+                    g.t.R[row * kDS + n] = okd ? rv[i] : 0.f;
+                    g.t.O[row * kDS + n] = okd && row < nrows ? oo[i] : 0.f;
+                }
             }
             // The next dense tile, or the next item's first (unconditional: see the forward).
             const bool more = dt + 1 < a.n_dt;
@@ -1467,7 +1515,12 @@ hipError_t launch_bwd_t(const WyArgs& a, hipStream_t st) {
                                    dim3(kThreads), params, 0, st);
     if (e != hipSuccess) return e;
     if (!a.dq && !a.dk && !a.dv && !a.db && !a.dw && !a.dg) return hipSuccess;
-    const void* grad = reinterpret_cast<const void*>(&wy_bwd_grad_kernel<CP, LP>);
+    // 16-byte dense loads where every dense row and base allows them.
+    const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const bool vec = CP == 32 && LP >= 32 && a.D % 4 == 0 && al16(a.bnd_in) && al16(a.dbnd) && al16(a.ubuf) &&
+                     al16(a.drhs) && al16(a.dctx);
+    const void* grad = vec ? reinterpret_cast<const void*>(&wy_bwd_grad_kernel<CP, LP, (CP == 32 && LP >= 32)>)
+                           : reinterpret_cast<const void*>(&wy_bwd_grad_kernel<CP, LP, false>);
     int dev = 0, cus = 0, per_cu = 0;
     e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
