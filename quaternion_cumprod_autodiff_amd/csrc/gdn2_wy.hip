@@ -703,7 +703,11 @@ struct alignas(16) StripT {                // one wave's transposes: S^T [16][LP
     float st[16 * (LP + 4)], rt[16 * (CP + 4)], ut[16 * (CP + 4)];
 };
 
-template <int CP, int LP>
+// kVec: w and v rows 16-byte aligned (D a multiple of 4, both bases
+// aligned): they are loaded as 16-byte row pieces (lane: rows vr + 16 k,
+// columns vn .. vn + 3 of its strip), a quarter of the load instructions,
+// and w.v reaches the accumulator layout through the rhs^T area.
+template <int CP, int LP, bool kVec>
 __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
     using F = StagedFactors<CP, LP>;
     using R = Rec<CP, LP>;
@@ -735,20 +739,38 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
     // w and v of chunk c at this lane's accumulator elements (raw, clamped;
     // masked where used).
     float wv[NT][4], vv[NT][4];
+    const int vr = lane >> 2, vn = 4 * (lane & 3);
+    const bool vcol = d0 + vn < a.D;
+    const int vcc = int(vcol ? d0 + vn : a.D - 4);   // kVec: clamped first column (D >= 4)
     auto load_wv = [&](int64_t c) {
         const int64_t t0 = c * CP;
         const int lr = last_row(a, t0, CP);
         const float* wb = a.w + (head * a.T + t0) * a.D;
         const float* vb = a.v + (head * a.T + t0) * a.D;
+        if constexpr (kVec) {
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti)
+            for (int k = 0; k < NT; ++k) {
+                const int row = vr + 16 * k;
+                const int off = (row < lr ? row : lr) * D + vcc;
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wb + off);
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(vb + off);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * ti + g4 + r;
-                const int off = (row < lr ? row : lr) * D + cc;
-                wv[ti][r] = wb[off];
-                vv[ti][r] = vb[off];
+                for (int e = 0; e < 4; ++e) {
+                    wv[k][e] = w4[e];
+                    vv[k][e] = v4[e];
+                }
             }
+        } else {
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ti + g4 + r;
+                    const int off = (row < lr ? row : lr) * D + cc;
+                    wv[ti][r] = wb[off];
+                    vv[ti][r] = vb[off];
+                }
+        }
     };
     auto write_t = [&](float* dstT, int stride, int row0, const f32x4& v) {   // rows row0 + g4 + r, column col
         *reinterpret_cast<f32x4*>(dstT + col * stride + row0 + g4) = v;
@@ -794,13 +816,28 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
         // x = w.v of this chunk (zero on padded steps), as the negated
         // initial value of M S - x.
         f32x4 nr[NT];
+        if constexpr (kVec) {
+            // Rows of -x into the rhs^T area (free: its last readers were in the
+            // chunk before), read back in the accumulator layout.
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti)
+            for (int k = 0; k < NT; ++k) {
+                const int row = vr + 16 * k;
+                const bool ok = t0 + row < a.T && vcol;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool ok = t0 + 16 * ti + g4 + r < a.T && col_ok;
-                nr[ti][r] = ok ? -(wv[ti][r] * vv[ti][r]) : 0.f;
+                for (int e = 0; e < 4; ++e) myRT[(vn + e) * SCT + row] = ok ? -(wv[k][e] * vv[k][e]) : 0.f;
             }
+            wave_sync();
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) nr[ti] = *reinterpret_cast<const f32x4*>(myRT + col * SCT + 16 * ti + g4);
+        } else {
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool ok = t0 + 16 * ti + g4 + r < a.T && col_ok;
+                    nr[ti][r] = ok ? -(wv[ti][r] * vv[ti][r]) : 0.f;
+                }
+        }
         // The next chunk's record into the other copy (its last readers were
         // behind the previous chunk's barrier), then the loads for later
         // chunks (unconditional, clamped: see the other kernels).
@@ -1502,8 +1539,10 @@ hipError_t launch_fwd_t(const WyArgs& a, hipStream_t st) {
                                    dim3(unsigned(a.BH * a.n_chunks)), dim3(kThreads), params, 0, st);
     if (e != hipSuccess) return e;
     const unsigned strips = unsigned((a.BH + 7) / 8 * 8 * ((a.D + kStripBlock - 1) / kStripBlock));
-    return hipLaunchKernel(reinterpret_cast<const void*>(&wy_fwd_strip_kernel<CP, LP>), dim3(strips),
-                           dim3(kThreads), params, 0, st);
+    const bool vec = a.D % 4 == 0 && ((reinterpret_cast<uintptr_t>(a.w) | reinterpret_cast<uintptr_t>(a.v)) & 15) == 0;
+    return hipLaunchKernel(vec ? reinterpret_cast<const void*>(&wy_fwd_strip_kernel<CP, LP, true>)
+                               : reinterpret_cast<const void*>(&wy_fwd_strip_kernel<CP, LP, false>),
+                           dim3(strips), dim3(kThreads), params, 0, st);
 }
 
 template <int CP, int LP>
