@@ -687,6 +687,12 @@ struct OutRegion {
     __device__ void store(float v, bool ok, int idx) const {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, ok ? idx * 4 : kDrop, 0, 0);
     }
+    // Four floats from idx (a multiple of 4 in a 16-byte aligned region).
+    __device__ void store4(const f32x4& v, bool ok, int idx) const {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 x = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(x, r, ok ? idx * 4 : kDrop & ~15, 0, 0);
+    }
 };
 
 constexpr int kStrip = 16;                 // dense columns per wave
@@ -951,7 +957,11 @@ struct alignas(16) CarryStripT {          // one wave's transposes: dS^T [16][LP
     float st[16 * (LP + 4)], ot[16 * (CP + 4)], ut[16 * (CP + 4)], rt[16 * (CP + 4)];
 };
 
-template <int CP, int LP>
+// kVec: dense rows 16-byte aligned (D a multiple of 4; dO, w, v, dw, dv and
+// drhs aligned): dO, w and v are loaded, and drhs, dw and dv stored, as
+// 16-byte row pieces (lane: rows vr + 16 k, columns vn .. vn + 3 of its
+// strip), dO reaching its transpose and drhs its rows through LDS.
+template <int CP, int LP, bool kVec>
 __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs a) {
     using F = StagedFactors<CP, LP>;
     using R = Rec<CP, LP>;
@@ -982,22 +992,43 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
         *reinterpret_cast<f32x4*>(dstT + col * stride + row0 + g4) = v;
     };
 
-    // dO, w and v of chunk c at this lane's accumulator elements (raw, clamped).
+    // dO, w and v of chunk c at this lane's accumulator elements, or (kVec)
+    // row pieces (raw, clamped).
     float ov[NT][4], wv[NT][4], vv[NT][4];
+    const int vr = lane >> 2, vn = 4 * (lane & 3);
+    const bool vcol = d0 + vn < a.D;
+    const int vcc = int(vcol ? d0 + vn : a.D - 4);   // kVec: clamped first column (D >= 4)
     auto load_dense3 = [&](int64_t c) {
         const int64_t t0 = c * CP;
         const int lr = last_row(a, t0, CP);
         const int64_t base = (head * a.T + t0) * a.D;
+        if constexpr (kVec) {
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti)
+            for (int k = 0; k < NT; ++k) {
+                const int row = vr + 16 * k;
+                const int off = (row < lr ? row : lr) * D + vcc;
+                const f32x4 o4 = *reinterpret_cast<const f32x4*>(a.dctx + base + off);
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(a.w + base + off);
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(a.v + base + off);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * ti + g4 + r;
-                const int off = (row < lr ? row : lr) * D + cc;
-                ov[ti][r] = a.dctx[base + off];
-                wv[ti][r] = a.w[base + off];
-                vv[ti][r] = a.v[base + off];
+                for (int e = 0; e < 4; ++e) {
+                    ov[k][e] = o4[e];
+                    wv[k][e] = w4[e];
+                    vv[k][e] = v4[e];
+                }
             }
+        } else {
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ti + g4 + r;
+                    const int off = (row < lr ? row : lr) * D + cc;
+                    ov[ti][r] = a.dctx[base + off];
+                    wv[ti][r] = a.w[base + off];
+                    vv[ti][r] = a.v[base + off];
+                }
+        }
     };
 
     // The cotangent of the final state (zero if none), in accumulator layout,
@@ -1048,15 +1079,26 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
         float wc[NT][4], vc[NT][4];
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
-            f32x4 o4;
+            if constexpr (kVec) {
+                const int row = vr + 16 * ti;
+                const bool ok = row < rows && vcol;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool ok = 16 * ti + g4 + r < rows && col_ok;
-                o4[r] = ok ? ov[ti][r] : 0.f;
-                wc[ti][r] = wv[ti][r];
-                vc[ti][r] = vv[ti][r];
+                for (int e = 0; e < 4; ++e) {
+                    myOT[(vn + e) * SCT + row] = ok ? ov[ti][e] : 0.f;
+                    wc[ti][e] = wv[ti][e];
+                    vc[ti][e] = vv[ti][e];
+                }
+            } else {
+                f32x4 o4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool ok = 16 * ti + g4 + r < rows && col_ok;
+                    o4[r] = ok ? ov[ti][r] : 0.f;
+                    wc[ti][r] = wv[ti][r];
+                    vc[ti][r] = vv[ti][r];
+                }
+                write_t(myOT, SCT, 16 * ti, o4);
             }
-            write_t(myOT, SCT, 16 * ti, o4);
         }
         // The previous chunk's record into the other copy, then the loads for
         // earlier chunks (unconditional, clamped).
@@ -1097,17 +1139,35 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
         const OutRegion dvb(a.dv ? a.dv + gbase : nullptr, rows * a.D);
 #pragma unroll
         for (int ti = 0; ti < NT; ++ti) {
+            if constexpr (!kVec) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * ti + g4 + r;
-                const int off = row * D + int(d0) + col;
-                rb.store(dr[ti][r], col_ok, off);   // for the gradient kernel
-                dwb.store(dr[ti][r] * vc[ti][r], col_ok && row < rows, off);
-                dvb.store(dr[ti][r] * wc[ti][r], col_ok && row < rows, off);
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ti + g4 + r;
+                    const int off = row * D + int(d0) + col;
+                    rb.store(dr[ti][r], col_ok, off);   // for the gradient kernel
+                    dwb.store(dr[ti][r] * vc[ti][r], col_ok && row < rows, off);
+                    dvb.store(dr[ti][r] * wc[ti][r], col_ok && row < rows, off);
+                }
             }
             write_t(myRT, SCT, 16 * ti, dr[ti]);
         }
         wave_sync();
+        if constexpr (kVec) {   // rows of drhs from its transpose; drhs, dw, dv as 16-byte pieces
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                const int row = vr + 16 * k, off = row * D + vcc;
+                f32x4 d4, w4, v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    d4[e] = myRT[(vn + e) * SCT + row];
+                    w4[e] = d4[e] * vc[k][e];
+                    v4[e] = d4[e] * wc[k][e];
+                }
+                rb.store4(d4, vcol, off);   // for the gradient kernel
+                dwb.store4(w4, vcol && row < rows, off);
+                dvb.store4(v4, vcol && row < rows, off);
+            }
+        }
         // dS0 = Qc^T dO / sqrt(L) + diag(c_last) dS - M^T drhs.
 #pragma unroll
         for (int tl = 0; tl < NL; ++tl) {
@@ -1550,8 +1610,13 @@ hipError_t launch_bwd_t(const WyArgs& a, hipStream_t st) {
     WyArgs args = a;
     void* params[] = {&args};
     const unsigned strips = unsigned((a.BH + 7) / 8 * 8 * ((a.D + kStripBlock - 1) / kStripBlock));
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wy_bwd_carry_strip_kernel<CP, LP>), dim3(strips),
-                                   dim3(kThreads), params, 0, st);
+    const uintptr_t dense = reinterpret_cast<uintptr_t>(a.dctx) | reinterpret_cast<uintptr_t>(a.w) |
+                            reinterpret_cast<uintptr_t>(a.v) | reinterpret_cast<uintptr_t>(a.dw) |
+                            reinterpret_cast<uintptr_t>(a.dv) | reinterpret_cast<uintptr_t>(a.drhs);
+    const bool cvec = a.D % 4 == 0 && (dense & 15) == 0;
+    hipError_t e = hipLaunchKernel(cvec ? reinterpret_cast<const void*>(&wy_bwd_carry_strip_kernel<CP, LP, true>)
+                                        : reinterpret_cast<const void*>(&wy_bwd_carry_strip_kernel<CP, LP, false>),
+                                   dim3(strips), dim3(kThreads), params, 0, st);
     if (e != hipSuccess) return e;
     if (!a.dq && !a.dk && !a.dv && !a.db && !a.dw && !a.dg) return hipSuccess;
     // 16-byte dense loads where every dense row and base allows them.
