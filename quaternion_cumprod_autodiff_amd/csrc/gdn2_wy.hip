@@ -709,10 +709,12 @@ struct alignas(16) StripT {                // one wave's transposes: S^T [16][LP
     float st[16 * (LP + 4)], rt[16 * (CP + 4)], ut[16 * (CP + 4)];
 };
 
-// kVec: w and v rows 16-byte aligned (D a multiple of 4, both bases
-// aligned): they are loaded as 16-byte row pieces (lane: rows vr + 16 k,
-// columns vn .. vn + 3 of its strip), a quarter of the load instructions,
-// and w.v reaches the accumulator layout through the rhs^T area.
+// kVec: dense rows 16-byte aligned (D a multiple of 4; w, v, the context,
+// the final state and the saved state aligned): w and v are loaded, and U,
+// the context and the state stored, as 16-byte row pieces (lane: rows
+// vr + 16 k, columns vn .. vn + 3 of its strip), a quarter of the memory
+// instructions; w.v reaches the accumulator layout, and the outputs their
+// rows, through the strip's transposes.
 template <int CP, int LP, bool kVec>
 __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
     using F = StagedFactors<CP, LP>;
@@ -894,11 +896,20 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 u[ti][r] = -u[ti][r];
-                ub.store(u[ti][r], col_ok, (16 * ti + g4 + r) * D + int(d0) + col);
+                if constexpr (!kVec) ub.store(u[ti][r], col_ok, (16 * ti + g4 + r) * D + int(d0) + col);
             }
             write_t(myUT, SCT, 16 * ti, u[ti]);
         }
         wave_sync();
+        // (kVec: outputs leave as 16-byte row pieces read back from the transposes.)
+        auto row4 = [&](const float* srcT, int stride, int row) {
+            return f32x4{srcT[vn * stride + row], srcT[(vn + 1) * stride + row], srcT[(vn + 2) * stride + row],
+                         srcT[(vn + 3) * stride + row]};
+        };
+        if constexpr (kVec) {
+#pragma unroll
+            for (int k = 0; k < NT; ++k) ub.store4(row4(myUT, SCT, vr + 16 * k), vcol, (vr + 16 * k) * D + vcc);
+        }
         // O = (Qc S + Bq U) / sqrt(L); Bq is lower triangular.
         {
             const float* aa[NT];
@@ -906,6 +917,12 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
             for (int ti = 0; ti < NT; ++ti) aa[ti] = fc.Bq + 16 * ti * CS;
             mma_kc_n<NT, 16, CS, SCT>(o, aa, myUT, lane);
             if constexpr (NT == 2) mma_kc<16, CS, SCT>(o[1], fc.Bq + 16 * CS + 16, myUT + 16, lane);
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[ti][r] *= a.scale;
+                if constexpr (kVec) write_t(myRT, SCT, 16 * ti, o[ti]);   // rhs^T is dead: O^T takes its place
+            }
         }
         // S_end = diag(c_last) S + Kt^T U.
         {
@@ -920,13 +937,15 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
         }
         const int rows = a.T - t0 < CP ? int(a.T - t0) : CP;
         const OutRegion ob(a.ctx + (head * a.T + t0) * a.D, rows * a.D);
+        if constexpr (!kVec) {
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti)
+            for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * ti + g4 + r;
-                ob.store(o[ti][r] * a.scale, row < rows && col_ok, row * D + int(d0) + col);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ti + g4 + r;
+                    ob.store(o[ti][r], row < rows && col_ok, row * D + int(d0) + col);
+                }
+        }
         // The state goes to the next chunk's boundary slot, or (last chunk)
         // to the final state.
         const OutRegion sb = c + 1 < nb
@@ -934,12 +953,27 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
             : OutRegion(a.state ? a.state + head * a.L * a.D : nullptr, a.L * a.D);
 #pragma unroll
         for (int tl = 0; tl < NL; ++tl) {
+            if constexpr (!kVec) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int l = 16 * tl + g4 + r;
-                sb.store(sc[tl][r], l < a.L && col_ok, l * D + int(d0) + col);
+                for (int r = 0; r < 4; ++r) {
+                    const int l = 16 * tl + g4 + r;
+                    sb.store(sc[tl][r], l < a.L && col_ok, l * D + int(d0) + col);
+                }
             }
             write_t(myST, SST, 16 * tl, sc[tl]);
+        }
+        if constexpr (kVec) {
+            wave_sync();
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                const int row = vr + 16 * k;
+                ob.store4(row4(myRT, SCT, row), vcol && row < rows, row * D + vcc);
+            }
+#pragma unroll
+            for (int k = 0; k < NL; ++k) {
+                const int l = vr + 16 * k;
+                sb.store4(row4(myST, SST, l), vcol && l < a.L, l * D + vcc);
+            }
         }
         __syncthreads();   // the next record is staged, this one is free for the one after, S^T is written
     }
@@ -1599,7 +1633,10 @@ hipError_t launch_fwd_t(const WyArgs& a, hipStream_t st) {
                                    dim3(unsigned(a.BH * a.n_chunks)), dim3(kThreads), params, 0, st);
     if (e != hipSuccess) return e;
     const unsigned strips = unsigned((a.BH + 7) / 8 * 8 * ((a.D + kStripBlock - 1) / kStripBlock));
-    const bool vec = a.D % 4 == 0 && ((reinterpret_cast<uintptr_t>(a.w) | reinterpret_cast<uintptr_t>(a.v)) & 15) == 0;
+    const uintptr_t dense = reinterpret_cast<uintptr_t>(a.w) | reinterpret_cast<uintptr_t>(a.v) |
+                            reinterpret_cast<uintptr_t>(a.ctx) | reinterpret_cast<uintptr_t>(a.state) |
+                            reinterpret_cast<uintptr_t>(a.bnd) | reinterpret_cast<uintptr_t>(a.ubuf);
+    const bool vec = a.D % 4 == 0 && (dense & 15) == 0;
     return hipLaunchKernel(vec ? reinterpret_cast<const void*>(&wy_fwd_strip_kernel<CP, LP, true>)
                                : reinterpret_cast<const void*>(&wy_fwd_strip_kernel<CP, LP, false>),
                            dim3(strips), dim3(kThreads), params, 0, st);
