@@ -239,6 +239,38 @@ def test_chunk_wy_outputs_only_4_byte_aligned(chunk):
     assert torch.equal(c1.flatten(), cbuf[1:]) and torch.equal(s1.flatten(), sbuf[1:])
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_chunk_wy_backward_dense_only_4_byte_aligned(chunk):
+    """The VJP through the C ABI with d_context and every cotangent one float
+    past 16-byte alignment, D and L multiples of 4 (where aligned tensors take
+    16-byte loads and stores): bit-equal to aligned tensors."""
+    B, H, T, L, D = 1, 3, 70, 40, 96
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=32)
+    ins = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
+    d_ctx = torch.randn((B, H, T, D), device=DEV, generator=torch.Generator(device=DEV).manual_seed(8))
+    _, _, bnd = capi.gdn2_fwd(*ins, chunk=chunk)
+    ref = capi.gdn2_bwd(*ins[:6], bnd, d_ctx, chunk=chunk)
+
+    def shifted(n):   # a view one float into a fresh buffer
+        buf = torch.empty(n + 1, dtype=torch.float32, device=DEV)
+        assert (buf.data_ptr() + 4) % 16 != 0
+        return buf[1:]
+
+    dc = shifted(d_ctx.numel())
+    dc.copy_(d_ctx.flatten())
+    outs = [shifted(x.numel()) for x in ref]
+    lib = capi.load()
+    nscr = int(lib.gdn2_scratch_bytes(B, H, T, L, D, chunk))
+    scratch = torch.empty(nscr // 4, dtype=torch.float32, device=DEV)
+    rc = lib.gdn2_bwd(*[x.data_ptr() for x in ins[:6]], bnd.data_ptr(), dc.data_ptr(), None,
+                      *[o.data_ptr() for o in outs], scratch.data_ptr(), nscr, B, H, T, L, D, chunk,
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    for n, r, o in zip(NAMES, ref, outs):
+        assert torch.equal(r.flatten(), o), n
+
+
 @pytest.mark.parametrize("geom", [(1, 2, 60, 32, 100, 8), (1, 1, 37, 64, 65, 5), (2, 1, 21, 16, 70, 4)],
                          ids=lambda g: "b%dh%dt%dl%dd%dc%d" % g)
 def test_backward_ignores_scratch_contents(geom):
