@@ -37,7 +37,7 @@
 //                       through two LDS copies; each wave carries its strip
 //                       of the state alone; saves the state at every chunk
 //                       start and U.
-//   wy_fwd_kernel       without a boundary buffer (no backward to follow):
+//   wy_fwd_fused_kernel without a boundary buffer (no backward to follow):
 //                       one block per (head, 32 dense columns), building
 //                       each chunk's factors itself.
 //   wy_bwd_carry_strip_kernel  as the forward strip kernel, the chunks in
@@ -447,16 +447,6 @@ __device__ __forceinline__ void load_rec(RecRegs<CP, LP>& r, const float* rec, i
     }
 }
 
-template <int CP, int LP, class F>
-__device__ __forceinline__ void stage_rec(F& f, const RecRegs<CP, LP>& r, int tid) {
-    using R = Rec<CP, LP>;
-#pragma unroll
-    for (int i = 0; i < R::kPer; ++i) {
-        const int j = tid + i * kThreads;
-        if (j < R::kN4) *reinterpret_cast<f32x4*>(rec_lds<CP, LP>(f, 4 * j)) = r.v[i];
-    }
-}
-
 // Where this thread's float4 of a record land in staged factors F: offsets
 // in floats from the start of F (-1: none), formed once per kernel, so that
 // staging a record is a run of 16-byte LDS stores.
@@ -514,161 +504,6 @@ __device__ __forceinline__ bool seq_block(const WyArgs& a, int64_t* head, int64_
 
 // --------------------------------------------------------------- forward
 
-// kRec: stream the chunks' records (written by wy_factor_kernel); else build
-// each chunk's factors here (no boundary buffer, so nowhere to keep them).
-template <int CP, int LP, bool kRec>
-__global__ void __launch_bounds__(kThreads, 2) wy_fwd_kernel(WyArgs a) {
-    using F = std::conditional_t<kRec, StagedFactors<CP, LP>, BuildFactors<CP, LP>>;
-    using R = Rec<CP, LP>;
-    constexpr int kDS = kSeqDS;   // dense tiles here are read only as row-major B operands
-    constexpr int LS = F::LS, CS = F::CS, NT = F::NT, RPT = F::RPT;
-    constexpr int NS = (LP / 16) * (kDN / 16);        // state tiles
-    constexpr int NSW = (NS + 3) / 4;                   // state tiles per wave
-    __shared__ F f;
-    __shared__ float sX[CP * kDS], sU[CP * kDS], sS[LP * kDS];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int64_t head, d0;
-    if (!seq_block(a, &head, &d0)) return;
-    const int64_t nb = a.n_chunks;
-
-    for (int idx = tid; idx < LP * kDN; idx += kThreads) {
-        const int l = idx / kDN, n = idx % kDN;
-        float v = 0.f;
-        if (l < a.L && d0 + n < a.D) {
-            v = a.s0[(head * a.L + l) * a.D + d0 + n];
-            if (a.bnd) a.bnd[((head * nb) * LP + l) * a.D + d0 + n] = v;
-        }
-        sS[l * kDS + n] = v;
-    }
-
-    // The next chunk's inputs are loaded into registers while this chunk
-    // computes (barriers wait for LDS traffic only, not for these loads).
-    constexpr int EPT = CP * kDN / kThreads;
-    LatIn<kRec ? 1 : RPT> in;
-    RecRegs<CP, LP> rr;
-    float vv[EPT], ww[EPT];
-    if constexpr (kRec)
-        load_rec<CP, LP>(rr, a.rec + head * nb * R::kSize, tid);
-    else
-        load_latent<CP, LP>(a, head, 0, tid, in);
-    load_dense<CP, true>(a.v, a.w, a, head, 0, d0, tid, vv, ww);
-    for (int64_t c = 0; c < nb; ++c) {
-        const int64_t t0 = c * CP;
-        // sX (this chunk's w.v) and the factors are free: their last readers
-        // are behind the previous chunk's final barrier.
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int idx = tid + i * kThreads;
-            sX[(idx / kDN) * kDS + idx % kDN] = dense_ok(a, t0, d0, tid, i) ? ww[i] * vv[i] : 0.f;
-        }
-        // Prefetches are unconditional: the last chunk reloads its own record
-        // (and dense loads past T are clamped and masked); a branch around
-        // them would make the compiler wait for them where it rejoins.
-        const int64_t cn = c + 1 < nb ? c + 1 : c;
-        if constexpr (kRec) {
-            stage_rec<CP, LP>(f, rr, tid);
-            __syncthreads();
-            load_rec<CP, LP>(rr, a.rec + (head * nb + cn) * R::kSize, tid);
-        } else {
-            float e[RPT], ie[RPT];
-            make_factors<CP, LP>(f, in, a, t0, tid, e, ie);   // its barriers also order the stores above
-            load_latent<CP, LP>(a, head, cn * CP, tid, in);
-        }
-        load_dense<CP, true>(a.v, a.w, a, head, cn * CP, d0, tid, vv, ww);
-
-        // rhs = w.v - M S0 (in place in sX); in the fused variant wave 0 may
-        // still be finishing T.
-        for (int job = wave; job < NT * 2; job += 4) {
-            const int ti = job >> 1, tj = job & 1;
-            f32x4 acc = zero4();
-            mma<LP, LS, 1, kDS, 1>(acc, f.M + ti * 16 * LS, sS + tj * 16, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float* p = sX + (ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane);
-                *p = *p - acc[r];
-            }
-        }
-        __syncthreads();
-        // U = T rhs (T lower triangular).
-        const int lr = last_row(a, t0, CP), lc = last_col(a, d0), D = int(a.D);
-        float* ub = kRec ? a.ubuf + (head * nb * CP + t0) * a.D + d0 : nullptr;
-        for (int job = wave; job < NT * 2; job += 4) {
-            const int ti = job >> 1, tj = job & 1;
-            f32x4 acc = zero4();
-            mma16<CP, CS, 1, kDS, 1>(acc, f.Tm + ti * 16 * CS, sX + tj * 16, ti + 1, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
-                sU[row * kDS + col] = acc[r];
-                // U is kept for the backward (rows of the padded chunk, columns < D).
-                if (kRec && col <= lc) ub[row * D + col] = acc[r];
-            }
-        }
-        __syncthreads();
-        // O = (Qc S0 + Bq U) / sqrt(L).
-        float* ob = a.ctx + tile_base(a, head, t0, d0);
-        for (int job = wave; job < NT * 2; job += 4) {
-            const int ti = job >> 1, tj = job & 1;
-            f32x4 acc = zero4();
-            mma<LP, LS, 1, kDS, 1>(acc, f.Qc + ti * 16 * LS, sS + tj * 16, lane);
-            mma16<CP, CS, 1, kDS, 1>(acc, f.Bq + ti * 16 * CS, sU + tj * 16, ti + 1, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
-                if (row <= lr && col <= lc) ob[row * D + col] = acc[r] * a.scale;
-            }
-        }
-        // S_end = diag(c_last) S0 + Kt^T U.
-        f32x4 snew[NSW];
-#pragma unroll
-        for (int s = 0; s < NSW; ++s) {
-            const int job = wave + 4 * s;
-            if (job < NS) {
-                const int ti = job >> 1, tj = job & 1;
-                f32x4 acc;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int l = ti * 16 + acc_row(lane, r);
-                    acc[r] = f.clast[l] * sS[l * kDS + tj * 16 + acc_col(lane)];
-                }
-                mma<CP, 1, LS, kDS, 1>(acc, f.Kt + ti * 16, sU + tj * 16, lane);
-                snew[s] = acc;
-            }
-        }
-        __syncthreads();
-        // The state goes to the next chunk's boundary slot, or (last chunk)
-        // to the final state.
-        float* sb = c + 1 < nb ? (a.bnd ? a.bnd + (head * nb + c + 1) * LP * a.D + d0 : nullptr)
-                               : (a.state ? a.state + head * a.L * a.D + d0 : nullptr);
-#pragma unroll
-        for (int s = 0; s < NSW; ++s) {
-            const int job = wave + 4 * s;
-            if (job < NS) {
-                const int ti = job >> 1, tj = job & 1;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int l = ti * 16 + acc_row(lane, r), n = tj * 16 + acc_col(lane);
-                    sS[l * kDS + n] = snew[s][r];
-                    if (sb && l < a.L && n <= lc) sb[l * D + n] = snew[s][r];
-                }
-            }
-        }
-    }
-}
-
-// The forward over saved records, one wave per 16-column strip of the dense
-// axis: a block of 4 waves takes 64 dense columns of one head, and each wave
-// carries its strip's state S[:, strip] through the chunks alone.  Within a
-// chunk no wave needs another's results: rhs = w.v - M S, U = T rhs, O and
-// S_end of a strip use only that strip's columns.  The chunk's record is the
-// only shared operand; two LDS copies alternate, the next chunk's staged
-// while this one computes, so a chunk costs one barrier.  The strip's S^T,
-// rhs^T and U^T pass through the wave's own LDS area, from the accumulator
-// layout into the K-contiguous operand layout.  LDS operations of one wave
-// complete in order, so wave_sync (wavefront-scope fences around a wave
-// barrier: no instructions, only no compiler reordering) is all the ordering
-// that the exchange needs.
 // Stores without branches.  Loads and stores share one counter on gfx950,
 // and where a store sits under a branch (a lane mask, an optional output) the
 // compiler assumes, when it later waits for a load issued before the store,
@@ -695,6 +530,141 @@ struct OutRegion {
     }
 };
 
+
+// The forward without a boundary buffer (no backward to follow, so nowhere
+// to keep records): each chunk's factors are built here, one block per
+// (head, 32 dense columns), the chunks in order.
+template <int CP, int LP>
+__global__ void __launch_bounds__(kThreads, 2) wy_fwd_fused_kernel(WyArgs a) {
+    using F = BuildFactors<CP, LP>;
+    constexpr int kDS = kSeqDS;   // dense tiles here are read only as row-major B operands
+    constexpr int LS = F::LS, CS = F::CS, NT = F::NT, RPT = F::RPT;
+    constexpr int NS = (LP / 16) * (kDN / 16);        // state tiles
+    constexpr int NSW = (NS + 3) / 4;                   // state tiles per wave
+    __shared__ F f;
+    __shared__ float sX[CP * kDS], sU[CP * kDS], sS[LP * kDS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int64_t head, d0;
+    if (!seq_block(a, &head, &d0)) return;
+    const int64_t nb = a.n_chunks;
+
+    for (int idx = tid; idx < LP * kDN; idx += kThreads) {
+        const int l = idx / kDN, n = idx % kDN;
+        sS[l * kDS + n] = l < a.L && d0 + n < a.D ? a.s0[(head * a.L + l) * a.D + d0 + n] : 0.f;
+    }
+
+    // The next chunk's inputs are loaded into registers while this chunk
+    // computes (barriers wait for LDS traffic only, not for these loads).
+    constexpr int EPT = CP * kDN / kThreads;
+    LatIn<RPT> in;
+    float vv[EPT], ww[EPT];
+    load_latent<CP, LP>(a, head, 0, tid, in);
+    load_dense<CP, true>(a.v, a.w, a, head, 0, d0, tid, vv, ww);
+    for (int64_t c = 0; c < nb; ++c) {
+        const int64_t t0 = c * CP;
+        // sX (this chunk's w.v) and the factors are free: their last readers
+        // are behind the previous chunk's final barrier.
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int idx = tid + i * kThreads;
+            sX[(idx / kDN) * kDS + idx % kDN] = dense_ok(a, t0, d0, tid, i) ? ww[i] * vv[i] : 0.f;
+        }
+        // Prefetches are unconditional: the last chunk reloads its own inputs
+        // (dense loads past T are clamped and masked); a branch around them
+        // would make the compiler wait for them where it rejoins.
+        const int64_t cn = c + 1 < nb ? c + 1 : c;
+        {
+            float e[RPT], ie[RPT];
+            make_factors<CP, LP>(f, in, a, t0, tid, e, ie);   // its barriers also order the stores above
+        }
+        load_latent<CP, LP>(a, head, cn * CP, tid, in);
+        load_dense<CP, true>(a.v, a.w, a, head, cn * CP, d0, tid, vv, ww);
+
+        // rhs = w.v - M S0 (in place in sX); wave 0 may still be finishing T.
+        for (int job = wave; job < NT * 2; job += 4) {
+            const int ti = job >> 1, tj = job & 1;
+            f32x4 acc = zero4();
+            mma<LP, LS, 1, kDS, 1>(acc, f.M + ti * 16 * LS, sS + tj * 16, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float* p = sX + (ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane);
+                *p = *p - acc[r];
+            }
+        }
+        __syncthreads();
+        // U = T rhs (T lower triangular).
+        const int lr = last_row(a, t0, CP), lc = last_col(a, d0), D = int(a.D);
+        for (int job = wave; job < NT * 2; job += 4) {
+            const int ti = job >> 1, tj = job & 1;
+            f32x4 acc = zero4();
+            mma16<CP, CS, 1, kDS, 1>(acc, f.Tm + ti * 16 * CS, sX + tj * 16, ti + 1, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sU[(ti * 16 + acc_row(lane, r)) * kDS + tj * 16 + acc_col(lane)] = acc[r];
+        }
+        __syncthreads();
+        // O = (Qc S0 + Bq U) / sqrt(L).
+        const OutRegion ob(a.ctx + tile_base(a, head, t0, 0), (lr + 1) * a.D);
+        for (int job = wave; job < NT * 2; job += 4) {
+            const int ti = job >> 1, tj = job & 1;
+            f32x4 acc = zero4();
+            mma<LP, LS, 1, kDS, 1>(acc, f.Qc + ti * 16 * LS, sS + tj * 16, lane);
+            mma16<CP, CS, 1, kDS, 1>(acc, f.Bq + ti * 16 * CS, sU + tj * 16, ti + 1, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = ti * 16 + acc_row(lane, r), col = tj * 16 + acc_col(lane);
+                ob.store(acc[r] * a.scale, row <= lr && col <= lc, row * D + int(d0) + col);
+            }
+        }
+        // S_end = diag(c_last) S0 + Kt^T U.
+        f32x4 snew[NSW];
+#pragma unroll
+        for (int s = 0; s < NSW; ++s) {
+            const int job = wave + 4 * s;
+            if (job < NS) {
+                const int ti = job >> 1, tj = job & 1;
+                f32x4 acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int l = ti * 16 + acc_row(lane, r);
+                    acc[r] = f.clast[l] * sS[l * kDS + tj * 16 + acc_col(lane)];
+                }
+                mma<CP, 1, LS, kDS, 1>(acc, f.Kt + ti * 16, sU + tj * 16, lane);
+                snew[s] = acc;
+            }
+        }
+        __syncthreads();
+        // The state goes to the next chunk, and (last chunk) to the final state.
+        const OutRegion sb(c + 1 == nb && a.state ? a.state + head * a.L * a.D : nullptr, a.L * a.D);
+#pragma unroll
+        for (int s = 0; s < NSW; ++s) {
+            const int job = wave + 4 * s;
+            if (job < NS) {
+                const int ti = job >> 1, tj = job & 1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int l = ti * 16 + acc_row(lane, r), n = tj * 16 + acc_col(lane);
+                    sS[l * kDS + n] = snew[s][r];
+                    sb.store(snew[s][r], l < a.L && n <= lc, l * D + int(d0) + n);
+                }
+            }
+        }
+    }
+}
+
+// The forward over saved records, one wave per 16-column strip of the dense
+// axis: a block of 4 waves takes 64 dense columns of one head, and each wave
+// carries its strip's state S[:, strip] through the chunks alone.  Within a
+// chunk no wave needs another's results: rhs = w.v - M S, U = T rhs, O and
+// S_end of a strip use only that strip's columns.  The chunk's record is the
+// only shared operand; two LDS copies alternate, the next chunk's staged
+// while this one computes, so a chunk costs one barrier.  The strip's S^T,
+// rhs^T and U^T pass through the wave's own LDS area, from the accumulator
+// layout into the K-contiguous operand layout.  LDS operations of one wave
+// complete in order, so wave_sync (wavefront-scope fences around a wave
+// barrier: no instructions, only no compiler reordering) is all the ordering
+// that the exchange needs.
 constexpr int kStrip = 16;                 // dense columns per wave
 constexpr int kStripBlock = 4 * kStrip;    // dense columns per block
 
@@ -1627,7 +1597,7 @@ hipError_t launch_fwd_t(const WyArgs& a, hipStream_t st) {
     WyArgs args = a;
     void* params[] = {&args};
     if (a.rec == nullptr)
-        return hipLaunchKernel(reinterpret_cast<const void*>(&wy_fwd_kernel<CP, LP, false>), dim3(seq_blocks(a)),
+        return hipLaunchKernel(reinterpret_cast<const void*>(&wy_fwd_fused_kernel<CP, LP>), dim3(seq_blocks(a)),
                                dim3(kThreads), params, 0, st);
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wy_factor_kernel<CP, LP>),
                                    dim3(unsigned(a.BH * a.n_chunks)), dim3(kThreads), params, 0, st);
