@@ -25,18 +25,20 @@
 // The products with c and 1/c stay in range while a chunk's cumulative decay
 // stays above about 1e-37 per latent row.
 //
-// Kernels (256 threads = 4 waves; chunks of CP = 16 or 32 steps; latent
-// rows padded to LP = 16, 32 or 64; every matrix product is 16x16 output
-// tiles of the f32 MFMA, operands read from LDS):
+// Kernels (256 threads = 4 waves unless stated; chunks of CP = 16 or 32
+// steps; latent rows padded to LP = 16, 32 or 64; every matrix product is
+// 16x16 output tiles of the f32 MFMA, A operands read from LDS, B operands
+// from LDS or straight from the accumulators of the product before):
 //   wy_factor_kernel    one block per (head, chunk), all chunks at once: the
 //                       chunk's factors M, Qc, Kt, T, Bq and c_last, written
 //                       as one record per chunk after the boundary states
 //                       (the forward's saved state for the backward).
-//   wy_fwd_strip_kernel one wave per (head, 16 dense columns), four to a
-//                       block: the chunks in order, streaming their records
-//                       through two LDS copies; each wave carries its strip
-//                       of the state alone; saves the state at every chunk
-//                       start and U.
+//   wy_fwd_strip_kernel 512 threads: one chain wave per (head, 16 dense
+//                       columns), four to a block, each carrying its strip
+//                       of the state through the chunks in order, and one
+//                       memory wave per strip that streams the records
+//                       through two LDS copies and stores the strip's
+//                       results; saves the state at every chunk start and U.
 //   wy_fwd_fused_kernel without a boundary buffer (no backward to follow):
 //                       one block per (head, 32 dense columns), building
 //                       each chunk's factors itself.
@@ -160,6 +162,52 @@ __device__ __forceinline__ void mma_kc_n(f32x4 (&acc)[N], const float* const (&a
         for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int c = 0; c < N; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][j][e], bv[j][e], acc[c], 0, 0, 0);
+}
+
+// N independent products acc[c] += A_c B whose B is another product's
+// result as the accumulators hold it: K / 16 row tiles, lane l holding
+// B(16 t + 4 (l / 16) + r, l % 16) in b[t][r].  Lane group kq takes
+// k = 16 t + 4 kq + r at step (t, r) (the same reordering for A), so B goes
+// from one product to the next without a transpose through LDS.
+// acc_a reads the A operands, A_c(m, k) = a[c][m * SAM + k * SAK] (with
+// SAK = 1 and SAM a multiple of 4, a lane's four operands of a tile are one
+// 16-byte read; kNeg negates them, for acc[c] -= A_c B), so that they can be
+// read ahead of the product that needs them; acc_mma runs the chains with
+// the MFMAs of the N chains interleaved.
+template <int N, int K, int SAM, int SAK, bool kNeg = false>
+__device__ __forceinline__ void acc_a(f32x4 (&av)[N][K / 16], const float* const (&a)[N], int lane) {
+    static_assert(K % 16 == 0, "whole accumulator tiles");
+    const int i = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < K / 16; ++t)
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+            const float* p = a[c] + i * SAM + (16 * t + 4 * kq) * SAK;
+            if constexpr (SAK == 1) {
+                static_assert(SAM % 4 == 0, "16-byte operand reads");
+                av[c][t] = *reinterpret_cast<const f32x4*>(p);
+            } else {
+                av[c][t] = f32x4{p[0], p[SAK], p[2 * SAK], p[3 * SAK]};
+            }
+            if constexpr (kNeg) av[c][t] = -av[c][t];
+        }
+}
+
+template <int N, int K>
+__device__ __forceinline__ void acc_mma(f32x4 (&acc)[N], const f32x4 (&av)[N][K / 16], const f32x4* b) {
+#pragma unroll
+    for (int t = 0; t < K / 16; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < N; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][t][r], b[t][r], acc[c], 0, 0, 0);
+}
+
+template <int N, int K, int SAM, int SAK, bool kNeg = false>
+__device__ __forceinline__ void mma_acc_n(f32x4 (&acc)[N], const float* const (&a)[N], const f32x4* b, int lane) {
+    f32x4 av[N][K / 16];
+    acc_a<N, K, SAM, SAK, kNeg>(av, a, lane);
+    acc_mma<N, K>(acc, av, b);
 }
 
 // The same with K = 16 * k16, k16 wave-uniform in 1 .. KMAX / 16 (the
@@ -654,19 +702,24 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_fused_kernel(WyArgs a) {
 }
 
 // The forward over saved records, one wave per 16-column strip of the dense
-// axis: a block of 4 waves takes 64 dense columns of one head, and each wave
-// carries its strip's state S[:, strip] through the chunks alone.  Within a
-// chunk no wave needs another's results: rhs = w.v - M S, U = T rhs, O and
-// S_end of a strip use only that strip's columns.  The chunk's record is the
-// only shared operand; two LDS copies alternate, the next chunk's staged
-// while this one computes, so a chunk costs one barrier.  The strip's S^T,
-// rhs^T and U^T pass through the wave's own LDS area, from the accumulator
-// layout into the K-contiguous operand layout.  LDS operations of one wave
-// complete in order, so wave_sync (wavefront-scope fences around a wave
-// barrier: no instructions, only no compiler reordering) is all the ordering
-// that the exchange needs.
-constexpr int kStrip = 16;                 // dense columns per wave
+// axis: a block takes 64 dense columns of one head, and each of its first
+// four waves (the chain waves) carries its strip's state S[:, strip] through
+// the chunks alone.  Within a chunk no strip needs another's results:
+// rhs = w.v - M S, U = T rhs, O and S_end of a strip use only that strip's
+// columns, and every product takes its B operand straight from the
+// accumulators of the one before (mma_acc_n), so the chain from S to S_end
+// passes through no LDS.  The block's other four waves (the memory waves,
+// one per strip) move everything else: they stage the next chunk's record
+// into the other of two LDS copies, load the one after, and store the
+// previous chunk's U, context and state, which the chain wave left in LDS
+// (two copies per strip, as for the records).  The two kinds of wave share
+// each SIMD, so one's memory waits and the other's MFMA chains overlap, and a
+// chunk costs one barrier.  LDS operations of one wave complete in order, so
+// wave_sync (wavefront-scope fences around a wave barrier: no instructions,
+// only no compiler reordering) orders a wave's own transposes.
+constexpr int kStrip = 16;                 // dense columns per strip
 constexpr int kStripBlock = 4 * kStrip;    // dense columns per block
+constexpr int kStripThreads = 2 * kThreads;
 
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -675,90 +728,92 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 template <int CP, int LP>
-struct alignas(16) StripT {                // one wave's transposes: S^T [16][LP + 4], rhs^T and U^T [16][CP + 4]
-    float st[16 * (LP + 4)], rt[16 * (CP + 4)], ut[16 * (CP + 4)];
+struct alignas(16) StripOut {              // one strip's chunk results, transposed: U^T, O^T [16][CP + 4], S^T [16][LP + 4]
+    float ut[16 * (CP + 4)], ot[16 * (CP + 4)], st[16 * (LP + 4)];
 };
 
 // kVec: dense rows 16-byte aligned (D a multiple of 4; w, v, the context,
-// the final state and the saved state aligned): w and v are loaded, and U,
+// the final state, the saved state and U aligned): w and v are loaded, and U,
 // the context and the state stored, as 16-byte row pieces (lane: rows
 // vr + 16 k, columns vn .. vn + 3 of its strip), a quarter of the memory
-// instructions; w.v reaches the accumulator layout, and the outputs their
-// rows, through the strip's transposes.
+// instructions; w.v reaches the accumulator layout through the chain wave's
+// own transpose.
 template <int CP, int LP, bool kVec>
-__global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
+__global__ void __launch_bounds__(kStripThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
     using F = StagedFactors<CP, LP>;
     using R = Rec<CP, LP>;
     constexpr int LS = F::LS, CS = F::CS, NT = F::NT;
     constexpr int NL = LP / 16;            // 16-row tiles of the state
-    constexpr int SST = LP + 4;            // row stride of the strip's S^T [16][LP]
-    constexpr int SCT = CP + 4;            // row stride of rhs^T and U^T [16][CP]
+    constexpr int SST = LP + 4;            // row stride of S^T [16][LP]
+    constexpr int SCT = CP + 4;            // row stride of U^T, O^T and x^T [16][CP]
     static_assert((SST / 4) % 2 == 1 && (SCT / 4) % 2 == 1 && (LS / 4) % 2 == 1 && (CS / 4) % 2 == 1,
                   "16-byte operand reads on distinct banks");
     __shared__ F f[2];
-    __shared__ StripT<CP, LP> strip[4];
+    __shared__ StripOut<CP, LP> out[2][4];
+    __shared__ float xt[4][16 * SCT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool chain = wave < 4;           // wave-uniform role
+    const int strip = wave & 3;
     const int g4 = 4 * (lane >> 4), col = lane & 15;   // accumulator rows g4 + r, column col
     // Blocks as the other sequential kernels deal them: a head's column groups on one XCD.
     const int64_t n_dg = (a.D + kStripBlock - 1) / kStripBlock;
     const int64_t xcd = blockIdx.x % 8, rest = blockIdx.x / 8;
     const int64_t head = (rest / n_dg) * 8 + xcd;
     if (head >= a.BH) return;
-    const int64_t d0 = (rest % n_dg) * kStripBlock + kStrip * wave;   // this wave's first column
+    const int64_t d0 = (rest % n_dg) * kStripBlock + kStrip * strip;   // the strip's first column
     const int64_t nb = a.n_chunks;
     const int D = int(a.D);
     const bool col_ok = d0 + col < a.D;
     const int cc = int(d0 + col < a.D ? d0 + col : a.D - 1);         // clamped column (absolute)
-    float* myST = strip[wave].st;
-    float* myRT = strip[wave].rt;
-    float* myUT = strip[wave].ut;
-
-    // w and v of chunk c at this lane's accumulator elements (raw, clamped;
-    // masked where used).
-    float wv[NT][4], vv[NT][4];
-    const int vr = lane >> 2, vn = 4 * (lane & 3);
+    const int vr = lane >> 2, vn = 4 * (lane & 3);                    // kVec row pieces
     const bool vcol = d0 + vn < a.D;
     const int vcc = int(vcol ? d0 + vn : a.D - 4);   // kVec: clamped first column (D >= 4)
-    auto load_wv = [&](int64_t c) {
-        const int64_t t0 = c * CP;
-        const int lr = last_row(a, t0, CP);
-        const float* wb = a.w + (head * a.T + t0) * a.D;
-        const float* vb = a.v + (head * a.T + t0) * a.D;
-        if constexpr (kVec) {
-#pragma unroll
-            for (int k = 0; k < NT; ++k) {
-                const int row = vr + 16 * k;
-                const int off = (row < lr ? row : lr) * D + vcc;
-                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wb + off);
-                const f32x4 v4 = *reinterpret_cast<const f32x4*>(vb + off);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    wv[k][e] = w4[e];
-                    vv[k][e] = v4[e];
-                }
-            }
-        } else {
-#pragma unroll
-            for (int ti = 0; ti < NT; ++ti)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * ti + g4 + r;
-                    const int off = (row < lr ? row : lr) * D + cc;
-                    wv[ti][r] = wb[off];
-                    vv[ti][r] = vb[off];
-                }
-        }
-    };
-    auto write_t = [&](float* dstT, int stride, int row0, const f32x4& v) {   // rows row0 + g4 + r, column col
-        *reinterpret_cast<f32x4*>(dstT + col * stride + row0 + g4) = v;
-    };
+    const float* recs = a.rec + head * nb * R::kSize;
 
-    // The state entering chunk 0, in accumulator layout: S[16 tl + g4 + r][col].
-    f32x4 sc[NL];
-    {
+    if (chain) {
+        // ------------------------------------------------ chain wave
+        float* myX = xt[strip];
+        // w and v of a chunk, raw and clamped (masked where used): at this
+        // lane's accumulator elements, or (kVec) row pieces.
+        float wv[NT][4], vv[NT][4];
+        auto load_wv = [&](int64_t c) {
+            const int64_t t0 = c * CP;
+            const int lr = last_row(a, t0, CP);
+            const float* wb = a.w + (head * a.T + t0) * a.D;
+            const float* vb = a.v + (head * a.T + t0) * a.D;
+            if constexpr (kVec) {
+#pragma unroll
+                for (int k = 0; k < NT; ++k) {
+                    const int row = vr + 16 * k;
+                    const int off = (row < lr ? row : lr) * D + vcc;
+                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(wb + off);
+                    const f32x4 v4 = *reinterpret_cast<const f32x4*>(vb + off);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        wv[k][e] = w4[e];
+                        vv[k][e] = v4[e];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * ti + g4 + r;
+                        const int off = (row < lr ? row : lr) * D + cc;
+                        wv[ti][r] = wb[off];
+                        vv[ti][r] = vb[off];
+                    }
+            }
+        };
+        auto write_t = [&](float* dstT, int stride, int row0, const f32x4& v) {   // rows row0 + g4 + r, column col
+            *reinterpret_cast<f32x4*>(dstT + col * stride + row0 + g4) = v;
+        };
+
+        // The state entering chunk 0, in accumulator layout: S[16 tl + g4 + r][col].
+        f32x4 sc[NL];
         const float* s0 = a.s0 + head * a.L * a.D;
-        const OutRegion b0(a.bnd ? a.bnd + head * nb * LP * a.D : nullptr, LP * a.D);
 #pragma unroll
         for (int tl = 0; tl < NL; ++tl)
 #pragma unroll
@@ -766,186 +821,217 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
                 const int l = 16 * tl + g4 + r;
                 sc[tl][r] = s0[(l < a.L ? l : int(a.L) - 1) * D + cc];   // clamped, masked below
             }
-#pragma unroll
-        for (int tl = 0; tl < NL; ++tl)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int l = 16 * tl + g4 + r;
-                const bool ok = l < a.L && col_ok;
-                sc[tl][r] = ok ? sc[tl][r] : 0.f;
-                b0.store(sc[tl][r], ok, l * D + int(d0) + col);
-            }
-    }
-#pragma unroll
-    for (int tl = 0; tl < NL; ++tl) write_t(myST, SST, 16 * tl, sc[tl]);
-
-    RecRegs<CP, LP> rr;
-    const RecStage<CP, LP, F> rs(tid);
-    const float* recs = a.rec + head * nb * R::kSize;
-    load_rec<CP, LP>(rr, recs, tid);
-    rs.stage(f[0], rr);
-    load_rec<CP, LP>(rr, recs + (nb > 1 ? 1 : 0) * R::kSize, tid);
-    load_wv(0);
-    __syncthreads();
-
-    for (int64_t c = 0; c < nb; ++c) {
-        const int64_t t0 = c * CP;
-        F& fc = f[c & 1];
-        // x = w.v of this chunk (zero on padded steps), as the negated
-        // initial value of M S - x.
-        f32x4 nr[NT];
-        if constexpr (kVec) {
-            // Rows of -x into the rhs^T area (free: its last readers were in the
-            // chunk before), read back in the accumulator layout.
-#pragma unroll
-            for (int k = 0; k < NT; ++k) {
-                const int row = vr + 16 * k;
-                const bool ok = t0 + row < a.T && vcol;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) myRT[(vn + e) * SCT + row] = ok ? -(wv[k][e] * vv[k][e]) : 0.f;
-            }
-            wave_sync();
-#pragma unroll
-            for (int ti = 0; ti < NT; ++ti) nr[ti] = *reinterpret_cast<const f32x4*>(myRT + col * SCT + 16 * ti + g4);
-        } else {
-#pragma unroll
-            for (int ti = 0; ti < NT; ++ti)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool ok = t0 + 16 * ti + g4 + r < a.T && col_ok;
-                    nr[ti][r] = ok ? -(wv[ti][r] * vv[ti][r]) : 0.f;
-                }
-        }
-        // The next chunk's record into the other copy (its last readers were
-        // behind the previous chunk's barrier), then the loads for later
-        // chunks (unconditional, clamped: see the other kernels).
-        rs.stage(f[(c + 1) & 1], rr);
-        const int64_t c2 = c + 2 < nb ? c + 2 : nb - 1;
-        load_rec<CP, LP>(rr, recs + c2 * R::kSize, tid);
-        load_wv(c + 1 < nb ? c + 1 : c);
-
-        // M S - x and Qc S, tile rows ti (independent chains).
-        f32x4 o[NT];
+        load_wv(0);
+        // The state goes to chunk 0's boundary slot after the loads above, as
+        // every chunk's stores follow its loads: the wait for w and v at the
+        // top of the loop then need not cover the stores.
         {
-            f32x4 acc[2 * NT];
-            const float* aa[2 * NT];
+            const OutRegion b0(a.bnd ? a.bnd + head * nb * LP * a.D : nullptr, LP * a.D);
 #pragma unroll
-            for (int ti = 0; ti < NT; ++ti) {
-                acc[2 * ti] = nr[ti];
-                acc[2 * ti + 1] = zero4();
-                aa[2 * ti] = fc.M + 16 * ti * LS;
-                aa[2 * ti + 1] = fc.Qc + 16 * ti * LS;
-            }
-            mma_kc_n<2 * NT, LP, LS, SST>(acc, aa, myST, lane);
-#pragma unroll
-            for (int ti = 0; ti < NT; ++ti) {
-                nr[ti] = acc[2 * ti];
-                o[ti] = acc[2 * ti + 1];
-            }
-        }
-#pragma unroll
-        for (int ti = 0; ti < NT; ++ti) write_t(myRT, SCT, 16 * ti, nr[ti]);
-        wave_sync();
-        // U = T rhs = -T (M S - x); T is lower triangular.
-        // (Row tile 1 sums over steps 0..15 together with row tile 0, then over 16..31.)
-        f32x4 u[NT];
-        {
-            const float* aa[NT];
-#pragma unroll
-            for (int ti = 0; ti < NT; ++ti) {
-                u[ti] = zero4();
-                aa[ti] = fc.Tm + 16 * ti * CS;
-            }
-            mma_kc_n<NT, 16, CS, SCT>(u, aa, myRT, lane);
-            if constexpr (NT == 2) mma_kc<16, CS, SCT>(u[1], fc.Tm + 16 * CS + 16, myRT + 16, lane);
-        }
-        // U is kept for the backward (rows of the padded chunk, columns < D).
-        const OutRegion ub(a.ubuf ? a.ubuf + (head * nb * CP + t0) * a.D : nullptr, CP * a.D);
-#pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                u[ti][r] = -u[ti][r];
-                if constexpr (!kVec) ub.store(u[ti][r], col_ok, (16 * ti + g4 + r) * D + int(d0) + col);
-            }
-            write_t(myUT, SCT, 16 * ti, u[ti]);
-        }
-        wave_sync();
-        // (kVec: outputs leave as 16-byte row pieces read back from the transposes.)
-        auto row4 = [&](const float* srcT, int stride, int row) {
-            return f32x4{srcT[vn * stride + row], srcT[(vn + 1) * stride + row], srcT[(vn + 2) * stride + row],
-                         srcT[(vn + 3) * stride + row]};
-        };
-        if constexpr (kVec) {
-#pragma unroll
-            for (int k = 0; k < NT; ++k) ub.store4(row4(myUT, SCT, vr + 16 * k), vcol, (vr + 16 * k) * D + vcc);
-        }
-        // O = (Qc S + Bq U) / sqrt(L); Bq is lower triangular.
-        {
-            const float* aa[NT];
-#pragma unroll
-            for (int ti = 0; ti < NT; ++ti) aa[ti] = fc.Bq + 16 * ti * CS;
-            mma_kc_n<NT, 16, CS, SCT>(o, aa, myUT, lane);
-            if constexpr (NT == 2) mma_kc<16, CS, SCT>(o[1], fc.Bq + 16 * CS + 16, myUT + 16, lane);
-#pragma unroll
-            for (int ti = 0; ti < NT; ++ti) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[ti][r] *= a.scale;
-                if constexpr (kVec) write_t(myRT, SCT, 16 * ti, o[ti]);   // rhs^T is dead: O^T takes its place
-            }
-        }
-        // S_end = diag(c_last) S + Kt^T U.
-        {
-            const float* aa[NL];
-#pragma unroll
-            for (int tl = 0; tl < NL; ++tl) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[tl][r] *= fc.clast[16 * tl + g4 + r];
-                aa[tl] = fc.Kt + 16 * tl;
-            }
-            mma_n<NL, CP, 1, LS, 1, SCT>(sc, aa, myUT, lane);
-        }
-        const int rows = a.T - t0 < CP ? int(a.T - t0) : CP;
-        const OutRegion ob(a.ctx + (head * a.T + t0) * a.D, rows * a.D);
-        if constexpr (!kVec) {
-#pragma unroll
-            for (int ti = 0; ti < NT; ++ti)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * ti + g4 + r;
-                    ob.store(o[ti][r], row < rows && col_ok, row * D + int(d0) + col);
-                }
-        }
-        // The state goes to the next chunk's boundary slot, or (last chunk)
-        // to the final state.
-        const OutRegion sb = c + 1 < nb
-            ? OutRegion(a.bnd ? a.bnd + (head * nb + c + 1) * LP * a.D : nullptr, LP * a.D)
-            : OutRegion(a.state ? a.state + head * a.L * a.D : nullptr, a.L * a.D);
-#pragma unroll
-        for (int tl = 0; tl < NL; ++tl) {
-            if constexpr (!kVec) {
+            for (int tl = 0; tl < NL; ++tl)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int l = 16 * tl + g4 + r;
-                    sb.store(sc[tl][r], l < a.L && col_ok, l * D + int(d0) + col);
+                    const bool ok = l < a.L && col_ok;
+                    sc[tl][r] = ok ? sc[tl][r] : 0.f;
+                    b0.store(sc[tl][r], ok, l * D + int(d0) + col);
+                }
+        }
+        __syncthreads();   // record 0 staged
+
+        for (int64_t c = 0; c < nb; ++c) {
+            const int64_t t0 = c * CP;
+            F& fc = f[c & 1];
+            // x = w.v of this chunk (zero on padded steps), as the negated
+            // initial value of M S - x.
+            f32x4 nr[NT];
+            if constexpr (kVec) {
+                // Rows of -x into the strip's x^T, read back in the accumulator layout.
+#pragma unroll
+                for (int k = 0; k < NT; ++k) {
+                    const int row = vr + 16 * k;
+                    const bool ok = t0 + row < a.T && vcol;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) myX[(vn + e) * SCT + row] = ok ? -(wv[k][e] * vv[k][e]) : 0.f;
+                }
+                wave_sync();
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) nr[ti] = *reinterpret_cast<const f32x4*>(myX + col * SCT + 16 * ti + g4);
+            } else {
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool ok = t0 + 16 * ti + g4 + r < a.T && col_ok;
+                        nr[ti][r] = ok ? -(wv[ti][r] * vv[ti][r]) : 0.f;
+                    }
+            }
+            load_wv(c + 1 < nb ? c + 1 : c);   // unconditional, clamped
+            __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the chunk's products
+            // Every A operand of the chunk's products (none depends on the
+            // state), read before the chain from S to S_end starts.
+            f32x4 amq[2 * NT][LP / 16], at[NT][1], ab[NT][1], ak[NL][CP / 16];
+            {
+                const float* pmq[2 * NT];
+                const float* pt[NT];
+                const float* pb[NT];
+                const float* pk[NL];
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) {
+                    pmq[2 * ti] = fc.M + 16 * ti * LS;
+                    pmq[2 * ti + 1] = fc.Qc + 16 * ti * LS;
+                    // Row tile 1 of T and Bq (lower triangular) sums over steps
+                    // 0..15 together with row tile 0, then over 16..31 alone.
+                    pt[ti] = fc.Tm + 16 * ti * CS;
+                    pb[ti] = fc.Bq + 16 * ti * CS;
+                }
+#pragma unroll
+                for (int tl = 0; tl < NL; ++tl) pk[tl] = fc.Kt + 16 * tl;
+                acc_a<2 * NT, LP, LS, 1>(amq, pmq, lane);
+                acc_a<NT, 16, CS, 1>(at, pt, lane);
+                acc_a<NT, 16, CS, 1>(ab, pb, lane);
+                acc_a<NL, CP, 1, LS>(ak, pk, lane);
+            }
+            f32x4 at1[1][1], ab1[1][1];
+            if constexpr (NT == 2) {
+                const float* pt1[1] = {fc.Tm + 16 * CS + 16};
+                const float* pb1[1] = {fc.Bq + 16 * CS + 16};
+                acc_a<1, 16, CS, 1>(at1, pt1, lane);
+                acc_a<1, 16, CS, 1>(ab1, pb1, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // M S - x and Qc S (independent chains), S straight from the
+            // accumulators.
+            f32x4 o[NT];
+            {
+                f32x4 acc[2 * NT];
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) {
+                    acc[2 * ti] = nr[ti];
+                    acc[2 * ti + 1] = zero4();
+                }
+                acc_mma<2 * NT, LP>(acc, amq, sc);
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti) {
+                    nr[ti] = acc[2 * ti];
+                    o[ti] = acc[2 * ti + 1];
                 }
             }
-            write_t(myST, SST, 16 * tl, sc[tl]);
-        }
-        if constexpr (kVec) {
-            wave_sync();
+            // U = -T (M S - x).
+            f32x4 u[NT];
+            {
 #pragma unroll
-            for (int k = 0; k < NT; ++k) {
-                const int row = vr + 16 * k;
-                ob.store4(row4(myRT, SCT, row), vcol && row < rows, row * D + vcc);
+                for (int ti = 0; ti < NT; ++ti) u[ti] = zero4();
+                acc_mma<NT, 16>(u, at, nr);
+                if constexpr (NT == 2) {
+                    f32x4 u1[1] = {u[1]};
+                    acc_mma<1, 16>(u1, at1, nr + 1);
+                    u[1] = u1[0];
+                }
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) u[ti][r] = -u[ti][r];
+            }
+            // O = (Qc S + Bq U) / sqrt(L) and S_end = diag(c_last) S + Kt^T U:
+            // independent chains over U.
+            {
+#pragma unroll
+                for (int tl = 0; tl < NL; ++tl)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sc[tl][r] *= fc.clast[16 * tl + g4 + r];
+                acc_mma<NT, 16>(o, ab, u);
+                if constexpr (NT == 2) {
+                    f32x4 o1[1] = {o[1]};
+                    acc_mma<1, 16>(o1, ab1, u + 1);
+                    o[1] = o1[0];
+                }
+                acc_mma<NL, CP>(sc, ak, u);
+#pragma unroll
+                for (int ti = 0; ti < NT; ++ti)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[ti][r] *= a.scale;
+            }
+            // The chunk's results to the strip's output copy, for its memory wave.
+            StripOut<CP, LP>& so = out[c & 1][strip];
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+                write_t(so.ut, SCT, 16 * ti, u[ti]);
+                write_t(so.ot, SCT, 16 * ti, o[ti]);
             }
 #pragma unroll
-            for (int k = 0; k < NL; ++k) {
-                const int l = vr + 16 * k;
-                sb.store4(row4(myST, SST, l), vcol && l < a.L, l * D + vcc);
-            }
+            for (int tl = 0; tl < NL; ++tl) write_t(so.st, SST, 16 * tl, sc[tl]);
+            __syncthreads();   // results handed over; the next record staged, this one free
         }
-        __syncthreads();   // the next record is staged, this one is free for the one after, S^T is written
+    } else {
+        // ------------------------------------------------ memory wave
+        const int mtid = tid - kThreads;   // 0 .. 255 over the four memory waves
+        // One chunk's U (all CP rows, for the backward), context (rows < T)
+        // and end state (to the next chunk's boundary slot, or after the last
+        // chunk to the final state), from the chain wave's output copy.
+        // Every store instruction issues whether or not `live` (dropped
+        // lanes): a store under a branch would make the compiler's wait for
+        // the record at the top of the loop cover the stores.
+        auto store_out = [&](int64_t c, bool live) {
+            const int64_t t0 = c * CP;
+            const StripOut<CP, LP>& so = out[c & 1][strip];
+            const OutRegion ub(a.ubuf ? a.ubuf + (head * nb * CP + t0) * a.D : nullptr, CP * a.D);
+            const int rows = a.T - t0 < CP ? int(a.T - t0) : CP;
+            const OutRegion ob(a.ctx + (head * a.T + t0) * a.D, rows * a.D);
+            const OutRegion sb = c + 1 < nb
+                ? OutRegion(a.bnd ? a.bnd + (head * nb + c + 1) * LP * a.D : nullptr, LP * a.D)
+                : OutRegion(a.state ? a.state + head * a.L * a.D : nullptr, a.L * a.D);
+            if constexpr (kVec) {
+                auto row4 = [&](const float* srcT, int stride, int row) {
+                    return f32x4{srcT[vn * stride + row], srcT[(vn + 1) * stride + row],
+                                 srcT[(vn + 2) * stride + row], srcT[(vn + 3) * stride + row]};
+                };
+#pragma unroll
+                for (int k = 0; k < NT; ++k) {
+                    const int row = vr + 16 * k;
+                    ub.store4(row4(so.ut, SCT, row), live && vcol, row * D + vcc);
+                    ob.store4(row4(so.ot, SCT, row), live && vcol && row < rows, row * D + vcc);
+                }
+#pragma unroll
+                for (int k = 0; k < NL; ++k) {
+                    const int l = vr + 16 * k;
+                    sb.store4(row4(so.st, SST, l), live && vcol && l < a.L, l * D + vcc);
+                }
+            } else {
+                // Lane: column col, rows 4 k + lane / 16.
+                const int rq = lane >> 4;
+#pragma unroll
+                for (int k = 0; k < CP / 4; ++k) {
+                    const int row = 4 * k + rq;
+                    ub.store(so.ut[col * SCT + row], live && col_ok, row * D + int(d0) + col);
+                    ob.store(so.ot[col * SCT + row], live && col_ok && row < rows, row * D + int(d0) + col);
+                }
+#pragma unroll
+                for (int k = 0; k < LP / 4; ++k) {
+                    const int l = 4 * k + rq;
+                    sb.store(so.st[col * SST + l], live && col_ok && l < a.L, l * D + int(d0) + col);
+                }
+            }
+        };
+
+        RecRegs<CP, LP> rr;
+        const RecStage<CP, LP, F> rs(mtid);
+        load_rec<CP, LP>(rr, recs, mtid);
+        rs.stage(f[0], rr);
+        load_rec<CP, LP>(rr, recs + (nb > 1 ? 1 : 0) * R::kSize, mtid);
+        __syncthreads();   // record 0 staged
+
+        for (int64_t c = 0; c < nb; ++c) {
+            // The previous chunk's results out, the next chunk's record into
+            // the other copy (its last readers were behind the previous
+            // barrier), then the load of the one after (unconditional, clamped).
+            store_out(c > 0 ? c - 1 : 0, c > 0);
+            rs.stage(f[(c + 1) & 1], rr);
+            const int64_t c2 = c + 2 < nb ? c + 2 : nb - 1;
+            load_rec<CP, LP>(rr, recs + c2 * R::kSize, mtid);
+            __syncthreads();
+        }
+        store_out(nb - 1, true);
     }
 }
 
@@ -957,8 +1043,8 @@ __global__ void __launch_bounds__(kThreads, 1) wy_fwd_strip_kernel(WyArgs a) {
 // barrier per chunk); dO^T, dU^T, drhs^T and dS^T pass through the wave's own
 // LDS area.
 template <int CP, int LP>
-struct alignas(16) CarryStripT {          // one wave's transposes: dS^T [16][LP + 4]; dO^T, dU^T, drhs^T [16][CP + 4]
-    float st[16 * (LP + 4)], ot[16 * (CP + 4)], ut[16 * (CP + 4)], rt[16 * (CP + 4)];
+struct alignas(16) CarryStripT {          // one wave's transposes: dO^T and drhs^T [16][CP + 4]
+    float ot[16 * (CP + 4)], rt[16 * (CP + 4)];
 };
 
 // kVec: dense rows 16-byte aligned (D a multiple of 4; dO, w, v, dw, dv and
@@ -971,8 +1057,8 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
     using R = Rec<CP, LP>;
     constexpr int LS = F::LS, CS = F::CS, NT = F::NT;
     constexpr int NL = LP / 16;
-    constexpr int SST = LP + 4, SCT = CP + 4;
-    static_assert((SST / 4) % 2 == 1 && (SCT / 4) % 2 == 1 && (LS / 4) % 2 == 1, "16-byte operand reads on distinct banks");
+    constexpr int SCT = CP + 4;
+    static_assert((SCT / 4) % 2 == 1 && (LS / 4) % 2 == 1 && CS % 4 == 0, "16-byte operand reads on distinct banks");
     __shared__ F f[2];
     __shared__ CarryStripT<CP, LP> strip[4];
 
@@ -988,9 +1074,7 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
     const float s = a.scale;
     const bool col_ok = d0 + col < a.D;
     const int cc = int(d0 + col < a.D ? d0 + col : a.D - 1);
-    float* myST = strip[wave].st;
     float* myOT = strip[wave].ot;
-    float* myUT = strip[wave].ut;
     float* myRT = strip[wave].rt;
     auto write_t = [&](float* dstT, int stride, int row0, const f32x4& v) {
         *reinterpret_cast<f32x4*>(dstT + col * stride + row0 + g4) = v;
@@ -1039,7 +1123,6 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
     // is what enters the last chunk from later ones.
     f32x4 sc[NL];
     {
-        const OutRegion b0(a.dbnd + (head * nb + nb - 1) * LP * a.D, LP * a.D);
         if (a.dstate) {
             const float* ds = a.dstate + head * a.L * a.D;
 #pragma unroll
@@ -1053,17 +1136,6 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
 #pragma unroll
             for (int tl = 0; tl < NL; ++tl) sc[tl] = zero4();
         }
-#pragma unroll
-        for (int tl = 0; tl < NL; ++tl) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int l = 16 * tl + g4 + r;
-                const bool ok = l < a.L && col_ok;
-                sc[tl][r] = ok ? sc[tl][r] : 0.f;
-                b0.store(sc[tl][r], ok, l * D + int(d0) + col);
-            }
-            write_t(myST, SST, 16 * tl, sc[tl]);
-        }
     }
 
     RecRegs<CP, LP> rr;
@@ -1073,6 +1145,21 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
     rs.stage(f[(nb - 1) & 1], rr);
     load_rec<CP, LP>(rr, recs + (nb > 1 ? nb - 2 : 0) * R::kSize, tid);
     load_dense3(nb - 1);
+    // The last chunk's slot after the loads above, as every chunk's stores
+    // follow its loads (so the waits at the top of the loop need not cover
+    // stores).
+    {
+        const OutRegion b0(a.dbnd + (head * nb + nb - 1) * LP * a.D, LP * a.D);
+#pragma unroll
+        for (int tl = 0; tl < NL; ++tl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int l = 16 * tl + g4 + r;
+                const bool ok = l < a.L && col_ok;
+                sc[tl][r] = ok ? sc[tl][r] : 0.f;
+                b0.store(sc[tl][r], ok, l * D + int(d0) + col);
+            }
+    }
     __syncthreads();
 
     for (int64_t c = nb - 1; c >= 0; --c) {
@@ -1111,6 +1198,34 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
         load_dense3(c >= 1 ? c - 1 : 0);
         wave_sync();
 
+        // The chunk's loads stay ahead of its products.
+        __builtin_amdgcn_sched_barrier(0);
+        // The A operands of the chain from dS to the dS entering this chunk,
+        // read before it starts; the chain takes every B operand from the
+        // accumulators, and the products with dO (its transpose in LDS) hang
+        // off it.
+        f32x4 ak[NT][LP / 16], at0[1][CP / 16], at1[1][1], am[NL][CP / 16];
+        {
+            const float* pk[NT];
+            const float* pm[NL];
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) pk[ti] = fc.Kt + 16 * ti * LS;
+#pragma unroll
+            for (int tl = 0; tl < NL; ++tl) pm[tl] = fc.M + 16 * tl;
+            const float* pt0[1] = {fc.Tm};
+            acc_a<NT, LP, LS, 1>(ak, pk, lane);
+            acc_a<1, CP, 1, CS>(at0, pt0, lane);
+            if constexpr (NT == 2) {
+                const float* pt1[1] = {fc.Tm + 16 * CS + 16};
+                acc_a<1, 16, 1, CS>(at1, pt1, lane);
+            }
+            acc_a<NL, CP, 1, LS>(am, pm, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tl = 0; tl < NL; ++tl)
+#pragma unroll
+            for (int t = 0; t < CP / 16; ++t) am[tl][t] = -am[tl][t];   // for dS0 -= M^T drhs
         // dU = Bq^T dO / sqrt(L) + Kt dS  (Bq^T upper triangular: tile ti
         // sums over steps 16 ti ..).
         f32x4 du[NT], kd[NT];
@@ -1118,45 +1233,44 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
         for (int ti = 0; ti < NT; ++ti) {
             du[ti] = zero4();
             kd[ti] = zero4();
-            mma_kc<LP, LS, SST>(kd[ti], fc.Kt + 16 * ti * LS, myST, lane);
         }
+        acc_mma<NT, LP>(kd, ak, sc);
         mma<CP, 1, CS, 1, SCT>(du[0], fc.Bq, myOT, lane);
         if constexpr (NT == 2) mma<16, 1, CS, 1, SCT>(du[1], fc.Bq + 16 * CS + 16, myOT + 16, lane);
+        // diag(c_last) dS + Qc^T dO / sqrt(L), which M^T drhs is taken from below.
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
+        for (int tl = 0; tl < NL; ++tl) {
+            f32x4 aq = zero4();
+            mma<CP, 1, LS, 1, SCT>(aq, fc.Qc + 16 * tl, myOT, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[tl][r] = fc.clast[16 * tl + g4 + r] * sc[tl][r] + aq[r] * s;
+        }
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
             for (int r = 0; r < 4; ++r) du[ti][r] = du[ti][r] * s + kd[ti][r];
-            write_t(myUT, SCT, 16 * ti, du[ti]);
-        }
-        wave_sync();
         // drhs = T^T dU (upper triangular as Bq^T); dw = drhs . v, dv = drhs . w.
         f32x4 dr[NT];
-        dr[0] = zero4();
-        mma<CP, 1, CS, 1, SCT>(dr[0], fc.Tm, myUT, lane);
-        if constexpr (NT == 2) {
-            dr[1] = zero4();
-            mma<16, 1, CS, 1, SCT>(dr[1], fc.Tm + 16 * CS + 16, myUT + 16, lane);
+        {
+            f32x4 d0a[1] = {zero4()};
+            acc_mma<1, CP>(d0a, at0, du);
+            dr[0] = d0a[0];
+            if constexpr (NT == 2) {
+                f32x4 d1a[1] = {zero4()};
+                acc_mma<1, 16>(d1a, at1, du + 1);
+                dr[1] = d1a[0];
+            }
         }
+        // dS0 = diag(c_last) dS + Qc^T dO / sqrt(L) - M^T drhs.
+        acc_mma<NL, CP>(sc, am, dr);
         const OutRegion rb(a.drhs + (head * nb * CP + t0) * a.D, CP * a.D);
         const int64_t gbase = (head * a.T + t0) * a.D;
         const OutRegion dwb(a.dw ? a.dw + gbase : nullptr, rows * a.D);
         const OutRegion dvb(a.dv ? a.dv + gbase : nullptr, rows * a.D);
-#pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
-            if constexpr (!kVec) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * ti + g4 + r;
-                    const int off = row * D + int(d0) + col;
-                    rb.store(dr[ti][r], col_ok, off);   // for the gradient kernel
-                    dwb.store(dr[ti][r] * vc[ti][r], col_ok && row < rows, off);
-                    dvb.store(dr[ti][r] * wc[ti][r], col_ok && row < rows, off);
-                }
-            }
-            write_t(myRT, SCT, 16 * ti, dr[ti]);
-        }
-        wave_sync();
         if constexpr (kVec) {   // rows of drhs from its transpose; drhs, dw, dv as 16-byte pieces
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) write_t(myRT, SCT, 16 * ti, dr[ti]);
+            wave_sync();
 #pragma unroll
             for (int k = 0; k < NT; ++k) {
                 const int row = vr + 16 * k, off = row * D + vcc;
@@ -1171,29 +1285,29 @@ __global__ void __launch_bounds__(kThreads, 1) wy_bwd_carry_strip_kernel(WyArgs 
                 dwb.store4(w4, vcol && row < rows, off);
                 dvb.store4(v4, vcol && row < rows, off);
             }
-        }
-        // dS0 = Qc^T dO / sqrt(L) + diag(c_last) dS - M^T drhs.
+        } else {
 #pragma unroll
-        for (int tl = 0; tl < NL; ++tl) {
-            f32x4 aq = zero4(), am = zero4();
-            mma<CP, 1, LS, 1, SCT>(aq, fc.Qc + 16 * tl, myOT, lane);
-            mma<CP, 1, LS, 1, SCT>(am, fc.M + 16 * tl, myRT, lane);
+            for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sc[tl][r] = fc.clast[16 * tl + g4 + r] * sc[tl][r] + aq[r] * s - am[r];
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * ti + g4 + r;
+                    const int off = row * D + int(d0) + col;
+                    rb.store(dr[ti][r], col_ok, off);   // for the gradient kernel
+                    dwb.store(dr[ti][r] * vc[ti][r], col_ok && row < rows, off);
+                    dvb.store(dr[ti][r] * wc[ti][r], col_ok && row < rows, off);
+                }
         }
         // dS entering this chunk: the previous chunk's slot, or (first chunk)
         // d initial_state.
         const OutRegion db = c > 0 ? OutRegion(a.dbnd + (head * nb + c - 1) * LP * a.D, LP * a.D)
                                    : OutRegion(a.ds0 ? a.ds0 + head * a.L * a.D : nullptr, a.L * a.D);
 #pragma unroll
-        for (int tl = 0; tl < NL; ++tl) {
+        for (int tl = 0; tl < NL; ++tl)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int l = 16 * tl + g4 + r;
                 db.store(sc[tl][r], l < a.L && col_ok, l * D + int(d0) + col);
             }
-            write_t(myST, SST, 16 * tl, sc[tl]);
-        }
         __syncthreads();   // the previous record is staged, this one is free for the one before
     }
 }
@@ -1609,7 +1723,7 @@ hipError_t launch_fwd_t(const WyArgs& a, hipStream_t st) {
     const bool vec = a.D % 4 == 0 && (dense & 15) == 0;
     return hipLaunchKernel(vec ? reinterpret_cast<const void*>(&wy_fwd_strip_kernel<CP, LP, true>)
                                : reinterpret_cast<const void*>(&wy_fwd_strip_kernel<CP, LP, false>),
-                           dim3(strips), dim3(kThreads), params, 0, st);
+                           dim3(strips), dim3(kStripThreads), params, 0, st);
 }
 
 template <int CP, int LP>
