@@ -123,47 +123,6 @@ __device__ __forceinline__ void mma_kc(f32x4& acc, const float* a, const float* 
         for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][e], bv[j][e], acc, 0, 0, 0);
 }
 
-// N independent products over one B, acc[c] += A_c B, with the MFMAs of the
-// N chains interleaved (no MFMA waits for the one just before it) and B read
-// once: the strided form of mma (A_c(m, k) = a[c][m * SAM + k * SAK]) ...
-template <int N, int K, int SAM, int SAK, int SBK, int SBN>
-__device__ __forceinline__ void mma_n(f32x4 (&acc)[N], const float* const (&a)[N], const float* b, int lane) {
-    const int i = lane & 15, kq = lane >> 4;
-    float bv[K / 4], av[N][K / 4];
-#pragma unroll
-    for (int k = 0; k < K / 4; ++k) {
-        bv[k] = b[(4 * k + kq) * SBK + i * SBN];
-#pragma unroll
-        for (int c = 0; c < N; ++c) av[c][k] = a[c][i * SAM + (4 * k + kq) * SAK];
-    }
-#pragma unroll
-    for (int k = 0; k < K / 4; ++k)
-#pragma unroll
-        for (int c = 0; c < N; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][k], bv[k], acc[c], 0, 0, 0);
-}
-
-// ... and the K-contiguous form of mma_kc (the same reordering of k).
-template <int N, int K, int SA, int SB>
-__device__ __forceinline__ void mma_kc_n(f32x4 (&acc)[N], const float* const (&a)[N], const float* bt, int lane) {
-    static_assert(K % 16 == 0 && SA % 4 == 0 && SB % 4 == 0, "16-byte operand reads");
-    constexpr int KQ = K / 4;
-    const int i = lane & 15, kq = lane >> 4;
-    const f32x4* pb = reinterpret_cast<const f32x4*>(bt + i * SB + kq * KQ);
-    f32x4 bv[KQ / 4], av[N][KQ / 4];
-#pragma unroll
-    for (int j = 0; j < KQ / 4; ++j) {
-        bv[j] = pb[j];
-#pragma unroll
-        for (int c = 0; c < N; ++c) av[c][j] = reinterpret_cast<const f32x4*>(a[c] + i * SA + kq * KQ)[j];
-    }
-#pragma unroll
-    for (int j = 0; j < KQ / 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int c = 0; c < N; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][j][e], bv[j][e], acc[c], 0, 0, 0);
-}
-
 // N independent products acc[c] += A_c B whose B is another product's
 // result as the accumulators hold it: K / 16 row tiles, lane l holding
 // B(16 t + 4 (l / 16) + r, l % 16) in b[t][r].  Lane group kq takes
@@ -171,10 +130,9 @@ __device__ __forceinline__ void mma_kc_n(f32x4 (&acc)[N], const float* const (&a
 // from one product to the next without a transpose through LDS.
 // acc_a reads the A operands, A_c(m, k) = a[c][m * SAM + k * SAK] (with
 // SAK = 1 and SAM a multiple of 4, a lane's four operands of a tile are one
-// 16-byte read; kNeg negates them, for acc[c] -= A_c B), so that they can be
-// read ahead of the product that needs them; acc_mma runs the chains with
-// the MFMAs of the N chains interleaved.
-template <int N, int K, int SAM, int SAK, bool kNeg = false>
+// 16-byte read), so that they can be read ahead of the product that needs
+// them; acc_mma runs the chains with the MFMAs of the N chains interleaved.
+template <int N, int K, int SAM, int SAK>
 __device__ __forceinline__ void acc_a(f32x4 (&av)[N][K / 16], const float* const (&a)[N], int lane) {
     static_assert(K % 16 == 0, "whole accumulator tiles");
     const int i = lane & 15, kq = lane >> 4;
@@ -189,7 +147,6 @@ __device__ __forceinline__ void acc_a(f32x4 (&av)[N][K / 16], const float* const
             } else {
                 av[c][t] = f32x4{p[0], p[SAK], p[2 * SAK], p[3 * SAK]};
             }
-            if constexpr (kNeg) av[c][t] = -av[c][t];
         }
 }
 
@@ -201,13 +158,6 @@ __device__ __forceinline__ void acc_mma(f32x4 (&acc)[N], const f32x4 (&av)[N][K 
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int c = 0; c < N; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][t][r], b[t][r], acc[c], 0, 0, 0);
-}
-
-template <int N, int K, int SAM, int SAK, bool kNeg = false>
-__device__ __forceinline__ void mma_acc_n(f32x4 (&acc)[N], const float* const (&a)[N], const f32x4* b, int lane) {
-    f32x4 av[N][K / 16];
-    acc_a<N, K, SAM, SAK, kNeg>(av, a, lane);
-    acc_mma<N, K>(acc, av, b);
 }
 
 // The same with K = 16 * k16, k16 wave-uniform in 1 .. KMAX / 16 (the
@@ -707,7 +657,7 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_fused_kernel(WyArgs a) {
 // the chunks alone.  Within a chunk no strip needs another's results:
 // rhs = w.v - M S, U = T rhs, O and S_end of a strip use only that strip's
 // columns, and every product takes its B operand straight from the
-// accumulators of the one before (mma_acc_n), so the chain from S to S_end
+// accumulators of the one before (acc_mma), so the chain from S to S_end
 // passes through no LDS.  The block's other four waves (the memory waves,
 // one per strip) move everything else: they stage the next chunk's record
 // into the other of two LDS copies, load the one after, and store the
@@ -1037,11 +987,13 @@ __global__ void __launch_bounds__(kStripThreads, 1) wy_fwd_strip_kernel(WyArgs a
 
 // ----------------------------------------------------- backward: the carry
 
-// The reverse carry over saved records, one wave per 16-column strip as in
-// wy_fwd_strip_kernel: each wave carries its strip of dS through the chunks
-// in reverse, the chunk's record the only shared operand (two LDS copies, one
-// barrier per chunk); dO^T, dU^T, drhs^T and dS^T pass through the wave's own
-// LDS area.
+// The reverse carry over saved records, one wave per 16-column strip: each
+// wave carries its strip of dS through the chunks in reverse, the chunk's
+// record the only shared operand (two LDS copies, one barrier per chunk).
+// The chain from dS to the dS entering the chunk takes its B operands from
+// the accumulators (acc_mma); dO^T, which the products with dO read, and
+// drhs^T, on its way to 16-byte row stores, pass through the wave's own LDS
+// area.
 template <int CP, int LP>
 struct alignas(16) CarryStripT {          // one wave's transposes: dO^T and drhs^T [16][CP + 4]
     float ot[16 * (CP + 4)], rt[16 * (CP + 4)];
