@@ -614,6 +614,8 @@ def gdn2_bench(args):
     wy = chunk in (16, 32)
     tflops = bf / (bwd_ms * 1e-3) / 1e12
     workload = f"gdn2 b{B} h{H} t{T} latent{L} dense{D} chunk{chunk} f32, forward + VJP"
+    traffic = load_gdn2_traffic(workload) if wy else None
+    traffic_gbps = traffic / (bwd_ms * 1e-3) / 1e9 if traffic else None
     rec = {
         "metric": f"Gated DeltaNet-2 fwd+bwd GB/s, b{B} h{H} t{T} latent{L} dense{D} fp32",
         "value": round((fb + bb) / wall / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": steps,
@@ -630,7 +632,10 @@ def gdn2_bench(args):
                      "achieved": round(tflops, 3), "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 5),
                      "flops_per_launch": bf,
-                     "traffic": load_gdn2_traffic(workload) if wy else None},
+                     "traffic": traffic,
+                     # The same VJP seen from HBM: its measured bytes over its time.
+                     "traffic_GBps": round(traffic_gbps, 1) if traffic else None,
+                     "traffic_frac_of_hbm_peak": round(traffic_gbps / HBM_PEAK_GBPS, 4) if traffic else None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
