@@ -658,9 +658,9 @@ __global__ void __launch_bounds__(kThreads, 2) wy_fwd_fused_kernel(WyArgs a) {
 // rhs = w.v - M S, U = T rhs, O and S_end of a strip use only that strip's
 // columns, and every product takes its B operand straight from the
 // accumulators of the one before (acc_mma), so the chain from S to S_end
-// passes through no LDS.  The block's other four waves (the memory waves,
-// one per strip) move everything else: they stage the next chunk's record
-// into the other of two LDS copies, load the one after, and store the
+// passes through no LDS (a chain wave loads only its w and v).  The block's
+// other four waves (the memory waves, one per strip) stage the next chunk's
+// record into the other of two LDS copies, load the one after, and store the
 // previous chunk's U, context and state, which the chain wave left in LDS
 // (two copies per strip, as for the records).  The two kinds of wave share
 // each SIMD, so one's memory waits and the other's MFMA chains overlap, and a
