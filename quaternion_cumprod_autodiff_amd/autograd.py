@@ -206,13 +206,19 @@ class GatedDeltaNet2Function(torch.autograd.Function):
         return (*grads, None)
 
 
-def gated_deltanet2(query, key, value, erase, write, log_decay, initial_state, *, chunk: int = 32):
+def gated_deltanet2(query, key, value, erase, write, log_decay, initial_state, *, chunk: int = 32,
+                    low_memory: bool = False):
     """(context [B, H, T, D], final state [B, H, L, D]) of the gated delta-rule
     recurrence, differentiable in all seven inputs; float32 tensors on the GPU
     (query, key, erase, log_decay [B, H, T, L]; value, write [B, H, T, D];
-    initial_state [B, H, L, D])."""
+    initial_state [B, H, L, D]).
+
+    Without gradients to track, chunks of 16 and 32 run the factor and strip
+    kernels through a temporary boundary buffer (gdn2_boundary_bytes), the
+    faster forward; low_memory=True runs the kernel that needs no memory
+    beyond the outputs instead."""
     ins = (query, key, value, erase, write, log_decay, initial_state)
     if torch.is_grad_enabled() and any(t.requires_grad for t in ins):
         return GatedDeltaNet2Function.apply(*ins, chunk)
-    context, state, _ = capi.gdn2_fwd(*[t.contiguous() for t in ins], chunk=chunk, want_boundary=False)
+    context, state, _ = capi.gdn2_fwd(*[t.contiguous() for t in ins], chunk=chunk, want_boundary=not low_memory)
     return context, state

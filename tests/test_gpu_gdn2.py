@@ -161,6 +161,28 @@ def test_autograd_node_against_oracle():
     assert c3.grad_fn is None and torch.equal(c3, context.detach()) and torch.equal(s3, state.detach())
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_no_grad_forward_paths_chunk_wy(chunk):
+    """autograd.gated_deltanet2 without gradients: the default runs the factor
+    and strip kernels through a temporary boundary buffer, equal bit for bit to
+    the forward the autograd node runs; low_memory=True runs the fused kernel.
+    Both against the oracle."""
+    from quaternion_cumprod_autodiff_amd.autograd import gated_deltanet2
+    B, H, T, L, D = 1, 3, 77, 20, 52
+    arrays = make_gdn2_random_inputs(B, H, T, L, D, seed=21)
+    ts = [torch.from_numpy(arrays[n]).to(DEV) for n in NAMES]
+    r_ctx, r_state = oracle.gdn2_fwd(*[arrays[n] for n in NAMES])
+    with torch.no_grad():
+        c_fast, s_fast = gated_deltanet2(*ts, chunk=chunk)
+        c_low, s_low = gated_deltanet2(*ts, chunk=chunk, low_memory=True)
+    c_node, s_node, _ = capi.gdn2_fwd(*ts, chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(c_fast, c_node) and torch.equal(s_fast, s_node)
+    for label, c, st in (("default", c_fast, s_fast), ("low_memory", c_low, s_low)):
+        close(label + " context", c, r_ctx)
+        close(label + " state", st, r_state)
+
+
 def test_bench_workload_sampled_heads():
     """The bench's launch configuration (8 x 16 heads, 2048 steps, latent 64,
     dense 128, chunk 8: the register path), checked on sampled heads: heads are independent, so
