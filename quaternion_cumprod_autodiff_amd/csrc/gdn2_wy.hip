@@ -921,10 +921,12 @@ __global__ void __launch_bounds__(kStripThreads, 1) wy_fwd_strip_kernel(WyArgs a
         // chunk to the final state), from the chain wave's output copy.
         // Every store instruction issues whether or not `live` (dropped
         // lanes): a store under a branch would make the compiler's wait for
-        // the record at the top of the loop cover the stores.
-        auto store_out = [&](int64_t c, bool live) {
+        // the record at the top of the loop cover the stores.  `buf` is the
+        // output copy read: chunk c's, or (not live) the one no chain wave
+        // writes during the first chunk.
+        auto store_out = [&](int64_t c, int buf, bool live) {
             const int64_t t0 = c * CP;
-            const StripOut<CP, LP>& so = out[c & 1][strip];
+            const StripOut<CP, LP>& so = out[buf][strip];
             const OutRegion ub(a.ubuf ? a.ubuf + (head * nb * CP + t0) * a.D : nullptr, CP * a.D);
             const int rows = a.T - t0 < CP ? int(a.T - t0) : CP;
             const OutRegion ob(a.ctx + (head * a.T + t0) * a.D, rows * a.D);
@@ -975,13 +977,13 @@ __global__ void __launch_bounds__(kStripThreads, 1) wy_fwd_strip_kernel(WyArgs a
             // The previous chunk's results out, the next chunk's record into
             // the other copy (its last readers were behind the previous
             // barrier), then the load of the one after (unconditional, clamped).
-            store_out(c > 0 ? c - 1 : 0, c > 0);
+            store_out(c > 0 ? c - 1 : 0, int((c + 1) & 1), c > 0);
             rs.stage(f[(c + 1) & 1], rr);
             const int64_t c2 = c + 2 < nb ? c + 2 : nb - 1;
             load_rec<CP, LP>(rr, recs + c2 * R::kSize, mtid);
             __syncthreads();
         }
-        store_out(nb - 1, true);
+        store_out(nb - 1, int((nb - 1) & 1), true);
     }
 }
 
