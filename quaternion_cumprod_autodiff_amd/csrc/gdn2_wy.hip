@@ -971,16 +971,20 @@ __global__ void __launch_bounds__(kStripThreads, 1) wy_fwd_strip_kernel(WyArgs a
         load_rec<CP, LP>(rr, recs, mtid);
         rs.stage(f[0], rr);
         load_rec<CP, LP>(rr, recs + (nb > 1 ? 1 : 0) * R::kSize, mtid);
+        // As many (dropped) stores after that load as every chunk issues after
+        // its own, so that the wait for the record at the top of the loop does
+        // not cover the stores on any path into it.
+        store_out(0, 1, false);
         __syncthreads();   // record 0 staged
 
         for (int64_t c = 0; c < nb; ++c) {
-            // The previous chunk's results out, the next chunk's record into
-            // the other copy (its last readers were behind the previous
-            // barrier), then the load of the one after (unconditional, clamped).
-            store_out(c > 0 ? c - 1 : 0, int((c + 1) & 1), c > 0);
+            // The next chunk's record into the other copy (its last readers
+            // were behind the previous barrier), the load of the one after
+            // (unconditional, clamped), then the previous chunk's results out.
             rs.stage(f[(c + 1) & 1], rr);
             const int64_t c2 = c + 2 < nb ? c + 2 : nb - 1;
             load_rec<CP, LP>(rr, recs + c2 * R::kSize, mtid);
+            store_out(c > 0 ? c - 1 : 0, int((c + 1) & 1), c > 0);
             __syncthreads();
         }
         store_out(nb - 1, int((nb - 1) & 1), true);
